@@ -1,0 +1,149 @@
+/*
+ * mamba_scan.h -- C ABI of the MI355X (gfx950) selective-scan library.
+ *
+ * The library computes Mamba's selective state-space scan: the forward pass
+ * over a whole sequence and the single-token recurrent step used in O(1)
+ * decoding.  For every batch row b, channel d and state n, with a diagonal
+ * real A[d,n] = -exp(A_log[d,n]):
+ *
+ *   Delta_t   = softplus(delta[b,d,t] + delta_bias[d])      (or without softplus)
+ *   Abar_t    = exp(Delta_t * A[d,n])                       zero-order hold
+ *   Bbar_t    = (exp(Delta_t * A[d,n]) - 1) / A[d,n] * B[b,n,t]
+ *   h_t[n]    = Abar_t * h_{t-1}[n] + Bbar_t * u[b,d,t]      h_{-1} = initial_state or 0
+ *   y[b,d,t]  = (sum_n C[b,n,t] * h_t[n] + D[d] * u[b,d,t]) * SiLU(z[b,d,t])
+ *
+ * Sources (page and section): the selection mechanism and ZOH discretization,
+ * Mamba notes (awesome.papernotes.org), 设计 1; A = -exp(A_log) and the
+ * softplus-plus-bias step, same notes, 训练策略, and State space models and
+ * Mamba (jonathanding.github.io), §1.5 and §4; the ZOH formula
+ * Bbar = A^-1 (exp(Delta A) - I) B, State space models and Mamba, §2; the D
+ * skip, Mamba notes 设计 1 pseudo-code; the SiLU gate, Mamba notes 设计 3
+ * pseudo-code and 整体框架 figure; the single-token recurrence with a fixed
+ * (d, N) state, State space models and Mamba, §3 (recurrence mode) and Mamba
+ * notes 设计 2.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every tensor pointer is a caller-owned DEVICE pointer to contiguous,
+ *   row-major memory on the current HIP device.  The library never allocates
+ *   or frees device memory, never keeps a pointer after returning, and holds
+ *   no mutable global state; calls on different streams may run concurrently.
+ * - Element types: tensors marked "io" are float32 (MAMBA_SCAN_F32) or
+ *   bfloat16 (MAMBA_SCAN_BF16) according to io_dtype; tensors marked "f32"
+ *   are always float32.  Each pointer must be aligned to its element size.
+ * - All arithmetic is float32 on the device (state included); bfloat16
+ *   outputs are rounded to nearest even.
+ * - Validation (null pointers, sizes, dtype, alignment, workspace size) is
+ *   done on the host before any HIP call.  A failing call returns a non-zero
+ *   mamba_scan_status and launches nothing.  After launching, a launch error
+ *   reported by hipGetLastError() is returned as MAMBA_SCAN_ERR_HIP.
+ * - Work is queued asynchronously on `stream` (a hipStream_t; NULL means the
+ *   null stream).  The host never synchronizes.
+ * - No output may overlap any input, except `state` in mamba_scan_step,
+ *   which is updated in place by design.
+ * - NaN and Inf in inputs propagate; they are not checked.  A_log must be
+ *   finite (A = 0 is not supported).
+ */
+#ifndef MAMBA_SCAN_H
+#define MAMBA_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_MAX_DSTATE 16
+
+typedef enum { MAMBA_SCAN_F32 = 0, MAMBA_SCAN_BF16 = 1 } mamba_scan_dtype;
+
+typedef enum {
+  MAMBA_SCAN_OK = 0,
+  MAMBA_SCAN_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  MAMBA_SCAN_ERR_SHAPE = 2,       /* a size is out of range                              */
+  MAMBA_SCAN_ERR_DTYPE = 3,       /* io_dtype is not a mamba_scan_dtype                  */
+  MAMBA_SCAN_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size        */
+  MAMBA_SCAN_ERR_UNSUPPORTED = 5, /* dstate > MAMBA_SCAN_MAX_DSTATE or a bad tuning knob */
+  MAMBA_SCAN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required             */
+  MAMBA_SCAN_ERR_HIP = 7          /* the HIP runtime reported an error at launch         */
+} mamba_scan_status;
+
+/*
+ * Forward selective scan over a whole sequence.
+ *
+ *   u            (batch, dim, seqlen) io     input sequence, seqlen contiguous
+ *   delta        (batch, dim, seqlen) io     pre-activation step size
+ *   A_log        (dim, dstate)        f32    A = -exp(A_log)
+ *   B, C         (batch, dstate, seqlen) io  input / output projections, shared by all channels
+ *   D            (dim)                f32    skip weight, NULL means 0
+ *   z            (batch, dim, seqlen) io     gate, NULL means no gate (y is not multiplied)
+ *   delta_bias   (dim)                f32    added to delta before softplus, NULL means 0
+ *   initial_state(batch, dim, dstate) f32    h_{-1}, NULL means 0
+ *   final_state  (batch, dim, dstate) f32    OUT: h after the last token, NULL means not written
+ *   y            (batch, dim, seqlen) io     OUT: gated output
+ *   delta_softplus  non-zero: Delta = softplus(delta + bias); zero: Delta = delta + bias
+ *   workspace    device scratch of at least mamba_scan_fwd_workspace_size(...) bytes,
+ *                256-byte aligned; its contents on entry are ignored and on exit undefined
+ *
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, seqlen >= 0.  seqlen == 0
+ * writes no y and sets final_state to initial_state (or zeros).
+ */
+int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                   float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                   int io_dtype, int delta_softplus, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mamba_scan_fwd needs for these sizes (0 only for seqlen == 0).
+ * Returns (size_t)-1 for sizes mamba_scan_fwd would reject. */
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
+
+/*
+ * Same as mamba_scan_fwd with two explicit launch choices (0 = automatic):
+ *   nchunks          number of time chunks scanned in parallel, joined by an
+ *                    inter-chunk carry of the state (1 = one sequential pass);
+ *                    must be <= max(1, ceil(seqlen / 64)).
+ *   states_per_wave  states held per lane: 2 or 4.
+ * The result is the same function; only rounding order differs.  The
+ * workspace must be at least mamba_scan_fwd_workspace_size_ex(...) bytes.
+ * Used for testing the chunked path at small sizes and for tuning.
+ */
+int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                      const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                      float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                      int io_dtype, int delta_softplus, int64_t nchunks, int states_per_wave, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                                        int64_t nchunks, int states_per_wave);
+
+/*
+ * One recurrent step for one token per (batch, channel); the state is updated
+ * IN PLACE and y is written.  Exactly one iteration of the forward recurrence.
+ *
+ *   state     (batch, dim, dstate) f32   IN/OUT
+ *   x, dt     (batch, dim)         io    token input and pre-activation step size
+ *   A_log     (dim, dstate)        f32
+ *   B, C      (batch, dstate)      io
+ *   D         (dim)                f32   NULL means 0
+ *   z         (batch, dim)         io    NULL means no gate
+ *   dt_bias   (dim)                f32   NULL means 0
+ *   dt_softplus  as delta_softplus above
+ *   y         (batch, dim)         io    OUT
+ */
+int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,
+                    int64_t dim, int64_t dstate, int io_dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* mamba_scan_status_str(int status);
+
+/* MAMBA_SCAN_ABI_VERSION of the built library. */
+int mamba_scan_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA_SCAN_H */

@@ -1,0 +1,177 @@
+"""fp64 CPU oracle for the selective scan (forward pass and single-token step).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The product path (the
+HIP library and its Python binding) never imports, links or executes anything
+here, and nothing here imports the product package.
+
+The arithmetic lives in ``scan_oracle.c`` (plain C, double precision, one
+sequential time loop per (batch, channel); see its header for the passages of
+the pages each step follows).  This module only builds that file with gcc,
+loads it with ctypes and converts arguments to contiguous float64 arrays.
+Inputs given in bfloat16 or float32 are widened exactly (every bf16/fp32
+value is representable in fp64), so the oracle sees the very values the GPU
+consumes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "scan_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_scan.so")
+_lib = None
+
+
+def build(verbose: bool = False) -> str:
+    """Compile scan_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
+    return _LIB_PATH
+
+
+def _bind(path: str):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_scan_fwd.restype = ctypes.c_int
+    lib.oracle_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
+    lib.oracle_scan_step.restype = ctypes.c_int
+    lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        build()
+    _lib = _bind(_LIB_PATH)
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def _f64(a, shape=None) -> Optional[np.ndarray]:
+    """Exact widening to a C-contiguous float64 array (accepts numpy or torch CPU)."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor
+        import torch
+
+        a = a.detach().to("cpu")
+        if a.dtype in (torch.bfloat16, torch.float16):
+            a = a.to(torch.float32)
+        a = a.numpy()
+    out = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and out.shape != tuple(shape):
+        raise ValueError(f"oracle: expected shape {tuple(shape)}, got {out.shape}")
+    return out
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan_fwd(u, delta, A_log, B, C, D=None, z=None, delta_bias=None, initial_state=None,
+             delta_softplus: bool = True, return_final_state: bool = True,
+             nthreads: int = 0, _lib_override=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Selective-scan forward in fp64.
+
+    Shapes: u, delta, z: (batch, dim, L); B, C: (batch, dstate, L); A_log: (dim, dstate);
+    D, delta_bias: (dim,); initial_state: (batch, dim, dstate).
+    Returns (y (batch, dim, L) float64, final_state (batch, dim, dstate) float64 or None).
+    """
+    u = _f64(u)
+    if u.ndim != 3:
+        raise ValueError("oracle: u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    delta = _f64(delta, (batch, dim, L))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (batch, dstate, L))
+    C = _f64(C, (batch, dstate, L))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, L))
+    delta_bias = _f64(delta_bias, (dim,))
+    initial_state = _f64(initial_state, (batch, dim, dstate))
+    y = np.empty((batch, dim, L), dtype=np.float64)
+    fs = np.empty((batch, dim, dstate), dtype=np.float64) if return_final_state else None
+    rc = (_lib_override or _load()).oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(delta_bias), _ptr(initial_state), _ptr(fs), _ptr(y), batch, dim,
+                                 dstate, L, int(bool(delta_softplus)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_fwd returned {rc}")
+    return y, fs
+
+
+def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True,
+              nthreads: int = 0, _lib_override=None) -> Tuple[np.ndarray, np.ndarray]:
+    """One recurrent step in fp64.  Returns (y (batch, dim), new_state (batch, dim, dstate)).
+
+    Shapes: state: (batch, dim, dstate); x, dt, z: (batch, dim); B, C: (batch, dstate);
+    A_log: (dim, dstate); D, dt_bias: (dim,).  The input state is not modified.
+    """
+    st = _f64(state).copy()
+    if st.ndim != 3:
+        raise ValueError("oracle: state must be (batch, dim, dstate)")
+    batch, dim, dstate = st.shape
+    x = _f64(x, (batch, dim))
+    dt = _f64(dt, (batch, dim))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (batch, dstate))
+    C = _f64(C, (batch, dstate))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim))
+    dt_bias = _f64(dt_bias, (dim,))
+    y = np.empty((batch, dim), dtype=np.float64)
+    rc = (_lib_override or _load()).oracle_scan_step(_ptr(st), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                  _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), batch, dim,
+                                  dstate, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_step returned {rc}")
+    return y, st
+
+
+class Variant:
+    """The same wrapper bound to another build of scan_oracle.c (used by the
+    tests that plant a mistake in a copy of the oracle and check that the pins
+    catch it)."""
+
+    def __init__(self, lib_path: str):
+        self._lib = _bind(lib_path)
+
+    def scan_fwd(self, *a, **k):
+        return scan_fwd(*a, _lib_override=self._lib, **k)
+
+    def scan_step(self, *a, **k):
+        return scan_step(*a, _lib_override=self._lib, **k)
+
+
+def build_variant(src_text: str, out_dir: str, name: str) -> "Variant":
+    """Compile C source text (a modified copy of scan_oracle.c) and bind it."""
+    src = os.path.join(out_dir, name + ".c")
+    so = os.path.join(out_dir, "lib" + name + ".so")
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", so, src, "-lm"], check=True)
+    return Variant(so)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()

@@ -1,0 +1,155 @@
+"""Seeded input generation for the selective-scan workloads.
+
+Every tensor is drawn from its own numpy PCG64 stream keyed by
+``SeedSequence(seed, spawn_key=(tensor_key, block))``; large tensors are cut
+into blocks of whole rows (about 2^20 elements each) with one stream per block,
+so generation runs in parallel threads and stays reproducible regardless of the
+thread count.  Draws are float32; bfloat16 inputs are the round-to-nearest-even
+rounding of those draws (torch CPU conversion).  All outputs are CPU tensors.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, Optional, Union
+
+import numpy as np
+import torch
+
+from .configs import Config, get_config
+
+# stream keys, fixed order
+K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS = range(9)
+_BLOCK_ELEMS = 1 << 20
+
+
+def _threads(threads: Optional[int]) -> int:
+    if threads:
+        return int(threads)
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _gen(seed: int, key: tuple) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=key)))
+
+
+def _normal_rows(seed: int, key: tuple, rows: int, L: int, io: str, std: float = 1.0,
+                 threads: Optional[int] = None) -> torch.Tensor:
+    """(rows, L) tensor of N(0, std^2) draws in the io dtype."""
+    dtype = torch.float32 if io == "f32" else torch.bfloat16
+    out = torch.empty((rows, L), dtype=dtype)
+    if rows == 0 or L == 0:
+        return out
+    block_rows = max(1, _BLOCK_ELEMS // L)
+    nblk = math.ceil(rows / block_rows)
+
+    def work(i: int) -> None:
+        r0 = i * block_rows
+        r1 = min(rows, r0 + block_rows)
+        tmp = _gen(seed, key + (i,)).standard_normal((r1 - r0, L), dtype=np.float32)
+        if std != 1.0:
+            tmp *= np.float32(std)
+        out[r0:r1] = torch.from_numpy(tmp).to(dtype)
+
+    nt = _threads(threads)
+    if nblk == 1 or nt == 1:
+        for i in range(nblk):
+            work(i)
+    else:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(work, range(nblk)))
+    return out
+
+
+def a_log_s4d_real(dim: int, dstate: int) -> torch.Tensor:
+    """float32(log(1..N)) for every channel, shape (dim, dstate)."""
+    row = np.log(np.arange(1, dstate + 1, dtype=np.float64)).astype(np.float32)
+    return torch.from_numpy(np.ascontiguousarray(np.broadcast_to(row, (dim, dstate))).copy())
+
+
+def delta_bias_init(seed: int, dim: int, lo: float = 0.001, hi: float = 0.1) -> torch.Tensor:
+    """float32(log(expm1(U[lo, hi]))) per channel: softplus of it is uniform on [lo, hi]."""
+    uni = _gen(seed, (K_BIAS, 0)).uniform(lo, hi, size=dim)
+    return torch.from_numpy(np.log(np.expm1(uni)).astype(np.float32))
+
+
+def forward_inputs(cfg: Union[int, Config, None] = None, *, seed: int = 0, batch: int = None, dim: int = None,
+                   dstate: int = None, seqlen: int = None, io: str = None, gated: bool = None,
+                   has_D: bool = None, has_bias: bool = None, initial_state: bool = False,
+                   threads: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Inputs of one forward scan as CPU tensors.
+
+    Either a config (index or Config) or explicit shape keywords (which override
+    the config's values).  Keys: u, delta, z, B, C (io dtype), A_log, D,
+    delta_bias (float32), initial_state (float32 or None).
+    """
+    c = get_config(cfg) if isinstance(cfg, int) else cfg
+    pick = lambda v, attr, dflt: v if v is not None else (getattr(c, attr) if c is not None else dflt)
+    b = pick(batch, "batch", 1)
+    d = pick(dim, "dim", 64)
+    n = pick(dstate, "dstate", 16)
+    L = pick(seqlen, "seqlen", 256)
+    io_ = pick(io, "io", "bf16")
+    gated_ = pick(gated, "gated", True)
+    hasD = pick(has_D, "has_D", True)
+    hasB = pick(has_bias, "has_bias", True)
+    out: Dict[str, Optional[torch.Tensor]] = {}
+    out["u"] = _normal_rows(seed, (K_U,), b * d, L, io_, threads=threads).view(b, d, L)
+    out["delta"] = _normal_rows(seed, (K_DELTA,), b * d, L, io_, threads=threads).view(b, d, L)
+    out["z"] = _normal_rows(seed, (K_Z,), b * d, L, io_, threads=threads).view(b, d, L) if gated_ else None
+    out["B"] = _normal_rows(seed, (K_B,), b * n, L, io_, threads=threads).view(b, n, L)
+    out["C"] = _normal_rows(seed, (K_C,), b * n, L, io_, threads=threads).view(b, n, L)
+    out["A_log"] = a_log_s4d_real(d, n)
+    out["D"] = torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(d, dtype=np.float32)) if hasD else None
+    out["delta_bias"] = delta_bias_init(seed, d) if hasB else None
+    out["initial_state"] = (_normal_rows(seed, (K_STATE,), b * d, n, "f32", std=0.1, threads=threads)
+                            .view(b, d, n) if initial_state else None)
+    return out
+
+
+def step_initial(cfg: Union[int, Config, None] = None, *, seed: int = 0, batch: int = None, dim: int = None,
+                 dstate: int = None, threads: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Decode-step state and parameters: state (b,d,n) fp32 ~ N(0, 0.1^2), A_log, D, dt_bias."""
+    c = get_config(cfg) if isinstance(cfg, int) else cfg
+    b = batch if batch is not None else c.batch
+    d = dim if dim is not None else c.dim
+    n = dstate if dstate is not None else c.dstate
+    return {
+        "state": _normal_rows(seed, (K_STATE,), b * d, n, "f32", std=0.1, threads=threads).view(b, d, n),
+        "A_log": a_log_s4d_real(d, n),
+        "D": torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(d, dtype=np.float32)),
+        "dt_bias": delta_bias_init(seed, d),
+    }
+
+
+def step_inputs(cfg: Union[int, Config, None], k: int, *, seed: int = 0, batch: int = None, dim: int = None,
+                dstate: int = None, io: str = None, gated: bool = None,
+                threads: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Fresh per-step inputs of decode step k: x, dt, z (b,d) and B, C (b,n) in the io dtype."""
+    c = get_config(cfg) if isinstance(cfg, int) else cfg
+    b = batch if batch is not None else c.batch
+    d = dim if dim is not None else c.dim
+    n = dstate if dstate is not None else c.dstate
+    io_ = io if io is not None else c.io
+    g_ = gated if gated is not None else c.gated
+    key = (K_STEPS, int(k))
+    return {
+        "x": _normal_rows(seed, key + (0,), b, d, io_, threads=threads),
+        "dt": _normal_rows(seed, key + (1,), b, d, io_, threads=threads),
+        "z": _normal_rows(seed, key + (2,), b, d, io_, threads=threads) if g_ else None,
+        "B": _normal_rows(seed, key + (3,), b, n, io_, threads=threads),
+        "C": _normal_rows(seed, key + (4,), b, n, io_, threads=threads),
+    }
+
+
+def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of a CPU tensor (bf16/fp16/fp32/fp64) to float64 numpy."""
+    t = t.detach().to("cpu")
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.to(torch.float32)
+    return t.numpy().astype(np.float64)
