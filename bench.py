@@ -1,0 +1,226 @@
+"""Benchmark: selective-scan forward throughput on one MI355X.
+
+A step is one forward selective scan (all of: staging, softplus, ZOH
+discretization, recurrence, readout, D skip, SiLU gate, final state) over the
+Mamba-1.4B-shaped layer workload: batch 4, d_inner 4096, d_state 16, L 8192,
+bf16 io, fp32 state, gated, final state returned.  Inputs are synthetic
+(seeded), resident in HBM before timing starts.
+
+Prints one JSON line with the throughput in Gtok*ch/s, the algorithmic HBM
+bandwidth, a roofline record for the scan kernel and the fp64 oracle's
+throughput on the host cores (CPU baseline, on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "selective-scan fwd Gtok·ch/s and achieved HBM GB/s (% of peak), 1.4B shape"
+HBM_PEAK_GBPS = 8000.0
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz (unpacked fp32; a
+# transcendental occupies two issue slots on gfx950, measured)
+VALU_SLOTS_PEAK = 256 * 4 * 16 * 2.4e9
+# algorithmic issue slots: per (token, channel, state) 6 fp32 VALU ops + 1 exp
+# (2 slots); per (token, channel) softplus (exp + log + 3 ops = 7), SiLU gate
+# (exp + rcp + 3 ops + the multiply = 8) and the D skip (1)
+SLOTS_PER_TCN = 8.0
+SLOTS_PER_TC_GATED = 16.0
+SLOTS_PER_TC_UNGATED = 8.0
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_55_amd", "csrc", f)
+                  for f in ("scan_fwd.hip", "io.h", "internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(nbytes_alg: float):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+    if it was taken on the current kernel source; else None."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    for line in open(PROFILE_TRAFFIC):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload index (forward configs 0-3)")
+    ap.add_argument("--npw", type=int, default=0, help="states per wave (0 = library default)")
+    ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); the scan shards over "
+              "(batch, channel) with no communication, so the whole-job rate at N GPUs is N times the one-GPU "
+              "rate of the per-GPU share -- run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import CONFIGS, forward_inputs, max_rel_err
+
+    c = CONFIGS[args.config]
+    if c.kind != "fwd":
+        raise SystemExit("bench.py times the forward scan (configs 0-3)")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = forward_inputs(c)
+    gen_s = time.time() - t0
+    a = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    b, d, n, L = c.batch, c.dim, c.dstate, c.seqlen
+    io = mscan.BF16 if c.io == "bf16" else mscan.F32
+    ws_bytes = mscan.fwd_workspace_size(b, d, n, L, io, args.nchunks, args.npw)
+    ws = torch.empty(max(ws_bytes, 1) + 256, dtype=torch.uint8, device=dev)
+    y = torch.empty((b, d, L), dtype=a["u"].dtype, device=dev)
+    fs = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                       delta_bias=a["delta_bias"], out=y, final_state=fs, return_final_state=True,
+                       workspace=ws, nchunks=args.nchunks, states_per_wave=args.npw, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    launch_ms_avg = sum(launch_ms) / len(launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    tc = b * d * L
+    value = tc / (ms_per_step * 1e-3) / 1e9
+    alg_bytes = c.algorithmic_bytes()
+    hbm_gbps = alg_bytes / (launch_ms_avg * 1e-3) / 1e9
+    slots = tc * n * SLOTS_PER_TCN + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
+    achieved = slots / (launch_ms_avg * 1e-3) / 1e12
+    peak = VALU_SLOTS_PEAK / 1e12
+    traffic = read_traffic(alg_bytes)
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        rows = [0, d // 3, d - 1] if b == 1 else [0, d // 2 + 7, (b - 1) * d + d - 1]
+        yg = y.view(b * d, L)[rows].cpu()
+        fg = fs.view(b * d, n)[rows].cpu()
+        errs = []
+        for i, r in enumerate(rows):
+            bb, dd = divmod(r, d)
+            sub = dict(u=inp["u"][bb:bb + 1, dd:dd + 1], delta=inp["delta"][bb:bb + 1, dd:dd + 1],
+                       A_log=inp["A_log"][dd:dd + 1], B=inp["B"][bb:bb + 1], C=inp["C"][bb:bb + 1],
+                       D=None if inp["D"] is None else inp["D"][dd:dd + 1],
+                       z=None if inp["z"] is None else inp["z"][bb:bb + 1, dd:dd + 1],
+                       delta_bias=None if inp["delta_bias"] is None else inp["delta_bias"][dd:dd + 1])
+            yr, fr = oracle.scan_fwd(**sub)
+            errs.append((yr[0, 0], fr[0, 0]))
+        parity = {
+            "rows": rows,
+            "y_max_rel": max_rel_err(yg, np.stack([e[0] for e in errs])),
+            "final_state_max_rel": max_rel_err(fg, np.stack([e[1] for e in errs])),
+            "tol": c.tol,
+        }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = host_cores()
+        # bounded sample: batch row 0 of the same workload (all channels, full length)
+        sub = {k: (v[:1] if (v is not None and k in ("u", "delta", "z", "B", "C", "initial_state")) else v)
+               for k, v in inp.items()}
+        c0 = time.perf_counter()
+        oracle.scan_fwd(sub["u"], sub["delta"], sub["A_log"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
+                        delta_bias=sub["delta_bias"], nthreads=cores)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(d * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"batch row 0 of the workload: 1 x {d} channels x {L} tokens x {n} states, fp64, "
+                         f"{cs:.2f} s wall incl. fp64 widening of inputs"}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{c.name} selective-scan forward: batch {b}, d_inner {d}, d_state {n}, L {L}, "
+                        f"{c.io} io, fp32 state, {'gated' if c.gated else 'ungated'}, final state",
+            "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io": c.io, "gated": c.gated,
+            "parallelism": "single GPU",
+        },
+        "kernel_ms": round(launch_ms_avg, 4),
+        "hbm": {"algorithmic_bytes": alg_bytes, "GBps": round(hbm_gbps, 1),
+                "frac_of_8TBps": round(hbm_gbps / HBM_PEAK_GBPS, 4)},
+        "roofline": {
+            "bound": "alu",
+            "achieved": round(achieved, 3),
+            "peak": round(peak, 3),
+            "unit": "T VALU issue-slots/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "parity_sampled": parity,
+        "input_gen_s": round(gen_s, 2),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,205 @@
+"""MI355X-native selective scan (Mamba): Python binding over libmamba_scan.so.
+
+This module only marshals arguments: it checks torch tensors (device, dtype,
+contiguity, shape), allocates outputs and the workspace with torch, and calls
+the C ABI declared in include/mamba_scan.h on the current HIP stream.  Every
+step of the computation runs in the library's HIP kernels.  If the library is
+not built, importing works but every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmamba_scan.so")
+
+F32, BF16 = 0, 1
+STATUS = {
+    0: "MAMBA_SCAN_OK", 1: "MAMBA_SCAN_ERR_NULL", 2: "MAMBA_SCAN_ERR_SHAPE", 3: "MAMBA_SCAN_ERR_DTYPE",
+    4: "MAMBA_SCAN_ERR_ALIGN", 5: "MAMBA_SCAN_ERR_UNSUPPORTED", 6: "MAMBA_SCAN_ERR_WORKSPACE",
+    7: "MAMBA_SCAN_ERR_HIP",
+}
+EXPORTED = (
+    "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
+    "mamba_scan_step", "mamba_scan_status_str", "mamba_scan_abi_version",
+)
+
+_lib = None
+
+
+class MambaScanError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)} ({msg})")
+        self.code = code
+
+
+def load_library():
+    """Loads libmamba_scan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m selective_state_space_55_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    lib.mamba_scan_fwd.restype = I
+    lib.mamba_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [I, I, P, SZ, P]
+    lib.mamba_scan_fwd_ex.restype = I
+    lib.mamba_scan_fwd_ex.argtypes = [P] * 11 + [I64] * 4 + [I, I, I64, I, P, SZ, P]
+    lib.mamba_scan_fwd_workspace_size.restype = SZ
+    lib.mamba_scan_fwd_workspace_size.argtypes = [I64] * 4 + [I]
+    lib.mamba_scan_fwd_workspace_size_ex.restype = SZ
+    lib.mamba_scan_fwd_workspace_size_ex.argtypes = [I64] * 4 + [I, I64, I]
+    lib.mamba_scan_step.restype = I
+    lib.mamba_scan_step.argtypes = [P] * 9 + [I, P] + [I64] * 3 + [I, P]
+    lib.mamba_scan_status_str.restype = ctypes.c_char_p
+    lib.mamba_scan_status_str.argtypes = [I]
+    lib.mamba_scan_abi_version.restype = I
+    lib.mamba_scan_abi_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load_library().mamba_scan_abi_version())
+
+
+def status_str(code: int) -> str:
+    return load_library().mamba_scan_status_str(int(code)).decode()
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise MambaScanError(fn, code, status_str(code))
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise ValueError(f"io tensors must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _req(name: str, t: Optional[torch.Tensor], shape, dtype, device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def fwd_workspace_size(batch: int, dim: int, dstate: int, seqlen: int, io_dtype: int = BF16, nchunks: int = 0,
+                       states_per_wave: int = 0) -> int:
+    n = load_library().mamba_scan_fwd_workspace_size_ex(batch, dim, dstate, seqlen, io_dtype, nchunks,
+                                                        states_per_wave)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("mamba_scan_fwd_workspace_size: sizes rejected")
+    return int(n)
+
+
+def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+             delta_softplus: bool = True, return_final_state: bool = False, *,
+             out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None, nchunks: int = 0, states_per_wave: int = 0,
+             stream=None):
+    """Selective-scan forward.  u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in the io dtype
+    (float32 or bfloat16); A_log (dim, dstate), D, delta_bias (dim,), initial_state (batch, dim, dstate)
+    in float32.  Returns y (batch, dim, L), or (y, final_state) if return_final_state."""
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd needs device tensors (HIP)")
+    io = _io_dtype(u)
+    iot = u.dtype
+    dstate = A_log.shape[-1] if A_log.dim() == 2 else -1
+    _req("u", u, (batch, dim, L), iot, dev)
+    _req("delta", delta, (batch, dim, L), iot, dev)
+    _req("A_log", A_log, (dim, dstate), torch.float32, dev)
+    _req("B", B, (batch, dstate, L), iot, dev)
+    _req("C", C, (batch, dstate, L), iot, dev)
+    _req("D", D, (dim,), torch.float32, dev)
+    _req("z", z, (batch, dim, L), iot, dev)
+    _req("delta_bias", delta_bias, (dim,), torch.float32, dev)
+    _req("initial_state", initial_state, (batch, dim, dstate), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, dim, L), dtype=iot, device=dev)
+    _req("out", y, (batch, dim, L), iot, dev)
+    fs = final_state
+    if fs is None and return_final_state:
+        fs = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _req("final_state", fs, (batch, dim, dstate), torch.float32, dev)
+    need = fwd_workspace_size(batch, dim, dstate, L, io, nchunks, states_per_wave)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if ws is not None:
+        base = ws.data_ptr()
+        off = (-base) % 256
+        ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, ws.numel() * ws.element_size() - off)
+    rc = lib.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), _ptr(initial_state), _ptr(fs), _ptr(y), batch, dim, dstate, L, io,
+                               int(bool(delta_softplus)), int(nchunks), int(states_per_wave), ws_ptr, ws_bytes,
+                               _stream(dev, stream))
+    _check("mamba_scan_fwd", rc)
+    return (y, fs) if return_final_state else y
+
+
+def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor,
+              C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+              dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True, *,
+              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One recurrent step.  state (batch, dim, dstate) float32 is updated IN PLACE; x, dt, z (batch, dim)
+    and B, C (batch, dstate) in the io dtype.  Returns y (batch, dim)."""
+    lib = load_library()
+    if state.dim() != 3:
+        raise ValueError("state must be (batch, dim, dstate)")
+    batch, dim, dstate = state.shape
+    dev = state.device
+    if dev.type != "cuda":
+        raise ValueError("scan_step needs device tensors (HIP)")
+    io = _io_dtype(x)
+    iot = x.dtype
+    _req("state", state, (batch, dim, dstate), torch.float32, dev)
+    _req("x", x, (batch, dim), iot, dev)
+    _req("dt", dt, (batch, dim), iot, dev)
+    _req("A_log", A_log, (dim, dstate), torch.float32, dev)
+    _req("B", B, (batch, dstate), iot, dev)
+    _req("C", C, (batch, dstate), iot, dev)
+    _req("D", D, (dim,), torch.float32, dev)
+    _req("z", z, (batch, dim), iot, dev)
+    _req("dt_bias", dt_bias, (dim,), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, dim), dtype=iot, device=dev)
+    _req("out", y, (batch, dim), iot, dev)
+    rc = lib.mamba_scan_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), batch, dim, dstate, io,
+                             _stream(dev, stream))
+    _check("mamba_scan_step", rc)
+    return y

@@ -1,0 +1,65 @@
+"""Builds lib/libmamba_scan.so from csrc/*.hip with hipcc for gfx950.
+
+Usage: python -m selective_state_space_55_amd.build  (or __graft_entry__.build()).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB_DIR = os.path.join(HERE, "lib")
+LIB_PATH = os.path.join(LIB_DIR, "libmamba_scan.so")
+SOURCES = ["api.hip", "scan_fwd.hip", "scan_step.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
+
+
+def flags() -> list:
+    return [
+        f"--offload-arch={ARCH}",
+        "-O3",
+        "-std=c++17",
+        "-fPIC",
+        "-shared",
+        # packed fp32 VALU ops are kept out of generated code
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-Wno-unused-command-line-argument",
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(LIB_DIR, exist_ok=True)
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc()] + flags() + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
+    if verbose and err:
+        print(err, file=sys.stderr)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+def asm(out_path: str) -> str:
+    """Writes the gfx950 assembly of the kernels (for inspection)."""
+    cmd = [hipcc()] + [f for f in flags() if f not in ("-shared", "-fPIC")] + [
+        "--cuda-device-only", "-S", "-o", out_path, os.path.join(CSRC, "scan_fwd.hip")]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return out_path
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,130 @@
+// api.hip -- C ABI of libmamba_scan (declared in include/mamba_scan.h).
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime; a rejected call launches nothing and returns a status code.
+#include <limits.h>
+
+#include <algorithm>
+
+#include "../../include/mamba_scan.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+int check_common(int64_t batch, int64_t dim, int64_t dstate, int io_dtype) {
+  if (io_dtype != MAMBA_SCAN_F32 && io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || dstate < 1) return MAMBA_SCAN_ERR_SHAPE;
+  if (dstate > MAMBA_SCAN_MAX_DSTATE) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(batch, dim, &t) || !mul_ok(t, 64, &t)) return MAMBA_SCAN_ERR_SHAPE;
+  return MAMBA_SCAN_OK;
+}
+
+int check_fwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype) {
+  int st = check_common(batch, dim, dstate, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (seqlen < 0) return MAMBA_SCAN_ERR_SHAPE;
+  int64_t t;
+  // (batch*dim*(seqlen+64)*4 bytes must be representable)
+  if (!mul_ok(batch * dim, seqlen + 64, &t) || !mul_ok(t, 16, &t)) return MAMBA_SCAN_ERR_SHAPE;
+  return MAMBA_SCAN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mamba_scan_status_str(int status) {
+  switch (status) {
+    case MAMBA_SCAN_OK: return "ok";
+    case MAMBA_SCAN_ERR_NULL: return "a required pointer is NULL";
+    case MAMBA_SCAN_ERR_SHAPE: return "a size is out of range";
+    case MAMBA_SCAN_ERR_DTYPE: return "io_dtype is not MAMBA_SCAN_F32 or MAMBA_SCAN_BF16";
+    case MAMBA_SCAN_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case MAMBA_SCAN_ERR_UNSUPPORTED: return "unsupported option (dstate > 16 or an invalid tuning knob)";
+    case MAMBA_SCAN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MAMBA_SCAN_ERR_HIP: return "the HIP runtime reported an error";
+    default: return "unknown status";
+  }
+}
+
+int mamba_scan_abi_version(void) { return MAMBA_SCAN_ABI_VERSION; }
+
+size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
+                                        int64_t nchunks, int states_per_wave) {
+  if (check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
+  mscan::FwdPlan p;
+  if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, nchunks, states_per_wave, &p)) return (size_t)-1;
+  return p.ws_total;
+}
+
+size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype) {
+  return mamba_scan_fwd_workspace_size_ex(batch, dim, dstate, seqlen, io_dtype, 0, 0);
+}
+
+int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                      const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                      float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                      int io_dtype, int delta_softplus, int64_t nchunks, int states_per_wave, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (!u || !delta || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, delta_bias, initial_state, final_state};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::FwdPlan plan;
+  if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, nchunks, states_per_wave, &plan))
+    return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (plan.ws_total > 0) {
+    if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
+  }
+  mscan::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_state; a.final_state = final_state; a.y = y;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = delta_softplus != 0;
+  a.workspace = workspace;
+  hipError_t e = mscan::launch_fwd(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
+int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                   float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                   int io_dtype, int delta_softplus, void* workspace, size_t workspace_bytes, void* stream) {
+  return mamba_scan_fwd_ex(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim,
+                           dstate, seqlen, io_dtype, delta_softplus, 0, 0, workspace, workspace_bytes, stream);
+}
+
+int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
+                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,
+                    int64_t dim, int64_t dstate, int io_dtype, void* stream) {
+  int st = check_common(batch, dim, dstate, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (!state || !x || !dt || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {x, dt, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {state, A_log, D, dt_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::StepArgs a{};
+  a.state = state; a.x = x; a.dt = dt; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = dt_bias;
+  a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate; a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = dt_softplus != 0;
+  hipError_t e = mscan::launch_step(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
+}  // extern "C"

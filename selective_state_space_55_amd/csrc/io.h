@@ -1,0 +1,136 @@
+// io.h -- device-side element access for float32 and bfloat16 tensors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mscan {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bfloat16 storage is handled as raw uint16_t bits.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two bfloat16 (round to nearest even) packed low|high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <typename IoT>
+struct Io;
+
+// Eight consecutive elements, as raw storage.
+template <>
+struct Io<uint16_t> {
+  struct V8 {
+    uint4 w;
+  };
+  static __device__ __forceinline__ V8 zero() { return V8{make_uint4(0, 0, 0, 0)}; }
+  static __device__ __forceinline__ V8 load8(const uint16_t* p) { return V8{*reinterpret_cast<const uint4*>(p)}; }
+  static __device__ __forceinline__ V8 load_n(const uint16_t* p, int n) {
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (j < n) ? p[j] : (uint16_t)0;
+    V8 v;
+    v.w.x = e[0] | ((uint32_t)e[1] << 16);
+    v.w.y = e[2] | ((uint32_t)e[3] << 16);
+    v.w.z = e[4] | ((uint32_t)e[5] << 16);
+    v.w.w = e[6] | ((uint32_t)e[7] << 16);
+    return v;
+  }
+  static __device__ __forceinline__ void to_f32(const V8& v, float (&f)[8]) {
+    f[0] = bf16_lo(v.w.x); f[1] = bf16_hi(v.w.x);
+    f[2] = bf16_lo(v.w.y); f[3] = bf16_hi(v.w.y);
+    f[4] = bf16_lo(v.w.z); f[5] = bf16_hi(v.w.z);
+    f[6] = bf16_lo(v.w.w); f[7] = bf16_hi(v.w.w);
+  }
+  static __device__ __forceinline__ V8 from_f32(const float (&f)[8]) {
+    V8 v;
+    v.w.x = pack_bf16x2(f[0], f[1]);
+    v.w.y = pack_bf16x2(f[2], f[3]);
+    v.w.z = pack_bf16x2(f[4], f[5]);
+    v.w.w = pack_bf16x2(f[6], f[7]);
+    return v;
+  }
+  static __device__ __forceinline__ void store8(uint16_t* p, const V8& v) { *reinterpret_cast<uint4*>(p) = v.w; }
+  static __device__ __forceinline__ void store_n(uint16_t* p, const V8& v, int n) {
+    const uint32_t w[4] = {v.w.x, v.w.y, v.w.z, v.w.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < n) p[j] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+  }
+  static __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
+  static __device__ __forceinline__ void store1(uint16_t* p, float f) {
+    *p = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
+  }
+};
+
+template <>
+struct Io<float> {
+  struct V8 {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ V8 zero() { return V8{make_float4(0, 0, 0, 0), make_float4(0, 0, 0, 0)}; }
+  static __device__ __forceinline__ V8 load8(const float* p) {
+    return V8{reinterpret_cast<const float4*>(p)[0], reinterpret_cast<const float4*>(p)[1]};
+  }
+  static __device__ __forceinline__ V8 load_n(const float* p, int n) {
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = (j < n) ? p[j] : 0.0f;
+    return V8{make_float4(e[0], e[1], e[2], e[3]), make_float4(e[4], e[5], e[6], e[7])};
+  }
+  static __device__ __forceinline__ void to_f32(const V8& v, float (&f)[8]) {
+    f[0] = v.a.x; f[1] = v.a.y; f[2] = v.a.z; f[3] = v.a.w;
+    f[4] = v.b.x; f[5] = v.b.y; f[6] = v.b.z; f[7] = v.b.w;
+  }
+  static __device__ __forceinline__ V8 from_f32(const float (&f)[8]) {
+    return V8{make_float4(f[0], f[1], f[2], f[3]), make_float4(f[4], f[5], f[6], f[7])};
+  }
+  static __device__ __forceinline__ void store8(float* p, const V8& v) {
+    reinterpret_cast<float4*>(p)[0] = v.a;
+    reinterpret_cast<float4*>(p)[1] = v.b;
+  }
+  static __device__ __forceinline__ void store_n(float* p, const V8& v, int n) {
+    const float e[8] = {v.a.x, v.a.y, v.a.z, v.a.w, v.b.x, v.b.y, v.b.z, v.b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < n) p[j] = e[j];
+  }
+  static __device__ __forceinline__ float load1(const float* p) { return *p; }
+  static __device__ __forceinline__ void store1(float* p, float f) { *p = f; }
+};
+
+// softplus(x) * log2(e) = log2(1 + 2^(x*log2 e)), evaluated as
+// max(x,0)*log2e + log2(1 + e), e = 2^(-|x| log2e); the rounding error of
+// w = 1 + e is added back to first order so small e keeps full relative
+// accuracy (log2(1+e) ~ log2(w) + (e - (w-1)) * log2e).
+__device__ __forceinline__ float softplus_log2e(float x) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);
+  const float w = 1.0f + e;
+  const float r = e - (w - 1.0f);
+  const float l = fmaf(r, kLog2e, __builtin_amdgcn_logf(w));
+  return fmaf(fmaxf(x, 0.0f), kLog2e, l);
+}
+
+// z * sigmoid(z) = z / (1 + 2^(-z log2e))
+__device__ __forceinline__ float silu(float z) {
+  constexpr float kLog2e = 1.4426950408889634f;
+  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// Barrier for LDS producer/consumer hand-off only: orders LDS accesses, does
+// not wait for outstanding global loads or stores.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+}  // namespace mscan

@@ -1,0 +1,112 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mamba_scan.h declares, and rejects invalid arguments on the host
+(each call below fails validation, so no HIP call and no kernel is made;
+the pointers are fake, aligned or deliberately misaligned addresses)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_55_amd as mscan
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mamba_scan.h")
+
+OK, ENULL, ESHAPE, EDTYPE, EALIGN, EUNSUP, EWS, EHIP = range(8)
+P = 0x10000          # a fake, 256-byte aligned device address (never dereferenced)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return mscan.load_library()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mamba_scan_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(mscan.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the shared object's dynamic symbol table agrees
+    out = os.popen(f"nm -D --defined-only {mscan.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings(lib):
+    assert mscan.abi_version() == 1
+    for code in range(8):
+        s = mscan.status_str(code)
+        assert isinstance(s, str) and s
+    assert mscan.status_str(99) == "unknown status"
+
+
+def fwd(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None, fs=None, y=P,
+        batch=2, dim=64, dstate=16, seqlen=128, io=1, sp=1, nchunks=0, npw=0, ws=None, wsb=0):
+    return lib.mamba_scan_fwd_ex(u, delta, A_log, B, C, D, z, bias, h0, fs, y, batch, dim, dstate, seqlen, io, sp,
+                                 nchunks, npw, ws, wsb, None)
+
+
+def test_fwd_validation_errors(lib):
+    assert fwd(lib, u=None) == ENULL
+    assert fwd(lib, y=None) == ENULL
+    assert fwd(lib, A_log=None) == ENULL
+    assert fwd(lib, io=7) == EDTYPE
+    assert fwd(lib, batch=0) == ESHAPE
+    assert fwd(lib, dim=-1) == ESHAPE
+    assert fwd(lib, dstate=0) == ESHAPE
+    assert fwd(lib, seqlen=-1) == ESHAPE
+    assert fwd(lib, dstate=17) == EUNSUP
+    assert fwd(lib, batch=1 << 40, dim=1 << 30) == ESHAPE       # size overflow
+    assert fwd(lib, u=P + 1) == EALIGN                         # bf16 needs 2-byte alignment
+    assert fwd(lib, io=0, z=P + 2) == EALIGN                   # fp32 io needs 4-byte alignment
+    assert fwd(lib, D=P + 2) == EALIGN
+    assert fwd(lib, nchunks=-1) == EUNSUP
+    assert fwd(lib, npw=3) == EUNSUP
+    assert fwd(lib, ws=None, wsb=0) == EWS                     # workspace required for seqlen > 0
+    need = lib.mamba_scan_fwd_workspace_size(2, 64, 16, 128, 1)
+    assert need > 0
+    assert fwd(lib, ws=P, wsb=need - 1) == EWS
+    assert fwd(lib, ws=P + 16, wsb=need) == EWS                # not 256-byte aligned
+
+
+def test_workspace_size(lib):
+    bad = ctypes.c_size_t(-1).value
+    assert lib.mamba_scan_fwd_workspace_size(2, 64, 16, 0, 1) == 0
+    assert lib.mamba_scan_fwd_workspace_size(0, 64, 16, 10, 1) == bad
+    assert lib.mamba_scan_fwd_workspace_size(1, 64, 17, 10, 1) == bad
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 10, 1, 0, 3) == bad
+    # packed fp32 B/C: batch * padded L * padded N * 2 * 4 bytes (tile 64 tokens, N padded to 16)
+    assert lib.mamba_scan_fwd_workspace_size(4, 4096, 16, 8192, 1) == 4 * 8192 * 16 * 8
+    # a chunked plan also carries (h_end, sum Delta) per chunk
+    one = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 1, 4)
+    four = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 4, 4)
+    assert four > one
+
+
+def step(lib, state=P, x=P, dt=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, sp=1, y=P, batch=2, dim=64,
+         dstate=16, io=1):
+    return lib.mamba_scan_step(state, x, dt, A_log, B, C, D, z, bias, sp, y, batch, dim, dstate, io, None)
+
+
+def test_step_validation_errors(lib):
+    assert step(lib, state=None) == ENULL
+    assert step(lib, y=None) == ENULL
+    assert step(lib, io=2) == EDTYPE
+    assert step(lib, batch=0) == ESHAPE
+    assert step(lib, dstate=20) == EUNSUP
+    assert step(lib, state=P + 2) == EALIGN
+    assert step(lib, x=P + 1) == EALIGN
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    u = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        mscan.scan_fwd(u, u, torch.zeros(4, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
