@@ -72,6 +72,67 @@ def host_cores() -> int:
         return os.cpu_count() or 1
 
 
+def bench_step(args, c) -> int:
+    """Decode-step workload: `steps` chained single-token updates of a (batch, dim, N)
+    fp32 state, fresh seeded inputs per step (a pool of 64 distinct steps, resident)."""
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import step_initial, step_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    init = step_initial(c)
+    pool = 64
+    ins = [step_inputs(c, k) for k in range(pool)]
+    x = torch.stack([i["x"] for i in ins]).to(dev)
+    dt = torch.stack([i["dt"] for i in ins]).to(dev)
+    z = torch.stack([i["z"] for i in ins]).to(dev)
+    Bm = torch.stack([i["B"] for i in ins]).to(dev)
+    Cm = torch.stack([i["C"] for i in ins]).to(dev)
+    st = init["state"].to(dev)
+    A, D, bias = init["A_log"].to(dev), init["D"].to(dev), init["dt_bias"].to(dev)
+    y = torch.empty((c.batch, c.dim), dtype=x.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(k):
+        j = k % pool
+        mscan.scan_step(st, x[j], dt[j], A, Bm[j], Cm[j], D=D, z=z[j], dt_bias=bias, out=y, stream=stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    dev_ms = e0.elapsed_time(e1) / args.steps
+    bd = c.batch * c.dim
+    alg = c.algorithmic_bytes()
+    out = {
+        "metric": "selective-scan decode step throughput (state updates per second)",
+        "value": round(bd / (dev_ms * 1e-3) / 1e9, 3),
+        "unit": "G(batch*channel) updates/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "device_ms_per_step": round(dev_ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{c.name}: batch {c.batch}, d_inner {c.dim}, d_state {c.dstate}, fp32 state, "
+                               f"{c.io} io, gated, chained steps", "batch": c.batch, "d_inner": c.dim,
+                   "d_state": c.dstate},
+        "roofline": {"bound": "hbm", "achieved": round(alg / (dev_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(alg / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,6 +143,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -96,9 +159,20 @@ def main() -> int:
     import selective_state_space_55_amd as mscan
     from workloads import CONFIGS, forward_inputs, max_rel_err
 
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 3}))
+        return 0
+
     c = CONFIGS[args.config]
-    if c.kind != "fwd":
-        raise SystemExit("bench.py times the forward scan (configs 0-3)")
+    if c.kind == "step":
+        return bench_step(args, c)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

@@ -87,8 +87,11 @@ typedef enum {
  *   workspace    device scratch of at least mamba_scan_fwd_workspace_size(...) bytes,
  *                256-byte aligned; its contents on entry are ignored and on exit undefined
  *
- * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, seqlen >= 0.  seqlen == 0
- * writes no y and sets final_state to initial_state (or zeros).
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, seqlen >= 0, and
+ * 64 * (seqlen + 8) * sizeof(io element) < 2^31 (seqlen < 4,194,296 for
+ * bf16, 8,388,600 for fp32; larger returns MAMBA_SCAN_ERR_UNSUPPORTED).  seqlen == 0
+ * writes no y and sets final_state to initial_state (or zeros); the tensors
+ * with a seqlen dimension (u, delta, B, C, z, y) are then empty and may be NULL.
  */
 int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const float* initial_state,

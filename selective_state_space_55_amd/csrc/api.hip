@@ -28,6 +28,9 @@ int check_fwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, 
   int st = check_common(batch, dim, dstate, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
   if (seqlen < 0) return MAMBA_SCAN_ERR_SHAPE;
+  // a workgroup addresses 64 rows of one tensor with 32-bit byte offsets
+  const int64_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  if (seqlen > 0 && 64 * (seqlen + 8) * esz >= ((int64_t)1 << 31)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
   // (batch*dim*(seqlen+64)*4 bytes must be representable)
   if (!mul_ok(batch * dim, seqlen + 64, &t) || !mul_ok(t, 16, &t)) return MAMBA_SCAN_ERR_SHAPE;
@@ -73,7 +76,9 @@ int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, cons
                       size_t workspace_bytes, void* stream) {
   int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
-  if (!u || !delta || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
+  // tensors with a seqlen dimension are zero-sized when seqlen == 0 and may then be NULL
+  if (!A_log) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
   const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
   const void* io_ptrs[] = {u, delta, B, C, z, y};
   for (const void* p : io_ptrs)

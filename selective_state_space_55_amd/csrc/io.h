@@ -20,6 +20,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// Raw buffer descriptor over [base, base + bytes): loads past the end return
+// zero (hardware range check).  Third dword 0x00020000: 32-bit data format,
+// the value used for the gfx9 family.
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const T* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, 0x00020000);
+}
+
 template <typename IoT>
 struct Io;
 
@@ -57,11 +65,24 @@ struct Io<uint16_t> {
     return v;
   }
   static __device__ __forceinline__ void store8(uint16_t* p, const V8& v) { *reinterpret_cast<uint4*>(p) = v.w; }
+  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v.w), r,
+                                           off, 0, 0);
+  }
   static __device__ __forceinline__ void store_n(uint16_t* p, const V8& v, int n) {
     const uint32_t w[4] = {v.w.x, v.w.y, v.w.z, v.w.w};
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (j < n) p[j] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+  }
+  // 8 elements at byte offset off: one 16-byte load when rows are 16-byte
+  // aligned, else 8 element loads; bytes past the descriptor read as zero.
+  static __device__ __forceinline__ V8 buf_load8(__amdgpu_buffer_rsrc_t r, int off, int vec) {
+    if (vec) return V8{__builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0))};
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * j, 0, 0);
+    return V8{make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16))};
   }
   static __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
   static __device__ __forceinline__ void store1(uint16_t* p, float f) {
@@ -91,6 +112,11 @@ struct Io<float> {
   static __device__ __forceinline__ V8 from_f32(const float (&f)[8]) {
     return V8{make_float4(f[0], f[1], f[2], f[3]), make_float4(f[4], f[5], f[6], f[7])};
   }
+  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.a), r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.b), r, off + 16, 0, 0);
+  }
   static __device__ __forceinline__ void store8(float* p, const V8& v) {
     reinterpret_cast<float4*>(p)[0] = v.a;
     reinterpret_cast<float4*>(p)[1] = v.b;
@@ -100,6 +126,15 @@ struct Io<float> {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (j < n) p[j] = e[j];
+  }
+  static __device__ __forceinline__ V8 buf_load8(__amdgpu_buffer_rsrc_t r, int off, int vec) {
+    if (vec)
+      return V8{__builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0)),
+                __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0))};
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * j, 0, 0));
+    return V8{make_float4(e[0], e[1], e[2], e[3]), make_float4(e[4], e[5], e[6], e[7])};
   }
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
   static __device__ __forceinline__ void store1(float* p, float f) { *p = f; }
@@ -123,6 +158,40 @@ __device__ __forceinline__ float silu(float z) {
   constexpr float kLog2e = 1.4426950408889634f;
   const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
   return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Calls f(IntC<0>{}) .. f(IntC<N-1>{}) (compile-time loop index).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+// a * b and c + a * b where a is read from lane SRC of the same 16-lane row
+// (DPP row_newbcast on the first source): a wave-wide broadcast of one of 16
+// per-row values, folded into the arithmetic instruction.  The DPP source must
+// not be written by a VALU instruction in the two preceding instructions; the
+// callers pass registers loaded from LDS only.
+template <int SRC>
+__device__ __forceinline__ float dpp_bcast_mul(float a, float b) {
+  static_assert(SRC >= 0 && SRC < 16, "row lane");
+  float r;
+  asm("v_mul_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "=v"(r) : "v"(a), "v"(b), "n"(SRC));
+  return r;
+}
+
+template <int SRC>
+__device__ __forceinline__ float dpp_bcast_fmac(float c, float a, float b) {
+  static_assert(SRC >= 0 && SRC < 16, "row lane");
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(c) : "v"(a), "v"(b), "n"(SRC));
+  return c;
 }
 
 // Barrier for LDS producer/consumer hand-off only: orders LDS accesses, does

@@ -12,14 +12,15 @@
 // Mapping.  A workgroup owns 64 channels of one batch row (one channel per
 // lane) and NSPLIT waves; wave w holds states [w*NPW, (w+1)*NPW) of all 64
 // channels in VGPRs and scans them sequentially in time.  Per tile of T tokens:
-//   A. all threads load delta/u (and z) rows with 16-byte coalesced loads,
-//      compute Delta*log2e = softplus(delta+bias)*log2e once per token-channel,
-//      and stage Delta and u as fp32 in LDS (double-buffered; the next tile's
-//      global loads are issued before the scan so they overlap it);
-//   B. each wave scans the tile: Delta and u come from LDS, B and C -- shared
-//      by all channels of the batch row -- come from a packed fp32 copy through
-//      scalar loads (SGPR operands, no VGPR or LDS traffic); each wave leaves a
-//      partial readout over its states in LDS;
+//   A. all threads load the tile's delta/u/z rows and its B/C rows with
+//      16-byte coalesced loads (issued one tile ahead, so they overlap the
+//      previous tile's scan), compute Delta*log2e = softplus(delta+bias)*log2e
+//      once per token-channel, and stage Delta, u (per channel) and B, C
+//      (shared by the 64 channels) as fp32 in double-buffered LDS;
+//   B. each wave scans the tile; per group of 4 tokens it reads Delta/u of its
+//      lane's channel and the group's B/C values for its states (a broadcast
+//      LDS read), one group ahead; each wave leaves a partial readout over its
+//      states in LDS;
 //   C. all threads sum the NSPLIT partials, add D u, apply the SiLU gate and
 //      store y with 16-byte stores.
 // Inner step per (token, state): Abar = 2^(Delta*log2e * A); s = B u / A;
@@ -42,14 +43,14 @@ namespace mscan {
 namespace {
 
 constexpr int kCh = 64;   // channels per workgroup, one per lane
-typedef __attribute__((address_space(4))) const float kfloat;   // constant (scalar-loadable) memory
 constexpr int kPad = 4;   // LDS row padding in floats
 
 struct KArgs {
   const void* u;
   const void* delta;
   const float* A_log;
-  const float* bc;     // packed fp32 B/C: [batch][lp/4][np][8] = B[t0..t0+3], C[t0..t0+3]
+  const void* B;
+  const void* C;
   const float* D;
   const void* z;
   const float* bias;
@@ -58,7 +59,7 @@ struct KArgs {
   void* y;
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
-  int64_t dim, seqlen, lp, chunk_len, nchunks, chgroups, nwork;
+  int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, softplus, gated, vec_ok;
 };
 
@@ -70,21 +71,39 @@ __device__ __forceinline__ int64_t work_id(int64_t bid, int64_t nwork) {
   return (bid & 7) * (nwork >> 3) + (bid >> 3);
 }
 
+template <int NPW, int NSPLIT, int T, bool kAgg>
+struct Lds {
+  static constexpr int kRow = T + kPad;
+  static constexpr int kNp = NPW * NSPLIT;
+  static constexpr int kDU = 2 * kCh * kRow;            // one of Delta/u, double-buffered
+  static constexpr int kBC = 2 * (T / 4) * kNp * 8;     // B/C groups, double-buffered
+  static constexpr int kPar = 2 * kCh;                  // bias, D
+  static constexpr int kY = kAgg ? 0 : NSPLIT * kCh * kRow;
+  static constexpr int kFloats = 2 * kDU + kBC + kPar + kY;
+};
+
 template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
 __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V8 = typename IO::V8;
+  using L = Lds<NPW, NSPLIT, T, kAgg>;
   constexpr int NT = NSPLIT * 64;       // threads
-  constexpr int kRow = T + kPad;        // LDS row stride (floats)
-  constexpr int kChunks8 = kCh * T / 8; // 8-token pieces per tile
-  constexpr int CPT = (kChunks8 + NT - 1) / NT;
-  constexpr bool kAllBusy = (kChunks8 % NT) == 0;   // else the last round leaves some threads idle
+  constexpr int kRow = L::kRow;
+  constexpr int NP = L::kNp;            // padded state count (== a.np)
+  constexpr int kG = T / 4;             // 4-token groups per tile
+  constexpr int kPieces = kCh * T / 8;  // 8-token pieces of Delta/u/z per tile
+  constexpr int CPT = (kPieces + NT - 1) / NT;
+  constexpr bool kAllBusy = (kPieces % NT) == 0;
+  constexpr int kBCPieces = NP * (T / 8);       // (state, 8-token) pieces of B and C per tile
+  constexpr int BPT = (kBCPieces + NT - 1) / NT;
+  constexpr bool kBCAllBusy = (kBCPieces % NT) == 0;
 
   extern __shared__ float smem[];
   float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
-  float* ubuf = dbuf + 2 * kCh * kRow;     // [2][64][kRow]  u
-  float* par = ubuf + 2 * kCh * kRow;      // [2][64]        bias, D
-  float* ypart = par + 2 * kCh;            // [NSPLIT][64][kRow] partial readouts (full pass only)
+  float* ubuf = dbuf + L::kDU;             // [2][64][kRow]  u
+  float* bcs = ubuf + L::kDU;              // [2][kG][NP][4 tokens][B, C]
+  float* par = bcs + L::kBC;               // [2][64]        bias, D
+  float* ypart = par + L::kPar;            // [NSPLIT][64][kRow] partial readouts (output pass only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -99,13 +118,13 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   const int64_t d0 = cg * kCh;
   const int64_t t_begin = k * a.chunk_len;
   const int64_t t_end = min(t_begin + a.chunk_len, a.seqlen);   // valid tokens of this chunk
-  const int64_t t_stop = min(t_begin + a.chunk_len, a.lp);      // tile-padded end
 
   const IoT* __restrict__ gu = static_cast<const IoT*>(a.u);
   const IoT* __restrict__ gd = static_cast<const IoT*>(a.delta);
   const IoT* __restrict__ gz = static_cast<const IoT*>(a.z);
+  const IoT* __restrict__ gB = static_cast<const IoT*>(a.B);
+  const IoT* __restrict__ gC = static_cast<const IoT*>(a.C);
   IoT* __restrict__ gy = static_cast<IoT*>(a.y);
-  const float* __restrict__ bc = a.bc;
 
   if (tid < kCh) {
     const int64_t dd = d0 + tid;
@@ -138,32 +157,45 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   float dsum_acc = 0.0f;
 
   // ---- global -> register prefetch of one tile ----
+  // Buffer loads through per-workgroup descriptors: each descriptor covers
+  // exactly this workgroup's valid rows, so rows past dim (and bytes past the
+  // tensor's end) read as zero without a branch.  Tokens past the chunk end
+  // read neighbouring data and are zeroed when staged.  Branch-free loads let
+  // the next tile's data stay in flight during the scan.
+  constexpr int kEsz = (int)sizeof(IoT);
+  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
+  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
+  const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
+  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(a.gated ? gz + row0 : gu + row0, a.gated ? nrec_ch : 0);
+  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
+  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
+  const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, nrec_ch);
   constexpr int CZ = kAgg ? 1 : CPT;   // z is staged only by the output pass
-  V8 pd[CPT], pu[CPT], pz[CZ], zc[CZ];
+  V8 pd[CPT], pu[CPT], pz[CZ], zc[CZ], pb[BPT], pc[BPT];
+  float ureg[CZ][8];   // u of this thread's pieces, kept from staging to the epilogue
   auto prefetch = [&](int64_t tile) {
+    const int64_t trel = tile - t_begin;
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
-      const int e = tid + c * NT;
+      const int e = min(tid + c * NT, kPieces - 1);   // idle threads re-load a valid piece
       const int ch = e / (T / 8);
       const int c8 = e % (T / 8);
-      const int64_t t0 = tile + c8 * 8;
-      const int64_t dd = d0 + ch;
-      int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-      if (dd >= a.dim || (!kAllBusy && e >= kChunks8)) nv = 0;
-      const int64_t off = (b * a.dim + dd) * a.seqlen + t0;
-      if (nv == 8 && a.vec_ok) {
-        pd[c] = IO::load8(gd + off);
-        pu[c] = IO::load8(gu + off);
-        if constexpr (!kAgg) pz[c] = a.gated ? IO::load8(gz + off) : IO::zero();
-      } else if (nv > 0) {
-        pd[c] = IO::load_n(gd + off, nv);
-        pu[c] = IO::load_n(gu + off, nv);
-        if constexpr (!kAgg) pz[c] = a.gated ? IO::load_n(gz + off, nv) : IO::zero();
-      } else {
-        pd[c] = IO::zero();
-        pu[c] = IO::zero();
-        if constexpr (!kAgg) pz[c] = IO::zero();
-      }
+      const int off = (int)(((int64_t)ch * a.seqlen + t_begin + trel + c8 * 8) * kEsz);
+      pd[c] = IO::buf_load8(rs_d, off, a.vec_ok);
+      pu[c] = IO::buf_load8(rs_u, off, a.vec_ok);
+      if constexpr (!kAgg) pz[c] = IO::buf_load8(rs_z, off, a.vec_ok);
+    }
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      const int e = min(tid + c * NT, kBCPieces - 1);
+      const int n = e % NP;
+      const int c8 = (e / NP) % (T / 8);
+      const int off = (int)(((int64_t)n * a.seqlen + t_begin + trel + c8 * 8) * kEsz);
+      pb[c] = IO::buf_load8(rs_B, off, a.vec_ok);
+      pc[c] = IO::buf_load8(rs_C, off, a.vec_ok);
     }
   };
 
@@ -171,102 +203,156 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   prefetch(tile);
   __syncthreads();   // par[] visible
 
-  for (int it = 0; tile < t_stop; ++it, tile += T) {
+  for (int it = 0; tile < t_end; ++it, tile += T) {
     const int cur = it & 1;
     float* dcur = dbuf + cur * kCh * kRow;
     float* ucur = ubuf + cur * kCh * kRow;
+    float* bccur = bcs + cur * kG * NP * 8;
 
-    // ---- A: stage Delta*log2e and u in LDS ----
+    // ---- A: stage Delta*log2e, u and B/C in LDS ----
+    const bool tail = tile + T > t_end;   // uniform: only the last tile of a chunk can be partial
+    // The softplus switch is hoisted out of the element loops so each piece's
+    // 8 independent softplus chains can be interleaved.
+    auto stage = [&](auto sp_c) {
+      constexpr bool kSp = decltype(sp_c)::value;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = tid + c * NT;
-      if (!kAllBusy && e >= kChunks8) break;
-      const int ch = e / (T / 8);
-      const int c8 = e % (T / 8);
-      const int64_t t0 = tile + c8 * 8;
-      const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-      float fd[8], fu[8];
-      IO::to_f32(pd[c], fd);
-      IO::to_f32(pu[c], fu);
-      const float bi = par[ch];
+      for (int c = 0; c < CPT; ++c) {
+        const int e = tid + c * NT;
+        if (!kAllBusy && e >= kPieces) break;
+        const int ch = e / (T / 8);
+        const int c8 = e % (T / 8);
+        float fd[8], fu[8];
+        IO::to_f32(pd[c], fd);
+        IO::to_f32(pu[c], fu);
+        const float bi = par[ch];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = fd[j] + bi;
-        float dl = a.softplus ? softplus_log2e(x) : x * 1.4426950408889634f;
-        fd[j] = (j < nv) ? dl : 0.0f;   // padded tokens: Delta = 0, u = 0 leave h unchanged
+        for (int j = 0; j < 8; ++j) {
+          const float x = fd[j] + bi;
+          if constexpr (kSp)
+            fd[j] = softplus_log2e(x);
+          else
+            fd[j] = x * 1.4426950408889634f;
+        }
+        if (tail) {
+          // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
+          const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            fd[j] = (j < nv) ? fd[j] : 0.0f;
+            fu[j] = (j < nv) ? fu[j] : 0.0f;
+          }
+        }
+        float* dp = dcur + ch * kRow + c8 * 8;
+        float* up = ucur + ch * kRow + c8 * 8;
+        reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
+        reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
+        reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
+        reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+        if constexpr (!kAgg) {
+          zc[c] = pz[c];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) ureg[c][j] = fu[j];
+        }
       }
-      float* dp = dcur + ch * kRow + c8 * 8;
-      float* up = ucur + ch * kRow + c8 * 8;
-      reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-      reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-      reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-      reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
-      if constexpr (!kAgg) zc[c] = pz[c];
+    };
+    if (a.softplus)
+      stage(IntC<1>{});
+    else
+      stage(IntC<0>{});
+#pragma unroll
+    for (int c = 0; c < BPT; ++c) {
+      const int e = tid + c * NT;
+      if (!kBCAllBusy && e >= kBCPieces) break;
+      const int n = e % NP;
+      const int c8 = (e / NP) % (T / 8);
+      float fb[8], fc[8];
+      IO::to_f32(pb[c], fb);
+      IO::to_f32(pc[c], fc);
+      if (tail) {
+        const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          fb[j] = (j < nv) ? fb[j] : 0.0f;
+          fc[j] = (j < nv) ? fc[j] : 0.0f;
+        }
+      }
+      // tokens c8*8 .. +3 are group 2*c8, tokens +4 .. +7 group 2*c8+1;
+      // within a (group, state) the 8 floats are B0 C0 B1 C1 B2 C2 B3 C3
+      float2* p0 = reinterpret_cast<float2*>(bccur + ((2 * c8) * NP + n) * 8);
+      float2* p1 = reinterpret_cast<float2*>(bccur + ((2 * c8 + 1) * NP + n) * 8);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        p0[kk] = make_float2(fb[kk], fc[kk]);
+        p1[kk] = make_float2(fb[4 + kk], fc[4 + kk]);
+      }
     }
-    if (tile + T < t_stop) prefetch(tile + T);
+    if (tile + T < t_end) prefetch(tile + T);
     lds_barrier();
 
     // ---- B: scan the tile ----
-    // Software pipeline over groups of 4 tokens: the first token of group g
-    // consumes g's operands (scalar loads return out of order, so that use
-    // waits for every outstanding LDS/scalar load), then group g+1's Delta/u
-    // (LDS) and B/C (scalar) loads are issued, then the other three tokens run
-    // while they are in flight.  Fully unrolled so both SGPR buffers are fixed
-    // registers.
+    // B/C operands: per group of 4 tokens each lane loads one (B, C) pair --
+    // lane i of each 16-lane row holds state i/4 (of this wave's NPW states)
+    // at token i%4 -- and every use takes its value through a DPP
+    // row_newbcast source operand, so the 64-lane broadcast costs no LDS
+    // bandwidth and no extra instruction.  Software pipeline over groups:
+    // token 0 of group g consumes g's operands, then group g+1's Delta/u and
+    // B/C pairs are requested from LDS, then tokens 1..3 of group g run while
+    // those reads are in flight.  Fully unrolled so the two operand buffers
+    // are fixed registers written only by LDS loads.
     {
       const float* drow = dcur + lane * kRow;
       const float* urow = ucur + lane * kRow;
       float* yrow = ypart + (w * kCh + lane) * kRow;
-      // B/C are read-only for this kernel (written by the packing kernel before
-      // it): read them through the constant address space so the uniform
-      // loads become scalar loads into SGPRs.
-      const kfloat* bcp =
-          (const kfloat*)(bc + ((b * (a.lp >> 2) + (tile >> 2)) * a.np + w * NPW) * 8);
-      const int64_t gstride = (int64_t)a.np * 8;
+      const int sel = lane & 15;
+      const float* bcl = bccur + (w * NPW + ((sel >> 2) % NPW)) * 8 + 2 * (sel & 3);
       float4 dv = *reinterpret_cast<const float4*>(drow);
       float4 uv = *reinterpret_cast<const float4*>(urow);
-      float bcv[NPW * 8];
-#pragma unroll
-      for (int i = 0; i < NPW * 8; ++i) bcv[i] = bcp[i];
+      float2 bcv = *reinterpret_cast<const float2*>(bcl);
 
-      auto token = [&](float dl, float uu, const float* bq, int kk) -> float {
+      auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
+        constexpr int kk = decltype(kk_c)::value;
         float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < NPW; ++j) {
+        static_for<NPW>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
           const float av = __builtin_amdgcn_exp2f(dl * A[j]);
-          const float sv = bq[j * 8 + kk] * (uu * iA[j]);
-          h[j] = fmaf(av, h[j] + sv, -sv);
-          if (!kAgg) acc = fmaf(bq[j * 8 + 4 + kk], h[j], acc);
-        }
+          const float v = uu * iA[j];
+          const float sv = dpp_bcast_mul<src>(bq.x, v);          // B * u / A
+          const float hs = dpp_bcast_fmac<src>(h[j], bq.x, v);   // h + B * u / A
+          h[j] = fmaf(av, hs, -sv);
+          if constexpr (!kAgg) {
+            if constexpr (j == 0)
+              acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
+            else
+              acc = dpp_bcast_fmac<src>(acc, bq.y, h[j]);
+          }
+        });
         return acc;
       };
 
 #pragma unroll
-      for (int g = 0; g < T / 4; ++g) {
-        const float y0 = token(dv.x, uv.x, bcv, 0);
+      for (int g = 0; g < kG; ++g) {
+        const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
         __builtin_amdgcn_sched_barrier(0);
         float4 dn = dv, un = uv;
-        float bcn[NPW * 8];
-        if (g + 1 < T / 4) {
+        float2 bcn = bcv;
+        if (g + 1 < kG) {
           dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
           un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
-          const kfloat* q = bcp + (g + 1) * gstride;
-#pragma unroll
-          for (int i = 0; i < NPW * 8; ++i) bcn[i] = q[i];
+          bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
         }
         __builtin_amdgcn_sched_barrier(0);
-        const float y1 = token(dv.y, uv.y, bcv, 1);
-        const float y2 = token(dv.z, uv.z, bcv, 2);
-        const float y3 = token(dv.w, uv.w, bcv, 3);
+        const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
+        const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
+        const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
         if (!kAgg)
           *reinterpret_cast<float4*>(yrow + 4 * g) = make_float4(y0, y1, y2, y3);
         else
           dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
-        if (g + 1 < T / 4) {
+        if (g + 1 < kG) {
           dv = dn;
           uv = un;
-#pragma unroll
-          for (int i = 0; i < NPW * 8; ++i) bcv[i] = bcn[i];
+          bcv = bcn;
         }
       }
     }
@@ -274,51 +360,53 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
     if (!kAgg) {
       lds_barrier();
       // ---- C: combine partial readouts, D skip, gate, store ----
+      // all partial-readout reads are issued before any use
+      float4 yp[CZ][NSPLIT][2];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int e = min(tid + c * NT, kPieces - 1);
+        const int ch = e / (T / 8);
+        const int c8 = e % (T / 8);
+#pragma unroll
+        for (int s2 = 0; s2 < NSPLIT; ++s2) {
+          const float4* ps = reinterpret_cast<const float4*>(ypart + (s2 * kCh + ch) * kRow + c8 * 8);
+          yp[kAgg ? 0 : c][s2][0] = ps[0];
+          yp[kAgg ? 0 : c][s2][1] = ps[1];
+        }
+      }
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
         const int e = tid + c * NT;
-        if (!kAllBusy && e >= kChunks8) break;
+        if (!kAllBusy && e >= kPieces) break;
         const int ch = e / (T / 8);
         const int c8 = e % (T / 8);
-        const int64_t t0 = tile + c8 * 8;
-        const int64_t dd = d0 + ch;
-        int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-        if (dd >= a.dim) nv = 0;
-        float yv[8];
-        {
-          const float* p0 = ypart + ch * kRow + c8 * 8;
-          const float4 lo = reinterpret_cast<const float4*>(p0)[0];
-          const float4 hi = reinterpret_cast<const float4*>(p0)[1];
-          yv[0] = lo.x; yv[1] = lo.y; yv[2] = lo.z; yv[3] = lo.w;
-          yv[4] = hi.x; yv[5] = hi.y; yv[6] = hi.z; yv[7] = hi.w;
-        }
+        const int cc = kAgg ? 0 : c;
+        float yv[8] = {yp[cc][0][0].x, yp[cc][0][0].y, yp[cc][0][0].z, yp[cc][0][0].w,
+                       yp[cc][0][1].x, yp[cc][0][1].y, yp[cc][0][1].z, yp[cc][0][1].w};
 #pragma unroll
         for (int s2 = 1; s2 < NSPLIT; ++s2) {
-          const float* ps = ypart + (s2 * kCh + ch) * kRow + c8 * 8;
-          const float4 lo = reinterpret_cast<const float4*>(ps)[0];
-          const float4 hi = reinterpret_cast<const float4*>(ps)[1];
-          yv[0] += lo.x; yv[1] += lo.y; yv[2] += lo.z; yv[3] += lo.w;
-          yv[4] += hi.x; yv[5] += hi.y; yv[6] += hi.z; yv[7] += hi.w;
+          yv[0] += yp[cc][s2][0].x; yv[1] += yp[cc][s2][0].y; yv[2] += yp[cc][s2][0].z; yv[3] += yp[cc][s2][0].w;
+          yv[4] += yp[cc][s2][1].x; yv[5] += yp[cc][s2][1].y; yv[6] += yp[cc][s2][1].z; yv[7] += yp[cc][s2][1].w;
         }
-        const float* up = ucur + ch * kRow + c8 * 8;
-        const float4 ulo = reinterpret_cast<const float4*>(up)[0];
-        const float4 uhi = reinterpret_cast<const float4*>(up)[1];
-        const float uu[8] = {ulo.x, ulo.y, ulo.z, ulo.w, uhi.x, uhi.y, uhi.z, uhi.w};
         const float Dd = par[kCh + ch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, uu[j], yv[j]);
+        for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, ureg[cc][j], yv[j]);
         if (a.gated) {
           float zf[8];
-          IO::to_f32(zc[kAgg ? 0 : c], zf);
+          IO::to_f32(zc[cc], zf);
 #pragma unroll
           for (int j = 0; j < 8; ++j) yv[j] *= silu(zf[j]);
         }
         const V8 out = IO::from_f32(yv);
-        const int64_t off = (b * a.dim + dd) * a.seqlen + t0;
-        if (nv == 8 && a.vec_ok)
-          IO::store8(gy + off, out);
-        else if (nv > 0)
-          IO::store_n(gy + off, out, nv);
+        if (!tail && a.vec_ok) {
+          // rows past dim fall outside the descriptor and are dropped
+          IO::buf_store8(rs_y, (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz), out);
+        } else {
+          const int64_t t0 = tile + c8 * 8;
+          int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
+          if (d0 + ch >= a.dim) nv = 0;
+          IO::store_n(gy + (b * a.dim + d0 + ch) * a.seqlen + t0, out, nv);
+        }
       }
     }
   }
@@ -342,33 +430,6 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
       if (w == 0) a.dsum[bd * a.nchunks + k] = dsum_acc;
     }
   }
-}
-
-// Packs B and C (io dtype, (batch, dstate, L)) into fp32 [batch][lp/4][np][8]
-// groups of four tokens, zero-padded beyond L and beyond dstate.
-template <typename IoT>
-__global__ __launch_bounds__(256) void pack_bc_kernel(const IoT* __restrict__ B, const IoT* __restrict__ C,
-                                                      float* __restrict__ bc, int64_t batch, int64_t dstate,
-                                                      int64_t seqlen, int64_t lp, int np) {
-  using IO = Io<IoT>;
-  const int64_t G = lp >> 2;
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // over (b, n, g), g fastest
-  if (i >= batch * np * G) return;
-  const int64_t g = i % G;
-  const int64_t n = (i / G) % np;
-  const int64_t b = i / (G * np);
-  float bv[4], cv[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int64_t t = g * 4 + kk;
-    const bool ok = n < dstate && t < seqlen;
-    const int64_t off = (b * dstate + n) * seqlen + t;
-    bv[kk] = ok ? IO::load1(B + off) : 0.0f;
-    cv[kk] = ok ? IO::load1(C + off) : 0.0f;
-  }
-  float4* dst = reinterpret_cast<float4*>(bc + ((b * G + g) * np + n) * 8);
-  dst[0] = make_float4(bv[0], bv[1], bv[2], bv[3]);
-  dst[1] = make_float4(cv[0], cv[1], cv[2], cv[3]);
 }
 
 // Folds the chunk aggregates in time order; leaves in carry[.., k, ..] the
@@ -405,15 +466,15 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename IoT, int NPW, int NSPLIT, int T>
 hipError_t launch_scan(const KArgs& k, bool agg, int64_t grid, hipStream_t s) {
-  constexpr int kRow = T + kPad;
-  const size_t lds = sizeof(float) * (4 * kCh * kRow + 2 * kCh + (agg ? 0 : NSPLIT * kCh * kRow));
   if (agg) {
     auto kern = scan_fwd_kernel<IoT, NPW, NSPLIT, T, true>;
+    const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, true>::kFloats;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
   } else {
     auto kern = scan_fwd_kernel<IoT, NPW, NSPLIT, T, false>;
+    const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, false>::kFloats;
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
@@ -450,27 +511,19 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     return hipSuccess;
   }
   char* ws = static_cast<char*>(a.workspace);
-  float* bc = reinterpret_cast<float*>(ws);
-  float* carry = p.nchunks > 1 ? reinterpret_cast<float*>(ws + align256(p.ws_bc)) : nullptr;
+  float* carry = p.nchunks > 1 ? reinterpret_cast<float*>(ws) : nullptr;
   float* dsum = p.nchunks > 1
-                    ? reinterpret_cast<float*>(ws + align256(p.ws_bc) +
-                                               align256(sizeof(float) * (size_t)(a.batch * a.dim * p.nchunks * p.np)))
+                    ? reinterpret_cast<float*>(ws + align256(sizeof(float) *
+                                                             (size_t)(a.batch * a.dim * p.nchunks * p.np)))
                     : nullptr;
-  {
-    const int64_t n = a.batch * p.np * (p.lp >> 2);
-    hipLaunchKernelGGL(pack_bc_kernel<IoT>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
-                       static_cast<const IoT*>(a.B), static_cast<const IoT*>(a.C), bc, a.batch, a.dstate, a.seqlen,
-                       p.lp, p.np);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
   const size_t esz = sizeof(IoT);
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a.u) | reinterpret_cast<uintptr_t>(a.delta) |
-                        reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z);
+                        reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z) |
+                        reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C);
   KArgs k{};
-  k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.bc = bc; k.D = a.D; k.z = a.z; k.bias = a.bias;
+  k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
-  k.dim = a.dim; k.seqlen = a.seqlen; k.lp = p.lp; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
+  k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.softplus = a.softplus; k.gated = a.z != nullptr;
   k.vec_ok = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
@@ -517,12 +570,12 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   const int64_t tiles_per = (tiles + nch - 1) / nch;
   p->chunk_len = std::max<int64_t>(1, tiles_per) * T;
   p->nchunks = tiles > 0 ? (tiles + tiles_per - 1) / tiles_per : 1;
-  p->ws_bc = sizeof(float) * (size_t)(batch * (p->lp / 4) * p->np * 8);
+  p->ws_bc = 0;
   p->ws_carry = 0;
   if (p->nchunks > 1)
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +
                   align256(sizeof(float) * (size_t)(batch * dim * p->nchunks));
-  p->ws_total = seqlen == 0 ? 0 : align256(p->ws_bc) + p->ws_carry;
+  p->ws_total = seqlen == 0 ? 0 : p->ws_carry;
   return true;
 }
 

@@ -54,6 +54,7 @@ def fwd(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None
 
 def test_fwd_validation_errors(lib):
     assert fwd(lib, u=None) == ENULL
+    assert fwd(lib, A_log=None, seqlen=0) == ENULL
     assert fwd(lib, y=None) == ENULL
     assert fwd(lib, A_log=None) == ENULL
     assert fwd(lib, io=7) == EDTYPE
@@ -62,17 +63,19 @@ def test_fwd_validation_errors(lib):
     assert fwd(lib, dstate=0) == ESHAPE
     assert fwd(lib, seqlen=-1) == ESHAPE
     assert fwd(lib, dstate=17) == EUNSUP
+    assert fwd(lib, seqlen=1 << 24) == EUNSUP                 # 64 rows x L x 2 B must fit 31 bits
     assert fwd(lib, batch=1 << 40, dim=1 << 30) == ESHAPE       # size overflow
     assert fwd(lib, u=P + 1) == EALIGN                         # bf16 needs 2-byte alignment
     assert fwd(lib, io=0, z=P + 2) == EALIGN                   # fp32 io needs 4-byte alignment
     assert fwd(lib, D=P + 2) == EALIGN
     assert fwd(lib, nchunks=-1) == EUNSUP
     assert fwd(lib, npw=3) == EUNSUP
-    assert fwd(lib, ws=None, wsb=0) == EWS                     # workspace required for seqlen > 0
-    need = lib.mamba_scan_fwd_workspace_size(2, 64, 16, 128, 1)
+    # a chunked launch needs workspace for the inter-chunk carry
+    need = lib.mamba_scan_fwd_workspace_size_ex(2, 64, 16, 1024, 1, 4, 0)
     assert need > 0
-    assert fwd(lib, ws=P, wsb=need - 1) == EWS
-    assert fwd(lib, ws=P + 16, wsb=need) == EWS                # not 256-byte aligned
+    assert fwd(lib, seqlen=1024, nchunks=4, ws=None, wsb=0) == EWS
+    assert fwd(lib, seqlen=1024, nchunks=4, ws=P, wsb=need - 1) == EWS
+    assert fwd(lib, seqlen=1024, nchunks=4, ws=P + 16, wsb=need) == EWS   # not 256-byte aligned
 
 
 def test_workspace_size(lib):
@@ -81,8 +84,8 @@ def test_workspace_size(lib):
     assert lib.mamba_scan_fwd_workspace_size(0, 64, 16, 10, 1) == bad
     assert lib.mamba_scan_fwd_workspace_size(1, 64, 17, 10, 1) == bad
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 10, 1, 0, 3) == bad
-    # packed fp32 B/C: batch * padded L * padded N * 2 * 4 bytes (tile 64 tokens, N padded to 16)
-    assert lib.mamba_scan_fwd_workspace_size(4, 4096, 16, 8192, 1) == 4 * 8192 * 16 * 8
+    # one sequential pass needs no workspace
+    assert lib.mamba_scan_fwd_workspace_size(4, 4096, 16, 8192, 1) == 0
     # a chunked plan also carries (h_end, sum Delta) per chunk
     one = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 1, 4)
     four = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 4, 4)
