@@ -65,9 +65,18 @@ struct Io<uint16_t> {
     return v;
   }
   static __device__ __forceinline__ void store8(uint16_t* p, const V8& v) { *reinterpret_cast<uint4*>(p) = v.w; }
-  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v) {
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v.w), r,
-                                           off, 0, 0);
+  // 8 elements at byte offset off; stores past the descriptor are dropped.
+  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v, bool vec) {
+    if (vec) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v.w),
+                                             r, off, 0, 0);
+      return;
+    }
+    const uint32_t w[4] = {v.w.x, v.w.y, v.w.z, v.w.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu)), r,
+                                            off + 2 * j, 0, 0);
   }
   static __device__ __forceinline__ void store_n(uint16_t* p, const V8& v, int n) {
     const uint32_t w[4] = {v.w.x, v.w.y, v.w.z, v.w.w};
@@ -112,10 +121,16 @@ struct Io<float> {
   static __device__ __forceinline__ V8 from_f32(const float (&f)[8]) {
     return V8{make_float4(f[0], f[1], f[2], f[3]), make_float4(f[4], f[5], f[6], f[7])};
   }
-  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v) {
+  static __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, const V8& v, bool vec) {
     typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.a), r, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.b), r, off + 16, 0, 0);
+    if (vec) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.a), r, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.b), r, off + 16, 0, 0);
+      return;
+    }
+    const float e[8] = {v.a.x, v.a.y, v.a.z, v.a.w, v.b.x, v.b.y, v.b.z, v.b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, e[j]), r, off + 4 * j, 0, 0);
   }
   static __device__ __forceinline__ void store8(float* p, const V8& v) {
     reinterpret_cast<float4*>(p)[0] = v.a;

@@ -11,18 +11,25 @@
 //
 // Mapping.  A workgroup owns 64 channels of one batch row (one channel per
 // lane) and NSPLIT waves; wave w holds states [w*NPW, (w+1)*NPW) of all 64
-// channels in VGPRs and scans them sequentially in time.  Per tile of T tokens:
-//   A. all threads load the tile's delta/u/z rows and its B/C rows with
-//      16-byte coalesced loads (issued one tile ahead, so they overlap the
-//      previous tile's scan), compute Delta*log2e = softplus(delta+bias)*log2e
-//      once per token-channel, and stage Delta, u (per channel) and B, C
-//      (shared by the 64 channels) as fp32 in double-buffered LDS;
-//   B. each wave scans the tile; per group of 4 tokens it reads Delta/u of its
-//      lane's channel and the group's B/C values for its states (a broadcast
-//      LDS read), one group ahead; each wave leaves a partial readout over its
-//      states in LDS;
-//   C. all threads sum the NSPLIT partials, add D u, apply the SiLU gate and
-//      store y with 16-byte stores.
+// channels in VGPRs and scans them sequentially in time, tile by tile (T
+// tokens).  Three stages touch every tile:
+//   stage    -- convert the tile's delta/u rows (16-byte buffer loads), compute
+//               Delta*log2e = softplus(delta+bias)*log2e once per token-channel,
+//               and put Delta, u and the tile's B/C values (shared by the 64
+//               channels) as fp32 in LDS;
+//   scan     -- per group of 4 tokens read Delta/u of the lane's channel and
+//               one (B, C) pair per lane from LDS; every B/C use takes its value
+//               through a DPP row_newbcast operand (lane 4j+t of each 16-lane
+//               row holds state j, token t); leave a partial readout over the
+//               wave's states in LDS;
+//   epilogue -- sum the NSPLIT partials, add D u, apply the SiLU gate, store y.
+// With one wave per SIMD nothing hides a wave's own stalls, so the stages are
+// software-pipelined across tiles inside one instruction stream: while a wave
+// scans tile k it also finishes tile k-1's epilogue and stages tile k+1, and
+// the global loads of tile k+2 are in flight.  That work sits inside the
+// scan's group loop, so the compiler interleaves it with the recurrence.  LDS
+// holds two copies of the staged inputs and of the partial readouts; one
+// barrier per tile.
 // Inner step per (token, state): Abar = 2^(Delta*log2e * A); s = B u / A;
 // h = Abar (h + s) - s  (= Abar h + (Abar - 1)/A B u);  y += C h.
 //
@@ -60,7 +67,7 @@ struct KArgs {
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
-  int dstate, np, softplus, gated, vec_ok;
+  int dstate, np, softplus, gated;
 };
 
 // Work id with XCD-aware placement: the hardware deals consecutive workgroup
@@ -75,14 +82,14 @@ template <int NPW, int NSPLIT, int T, bool kAgg>
 struct Lds {
   static constexpr int kRow = T + kPad;
   static constexpr int kNp = NPW * NSPLIT;
-  static constexpr int kDU = 2 * kCh * kRow;            // one of Delta/u, double-buffered
-  static constexpr int kBC = 2 * (T / 4) * kNp * 8;     // B/C groups, double-buffered
+  static constexpr int kDU = 2 * kCh * kRow;            // Delta or u, two tiles
+  static constexpr int kBC = 2 * (T / 4) * kNp * 8;     // B/C pairs, two tiles
   static constexpr int kPar = 2 * kCh;                  // bias, D
-  static constexpr int kY = kAgg ? 0 : NSPLIT * kCh * kRow;
+  static constexpr int kY = kAgg ? 0 : 2 * NSPLIT * kCh * kRow;   // partial readouts, two tiles
   static constexpr int kFloats = 2 * kDU + kBC + kPar + kY;
 };
 
-template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
+template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg, bool kVec, bool kSp>
 __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V8 = typename IO::V8;
@@ -97,13 +104,17 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   constexpr int kBCPieces = NP * (T / 8);       // (state, 8-token) pieces of B and C per tile
   constexpr int BPT = (kBCPieces + NT - 1) / NT;
   constexpr bool kBCAllBusy = (kBCPieces % NT) == 0;
+  constexpr int CK = kAgg ? 1 : CPT;    // u/z kept from staging to the epilogue (output pass only)
+  constexpr int kEsz = (int)sizeof(IoT);
+  constexpr float kLog2e = 1.4426950408889634f;
+  static_assert(kG >= 4, "the pipeline places work in groups 0..3");
 
   extern __shared__ float smem[];
   float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
   float* ubuf = dbuf + L::kDU;             // [2][64][kRow]  u
   float* bcs = ubuf + L::kDU;              // [2][kG][NP][4 tokens][B, C]
   float* par = bcs + L::kBC;               // [2][64]        bias, D
-  float* ypart = par + L::kPar;            // [NSPLIT][64][kRow] partial readouts (output pass only)
+  float* ypart = par + L::kPar;            // [2][NSPLIT][64][kRow] partial readouts (output pass only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -111,13 +122,14 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
 
   int64_t wid = work_id(blockIdx.x, a.nwork);
   const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
-  const int64_t k = wid % nck;
+  const int64_t kc = wid % nck;
   wid /= nck;
   const int64_t cg = wid % a.chgroups;
   const int64_t b = wid / a.chgroups;
   const int64_t d0 = cg * kCh;
-  const int64_t t_begin = k * a.chunk_len;
+  const int64_t t_begin = kc * a.chunk_len;
   const int64_t t_end = min(t_begin + a.chunk_len, a.seqlen);   // valid tokens of this chunk
+  const int64_t ntile = (t_end - t_begin + T - 1) / T;
 
   const IoT* __restrict__ gu = static_cast<const IoT*>(a.u);
   const IoT* __restrict__ gd = static_cast<const IoT*>(a.delta);
@@ -147,274 +159,307 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
     iA[j] = valid ? 1.0f / An : 0.0f;
     float hv = 0.0f;
     if (!kAgg && valid) {
-      if (k > 0)
-        hv = a.carry[(bd * a.nchunks + k) * a.np + n];   // carried-in state of this chunk
+      if (kc > 0)
+        hv = a.carry[(bd * a.nchunks + kc) * a.np + n];   // carried-in state of this chunk
       else if (a.h0)
         hv = a.h0[bd * a.dstate + n];
     }
     h[j] = hv;
   }
   float dsum_acc = 0.0f;
+  const bool gate_on = a.gated != 0;
+  // gate factor = SiLU(z) + gate_off: ungated calls read z as zero, and SiLU(0) = 0
+  const float gate_off = gate_on ? 0.0f : 1.0f;
 
-  // ---- global -> register prefetch of one tile ----
-  // Buffer loads through per-workgroup descriptors: each descriptor covers
-  // exactly this workgroup's valid rows, so rows past dim (and bytes past the
-  // tensor's end) read as zero without a branch.  Tokens past the chunk end
-  // read neighbouring data and are zeroed when staged.  Branch-free loads let
-  // the next tile's data stay in flight during the scan.
-  constexpr int kEsz = (int)sizeof(IoT);
+  // ---- buffer descriptors ----
+  // Each covers exactly this workgroup's valid rows, so loads of rows past dim
+  // (and of bytes past a tensor's end) read zero and stores there are dropped,
+  // without branches.  Tokens past the chunk end read neighbouring data and are
+  // zeroed when staged.
   const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
   const int64_t row0 = (b * a.dim + d0) * a.seqlen;
   const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
   const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
   const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
   const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
-  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(a.gated ? gz + row0 : gu + row0, a.gated ? nrec_ch : 0);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(gate_on ? gz + row0 : gu + row0, gate_on ? nrec_ch : 0);
   const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
   const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
-  const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, nrec_ch);
-  constexpr int CZ = kAgg ? 1 : CPT;   // z is staged only by the output pass
-  V8 pd[CPT], pu[CPT], pz[CZ], zc[CZ], pb[BPT], pc[BPT];
-  float ureg[CZ][8];   // u of this thread's pieces, kept from staging to the epilogue
-  auto prefetch = [&](int64_t tile) {
-    const int64_t trel = tile - t_begin;
+
+  struct Pf {   // one tile's global data, in flight until staged
+    V8 d[CPT], u[CPT], z[CK], b[BPT], c[BPT];
+  };
+  struct Keep {   // one tile's u (fp32) and z, from staging to the epilogue
+    float u[CK][8];
+    V8 z[CK];
+  };
+
+  auto prefetch = [&](int64_t tile, Pf& p) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int e = min(tid + c * NT, kPieces - 1);   // idle threads re-load a valid piece
       const int ch = e / (T / 8);
       const int c8 = e % (T / 8);
-      const int off = (int)(((int64_t)ch * a.seqlen + t_begin + trel + c8 * 8) * kEsz);
-      pd[c] = IO::buf_load8(rs_d, off, a.vec_ok);
-      pu[c] = IO::buf_load8(rs_u, off, a.vec_ok);
-      if constexpr (!kAgg) pz[c] = IO::buf_load8(rs_z, off, a.vec_ok);
+      const int off = (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz);
+      p.d[c] = IO::buf_load8(rs_d, off, kVec);
+      p.u[c] = IO::buf_load8(rs_u, off, kVec);
+      if constexpr (!kAgg) p.z[c] = IO::buf_load8(rs_z, off, kVec);
     }
 #pragma unroll
     for (int c = 0; c < BPT; ++c) {
       const int e = min(tid + c * NT, kBCPieces - 1);
       const int n = e % NP;
       const int c8 = (e / NP) % (T / 8);
-      const int off = (int)(((int64_t)n * a.seqlen + t_begin + trel + c8 * 8) * kEsz);
-      pb[c] = IO::buf_load8(rs_B, off, a.vec_ok);
-      pc[c] = IO::buf_load8(rs_C, off, a.vec_ok);
+      const int off = (int)(((int64_t)n * a.seqlen + tile + c8 * 8) * kEsz);
+      p.b[c] = IO::buf_load8(rs_B, off, kVec);
+      p.c[c] = IO::buf_load8(rs_C, off, kVec);
     }
   };
 
-  int64_t tile = t_begin;
-  prefetch(tile);
-  __syncthreads();   // par[] visible
-
-  for (int it = 0; tile < t_end; ++it, tile += T) {
-    const int cur = it & 1;
-    float* dcur = dbuf + cur * kCh * kRow;
-    float* ucur = ubuf + cur * kCh * kRow;
-    float* bccur = bcs + cur * kG * NP * 8;
-
-    // ---- A: stage Delta*log2e, u and B/C in LDS ----
-    const bool tail = tile + T > t_end;   // uniform: only the last tile of a chunk can be partial
-    // The softplus switch is hoisted out of the element loops so each piece's
-    // 8 independent softplus chains can be interleaved.
-    auto stage = [&](auto sp_c) {
-      constexpr bool kSp = decltype(sp_c)::value;
+  // stage: tile -> LDS buffer `buf` (Delta*log2e, u, B/C), and u/z into kp
+  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp) {
+    float* dw = dbuf + buf * kCh * kRow;
+    float* uw = ubuf + buf * kCh * kRow;
+    float* bw = bcs + buf * kG * NP * 8;
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int e = tid + c * NT;
-        if (!kAllBusy && e >= kPieces) break;
-        const int ch = e / (T / 8);
-        const int c8 = e % (T / 8);
-        float fd[8], fu[8];
-        IO::to_f32(pd[c], fd);
-        IO::to_f32(pu[c], fu);
-        const float bi = par[ch];
+    for (int c = 0; c < CPT; ++c) {
+      const int e = tid + c * NT;
+      if (!kAllBusy && e >= kPieces) break;
+      const int ch = e / (T / 8);
+      const int c8 = e % (T / 8);
+      const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));   // valid tokens of the piece
+      float fd[8], fu[8];
+      IO::to_f32(p.d[c], fd);
+      IO::to_f32(p.u[c], fu);
+      const float bi = par[ch];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = fd[j] + bi;
-          if constexpr (kSp)
-            fd[j] = softplus_log2e(x);
-          else
-            fd[j] = x * 1.4426950408889634f;
-        }
-        if (tail) {
-          // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
-          const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            fd[j] = (j < nv) ? fd[j] : 0.0f;
-            fu[j] = (j < nv) ? fu[j] : 0.0f;
-          }
-        }
-        float* dp = dcur + ch * kRow + c8 * 8;
-        float* up = ucur + ch * kRow + c8 * 8;
-        reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-        reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-        reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-        reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
-        if constexpr (!kAgg) {
-          zc[c] = pz[c];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ureg[c][j] = fu[j];
-        }
+      for (int j = 0; j < 8; ++j) {
+        const float x = fd[j] + bi;
+        const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
+        const bool ok = j < nv;   // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
+        fd[j] = ok ? dl : 0.0f;
+        fu[j] = ok ? fu[j] : 0.0f;
       }
-    };
-    if (a.softplus)
-      stage(IntC<1>{});
-    else
-      stage(IntC<0>{});
+      float* dp = dw + ch * kRow + c8 * 8;
+      float* up = uw + ch * kRow + c8 * 8;
+      reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
+      reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
+      reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
+      reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+      if constexpr (!kAgg) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kp.u[c][j] = fu[j];
+        kp.z[c] = p.z[c];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < BPT; ++c) {
       const int e = tid + c * NT;
       if (!kBCAllBusy && e >= kBCPieces) break;
       const int n = e % NP;
       const int c8 = (e / NP) % (T / 8);
+      const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
       float fb[8], fc[8];
-      IO::to_f32(pb[c], fb);
-      IO::to_f32(pc[c], fc);
-      if (tail) {
-        const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
+      IO::to_f32(p.b[c], fb);
+      IO::to_f32(p.c[c], fc);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          fb[j] = (j < nv) ? fb[j] : 0.0f;
-          fc[j] = (j < nv) ? fc[j] : 0.0f;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = j < nv;
+        fb[j] = ok ? fb[j] : 0.0f;
+        fc[j] = ok ? fc[j] : 0.0f;
       }
       // tokens c8*8 .. +3 are group 2*c8, tokens +4 .. +7 group 2*c8+1;
       // within a (group, state) the 8 floats are B0 C0 B1 C1 B2 C2 B3 C3
-      float2* p0 = reinterpret_cast<float2*>(bccur + ((2 * c8) * NP + n) * 8);
-      float2* p1 = reinterpret_cast<float2*>(bccur + ((2 * c8 + 1) * NP + n) * 8);
+      float2* p0 = reinterpret_cast<float2*>(bw + ((2 * c8) * NP + n) * 8);
+      float2* p1 = reinterpret_cast<float2*>(bw + ((2 * c8 + 1) * NP + n) * 8);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         p0[kk] = make_float2(fb[kk], fc[kk]);
         p1[kk] = make_float2(fb[4 + kk], fc[4 + kk]);
       }
     }
-    if (tile + T < t_end) prefetch(tile + T);
-    lds_barrier();
+  };
 
-    // ---- B: scan the tile ----
-    // B/C operands: per group of 4 tokens each lane loads one (B, C) pair --
-    // lane i of each 16-lane row holds state i/4 (of this wave's NPW states)
-    // at token i%4 -- and every use takes its value through a DPP
-    // row_newbcast source operand, so the 64-lane broadcast costs no LDS
-    // bandwidth and no extra instruction.  Software pipeline over groups:
-    // token 0 of group g consumes g's operands, then group g+1's Delta/u and
-    // B/C pairs are requested from LDS, then tokens 1..3 of group g run while
-    // those reads are in flight.  Fully unrolled so the two operand buffers
-    // are fixed registers written only by LDS loads.
-    {
-      const float* drow = dcur + lane * kRow;
-      const float* urow = ucur + lane * kRow;
-      float* yrow = ypart + (w * kCh + lane) * kRow;
-      const int sel = lane & 15;
-      const float* bcl = bccur + (w * NPW + ((sel >> 2) % NPW)) * 8 + 2 * (sel & 3);
-      float4 dv = *reinterpret_cast<const float4*>(drow);
-      float4 uv = *reinterpret_cast<const float4*>(urow);
-      float2 bcv = *reinterpret_cast<const float2*>(bcl);
-
-      auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
-        constexpr int kk = decltype(kk_c)::value;
-        float acc = 0.0f;
-        static_for<NPW>([&](auto j_c) {
-          constexpr int j = decltype(j_c)::value;
-          constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
-          const float av = __builtin_amdgcn_exp2f(dl * A[j]);
-          const float v = uu * iA[j];
-          const float sv = dpp_bcast_mul<src>(bq.x, v);          // B * u / A
-          const float hs = dpp_bcast_fmac<src>(h[j], bq.x, v);   // h + B * u / A
-          h[j] = fmaf(av, hs, -sv);
-          if constexpr (!kAgg) {
-            if constexpr (j == 0)
-              acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
-            else
-              acc = dpp_bcast_fmac<src>(acc, bq.y, h[j]);
-          }
-        });
-        return acc;
-      };
-
+  // epilogue, in two halves: issue the partial-readout reads, then finish
+  struct Yp {
+    float4 v[CK][NSPLIT][2];
+  };
+  auto epi_read = [&](int ybuf, Yp& yp) {
+    const float* yr = ypart + ybuf * NSPLIT * kCh * kRow;
 #pragma unroll
-      for (int g = 0; g < kG; ++g) {
-        const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
-        __builtin_amdgcn_sched_barrier(0);
-        float4 dn = dv, un = uv;
-        float2 bcn = bcv;
-        if (g + 1 < kG) {
-          dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
-          un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
-          bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
-        const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
-        const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
-        if (!kAgg)
-          *reinterpret_cast<float4*>(yrow + 4 * g) = make_float4(y0, y1, y2, y3);
-        else
-          dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
-        if (g + 1 < kG) {
-          dv = dn;
-          uv = un;
-          bcv = bcn;
-        }
+    for (int c = 0; c < CK; ++c) {
+      const int e = min(tid + c * NT, kPieces - 1);
+      const int ch = e / (T / 8);
+      const int c8 = e % (T / 8);
+#pragma unroll
+      for (int s2 = 0; s2 < NSPLIT; ++s2) {
+        const float4* ps = reinterpret_cast<const float4*>(yr + (s2 * kCh + ch) * kRow + c8 * 8);
+        yp.v[c][s2][0] = ps[0];
+        yp.v[c][s2][1] = ps[1];
       }
     }
+  };
+  auto epi_finish = [&](const Yp& yp, const Keep& kp, int c, float (&yv)[8]) {
+    const int e = min(tid + c * NT, kPieces - 1);
+    const int ch = e / (T / 8);
+    yv[0] = yp.v[c][0][0].x; yv[1] = yp.v[c][0][0].y; yv[2] = yp.v[c][0][0].z; yv[3] = yp.v[c][0][0].w;
+    yv[4] = yp.v[c][0][1].x; yv[5] = yp.v[c][0][1].y; yv[6] = yp.v[c][0][1].z; yv[7] = yp.v[c][0][1].w;
+#pragma unroll
+    for (int s2 = 1; s2 < NSPLIT; ++s2) {
+      yv[0] += yp.v[c][s2][0].x; yv[1] += yp.v[c][s2][0].y; yv[2] += yp.v[c][s2][0].z; yv[3] += yp.v[c][s2][0].w;
+      yv[4] += yp.v[c][s2][1].x; yv[5] += yp.v[c][s2][1].y; yv[6] += yp.v[c][s2][1].z; yv[7] += yp.v[c][s2][1].w;
+    }
+    const float Dd = par[kCh + ch];
+    float zf[8];
+    IO::to_f32(kp.z[c], zf);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      yv[j] = fmaf(Dd, kp.u[c][j], yv[j]) * (silu(zf[j]) + gate_off);
+    }
+  };
+  // full tile, output rows: branch-free stores (rows past dim and disabled
+  // descriptors drop the writes)
+  auto epi_store_full = [&](int64_t tile, int c, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
+    if (!kAllBusy && tid + c * NT >= kPieces) return;   // threads without a piece store nothing
+    const int e = tid + c * NT;
+    const int ch = e / (T / 8);
+    const int c8 = e % (T / 8);
+    const int off = (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz);
+    IO::buf_store8(rs, off, IO::from_f32(yv), kVec);
+  };
+  // any tile (the last one may be partial): guarded element stores
+  auto epi_store_tail = [&](int64_t tile, int c, const float (&yv)[8]) {
+    const int e = tid + c * NT;
+    if (!kAllBusy && e >= kPieces) return;
+    const int ch = e / (T / 8);
+    const int c8 = e % (T / 8);
+    const int64_t t0 = tile + c8 * 8;
+    int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
+    if (d0 + ch >= a.dim) nv = 0;
+    IO::store_n(gy + (b * a.dim + d0 + ch) * a.seqlen + t0, IO::from_f32(yv), nv);
+  };
 
-    if (!kAgg) {
-      lds_barrier();
-      // ---- C: combine partial readouts, D skip, gate, store ----
-      // all partial-readout reads are issued before any use
-      float4 yp[CZ][NSPLIT][2];
+  // ---- the scan of one tile with the pipelined extra work ----
+  // Tile k, parity P: scan LDS buffer P into partial readouts P; finish the
+  // epilogue of tile k-1 (partials 1-P, keep kpOther); stage tile k+1 from
+  // pfOther into buffer 1-P and kpOther; issue the loads of tile k+2 into pfCur.
+  auto body = [&](int64_t k, auto P_c, Pf& pfCur, Pf& pfOther, Keep& kpOther) {
+    constexpr int P = decltype(P_c)::value;
+    const int64_t tile = t_begin + k * T;
+    const float* drow = dbuf + P * kCh * kRow + lane * kRow;
+    const float* urow = ubuf + P * kCh * kRow + lane * kRow;
+    const int sel = lane & 15;
+    const float* bcl = bcs + P * kG * NP * 8 + (w * NPW + ((sel >> 2) % NPW)) * 8 + 2 * (sel & 3);
+    float* yrow = ypart + P * NSPLIT * kCh * kRow + (w * kCh + lane) * kRow;
+
+    float4 dv = *reinterpret_cast<const float4*>(drow);
+    float4 uv = *reinterpret_cast<const float4*>(urow);
+    float2 bcv = *reinterpret_cast<const float2*>(bcl);
+    Yp yp;
+    if constexpr (!kAgg) epi_read(1 - P, yp);
+    prefetch(tile + 2 * T, pfCur);
+    // the epilogue of tile k-1 stores only when there is such a tile
+    const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
+
+    auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
+      constexpr int kk = decltype(kk_c)::value;
+      float acc = 0.0f;
+      static_for<NPW>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
+        const float av = __builtin_amdgcn_exp2f(dl * A[j]);
+        const float v = uu * iA[j];
+        const float sv = dpp_bcast_mul<src>(bq.x, v);          // B * u / A
+        const float hs = dpp_bcast_fmac<src>(h[j], bq.x, v);   // h + B * u / A
+        h[j] = fmaf(av, hs, -sv);
+        if constexpr (!kAgg) {
+          if constexpr (j == 0)
+            acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
+          else
+            acc = dpp_bcast_fmac<src>(acc, bq.y, h[j]);
+        }
+      });
+      return acc;
+    };
+
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int e = min(tid + c * NT, kPieces - 1);
-        const int ch = e / (T / 8);
-        const int c8 = e % (T / 8);
+    for (int g = 0; g < kG; ++g) {
+      const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
+      __builtin_amdgcn_sched_barrier(0);
+      float4 dn = dv, un = uv;
+      float2 bcn = bcv;
+      if (g + 1 < kG) {
+        dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
+        un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
+        bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
+      const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
+      const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
+      if constexpr (!kAgg)
+        *reinterpret_cast<float4*>(yrow + 4 * g) = make_float4(y0, y1, y2, y3);
+      else
+        dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
+      // interleaved work of the neighbouring tiles
+      if constexpr (!kAgg) {
+        if (g == 1) {
 #pragma unroll
-        for (int s2 = 0; s2 < NSPLIT; ++s2) {
-          const float4* ps = reinterpret_cast<const float4*>(ypart + (s2 * kCh + ch) * kRow + c8 * 8);
-          yp[kAgg ? 0 : c][s2][0] = ps[0];
-          yp[kAgg ? 0 : c][s2][1] = ps[1];
+          for (int c = 0; c < CK; ++c) {
+            float yv[8];
+            epi_finish(yp, kpOther, c, yv);
+            epi_store_full(tile - T, c, yv, rs_y);
+          }
         }
       }
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int e = tid + c * NT;
-        if (!kAllBusy && e >= kPieces) break;
-        const int ch = e / (T / 8);
-        const int c8 = e % (T / 8);
-        const int cc = kAgg ? 0 : c;
-        float yv[8] = {yp[cc][0][0].x, yp[cc][0][0].y, yp[cc][0][0].z, yp[cc][0][0].w,
-                       yp[cc][0][1].x, yp[cc][0][1].y, yp[cc][0][1].z, yp[cc][0][1].w};
-#pragma unroll
-        for (int s2 = 1; s2 < NSPLIT; ++s2) {
-          yv[0] += yp[cc][s2][0].x; yv[1] += yp[cc][s2][0].y; yv[2] += yp[cc][s2][0].z; yv[3] += yp[cc][s2][0].w;
-          yv[4] += yp[cc][s2][1].x; yv[5] += yp[cc][s2][1].y; yv[6] += yp[cc][s2][1].z; yv[7] += yp[cc][s2][1].w;
-        }
-        const float Dd = par[kCh + ch];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, ureg[cc][j], yv[j]);
-        if (a.gated) {
-          float zf[8];
-          IO::to_f32(zc[cc], zf);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) yv[j] *= silu(zf[j]);
-        }
-        const V8 out = IO::from_f32(yv);
-        if (!tail && a.vec_ok) {
-          // rows past dim fall outside the descriptor and are dropped
-          IO::buf_store8(rs_y, (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz), out);
-        } else {
-          const int64_t t0 = tile + c8 * 8;
-          int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-          if (d0 + ch >= a.dim) nv = 0;
-          IO::store_n(gy + (b * a.dim + d0 + ch) * a.seqlen + t0, out, nv);
-        }
+      if (g == 2) stage(tile + T, pfOther, 1 - P, kpOther);
+      if (g + 1 < kG) {
+        dv = dn;
+        uv = un;
+        bcv = bcn;
       }
+    }
+    lds_barrier();
+  };
+
+  // final epilogue of tile k (after the barrier that follows its scan)
+  auto last_epilogue = [&](int64_t k, int P, const Keep& kp) {
+    if constexpr (!kAgg) {
+      Yp yp;
+      epi_read(P, yp);
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        float yv[8];
+        epi_finish(yp, kp, c, yv);
+        epi_store_tail(t_begin + k * T, c, yv);
+      }
+    }
+  };
+
+  Pf pf0, pf1;
+  Keep kp0 = {}, kp1 = {};
+  prefetch(t_begin, pf0);
+  prefetch(t_begin + T, pf1);
+  __syncthreads();   // par[] visible
+  stage(t_begin, pf0, 0, kp0);
+  lds_barrier();
+  for (int64_t k = 0; k < ntile; k += 2) {
+    body(k, IntC<0>{}, pf0, pf1, kp1);
+    if (k + 1 >= ntile) {
+      last_epilogue(k, 0, kp0);
+      break;
+    }
+    body(k + 1, IntC<1>{}, pf1, pf0, kp0);
+    if (k + 2 >= ntile) {
+      last_epilogue(k + 1, 1, kp1);
+      break;
     }
   }
 
-  // ---- epilogue: final state or chunk aggregate ----
+  // ---- final state or chunk aggregate ----
   if (ch_ok) {
     if (!kAgg) {
-      if (k == a.nchunks - 1 && a.final_state) {
+      if (kc == a.nchunks - 1 && a.final_state) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
           const int n = w * NPW + j;
@@ -425,9 +470,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
 #pragma unroll
       for (int j = 0; j < NPW; ++j) {
         const int n = w * NPW + j;
-        a.carry[(bd * a.nchunks + k) * a.np + n] = h[j];
+        a.carry[(bd * a.nchunks + kc) * a.np + n] = h[j];
       }
-      if (w == 0) a.dsum[bd * a.nchunks + k] = dsum_acc;
+      if (w == 0) a.dsum[bd * a.nchunks + kc] = dsum_acc;
     }
   }
 }
@@ -464,39 +509,24 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-template <typename IoT, int NPW, int NSPLIT, int T>
-hipError_t launch_scan(const KArgs& k, bool agg, int64_t grid, hipStream_t s) {
-  if (agg) {
-    auto kern = scan_fwd_kernel<IoT, NPW, NSPLIT, T, true>;
-    const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, true>::kFloats;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
-  } else {
-    auto kern = scan_fwd_kernel<IoT, NPW, NSPLIT, T, false>;
-    const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, false>::kFloats;
-    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
-  }
+template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
+hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
+  auto kern = vec ? (k.softplus ? scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, true, true>
+                                : scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, true, false>)
+                  : (k.softplus ? scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, false, true>
+                                : scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, false, false>);
+  const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, kAgg>::kFloats;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
   return hipGetLastError();
 }
 
 template <typename IoT>
-hipError_t dispatch_scan(const KArgs& k, const FwdPlan& p, bool agg, int64_t grid, hipStream_t s) {
-  if (p.npw == 4) {
-    switch (p.nsplit) {
-      case 1: return launch_scan<IoT, 4, 1, 64>(k, agg, grid, s);
-      case 2: return launch_scan<IoT, 4, 2, 64>(k, agg, grid, s);
-      default: return launch_scan<IoT, 4, 4, 64>(k, agg, grid, s);
-    }
-  }
-  switch (p.nsplit) {
-    case 1: return launch_scan<IoT, 2, 1, 32>(k, agg, grid, s);
-    case 2: return launch_scan<IoT, 2, 2, 32>(k, agg, grid, s);
-    case 4: return launch_scan<IoT, 2, 4, 32>(k, agg, grid, s);
-    default: return launch_scan<IoT, 2, 8, 32>(k, agg, grid, s);
-  }
+hipError_t dispatch_scan(const KArgs& k, const FwdPlan& p, bool agg, bool vec, int64_t grid, hipStream_t s) {
+  if (p.npw == 4) return agg ? launch_scan<IoT, 4, 4, 32, true>(k, vec, grid, s)
+                             : launch_scan<IoT, 4, 4, 32, false>(k, vec, grid, s);
+  return agg ? launch_scan<IoT, 2, 8, 16, true>(k, vec, grid, s) : launch_scan<IoT, 2, 8, 16, false>(k, vec, grid, s);
 }
 
 template <typename IoT>
@@ -520,17 +550,17 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a.u) | reinterpret_cast<uintptr_t>(a.delta) |
                         reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z) |
                         reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C);
+  const bool vec = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
   KArgs k{};
   k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.softplus = a.softplus; k.gated = a.z != nullptr;
-  k.vec_ok = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
   const int64_t groups = a.batch * k.chgroups;
   if (p.nchunks > 1) {
     k.nwork = groups * (p.nchunks - 1);
-    hipError_t e = dispatch_scan<IoT>(k, p, true, k.nwork, s);
+    hipError_t e = dispatch_scan<IoT>(k, p, true, vec, k.nwork, s);
     if (e != hipSuccess) return e;
     const int64_t n = a.batch * a.dim * a.dstate;
     hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, carry, dsum, a.A_log,
@@ -539,7 +569,7 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   k.nwork = groups * p.nchunks;
-  return dispatch_scan<IoT>(k, p, false, k.nwork, s);
+  return dispatch_scan<IoT>(k, p, false, vec, k.nwork, s);
 }
 
 }  // namespace
@@ -548,13 +578,13 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    FwdPlan* p) {
   if (npw_req != 0 && npw_req != 2 && npw_req != 4) return false;
   if (nchunks_req < 0) return false;
+  (void)dstate;
+  // two layouts: 4 states per lane x 4 waves (32-token tiles) or 2 x 8 (16-token
+  // tiles); states past dstate are padding that contributes exactly zero
   p->npw = npw_req ? npw_req : 4;
-  p->tile = p->npw == 4 ? 64 : 32;
-  int need = (int)((dstate + p->npw - 1) / p->npw);
-  int ns = 1;
-  while (ns < need) ns <<= 1;
-  p->nsplit = ns;
-  p->np = ns * p->npw;
+  p->tile = p->npw == 4 ? 32 : 16;
+  p->nsplit = p->npw == 4 ? 4 : 8;
+  p->np = 16;
   const int64_t T = p->tile;
   const int64_t tiles = (seqlen + T - 1) / T;
   p->lp = tiles * T;
@@ -562,9 +592,9 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   const int64_t groups = batch * ((dim + kCh - 1) / kCh);
   if (nchunks_req > 0) {
     nch = nchunks_req;
-  } else if (groups < 128 && tiles >= 8) {
-    // too few workgroups to fill 256 CUs: scan time chunks in parallel (each >= 4 tiles)
-    nch = std::min<int64_t>(256 / groups, tiles / 4);
+  } else if (groups < 128 && tiles >= 16) {
+    // too few workgroups to fill 256 CUs: scan time chunks in parallel (each >= 8 tiles)
+    nch = std::min<int64_t>(256 / groups, tiles / 8);
   }
   nch = std::max<int64_t>(1, std::min<int64_t>(nch, std::max<int64_t>(tiles, 1)));
   const int64_t tiles_per = (tiles + nch - 1) / nch;
