@@ -93,6 +93,21 @@ struct Io<uint16_t> {
     for (int j = 0; j < 8; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * j, 0, 0);
     return V8{make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16))};
   }
+  // Four consecutive elements.
+  struct V4 {
+    uint2 w;
+  };
+  static __device__ __forceinline__ V4 buf_load4(__amdgpu_buffer_rsrc_t r, int off, int vec) {
+    if (vec) return V4{__builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0))};
+    uint32_t e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * j, 0, 0);
+    return V4{make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16))};
+  }
+  static __device__ __forceinline__ void to_f32(const V4& v, float (&f)[4]) {
+    f[0] = bf16_lo(v.w.x); f[1] = bf16_hi(v.w.x);
+    f[2] = bf16_lo(v.w.y); f[3] = bf16_hi(v.w.y);
+  }
   static __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
   static __device__ __forceinline__ void store1(uint16_t* p, float f) {
     *p = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
@@ -150,6 +165,19 @@ struct Io<float> {
 #pragma unroll
     for (int j = 0; j < 8; ++j) e[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * j, 0, 0));
     return V8{make_float4(e[0], e[1], e[2], e[3]), make_float4(e[4], e[5], e[6], e[7])};
+  }
+  struct V4 {
+    float4 a;
+  };
+  static __device__ __forceinline__ V4 buf_load4(__amdgpu_buffer_rsrc_t r, int off, int vec) {
+    if (vec) return V4{__builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0))};
+    float e[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) e[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * j, 0, 0));
+    return V4{make_float4(e[0], e[1], e[2], e[3])};
+  }
+  static __device__ __forceinline__ void to_f32(const V4& v, float (&f)[4]) {
+    f[0] = v.a.x; f[1] = v.a.y; f[2] = v.a.z; f[3] = v.a.w;
   }
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
   static __device__ __forceinline__ void store1(float* p, float f) { *p = f; }

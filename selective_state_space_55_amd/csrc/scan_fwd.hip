@@ -31,7 +31,8 @@
 // holds two copies of the staged inputs and of the partial readouts; one
 // barrier per tile.
 // Inner step per (token, state): Abar = 2^(Delta*log2e * A); s = B u / A;
-// h = Abar (h + s) - s  (= Abar h + (Abar - 1)/A B u);  y += C h.
+// h = Abar (h + s) - s  (= Abar h + (Abar - 1)/A B u);  y += C h.  Six VALU
+// instructions and one exp per (token, state), two of them with a DPP operand.
 //
 // Time chunks.  When batch x channel groups cannot fill the GPU (e.g. one
 // batch row of 2048 channels and a million tokens) the sequence is cut into
@@ -93,6 +94,7 @@ template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg, bool kVec, bool k
 __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V8 = typename IO::V8;
+  using V4 = typename IO::V4;
   using L = Lds<NPW, NSPLIT, T, kAgg>;
   constexpr int NT = NSPLIT * 64;       // threads
   constexpr int kRow = L::kRow;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   constexpr int kPieces = kCh * T / 8;  // 8-token pieces of Delta/u/z per tile
   constexpr int CPT = (kPieces + NT - 1) / NT;
   constexpr bool kAllBusy = (kPieces % NT) == 0;
-  constexpr int kBCPieces = NP * (T / 8);       // (state, 8-token) pieces of B and C per tile
+  constexpr int kBCPieces = 2 * NP * kG;        // (B or C, state, 4-token group) pieces per tile
   constexpr int BPT = (kBCPieces + NT - 1) / NT;
   constexpr bool kBCAllBusy = (kBCPieces % NT) == 0;
   constexpr int CK = kAgg ? 1 : CPT;    // u/z kept from staging to the epilogue (output pass only)
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   extern __shared__ float smem[];
   float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
   float* ubuf = dbuf + L::kDU;             // [2][64][kRow]  u
-  float* bcs = ubuf + L::kDU;              // [2][kG][NP][4 tokens][B, C]
+  float* bcs = ubuf + L::kDU;              // [2][kG][4 tokens][NP][B, C]
   float* par = bcs + L::kBC;               // [2][64]        bias, D
   float* ypart = par + L::kPar;            // [2][NSPLIT][64][kRow] partial readouts (output pass only)
 
@@ -187,7 +189,8 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
 
   struct Pf {   // one tile's global data, in flight until staged
-    V8 d[CPT], u[CPT], z[CK], b[BPT], c[BPT];
+    V8 d[CPT], u[CPT], z[CK];
+    V4 bc[BPT];
   };
   struct Keep {   // one tile's u (fp32) and z, from staging to the epilogue
     float u[CK][8];
@@ -208,16 +211,19 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
 #pragma unroll
     for (int c = 0; c < BPT; ++c) {
       const int e = min(tid + c * NT, kBCPieces - 1);
-      const int n = e % NP;
-      const int c8 = (e / NP) % (T / 8);
-      const int off = (int)(((int64_t)n * a.seqlen + tile + c8 * 8) * kEsz);
-      p.b[c] = IO::buf_load8(rs_B, off, kVec);
-      p.c[c] = IO::buf_load8(rs_C, off, kVec);
+      const int g = e % kG;
+      const int n = (e / kG) % NP;
+      const int off = (int)(((int64_t)n * a.seqlen + tile + g * 4) * kEsz);
+      // B rows fill whole waves, then C rows: the choice is uniform per wave
+      static_assert((NP * kG) % 64 == 0, "B/C pieces must fill whole waves");
+      const bool isB = __builtin_amdgcn_readfirstlane(e / (NP * kG)) == 0;
+      p.bc[c] = IO::buf_load4(isB ? rs_B : rs_C, off, kVec);
     }
   };
 
   // stage: tile -> LDS buffer `buf` (Delta*log2e, u, B/C), and u/z into kp
-  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp) {
+  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp, auto full_c) {
+    constexpr bool kFull = decltype(full_c)::value;   // every token of the tile is valid
     float* dw = dbuf + buf * kCh * kRow;
     float* uw = ubuf + buf * kCh * kRow;
     float* bw = bcs + buf * kG * NP * 8;
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
       if (!kAllBusy && e >= kPieces) break;
       const int ch = e / (T / 8);
       const int c8 = e % (T / 8);
-      const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));   // valid tokens of the piece
+      const int nv = kFull ? 8 : (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));   // valid tokens
       float fd[8], fu[8];
       IO::to_f32(p.d[c], fd);
       IO::to_f32(p.u[c], fu);
@@ -256,27 +262,16 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
     for (int c = 0; c < BPT; ++c) {
       const int e = tid + c * NT;
       if (!kBCAllBusy && e >= kBCPieces) break;
-      const int n = e % NP;
-      const int c8 = (e / NP) % (T / 8);
-      const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));
-      float fb[8], fc[8];
-      IO::to_f32(p.b[c], fb);
-      IO::to_f32(p.c[c], fc);
+      const int g = e % kG;
+      const int n = (e / kG) % NP;
+      const int which = e / (NP * kG);   // 0: B, 1: C
+      const int nv = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + g * 4)));
+      float f[4];
+      IO::to_f32(p.bc[c], f);
+      // (group, token, state) holds the pair (B, C)
+      float* q = bw + (g * 4 * NP + n) * 2 + which;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const bool ok = j < nv;
-        fb[j] = ok ? fb[j] : 0.0f;
-        fc[j] = ok ? fc[j] : 0.0f;
-      }
-      // tokens c8*8 .. +3 are group 2*c8, tokens +4 .. +7 group 2*c8+1;
-      // within a (group, state) the 8 floats are B0 C0 B1 C1 B2 C2 B3 C3
-      float2* p0 = reinterpret_cast<float2*>(bw + ((2 * c8) * NP + n) * 8);
-      float2* p1 = reinterpret_cast<float2*>(bw + ((2 * c8 + 1) * NP + n) * 8);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        p0[kk] = make_float2(fb[kk], fc[kk]);
-        p1[kk] = make_float2(fb[4 + kk], fc[4 + kk]);
-      }
+      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nv) ? f[kk] : 0.0f;
     }
   };
 
@@ -349,7 +344,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
     const float* drow = dbuf + P * kCh * kRow + lane * kRow;
     const float* urow = ubuf + P * kCh * kRow + lane * kRow;
     const int sel = lane & 15;
-    const float* bcl = bcs + P * kG * NP * 8 + (w * NPW + ((sel >> 2) % NPW)) * 8 + 2 * (sel & 3);
+    const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + w * NPW + ((sel >> 2) % NPW)) * 2;
     float* yrow = ypart + P * NSPLIT * kCh * kRow + (w * kCh + lane) * kRow;
 
     float4 dv = *reinterpret_cast<const float4*>(drow);
@@ -364,14 +359,19 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
     auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
       constexpr int kk = decltype(kk_c)::value;
       float acc = 0.0f;
+      float av[NPW], sv[NPW];
+      // all DPP products first: a DPP result read by the next VALU
+      // instruction costs a wait state
       static_for<NPW>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
-        const float av = __builtin_amdgcn_exp2f(dl * A[j]);
-        const float v = uu * iA[j];
-        const float sv = dpp_bcast_mul<src>(bq.x, v);          // B * u / A
-        const float hs = dpp_bcast_fmac<src>(h[j], bq.x, v);   // h + B * u / A
-        h[j] = fmaf(av, hs, -sv);
+        av[j] = __builtin_amdgcn_exp2f(dl * A[j]);
+        sv[j] = dpp_bcast_mul<src>(bq.x, uu * iA[j]);          // s = B * u / A
+      });
+      static_for<NPW>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        constexpr int src = 4 * j + kk;
+        h[j] = fmaf(av[j], h[j] + sv[j], -sv[j]);              // Abar (h + s) - s
         if constexpr (!kAgg) {
           if constexpr (j == 0)
             acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
@@ -412,7 +412,12 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
           }
         }
       }
-      if (g == 2) stage(tile + T, pfOther, 1 - P, kpOther);
+      if (g == 2) {
+        if (tile + 2 * T <= t_end)
+          stage(tile + T, pfOther, 1 - P, kpOther, IntC<1>{});
+        else
+          stage(tile + T, pfOther, 1 - P, kpOther, IntC<0>{});
+      }
       if (g + 1 < kG) {
         dv = dn;
         uv = un;
@@ -441,7 +446,7 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   prefetch(t_begin, pf0);
   prefetch(t_begin + T, pf1);
   __syncthreads();   // par[] visible
-  stage(t_begin, pf0, 0, kp0);
+  stage(t_begin, pf0, 0, kp0, IntC<0>{});
   lds_barrier();
   for (int64_t k = 0; k < ntile; k += 2) {
     body(k, IntC<0>{}, pf0, pf1, kp1);
