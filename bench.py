@@ -95,22 +95,51 @@ def bench_step(args, c) -> int:
     y = torch.empty((c.batch, c.dim), dtype=x.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(k):
+    def step(k, state, strm=None):
         j = k % pool
-        mscan.scan_step(st, x[j], dt[j], A, Bm[j], Cm[j], D=D, z=z[j], dt_bias=bias, out=y, stream=stream)
+        mscan.scan_step(state, x[j], dt[j], A, Bm[j], Cm[j], D=D, z=z[j], dt_bias=bias, out=y, stream=strm)
 
+    # A decode loop is launch-bound from Python, so the K chained steps are
+    # captured once in a HIP graph and replayed; the replay is checked against
+    # the same K steps launched one by one (bit-exact: same kernels, same order).
+    st0 = st.clone()
     for k in range(args.warmup):
-        step(k)
+        step(k, st, stream)
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for k in range(args.steps):
+            step(k, st)          # the capture stream is the current stream here
+    st.copy_(st0)
+    graph.replay()
+    st_eager = st0.clone()
+    for k in range(args.steps):
+        step(k, st_eager, stream)
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(st, st_eager))
+    if not graph_ok:
+        print("bench.py: graph replay differs from eager steps", file=sys.stderr)
+        return 1
+    for _ in range(max(1, args.warmup // max(1, args.steps))):
+        graph.replay()
+    torch.cuda.synchronize()
+    st_pre = st.clone()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     e0.record(stream)
-    for k in range(args.steps):
-        step(k)
+    graph.replay()
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     dev_ms = e0.elapsed_time(e1) / args.steps
+    # the timed replay too must equal eager steps from the state it started from
+    for k in range(args.steps):
+        step(k, st_pre, stream)
+    torch.cuda.synchronize()
+    graph_ok = graph_ok and bool(torch.equal(st, st_pre))
+    if not graph_ok:
+        print("bench.py: timed graph replay differs from eager steps", file=sys.stderr)
+        return 1
     bd = c.batch * c.dim
     alg = c.algorithmic_bytes()
     out = {
@@ -122,8 +151,8 @@ def bench_step(args, c) -> int:
         "device_ms_per_step": round(dev_ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{c.name}: batch {c.batch}, d_inner {c.dim}, d_state {c.dstate}, fp32 state, "
-                               f"{c.io} io, gated, chained steps", "batch": c.batch, "d_inner": c.dim,
-                   "d_state": c.dstate},
+                               f"{c.io} io, gated, chained steps replayed from one HIP graph",
+                   "batch": c.batch, "d_inner": c.dim, "d_state": c.dstate, "graph_matches_eager": graph_ok},
         "roofline": {"bound": "hbm", "achieved": round(alg / (dev_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(alg / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "traffic": None},

@@ -65,7 +65,7 @@ typedef enum {
   MAMBA_SCAN_ERR_SHAPE = 2,       /* a size is out of range                              */
   MAMBA_SCAN_ERR_DTYPE = 3,       /* io_dtype is not a mamba_scan_dtype                  */
   MAMBA_SCAN_ERR_ALIGN = 4,       /* a pointer is not aligned to its element size        */
-  MAMBA_SCAN_ERR_UNSUPPORTED = 5, /* dstate > MAMBA_SCAN_MAX_DSTATE or a bad tuning knob */
+  MAMBA_SCAN_ERR_UNSUPPORTED = 5, /* a size beyond a documented limit or a bad tuning knob */
   MAMBA_SCAN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than required             */
   MAMBA_SCAN_ERR_HIP = 7          /* the HIP runtime reported an error at launch         */
 } mamba_scan_status;
@@ -106,7 +106,9 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  * Same as mamba_scan_fwd with two explicit launch choices (0 = automatic):
  *   nchunks          number of time chunks scanned in parallel, joined by an
  *                    inter-chunk carry of the state (1 = one sequential pass);
- *                    must be <= max(1, ceil(seqlen / 64)).
+ *                    chunks are whole tiles of 32 tokens (16 when
+ *                    states_per_wave is 2), and a request for more chunks
+ *                    than tiles is reduced to one chunk per tile.
  *   states_per_wave  states held per lane: 2 or 4.
  * The result is the same function; only rounding order differs.  The
  * workspace must be at least mamba_scan_fwd_workspace_size_ex(...) bytes.
@@ -134,6 +136,10 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
  *   dt_bias   (dim)                f32   NULL means 0
  *   dt_softplus  as delta_softplus above
  *   y         (batch, dim)         io    OUT
+ *
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, and batch <= 262140 (a
+ * launch covers four batch rows per grid row; larger returns
+ * MAMBA_SCAN_ERR_UNSUPPORTED).
  */
 int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
                     const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,

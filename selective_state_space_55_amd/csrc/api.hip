@@ -116,6 +116,7 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
                     int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, dim, dstate, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
+  if ((batch + 3) / 4 > 65535) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid rows of four batch rows
   if (!state || !x || !dt || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
   const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
   const void* io_ptrs[] = {x, dt, B, C, z, y};

@@ -6,15 +6,20 @@
 // instead of a KV cache).  The step is a pure stream over the state: it reads
 // and writes 2 * N * 4 bytes per (batch, channel) and a handful of bf16/fp32
 // scalars, so the kernel is laid out for coalesced 16-byte state traffic:
-// four lanes own one (batch, channel), lane q holding states 4q .. 4q+3 as one
-// float4; consecutive quads cover consecutive channels, so a wave moves 1 KB
-// of contiguous state per access.  The readout sum over the four lanes uses
-// two cross-lane adds in a fixed order, so results are deterministic.
+// four lanes own one channel, lane q holding states 4q .. 4q+3 as one float4;
+// consecutive quads cover consecutive channels, so a wave moves 1 KB of
+// contiguous state per access.  Each thread walks kRows batch rows of its
+// channel, so A = -exp(A_log) and 1/A are formed once per channel and reused,
+// and all rows' loads are issued before the arithmetic.  The readout sum over
+// the four lanes uses two cross-lane adds in a fixed order, so results are
+// deterministic.
 #include "internal.h"
 #include "io.h"
 
 namespace mscan {
 namespace {
+
+constexpr int kRows = 4;   // batch rows per thread
 
 struct SArgs {
   float* state;
@@ -28,70 +33,111 @@ struct SArgs {
   const float* bias;
   void* y;
   int64_t batch, dim;
-  int dstate, softplus, vec_ok;
+  int dstate, softplus;
 };
 
-template <typename IoT>
+// B or C values of states 4q .. 4q+3 of batch row b (zero past dstate)
+template <typename IoT, bool kVec>
+__device__ __forceinline__ void load_bc4(const IoT* p, int64_t b, int q, int dstate, float (&f)[4]) {
+  using IO = Io<IoT>;
+  const IoT* r = p + b * dstate + 4 * q;
+  if constexpr (kVec) {
+    if constexpr (sizeof(IoT) == 2) {
+      const uint2 w = *reinterpret_cast<const uint2*>(r);
+      f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x); f[2] = bf16_lo(w.y); f[3] = bf16_hi(w.y);
+    } else {
+      const float4 v = *reinterpret_cast<const float4*>(r);
+      f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = (4 * q + j < dstate) ? IO::load1(r + j) : 0.0f;
+  }
+}
+
+// kVec: dstate == 16 and the state, B and C rows are vector aligned
+template <typename IoT, bool kVec>
 __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
   using IO = Io<IoT>;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t bd = gid >> 2;
+  const int64_t dq = gid >> 2;           // channel
   const int q = (int)(gid & 3);
-  const int64_t nbd = a.batch * a.dim;
-  const bool live = bd < nbd;   // whole quads share bd, so a quad is live or dead together
-  const int64_t bdc = live ? bd : 0;
-  const int64_t b = bdc / a.dim;
-  const int64_t d = bdc % a.dim;
+  const bool live_d = dq < a.dim;        // whole quads share the channel
+  const int64_t d = live_d ? dq : 0;
+  const int64_t b0 = (int64_t)blockIdx.y * kRows;
 
   const IoT* gx = static_cast<const IoT*>(a.x);
   const IoT* gdt = static_cast<const IoT*>(a.dt);
+  const IoT* gz = static_cast<const IoT*>(a.z);
   const IoT* gB = static_cast<const IoT*>(a.B);
   const IoT* gC = static_cast<const IoT*>(a.C);
 
-  const float xv = live ? IO::load1(gx + bdc) : 0.0f;
-  const float xr = (live ? IO::load1(gdt + bdc) : 0.0f) + (a.bias ? a.bias[d] : 0.0f);
-  const float dl = a.softplus ? softplus_log2e(xr) : xr * 1.4426950408889634f;   // Delta * log2e
-
-  float hs[4];
-  float* st = a.state + bdc * a.dstate + 4 * q;
-  if (live && a.vec_ok) {
-    const float4 v = *reinterpret_cast<const float4*>(st);
-    hs[0] = v.x; hs[1] = v.y; hs[2] = v.z; hs[3] = v.w;
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) hs[j] = (live && 4 * q + j < a.dstate) ? st[j] : 0.0f;
-  }
-
-  float acc = 0.0f;
+  // per-channel constants, shared by the thread's batch rows
+  float An[4], iA[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = 4 * q + j;
-    if (n < a.dstate) {
-      const float An = -expf(a.A_log[d * a.dstate + n]);
-      const float Bn = IO::load1(gB + b * a.dstate + n);
-      const float Cn = IO::load1(gC + b * a.dstate + n);
-      const float av = __builtin_amdgcn_exp2f(dl * An);
-      const float s = Bn * (xv * (1.0f / An));
-      hs[j] = fmaf(av, hs[j] + s, -s);
-      acc = fmaf(Cn, hs[j], acc);
+    const bool ok = n < a.dstate;
+    An[j] = ok ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
+    iA[j] = ok ? 1.0f / An[j] : 0.0f;
+  }
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float Dd = a.D ? a.D[d] : 0.0f;
+
+  // all loads of the thread's rows first
+  float xv[kRows], xr[kRows], zv[kRows], Bv[kRows][4], Cv[kRows][4], hs[kRows][4];
+  bool live[kRows];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    const int64_t b = b0 + r;
+    live[r] = live_d && b < a.batch;
+    const int64_t bc = live[r] ? b : 0;
+    const int64_t bd = bc * a.dim + d;
+    xv[r] = live[r] ? IO::load1(gx + bd) : 0.0f;
+    xr[r] = live[r] ? IO::load1(gdt + bd) : 0.0f;
+    zv[r] = (live[r] && gz) ? IO::load1(gz + bd) : 0.0f;
+    load_bc4<IoT, kVec>(gB, bc, q, a.dstate, Bv[r]);
+    load_bc4<IoT, kVec>(gC, bc, q, a.dstate, Cv[r]);
+    const float* st = a.state + bd * a.dstate + 4 * q;
+    if constexpr (kVec) {
+      const float4 v = live[r] ? *reinterpret_cast<const float4*>(st) : make_float4(0, 0, 0, 0);
+      hs[r][0] = v.x; hs[r][1] = v.y; hs[r][2] = v.z; hs[r][3] = v.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hs[r][j] = (live[r] && 4 * q + j < a.dstate) ? st[j] : 0.0f;
     }
   }
-  // sum over the quad: (q0 + q1) + (q2 + q3)
-  acc += __shfl_xor(acc, 1, 4);
-  acc += __shfl_xor(acc, 2, 4);
 
-  if (!live) return;
-  if (a.vec_ok) {
-    *reinterpret_cast<float4*>(st) = make_float4(hs[0], hs[1], hs[2], hs[3]);
-  } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (4 * q + j < a.dstate) st[j] = hs[j];
-  }
-  if (q == 0) {
-    float yv = fmaf(a.D ? a.D[d] : 0.0f, xv, acc);
-    if (a.z) yv *= silu(IO::load1(static_cast<const IoT*>(a.z) + bdc));
-    IO::store1(static_cast<IoT*>(a.y) + bdc, yv);
+  for (int r = 0; r < kRows; ++r) {
+    const float x = xr[r] + bias;
+    const float dl = a.softplus ? softplus_log2e(x) : x * 1.4426950408889634f;   // Delta * log2e
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+      const float s = Bv[r][j] * (xv[r] * iA[j]);   // B u / A (zero for states past dstate)
+      hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+      acc = fmaf(Cv[r][j], hs[r][j], acc);
+    }
+    // sum over the quad: (q0 + q1) + (q2 + q3)
+    acc += __shfl_xor(acc, 1, 4);
+    acc += __shfl_xor(acc, 2, 4);
+    if (!live[r]) continue;
+    const int64_t bd = (b0 + r) * a.dim + d;
+    float* st = a.state + bd * a.dstate + 4 * q;
+    if constexpr (kVec) {
+      *reinterpret_cast<float4*>(st) = make_float4(hs[r][0], hs[r][1], hs[r][2], hs[r][3]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (4 * q + j < a.dstate) st[j] = hs[r][j];
+    }
+    if (q == 0) {
+      float yv = fmaf(Dd, xv[r], acc);
+      if (gz) yv *= silu(zv[r]);
+      IO::store1(static_cast<IoT*>(a.y) + bd, yv);
+    }
   }
 }
 
@@ -101,10 +147,15 @@ hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   a.state = s.state; a.x = s.x; a.dt = s.dt; a.A_log = s.A_log; a.B = s.B; a.C = s.C; a.D = s.D; a.z = s.z;
   a.bias = s.bias; a.y = s.y; a.batch = s.batch; a.dim = s.dim; a.dstate = (int)s.dstate;
   a.softplus = s.softplus;
-  a.vec_ok = (s.dstate == 16) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0);
-  const int64_t threads = s.batch * s.dim * 4;
-  const int64_t grid = (threads + 255) / 256;
-  hipLaunchKernelGGL(scan_step_kernel<IoT>, dim3((unsigned)grid), dim3(256), 0, stream, a);
+  const uintptr_t bc_mis = reinterpret_cast<uintptr_t>(s.B) | reinterpret_cast<uintptr_t>(s.C);
+  const bool vec = (s.dstate == 16) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0) &&
+                   ((bc_mis & (4 * sizeof(IoT) - 1)) == 0);
+  const int64_t threads = s.dim * 4;
+  const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((s.batch + kRows - 1) / kRows));
+  if (vec)
+    hipLaunchKernelGGL((scan_step_kernel<IoT, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((scan_step_kernel<IoT, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

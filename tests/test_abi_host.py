@@ -103,6 +103,7 @@ def test_step_validation_errors(lib):
     assert step(lib, io=2) == EDTYPE
     assert step(lib, batch=0) == ESHAPE
     assert step(lib, dstate=20) == EUNSUP
+    assert step(lib, batch=4 * 65535 + 1) == EUNSUP              # grid rows of four batch rows
     assert step(lib, state=P + 2) == EALIGN
     assert step(lib, x=P + 1) == EALIGN
 
