@@ -108,6 +108,28 @@ struct Io<uint16_t> {
     f[0] = bf16_lo(v.w.x); f[1] = bf16_hi(v.w.x);
     f[2] = bf16_lo(v.w.y); f[3] = bf16_hi(v.w.y);
   }
+  static __device__ __forceinline__ V4 from_f32(const float (&f)[4]) {
+    return V4{make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]))};
+  }
+  // 4 elements at byte offset off; stores past the descriptor are dropped.
+  static __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int off, const V4& v, bool vec) {
+    if (vec) {
+      __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, v.w),
+                                            r, off, 0, 0);
+      return;
+    }
+    const uint32_t w[2] = {v.w.x, v.w.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_buffer_store_b16((uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu)), r,
+                                            off + 2 * j, 0, 0);
+  }
+  static __device__ __forceinline__ void store_n(uint16_t* p, const V4& v, int n) {
+    const uint32_t w[2] = {v.w.x, v.w.y};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < n) p[j] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu));
+  }
   static __device__ __forceinline__ float load1(const uint16_t* p) { return __uint_as_float((uint32_t)(*p) << 16); }
   static __device__ __forceinline__ void store1(uint16_t* p, float f) {
     *p = (uint16_t)(pack_bf16x2(f, 0.0f) & 0xffffu);
@@ -179,6 +201,23 @@ struct Io<float> {
   static __device__ __forceinline__ void to_f32(const V4& v, float (&f)[4]) {
     f[0] = v.a.x; f[1] = v.a.y; f[2] = v.a.z; f[3] = v.a.w;
   }
+  static __device__ __forceinline__ V4 from_f32(const float (&f)[4]) { return V4{make_float4(f[0], f[1], f[2], f[3])}; }
+  static __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int off, const V4& v, bool vec) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    if (vec) {
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v.a), r, off, 0, 0);
+      return;
+    }
+    const float e[4] = {v.a.x, v.a.y, v.a.z, v.a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, e[j]), r, off + 4 * j, 0, 0);
+  }
+  static __device__ __forceinline__ void store_n(float* p, const V4& v, int n) {
+    const float e[4] = {v.a.x, v.a.y, v.a.z, v.a.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < n) p[j] = e[j];
+  }
   static __device__ __forceinline__ float load1(const float* p) { return *p; }
   static __device__ __forceinline__ void store1(float* p, float f) { *p = f; }
 };
@@ -235,6 +274,14 @@ __device__ __forceinline__ float dpp_bcast_fmac(float c, float a, float b) {
   static_assert(SRC >= 0 && SRC < 16, "row lane");
   asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(c) : "v"(a), "v"(b), "n"(SRC));
   return c;
+}
+
+// Sum of a value over lanes l and l ^ 32, for two values at once: lanes 0-31
+// return a[l] + a[l+32], lanes 32-63 return b[l-32] + b[l]
+// (v_permlane32_swap exchanges the upper half of a with the lower half of b).
+__device__ __forceinline__ float half_sum2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Barrier for LDS producer/consumer hand-off only: orders LDS accesses, does

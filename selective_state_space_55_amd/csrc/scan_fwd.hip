@@ -9,10 +9,12 @@
 // read from HBM once, discretized and scanned on chip, and only y (and the
 // final state) are written back.
 //
-// Mapping.  A workgroup owns 64 channels of one batch row (one channel per
-// lane) and NSPLIT waves; wave w holds states [w*NPW, (w+1)*NPW) of all 64
-// channels in VGPRs and scans them sequentially in time, tile by tile (T
-// tokens).  Three stages touch every tile:
+// Mapping.  A workgroup owns 64 channels of one batch row and all 16 states
+// of each, held in VGPRs and scanned sequentially in time, tile by tile (32
+// tokens).  Two layouts: (a) four states per lane, 4 waves: wave w holds
+// states 4w .. 4w+3 of all 64 channels, one channel per lane (one wave per
+// SIMD); (b) two states per lane, 8 waves (two per SIMD), described above
+// scan_fwd_h2_kernel.  Three stages touch every tile:
 //   stage    -- convert the tile's delta/u rows (16-byte buffer loads), compute
 //               Delta*log2e = softplus(delta+bias)*log2e once per token-channel,
 //               and put Delta, u and the tile's B/C values (shared by the 64
@@ -22,9 +24,9 @@
 //               through a DPP row_newbcast operand (lane 4j+t of each 16-lane
 //               row holds state j, token t); leave a partial readout over the
 //               wave's states in LDS;
-//   epilogue -- sum the NSPLIT partials, add D u, apply the SiLU gate, store y.
-// With one wave per SIMD nothing hides a wave's own stalls, so the stages are
-// software-pipelined across tiles inside one instruction stream: while a wave
+//   epilogue -- sum the four partials, add D u, apply the SiLU gate, store y.
+// A wave cannot hide its own stalls, so the stages are software-pipelined
+// across tiles inside one instruction stream: while a wave
 // scans tile k it also finishes tile k-1's epilogue and stages tile k+1, and
 // the global loads of tile k+2 are in flight.  That work sits inside the
 // scan's group loop, so the compiler interleaves it with the recurrence.  LDS
@@ -482,6 +484,321 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   }
 }
 
+// Two-states-per-lane layout: 8 waves (two per SIMD) over 64 channels.  Wave w
+// covers channels (w & 1) * 32 .. +31; its lanes l and l + 32 hold the same
+// channel and different state pairs, states (w >> 1) * 4 + (l >> 5) * 2 + {0, 1}.
+// The two halves' readouts are summed in the wave (v_permlane32_swap), so a
+// (token, channel) again has four partial readouts, one per wave pair.  With
+// two waves per SIMD one wave's LDS, memory and barrier waits overlap the
+// other's arithmetic.  Staging and the epilogue use 4-token pieces, one per
+// thread.
+struct LdsH2 {
+  static constexpr int kT = 32;
+  static constexpr int kRow = kT + kPad;
+  static constexpr int kG = kT / 4;
+  static constexpr int kDU = 2 * kCh * kRow;
+  static constexpr int kBC = 2 * kG * 16 * 8;
+  static constexpr int kPar = 2 * kCh;
+  static constexpr int kY = 2 * 4 * kCh * kRow;
+  static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
+};
+
+template <typename IoT, bool kAgg, bool kVec, bool kSp>
+__global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
+  using IO = Io<IoT>;
+  using V4 = typename IO::V4;
+  constexpr int NT = 512;
+  constexpr int T = LdsH2::kT;
+  constexpr int kRow = LdsH2::kRow;
+  constexpr int kG = LdsH2::kG;
+  constexpr int NP = 16;
+  constexpr int kPieces = kCh * T / 4;     // (channel, 4-token group) pieces of Delta/u/z per tile
+  static_assert(kPieces == NT, "one piece per thread");
+  constexpr int kBCPieces = 2 * NP * kG;   // (B or C, state, 4-token group) pieces per tile
+  static_assert(kBCPieces == 4 * 64, "B/C pieces fill waves 0-3");
+  constexpr int kEsz = (int)sizeof(IoT);
+  constexpr float kLog2e = 1.4426950408889634f;
+
+  extern __shared__ float smem[];
+  float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
+  float* ubuf = dbuf + LdsH2::kDU;         // [2][64][kRow]  u
+  float* bcs = ubuf + LdsH2::kDU;          // [2][kG][4 tokens][NP][B, C]
+  float* par = bcs + LdsH2::kBC;           // [2][64]        bias, D
+  float* ypart = par + LdsH2::kPar;        // [2][4][64][kRow] partial readouts (output pass only)
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;                // lane half: which state pair of the wave's four states
+  const int chw = (w & 1) * 32 + (lane & 31);   // the lane's channel within the workgroup
+  const int sp = w >> 1;                   // partial-readout slot of the wave pair
+  const int pc = tid / kG;                 // this thread's staging/epilogue piece: channel
+  const int pg = tid % kG;                 //   and 4-token group
+
+  int64_t wid = work_id(blockIdx.x, a.nwork);
+  const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
+  const int64_t kc = wid % nck;
+  wid /= nck;
+  const int64_t cg = wid % a.chgroups;
+  const int64_t b = wid / a.chgroups;
+  const int64_t d0 = cg * kCh;
+  const int64_t t_begin = kc * a.chunk_len;
+  const int64_t t_end = min(t_begin + a.chunk_len, a.seqlen);
+  const int64_t ntile = (t_end - t_begin + T - 1) / T;
+
+  const IoT* __restrict__ gu = static_cast<const IoT*>(a.u);
+  const IoT* __restrict__ gd = static_cast<const IoT*>(a.delta);
+  const IoT* __restrict__ gz = static_cast<const IoT*>(a.z);
+  const IoT* __restrict__ gB = static_cast<const IoT*>(a.B);
+  const IoT* __restrict__ gC = static_cast<const IoT*>(a.C);
+  IoT* __restrict__ gy = static_cast<IoT*>(a.y);
+
+  if (tid < kCh) {
+    const int64_t dd = d0 + tid;
+    const bool ok = dd < a.dim;
+    par[tid] = (ok && a.bias) ? a.bias[dd] : 0.0f;
+    par[kCh + tid] = (ok && a.D) ? a.D[dd] : 0.0f;
+  }
+
+  // ---- per-lane constants and state ----
+  const int64_t d = d0 + chw;
+  const bool ch_ok = d < a.dim;
+  const int64_t bd = b * a.dim + d;
+  float A[2], iA[2], h[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = sp * 4 + hf * 2 + j;
+    const bool valid = ch_ok && n < a.dstate;
+    const float An = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
+    A[j] = An;
+    iA[j] = valid ? 1.0f / An : 0.0f;
+    float hv = 0.0f;
+    if (!kAgg && valid) {
+      if (kc > 0)
+        hv = a.carry[(bd * a.nchunks + kc) * a.np + n];
+      else if (a.h0)
+        hv = a.h0[bd * a.dstate + n];
+    }
+    h[j] = hv;
+  }
+  float dsum_acc = 0.0f;
+  const bool gate_on = a.gated != 0;
+  const float gate_off = gate_on ? 0.0f : 1.0f;
+
+  // ---- buffer descriptors (as in the four-states layout) ----
+  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
+  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
+  const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
+  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(gate_on ? gz + row0 : gu + row0, gate_on ? nrec_ch : 0);
+  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
+  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
+
+  // B/C piece of threads 0..255: state bn, group bg; waves 0-1 load B, 2-3 load C
+  const int bn = tid % NP;
+  const int bg = (tid / NP) % kG;
+  const bool isB = w < 2;
+
+  struct Pf {
+    V4 d, u, z, bc;
+  };
+  struct Keep {
+    float u[4];
+    V4 z;
+  };
+
+  auto prefetch = [&](int64_t tile, Pf& p) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 4) * kEsz);
+    p.d = IO::buf_load4(rs_d, off, kVec);
+    p.u = IO::buf_load4(rs_u, off, kVec);
+    if constexpr (!kAgg) p.z = IO::buf_load4(rs_z, off, kVec);
+    if (w < 4) {
+      const int boff = (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz);
+      p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
+    }
+  };
+
+  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp, auto full_c) {
+    constexpr bool kFull = decltype(full_c)::value;
+    const int nv = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + pg * 4)));
+    float fd[4], fu[4];
+    IO::to_f32(p.d, fd);
+    IO::to_f32(p.u, fu);
+    const float bi = par[pc];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float x = fd[j] + bi;
+      const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
+      const bool ok = j < nv;   // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
+      fd[j] = ok ? dl : 0.0f;
+      fu[j] = ok ? fu[j] : 0.0f;
+    }
+    *reinterpret_cast<float4*>(dbuf + (buf * kCh + pc) * kRow + pg * 4) = make_float4(fd[0], fd[1], fd[2], fd[3]);
+    *reinterpret_cast<float4*>(ubuf + (buf * kCh + pc) * kRow + pg * 4) = make_float4(fu[0], fu[1], fu[2], fu[3]);
+    if constexpr (!kAgg) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kp.u[j] = fu[j];
+      kp.z = p.z;
+    }
+    if (w < 4) {
+      const int nvb = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + bg * 4)));
+      float f[4];
+      IO::to_f32(p.bc, f);
+      float* q = bcs + buf * kG * NP * 8 + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+    }
+  };
+
+  auto epi_read = [&](int ybuf, float4 (&yp)[4]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+      yp[s2] = *reinterpret_cast<const float4*>(ypart + ((ybuf * 4 + s2) * kCh + pc) * kRow + pg * 4);
+  };
+  auto epi_finish = [&](const float4 (&yp)[4], const Keep& kp, float (&yv)[4]) {
+    yv[0] = yp[0].x; yv[1] = yp[0].y; yv[2] = yp[0].z; yv[3] = yp[0].w;
+#pragma unroll
+    for (int s2 = 1; s2 < 4; ++s2) {
+      yv[0] += yp[s2].x; yv[1] += yp[s2].y; yv[2] += yp[s2].z; yv[3] += yp[s2].w;
+    }
+    const float Dd = par[kCh + pc];
+    float zf[4];
+    IO::to_f32(kp.z, zf);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
+  };
+  auto epi_store_full = [&](int64_t tile, const float (&yv)[4], __amdgpu_buffer_rsrc_t rs) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 4) * kEsz);
+    IO::buf_store4(rs, off, IO::from_f32(yv), kVec);
+  };
+  auto epi_store_tail = [&](int64_t tile, const float (&yv)[4]) {
+    const int64_t t0 = tile + pg * 4;
+    int nv = (int)max((int64_t)0, min((int64_t)4, t_end - t0));
+    if (d0 + pc >= a.dim) nv = 0;
+    IO::store_n(gy + (b * a.dim + d0 + pc) * a.seqlen + t0, IO::from_f32(yv), nv);
+  };
+
+  auto body = [&](int64_t k, auto P_c, Pf& pfCur, Pf& pfOther, Keep& kpOther) {
+    constexpr int P = decltype(P_c)::value;
+    const int64_t tile = t_begin + k * T;
+    const float* drow = dbuf + (P * kCh + chw) * kRow;
+    const float* urow = ubuf + (P * kCh + chw) * kRow;
+    const int sel = lane & 15;
+    // lane 4j + kk of each row holds (B, C) of token kk, state j of the row's pair
+    const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + sp * 4 + hf * 2 + ((sel >> 2) & 1)) * 2;
+    float* yrow = ypart + ((P * 4 + sp) * kCh + chw) * kRow + 2 * hf;
+
+    float4 dv = *reinterpret_cast<const float4*>(drow);
+    float4 uv = *reinterpret_cast<const float4*>(urow);
+    float2 bcv = *reinterpret_cast<const float2*>(bcl);
+    float4 yp[4];
+    if constexpr (!kAgg) epi_read(1 - P, yp);
+    prefetch(tile + 2 * T, pfCur);
+    const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
+
+    auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
+      constexpr int kk = decltype(kk_c)::value;
+      const float av0 = __builtin_amdgcn_exp2f(dl * A[0]);
+      const float av1 = __builtin_amdgcn_exp2f(dl * A[1]);
+      const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);        // s = B * u / A
+      const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
+      h[0] = fmaf(av0, h[0] + s0, -s0);                            // Abar (h + s) - s
+      h[1] = fmaf(av1, h[1] + s1, -s1);
+      if constexpr (!kAgg) return dpp_bcast_fmac<4 + kk>(dpp_bcast_mul<kk>(bq.y, h[0]), bq.y, h[1]);   // C . h
+      return 0.0f;
+    };
+
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      // next group's LDS reads first, then the four tokens in one scheduling
+      // region (a DPP result needs two instructions before its first use)
+      float4 dn = dv, un = uv;
+      float2 bcn = bcv;
+      if (g + 1 < kG) {
+        dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
+        un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
+        bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
+      const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
+      const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
+      const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
+      if constexpr (!kAgg) {
+        // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
+        *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
+      } else {
+        dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
+      }
+      if constexpr (!kAgg) {
+        if (g == 1) {
+          float yv[4];
+          epi_finish(yp, kpOther, yv);
+          epi_store_full(tile - T, yv, rs_y);
+        }
+      }
+      if (g == 2) {
+        if (tile + 2 * T <= t_end)
+          stage(tile + T, pfOther, 1 - P, kpOther, IntC<1>{});
+        else
+          stage(tile + T, pfOther, 1 - P, kpOther, IntC<0>{});
+      }
+      if (g + 1 < kG) {
+        dv = dn;
+        uv = un;
+        bcv = bcn;
+      }
+    }
+    lds_barrier();
+  };
+
+  auto last_epilogue = [&](int64_t k, int P, const Keep& kp) {
+    if constexpr (!kAgg) {
+      float4 yp[4];
+      epi_read(P, yp);
+      float yv[4];
+      epi_finish(yp, kp, yv);
+      epi_store_tail(t_begin + k * T, yv);
+    }
+  };
+
+  Pf pf0, pf1;
+  Keep kp0 = {}, kp1 = {};
+  prefetch(t_begin, pf0);
+  prefetch(t_begin + T, pf1);
+  __syncthreads();   // par[] visible
+  stage(t_begin, pf0, 0, kp0, IntC<0>{});
+  lds_barrier();
+  for (int64_t k = 0; k < ntile; k += 2) {
+    body(k, IntC<0>{}, pf0, pf1, kp1);
+    if (k + 1 >= ntile) {
+      last_epilogue(k, 0, kp0);
+      break;
+    }
+    body(k + 1, IntC<1>{}, pf1, pf0, kp0);
+    if (k + 2 >= ntile) {
+      last_epilogue(k + 1, 1, kp1);
+      break;
+    }
+  }
+
+  // ---- final state or chunk aggregate ----
+  if (ch_ok) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = sp * 4 + hf * 2 + j;
+      if (!kAgg) {
+        if (kc == a.nchunks - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
+      } else {
+        a.carry[(bd * a.nchunks + kc) * a.np + n] = h[j];
+      }
+    }
+    if (kAgg && sp == 0 && hf == 0) a.dsum[bd * a.nchunks + kc] = dsum_acc;
+  }
+}
+
 // Folds the chunk aggregates in time order; leaves in carry[.., k, ..] the
 // state entering chunk k.  One thread per (batch, channel, state).
 __global__ __launch_bounds__(256) void carry_kernel(float* __restrict__ carry, const float* __restrict__ dsum,
@@ -527,11 +844,22 @@ hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename IoT, bool kAgg>
+hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
+  auto kern = vec ? (k.softplus ? scan_fwd_h2_kernel<IoT, kAgg, true, true> : scan_fwd_h2_kernel<IoT, kAgg, true, false>)
+                  : (k.softplus ? scan_fwd_h2_kernel<IoT, kAgg, false, true> : scan_fwd_h2_kernel<IoT, kAgg, false, false>);
+  const size_t lds = sizeof(float) * LdsH2::floats(kAgg);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, k);
+  return hipGetLastError();
+}
+
 template <typename IoT>
 hipError_t dispatch_scan(const KArgs& k, const FwdPlan& p, bool agg, bool vec, int64_t grid, hipStream_t s) {
   if (p.npw == 4) return agg ? launch_scan<IoT, 4, 4, 32, true>(k, vec, grid, s)
                              : launch_scan<IoT, 4, 4, 32, false>(k, vec, grid, s);
-  return agg ? launch_scan<IoT, 2, 8, 16, true>(k, vec, grid, s) : launch_scan<IoT, 2, 8, 16, false>(k, vec, grid, s);
+  return agg ? launch_scan_h2<IoT, true>(k, vec, grid, s) : launch_scan_h2<IoT, false>(k, vec, grid, s);
 }
 
 template <typename IoT>
@@ -584,11 +912,12 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   if (npw_req != 0 && npw_req != 2 && npw_req != 4) return false;
   if (nchunks_req < 0) return false;
   (void)dstate;
-  // two layouts: 4 states per lane x 4 waves (32-token tiles) or 2 x 8 (16-token
-  // tiles); states past dstate are padding that contributes exactly zero
-  p->npw = npw_req ? npw_req : 4;
-  p->tile = p->npw == 4 ? 32 : 16;
-  p->nsplit = p->npw == 4 ? 4 : 8;
+  // two layouts, both with 32-token tiles: 4 states per lane x 4 waves, or 2
+  // states per lane x 8 waves; states past dstate are padding that contributes
+  // exactly zero
+  p->npw = npw_req ? npw_req : 2;   // two waves per SIMD hide more stalls (measured faster at all shapes)
+  p->tile = 32;
+  p->nsplit = p->npw == 4 ? 4 : 8;   // waves per workgroup
   p->np = 16;
   const int64_t T = p->tile;
   const int64_t tiles = (seqlen + T - 1) / T;

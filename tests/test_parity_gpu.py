@@ -97,14 +97,15 @@ def test_edge_shapes_vs_oracle(case, npw):
 
 @pytest.mark.parametrize("nchunks", [2, 5, 47])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_chunked_carry_vs_oracle(nchunks, io):
+@pytest.mark.parametrize("npw", [4, 2])
+def test_chunked_carry_vs_oracle(nchunks, io, npw):
     inp = forward_inputs(batch=2, dim=96, dstate=16, seqlen=3001, io=io, initial_state=True, seed=nchunks)
-    say(f"chunked nchunks={nchunks} io={io}")
-    y, fs = gpu_fwd(inp, nchunks=nchunks)
+    say(f"chunked nchunks={nchunks} io={io} npw={npw}")
+    y, fs = gpu_fwd(inp, nchunks=nchunks, npw=npw)
     yr, fsr = oracle_fwd(inp)
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])
-    y1, fs1 = gpu_fwd(inp, nchunks=1)
+    y1, fs1 = gpu_fwd(inp, nchunks=1, npw=npw)
     # same function, different rounding order only
     assert max_rel_err(y, y1.double()) <= (1e-5 if io == "f32" else 1e-2)
 
@@ -119,31 +120,33 @@ def test_seqlen_zero():
         assert torch.equal(fs, ref)
 
 
-def test_deterministic_repeat():
+@pytest.mark.parametrize("npw", [4, 2])
+def test_deterministic_repeat(npw):
     inp = forward_inputs(batch=2, dim=256, dstate=16, seqlen=777, io="bf16", initial_state=True)
-    say("determinism")
-    y1, f1 = gpu_fwd(inp)
-    y2, f2 = gpu_fwd(inp)
+    say(f"determinism npw={npw}")
+    y1, f1 = gpu_fwd(inp, npw=npw)
+    y2, f2 = gpu_fwd(inp, npw=npw)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
-    y3, f3 = gpu_fwd(inp, nchunks=6)
-    y4, f4 = gpu_fwd(inp, nchunks=6)
+    y3, f3 = gpu_fwd(inp, nchunks=6, npw=npw)
+    y4, f4 = gpu_fwd(inp, nchunks=6, npw=npw)
     assert torch.equal(y3, y4) and torch.equal(f3, f4)
 
 
 @pytest.mark.parametrize("k", [1, 100, 128, 333])
-def test_split_resume_bitexact(k):
+@pytest.mark.parametrize("npw", [4, 2])
+def test_split_resume_bitexact(k, npw):
     """scan(0..L) == scan(0..k) followed by scan(k..L) from the returned state (same arithmetic)."""
     L = 600
     inp = forward_inputs(batch=2, dim=80, dstate=16, seqlen=L, io="f32", initial_state=True, seed=k)
-    say(f"split at {k}")
-    y, fs = gpu_fwd(inp, nchunks=1)
+    say(f"split at {k} npw={npw}")
+    y, fs = gpu_fwd(inp, nchunks=1, npw=npw)
     first = {kk: (v[..., :k].contiguous() if v is not None and v.dim() == 3 and v.shape[-1] == L else v)
              for kk, v in inp.items()}
     second = {kk: (v[..., k:].contiguous() if v is not None and v.dim() == 3 and v.shape[-1] == L else v)
               for kk, v in inp.items()}
-    y1, f1 = gpu_fwd(first, nchunks=1)
+    y1, f1 = gpu_fwd(first, nchunks=1, npw=npw)
     second["initial_state"] = f1
-    y2, f2 = gpu_fwd(second, nchunks=1)
+    y2, f2 = gpu_fwd(second, nchunks=1, npw=npw)
     assert torch.equal(torch.cat([y1, y2], dim=-1), y)
     assert torch.equal(f2, fs)
 
