@@ -490,16 +490,19 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
 // The two halves' readouts are summed in the wave (v_permlane32_swap), so a
 // (token, channel) again has four partial readouts, one per wave pair.  With
 // two waves per SIMD one wave's LDS, memory and barrier waits overlap the
-// other's arithmetic.  Staging and the epilogue use 4-token pieces, one per
-// thread.
+// other's arithmetic.  Tiles are 64 tokens, so the 8 threads that load a
+// row's tile read one whole 128-byte line (bf16) with one instruction; staging
+// and the epilogue use one 8-token piece per thread.  The partial readouts
+// are single-buffered: the epilogue reads of tile k-1 finish (barrier) before
+// tile k's scan writes its partials.
 struct LdsH2 {
-  static constexpr int kT = 32;
+  static constexpr int kT = 64;
   static constexpr int kRow = kT + kPad;
   static constexpr int kG = kT / 4;
   static constexpr int kDU = 2 * kCh * kRow;
   static constexpr int kBC = 2 * kG * 16 * 8;
   static constexpr int kPar = 2 * kCh;
-  static constexpr int kY = 2 * 4 * kCh * kRow;
+  static constexpr int kY = 4 * kCh * kRow;
   static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
 };
 
@@ -507,15 +510,16 @@ template <typename IoT, bool kAgg, bool kVec, bool kSp>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
+  using V8 = typename IO::V8;
   constexpr int NT = 512;
   constexpr int T = LdsH2::kT;
   constexpr int kRow = LdsH2::kRow;
   constexpr int kG = LdsH2::kG;
   constexpr int NP = 16;
-  constexpr int kPieces = kCh * T / 4;     // (channel, 4-token group) pieces of Delta/u/z per tile
+  constexpr int kPieces = kCh * T / 8;     // (channel, 8-token) pieces of Delta/u/z per tile
   static_assert(kPieces == NT, "one piece per thread");
   constexpr int kBCPieces = 2 * NP * kG;   // (B or C, state, 4-token group) pieces per tile
-  static_assert(kBCPieces == 4 * 64, "B/C pieces fill waves 0-3");
+  static_assert(kBCPieces == NT, "one B/C piece per thread");
   constexpr int kEsz = (int)sizeof(IoT);
   constexpr float kLog2e = 1.4426950408889634f;
 
@@ -524,7 +528,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   float* ubuf = dbuf + LdsH2::kDU;         // [2][64][kRow]  u
   float* bcs = ubuf + LdsH2::kDU;          // [2][kG][4 tokens][NP][B, C]
   float* par = bcs + LdsH2::kBC;           // [2][64]        bias, D
-  float* ypart = par + LdsH2::kPar;        // [2][4][64][kRow] partial readouts (output pass only)
+  float* ypart = par + LdsH2::kPar;        // [4][64][kRow]  partial readouts (output pass only)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -532,8 +536,8 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const int hf = lane >> 5;                // lane half: which state pair of the wave's four states
   const int chw = (w & 1) * 32 + (lane & 31);   // the lane's channel within the workgroup
   const int sp = w >> 1;                   // partial-readout slot of the wave pair
-  const int pc = tid / kG;                 // this thread's staging/epilogue piece: channel
-  const int pg = tid % kG;                 //   and 4-token group
+  const int pc = tid / 8;                  // this thread's staging/epilogue piece: channel
+  const int pg = tid % 8;                  //   and tokens 8 pg .. 8 pg + 7
 
   int64_t wid = work_id(blockIdx.x, a.nwork);
   const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
@@ -596,53 +600,56 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
   const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
 
-  // B/C piece of threads 0..255: state bn, group bg; waves 0-1 load B, 2-3 load C
+  // B/C piece: state bn, 4-token group bg; waves 0-3 load B, 4-7 load C
   const int bn = tid % NP;
   const int bg = (tid / NP) % kG;
-  const bool isB = w < 2;
+  const bool isB = w < 4;
 
   struct Pf {
-    V4 d, u, z, bc;
+    V8 d, u, z;
+    V4 bc;
   };
   struct Keep {
-    float u[4];
-    V4 z;
+    float u[8];
+    V8 z;
   };
 
   auto prefetch = [&](int64_t tile, Pf& p) {
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 4) * kEsz);
-    p.d = IO::buf_load4(rs_d, off, kVec);
-    p.u = IO::buf_load4(rs_u, off, kVec);
-    if constexpr (!kAgg) p.z = IO::buf_load4(rs_z, off, kVec);
-    if (w < 4) {
-      const int boff = (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz);
-      p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
-    }
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    p.d = IO::buf_load8(rs_d, off, kVec);
+    p.u = IO::buf_load8(rs_u, off, kVec);
+    if constexpr (!kAgg) p.z = IO::buf_load8(rs_z, off, kVec);
+    const int boff = (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz);
+    p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
   };
 
   auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp, auto full_c) {
     constexpr bool kFull = decltype(full_c)::value;
-    const int nv = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + pg * 4)));
-    float fd[4], fu[4];
+    const int nv = kFull ? 8 : (int)max((int64_t)0, min((int64_t)8, t_end - (tile + pg * 8)));
+    float fd[8], fu[8];
     IO::to_f32(p.d, fd);
     IO::to_f32(p.u, fu);
     const float bi = par[pc];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 8; ++j) {
       const float x = fd[j] + bi;
       const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
       const bool ok = j < nv;   // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
       fd[j] = ok ? dl : 0.0f;
       fu[j] = ok ? fu[j] : 0.0f;
     }
-    *reinterpret_cast<float4*>(dbuf + (buf * kCh + pc) * kRow + pg * 4) = make_float4(fd[0], fd[1], fd[2], fd[3]);
-    *reinterpret_cast<float4*>(ubuf + (buf * kCh + pc) * kRow + pg * 4) = make_float4(fu[0], fu[1], fu[2], fu[3]);
+    float* dp = dbuf + (buf * kCh + pc) * kRow + pg * 8;
+    float* up = ubuf + (buf * kCh + pc) * kRow + pg * 8;
+    reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
+    reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
+    reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
+    reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
     if constexpr (!kAgg) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kp.u[j] = fu[j];
+      for (int j = 0; j < 8; ++j) kp.u[j] = fu[j];
       kp.z = p.z;
     }
-    if (w < 4) {
+    {
       const int nvb = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + bg * 4)));
       float f[4];
       IO::to_f32(p.bc, f);
@@ -652,30 +659,37 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     }
   };
 
-  auto epi_read = [&](int ybuf, float4 (&yp)[4]) {
+  auto epi_read = [&](float4 (&yp)[4][2]) {
 #pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2)
-      yp[s2] = *reinterpret_cast<const float4*>(ypart + ((ybuf * 4 + s2) * kCh + pc) * kRow + pg * 4);
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const float4* q = reinterpret_cast<const float4*>(ypart + (s2 * kCh + pc) * kRow + pg * 8);
+      yp[s2][0] = q[0];
+      yp[s2][1] = q[1];
+    }
   };
-  auto epi_finish = [&](const float4 (&yp)[4], const Keep& kp, float (&yv)[4]) {
-    yv[0] = yp[0].x; yv[1] = yp[0].y; yv[2] = yp[0].z; yv[3] = yp[0].w;
+  auto epi_finish = [&](const float4 (&yp)[4][2], const Keep& kp, float (&yv)[8]) {
 #pragma unroll
-    for (int s2 = 1; s2 < 4; ++s2) {
-      yv[0] += yp[s2].x; yv[1] += yp[s2].y; yv[2] += yp[s2].z; yv[3] += yp[s2].w;
+    for (int h2 = 0; h2 < 2; ++h2) {
+      float* o = yv + 4 * h2;
+      o[0] = yp[0][h2].x; o[1] = yp[0][h2].y; o[2] = yp[0][h2].z; o[3] = yp[0][h2].w;
+#pragma unroll
+      for (int s2 = 1; s2 < 4; ++s2) {
+        o[0] += yp[s2][h2].x; o[1] += yp[s2][h2].y; o[2] += yp[s2][h2].z; o[3] += yp[s2][h2].w;
+      }
     }
     const float Dd = par[kCh + pc];
-    float zf[4];
+    float zf[8];
     IO::to_f32(kp.z, zf);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
+    for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
   };
-  auto epi_store_full = [&](int64_t tile, const float (&yv)[4], __amdgpu_buffer_rsrc_t rs) {
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 4) * kEsz);
-    IO::buf_store4(rs, off, IO::from_f32(yv), kVec);
+  auto epi_store_full = [&](int64_t tile, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    IO::buf_store8(rs, off, IO::from_f32(yv), kVec);
   };
-  auto epi_store_tail = [&](int64_t tile, const float (&yv)[4]) {
-    const int64_t t0 = tile + pg * 4;
-    int nv = (int)max((int64_t)0, min((int64_t)4, t_end - t0));
+  auto epi_store_tail = [&](int64_t tile, const float (&yv)[8]) {
+    const int64_t t0 = tile + pg * 8;
+    int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
     if (d0 + pc >= a.dim) nv = 0;
     IO::store_n(gy + (b * a.dim + d0 + pc) * a.seqlen + t0, IO::from_f32(yv), nv);
   };
@@ -688,14 +702,18 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     const int sel = lane & 15;
     // lane 4j + kk of each row holds (B, C) of token kk, state j of the row's pair
     const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + sp * 4 + hf * 2 + ((sel >> 2) & 1)) * 2;
-    float* yrow = ypart + ((P * 4 + sp) * kCh + chw) * kRow + 2 * hf;
+    float* yrow = ypart + (sp * kCh + chw) * kRow + 2 * hf;
 
     float4 dv = *reinterpret_cast<const float4*>(drow);
     float4 uv = *reinterpret_cast<const float4*>(urow);
     float2 bcv = *reinterpret_cast<const float2*>(bcl);
-    float4 yp[4];
-    if constexpr (!kAgg) epi_read(1 - P, yp);
     prefetch(tile + 2 * T, pfCur);
+    float4 yp[4][2];
+    if constexpr (!kAgg) {
+      // tile k-1's partials must be read by every wave before tile k's are written
+      epi_read(yp);
+      lds_barrier();
+    }
     const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
 
     auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
@@ -734,7 +752,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       }
       if constexpr (!kAgg) {
         if (g == 1) {
-          float yv[4];
+          float yv[8];
           epi_finish(yp, kpOther, yv);
           epi_store_full(tile - T, yv, rs_y);
         }
@@ -754,11 +772,11 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     lds_barrier();
   };
 
-  auto last_epilogue = [&](int64_t k, int P, const Keep& kp) {
+  auto last_epilogue = [&](int64_t k, const Keep& kp) {
     if constexpr (!kAgg) {
-      float4 yp[4];
-      epi_read(P, yp);
-      float yv[4];
+      float4 yp[4][2];
+      epi_read(yp);
+      float yv[8];
       epi_finish(yp, kp, yv);
       epi_store_tail(t_begin + k * T, yv);
     }
@@ -774,12 +792,12 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   for (int64_t k = 0; k < ntile; k += 2) {
     body(k, IntC<0>{}, pf0, pf1, kp1);
     if (k + 1 >= ntile) {
-      last_epilogue(k, 0, kp0);
+      last_epilogue(k, kp0);
       break;
     }
     body(k + 1, IntC<1>{}, pf1, pf0, kp0);
     if (k + 2 >= ntile) {
-      last_epilogue(k + 1, 1, kp1);
+      last_epilogue(k + 1, kp1);
       break;
     }
   }
@@ -912,11 +930,11 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   if (npw_req != 0 && npw_req != 2 && npw_req != 4) return false;
   if (nchunks_req < 0) return false;
   (void)dstate;
-  // two layouts, both with 32-token tiles: 4 states per lane x 4 waves, or 2
-  // states per lane x 8 waves; states past dstate are padding that contributes
-  // exactly zero
+  // two layouts: 4 states per lane x 4 waves with 32-token tiles, or 2 states
+  // per lane x 8 waves with 64-token tiles; states past dstate are padding that
+  // contributes exactly zero
   p->npw = npw_req ? npw_req : 2;   // two waves per SIMD hide more stalls (measured faster at all shapes)
-  p->tile = 32;
+  p->tile = p->npw == 4 ? 32 : 64;
   p->nsplit = p->npw == 4 ? 4 : 8;   // waves per workgroup
   p->np = 16;
   const int64_t T = p->tile;
