@@ -34,30 +34,33 @@ VALU_SLOTS_PEAK = 256 * 4 * 16 * 2.4e9
 SLOTS_PER_TCN = 8.0
 SLOTS_PER_TC_GATED = 16.0
 SLOTS_PER_TC_UNGATED = 8.0
+CSRC = os.path.join(ROOT, "selective_state_space_55_amd", "csrc")
+# committed rocprofv3 traffic summaries and the kernel sources they were taken on
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "selective_state_space_55_amd", "csrc", f)
-                  for f in ("scan_fwd.hip", "io.h", "internal.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "io.h", "internal.h")]
+PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traffic.txt")
+KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h", "internal.h")]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (sources or KERNEL_SOURCES):
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(nbytes_alg: float):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
+def read_traffic(nbytes_alg: float, profile: str = PROFILE_TRAFFIC, sources=None):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary,
     if it was taken on the current kernel source; else None."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+    if not os.path.exists(profile):
         return None
     kv = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(profile):
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != kernel_source_hash():
+    if kv.get("source_sha256_16") != kernel_source_hash(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -155,7 +158,7 @@ def bench_step(args, c) -> int:
                    "batch": c.batch, "d_inner": c.dim, "d_state": c.dstate, "graph_matches_eager": graph_ok},
         "roofline": {"bound": "hbm", "achieved": round(alg / (dev_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(alg / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": read_traffic(alg, PROFILE_TRAFFIC_STEP, KERNEL_SOURCES_STEP)},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -165,8 +168,10 @@ def bench_step(args, c) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the GPU's clock settles only after ~100 ms of sustained load, so the
+    # defaults warm up for a few hundred steps before timing
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", type=int, default=2, help="workload index (forward configs 0-3)")
     ap.add_argument("--npw", type=int, default=0, help="states per wave (0 = library default)")
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
@@ -276,15 +281,31 @@ def main() -> int:
         import oracle
 
         cores = host_cores()
-        # bounded sample: batch row 0 of the same workload (all channels, full length)
-        sub = {k: (v[:1] if (v is not None and k in ("u", "delta", "z", "B", "C", "initial_state")) else v)
-               for k, v in inp.items()}
+        # bounded sample of the same workload: whole batch rows and channels, full length,
+        # at most ~4e9 (token, channel, state) updates (a few seconds on 16 host cores)
+        budget = 4e9
+        nch = int(min(d, max(1, budget // (L * n))))
+        nrow = int(min(b, max(1, budget // (nch * L * n))))
+        per_ch = ("u", "delta", "z")
+        sub = {}
+        for k, v in inp.items():
+            if v is None:
+                sub[k] = None
+            elif k in per_ch:
+                sub[k] = v[:nrow, :nch]
+            elif k in ("B", "C"):
+                sub[k] = v[:nrow]
+            elif k in ("A_log", "D", "delta_bias"):
+                sub[k] = v[:nch]
+            else:
+                sub[k] = v
         c0 = time.perf_counter()
         oracle.scan_fwd(sub["u"], sub["delta"], sub["A_log"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
                         delta_bias=sub["delta_bias"], nthreads=cores)
         cs = time.perf_counter() - c0
-        cpu = {"value": round(d * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
-               "sample": f"batch row 0 of the workload: 1 x {d} channels x {L} tokens x {n} states, fp64, "
+        whole = "the whole workload" if (nrow == b and nch == d) else "a sample of the workload"
+        cpu = {"value": round(nrow * nch * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"{whole}: {nrow} batch rows x {nch} channels x {L} tokens x {n} states, fp64, "
                          f"{cs:.2f} s wall incl. fp64 widening of inputs"}
 
     out = {
