@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the selective scan (forward pass and single-token step).
+"""fp64 CPU oracle for the selective scan (forward pass, single-token step, backward pass).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The product path (the
@@ -46,6 +46,8 @@ def _bind(path: str):
     lib.oracle_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_scan_step.restype = ctypes.c_int
     lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
+    lib.oracle_scan_bwd.restype = ctypes.c_int
+    lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -147,6 +149,42 @@ def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softpl
     return y, st
 
 
+def scan_bwd(u, delta, A_log, B, C, dy, D=None, z=None, delta_bias=None, initial_state=None,
+             d_final_state=None, delta_softplus: bool = True, nthreads: int = 0, _lib_override=None) -> dict:
+    """Gradients of the selective-scan forward in fp64, given dL/dy (and optionally
+    dL/d final_state).  Returns a dict with du, ddelta, dA_log, dB, dC (always) and dD,
+    dz, ddelta_bias, d_initial_state (when D, z, delta_bias, initial_state are given)."""
+    u = _f64(u)
+    if u.ndim != 3:
+        raise ValueError("oracle: u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    delta = _f64(delta, (batch, dim, L))
+    B = _f64(B, (batch, dstate, L))
+    C = _f64(C, (batch, dstate, L))
+    dy = _f64(dy, (batch, dim, L))
+    D = _f64(D, (dim,))
+    z = _f64(z, (batch, dim, L))
+    delta_bias = _f64(delta_bias, (dim,))
+    initial_state = _f64(initial_state, (batch, dim, dstate))
+    d_final_state = _f64(d_final_state, (batch, dim, dstate))
+    g = {"du": np.empty((batch, dim, L)), "ddelta": np.empty((batch, dim, L)), "dA_log": np.empty((dim, dstate)),
+         "dB": np.empty((batch, dstate, L)), "dC": np.empty((batch, dstate, L))}
+    g["dD"] = np.empty((dim,)) if D is not None else None
+    g["dz"] = np.empty((batch, dim, L)) if z is not None else None
+    g["ddelta_bias"] = np.empty((dim,)) if delta_bias is not None else None
+    g["d_initial_state"] = np.empty((batch, dim, dstate)) if initial_state is not None else None
+    rc = (_lib_override or _load()).oracle_scan_bwd(
+        _ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+        _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]),
+        _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
+        _ptr(g["d_initial_state"]), batch, dim, dstate, L, int(bool(delta_softplus)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd returned {rc}")
+    return g
+
+
 class Variant:
     """The same wrapper bound to another build of scan_oracle.c (used by the
     tests that plant a mistake in a copy of the oracle and check that the pins
@@ -160,6 +198,9 @@ class Variant:
 
     def scan_step(self, *a, **k):
         return scan_step(*a, _lib_override=self._lib, **k)
+
+    def scan_bwd(self, *a, **k):
+        return scan_bwd(*a, _lib_override=self._lib, **k)
 
 
 def build_variant(src_text: str, out_dir: str, name: str) -> "Variant":

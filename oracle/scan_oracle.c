@@ -153,3 +153,170 @@ int oracle_max_threads(void) {
   return 1;
 #endif
 }
+
+/*
+ * Backward pass (gradients of a scalar loss through the forward above, given
+ * dL/dy and optionally dL/d(final_state)).
+ *
+ * The pages describe the backward pass only as a strategy -- the fused kernel
+ * keeps no intermediate states and recomputes them when gradients are needed
+ * (State space models and Mamba, jonathanding.github.io, Parallel Scan; Mamba
+ * notes, awesome.papernotes.org, 设计 2).  What it must compute is the
+ * gradient of the function defined above, obtained here by the chain rule
+ * through each step, in reverse time order.  With ytil_t = sum_n C h_t + D u
+ * the pre-gate output, s(z) = SiLU(z) and lam_t[n] = dL/dh_t[n] (total):
+ *
+ *   dytil_t  = dy_t s(z_t);      dz_t = dy_t ytil_t s'(z_t),
+ *              s'(z) = sigma(z) (1 + z (1 - sigma(z)))
+ *   lam_t    = dytil_t C_t + Abar_{t+1} lam_{t+1}   (lam_{L-1} adds dL/d(final))
+ *   dC_t[n] += dytil_t h_t[n]                       (summed over channels)
+ *   dB_t[n] += lam_t[n] u_t (Abar_t[n] - 1) / A[n]  (Delta u_t if A = 0)
+ *   du_t     = dytil_t D + sum_n lam_t[n] Bbar_t[n]
+ *   dDelta_t = sum_n lam_t[n] Abar_t[n] (A[n] h_{t-1}[n] + B_t[n] u_t)
+ *   dA[n]   += lam_t[n] (Delta_t Abar_t h_{t-1} + u_t B_t (Delta_t Abar_t A - (Abar_t - 1)) / A^2)
+ *              (limit Delta^2 B u / 2 if A = 0)
+ *   dA_log   = dA * A                               (A = -exp(A_log))
+ *   ddelta_t = dDelta_t sigma(delta_t + bias)       (dDelta_t without softplus)
+ *   dbias   += ddelta_t;  dD += dytil_t u_t;  d(initial state) = Abar_0 lam_0
+ *
+ * Outputs (float64, row-major like the inputs): du, ddelta, dz (batch, dim, L);
+ * dB, dC (batch, dstate, L); dA_log (dim, dstate); dD, ddelta_bias (dim);
+ * d_initial_state (batch, dim, dstate).  dz, dD, ddelta_bias and
+ * d_initial_state may be NULL (not computed); d_final_state may be NULL (0).
+ * The forward states are kept in full, per (batch, channel), for the reverse
+ * sweep.  Channels run in parallel within a batch row; the sums over channels
+ * (dB, dC) go through per-thread buffers added in a fixed order, and the sums
+ * over batch rows (dA_log, dD, ddelta_bias) run over batch rows in order.
+ */
+static double oracle_sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, const double* B,
+                    const double* C, const double* D, const double* z, const double* delta_bias,
+                    const double* initial_state, const double* dy, const double* d_final_state,
+                    double* du, double* ddelta, double* dA_log, double* dB, double* dC, double* dD,
+                    double* dz, double* ddelta_bias, double* d_initial_state, int64_t batch, int64_t dim,
+                    int64_t dstate, int64_t seqlen, int delta_softplus, int nthreads) {
+  if (!u || !delta || !A_log || !B || !C || !dy || !du || !ddelta || !dA_log || !dB || !dC) return 1;
+  if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  const int nthr = omp_get_max_threads();
+#else
+  (void)nthreads;
+  const int nthr = 1;
+#endif
+  const int64_t N = dstate, L = seqlen;
+  for (int64_t i = 0; i < dim * N; ++i) dA_log[i] = 0.0;
+  if (dD)
+    for (int64_t i = 0; i < dim; ++i) dD[i] = 0.0;
+  if (ddelta_bias)
+    for (int64_t i = 0; i < dim; ++i) ddelta_bias[i] = 0.0;
+  double* part = (double*)calloc((size_t)nthr * (size_t)(2 * N * L + 1), sizeof(double));   /* per-thread dB, dC */
+  double* pdim = (double*)calloc((size_t)dim * (size_t)(N + 2), sizeof(double));            /* per-channel sums of one row */
+  if (!part || !pdim) {
+    free(part);
+    free(pdim);
+    return 3;
+  }
+  for (int64_t b = 0; b < batch; ++b) {
+    for (int64_t i = 0; i < (int64_t)nthr * (2 * N * L + 1); ++i) part[i] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < dim; ++d) {
+#ifdef _OPENMP
+      const int tid = omp_get_thread_num();
+#else
+      const int tid = 0;
+#endif
+      double* pB = part + (int64_t)tid * (2 * N * L + 1);
+      double* pC = pB + N * L;
+      const int64_t bd = b * dim + d;
+      const int64_t row = bd * L, bcrow = b * N * L;
+      double* A = (double*)malloc(sizeof(double) * (size_t)(N * (L + 3) + 2 * L));
+      double* H = A + N;             /* H[(t + 1) N + n] = h_t[n], H[n] = initial state */
+      double* lam = H + N * (L + 1); /* running lam_t[n] */
+      double* Dl = lam + N;          /* Delta_t */
+      double* yt = Dl + L;           /* ytil_t */
+      const double bias = delta_bias ? delta_bias[d] : 0.0;
+      const double Dd = D ? D[d] : 0.0;
+      for (int64_t n = 0; n < N; ++n) {
+        A[n] = -exp(A_log[d * N + n]);
+        H[n] = initial_state ? initial_state[bd * N + n] : 0.0;
+      }
+      /* forward, keeping every state */
+      for (int64_t t = 0; t < L; ++t) {
+        const double x = delta[row + t] + bias;
+        const double Delta = delta_softplus ? oracle_softplus(x) : x;
+        Dl[t] = Delta;
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double dA = Delta * A[n];
+          const double Bn = B[bcrow + n * L + t];
+          const double Bbar = (A[n] != 0.0) ? expm1(dA) / A[n] * Bn : Delta * Bn;
+          const double hn = exp(dA) * H[t * N + n] + Bbar * u[row + t];
+          H[(t + 1) * N + n] = hn;
+          acc += C[bcrow + n * L + t] * hn;
+        }
+        yt[t] = acc + Dd * u[row + t];
+      }
+      /* reverse */
+      double dDacc = 0.0, dbacc = 0.0;
+      double* dAn = pdim + d * (N + 2);
+      for (int64_t n = 0; n < N; ++n) lam[n] = d_final_state ? d_final_state[bd * N + n] : 0.0;
+      for (int64_t t = L - 1; t >= 0; --t) {
+        const double ut = u[row + t], Delta = Dl[t];
+        double dyt = dy[row + t];
+        if (z) {
+          const double zz = z[row + t], sg = oracle_sigmoid(zz);
+          if (dz) dz[row + t] = dyt * yt[t] * sg * (1.0 + zz * (1.0 - sg));
+          dyt *= zz * sg;
+        } else if (dz) {
+          dz[row + t] = 0.0;
+        }
+        dDacc += dyt * ut;
+        double dut = dyt * Dd, dDelta = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+          const double Bn = B[bcrow + n * L + t], Cn = C[bcrow + n * L + t];
+          const double dA = Delta * A[n], Abar = exp(dA), em1 = expm1(dA);
+          const double hprev = H[t * N + n];
+          /* lam currently holds Abar_{t+1} lam_{t+1} (or dL/d final state) */
+          const double l = lam[n] + dyt * Cn;
+          pC[n * L + t] += dyt * H[(t + 1) * N + n];
+          const double bq = (A[n] != 0.0) ? em1 / A[n] : Delta;     /* Bbar / B */
+          pB[n * L + t] += l * ut * bq;
+          dut += l * bq * Bn;
+          dDelta += l * Abar * (A[n] * hprev + Bn * ut);
+          const double dbq = (A[n] != 0.0) ? (Delta * Abar * A[n] - em1) / (A[n] * A[n]) : 0.5 * Delta * Delta;
+          dAn[n] += l * (Delta * Abar * hprev + ut * Bn * dbq);
+          lam[n] = Abar * l;
+        }
+        du[row + t] = dut;
+        const double dd = delta_softplus ? dDelta * oracle_sigmoid(delta[row + t] + bias) : dDelta;
+        ddelta[row + t] = dd;
+        dbacc += dd;
+      }
+      if (d_initial_state)
+        for (int64_t n = 0; n < N; ++n) d_initial_state[bd * N + n] = lam[n];
+      dAn[N] += dDacc;
+      dAn[N + 1] += dbacc;
+      free(A);
+    }
+    /* channel sums for this batch row, threads added in order */
+    for (int64_t i = 0; i < N * L; ++i) {
+      double sb = 0.0, sc = 0.0;
+      for (int k = 0; k < nthr; ++k) {
+        sb += part[(int64_t)k * (2 * N * L + 1) + i];
+        sc += part[(int64_t)k * (2 * N * L + 1) + N * L + i];
+      }
+      dB[b * N * L + i] = sb;
+      dC[b * N * L + i] = sc;
+    }
+  }
+  for (int64_t d = 0; d < dim; ++d) {
+    for (int64_t n = 0; n < N; ++n) dA_log[d * N + n] = pdim[d * (N + 2) + n] * (-exp(A_log[d * N + n]));
+    if (dD) dD[d] = pdim[d * (N + 2) + N];
+    if (ddelta_bias) ddelta_bias[d] = pdim[d * (N + 2) + N + 1];
+  }
+  free(part);
+  free(pdim);
+  return 0;
+}
