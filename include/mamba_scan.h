@@ -145,6 +145,41 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
                     const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,
                     int64_t dim, int64_t dstate, int io_dtype, void* stream);
 
+/*
+ * Backward pass: gradients of a scalar loss through mamba_scan_fwd, given the
+ * gradient of its outputs (dy and, optionally, the final state).  Inputs are
+ * those of the forward call (same meaning, layout and NULL conventions).  The
+ * pages describe the backward pass as recomputing the states instead of
+ * storing them (State space models and Mamba, Parallel Scan; Mamba notes,
+ * 设计 2); the gradients are the chain rule through the forward recurrence.
+ *
+ *   dy               (batch, dim, seqlen) io    dL/dy
+ *   d_final_state    (batch, dim, dstate) f32   dL/d(final state), NULL means 0
+ * Outputs (written in full; no accumulation into existing values):
+ *   du, ddelta       (batch, dim, seqlen) io
+ *   dA_log           (dim, dstate)        f32
+ *   dB, dC           (batch, dstate, seqlen) io
+ *   dD               (dim)                f32   NULL: not computed
+ *   dz               (batch, dim, seqlen) io    required iff z is given
+ *   ddelta_bias      (dim)                f32   NULL: not computed
+ *   d_initial_state  (batch, dim, dstate) f32   NULL: not computed
+ *   workspace        at least mamba_scan_bwd_workspace_size(...) bytes, 256-byte aligned:
+ *                    the state entering every 32-token tile (batch x ceil(seqlen/32) x 16 x
+ *                    dim fp32) and per-channel-group / per-row partial sums
+ * Sizes and limits as for mamba_scan_fwd.  Sums over channels (dB, dC) and
+ * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so
+ * repeated calls give identical results.
+ */
+int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                   const void* dy, const float* d_final_state, void* du, void* ddelta, float* dA_log, void* dB,
+                   void* dC, float* dD, void* dz, float* ddelta_bias, float* d_initial_state, int64_t batch,
+                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int delta_softplus, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mamba_scan_bwd needs (0 only for seqlen == 0); (size_t)-1 for rejected sizes. */
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* mamba_scan_status_str(int status);
 

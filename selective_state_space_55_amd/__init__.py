@@ -25,7 +25,8 @@ STATUS = {
 }
 EXPORTED = (
     "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
-    "mamba_scan_step", "mamba_scan_status_str", "mamba_scan_abi_version",
+    "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_status_str",
+    "mamba_scan_abi_version",
 )
 
 _lib = None
@@ -56,6 +57,10 @@ def load_library():
     lib.mamba_scan_fwd_workspace_size_ex.argtypes = [I64] * 4 + [I, I64, I]
     lib.mamba_scan_step.restype = I
     lib.mamba_scan_step.argtypes = [P] * 9 + [I, P] + [I64] * 3 + [I, P]
+    lib.mamba_scan_bwd.restype = I
+    lib.mamba_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [I, I, P, SZ, P]
+    lib.mamba_scan_bwd_workspace_size.restype = SZ
+    lib.mamba_scan_bwd_workspace_size.argtypes = [I64] * 4 + [I]
     lib.mamba_scan_status_str.restype = ctypes.c_char_p
     lib.mamba_scan_status_str.argtypes = [I]
     lib.mamba_scan_abi_version.restype = I
@@ -203,3 +208,69 @@ def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: tor
                              _stream(dev, stream))
     _check("mamba_scan_step", rc)
     return y
+
+
+def bwd_workspace_size(batch: int, dim: int, dstate: int, seqlen: int, io_dtype: int = BF16) -> int:
+    n = load_library().mamba_scan_bwd_workspace_size(batch, dim, dstate, seqlen, io_dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("mamba_scan_bwd_workspace_size: sizes rejected")
+    return int(n)
+
+
+def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+             delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+             d_final_state: Optional[torch.Tensor] = None, delta_softplus: bool = True, *,
+             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Selective-scan backward.  Inputs as in scan_fwd plus dy (batch, dim, L) in the io dtype and
+    d_final_state (batch, dim, dstate) float32.  Returns a dict of gradients: du, ddelta, dz, dB, dC in
+    the io dtype; dA_log, dD, ddelta_bias, d_initial_state in float32 (dD, dz, ddelta_bias and
+    d_initial_state only when D, z, delta_bias and initial_state are given)."""
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_bwd needs device tensors (HIP)")
+    io = _io_dtype(u)
+    iot = u.dtype
+    dstate = A_log.shape[-1] if A_log.dim() == 2 else -1
+    _req("u", u, (batch, dim, L), iot, dev)
+    _req("delta", delta, (batch, dim, L), iot, dev)
+    _req("A_log", A_log, (dim, dstate), torch.float32, dev)
+    _req("B", B, (batch, dstate, L), iot, dev)
+    _req("C", C, (batch, dstate, L), iot, dev)
+    _req("dy", dy, (batch, dim, L), iot, dev)
+    _req("D", D, (dim,), torch.float32, dev)
+    _req("z", z, (batch, dim, L), iot, dev)
+    _req("delta_bias", delta_bias, (dim,), torch.float32, dev)
+    _req("initial_state", initial_state, (batch, dim, dstate), torch.float32, dev)
+    _req("d_final_state", d_final_state, (batch, dim, dstate), torch.float32, dev)
+    f32 = torch.float32
+    g = {"du": torch.empty((batch, dim, L), dtype=iot, device=dev),
+         "ddelta": torch.empty((batch, dim, L), dtype=iot, device=dev),
+         "dA_log": torch.empty((dim, dstate), dtype=f32, device=dev),
+         "dB": torch.empty((batch, dstate, L), dtype=iot, device=dev),
+         "dC": torch.empty((batch, dstate, L), dtype=iot, device=dev),
+         "dD": torch.empty((dim,), dtype=f32, device=dev) if D is not None else None,
+         "dz": torch.empty((batch, dim, L), dtype=iot, device=dev) if z is not None else None,
+         "ddelta_bias": torch.empty((dim,), dtype=f32, device=dev) if delta_bias is not None else None,
+         "d_initial_state": torch.empty((batch, dim, dstate), dtype=f32, device=dev)
+         if initial_state is not None else None}
+    need = bwd_workspace_size(batch, dim, dstate, L, io)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if ws is not None:
+        base = ws.data_ptr()
+        off = (-base) % 256
+        ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, ws.numel() * ws.element_size() - off)
+    rc = lib.mamba_scan_bwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(g["du"]),
+                            _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                            _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["d_initial_state"]), batch, dim, dstate,
+                            L, io, int(bool(delta_softplus)), ws_ptr, ws_bytes, _stream(dev, stream))
+    _check("mamba_scan_bwd", rc)
+    return g

@@ -133,4 +133,47 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
 }
 
+size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype) {
+  if (check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
+  mscan::BwdPlan p;
+  mscan::make_bwd_plan(batch, dim, seqlen, &p);
+  return p.ws_total;
+}
+
+int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                   const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                   const void* dy, const float* d_final_state, void* du, void* ddelta, float* dA_log, void* dB,
+                   void* dC, float* dD, void* dz, float* ddelta_bias, float* d_initial_state, int64_t batch,
+                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int delta_softplus, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (!A_log || !dA_log) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && z && !dz) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {u, delta, B, C, z, dy, du, ddelta, dB, dC, dz};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, delta_bias, initial_state, d_final_state, dA_log, dD, ddelta_bias, d_initial_state};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::BwdPlan plan;
+  mscan::make_bwd_plan(batch, dim, seqlen, &plan);
+  if (plan.ws_total > 0) {
+    if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
+  }
+  mscan::BwdArgs a{};
+  a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_state; a.dy = dy; a.dfs = d_final_state;
+  a.du = du; a.ddelta = ddelta; a.dA_log = dA_log; a.dB = dB; a.dC = dC; a.dD = dD; a.dz = dz;
+  a.dbias = ddelta_bias; a.dh0 = d_initial_state;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = delta_softplus != 0;
+  a.workspace = workspace;
+  hipError_t e = mscan::launch_bwd(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
 }  // extern "C"

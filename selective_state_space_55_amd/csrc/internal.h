@@ -63,4 +63,48 @@ struct StepArgs {
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 
+// Backward pass: workspace layout (byte offsets, each part 256-byte aligned).
+struct BwdPlan {
+  int64_t ntile;      // 32-token tiles
+  int64_t chgroups;   // 64-channel groups
+  size_t off_ckpt;    // (batch, ntile, 16, dim) fp32: state before each tile
+  size_t off_dB;      // (batch, chgroups, 16, seqlen) fp32: per-group partial dB
+  size_t off_dC;      // same for dC
+  size_t off_dA;      // (batch, dim, 16) fp32: per-row partial dA_log
+  size_t off_dD;      // (batch, dim) fp32: per-row partial dD
+  size_t off_dbias;   // (batch, dim) fp32: per-row partial ddelta_bias
+  size_t ws_total;
+};
+
+void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* plan);
+
+struct BwdArgs {
+  const void* u;
+  const void* delta;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* h0;
+  const void* dy;
+  const float* dfs;   // gradient of the final state, or NULL
+  void* du;
+  void* ddelta;
+  float* dA_log;
+  void* dB;
+  void* dC;
+  float* dD;          // NULL: not written
+  void* dz;           // written iff z is given
+  float* dbias;       // NULL: not written
+  float* dh0;         // NULL: not written
+  int64_t batch, dim, dstate, seqlen;
+  int io_bf16;
+  int softplus;
+  void* workspace;
+};
+
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t stream);
+
 }  // namespace mscan

@@ -1,0 +1,755 @@
+// scan_bwd.hip -- backward pass of the selective scan on gfx950 (CDNA4).
+//
+// Gradients of the forward pass (see scan_fwd.hip for the method) with respect
+// to u, delta, A_log, B, C, D, z, delta_bias and the initial state, given
+// dL/dy and optionally dL/d(final state).  Like the pages' fused kernel, no
+// per-token state is kept from the forward pass: states are recomputed on chip
+// (State space models and Mamba, jonathanding.github.io, Parallel Scan: the
+// backward pass recomputes intermediate states instead of storing them; Mamba
+// notes, awesome.papernotes.org, 设计 2).  The gradient formulas are the chain
+// rule through one step of the recurrence, run in reverse time:
+//   lam_t   = dytil_t C_t + Abar_{t+1} lam_{t+1}     (dytil = dy SiLU(z))
+//   dDelta_t = sum_n lam Abar (A h_{t-1} + B u),  du_t = dytil D + sum_n lam Bbar,
+//   dB_t = sum_d lam u (Abar-1)/A,  dC_t = sum_d dytil h_t,
+//   dA = sum_t lam (Delta Abar (h_{t-1} + s) - s (Abar-1)/A)  with s = B u / A.
+//
+// Three launches:
+//   1. checkpoint pass: the forward recurrence (no readout) writes the state
+//      entering every 32-token tile to the workspace;
+//   2. gradient pass, tiles in reverse order.  A workgroup owns 64 channels of
+//      one batch row (one per lane) and 4 waves; wave w holds states 4w..4w+3.
+//      Per tile: stage Delta, u, B, C in LDS; rerun the forward from the tile's
+//      checkpoint for the readout (four partial sums per token-channel, summed
+//      with D u into the pre-gate output, giving dz and dytil) and the states
+//      at four 8-token boundaries; then per 8-token sub-chunk in reverse,
+//      rerun those 8 tokens keeping every state and decay in registers and
+//      sweep them backwards carrying Abar lam.  dDelta and du are partial over
+//      a wave's states and summed across waves through LDS; dB and dC are
+//      summed over the 64 lanes (channels) by a reduce-scatter in registers
+//      and written per channel group to the workspace;
+//   3. reductions of the per-group and per-row partials in a fixed order
+//      (deterministic results).
+#include <algorithm>
+
+#include "internal.h"
+#include "io.h"
+
+namespace mscan {
+namespace {
+
+constexpr int kCh = 64;          // channels per workgroup, one per lane
+constexpr int kT = 32;           // tokens per tile
+constexpr int kRow = kT + 4;     // LDS row of one channel (floats)
+constexpr int kG = kT / 4;       // 4-token groups per tile
+constexpr int kSub = 8;          // tokens per recompute sub-chunk
+constexpr int NP = 16;           // padded states
+constexpr int NPW = 4;           // states per lane
+constexpr int NT = 256;          // threads per workgroup
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct BArgs {
+  const void* u;
+  const void* delta;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* bias;
+  const float* h0;
+  const void* dy;
+  const float* dfs;
+  void* du;
+  void* ddelta;
+  void* dz;
+  float* dh0;
+  float* ckpt;
+  float* wsB;
+  float* wsC;
+  float* wsA;
+  float* wsD;
+  float* wsBias;
+  int64_t dim, seqlen, chgroups, ntile, nwork;
+  int dstate, softplus;
+};
+
+// XCD-aware placement, as in the forward kernels.
+__device__ __forceinline__ int64_t work_id(int64_t bid, int64_t nwork) {
+  if ((nwork & 7) != 0) return bid;
+  return (bid & 7) * (nwork >> 3) + (bid >> 3);
+}
+
+// v from the lane given by a DPP control (compile-time), via the builtin so the
+// compiler inserts the hazard waits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+constexpr int kRowRor8 = 0x128;        // lane (l + 8) mod 16 of the row  == l ^ 8
+constexpr int kRowHalfMirror = 0x141;  // lane 7 - (l mod 8) of the half-row: flips bits 0-2
+constexpr int kQuad2301 = 0x4E;        // l ^ 2
+constexpr int kQuad1032 = 0xB1;        // l ^ 1
+
+// Rows 0, 2 return a[l] + a[l ^ 16]; rows 1, 3 return b[l] + b[l ^ 16].
+__device__ __forceinline__ float row_pair_sum2(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 64 lanes of a wave of 32 values held by every lane: a
+// reduce-scatter (each stage halves the values per lane and doubles the lanes
+// summed), then one all-reduce step.  Afterwards lanes 2i and 2i+1 hold the
+// total of value i.
+__device__ __forceinline__ float reduce64(const float (&v)[32], int lane) {
+  float w16[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w16[i] = half_sum2(v[i], v[i + 16]);        // lanes l, l ^ 32
+  float w8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w8[i] = row_pair_sum2(w16[i], w16[i + 8]);   // lanes l, l ^ 16
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0;
+  float w4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                                            // lanes l, l ^ 8
+    const float keep = b3 ? w8[i + 4] : w8[i];
+    const float send = b3 ? w8[i] : w8[i + 4];
+    w4[i] = keep + dpp_mov<kRowRor8>(send);
+  }
+  float w2[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {                                            // lanes l, l ^ 7
+    const float keep = b2 ? w4[i + 2] : w4[i];
+    const float send = b2 ? w4[i] : w4[i + 2];
+    w2[i] = keep + dpp_mov<kRowHalfMirror>(send);
+  }
+  const float keep = b1 ? w2[1] : w2[0];                                   // lanes l, l ^ 2
+  const float send = b1 ? w2[0] : w2[1];
+  const float r = keep + dpp_mov<kQuad2301>(send);
+  return r + dpp_mov<kQuad1032>(r);                                        // lanes l, l ^ 1
+}
+
+// The same for 16 values per lane: afterwards lanes 4i .. 4i+3 hold the total of value i.
+__device__ __forceinline__ float reduce64_16(const float (&v)[16], int lane) {
+  float w8[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w8[i] = half_sum2(v[i], v[i + 8]);          // lanes l, l ^ 32
+  float w4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w4[i] = row_pair_sum2(w8[i], w8[i + 4]);    // lanes l, l ^ 16
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+  float w2[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {                                           // lanes l, l ^ 8
+    const float keep = b3 ? w4[i + 2] : w4[i];
+    const float send = b3 ? w4[i] : w4[i + 2];
+    w2[i] = keep + dpp_mov<kRowRor8>(send);
+  }
+  const float keep = b2 ? w2[1] : w2[0];                                  // lanes l, l ^ 7
+  const float send = b2 ? w2[0] : w2[1];
+  float r = keep + dpp_mov<kRowHalfMirror>(send);
+  r += dpp_mov<kQuad2301>(r);                                             // lanes l, l ^ 2
+  return r + dpp_mov<kQuad1032>(r);                                       // lanes l, l ^ 1
+}
+
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
+// ---------------------------------------------------------------- checkpoints
+template <typename IoT, bool kVec, bool kSp>
+__global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
+  using IO = Io<IoT>;
+  using V8 = typename IO::V8;
+  using V4 = typename IO::V4;
+  constexpr int kEsz = (int)sizeof(IoT);
+  __shared__ float dbuf[kCh * kRow];
+  __shared__ float ubuf[kCh * kRow];
+  __shared__ float bbuf[kG * 4 * NP];   // [group][token][state]
+  __shared__ float par[kCh];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t wid = work_id(blockIdx.x, a.nwork);
+  const int64_t cg = wid % a.chgroups;
+  const int64_t b = wid / a.chgroups;
+  const int64_t d0 = cg * kCh;
+  const int64_t d = d0 + lane;
+  const bool ch_ok = d < a.dim;
+  const int64_t bd = b * a.dim + d;
+  if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
+
+  float A[NPW], iA[NPW], h[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int n = w * NPW + j;
+    const bool valid = ch_ok && n < a.dstate;
+    A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
+    iA[j] = valid ? 1.0f / A[j] : 0.0f;
+    h[j] = (valid && a.h0) ? a.h0[bd * a.dstate + n] : 0.0f;
+  }
+
+  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
+  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
+  const IoT* gu = static_cast<const IoT*>(a.u);
+  const IoT* gd = static_cast<const IoT*>(a.delta);
+  const IoT* gB = static_cast<const IoT*>(a.B);
+  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, (int)((int64_t)a.dstate * a.seqlen * kEsz));
+  const int pc = tid / 4, pg = tid % 4;            // piece: channel, tokens 8 pg .. 8 pg + 7
+  const int bn = tid % NP, bg = (tid / NP) % kG;   // B piece (threads 0..127): state, 4-token group
+  const int sel = lane & 15;
+  __syncthreads();
+
+  for (int64_t k = 0; k < a.ntile; ++k) {
+    const int64_t tile = k * kT;
+    if (ch_ok) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) a.ckpt[((b * a.ntile + k) * NP + w * NPW + j) * a.dim + d] = h[j];
+    }
+    if (k + 1 == a.ntile) break;   // the last tile's entering state is all the gradient pass needs
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    const V8 rd = IO::buf_load8(rs_d, off, kVec);
+    const V8 ru = IO::buf_load8(rs_u, off, kVec);
+    V4 rb{};
+    if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    // every tile but the last is full
+    float fd[8], fu[8];
+    IO::to_f32(rd, fd);
+    IO::to_f32(ru, fu);
+    const float bi = par[pc];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = fd[j] + bi;
+      fd[j] = kSp ? softplus_log2e(x) : x * kLog2e;
+    }
+    float* dp = dbuf + pc * kRow + pg * 8;
+    float* up = ubuf + pc * kRow + pg * 8;
+    reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
+    reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
+    reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
+    reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+    if (w < 2) {
+      float f[4];
+      IO::to_f32(rb, f);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) bbuf[(bg * 4 + kk) * NP + bn] = f[kk];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int g = 0; g < kG; ++g) {
+      const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * g);
+      const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * g);
+      const float bq = bbuf[(g * 4 + (sel & 3)) * NP + w * NPW + (sel >> 2)];   // lane 4j+kk: state j, token kk
+      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+      const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+      static_for<4>([&](auto kk_c) {
+        constexpr int kk = decltype(kk_c)::value;
+        static_for<NPW>([&](auto j_c) {
+          constexpr int j = decltype(j_c)::value;
+          const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
+          const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk] * iA[j]);
+          h[j] = fmaf(av, h[j] + sv, -sv);
+        });
+      });
+    }
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------- gradients
+struct LdsB {
+  static constexpr int kDU = kCh * kRow;            // Delta*log2e, u, dytil: one tile each
+  static constexpr int kBC = kG * 4 * NP * 2;       // (B, C) pairs
+  static constexpr int kPart = 4 * kCh * kRow;      // per-wave partials (readout, then dDelta), and du
+  static constexpr int kHB = 4 * 4 * kCh * NPW;     // state entering each 8-token sub-chunk, per wave and lane
+  static constexpr int kFloats = 3 * kDU + kBC + 2 * kPart + kHB + 2 * kCh;
+};
+
+template <typename IoT, bool kVec, bool kSp, bool kGate>
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
+  using IO = Io<IoT>;
+  using V8 = typename IO::V8;
+  using V4 = typename IO::V4;
+  constexpr int kEsz = (int)sizeof(IoT);
+  extern __shared__ float smem[];
+  float* dbuf = smem;                     // [64][kRow] Delta*log2e
+  float* ubuf = dbuf + LdsB::kDU;         // [64][kRow] u
+  float* ybuf = ubuf + LdsB::kDU;         // [64][kRow] dytil
+  float* bcs = ybuf + LdsB::kDU;          // [kG][4 tokens][NP][B, C]
+  float* part1 = bcs + LdsB::kBC;         // [4][64][kRow] readout partials, then dDelta partials
+  float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
+  float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][4 waves][64 lanes][4 states]
+  float* par = hbuf + LdsB::kHB;          // [2][64] bias, D
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t wid = work_id(blockIdx.x, a.nwork);
+  const int64_t cg = wid % a.chgroups;
+  const int64_t b = wid / a.chgroups;
+  const int64_t d0 = cg * kCh;
+  const int64_t d = d0 + lane;
+  const bool ch_ok = d < a.dim;
+  const int64_t bd = b * a.dim + d;
+  if (tid < kCh) {
+    const bool ok = d0 + tid < a.dim;
+    par[tid] = (ok && a.bias) ? a.bias[d0 + tid] : 0.0f;
+    par[kCh + tid] = (ok && a.D) ? a.D[d0 + tid] : 0.0f;
+  }
+
+  float A[NPW], iA[NPW], g[NPW], X[NPW], Y[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int n = w * NPW + j;
+    const bool valid = ch_ok && n < a.dstate;
+    A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
+    iA[j] = valid ? 1.0f / A[j] : 0.0f;
+    g[j] = (valid && a.dfs) ? a.dfs[bd * a.dstate + n] : 0.0f;   // Abar_{t+1} lam_{t+1}, from the end
+    X[j] = 0.0f;
+    Y[j] = 0.0f;
+  }
+
+  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
+  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
+  const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
+  const IoT* gu = static_cast<const IoT*>(a.u);
+  const IoT* gd = static_cast<const IoT*>(a.delta);
+  const IoT* gz = static_cast<const IoT*>(a.z);
+  const IoT* gdy = static_cast<const IoT*>(a.dy);
+  const IoT* gB = static_cast<const IoT*>(a.B);
+  const IoT* gC = static_cast<const IoT*>(a.C);
+  IoT* gdu = static_cast<IoT*>(a.du);
+  IoT* gdd = static_cast<IoT*>(a.ddelta);
+  IoT* gdz = static_cast<IoT*>(a.dz);
+  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_dy = make_rsrc(gdy + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(kGate ? gz + row0 : gu + row0, kGate ? nrec_ch : 0);
+  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
+  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
+  const __amdgpu_buffer_rsrc_t rs_du = make_rsrc(gdu + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_dd = make_rsrc(gdd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_dz = make_rsrc(kGate ? gdz + row0 : gdu + row0, kGate ? nrec_ch : 0);
+
+  const int pc = tid / 4, pg = tid % 4;              // piece: channel, tokens 8 pg .. 8 pg + 7
+  const int bn = tid % NP, bg = (tid / NP) % kG;     // (B or C) piece: state, 4-token group
+  const bool isB = w < 2;                            // waves 0-1 stage B, 2-3 stage C
+  const int sel = lane & 15;
+  const float* bcl = bcs + ((sel & 3) * NP + w * NPW + (sel >> 2)) * 2;   // lane 4j+kk: state j, token kk
+  float dD_acc = 0.0f, db_acc = 0.0f;
+  __syncthreads();
+
+  for (int64_t k = a.ntile - 1; k >= 0; --k) {
+    const int64_t tile = k * kT;
+    const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
+    const bool full = nv_tile == kT;
+    const int nv = max(0, min(8, nv_tile - pg * 8));   // valid tokens of this thread's piece
+
+    // ---- load and stage ----
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    const V8 rd = IO::buf_load8(rs_d, off, kVec);
+    const V8 ru = IO::buf_load8(rs_u, off, kVec);
+    const V8 rdy = IO::buf_load8(rs_dy, off, kVec);
+    V8 rz = IO::zero();
+    if constexpr (kGate) rz = IO::buf_load8(rs_z, off, kVec);
+    const V4 rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    float h0t[NPW];   // state entering the tile
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) h0t[j] = ch_ok ? a.ckpt[((b * a.ntile + k) * NP + w * NPW + j) * a.dim + d] : 0.0f;
+
+    float fd[8], fu[8], fdy[8], fz[8], xs[8];
+    IO::to_f32(rd, fd);
+    IO::to_f32(ru, fu);
+    IO::to_f32(rdy, fdy);
+    IO::to_f32(rz, fz);
+    {
+      const float bi = par[pc];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bool ok = j < nv;   // tokens past the end: Delta = 0, u = 0, dy = 0 change nothing
+        xs[j] = fd[j] + bi;
+        const float dl = kSp ? softplus_log2e(xs[j]) : xs[j] * kLog2e;
+        fd[j] = ok ? dl : 0.0f;
+        fu[j] = ok ? fu[j] : 0.0f;
+        fdy[j] = ok ? fdy[j] : 0.0f;
+      }
+      float* dp = dbuf + pc * kRow + pg * 8;
+      float* up = ubuf + pc * kRow + pg * 8;
+      reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
+      reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
+      reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
+      reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+      const int nvb = max(0, min(4, nv_tile - bg * 4));
+      float f[4];
+      IO::to_f32(rbc, f);
+      float* q = bcs + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+    }
+    lds_barrier();
+
+    // ---- forward over the tile: readout partials and sub-chunk boundary states ----
+    {
+      float h[NPW];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) h[j] = h0t[j];
+#pragma unroll
+      for (int gq = 0; gq < kG; ++gq) {
+        if (gq % 2 == 0)   // state entering sub-chunk gq / 2
+          *reinterpret_cast<float4*>(hbuf + (((gq / 2) * 4 + w) * kCh + lane) * NPW) = make_float4(h[0], h[1], h[2], h[3]);
+        const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * gq);
+        const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * gq);
+        const float2 bq = *reinterpret_cast<const float2*>(bcl + gq * NP * 8);
+        const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+        const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+        float ys[4];
+        static_for<4>([&](auto kk_c) {
+          constexpr int kk = decltype(kk_c)::value;
+          float acc = 0.0f;
+          static_for<NPW>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
+            const float sv = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk] * iA[j]);
+            h[j] = fmaf(av, h[j] + sv, -sv);
+            acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
+          });
+          ys[kk] = acc;
+        });
+        *reinterpret_cast<float4*>(part1 + (w * kCh + lane) * kRow + 4 * gq) = make_float4(ys[0], ys[1], ys[2], ys[3]);
+      }
+    }
+    lds_barrier();
+
+    // ---- piece owners: pre-gate output, dz, dytil ----
+    {
+      float dyt[8];
+      const float Dd = par[kCh + pc];
+      float ysum[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ysum[j] = 0.0f;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const float4* q = reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * 8);
+        const float4 q0 = q[0], q1 = q[1];
+        ysum[0] += q0.x; ysum[1] += q0.y; ysum[2] += q0.z; ysum[3] += q0.w;
+        ysum[4] += q1.x; ysum[5] += q1.y; ysum[6] += q1.z; ysum[7] += q1.w;
+      }
+      float dzv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float ytil = fmaf(Dd, fu[j], ysum[j]);
+        if constexpr (kGate) {
+          const float sg = sigmoidf_fast(fz[j]);
+          dzv[j] = fdy[j] * ytil * sg * fmaf(fz[j], 1.0f - sg, 1.0f);
+          dyt[j] = fdy[j] * fz[j] * sg;
+        } else {
+          dzv[j] = 0.0f;
+          dyt[j] = fdy[j];
+        }
+        dD_acc = fmaf(dyt[j], fu[j], dD_acc);
+      }
+      if constexpr (kGate) {
+        if (full)
+          IO::buf_store8(rs_dz, off, IO::from_f32(dzv), kVec);
+        else if (d0 + pc < a.dim)
+          IO::store_n(gdz + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(dzv), nv);
+      }
+      float* yp = ybuf + pc * kRow + pg * 8;
+      reinterpret_cast<float4*>(yp)[0] = make_float4(dyt[0], dyt[1], dyt[2], dyt[3]);
+      reinterpret_cast<float4*>(yp)[1] = make_float4(dyt[4], dyt[5], dyt[6], dyt[7]);
+    }
+    lds_barrier();
+
+    // ---- reverse sweep, one 8-token sub-chunk at a time ----
+#pragma unroll 1
+    for (int s = 3; s >= 0; --s) {
+      float hb[NPW], hh[kSub][NPW], ha[kSub][NPW];
+      {
+        const float4 q = *reinterpret_cast<const float4*>(hbuf + ((s * 4 + w) * kCh + lane) * NPW);
+        hb[0] = q.x; hb[1] = q.y; hb[2] = q.z; hb[3] = q.w;
+        float h[NPW] = {hb[0], hb[1], hb[2], hb[3]};
+        static_for<2>([&](auto gq_c) {
+          constexpr int gq = decltype(gq_c)::value;
+          const int tg = 2 * s + gq;
+          const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * tg);
+          const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * tg);
+          const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
+          const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+          const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+          static_for<4>([&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            static_for<NPW>([&](auto j_c) {
+              constexpr int j = decltype(j_c)::value;
+              const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
+              const float sv = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk] * iA[j]);
+              h[j] = fmaf(av, h[j] + sv, -sv);
+              hh[4 * gq + kk][j] = h[j];
+              ha[4 * gq + kk][j] = av;
+            });
+          });
+        });
+      }
+      static_for<2>([&](auto gr_c) {
+        constexpr int gq = 1 - decltype(gr_c)::value;   // the sub-chunk's two 4-token groups, later first
+        const int tg = 2 * s + gq;
+        const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * tg);
+        const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * tg);
+        const float4 yv = *reinterpret_cast<const float4*>(ybuf + lane * kRow + 4 * tg);
+        const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
+        const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+        const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+        const float dys[4] = {yv.x, yv.y, yv.z, yv.w};
+        float dDp[4], dup[4], dBv[16], dCv[16];   // dBv, dCv: value j*4 + kk
+        static_for<4>([&](auto kr_c) {
+          constexpr int kk = 3 - decltype(kr_c)::value;   // tokens in reverse
+          constexpr int t = 4 * gq + kk;                  // token within the sub-chunk
+          const float Delta = dls[kk] * kLn2;
+          float dD_p = 0.0f, du_p = 0.0f;
+          static_for<NPW>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            constexpr int src = 4 * j + kk;               // lane of the row holding (state j, token kk)
+            const float hp = (t > 0) ? hh[t > 0 ? t - 1 : 0][j] : hb[j];
+            const float av = ha[t][j];
+            const float l = dpp_bcast_fmac<src>(g[j], bq.y, dys[kk]);   // lam_t = dytil C + Abar lam_{t+1}
+            g[j] = av * l;                                              // Abar_t lam_t, for token t-1
+            const float v = uus[kk] * iA[j];
+            const float sv = dpp_bcast_mul<src>(bq.x, v);               // s = B u / A
+            const float t1 = hp + sv;
+            dD_p = fmaf(g[j] * A[j], t1, dD_p);                         // lam Abar (A h_{t-1} + B u)
+            const float am1 = av - 1.0f;
+            const float la = l * am1;
+            dBv[j * 4 + kk] = la * v;                                   // lam u (Abar - 1) / A
+            du_p = fmaf(la, dpp_bcast_mul<src>(bq.x, iA[j]), du_p);     // lam Bbar / u
+            X[j] = fmaf(l * (Delta * av), t1, X[j]);
+            Y[j] = fmaf(l * sv, am1, Y[j]);
+            dCv[j * 4 + kk] = dys[kk] * hh[t][j];                       // dytil h_t
+          });
+          dDp[kk] = dD_p;
+          dup[kk] = du_p;
+        });
+        *reinterpret_cast<float4*>(part1 + (w * kCh + lane) * kRow + 4 * tg) = make_float4(dDp[0], dDp[1], dDp[2], dDp[3]);
+        *reinterpret_cast<float4*>(part2 + (w * kCh + lane) * kRow + 4 * tg) = make_float4(dup[0], dup[1], dup[2], dup[3]);
+        // sums over the 64 channels: lanes 4i .. 4i+3 hold value i = j*4 + kk
+        const float rB = reduce64_16(dBv, lane);
+        const float rC = reduce64_16(dCv, lane);
+        const int i = lane >> 2;
+        const int64_t tt = tile + 4 * tg + (i & 3);
+        if ((lane & 3) == 0 && tt < a.seqlen) {
+          const int64_t o = ((b * a.chgroups + cg) * NP + w * NPW + (i >> 2)) * a.seqlen + tt;
+          a.wsB[o] = rB;
+          a.wsC[o] = rC;
+        }
+      });
+    }
+    lds_barrier();
+
+    // ---- piece owners: ddelta, du ----
+    {
+      const float Dd = par[kCh + pc];
+      float dyt[8];
+      {
+        const float4* q = reinterpret_cast<const float4*>(ybuf + pc * kRow + pg * 8);
+        const float4 q0 = q[0], q1 = q[1];
+        dyt[0] = q0.x; dyt[1] = q0.y; dyt[2] = q0.z; dyt[3] = q0.w;
+        dyt[4] = q1.x; dyt[5] = q1.y; dyt[6] = q1.z; dyt[7] = q1.w;
+      }
+      float sd[8], su[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        sd[j] = 0.0f;
+        su[j] = 0.0f;
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const float4* q1 = reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * 8);
+        const float4* q2 = reinterpret_cast<const float4*>(part2 + (s2 * kCh + pc) * kRow + pg * 8);
+        const float4 a0 = q1[0], a1 = q1[1], c0 = q2[0], c1 = q2[1];
+        sd[0] += a0.x; sd[1] += a0.y; sd[2] += a0.z; sd[3] += a0.w;
+        sd[4] += a1.x; sd[5] += a1.y; sd[6] += a1.z; sd[7] += a1.w;
+        su[0] += c0.x; su[1] += c0.y; su[2] += c0.z; su[3] += c0.w;
+        su[4] += c1.x; su[5] += c1.y; su[6] += c1.z; su[7] += c1.w;
+      }
+      float ddv[8], duv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ddv[j] = kSp ? sd[j] * sigmoidf_fast(xs[j]) : sd[j];
+        duv[j] = fmaf(dyt[j], Dd, su[j]);
+        db_acc += (j < nv) ? ddv[j] : 0.0f;
+      }
+      if (full) {
+        IO::buf_store8(rs_dd, off, IO::from_f32(ddv), kVec);
+        IO::buf_store8(rs_du, off, IO::from_f32(duv), kVec);
+      } else if (d0 + pc < a.dim) {
+        IO::store_n(gdd + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(ddv), nv);
+        IO::store_n(gdu + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(duv), nv);
+      }
+    }
+    lds_barrier();
+  }
+
+  // ---- per-row partials of the parameter gradients, gradient of the initial state ----
+  if (ch_ok) {
+#pragma unroll
+    for (int j = 0; j < NPW; ++j) {
+      const int n = w * NPW + j;
+      a.wsA[bd * NP + n] = (X[j] - iA[j] * Y[j]) * A[j];   // dA * dA/dA_log
+      if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
+    }
+  }
+  dD_acc += __shfl_xor(dD_acc, 1, 4);
+  dD_acc += __shfl_xor(dD_acc, 2, 4);
+  db_acc += __shfl_xor(db_acc, 1, 4);
+  db_acc += __shfl_xor(db_acc, 2, 4);
+  if (pg == 0 && d0 + pc < a.dim) {
+    a.wsD[b * a.dim + d0 + pc] = dD_acc;
+    a.wsBias[b * a.dim + d0 + pc] = db_acc;
+  }
+}
+
+// ---------------------------------------------------------------- reductions
+template <typename IoT>
+__global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ wsB, const float* __restrict__ wsC,
+                                                            IoT* __restrict__ dB, IoT* __restrict__ dC, int64_t batch,
+                                                            int64_t chgroups, int dstate, int64_t seqlen) {
+  using IO = Io<IoT>;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= batch * dstate * seqlen) return;
+  const int64_t b = i / ((int64_t)dstate * seqlen);
+  const int64_t r = i % ((int64_t)dstate * seqlen);
+  const int64_t n = r / seqlen, t = r % seqlen;
+  float sb = 0.0f, sc = 0.0f;
+  for (int64_t c = 0; c < chgroups; ++c) {
+    const int64_t o = ((b * chgroups + c) * NP + n) * seqlen + t;
+    sb += wsB[o];
+    sc += wsC[o];
+  }
+  IO::store1(dB + i, sb);
+  IO::store1(dC + i, sc);
+}
+
+__global__ __launch_bounds__(256) void bwd_reduce_param_kernel(const float* __restrict__ wsA, const float* __restrict__ wsD,
+                                                               const float* __restrict__ wsBias, float* __restrict__ dA_log,
+                                                               float* __restrict__ dD, float* __restrict__ dbias,
+                                                               int64_t batch, int64_t dim, int dstate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < dim * dstate) {
+    const int64_t d = i / dstate, n = i % dstate;
+    float s = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) s += wsA[(b * dim + d) * NP + n];
+    dA_log[i] = s;
+  }
+  if (i < dim) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sd += wsD[b * dim + i];
+      sb += wsBias[b * dim + i];
+    }
+    if (dD) dD[i] = sd;
+    if (dbias) dbias[i] = sb;
+  }
+}
+
+// seqlen == 0: parameter gradients are zero, the initial state's is the final state's.
+__global__ __launch_bounds__(256) void bwd_empty_kernel(float* dA_log, float* dD, float* dbias, float* dh0,
+                                                        const float* dfs, int64_t dim, int dstate, int64_t nstate) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < dim * dstate) dA_log[i] = 0.0f;
+  if (i < dim) {
+    if (dD) dD[i] = 0.0f;
+    if (dbias) dbias[i] = 0.0f;
+  }
+  if (dh0 && i < nstate) dh0[i] = dfs ? dfs[i] : 0.0f;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename IoT>
+hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
+  if (a.seqlen == 0) {
+    const int64_t n = std::max<int64_t>(a.dim * a.dstate, a.batch * a.dim * a.dstate);
+    hipLaunchKernelGGL(bwd_empty_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.dA_log, a.dD, a.dbias,
+                       a.dh0, a.dfs, a.dim, (int)a.dstate, a.batch * a.dim * a.dstate);
+    return hipGetLastError();
+  }
+  char* ws = static_cast<char*>(a.workspace);
+  BArgs k{};
+  k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
+  k.h0 = a.h0; k.dy = a.dy; k.dfs = a.dfs; k.du = a.du; k.ddelta = a.ddelta; k.dz = a.dz; k.dh0 = a.dh0;
+  k.ckpt = reinterpret_cast<float*>(ws + p.off_ckpt);
+  k.wsB = reinterpret_cast<float*>(ws + p.off_dB);
+  k.wsC = reinterpret_cast<float*>(ws + p.off_dC);
+  k.wsA = reinterpret_cast<float*>(ws + p.off_dA);
+  k.wsD = reinterpret_cast<float*>(ws + p.off_dD);
+  k.wsBias = reinterpret_cast<float*>(ws + p.off_dbias);
+  k.dim = a.dim; k.seqlen = a.seqlen; k.chgroups = p.chgroups; k.ntile = p.ntile;
+  k.nwork = a.batch * p.chgroups;
+  k.dstate = (int)a.dstate; k.softplus = a.softplus;
+  const size_t esz = sizeof(IoT);
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a.u) | reinterpret_cast<uintptr_t>(a.delta) |
+                        reinterpret_cast<uintptr_t>(a.dy) | reinterpret_cast<uintptr_t>(a.z) |
+                        reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C) |
+                        reinterpret_cast<uintptr_t>(a.du) | reinterpret_cast<uintptr_t>(a.ddelta) |
+                        reinterpret_cast<uintptr_t>(a.dz);
+  const bool vec = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
+  const dim3 grid((unsigned)k.nwork);
+
+  auto ck = vec ? (a.softplus ? bwd_ckpt_kernel<IoT, true, true> : bwd_ckpt_kernel<IoT, true, false>)
+                : (a.softplus ? bwd_ckpt_kernel<IoT, false, true> : bwd_ckpt_kernel<IoT, false, false>);
+  hipLaunchKernelGGL(ck, grid, dim3(NT), 0, s, k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const bool gate = a.z != nullptr;
+  auto gk = vec ? (a.softplus ? (gate ? bwd_grad_kernel<IoT, true, true, true> : bwd_grad_kernel<IoT, true, true, false>)
+                              : (gate ? bwd_grad_kernel<IoT, true, false, true> : bwd_grad_kernel<IoT, true, false, false>))
+                : (a.softplus ? (gate ? bwd_grad_kernel<IoT, false, true, true> : bwd_grad_kernel<IoT, false, true, false>)
+                              : (gate ? bwd_grad_kernel<IoT, false, false, true> : bwd_grad_kernel<IoT, false, false, false>));
+  const size_t lds = sizeof(float) * LdsB::kFloats;
+  e = hipFuncSetAttribute((const void*)gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(gk, grid, dim3(NT), lds, s, k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int64_t nbc = a.batch * a.dstate * a.seqlen;
+  hipLaunchKernelGGL(bwd_reduce_bc_kernel<IoT>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, k.wsB, k.wsC,
+                     static_cast<IoT*>(a.dB), static_cast<IoT*>(a.dC), a.batch, p.chgroups, (int)a.dstate, a.seqlen);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t np = std::max<int64_t>(a.dim * a.dstate, a.dim);
+  hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, k.wsA, k.wsD,
+                     k.wsBias, a.dA_log, a.dD, a.dbias, a.batch, a.dim, (int)a.dstate);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* p) {
+  p->ntile = (seqlen + kT - 1) / kT;
+  p->chgroups = (dim + kCh - 1) / kCh;
+  size_t off = 0;
+  p->off_ckpt = off;
+  off += align256(sizeof(float) * (size_t)(batch * p->ntile * NP * dim));
+  p->off_dB = off;
+  off += align256(sizeof(float) * (size_t)(batch * p->chgroups * NP * seqlen));
+  p->off_dC = off;
+  off += align256(sizeof(float) * (size_t)(batch * p->chgroups * NP * seqlen));
+  p->off_dA = off;
+  off += align256(sizeof(float) * (size_t)(batch * dim * NP));
+  p->off_dD = off;
+  off += align256(sizeof(float) * (size_t)(batch * dim));
+  p->off_dbias = off;
+  off += align256(sizeof(float) * (size_t)(batch * dim));
+  p->ws_total = seqlen == 0 ? 0 : off;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t stream) {
+  return a.io_bf16 ? run_bwd<uint16_t>(a, p, stream) : run_bwd<float>(a, p, stream);
+}
+
+}  // namespace mscan

@@ -114,3 +114,35 @@ def test_binding_refuses_host_tensors():
     u = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         mscan.scan_fwd(u, u, torch.zeros(4, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
+
+
+def bwd(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None, dy=P, dfs=None, du=P, dd=P,
+        dA=P, dB=P, dC=P, dD=None, dz=None, dbias=None, dh0=None, batch=2, dim=64, dstate=16, seqlen=128, io=1,
+        sp=1, ws=P, wsb=1 << 40):
+    return lib.mamba_scan_bwd(u, delta, A_log, B, C, D, z, bias, h0, dy, dfs, du, dd, dA, dB, dC, dD, dz, dbias,
+                              dh0, batch, dim, dstate, seqlen, io, sp, ws, wsb, None)
+
+
+def test_bwd_validation_errors(lib):
+    assert bwd(lib, dy=None) == ENULL
+    assert bwd(lib, dA=None) == ENULL
+    assert bwd(lib, dB=None) == ENULL
+    assert bwd(lib, z=P, dz=None) == ENULL             # a gate needs its gradient output
+    assert bwd(lib, io=3) == EDTYPE
+    assert bwd(lib, dim=0) == ESHAPE
+    assert bwd(lib, dstate=17) == EUNSUP
+    assert bwd(lib, du=P + 1) == EALIGN
+    assert bwd(lib, dA=P + 2) == EALIGN
+    assert bwd(lib, ws=None) == EWS
+    assert bwd(lib, wsb=16) == EWS
+    assert bwd(lib, ws=P + 16) == EWS                  # 256-byte alignment
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.mamba_scan_bwd_workspace_size
+    assert f(2, 64, 16, 0, 1) == 0
+    n = f(4, 4096, 16, 8192, 1)
+    ckpt = 4 * (8192 // 32) * 16 * 4096 * 4
+    parts = 2 * 4 * 64 * 16 * 8192 * 4
+    assert ckpt + parts <= n <= ckpt + parts + 4 * 4096 * 18 * 4 + 6 * 256
+    assert f(2, 64, 17, 100, 1) == ctypes.c_size_t(-1).value

@@ -20,7 +20,7 @@ import torch
 from .configs import Config, get_config
 
 # stream keys, fixed order
-K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS = range(9)
+K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS = range(11)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -153,3 +153,14 @@ def bf16_bits_to_f64(t: torch.Tensor) -> np.ndarray:
     if t.dtype in (torch.bfloat16, torch.float16):
         t = t.to(torch.float32)
     return t.numpy().astype(np.float64)
+
+
+def backward_inputs(batch: int, dim: int, dstate: int, seqlen: int, io: str, *, seed: int = 0,
+                    d_final_state: bool = False, threads: Optional[int] = None):
+    """Output gradients for a backward pass: dy (batch, dim, L) ~ N(0, 1) in the io dtype and,
+    if asked, dL/d(final state) (batch, dim, dstate) ~ N(0, 1) float32.  Returns (dy, dfs or None)."""
+    dy = _normal_rows(seed, (K_DY,), batch * dim, seqlen, io, threads=threads).view(batch, dim, seqlen)
+    dfs = None
+    if d_final_state:
+        dfs = _normal_rows(seed, (K_DFS,), batch * dim, dstate, "f32", threads=threads).view(batch, dim, dstate)
+    return dy, dfs
