@@ -165,6 +165,97 @@ def bench_step(args, c) -> int:
     return 0
 
 
+# algorithmic issue slots of the backward pass: per (token, channel, state) one
+# forward recompute (8) and the gradient terms (lam, Abar lam, s, h + s, dDelta,
+# dB, du, dA's two sums, dC: 16); per (token, channel) softplus (7), its
+# derivative (sigmoid, 4), SiLU and its derivative (10) and the D terms (2)
+SLOTS_BWD_PER_TCN = 24.0
+SLOTS_BWD_PER_TC_GATED = 23.0
+SLOTS_BWD_PER_TC_UNGATED = 13.0
+
+
+def bench_bwd(args, c) -> int:
+    """Backward pass of a forward workload: gradients of all inputs from a seeded dy."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import backward_inputs, forward_inputs, max_rel_err
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = forward_inputs(c)
+    b, d, n, L = c.batch, c.dim, c.dstate, c.seqlen
+    dy, _ = backward_inputs(b, d, n, L, c.io, seed=0)
+    a = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    dyd = dy.to(dev)
+    io = mscan.BF16 if c.io == "bf16" else mscan.F32
+    ws = torch.empty(mscan.bwd_workspace_size(b, d, n, L, io) + 256, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        return mscan.scan_bwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], dyd, D=a["D"], z=a["z"],
+                              delta_bias=a["delta_bias"], workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        g = step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        g = step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tc = b * d * L
+    slots = tc * n * SLOTS_BWD_PER_TCN + tc * (SLOTS_BWD_PER_TC_GATED if c.gated else SLOTS_BWD_PER_TC_UNGATED)
+    achieved = slots / (launch_ms * 1e-3) / 1e12
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        # sampled check: batch row 0, channels 0..63 (dB, dC need every channel of the row,
+        # so they are compared on a 64-channel problem run on both sides)
+        sub = {k: (v[:1, :64] if (v is not None and k in ("u", "delta", "z")) else
+                   (v[:1] if (v is not None and k in ("B", "C")) else
+                    (v[:64] if (v is not None and k in ("A_log", "D", "delta_bias")) else v)))
+               for k, v in inp.items()}
+        dys = dy[:1, :64].contiguous()
+        gs = mscan.scan_bwd(*(t.contiguous().to(dev) for t in (sub["u"], sub["delta"], sub["A_log"], sub["B"],
+                                                               sub["C"], dys)),
+                            D=sub["D"].to(dev), z=None if sub["z"] is None else sub["z"].contiguous().to(dev),
+                            delta_bias=sub["delta_bias"].to(dev))
+        r = oracle.scan_bwd(sub["u"], sub["delta"], sub["A_log"], sub["B"], sub["C"], dys, D=sub["D"], z=sub["z"],
+                            delta_bias=sub["delta_bias"])
+        parity = {k: max_rel_err(gs[k].float().cpu(), r[k]) for k in ("du", "ddelta", "dA_log", "dB", "dC", "dD")}
+        parity["tol"] = c.tol
+        parity["sample"] = "batch row 0, channels 0-63, full length"
+
+    out = {
+        "metric": "selective-scan backward Gtok·ch/s (all input gradients)",
+        "value": round(tc / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{c.name} selective-scan backward: batch {b}, d_inner {d}, d_state {n}, L {L}, "
+                               f"{c.io} io, fp32 state, {'gated' if c.gated else 'ungated'}",
+                   "batch": b, "d_inner": d, "d_state": n, "seqlen": L},
+        "kernel_ms": round(launch_ms, 4),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_SLOTS_PEAK / 1e12, 3),
+                     "unit": "T VALU issue-slots/s", "frac": round(achieved / (VALU_SLOTS_PEAK / 1e12), 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +266,7 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=2, help="workload index (forward configs 0-3)")
     ap.add_argument("--npw", type=int, default=0, help="states per wave (0 = library default)")
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
+    ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -207,6 +299,8 @@ def main() -> int:
     c = CONFIGS[args.config]
     if c.kind == "step":
         return bench_step(args, c)
+    if args.bwd:
+        return bench_bwd(args, c)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

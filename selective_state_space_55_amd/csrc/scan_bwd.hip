@@ -204,6 +204,16 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const int sel = lane & 15;
   __syncthreads();
 
+  // tile k's loads are issued while tile k-1 is scanned
+  auto load_tile = [&](int64_t tile, V8& rd, V8& ru, V4& rb) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    rd = IO::buf_load8(rs_d, off, kVec);
+    ru = IO::buf_load8(rs_u, off, kVec);
+    if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+  };
+  V8 rd = IO::zero(), ru = IO::zero();
+  V4 rb{};
+  if (a.ntile > 1) load_tile(0, rd, ru, rb);
   for (int64_t k = 0; k < a.ntile; ++k) {
     const int64_t tile = k * kT;
     if (ch_ok) {
@@ -211,11 +221,6 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
       for (int j = 0; j < NPW; ++j) a.ckpt[((b * a.ntile + k) * NP + w * NPW + j) * a.dim + d] = h[j];
     }
     if (k + 1 == a.ntile) break;   // the last tile's entering state is all the gradient pass needs
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    const V8 rd = IO::buf_load8(rs_d, off, kVec);
-    const V8 ru = IO::buf_load8(rs_u, off, kVec);
-    V4 rb{};
-    if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
     // every tile but the last is full
     float fd[8], fu[8];
     IO::to_f32(rd, fd);
@@ -238,6 +243,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) bbuf[(bg * 4 + kk) * NP + bn] = f[kk];
     }
+    if (k + 2 < a.ntile) load_tile(tile + kT, rd, ru, rb);
     lds_barrier();
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
@@ -344,6 +350,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float dD_acc = 0.0f, db_acc = 0.0f;
   __syncthreads();
 
+  // (issuing the next tile's loads a tile ahead was measured: no gain, the
+  // kernel is issue-bound, and it raises register pressure)
   for (int64_t k = a.ntile - 1; k >= 0; --k) {
     const int64_t tile = k * kT;
     const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
