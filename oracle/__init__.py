@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the selective scan (forward pass, single-token step, backward pass).
+"""fp64 CPU oracle for the selective scan (forward pass, single-token step, backward pass) and
+the causal conv1d + SiLU in front of it.
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The product path (the
@@ -48,6 +49,8 @@ def _bind(path: str):
     lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
+    lib.oracle_conv1d_fwd.restype = ctypes.c_int
+    lib.oracle_conv1d_fwd.argtypes = [P] * 6 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     return lib
@@ -185,6 +188,28 @@ def scan_bwd(u, delta, A_log, B, C, dy, D=None, z=None, delta_bias=None, initial
     return g
 
 
+def conv1d_fwd(x, weight, bias=None, conv_state=None, silu: bool = True, return_state: bool = False,
+               nthreads: int = 0, _lib_override=None):
+    """Causal depthwise conv1d (+ SiLU) in fp64.  x: (batch, dim, L); weight: (dim, K); bias: (dim,);
+    conv_state: (batch, dim, K-1), oldest first.  Returns u (batch, dim, L) [, final conv state]."""
+    x = _f64(x)
+    if x.ndim != 3:
+        raise ValueError("oracle: x must be (batch, dim, L)")
+    batch, dim, L = x.shape
+    weight = _f64(weight)
+    K = weight.shape[1]
+    weight = _f64(weight, (dim, K))
+    bias = _f64(bias, (dim,))
+    conv_state = _f64(conv_state, (batch, dim, K - 1))
+    u = np.empty((batch, dim, L))
+    st = np.empty((batch, dim, K - 1)) if return_state else None
+    rc = (_lib_override or _load()).oracle_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(st),
+                                                      _ptr(u), batch, dim, L, K, int(bool(silu)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_conv1d_fwd returned {rc}")
+    return (u, st) if return_state else u
+
+
 class Variant:
     """The same wrapper bound to another build of scan_oracle.c (used by the
     tests that plant a mistake in a copy of the oracle and check that the pins
@@ -201,6 +226,9 @@ class Variant:
 
     def scan_bwd(self, *a, **k):
         return scan_bwd(*a, _lib_override=self._lib, **k)
+
+    def conv1d_fwd(self, *a, **k):
+        return conv1d_fwd(*a, _lib_override=self._lib, **k)
 
 
 def build_variant(src_text: str, out_dir: str, name: str) -> "Variant":

@@ -320,3 +320,57 @@ int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, c
   free(pdim);
   return 0;
 }
+
+/*
+ * Causal depthwise 1-D convolution followed by SiLU, the step in front of the
+ * scan in the Mamba block (Mamba notes, awesome.papernotes.org, 设计 3 block
+ * pseudo-code: kernel size 4; State space models and Mamba,
+ * jonathanding.github.io, Mamba block architecture: Conv1d -> SiLU -> SSM; the
+ * layer configuration in MAMBA walkthrough, x-humanoid.csdn.net, §6: d_conv=4).
+ * Per (batch, channel) with K taps:
+ *
+ *   a[t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * x[t - (K-1) + k]
+ *   u[t] = a[t] * sigmoid(a[t])     (or a[t] without the activation)
+ *
+ * where x at negative times is the caller's initial conv state
+ * (batch, dim, K-1), oldest first, or zero.  The final conv state is the last
+ * K-1 inputs of the sequence (older ones from the initial state when
+ * L < K-1).  Layouts: x, u (batch, dim, L); w (dim, K); bias (dim).
+ */
+int oracle_conv1d_fwd(const double* x, const double* w, const double* bias, const double* conv_state_in,
+                      double* conv_state_out, double* u, int64_t batch, int64_t dim, int64_t seqlen, int64_t K,
+                      int silu_on, int nthreads) {
+  if (!x || !w || !u) return 1;
+  if (batch < 0 || dim < 0 || seqlen < 0 || K < 1) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t BD = batch * dim, S = K - 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t bd = 0; bd < BD; ++bd) {
+    const int64_t d = bd % dim;
+    const double* xr = x + bd * seqlen;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      double acc = bias ? bias[d] : 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const int64_t tt = t - S + k;   /* input time of tap k */
+        double xv;
+        if (tt >= 0)
+          xv = xr[tt];
+        else
+          xv = conv_state_in ? conv_state_in[bd * S + (S + tt)] : 0.0;
+        acc += w[d * K + k] * xv;
+      }
+      u[bd * seqlen + t] = silu_on ? acc * oracle_sigmoid(acc) : acc;
+    }
+    if (conv_state_out) {
+      for (int64_t i = 0; i < S; ++i) {
+        const int64_t tt = seqlen - S + i;
+        conv_state_out[bd * S + i] = tt >= 0 ? xr[tt] : (conv_state_in ? conv_state_in[bd * S + (S + tt)] : 0.0);
+      }
+    }
+  }
+  return 0;
+}
