@@ -40,6 +40,8 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "io.h", "internal.h")]
 PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traffic.txt")
 KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h", "internal.h")]
+PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
+KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h", "internal.h")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -256,6 +258,90 @@ def bench_bwd(args, c) -> int:
     return 0
 
 
+def bench_conv(args, c) -> int:
+    """Causal depthwise conv1d (K = 4) + SiLU over the forward config's (batch, d_inner, L)
+    input, the step in front of the scan in the Mamba block: a pure HBM stream."""
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import conv_inputs, max_rel_err
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b, d, L, K = c.batch, c.dim, c.seqlen, 4
+    x, w, bias, _ = conv_inputs(b, d, L, K, c.io, seed=0)
+    xd, wd, bd = x.to(dev), w.to(dev), bias.to(dev)
+    u = torch.empty_like(xd)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mscan.conv1d_fwd(xd, wd, bd, out=u, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tc = b * d * L
+    alg_bytes = 2 * tc * x.element_size() + d * (K + 1) * 4   # read x, write u, weights + bias
+    gbps = alg_bytes / (launch_ms * 1e-3) / 1e9
+    traffic = read_traffic(alg_bytes, PROFILE_TRAFFIC_CONV, KERNEL_SOURCES_CONV)
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        rows = [(0, 0), (b // 2, d // 2 + 1), (b - 1, d - 1)]
+        err = 0.0
+        for bb, dd in rows:
+            ur = oracle.conv1d_fwd(x[bb:bb + 1, dd:dd + 1], w[dd:dd + 1], bias[dd:dd + 1])
+            err = max(err, max_rel_err(u[bb:bb + 1, dd:dd + 1].float().cpu(), ur))
+        parity = {"rows": rows, "u_max_rel": err, "tol": 1e-2 if c.io == "bf16" else 1e-5}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = host_cores()
+        nrow = min(b * d, max(1, int(5e8 // L)))
+        xs = x.view(b * d, L)[:nrow].view(1, nrow, L)
+        c0 = time.perf_counter()
+        oracle.conv1d_fwd(xs, w.repeat((nrow + d - 1) // d, 1)[:nrow], bias.repeat((nrow + d - 1) // d)[:nrow],
+                          nthreads=cores)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(nrow * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"{nrow} of {b * d} (batch, channel) rows x {L} tokens, K {K}, fp64, {cs:.2f} s wall "
+                         "incl. fp64 widening of inputs"}
+
+    out = {
+        "metric": "causal conv1d + SiLU Gtok·ch/s and achieved HBM GB/s",
+        "value": round(tc / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{c.name} causal depthwise conv1d + SiLU: batch {b}, d_inner {d}, L {L}, K {K}, "
+                               f"{c.io} io, bias",
+                   "batch": b, "d_inner": d, "seqlen": L, "K": K},
+        "kernel_ms": round(launch_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -267,6 +353,7 @@ def main() -> int:
     ap.add_argument("--npw", type=int, default=0, help="states per wave (0 = library default)")
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
+    ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -301,6 +388,8 @@ def main() -> int:
         return bench_step(args, c)
     if args.bwd:
         return bench_bwd(args, c)
+    if args.conv:
+        return bench_conv(args, c)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

@@ -180,6 +180,31 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
 /* Bytes of workspace mamba_scan_bwd needs (0 only for seqlen == 0); (size_t)-1 for rejected sizes. */
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
 
+/*
+ * Causal depthwise 1-D convolution + SiLU, the step in front of the scan in the
+ * Mamba block (Mamba notes, 设计 3 block pseudo-code, kernel size 4; State space
+ * models and Mamba, Mamba block architecture: Conv1d -> SiLU -> SSM).  Per
+ * (batch, channel) with K = kernel_size taps:
+ *
+ *   a[t] = bias[d] + sum_{k<K} weight[d,k] * x[t - (K-1) + k],   u[t] = a[t] * sigmoid(a[t])
+ *
+ * (u = a when silu is zero); x at negative times is read from conv_state_in.
+ *
+ *   x               (batch, dim, seqlen)  io    input
+ *   weight          (dim, kernel_size)    f32   taps, oldest input first
+ *   bias            (dim)                 f32   NULL means 0
+ *   conv_state_in   (batch, dim, K-1)     io    the K-1 inputs before x, oldest first; NULL means 0
+ *   conv_state_out  (batch, dim, K-1)     io    OUT: the last K-1 inputs (older ones from conv_state_in
+ *                                               when seqlen < K-1); NULL: not written; may equal
+ *                                               conv_state_in (updated in place)
+ *   u               (batch, dim, seqlen)  io    OUT; must not overlap x
+ * Sizes: batch, dim >= 1, seqlen >= 0, 1 <= kernel_size <= 4 (else MAMBA_SCAN_ERR_UNSUPPORTED).
+ * Arithmetic in fp32; u is rounded to the io dtype (RNE for bf16).
+ */
+int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, const void* conv_state_in,
+                     void* conv_state_out, void* u, int64_t batch, int64_t dim, int64_t seqlen, int64_t kernel_size,
+                     int io_dtype, int silu, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* mamba_scan_status_str(int status);
 

@@ -25,8 +25,8 @@ STATUS = {
 }
 EXPORTED = (
     "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
-    "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_scan_status_str",
-    "mamba_scan_abi_version",
+    "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd",
+    "mamba_scan_status_str", "mamba_scan_abi_version",
 )
 
 _lib = None
@@ -61,6 +61,8 @@ def load_library():
     lib.mamba_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [I, I, P, SZ, P]
     lib.mamba_scan_bwd_workspace_size.restype = SZ
     lib.mamba_scan_bwd_workspace_size.argtypes = [I64] * 4 + [I]
+    lib.mamba_conv1d_fwd.restype = I
+    lib.mamba_conv1d_fwd.argtypes = [P] * 6 + [I64] * 4 + [I, I, P]
     lib.mamba_scan_status_str.restype = ctypes.c_char_p
     lib.mamba_scan_status_str.argtypes = [I]
     lib.mamba_scan_abi_version.restype = I
@@ -274,3 +276,35 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
                             L, io, int(bool(delta_softplus)), ws_ptr, ws_bytes, _stream(dev, stream))
     _check("mamba_scan_bwd", rc)
     return g
+
+
+def conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+               conv_state: Optional[torch.Tensor] = None, silu: bool = True, return_state: bool = False, *,
+               out: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None, stream=None):
+    """Causal depthwise conv1d (+ SiLU).  x (batch, dim, L) in the io dtype, weight (dim, K) float32 with
+    K <= 4, bias (dim,) float32, conv_state (batch, dim, K-1) in the io dtype (inputs before x, oldest
+    first).  Returns u (batch, dim, L), or (u, final conv state) if return_state (state_out may be
+    conv_state itself, for an in-place update)."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, L)")
+    batch, dim, L = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("conv1d_fwd needs device tensors (HIP)")
+    io = _io_dtype(x)
+    iot = x.dtype
+    K = weight.shape[-1] if weight.dim() == 2 else -1
+    _req("weight", weight, (dim, K), torch.float32, dev)
+    _req("bias", bias, (dim,), torch.float32, dev)
+    _req("conv_state", conv_state, (batch, dim, K - 1), iot, dev)
+    u = out if out is not None else torch.empty((batch, dim, L), dtype=iot, device=dev)
+    _req("out", u, (batch, dim, L), iot, dev)
+    so = state_out
+    if so is None and return_state:
+        so = torch.empty((batch, dim, K - 1), dtype=iot, device=dev)
+    _req("state_out", so, (batch, dim, K - 1), iot, dev)
+    rc = lib.mamba_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(so), _ptr(u), batch, dim,
+                              L, K, io, int(bool(silu)), _stream(dev, stream))
+    _check("mamba_conv1d_fwd", rc)
+    return (u, so) if return_state else u

@@ -176,4 +176,30 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
 }
 
+int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, const void* conv_state_in,
+                     void* conv_state_out, void* u, int64_t batch, int64_t dim, int64_t seqlen, int64_t kernel_size,
+                     int io_dtype, int silu, void* stream) {
+  if (io_dtype != MAMBA_SCAN_F32 && io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+  if (batch < 1 || dim < 1 || seqlen < 0) return MAMBA_SCAN_ERR_SHAPE;
+  if (kernel_size < 1 || kernel_size > 4) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(batch, dim, &t) || !mul_ok(t, seqlen + 8, &t) || !mul_ok(t, 4, &t)) return MAMBA_SCAN_ERR_SHAPE;
+  if (!weight) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!x || !u)) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {x, u, conv_state_in, conv_state_out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {weight, bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::ConvArgs a{};
+  a.x = x; a.weight = weight; a.bias = bias; a.state_in = conv_state_in; a.state_out = conv_state_out; a.u = u;
+  a.batch = batch; a.dim = dim; a.seqlen = seqlen; a.K = kernel_size;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.silu = silu != 0;
+  hipError_t e = mscan::launch_conv(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
 }  // extern "C"

@@ -107,4 +107,18 @@ struct BwdArgs {
 
 hipError_t launch_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t stream);
 
+struct ConvArgs {
+  const void* x;
+  const float* weight;     // (dim, K)
+  const float* bias;       // (dim) or NULL
+  const void* state_in;    // (batch, dim, K-1) io or NULL
+  void* state_out;         // (batch, dim, K-1) io or NULL; may equal state_in
+  void* u;
+  int64_t batch, dim, seqlen, K;
+  int io_bf16;
+  int silu;
+};
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+
 }  // namespace mscan

@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_scan_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba_(?:scan|conv1d)_\w+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -146,3 +146,20 @@ def test_bwd_workspace_size(lib):
     parts = 2 * 4 * 64 * 16 * 8192 * 4
     assert ckpt + parts <= n <= ckpt + parts + 4 * 4096 * 18 * 4 + 6 * 256
     assert f(2, 64, 17, 100, 1) == ctypes.c_size_t(-1).value
+
+
+def conv(lib, x=P, w=P, bias=None, si=None, so=None, u=P, batch=2, dim=64, seqlen=100, K=4, io=1, silu=1):
+    return lib.mamba_conv1d_fwd(x, w, bias, si, so, u, batch, dim, seqlen, K, io, silu, None)
+
+
+def test_conv_validation_errors(lib):
+    assert conv(lib, w=None) == ENULL
+    assert conv(lib, x=None) == ENULL
+    assert conv(lib, u=None) == ENULL
+    assert conv(lib, K=5) == EUNSUP
+    assert conv(lib, K=0) == EUNSUP
+    assert conv(lib, io=2) == EDTYPE
+    assert conv(lib, batch=0) == ESHAPE
+    assert conv(lib, seqlen=-1) == ESHAPE
+    assert conv(lib, x=P + 1) == EALIGN
+    assert conv(lib, w=P + 2) == EALIGN

@@ -20,7 +20,7 @@ import torch
 from .configs import Config, get_config
 
 # stream keys, fixed order
-K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS = range(11)
+K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS, K_CONVW, K_CONVB, K_CONVS = range(14)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -164,3 +164,18 @@ def backward_inputs(batch: int, dim: int, dstate: int, seqlen: int, io: str, *, 
     if d_final_state:
         dfs = _normal_rows(seed, (K_DFS,), batch * dim, dstate, "f32", threads=threads).view(batch, dim, dstate)
     return dy, dfs
+
+
+def conv_inputs(batch: int, dim: int, seqlen: int, K: int, io: str, *, seed: int = 0, state: bool = False,
+                threads: Optional[int] = None):
+    """Inputs of the causal conv1d: x (batch, dim, L) ~ N(0, 1) in the io dtype, weight (dim, K) ~
+    N(0, 1/K) float32, bias (dim,) ~ N(0, 0.1^2) float32, and optionally a conv state
+    (batch, dim, K-1) ~ N(0, 1) in the io dtype.  Returns (x, weight, bias, state or None)."""
+    x = _normal_rows(seed, (K_U,), batch * dim, seqlen, io, threads=threads).view(batch, dim, seqlen)
+    w = torch.from_numpy(_gen(seed, (K_CONVW, 0)).standard_normal((dim, K), dtype=np.float32)
+                         * np.float32(1.0 / math.sqrt(K)))
+    bias = torch.from_numpy(_gen(seed, (K_CONVB, 0)).standard_normal(dim, dtype=np.float32) * np.float32(0.1))
+    st = None
+    if state:
+        st = _normal_rows(seed, (K_CONVS,), batch * dim, K - 1, io, threads=threads).view(batch, dim, K - 1)
+    return x, w, bias, st
