@@ -35,13 +35,13 @@ SLOTS_PER_TCN = 8.0
 SLOTS_PER_TC_GATED = 16.0
 SLOTS_PER_TC_UNGATED = 8.0
 CSRC = os.path.join(ROOT, "selective_state_space_55_amd", "csrc")
-# committed rocprofv3 traffic summaries and the kernel sources they were taken on
+# committed rocprofv3 traffic summaries and the device sources (kernel file + io helpers) they were taken on
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "io.h", "internal.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "io.h")]
 PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traffic.txt")
-KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h", "internal.h")]
+KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
 PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
-KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h", "internal.h")]
+KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -258,6 +258,41 @@ def bench_bwd(args, c) -> int:
     return 0
 
 
+def _conv_graph_timing(args, step, u, stream):
+    """Times K conv launches replayed from one HIP graph: (ms per launch, wall s), or
+    None if the replayed output differs from the eager launch's."""
+    import torch
+
+    # One launch is shorter than the Python call that makes it, so the K steps
+    # are captured once in a HIP graph and replayed (as for decoding); the
+    # replayed output must equal an eager launch's bit for bit.
+    step(stream)
+    torch.cuda.synchronize()
+    u_eager = u.clone()
+    u.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(args.steps):
+            step()               # the capture stream is the current stream here
+    graph.replay()
+    torch.cuda.synchronize()
+    if not torch.equal(u, u_eager):
+        print("bench.py: graph replay of the conv differs from the eager launch", file=sys.stderr)
+        return None
+    for _ in range(max(1, args.warmup // max(1, args.steps))):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(stream)
+    graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = e0.elapsed_time(e1) / args.steps
+    return launch_ms, wall
+
+
 def bench_conv(args, c) -> int:
     """Causal depthwise conv1d (K = 4) + SiLU over the forward config's (batch, d_inner, L)
     input, the step in front of the scan in the Mamba block: a pure HBM stream."""
@@ -274,21 +309,27 @@ def bench_conv(args, c) -> int:
     u = torch.empty_like(xd)
     stream = torch.cuda.current_stream(dev)
 
-    def step():
-        mscan.conv1d_fwd(xd, wd, bd, out=u, stream=stream)
+    def step(strm=None):
+        mscan.conv1d_fwd(xd, wd, bd, out=u, stream=strm)
 
     for _ in range(args.warmup):
-        step()
+        step(stream)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    w0 = time.perf_counter()
-    for i in range(args.steps):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    if args.no_graph:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            step(stream)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    else:
+        r = _conv_graph_timing(args, step, u, stream)
+        if r is None:
+            return 1
+        launch_ms, wall = r
     ms_per_step = wall * 1e3 / args.steps
     tc = b * d * L
     alg_bytes = 2 * tc * x.element_size() + d * (K + 1) * 4   # read x, write u, weights + bias
@@ -329,7 +370,8 @@ def bench_conv(args, c) -> int:
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{c.name} causal depthwise conv1d + SiLU: batch {b}, d_inner {d}, L {L}, K {K}, "
-                               f"{c.io} io, bias",
+                               f"{c.io} io, bias, "
+                               + ("eager launches" if args.no_graph else "launches replayed from one HIP graph"),
                    "batch": b, "d_inner": d, "seqlen": L, "K": K},
         "kernel_ms": round(launch_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -354,6 +396,7 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--no-graph", action="store_true", help="conv: time eager launches (per-launch events) instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",

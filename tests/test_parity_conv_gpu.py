@@ -30,6 +30,10 @@ CASES = [  # (batch, dim, L, K, io, bias, silu, state)
     (3, 33, 100, 2, "bf16", True, True, False),
     (1, 8, 31, 1, "f32", True, True, False),
     (2, 130, 2049, 4, "bf16", True, True, True),
+    (2, 40, 1536, 4, "f32", True, True, True),
+    (1, 16, 1024, 3, "bf16", True, True, True),
+    (1, 4, 520, 4, "bf16", True, True, True),
+    (1, 6, 1031, 2, "f32", False, False, True),
 ]
 
 
