@@ -44,9 +44,9 @@ def _bind(path: str):
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     lib.oracle_scan_fwd.restype = ctypes.c_int
-    lib.oracle_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
+    lib.oracle_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int] * 3
     lib.oracle_scan_step.restype = ctypes.c_int
-    lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
+    lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_conv1d_fwd.restype = ctypes.c_int
@@ -87,14 +87,21 @@ def _f64(a, shape=None) -> Optional[np.ndarray]:
     return out
 
 
+def _euler(discretization: str) -> int:
+    if discretization not in ("zoh", "euler"):
+        raise ValueError(f"oracle: discretization must be 'zoh' or 'euler', got {discretization!r}")
+    return int(discretization == "euler")
+
+
 def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
 def scan_fwd(u, delta, A_log, B, C, D=None, z=None, delta_bias=None, initial_state=None,
              delta_softplus: bool = True, return_final_state: bool = True,
-             nthreads: int = 0, _lib_override=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
-    """Selective-scan forward in fp64.
+             nthreads: int = 0, _lib_override=None, discretization: str = "zoh"
+             ) -> Tuple[np.ndarray, Optional[np.ndarray]]:
+    """Selective-scan forward in fp64 (discretization "zoh", or "euler": Bbar = Delta B).
 
     Shapes: u, delta, z: (batch, dim, L); B, C: (batch, dstate, L); A_log: (dim, dstate);
     D, delta_bias: (dim,); initial_state: (batch, dim, dstate).
@@ -118,14 +125,14 @@ def scan_fwd(u, delta, A_log, B, C, D=None, z=None, delta_bias=None, initial_sta
     fs = np.empty((batch, dim, dstate), dtype=np.float64) if return_final_state else None
     rc = (_lib_override or _load()).oracle_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                  _ptr(delta_bias), _ptr(initial_state), _ptr(fs), _ptr(y), batch, dim,
-                                 dstate, L, int(bool(delta_softplus)), int(nthreads))
+                                 dstate, L, int(bool(delta_softplus)), _euler(discretization), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_scan_fwd returned {rc}")
     return y, fs
 
 
 def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True,
-              nthreads: int = 0, _lib_override=None) -> Tuple[np.ndarray, np.ndarray]:
+              nthreads: int = 0, _lib_override=None, discretization: str = "zoh") -> Tuple[np.ndarray, np.ndarray]:
     """One recurrent step in fp64.  Returns (y (batch, dim), new_state (batch, dim, dstate)).
 
     Shapes: state: (batch, dim, dstate); x, dt, z: (batch, dim); B, C: (batch, dstate);
@@ -145,7 +152,8 @@ def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softpl
     dt_bias = _f64(dt_bias, (dim,))
     y = np.empty((batch, dim), dtype=np.float64)
     rc = (_lib_override or _load()).oracle_scan_step(_ptr(st), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                                  _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), batch, dim,
+                                  _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _euler(discretization), _ptr(y),
+                                  batch, dim,
                                   dstate, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_scan_step returned {rc}")

@@ -28,6 +28,10 @@
  *   out    = y * SiLU(z[b,d,t])                   (Mamba notes, 设计 3 block
  *            pseudo-code and the 整体框架 figure: out = y * SiLU(z))
  *
+ * Variant (flag `euler`): Bbar = Delta * B[b,n,t], the first-order (Euler)
+ * input term that the Mamba notes' 设计 1 pseudo-code writes as Delta B x;
+ * Abar stays exp(Delta*A[n]).
+ *
  * The single-token step is exactly one iteration of the time loop applied to a
  * caller-held state (State space models and Mamba, §3, recurrence mode;
  * Mamba notes, 设计 2: only a (d, N) state is kept at inference).
@@ -66,8 +70,8 @@ static double oracle_silu(double z) {
 /* One time step of one (batch, channel) recurrence: updates h[0..N) in place
  * and returns the gated output for this token. */
 static double oracle_one_token(double* h, int64_t N, const double* A, double u, double dlt, double bias,
-                               int softplus_on, const double* Bt, int64_t b_stride, const double* Ct,
-                               int64_t c_stride, double Dd, const double* zt) {
+                               int softplus_on, int euler, const double* Bt, int64_t b_stride,
+                               const double* Ct, int64_t c_stride, double Dd, const double* zt) {
   double x = dlt + bias;
   double Delta = softplus_on ? oracle_softplus(x) : x;
   double acc = 0.0;
@@ -75,7 +79,11 @@ static double oracle_one_token(double* h, int64_t N, const double* A, double u, 
     double dA = Delta * A[n];
     double Abar = exp(dA);
     double Bn = Bt[n * b_stride];
-    double Bbar = (A[n] != 0.0) ? expm1(dA) / A[n] * Bn : Delta * Bn;
+    double Bbar;
+    if (euler)
+      Bbar = Delta * Bn;                                            /* Euler input term */
+    else
+      Bbar = (A[n] != 0.0) ? expm1(dA) / A[n] * Bn : Delta * Bn;    /* zero-order hold */
     h[n] = Abar * h[n] + Bbar * u;
     acc += Ct[n * c_stride] * h[n];
   }
@@ -87,7 +95,8 @@ static double oracle_one_token(double* h, int64_t N, const double* A, double u, 
 int oracle_scan_fwd(const double* u, const double* delta, const double* A_log, const double* B,
                     const double* C, const double* D, const double* z, const double* delta_bias,
                     const double* initial_state, double* final_state, double* y, int64_t batch,
-                    int64_t dim, int64_t dstate, int64_t seqlen, int delta_softplus, int nthreads) {
+                    int64_t dim, int64_t dstate, int64_t seqlen, int delta_softplus, int euler,
+                    int nthreads) {
   if (!u || !delta || !A_log || !B || !C || !y) return 1;
   if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0) return 2;
 #ifdef _OPENMP
@@ -110,7 +119,7 @@ int oracle_scan_fwd(const double* u, const double* delta, const double* A_log, c
     const int64_t row = bd * seqlen;                 /* (b, d, :) */
     const int64_t bcrow = b * dstate * seqlen;       /* (b, 0, :) */
     for (int64_t t = 0; t < seqlen; ++t) {
-      y[row + t] = oracle_one_token(h, dstate, A, u[row + t], delta[row + t], bias, delta_softplus,
+      y[row + t] = oracle_one_token(h, dstate, A, u[row + t], delta[row + t], bias, delta_softplus, euler,
                                     B + bcrow + t, seqlen, C + bcrow + t, seqlen, Dd,
                                     z ? z + row + t : NULL);
     }
@@ -123,8 +132,8 @@ int oracle_scan_fwd(const double* u, const double* delta, const double* A_log, c
 
 int oracle_scan_step(double* state, const double* x, const double* dt, const double* A_log,
                      const double* B, const double* C, const double* D, const double* z,
-                     const double* dt_bias, int dt_softplus, double* y, int64_t batch, int64_t dim,
-                     int64_t dstate, int nthreads) {
+                     const double* dt_bias, int dt_softplus, int euler, double* y, int64_t batch,
+                     int64_t dim, int64_t dstate, int nthreads) {
   if (!state || !x || !dt || !A_log || !B || !C || !y) return 1;
   if (batch < 0 || dim < 0 || dstate < 1) return 2;
 #ifdef _OPENMP
@@ -139,7 +148,7 @@ int oracle_scan_step(double* state, const double* x, const double* dt, const dou
     double* A = (double*)malloc(sizeof(double) * (size_t)dstate);
     for (int64_t n = 0; n < dstate; ++n) A[n] = -exp(A_log[d * dstate + n]);
     y[bd] = oracle_one_token(state + bd * dstate, dstate, A, x[bd], dt[bd], dt_bias ? dt_bias[d] : 0.0,
-                             dt_softplus, B + b * dstate, 1, C + b * dstate, 1, D ? D[d] : 0.0,
+                             dt_softplus, euler, B + b * dstate, 1, C + b * dstate, 1, D ? D[d] : 0.0,
                              z ? z + bd : NULL);
     free(A);
   }
