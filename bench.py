@@ -32,6 +32,8 @@ VALU_SLOTS_PEAK = 256 * 4 * 16 * 2.4e9
 # (2 slots); per (token, channel) softplus (exp + log + 3 ops = 7), SiLU gate
 # (exp + rcp + 3 ops + the multiply = 8) and the D skip (1)
 SLOTS_PER_TCN = 8.0
+# Euler input term: the exp, Delta*A, B*(Delta u), one FMA update and the readout FMA
+SLOTS_PER_TCN_EULER = 6.0
 SLOTS_PER_TC_GATED = 16.0
 SLOTS_PER_TC_UNGATED = 8.0
 CSRC = os.path.join(ROOT, "selective_state_space_55_amd", "csrc")
@@ -102,7 +104,8 @@ def bench_step(args, c) -> int:
 
     def step(k, state, strm=None):
         j = k % pool
-        mscan.scan_step(state, x[j], dt[j], A, Bm[j], Cm[j], D=D, z=z[j], dt_bias=bias, out=y, stream=strm)
+        mscan.scan_step(state, x[j], dt[j], A, Bm[j], Cm[j], D=D, z=z[j], dt_bias=bias, out=y, stream=strm,
+                        discretization=args.discretization)
 
     # A decode loop is launch-bound from Python, so the K chained steps are
     # captured once in a HIP graph and replayed; the replay is checked against
@@ -160,7 +163,8 @@ def bench_step(args, c) -> int:
                    "batch": c.batch, "d_inner": c.dim, "d_state": c.dstate, "graph_matches_eager": graph_ok},
         "roofline": {"bound": "hbm", "achieved": round(alg / (dev_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(alg / (dev_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "traffic": read_traffic(alg, PROFILE_TRAFFIC_STEP, KERNEL_SOURCES_STEP)},
+                     "traffic": (read_traffic(alg, PROFILE_TRAFFIC_STEP, KERNEL_SOURCES_STEP)
+                                 if args.discretization == "zoh" else None)},
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
@@ -396,6 +400,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--discretization", choices=["zoh", "euler"], default="zoh",
+                    help="input term of the forward/decode workloads (zoh: the default, Euler: Delta B u)")
     ap.add_argument("--no-graph", action="store_true", help="conv: time eager launches (per-launch events) instead of a graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
@@ -450,7 +456,8 @@ def main() -> int:
     def step():
         mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
                        delta_bias=a["delta_bias"], out=y, final_state=fs, return_final_state=True,
-                       workspace=ws, nchunks=args.nchunks, states_per_wave=args.npw, stream=stream)
+                       workspace=ws, nchunks=args.nchunks, states_per_wave=args.npw, stream=stream,
+                       discretization=args.discretization)
 
     for _ in range(args.warmup):
         step()
@@ -473,10 +480,11 @@ def main() -> int:
     value = tc / (ms_per_step * 1e-3) / 1e9
     alg_bytes = c.algorithmic_bytes()
     hbm_gbps = alg_bytes / (launch_ms_avg * 1e-3) / 1e9
-    slots = tc * n * SLOTS_PER_TCN + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
+    per_tcn = SLOTS_PER_TCN if args.discretization == "zoh" else SLOTS_PER_TCN_EULER
+    slots = tc * n * per_tcn + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
     achieved = slots / (launch_ms_avg * 1e-3) / 1e12
     peak = VALU_SLOTS_PEAK / 1e12
-    traffic = read_traffic(alg_bytes)
+    traffic = read_traffic(alg_bytes) if args.discretization == "zoh" else None   # counters taken on the ZOH kernel
 
     parity = None
     if not args.no_parity:
@@ -493,7 +501,7 @@ def main() -> int:
                        D=None if inp["D"] is None else inp["D"][dd:dd + 1],
                        z=None if inp["z"] is None else inp["z"][bb:bb + 1, dd:dd + 1],
                        delta_bias=None if inp["delta_bias"] is None else inp["delta_bias"][dd:dd + 1])
-            yr, fr = oracle.scan_fwd(**sub)
+            yr, fr = oracle.scan_fwd(**sub, discretization=args.discretization)
             errs.append((yr[0, 0], fr[0, 0]))
         parity = {
             "rows": rows,
@@ -527,7 +535,7 @@ def main() -> int:
                 sub[k] = v
         c0 = time.perf_counter()
         oracle.scan_fwd(sub["u"], sub["delta"], sub["A_log"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
-                        delta_bias=sub["delta_bias"], nthreads=cores)
+                        delta_bias=sub["delta_bias"], nthreads=cores, discretization=args.discretization)
         cs = time.perf_counter() - c0
         whole = "the whole workload" if (nrow == b and nch == d) else "a sample of the workload"
         cpu = {"value": round(nrow * nch * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
@@ -548,7 +556,8 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": f"{c.name} selective-scan forward: batch {b}, d_inner {d}, d_state {n}, L {L}, "
+            "workload": f"{c.name} selective-scan forward" + ("" if args.discretization == "zoh" else " (Euler)")
+                        + f": batch {b}, d_inner {d}, d_state {n}, L {L}, "
                         f"{c.io} io, fp32 state, {'gated' if c.gated else 'ungated'}, final state",
             "batch": b, "d_inner": d, "d_state": n, "seqlen": L, "io": c.io, "gated": c.gated,
             "parallelism": "single GPU",

@@ -9,6 +9,7 @@
  *   Delta_t   = softplus(delta[b,d,t] + delta_bias[d])      (or without softplus)
  *   Abar_t    = exp(Delta_t * A[d,n])                       zero-order hold
  *   Bbar_t    = (exp(Delta_t * A[d,n]) - 1) / A[d,n] * B[b,n,t]
+ *               (or Delta_t * B[b,n,t] with MAMBA_SCAN_FLAG_EULER)
  *   h_t[n]    = Abar_t * h_{t-1}[n] + Bbar_t * u[b,d,t]      h_{-1} = initial_state or 0
  *   y[b,d,t]  = (sum_n C[b,n,t] * h_t[n] + D[d] * u[b,d,t]) * SiLU(z[b,d,t])
  *
@@ -18,7 +19,8 @@
  * Mamba (jonathanding.github.io), §1.5 and §4; the ZOH formula
  * Bbar = A^-1 (exp(Delta A) - I) B, State space models and Mamba, §2; the D
  * skip, Mamba notes 设计 1 pseudo-code; the SiLU gate, Mamba notes 设计 3
- * pseudo-code and 整体框架 figure; the single-token recurrence with a fixed
+ * pseudo-code and 整体框架 figure; the Euler input term Delta B u, the same
+ * notes' 设计 1 pseudo-code; the single-token recurrence with a fixed
  * (d, N) state, State space models and Mamba, §3 (recurrence mode) and Mamba
  * notes 设计 2.
  *
@@ -54,8 +56,12 @@
 extern "C" {
 #endif
 
-#define MAMBA_SCAN_ABI_VERSION 1
+#define MAMBA_SCAN_ABI_VERSION 2
 #define MAMBA_SCAN_MAX_DSTATE 16
+
+/* Bits of the `flags` argument; any other bit set returns MAMBA_SCAN_ERR_UNSUPPORTED. */
+#define MAMBA_SCAN_FLAG_SOFTPLUS 1 /* Delta = softplus(delta + bias); without it Delta = delta + bias */
+#define MAMBA_SCAN_FLAG_EULER 2    /* Bbar u = Delta B u (Euler) instead of the zero-order hold      */
 
 typedef enum { MAMBA_SCAN_F32 = 0, MAMBA_SCAN_BF16 = 1 } mamba_scan_dtype;
 
@@ -83,7 +89,7 @@ typedef enum {
  *   initial_state(batch, dim, dstate) f32    h_{-1}, NULL means 0
  *   final_state  (batch, dim, dstate) f32    OUT: h after the last token, NULL means not written
  *   y            (batch, dim, seqlen) io     OUT: gated output
- *   delta_softplus  non-zero: Delta = softplus(delta + bias); zero: Delta = delta + bias
+ *   flags        MAMBA_SCAN_FLAG_SOFTPLUS and/or MAMBA_SCAN_FLAG_EULER (see above)
  *   workspace    device scratch of at least mamba_scan_fwd_workspace_size(...) bytes,
  *                256-byte aligned; its contents on entry are ignored and on exit undefined
  *
@@ -96,7 +102,7 @@ typedef enum {
 int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const float* initial_state,
                    float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                   int io_dtype, int delta_softplus, void* workspace, size_t workspace_bytes, void* stream);
+                   int io_dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace mamba_scan_fwd needs for these sizes (0 only for seqlen == 0).
  * Returns (size_t)-1 for sizes mamba_scan_fwd would reject. */
@@ -117,7 +123,7 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
 int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                       const float* D, const void* z, const float* delta_bias, const float* initial_state,
                       float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                      int io_dtype, int delta_softplus, int64_t nchunks, int states_per_wave, void* workspace,
+                      int io_dtype, int flags, int64_t nchunks, int states_per_wave, void* workspace,
                       size_t workspace_bytes, void* stream);
 
 size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype,
@@ -134,7 +140,7 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
  *   D         (dim)                f32   NULL means 0
  *   z         (batch, dim)         io    NULL means no gate
  *   dt_bias   (dim)                f32   NULL means 0
- *   dt_softplus  as delta_softplus above
+ *   flags        as for mamba_scan_fwd (softplus of dt + dt_bias; Euler input term)
  *   y         (batch, dim)         io    OUT
  *
  * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, and batch <= 262140 (a
@@ -142,7 +148,7 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
  * MAMBA_SCAN_ERR_UNSUPPORTED).
  */
 int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
-                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,
+                    const float* D, const void* z, const float* dt_bias, int flags, void* y, int64_t batch,
                     int64_t dim, int64_t dstate, int io_dtype, void* stream);
 
 /*
@@ -166,6 +172,8 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *   workspace        at least mamba_scan_bwd_workspace_size(...) bytes, 256-byte aligned:
  *                    the state entering every 32-token tile (batch x ceil(seqlen/32) x 16 x
  *                    dim fp32) and per-channel-group / per-row partial sums
+ *   flags            MAMBA_SCAN_FLAG_SOFTPLUS or 0; the backward pass is built for the
+ *                    zero-order hold only (MAMBA_SCAN_FLAG_EULER returns MAMBA_SCAN_ERR_UNSUPPORTED)
  * Sizes and limits as for mamba_scan_fwd.  Sums over channels (dB, dC) and
  * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so
  * repeated calls give identical results.
@@ -174,7 +182,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
                    const float* D, const void* z, const float* delta_bias, const float* initial_state,
                    const void* dy, const float* d_final_state, void* du, void* ddelta, float* dA_log, void* dB,
                    void* dC, float* dD, void* dz, float* ddelta_bias, float* d_initial_state, int64_t batch,
-                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int delta_softplus, void* workspace,
+                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int flags, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace mamba_scan_bwd needs (0 only for seqlen == 0); (size_t)-1 for rejected sizes. */

@@ -112,6 +112,15 @@ def _req(name: str, t: Optional[torch.Tensor], shape, dtype, device) -> Optional
     return t
 
 
+FLAG_SOFTPLUS, FLAG_EULER = 1, 2
+
+
+def _flags(softplus: bool, discretization: str) -> int:
+    if discretization not in ("zoh", "euler"):
+        raise ValueError(f"discretization must be 'zoh' or 'euler', got {discretization!r}")
+    return (FLAG_SOFTPLUS if softplus else 0) | (FLAG_EULER if discretization == "euler" else 0)
+
+
 def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -133,8 +142,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
              delta_softplus: bool = True, return_final_state: bool = False, *,
              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None, nchunks: int = 0, states_per_wave: int = 0,
-             stream=None):
-    """Selective-scan forward.  u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in the io dtype
+             discretization: str = "zoh", stream=None):
+    """Selective-scan forward (discretization "zoh", or "euler" for Bbar u = Delta B u).  u, delta, z: (batch, dim, L); B, C: (batch, dstate, L) in the io dtype
     (float32 or bfloat16); A_log (dim, dstate), D, delta_bias (dim,), initial_state (batch, dim, dstate)
     in float32.  Returns y (batch, dim, L), or (y, final_state) if return_final_state."""
     lib = load_library()
@@ -173,7 +182,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
         ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, ws.numel() * ws.element_size() - off)
     rc = lib.mamba_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                _ptr(delta_bias), _ptr(initial_state), _ptr(fs), _ptr(y), batch, dim, dstate, L, io,
-                               int(bool(delta_softplus)), int(nchunks), int(states_per_wave), ws_ptr, ws_bytes,
+                               _flags(delta_softplus, discretization), int(nchunks), int(states_per_wave), ws_ptr,
+                               ws_bytes,
                                _stream(dev, stream))
     _check("mamba_scan_fwd", rc)
     return (y, fs) if return_final_state else y
@@ -182,8 +192,8 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
 def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor,
               C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
               dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True, *,
-              out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One recurrent step.  state (batch, dim, dstate) float32 is updated IN PLACE; x, dt, z (batch, dim)
+              out: Optional[torch.Tensor] = None, discretization: str = "zoh", stream=None) -> torch.Tensor:
+    """One recurrent step (discretization as in scan_fwd).  state (batch, dim, dstate) float32 is updated IN PLACE; x, dt, z (batch, dim)
     and B, C (batch, dstate) in the io dtype.  Returns y (batch, dim)."""
     lib = load_library()
     if state.dim() != 3:
@@ -206,7 +216,7 @@ def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: tor
     y = out if out is not None else torch.empty((batch, dim), dtype=iot, device=dev)
     _req("out", y, (batch, dim), iot, dev)
     rc = lib.mamba_scan_step(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                             _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), batch, dim, dstate, io,
+                             _ptr(dt_bias), _flags(dt_softplus, discretization), _ptr(y), batch, dim, dstate, io,
                              _stream(dev, stream))
     _check("mamba_scan_step", rc)
     return y

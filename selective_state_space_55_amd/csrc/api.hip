@@ -72,10 +72,11 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
 int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                       const float* D, const void* z, const float* delta_bias, const float* initial_state,
                       float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                      int io_dtype, int delta_softplus, int64_t nchunks, int states_per_wave, void* workspace,
+                      int io_dtype, int flags, int64_t nchunks, int states_per_wave, void* workspace,
                       size_t workspace_bytes, void* stream) {
   int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   // tensors with a seqlen dimension are zero-sized when seqlen == 0 and may then be NULL
   if (!A_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
@@ -97,7 +98,8 @@ int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, cons
   a.h0 = initial_state; a.final_state = final_state; a.y = y;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
-  a.softplus = delta_softplus != 0;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
   a.workspace = workspace;
   hipError_t e = mscan::launch_fwd(a, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
@@ -106,17 +108,18 @@ int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, cons
 int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                    const float* D, const void* z, const float* delta_bias, const float* initial_state,
                    float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
-                   int io_dtype, int delta_softplus, void* workspace, size_t workspace_bytes, void* stream) {
+                   int io_dtype, int flags, void* workspace, size_t workspace_bytes, void* stream) {
   return mamba_scan_fwd_ex(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim,
-                           dstate, seqlen, io_dtype, delta_softplus, 0, 0, workspace, workspace_bytes, stream);
+                           dstate, seqlen, io_dtype, flags, 0, 0, workspace, workspace_bytes, stream);
 }
 
 int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
-                    const float* D, const void* z, const float* dt_bias, int dt_softplus, void* y, int64_t batch,
+                    const float* D, const void* z, const float* dt_bias, int flags, void* y, int64_t batch,
                     int64_t dim, int64_t dstate, int io_dtype, void* stream) {
   int st = check_common(batch, dim, dstate, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
   if ((batch + 3) / 4 > 65535) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid rows of four batch rows
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!state || !x || !dt || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
   const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
   const void* io_ptrs[] = {x, dt, B, C, z, y};
@@ -128,7 +131,8 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
   mscan::StepArgs a{};
   a.state = state; a.x = x; a.dt = dt; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = dt_bias;
   a.y = y; a.batch = batch; a.dim = dim; a.dstate = dstate; a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
-  a.softplus = dt_softplus != 0;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
   hipError_t e = mscan::launch_step(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
 }
@@ -144,10 +148,11 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
                    const float* D, const void* z, const float* delta_bias, const float* initial_state,
                    const void* dy, const float* d_final_state, void* du, void* ddelta, float* dA_log, void* dB,
                    void* dC, float* dD, void* dz, float* ddelta_bias, float* d_initial_state, int64_t batch,
-                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int delta_softplus, void* workspace,
+                   int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int flags, void* workspace,
                    size_t workspace_bytes, void* stream) {
   int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
+  if (flags & ~MAMBA_SCAN_FLAG_SOFTPLUS) return MAMBA_SCAN_ERR_UNSUPPORTED;   // zero-order hold only
   if (!A_log || !dA_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && z && !dz) return MAMBA_SCAN_ERR_NULL;
@@ -170,7 +175,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   a.dbias = ddelta_bias; a.dh0 = d_initial_state;
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
-  a.softplus = delta_softplus != 0;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
   a.workspace = workspace;
   hipError_t e = mscan::launch_bwd(a, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;

@@ -40,6 +40,7 @@ struct FwdArgs {
   int64_t batch, dim, dstate, seqlen;
   int io_bf16;
   int softplus;
+  int euler;          // Bbar = Delta B (Euler) instead of the zero-order hold
   void* workspace;
 };
 
@@ -59,6 +60,7 @@ struct StepArgs {
   int64_t batch, dim, dstate;
   int io_bf16;
   int softplus;
+  int euler;
 };
 
 hipError_t launch_step(const StepArgs& a, hipStream_t stream);

@@ -54,6 +54,8 @@ namespace {
 
 constexpr int kCh = 64;   // channels per workgroup, one per lane
 constexpr int kPad = 4;   // LDS row padding in floats
+constexpr int kModeSoftplus = 1;   // Delta = softplus(delta + bias)
+constexpr int kModeEuler = 2;      // Bbar u = Delta B u instead of the zero-order hold
 
 struct KArgs {
   const void* u;
@@ -70,7 +72,7 @@ struct KArgs {
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
-  int dstate, np, softplus, gated;
+  int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
 };
 
 // Work id with XCD-aware placement: the hardware deals consecutive workgroup
@@ -92,7 +94,7 @@ struct Lds {
   static constexpr int kFloats = 2 * kDU + kBC + kPar + kY;
 };
 
-template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg, bool kVec, bool kSp>
+template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg, bool kVec, int kMode>
 __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V8 = typename IO::V8;
@@ -111,6 +113,9 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   constexpr int CK = kAgg ? 1 : CPT;    // u/z kept from staging to the epilogue (output pass only)
   constexpr int kEsz = (int)sizeof(IoT);
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  constexpr bool kSp = (kMode & kModeSoftplus) != 0;
+  constexpr bool kEuler = (kMode & kModeEuler) != 0;
   static_assert(kG >= 4, "the pipeline places work in groups 0..3");
 
   extern __shared__ float smem[];
@@ -248,12 +253,15 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
         fd[j] = ok ? dl : 0.0f;
         fu[j] = ok ? fu[j] : 0.0f;
       }
+      float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
+#pragma unroll
+      for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
       float* dp = dw + ch * kRow + c8 * 8;
       float* up = uw + ch * kRow + c8 * 8;
       reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
       reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-      reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-      reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+      reinterpret_cast<float4*>(up)[0] = make_float4(fs[0], fs[1], fs[2], fs[3]);
+      reinterpret_cast<float4*>(up)[1] = make_float4(fs[4], fs[5], fs[6], fs[7]);
       if constexpr (!kAgg) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) kp.u[c][j] = fu[j];
@@ -368,12 +376,18 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
         constexpr int j = decltype(j_c)::value;
         constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
         av[j] = __builtin_amdgcn_exp2f(dl * A[j]);
-        sv[j] = dpp_bcast_mul<src>(bq.x, uu * iA[j]);          // s = B * u / A
+        if constexpr (kEuler)
+          sv[j] = dpp_bcast_mul<src>(bq.x, uu);                // s = B * Delta * u
+        else
+          sv[j] = dpp_bcast_mul<src>(bq.x, uu * iA[j]);        // s = B * u / A
       });
       static_for<NPW>([&](auto j_c) {
         constexpr int j = decltype(j_c)::value;
         constexpr int src = 4 * j + kk;
-        h[j] = fmaf(av[j], h[j] + sv[j], -sv[j]);              // Abar (h + s) - s
+        if constexpr (kEuler)
+          h[j] = fmaf(av[j], h[j], sv[j]);                     // Abar h + s
+        else
+          h[j] = fmaf(av[j], h[j] + sv[j], -sv[j]);            // Abar (h + s) - s
         if constexpr (!kAgg) {
           if constexpr (j == 0)
             acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
@@ -506,7 +520,7 @@ struct LdsH2 {
   static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
 };
 
-template <typename IoT, bool kAgg, bool kVec, bool kSp>
+template <typename IoT, bool kAgg, bool kVec, int kMode>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -522,6 +536,9 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   static_assert(kBCPieces == NT, "one B/C piece per thread");
   constexpr int kEsz = (int)sizeof(IoT);
   constexpr float kLog2e = 1.4426950408889634f;
+  constexpr float kLn2 = 0.6931471805599453f;
+  constexpr bool kSp = (kMode & kModeSoftplus) != 0;
+  constexpr bool kEuler = (kMode & kModeEuler) != 0;
 
   extern __shared__ float smem[];
   float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
@@ -638,12 +655,15 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       fd[j] = ok ? dl : 0.0f;
       fu[j] = ok ? fu[j] : 0.0f;
     }
+    float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
     float* dp = dbuf + (buf * kCh + pc) * kRow + pg * 8;
     float* up = ubuf + (buf * kCh + pc) * kRow + pg * 8;
     reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
     reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-    reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-    reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+    reinterpret_cast<float4*>(up)[0] = make_float4(fs[0], fs[1], fs[2], fs[3]);
+    reinterpret_cast<float4*>(up)[1] = make_float4(fs[4], fs[5], fs[6], fs[7]);
     if constexpr (!kAgg) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) kp.u[j] = fu[j];
@@ -720,10 +740,17 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       constexpr int kk = decltype(kk_c)::value;
       const float av0 = __builtin_amdgcn_exp2f(dl * A[0]);
       const float av1 = __builtin_amdgcn_exp2f(dl * A[1]);
-      const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);        // s = B * u / A
-      const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
-      h[0] = fmaf(av0, h[0] + s0, -s0);                            // Abar (h + s) - s
-      h[1] = fmaf(av1, h[1] + s1, -s1);
+      if constexpr (kEuler) {
+        const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * Delta * u
+        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
+        h[0] = fmaf(av0, h[0], s0);                                 // Abar h + s
+        h[1] = fmaf(av1, h[1], s1);
+      } else {
+        const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);       // s = B * u / A
+        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
+        h[0] = fmaf(av0, h[0] + s0, -s0);                           // Abar (h + s) - s
+        h[1] = fmaf(av1, h[1] + s1, -s1);
+      }
       if constexpr (!kAgg) return dpp_bcast_fmac<4 + kk>(dpp_bcast_mul<kk>(bq.y, h[0]), bq.y, h[1]);   // C . h
       return 0.0f;
     };
@@ -849,12 +876,32 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+template <template <typename, bool, bool, int> class Pick, typename IoT, bool kAgg>
+auto pick_kernel(bool vec, int mode) {
+  switch (mode) {
+    case 1: return vec ? Pick<IoT, kAgg, true, 1>::get() : Pick<IoT, kAgg, false, 1>::get();
+    case 2: return vec ? Pick<IoT, kAgg, true, 2>::get() : Pick<IoT, kAgg, false, 2>::get();
+    case 3: return vec ? Pick<IoT, kAgg, true, 3>::get() : Pick<IoT, kAgg, false, 3>::get();
+    default: return vec ? Pick<IoT, kAgg, true, 0>::get() : Pick<IoT, kAgg, false, 0>::get();
+  }
+}
+
+template <int NPW, int NSPLIT, int T>
+struct PickNpw {
+  template <typename IoT, bool kAgg, bool kVec, int kMode>
+  struct P {
+    static auto get() { return scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, kVec, kMode>; }
+  };
+};
+
+template <typename IoT, bool kAgg, bool kVec, int kMode>
+struct PickH2 {
+  static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode>; }
+};
+
 template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
 hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = vec ? (k.softplus ? scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, true, true>
-                                : scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, true, false>)
-                  : (k.softplus ? scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, false, true>
-                                : scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, false, false>);
+  auto kern = pick_kernel<PickNpw<NPW, NSPLIT, T>::template P, IoT, kAgg>(vec, k.mode);
   const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, kAgg>::kFloats;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -864,8 +911,7 @@ hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
 
 template <typename IoT, bool kAgg>
 hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = vec ? (k.softplus ? scan_fwd_h2_kernel<IoT, kAgg, true, true> : scan_fwd_h2_kernel<IoT, kAgg, true, false>)
-                  : (k.softplus ? scan_fwd_h2_kernel<IoT, kAgg, false, true> : scan_fwd_h2_kernel<IoT, kAgg, false, false>);
+  auto kern = pick_kernel<PickH2, IoT, kAgg>(vec, k.mode);
   const size_t lds = sizeof(float) * LdsH2::floats(kAgg);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -907,7 +953,7 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
-  k.dstate = (int)a.dstate; k.np = p.np; k.softplus = a.softplus; k.gated = a.z != nullptr;
+  k.dstate = (int)a.dstate; k.np = p.np; k.mode = (a.softplus ? kModeSoftplus : 0) | (a.euler ? kModeEuler : 0); k.gated = a.z != nullptr;
   const int64_t groups = a.batch * k.chgroups;
   if (p.nchunks > 1) {
     k.nwork = groups * (p.nchunks - 1);

@@ -33,7 +33,7 @@ struct SArgs {
   const float* bias;
   void* y;
   int64_t batch, dim;
-  int dstate, softplus;
+  int dstate, softplus, euler;
 };
 
 // B or C values of states 4q .. 4q+3 of batch row b (zero past dstate)
@@ -113,12 +113,22 @@ __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
     const float x = xr[r] + bias;
     const float dl = a.softplus ? softplus_log2e(x) : x * 1.4426950408889634f;   // Delta * log2e
     float acc = 0.0f;
+    if (a.euler) {
+      const float du = (dl * 0.6931471805599453f) * xv[r];   // Delta u
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float av = __builtin_amdgcn_exp2f(dl * An[j]);
-      const float s = Bv[r][j] * (xv[r] * iA[j]);   // B u / A (zero for states past dstate)
-      hs[r][j] = fmaf(av, hs[r][j] + s, -s);
-      acc = fmaf(Cv[r][j], hs[r][j], acc);
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);           // Abar h + Delta B u
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float s = Bv[r][j] * (xv[r] * iA[j]);   // B u / A (zero for states past dstate)
+        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
     }
     // sum over the quad: (q0 + q1) + (q2 + q3)
     acc += __shfl_xor(acc, 1, 4);
@@ -147,6 +157,7 @@ hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   a.state = s.state; a.x = s.x; a.dt = s.dt; a.A_log = s.A_log; a.B = s.B; a.C = s.C; a.D = s.D; a.z = s.z;
   a.bias = s.bias; a.y = s.y; a.batch = s.batch; a.dim = s.dim; a.dstate = (int)s.dstate;
   a.softplus = s.softplus;
+  a.euler = s.euler;
   const uintptr_t bc_mis = reinterpret_cast<uintptr_t>(s.B) | reinterpret_cast<uintptr_t>(s.C);
   const bool vec = (s.dstate == 16) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0) &&
                    ((bc_mis & (4 * sizeof(IoT) - 1)) == 0);

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert mscan.abi_version() == 1
+    assert mscan.abi_version() == 2
     for code in range(8):
         s = mscan.status_str(code)
         assert isinstance(s, str) and s
@@ -70,6 +70,8 @@ def test_fwd_validation_errors(lib):
     assert fwd(lib, D=P + 2) == EALIGN
     assert fwd(lib, nchunks=-1) == EUNSUP
     assert fwd(lib, npw=3) == EUNSUP
+    assert fwd(lib, sp=4) == EUNSUP                            # unknown flag bit
+    assert fwd(lib, sp=-1) == EUNSUP
     # a chunked launch needs workspace for the inter-chunk carry
     need = lib.mamba_scan_fwd_workspace_size_ex(2, 64, 16, 1024, 1, 4, 0)
     assert need > 0
@@ -104,6 +106,7 @@ def test_step_validation_errors(lib):
     assert step(lib, batch=0) == ESHAPE
     assert step(lib, dstate=20) == EUNSUP
     assert step(lib, batch=4 * 65535 + 1) == EUNSUP              # grid rows of four batch rows
+    assert step(lib, sp=8) == EUNSUP                             # unknown flag bit
     assert step(lib, state=P + 2) == EALIGN
     assert step(lib, x=P + 1) == EALIGN
 
@@ -131,6 +134,8 @@ def test_bwd_validation_errors(lib):
     assert bwd(lib, io=3) == EDTYPE
     assert bwd(lib, dim=0) == ESHAPE
     assert bwd(lib, dstate=17) == EUNSUP
+    assert bwd(lib, sp=2) == EUNSUP                              # Euler: zero-order hold only
+    assert bwd(lib, sp=3) == EUNSUP
     assert bwd(lib, du=P + 1) == EALIGN
     assert bwd(lib, dA=P + 2) == EALIGN
     assert bwd(lib, ws=None) == EWS

@@ -1,0 +1,126 @@
+"""GPU parity of the Euler variant (Bbar u = Delta B u, MAMBA_SCAN_FLAG_EULER)
+against the fp64 oracle's Euler variant, through the C ABI: edge shapes in
+both lane layouts, the chunked carry path, decode steps, chained steps equal
+to one scan; same tolerances as the zero-order-hold tests."""
+import sys
+
+import pytest
+import torch
+
+import oracle
+import selective_state_space_55_amd as mscan
+from workloads import err_report, forward_inputs, max_rel_err, step_initial, step_inputs
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def say(msg):
+    print(f"[euler] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(t):
+    return None if t is None else t.to(DEV)
+
+
+def gpu_fwd(inp, softplus=True, nchunks=0, npw=0, disc="euler"):
+    a = {k: dev(v) for k, v in inp.items()}
+    y, fs = mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                           delta_bias=a["delta_bias"], initial_state=a["initial_state"], delta_softplus=softplus,
+                           return_final_state=True, nchunks=nchunks, states_per_wave=npw, discretization=disc)
+    torch.cuda.synchronize()
+    return y.cpu(), fs.cpu()
+
+
+def oracle_fwd(inp, softplus=True):
+    return oracle.scan_fwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                           delta_bias=inp["delta_bias"], initial_state=inp["initial_state"],
+                           delta_softplus=softplus, discretization="euler")
+
+
+def check(name, got, ref, tol):
+    rep = err_report(got, ref)
+    say(f"  {name}: {rep}")
+    assert rep["max_rel"] <= tol, (name, rep)
+
+
+# (batch, dim, dstate, L, io, gated, h0, softplus)
+EDGE = [
+    (1, 64, 16, 256, "f32", True, False, True),
+    (2, 3, 16, 1, "f32", True, True, True),
+    (3, 130, 16, 65, "bf16", True, True, True),
+    (1, 128, 8, 257, "f32", True, True, False),
+    (1, 200, 12, 1000, "bf16", True, True, True),
+    (2, 192, 16, 513, "f32", False, True, True),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}" for c in EDGE])
+@pytest.mark.parametrize("npw", [4, 2])
+def test_euler_edge_shapes(case, npw):
+    b, d, n, L, io, gated, h0, sp = case
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, initial_state=h0, seed=L + d)
+    if not sp:
+        inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
+        inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
+    say(f"edge {case} npw={npw}")
+    y, fs = gpu_fwd(inp, softplus=sp, nchunks=1, npw=npw)
+    yr, fsr = oracle_fwd(inp, softplus=sp)
+    check("y", y, yr, TOL[io])
+    check("final_state", fs, fsr, TOL[io])
+
+
+@pytest.mark.parametrize("nchunks", [2, 5])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("npw", [4, 2])
+def test_euler_chunked_carry(nchunks, io, npw):
+    inp = forward_inputs(batch=2, dim=96, dstate=16, seqlen=3001, io=io, initial_state=True, seed=nchunks)
+    say(f"chunked nchunks={nchunks} io={io} npw={npw}")
+    y, fs = gpu_fwd(inp, nchunks=nchunks, npw=npw)
+    yr, fsr = oracle_fwd(inp)
+    check("y", y, yr, TOL[io])
+    check("final_state", fs, fsr, TOL[io])
+
+
+def test_euler_differs_from_zoh():
+    inp = forward_inputs(batch=1, dim=64, dstate=16, seqlen=300, io="f32", seed=3)
+    say("euler vs zoh")
+    ye, _ = gpu_fwd(inp, disc="euler")
+    yz, _ = gpu_fwd(inp, disc="zoh")
+    assert max_rel_err(ye, yz.double()) > 1e-3
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("dstate", [16, 5])
+def test_euler_steps_vs_oracle(io, dstate):
+    b, d, steps = 3, 70, 30
+    init = step_initial(None, batch=b, dim=d, dstate=dstate)
+    st_gpu = init["state"].to(DEV)
+    st_ref = init["state"].double().numpy()
+    A, D, bias = init["A_log"], init["D"], init["dt_bias"]
+    say(f"steps io={io} dstate={dstate}")
+    for k in range(steps):
+        s = step_inputs(None, k, batch=b, dim=d, dstate=dstate, io=io, gated=True)
+        y = mscan.scan_step(st_gpu, dev(s["x"]), dev(s["dt"]), dev(A), dev(s["B"]), dev(s["C"]), D=dev(D),
+                            z=dev(s["z"]), dt_bias=dev(bias), discretization="euler")
+        yr, st_ref = oracle.scan_step(st_ref, s["x"], s["dt"], A, s["B"], s["C"], D=D, z=s["z"], dt_bias=bias,
+                                      discretization="euler")
+        assert max_rel_err(y.cpu(), yr) <= TOL[io], k
+    assert max_rel_err(st_gpu.cpu(), st_ref) <= TOL[io]
+
+
+def test_euler_chained_steps_match_scan():
+    b, d, n, L = 2, 96, 16, 50
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io="f32", initial_state=True)
+    say("euler steps vs scan")
+    y, fs = gpu_fwd(inp, nchunks=1)
+    st = dev(inp["initial_state"]).clone()
+    for t in range(L):
+        yt = mscan.scan_step(st, dev(inp["u"][..., t].contiguous()), dev(inp["delta"][..., t].contiguous()),
+                             dev(inp["A_log"]), dev(inp["B"][..., t].contiguous()), dev(inp["C"][..., t].contiguous()),
+                             D=dev(inp["D"]), z=dev(inp["z"][..., t].contiguous()), dt_bias=dev(inp["delta_bias"]),
+                             discretization="euler")
+        assert max_rel_err(yt.cpu(), y[..., t].double()) <= 1e-5
+    assert max_rel_err(st.cpu(), fs.double()) <= 1e-5
