@@ -400,6 +400,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--dstate", type=int, default=0,
+                    help="override the workload's d_state (up to 64; the headline workload uses 16)")
     ap.add_argument("--discretization", choices=["zoh", "euler"], default="zoh",
                     help="input term of the forward/decode workloads (zoh: the default, Euler: Delta B u)")
     ap.add_argument("--no-graph", action="store_true", help="conv: time eager launches (per-launch events) instead of a graph")
@@ -433,6 +435,10 @@ def main() -> int:
         return 0
 
     c = CONFIGS[args.config]
+    if args.dstate:
+        import dataclasses
+
+        c = dataclasses.replace(c, dstate=args.dstate, name=f"{c.name} (d_state {args.dstate})")
     if c.kind == "step":
         return bench_step(args, c)
     if args.bwd:
@@ -484,7 +490,8 @@ def main() -> int:
     slots = tc * n * per_tcn + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
     achieved = slots / (launch_ms_avg * 1e-3) / 1e12
     peak = VALU_SLOTS_PEAK / 1e12
-    traffic = read_traffic(alg_bytes) if args.discretization == "zoh" else None   # counters taken on the ZOH kernel
+    # the committed counters were taken on the ZOH kernel at the workload's own d_state
+    traffic = read_traffic(alg_bytes) if (args.discretization == "zoh" and not args.dstate) else None
 
     parity = None
     if not args.no_parity:

@@ -57,7 +57,8 @@ extern "C" {
 #endif
 
 #define MAMBA_SCAN_ABI_VERSION 2
-#define MAMBA_SCAN_MAX_DSTATE 16
+#define MAMBA_SCAN_MAX_DSTATE 64     /* forward scan and decode step */
+#define MAMBA_SCAN_MAX_DSTATE_BWD 16 /* backward pass */
 
 /* Bits of the `flags` argument; any other bit set returns MAMBA_SCAN_ERR_UNSUPPORTED. */
 #define MAMBA_SCAN_FLAG_SOFTPLUS 1 /* Delta = softplus(delta + bias); without it Delta = delta + bias */
@@ -91,9 +92,12 @@ typedef enum {
  *   y            (batch, dim, seqlen) io     OUT: gated output
  *   flags        MAMBA_SCAN_FLAG_SOFTPLUS and/or MAMBA_SCAN_FLAG_EULER (see above)
  *   workspace    device scratch of at least mamba_scan_fwd_workspace_size(...) bytes,
- *                256-byte aligned; its contents on entry are ignored and on exit undefined
+ *                256-byte aligned; its contents on entry are ignored and on exit undefined.
+ *                It holds the chunk carry of a chunked scan and, for dstate > 16 (run as
+ *                one pass per 16 states), the fp32 readout summed over the passes
+ *                (batch x dim x seqlen x 4 bytes)
  *
- * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, seqlen >= 0, and
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, seqlen >= 0, and
  * 64 * (seqlen + 8) * sizeof(io element) < 2^31 (seqlen < 4,194,296 for
  * bf16, 8,388,600 for fp32; larger returns MAMBA_SCAN_ERR_UNSUPPORTED).  seqlen == 0
  * writes no y and sets final_state to initial_state (or zeros); the tensors
@@ -115,7 +119,8 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *                    chunks are whole tiles of 32 tokens, and a request for
  *                    more chunks than tiles is reduced to one chunk per tile.
  *   states_per_wave  states held per lane: 2 (eight waves per workgroup, two
- *                    per SIMD; the automatic choice) or 4 (four waves).
+ *                    per SIMD; the automatic choice) or 4 (four waves; only
+ *                    for dstate <= 16, otherwise MAMBA_SCAN_ERR_UNSUPPORTED).
  * The result is the same function; only rounding order differs.  The
  * workspace must be at least mamba_scan_fwd_workspace_size_ex(...) bytes.
  * Used for testing the chunked path at small sizes and for tuning.
@@ -143,7 +148,7 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
  *   flags        as for mamba_scan_fwd (softplus of dt + dt_bias; Euler input term)
  *   y         (batch, dim)         io    OUT
  *
- * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 16, and batch <= 262140 (a
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, and batch <= 262140 (a
  * launch covers four batch rows per grid row; larger returns
  * MAMBA_SCAN_ERR_UNSUPPORTED).
  */
@@ -174,7 +179,8 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *                    dim fp32) and per-channel-group / per-row partial sums
  *   flags            MAMBA_SCAN_FLAG_SOFTPLUS or 0; the backward pass is built for the
  *                    zero-order hold only (MAMBA_SCAN_FLAG_EULER returns MAMBA_SCAN_ERR_UNSUPPORTED)
- * Sizes and limits as for mamba_scan_fwd.  Sums over channels (dB, dC) and
+ * Sizes and limits as for mamba_scan_fwd, except 1 <= dstate <= 16
+ * (MAMBA_SCAN_MAX_DSTATE_BWD).  Sums over channels (dB, dC) and
  * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so
  * repeated calls give identical results.
  */

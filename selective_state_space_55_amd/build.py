@@ -37,10 +37,7 @@ def flags() -> list:
     ]
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(LIB_DIR, exist_ok=True)
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc()] + flags() + ["-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,6 +46,24 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err:
         print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles each source to an object in parallel, then links the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(LIB_DIR, exist_ok=True)
+    obj_dir = os.path.join(LIB_DIR, "obj")
+    os.makedirs(obj_dir, exist_ok=True)
+    cflags = [f for f in flags() if f != "-shared"]
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[hipcc()] + cflags + ["-c", "-o", o, os.path.join(CSRC, s)] for s, o in zip(SOURCES, objs)]
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 8))
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB_PATH + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -48,7 +48,7 @@ const char* mamba_scan_status_str(int status) {
     case MAMBA_SCAN_ERR_SHAPE: return "a size is out of range";
     case MAMBA_SCAN_ERR_DTYPE: return "io_dtype is not MAMBA_SCAN_F32 or MAMBA_SCAN_BF16";
     case MAMBA_SCAN_ERR_ALIGN: return "a pointer is not aligned to its element size";
-    case MAMBA_SCAN_ERR_UNSUPPORTED: return "unsupported option (dstate > 16 or an invalid tuning knob)";
+    case MAMBA_SCAN_ERR_UNSUPPORTED: return "unsupported option (a size past a documented limit, an unknown flag or an invalid tuning knob)";
     case MAMBA_SCAN_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     case MAMBA_SCAN_ERR_HIP: return "the HIP runtime reported an error";
     default: return "unknown status";
@@ -139,6 +139,7 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
 
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype) {
   if (check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
+  if (dstate > MAMBA_SCAN_MAX_DSTATE_BWD) return (size_t)-1;
   mscan::BwdPlan p;
   mscan::make_bwd_plan(batch, dim, seqlen, &p);
   return p.ws_total;
@@ -153,6 +154,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
   if (flags & ~MAMBA_SCAN_FLAG_SOFTPLUS) return MAMBA_SCAN_ERR_UNSUPPORTED;   // zero-order hold only
+  if (dstate > MAMBA_SCAN_MAX_DSTATE_BWD) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!A_log || !dA_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && z && !dz) return MAMBA_SCAN_ERR_NULL;

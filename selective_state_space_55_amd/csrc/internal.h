@@ -11,13 +11,16 @@ namespace mscan {
 struct FwdPlan {
   int npw;            // states per lane (per wave): 2 or 4
   int nsplit;         // waves per workgroup = padded states / npw (power of two)
-  int np;             // padded state count = nsplit * npw
+  int np;             // padded state count (16 per state group)
   int tile;           // tokens staged per workgroup iteration
   int64_t nchunks;    // time chunks scanned in parallel (1 = one pass)
   int64_t chunk_len;  // tokens per chunk, a multiple of tile
   int64_t lp;         // seqlen rounded up to a multiple of tile
+  int ngroups;        // 16-state passes (dstate > 16 runs several)
   size_t ws_bc;       // bytes of packed fp32 B/C
   size_t ws_carry;    // bytes of chunk carry (h_end / h_in) + chunk Delta sums
+  size_t off_yacc;    // byte offset of the fp32 readout sum over state groups
+  size_t ws_yacc;     // its bytes (0 when ngroups == 1)
   size_t ws_total;
 };
 

@@ -71,8 +71,11 @@ struct KArgs {
   void* y;
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
+  float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
+  int n0;              // first state of this pass (a multiple of 16)
+  int acc;             // state-group pass: 1 first (writes yacc), 2 middle (adds), 3 last (adds, writes y)
 };
 
 // Work id with XCD-aware placement: the hardware deals consecutive workgroup
@@ -520,7 +523,10 @@ struct LdsH2 {
   static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
 };
 
-template <typename IoT, bool kAgg, bool kVec, int kMode>
+// kMulti: one of several 16-state passes of a dstate > 16 scan; the readout of
+// the pass is summed into an fp32 buffer, and the last pass adds D u, gates
+// and writes y.
+template <typename IoT, bool kAgg, bool kVec, int kMode, bool kMulti>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -588,7 +594,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   float A[2], iA[2], h[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = sp * 4 + hf * 2 + j;
+    const int n = a.n0 + sp * 4 + hf * 2 + j;
     const bool valid = ch_ok && n < a.dstate;
     const float An = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     A[j] = An;
@@ -618,7 +624,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
 
   // B/C piece: state bn, 4-token group bg; waves 0-3 load B, 4-7 load C
-  const int bn = tid % NP;
+  const int bn = tid % NP;          // state of this thread's B/C piece within the pass's 16
   const int bg = (tid / NP) % kG;
   const bool isB = w < 4;
 
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     p.d = IO::buf_load8(rs_d, off, kVec);
     p.u = IO::buf_load8(rs_u, off, kVec);
     if constexpr (!kAgg) p.z = IO::buf_load8(rs_z, off, kVec);
-    const int boff = (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz);
+    const int boff = (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz);   // past dstate: reads 0
     p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
   };
 
@@ -687,7 +693,8 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       yp[s2][1] = q[1];
     }
   };
-  auto epi_finish = [&](const float4 (&yp)[4][2], const Keep& kp, float (&yv)[8]) {
+  // returns false when this pass only accumulates into yacc (no y store)
+  auto epi_finish = [&](const float4 (&yp)[4][2], const Keep& kp, float (&yv)[8], int64_t tile) -> bool {
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       float* o = yv + 4 * h2;
@@ -697,11 +704,37 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         o[0] += yp[s2][h2].x; o[1] += yp[s2][h2].y; o[2] += yp[s2][h2].z; o[3] += yp[s2][h2].w;
       }
     }
+    if constexpr (kMulti) {
+      // the pipelined body calls the epilogue of tile k-1 at k = 0 too, where
+      // y stores are dropped by an empty buffer descriptor; yacc is a plain
+      // pointer, so that call must not touch it
+      if (tile < t_begin) return false;
+      using IOF = Io<float>;
+      const int64_t t0 = tile + pg * 8;
+      int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
+      if (d0 + pc >= a.dim) nv = 0;
+      float* ya = a.yacc + (b * a.dim + d0 + pc) * a.seqlen + t0;
+      const bool vec8 = nv == 8 && (a.seqlen & 3) == 0;
+      if (a.acc >= 2) {
+        float prev[8];
+        IOF::to_f32(vec8 ? IOF::load8(ya) : IOF::load_n(ya, nv), prev);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) yv[j] += prev[j];
+      }
+      if (a.acc < 3) {
+        if (vec8)
+          IOF::store8(ya, IOF::from_f32(yv));
+        else
+          IOF::store_n(ya, IOF::from_f32(yv), nv);
+        return false;
+      }
+    }
     const float Dd = par[kCh + pc];
     float zf[8];
     IO::to_f32(kp.z, zf);
 #pragma unroll
     for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
+    return true;
   };
   auto epi_store_full = [&](int64_t tile, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
@@ -780,8 +813,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       if constexpr (!kAgg) {
         if (g == 1) {
           float yv[8];
-          epi_finish(yp, kpOther, yv);
-          epi_store_full(tile - T, yv, rs_y);
+          if (epi_finish(yp, kpOther, yv, tile - T)) epi_store_full(tile - T, yv, rs_y);
         }
       }
       if (g == 2) {
@@ -804,8 +836,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       float4 yp[4][2];
       epi_read(yp);
       float yv[8];
-      epi_finish(yp, kp, yv);
-      epi_store_tail(t_begin + k * T, yv);
+      if (epi_finish(yp, kp, yv, t_begin + k * T)) epi_store_tail(t_begin + k * T, yv);
     }
   };
 
@@ -833,7 +864,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   if (ch_ok) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = sp * 4 + hf * 2 + j;
+      const int n = a.n0 + sp * 4 + hf * 2 + j;
       if (!kAgg) {
         if (kc == a.nchunks - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
       } else {
@@ -894,9 +925,12 @@ struct PickNpw {
   };
 };
 
-template <typename IoT, bool kAgg, bool kVec, int kMode>
+template <bool kMulti>
 struct PickH2 {
-  static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode>; }
+  template <typename IoT, bool kAgg, bool kVec, int kMode>
+  struct P {
+    static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, kMulti>; }
+  };
 };
 
 template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
@@ -911,7 +945,10 @@ hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
 
 template <typename IoT, bool kAgg>
 hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = pick_kernel<PickH2, IoT, kAgg>(vec, k.mode);
+  auto kern = pick_kernel<PickH2<false>::template P, IoT, kAgg>(vec, k.mode);
+  if constexpr (!kAgg) {
+    if (k.acc != 0) kern = pick_kernel<PickH2<true>::template P, IoT, kAgg>(vec, k.mode);
+  }
   const size_t lds = sizeof(float) * LdsH2::floats(kAgg);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -955,10 +992,17 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.mode = (a.softplus ? kModeSoftplus : 0) | (a.euler ? kModeEuler : 0); k.gated = a.z != nullptr;
   const int64_t groups = a.batch * k.chgroups;
+  // dstate > 16: one pass per 16-state group; the readouts are summed in yacc
+  const int ng = p.ngroups;
+  k.yacc = ng > 1 ? reinterpret_cast<float*>(ws + p.off_yacc) : nullptr;
   if (p.nchunks > 1) {
     k.nwork = groups * (p.nchunks - 1);
-    hipError_t e = dispatch_scan<IoT>(k, p, true, vec, k.nwork, s);
-    if (e != hipSuccess) return e;
+    for (int g = 0; g < ng; ++g) {
+      k.n0 = 16 * g;
+      hipError_t e = dispatch_scan<IoT>(k, p, true, vec, k.nwork, s);
+      if (e != hipSuccess) return e;
+    }
+    hipError_t e;
     const int64_t n = a.batch * a.dim * a.dstate;
     hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, carry, dsum, a.A_log,
                        a.h0, a.batch, a.dim, (int)a.dstate, p.np, p.nchunks);
@@ -966,7 +1010,13 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   k.nwork = groups * p.nchunks;
-  return dispatch_scan<IoT>(k, p, false, vec, k.nwork, s);
+  for (int g = 0; g < ng; ++g) {
+    k.n0 = 16 * g;
+    k.acc = ng == 1 ? 0 : (g == 0 ? 1 : (g == ng - 1 ? 3 : 2));
+    hipError_t e = dispatch_scan<IoT>(k, p, false, vec, k.nwork, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -975,14 +1025,16 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
                    FwdPlan* p) {
   if (npw_req != 0 && npw_req != 2 && npw_req != 4) return false;
   if (nchunks_req < 0) return false;
-  (void)dstate;
+  if (dstate < 1 || dstate > 64) return false;
+  p->ngroups = (int)((dstate + 15) / 16);
+  if (p->ngroups > 1 && npw_req == 4) return false;   // the four-states layout covers 16 states only
   // two layouts: 4 states per lane x 4 waves with 32-token tiles, or 2 states
   // per lane x 8 waves with 64-token tiles; states past dstate are padding that
   // contributes exactly zero
   p->npw = npw_req ? npw_req : 2;   // two waves per SIMD hide more stalls (measured faster at all shapes)
   p->tile = p->npw == 4 ? 32 : 64;
   p->nsplit = p->npw == 4 ? 4 : 8;   // waves per workgroup
-  p->np = 16;
+  p->np = 16 * p->ngroups;
   const int64_t T = p->tile;
   const int64_t tiles = (seqlen + T - 1) / T;
   p->lp = tiles * T;
@@ -1003,7 +1055,9 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   if (p->nchunks > 1)
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +
                   align256(sizeof(float) * (size_t)(batch * dim * p->nchunks));
-  p->ws_total = seqlen == 0 ? 0 : p->ws_carry;
+  p->off_yacc = p->ws_carry;
+  p->ws_yacc = p->ngroups > 1 ? align256(sizeof(float) * (size_t)(batch * dim * seqlen)) : 0;
+  p->ws_total = seqlen == 0 ? 0 : p->ws_carry + p->ws_yacc;
   return true;
 }
 

@@ -6,12 +6,12 @@
 // instead of a KV cache).  The step is a pure stream over the state: it reads
 // and writes 2 * N * 4 bytes per (batch, channel) and a handful of bf16/fp32
 // scalars, so the kernel is laid out for coalesced 16-byte state traffic:
-// four lanes own one channel, lane q holding states 4q .. 4q+3 as one float4;
-// consecutive quads cover consecutive channels, so a wave moves 1 KB of
-// contiguous state per access.  Each thread walks kRows batch rows of its
+// LPC lanes own one channel (4, 8 or 16 for up to 16, 32 or 64 states), lane
+// q holding states 4q .. 4q+3 as one float4; consecutive lane groups cover
+// consecutive channels, so a wave moves 1 KB of contiguous state per access.  Each thread walks kRows batch rows of its
 // channel, so A = -exp(A_log) and 1/A are formed once per channel and reused,
 // and all rows' loads are issued before the arithmetic.  The readout sum over
-// the four lanes uses two cross-lane adds in a fixed order, so results are
+// a channel's lanes uses cross-lane adds in a fixed order, so results are
 // deterministic.
 #include "internal.h"
 #include "io.h"
@@ -55,14 +55,14 @@ __device__ __forceinline__ void load_bc4(const IoT* p, int64_t b, int q, int dst
   }
 }
 
-// kVec: dstate == 16 and the state, B and C rows are vector aligned
-template <typename IoT, bool kVec>
+// kVec: dstate == 4 * LPC and the state, B and C rows are vector aligned
+template <typename IoT, bool kVec, int LPC>
 __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
   using IO = Io<IoT>;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t dq = gid >> 2;           // channel
-  const int q = (int)(gid & 3);
-  const bool live_d = dq < a.dim;        // whole quads share the channel
+  const int64_t dq = gid / LPC;          // channel
+  const int q = (int)(gid % LPC);
+  const bool live_d = dq < a.dim;        // whole lane groups share the channel
   const int64_t d = live_d ? dq : 0;
   const int64_t b0 = (int64_t)blockIdx.y * kRows;
 
@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     }
-    // sum over the quad: (q0 + q1) + (q2 + q3)
-    acc += __shfl_xor(acc, 1, 4);
-    acc += __shfl_xor(acc, 2, 4);
+    // sum over the channel's lanes: pairs, then pairs of pairs, ...
+#pragma unroll
+    for (int m = 1; m < LPC; m <<= 1) acc += __shfl_xor(acc, m, LPC);
     if (!live[r]) continue;
     const int64_t bd = (b0 + r) * a.dim + d;
     float* st = a.state + bd * a.dstate + 4 * q;
@@ -159,14 +159,19 @@ hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   a.softplus = s.softplus;
   a.euler = s.euler;
   const uintptr_t bc_mis = reinterpret_cast<uintptr_t>(s.B) | reinterpret_cast<uintptr_t>(s.C);
-  const bool vec = (s.dstate == 16) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0) &&
+  const int lpc = s.dstate <= 16 ? 4 : (s.dstate <= 32 ? 8 : 16);   // lanes per channel
+  const bool vec = (s.dstate == 4 * lpc) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0) &&
                    ((bc_mis & (4 * sizeof(IoT) - 1)) == 0);
-  const int64_t threads = s.dim * 4;
+  const int64_t threads = s.dim * lpc;
   const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((s.batch + kRows - 1) / kRows));
-  if (vec)
-    hipLaunchKernelGGL((scan_step_kernel<IoT, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((scan_step_kernel<IoT, false>), grid, dim3(256), 0, stream, a);
+  switch (lpc * 2 + (vec ? 1 : 0)) {
+    case 9: hipLaunchKernelGGL((scan_step_kernel<IoT, true, 4>), grid, dim3(256), 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((scan_step_kernel<IoT, false, 4>), grid, dim3(256), 0, stream, a); break;
+    case 17: hipLaunchKernelGGL((scan_step_kernel<IoT, true, 8>), grid, dim3(256), 0, stream, a); break;
+    case 16: hipLaunchKernelGGL((scan_step_kernel<IoT, false, 8>), grid, dim3(256), 0, stream, a); break;
+    case 33: hipLaunchKernelGGL((scan_step_kernel<IoT, true, 16>), grid, dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL((scan_step_kernel<IoT, false, 16>), grid, dim3(256), 0, stream, a); break;
+  }
   return hipGetLastError();
 }
 

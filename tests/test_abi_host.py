@@ -62,7 +62,8 @@ def test_fwd_validation_errors(lib):
     assert fwd(lib, dim=-1) == ESHAPE
     assert fwd(lib, dstate=0) == ESHAPE
     assert fwd(lib, seqlen=-1) == ESHAPE
-    assert fwd(lib, dstate=17) == EUNSUP
+    assert fwd(lib, dstate=65) == EUNSUP
+    assert fwd(lib, dstate=17, npw=4) == EUNSUP                # four-states layout: 16 states only
     assert fwd(lib, seqlen=1 << 24) == EUNSUP                 # 64 rows x L x 2 B must fit 31 bits
     assert fwd(lib, batch=1 << 40, dim=1 << 30) == ESHAPE       # size overflow
     assert fwd(lib, u=P + 1) == EALIGN                         # bf16 needs 2-byte alignment
@@ -84,7 +85,7 @@ def test_workspace_size(lib):
     bad = ctypes.c_size_t(-1).value
     assert lib.mamba_scan_fwd_workspace_size(2, 64, 16, 0, 1) == 0
     assert lib.mamba_scan_fwd_workspace_size(0, 64, 16, 10, 1) == bad
-    assert lib.mamba_scan_fwd_workspace_size(1, 64, 17, 10, 1) == bad
+    assert lib.mamba_scan_fwd_workspace_size(1, 64, 65, 10, 1) == bad
     assert lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 10, 1, 0, 3) == bad
     # one sequential pass needs no workspace
     assert lib.mamba_scan_fwd_workspace_size(4, 4096, 16, 8192, 1) == 0
@@ -104,7 +105,7 @@ def test_step_validation_errors(lib):
     assert step(lib, y=None) == ENULL
     assert step(lib, io=2) == EDTYPE
     assert step(lib, batch=0) == ESHAPE
-    assert step(lib, dstate=20) == EUNSUP
+    assert step(lib, dstate=65) == EUNSUP
     assert step(lib, batch=4 * 65535 + 1) == EUNSUP              # grid rows of four batch rows
     assert step(lib, sp=8) == EUNSUP                             # unknown flag bit
     assert step(lib, state=P + 2) == EALIGN
@@ -168,3 +169,18 @@ def test_conv_validation_errors(lib):
     assert conv(lib, seqlen=-1) == ESHAPE
     assert conv(lib, x=P + 1) == EALIGN
     assert conv(lib, w=P + 2) == EALIGN
+
+
+def test_fwd_workspace_holds_readout_sum_for_wide_state():
+    """dstate > 16 runs one pass per 16 states and sums the readouts in an fp32 workspace buffer."""
+    b, d, L = 2, 64, 1000
+    assert mscan.fwd_workspace_size(b, d, 16, L, mscan.BF16, 1) == 0
+    for n in (17, 32, 64):
+        need = mscan.fwd_workspace_size(b, d, n, L, mscan.BF16, 1)
+        assert need >= b * d * L * 4
+    # chunked: carry (16 padded states per group) plus the readout sum
+    assert mscan.fwd_workspace_size(b, d, 64, L, mscan.BF16, 4) > mscan.fwd_workspace_size(b, d, 64, L, mscan.BF16, 1)
+    assert mscan.fwd_workspace_size(b, d, 64, 0, mscan.BF16, 0) == 0
+    assert mscan.bwd_workspace_size(b, d, 16, L, mscan.BF16) > 0
+    with pytest.raises(ValueError):
+        mscan.bwd_workspace_size(b, d, 17, L, mscan.BF16)
