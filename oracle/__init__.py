@@ -46,6 +46,8 @@ def _bind(path: str):
     lib.oracle_scan_fwd.restype = ctypes.c_int
     lib.oracle_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [ctypes.c_int] * 3
     lib.oracle_scan_step.restype = ctypes.c_int
+    lib.oracle_scan_fwd_varlen.restype = ctypes.c_int
+    lib.oracle_scan_fwd_varlen.argtypes = [P] * 12 + [I64] * 4 + [ctypes.c_int] * 3
     lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
@@ -128,6 +130,39 @@ def scan_fwd(u, delta, A_log, B, C, D=None, z=None, delta_bias=None, initial_sta
                                  dstate, L, int(bool(delta_softplus)), _euler(discretization), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_scan_fwd returned {rc}")
+    return y, fs
+
+
+def scan_fwd_varlen(u, delta, A_log, B, C, cu_seqlens, D=None, z=None, delta_bias=None, initial_states=None,
+                    delta_softplus: bool = True, discretization: str = "zoh", nthreads: int = 0,
+                    _lib_override=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Variable-length batch in fp64: nseq sequences packed along time, sequence s on tokens
+    [cu_seqlens[s], cu_seqlens[s+1]).  u, delta, z: (dim, total); B, C: (dstate, total);
+    initial_states: (nseq, dim, dstate).  Returns (y (dim, total), final_states (nseq, dim, dstate))."""
+    u = _f64(u)
+    if u.ndim != 2:
+        raise ValueError("oracle: u must be (dim, total)")
+    dim, total = u.shape
+    A_log = _f64(A_log)
+    dstate = A_log.shape[1]
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64).ravel())
+    nseq = cu.size - 1
+    delta = _f64(delta, (dim, total))
+    A_log = _f64(A_log, (dim, dstate))
+    B = _f64(B, (dstate, total))
+    C = _f64(C, (dstate, total))
+    D = _f64(D, (dim,))
+    z = _f64(z, (dim, total))
+    delta_bias = _f64(delta_bias, (dim,))
+    initial_states = _f64(initial_states, (nseq, dim, dstate))
+    y = np.zeros((dim, total), dtype=np.float64)
+    fs = np.empty((nseq, dim, dstate), dtype=np.float64)
+    rc = (_lib_override or _load()).oracle_scan_fwd_varlen(
+        _ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias), _ptr(cu),
+        _ptr(initial_states), _ptr(fs), _ptr(y), nseq, dim, dstate, total, int(bool(delta_softplus)),
+        _euler(discretization), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_fwd_varlen returned {rc}")
     return y, fs
 
 
@@ -231,6 +266,9 @@ class Variant:
 
     def scan_step(self, *a, **k):
         return scan_step(*a, _lib_override=self._lib, **k)
+
+    def scan_fwd_varlen(self, *a, **k):
+        return scan_fwd_varlen(*a, _lib_override=self._lib, **k)
 
     def scan_bwd(self, *a, **k):
         return scan_bwd(*a, _lib_override=self._lib, **k)

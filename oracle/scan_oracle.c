@@ -155,6 +155,59 @@ int oracle_scan_step(double* state, const double* x, const double* dt, const dou
   return 0;
 }
 
+/*
+ * Variable-length batch: nseq sequences packed one after another along the
+ * time axis of a single row per channel, sequence s covering tokens
+ * [cu_seqlens[s], cu_seqlens[s+1]).  Each sequence is its own scan of the
+ * definition above, from its own initial state (or zero), with its own final
+ * state; nothing carries across a boundary.  (The pages define the scan of
+ * one sequence; packing several into one row is how batches of unequal
+ * lengths are laid out without padding -- the plain reading is that the
+ * recurrence restarts at each sequence start.)
+ *
+ *   u, delta, z, y : (dim, total)     B, C : (dstate, total)
+ *   initial_states, final_states : (nseq, dim, dstate)
+ * cu_seqlens must be non-decreasing from 0 to total (checked: returns 3).
+ */
+int oracle_scan_fwd_varlen(const double* u, const double* delta, const double* A_log, const double* B,
+                           const double* C, const double* D, const double* z, const double* delta_bias,
+                           const int64_t* cu_seqlens, const double* initial_states, double* final_states,
+                           double* y, int64_t nseq, int64_t dim, int64_t dstate, int64_t total,
+                           int delta_softplus, int euler, int nthreads) {
+  if (!A_log || !cu_seqlens || !y || (total > 0 && (!u || !delta || !B || !C))) return 1;
+  if (nseq < 1 || dim < 0 || dstate < 1 || total < 0) return 2;
+  if (cu_seqlens[0] != 0 || cu_seqlens[nseq] != total) return 3;
+  for (int64_t s = 0; s < nseq; ++s)
+    if (cu_seqlens[s + 1] < cu_seqlens[s]) return 3;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t SD = nseq * dim;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t sd = 0; sd < SD; ++sd) {
+    const int64_t s = sd / dim, d = sd % dim;
+    double* h = (double*)malloc(sizeof(double) * (size_t)(2 * dstate));
+    double* A = h + dstate;
+    for (int64_t n = 0; n < dstate; ++n) {
+      A[n] = -exp(A_log[d * dstate + n]);
+      h[n] = initial_states ? initial_states[sd * dstate + n] : 0.0;   /* restart at the sequence start */
+    }
+    const double bias = delta_bias ? delta_bias[d] : 0.0;
+    const double Dd = D ? D[d] : 0.0;
+    const int64_t row = d * total;
+    for (int64_t t = cu_seqlens[s]; t < cu_seqlens[s + 1]; ++t) {
+      y[row + t] = oracle_one_token(h, dstate, A, u[row + t], delta[row + t], bias, delta_softplus, euler,
+                                    B + t, total, C + t, total, Dd, z ? z + row + t : NULL);
+    }
+    if (final_states)
+      for (int64_t n = 0; n < dstate; ++n) final_states[sd * dstate + n] = h[n];
+    free(h);
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
