@@ -39,7 +39,7 @@ SLOTS_PER_TC_UNGATED = 8.0
 CSRC = os.path.join(ROOT, "selective_state_space_55_amd", "csrc")
 # committed rocprofv3 traffic summaries and the device sources (kernel file + io helpers) they were taken on
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt")
-KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "io.h")]
+KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "scan_fwd_h2.h", "io.h")]
 PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traffic.txt")
 KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
 PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
@@ -388,6 +388,91 @@ def bench_conv(args, c) -> int:
     return 0
 
 
+def bench_varlen(args, c) -> int:
+    """Variable-length batch over the forward config's channels and total tokens: batch x L tokens
+    per channel split into a seeded mix of sequence lengths (uniform 64..2048, the last one
+    trimmed), packed along time, each sequence from its own initial state."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import forward_inputs, max_rel_err
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    total = c.batch * c.seqlen
+    rng = np.random.default_rng(1234)
+    lens = []
+    while sum(lens) < total:
+        lens.append(int(min(rng.integers(64, 2049), total - sum(lens))))
+    nseq = len(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int64)
+    inp = forward_inputs(batch=1, dim=c.dim, dstate=c.dstate, seqlen=total, io=c.io, gated=c.gated, seed=0)
+    a = {k: (None if v is None else (v[0] if v.dim() == 3 else v).to(dev)) for k, v in inp.items()
+         if k != "initial_state"}
+    h0 = (torch.randn(nseq, c.dim, c.dstate, generator=torch.Generator().manual_seed(3)) * 0.1).to(dev)
+    cud = cu.to(dev)
+    y = torch.empty_like(a["u"])
+    fs = torch.empty(nseq, c.dim, c.dstate, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mscan.scan_fwd_varlen(a["u"], a["delta"], a["A_log"], a["B"], a["C"], cud, D=a["D"], z=a["z"],
+                              delta_bias=a["delta_bias"], initial_states=h0, out=y, final_states=fs,
+                              return_final_states=True, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    tc = total * c.dim
+    slots = tc * c.dstate * SLOTS_PER_TCN + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
+    achieved = slots / (launch_ms * 1e-3) / 1e12
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        chans = [0, c.dim // 2 + 3, c.dim - 1]
+        host = {k: (None if v is None else v.cpu()) for k, v in a.items()}
+        yr, fr = oracle.scan_fwd_varlen(host["u"][chans], host["delta"][chans], host["A_log"][chans], host["B"],
+                                        host["C"], cu.numpy(), D=host["D"][chans],
+                                        z=None if host["z"] is None else host["z"][chans],
+                                        delta_bias=host["delta_bias"][chans], initial_states=h0.cpu()[:, chans])
+        parity = {"channels": chans, "y_max_rel": max_rel_err(y.cpu()[chans], yr),
+                  "final_states_max_rel": max_rel_err(fs.cpu()[:, chans], fr), "tol": c.tol}
+
+    out = {
+        "metric": "selective-scan fwd over a variable-length batch, Gtok·ch/s",
+        "value": round(tc / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{c.name} channels, variable-length batch: {nseq} sequences of 64-2048 tokens "
+                               f"(seeded uniform), {total} tokens, d_inner {c.dim}, d_state {c.dstate}, {c.io} io, "
+                               f"{'gated' if c.gated else 'ungated'}, per-sequence initial and final states",
+                   "nseq": nseq, "total_tokens": total, "d_inner": c.dim, "d_state": c.dstate},
+        "kernel_ms": round(launch_ms, 4),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_SLOTS_PEAK / 1e12, 3),
+                     "unit": "T VALU issue-slots/s", "frac": round(achieved / (VALU_SLOTS_PEAK / 1e12), 4),
+                     "traffic": None},
+        "cpu_baseline": None,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -400,6 +485,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--varlen", action="store_true",
+                    help="time a variable-length batch with the forward config's channels and total tokens")
     ap.add_argument("--dstate", type=int, default=0,
                     help="override the workload's d_state (up to 64; the headline workload uses 16)")
     ap.add_argument("--discretization", choices=["zoh", "euler"], default="zoh",
@@ -445,6 +532,8 @@ def main() -> int:
         return bench_bwd(args, c)
     if args.conv:
         return bench_conv(args, c)
+    if args.varlen:
+        return bench_varlen(args, c)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()

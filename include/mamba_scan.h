@@ -135,6 +135,42 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
                                         int64_t nchunks, int states_per_wave);
 
 /*
+ * Forward scan over a variable-length batch: nseq sequences packed one after
+ * another along the time axis, sequence s on tokens [cu_seqlens[s],
+ * cu_seqlens[s+1]).  Each sequence is scanned exactly as mamba_scan_fwd scans
+ * one batch row -- from its own initial state, with its own final state;
+ * nothing crosses a sequence boundary.  (The pages define the scan of one
+ * sequence: Mamba notes, 设计 1 and 设计 2; State space models and Mamba, §3.
+ * Packing unequal lengths without padding restarts the recurrence at every
+ * sequence start.)
+ *
+ *   u, delta, z, y    (dim, total_len)          io   one packed row per channel
+ *   B, C              (dstate, total_len)       io
+ *   cu_seqlens        (nseq + 1)                int64, DEVICE memory, 8-byte aligned:
+ *                     0 = cu[0] <= cu[1] <= ... <= cu[nseq] = total_len (empty
+ *                     sequences allowed).  Not checked on the host (it is device
+ *                     memory); offsets outside [0, total_len] are clamped, so a bad
+ *                     array gives wrong results but no out-of-bounds access.
+ *   initial_states    (nseq, dim, dstate) f32   NULL means zeros
+ *   final_states      (nseq, dim, dstate) f32   OUT, NULL means not written
+ *   A_log, D, delta_bias, flags, workspace: as for mamba_scan_fwd (workspace from
+ *                     mamba_scan_fwd_varlen_workspace_size; 0 bytes for dstate <= 16)
+ * Sizes: nseq >= 1, dim >= 1, 1 <= dstate <= 64, total_len >= 0 with the seqlen
+ * limit of mamba_scan_fwd; nseq * ceil(dim / 64) < 2^31.  No time chunking: work
+ * items are (sequence, 64-channel group), so a few very long sequences use few
+ * workgroups.
+ */
+int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, const int64_t* cu_seqlens,
+                          const float* initial_states, float* final_states, void* y, int64_t nseq, int64_t dim,
+                          int64_t dstate, int64_t total_len, int io_dtype, int flags, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace mamba_scan_fwd_varlen needs; (size_t)-1 for rejected sizes. */
+size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t dstate, int64_t total_len,
+                                            int io_dtype);
+
+/*
  * One recurrent step for one token per (batch, channel); the state is updated
  * IN PLACE and y is written.  Exactly one iteration of the forward recurrence.
  *

@@ -25,7 +25,7 @@ STATUS = {
 }
 EXPORTED = (
     "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
-    "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd",
+    "mamba_scan_fwd_varlen", "mamba_scan_fwd_varlen_workspace_size", "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd",
     "mamba_scan_status_str", "mamba_scan_abi_version",
 )
 
@@ -61,6 +61,10 @@ def load_library():
     lib.mamba_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [I, I, P, SZ, P]
     lib.mamba_scan_bwd_workspace_size.restype = SZ
     lib.mamba_scan_bwd_workspace_size.argtypes = [I64] * 4 + [I]
+    lib.mamba_scan_fwd_varlen.restype = I
+    lib.mamba_scan_fwd_varlen.argtypes = [P] * 12 + [I64] * 4 + [I, I, P, SZ, P]
+    lib.mamba_scan_fwd_varlen_workspace_size.restype = SZ
+    lib.mamba_scan_fwd_varlen_workspace_size.argtypes = [I64] * 4 + [I]
     lib.mamba_conv1d_fwd.restype = I
     lib.mamba_conv1d_fwd.argtypes = [P] * 6 + [I64] * 4 + [I, I, P]
     lib.mamba_scan_status_str.restype = ctypes.c_char_p
@@ -187,6 +191,68 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
                                _stream(dev, stream))
     _check("mamba_scan_fwd", rc)
     return (y, fs) if return_final_state else y
+
+
+def fwd_varlen_workspace_size(nseq: int, dim: int, dstate: int, total_len: int, io_dtype: int = BF16) -> int:
+    n = load_library().mamba_scan_fwd_varlen_workspace_size(nseq, dim, dstate, total_len, io_dtype)
+    if n == ctypes.c_size_t(-1).value:
+        raise ValueError("mamba_scan_fwd_varlen_workspace_size: sizes rejected")
+    return int(n)
+
+
+def scan_fwd_varlen(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                    cu_seqlens: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                    delta_bias: Optional[torch.Tensor] = None, initial_states: Optional[torch.Tensor] = None,
+                    delta_softplus: bool = True, return_final_states: bool = False, *,
+                    out: Optional[torch.Tensor] = None, final_states: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None, discretization: str = "zoh", stream=None):
+    """Variable-length batch: nseq sequences packed along time.  u, delta, z: (dim, total); B, C:
+    (dstate, total) in the io dtype; cu_seqlens (nseq + 1,) int64 on the device; initial_states
+    (nseq, dim, dstate) float32.  Returns y (dim, total), or (y, final_states)."""
+    lib = load_library()
+    if u.dim() != 2:
+        raise ValueError("u must be (dim, total)")
+    dim, total = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_varlen needs device tensors (HIP)")
+    io = _io_dtype(u)
+    iot = u.dtype
+    dstate = A_log.shape[-1] if A_log.dim() == 2 else -1
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be (nseq + 1,)")
+    nseq = cu_seqlens.numel() - 1
+    _req("cu_seqlens", cu_seqlens, (nseq + 1,), torch.int64, dev)
+    _req("u", u, (dim, total), iot, dev)
+    _req("delta", delta, (dim, total), iot, dev)
+    _req("A_log", A_log, (dim, dstate), torch.float32, dev)
+    _req("B", B, (dstate, total), iot, dev)
+    _req("C", C, (dstate, total), iot, dev)
+    _req("D", D, (dim,), torch.float32, dev)
+    _req("z", z, (dim, total), iot, dev)
+    _req("delta_bias", delta_bias, (dim,), torch.float32, dev)
+    _req("initial_states", initial_states, (nseq, dim, dstate), torch.float32, dev)
+    y = out if out is not None else torch.empty((dim, total), dtype=iot, device=dev)
+    _req("out", y, (dim, total), iot, dev)
+    fs = final_states
+    if fs is None and return_final_states:
+        fs = torch.empty((nseq, dim, dstate), dtype=torch.float32, device=dev)
+    _req("final_states", fs, (nseq, dim, dstate), torch.float32, dev)
+    need = fwd_varlen_workspace_size(nseq, dim, dstate, total, io)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if ws is not None:
+        base = ws.data_ptr()
+        off = (-base) % 256
+        ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, ws.numel() * ws.element_size() - off)
+    rc = lib.mamba_scan_fwd_varlen(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                   _ptr(delta_bias), _ptr(cu_seqlens), _ptr(initial_states), _ptr(fs), _ptr(y),
+                                   nseq, dim, dstate, total, io, _flags(delta_softplus, discretization), ws_ptr,
+                                   ws_bytes, _stream(dev, stream))
+    _check("mamba_scan_fwd_varlen", rc)
+    return (y, fs) if return_final_states else y
 
 
 def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor,

@@ -113,6 +113,55 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const v
                            dstate, seqlen, io_dtype, flags, 0, 0, workspace, workspace_bytes, stream);
 }
 
+size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t dstate, int64_t total_len,
+                                            int io_dtype) {
+  if (nseq < 1) return (size_t)-1;
+  if (check_fwd_sizes(1, dim, dstate, total_len, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
+  mscan::FwdPlan p;
+  if (!mscan::make_fwd_plan(1, dim, dstate, total_len, 1, 2, &p)) return (size_t)-1;
+  return p.ws_total;
+}
+
+int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, const int64_t* cu_seqlens,
+                          const float* initial_states, float* final_states, void* y, int64_t nseq, int64_t dim,
+                          int64_t dstate, int64_t total_len, int io_dtype, int flags, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (nseq < 1) return MAMBA_SCAN_ERR_SHAPE;
+  int st = check_fwd_sizes(1, dim, dstate, total_len, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(nseq, (dim + 63) / 64, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid size
+  if (!A_log || !cu_seqlens) return MAMBA_SCAN_ERR_NULL;
+  if (total_len > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, delta_bias, initial_states, final_states};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  if (!aligned(cu_seqlens, 8)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::FwdPlan plan;
+  if (!mscan::make_fwd_plan(1, dim, dstate, total_len, 1, 2, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (plan.ws_total > 0) {
+    if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
+  }
+  mscan::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_states; a.final_state = final_states; a.y = y;
+  a.batch = 1; a.dim = dim; a.dstate = dstate; a.seqlen = total_len;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
+  a.workspace = workspace;
+  a.cu = cu_seqlens;
+  a.nseq = nseq;
+  hipError_t e = mscan::launch_fwd_varlen(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
 int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
                     const float* D, const void* z, const float* dt_bias, int flags, void* y, int64_t batch,
                     int64_t dim, int64_t dstate, int io_dtype, void* stream) {

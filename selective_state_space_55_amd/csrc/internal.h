@@ -45,9 +45,13 @@ struct FwdArgs {
   int softplus;
   int euler;          // Bbar = Delta B (Euler) instead of the zero-order hold
   void* workspace;
+  const int64_t* cu;  // variable-length batch: sequence offsets (nseq + 1), device; rows are (dim, seqlen)
+  int64_t nseq;
 };
 
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
+// batch must be 1 in the plan; h0 / final_state are (nseq, dim, dstate)
+hipError_t launch_fwd_varlen(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
 
 struct StepArgs {
   float* state;

@@ -46,45 +46,10 @@
 // walkthrough, x-humanoid.csdn.net, §2.2: chunks in parallel, only the state
 // crosses chunk boundaries; State space models and Mamba, Parallel Scan: the
 // associative operator).
-#include "internal.h"
-#include "io.h"
+#include "scan_fwd_h2.h"
 
 namespace mscan {
 namespace {
-
-constexpr int kCh = 64;   // channels per workgroup, one per lane
-constexpr int kPad = 4;   // LDS row padding in floats
-constexpr int kModeSoftplus = 1;   // Delta = softplus(delta + bias)
-constexpr int kModeEuler = 2;      // Bbar u = Delta B u instead of the zero-order hold
-
-struct KArgs {
-  const void* u;
-  const void* delta;
-  const float* A_log;
-  const void* B;
-  const void* C;
-  const float* D;
-  const void* z;
-  const float* bias;
-  const float* h0;
-  float* final_state;
-  void* y;
-  float* carry;        // [batch][dim][nchunks][np]
-  float* dsum;         // [batch][dim][nchunks]
-  float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
-  int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
-  int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
-  int n0;              // first state of this pass (a multiple of 16)
-  int acc;             // state-group pass: 1 first (writes yacc), 2 middle (adds), 3 last (adds, writes y)
-};
-
-// Work id with XCD-aware placement: the hardware deals consecutive workgroup
-// ids round-robin over the 8 XCDs; map them so each XCD gets a contiguous
-// range of work ids (same batch row -> same B/C lines in that XCD's L2).
-__device__ __forceinline__ int64_t work_id(int64_t bid, int64_t nwork) {
-  if ((nwork & 7) != 0) return bid;
-  return (bid & 7) * (nwork >> 3) + (bid >> 3);
-}
 
 template <int NPW, int NSPLIT, int T, bool kAgg>
 struct Lds {
@@ -501,380 +466,6 @@ __global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
   }
 }
 
-// Two-states-per-lane layout: 8 waves (two per SIMD) over 64 channels.  Wave w
-// covers channels (w & 1) * 32 .. +31; its lanes l and l + 32 hold the same
-// channel and different state pairs, states (w >> 1) * 4 + (l >> 5) * 2 + {0, 1}.
-// The two halves' readouts are summed in the wave (v_permlane32_swap), so a
-// (token, channel) again has four partial readouts, one per wave pair.  With
-// two waves per SIMD one wave's LDS, memory and barrier waits overlap the
-// other's arithmetic.  Tiles are 64 tokens, so the 8 threads that load a
-// row's tile read one whole 128-byte line (bf16) with one instruction; staging
-// and the epilogue use one 8-token piece per thread.  The partial readouts
-// are single-buffered: the epilogue reads of tile k-1 finish (barrier) before
-// tile k's scan writes its partials.
-struct LdsH2 {
-  static constexpr int kT = 64;
-  static constexpr int kRow = kT + kPad;
-  static constexpr int kG = kT / 4;
-  static constexpr int kDU = 2 * kCh * kRow;
-  static constexpr int kBC = 2 * kG * 16 * 8;
-  static constexpr int kPar = 2 * kCh;
-  static constexpr int kY = 4 * kCh * kRow;
-  static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
-};
-
-// kMulti: one of several 16-state passes of a dstate > 16 scan; the readout of
-// the pass is summed into an fp32 buffer, and the last pass adds D u, gates
-// and writes y.
-template <typename IoT, bool kAgg, bool kVec, int kMode, bool kMulti>
-__global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
-  using IO = Io<IoT>;
-  using V4 = typename IO::V4;
-  using V8 = typename IO::V8;
-  constexpr int NT = 512;
-  constexpr int T = LdsH2::kT;
-  constexpr int kRow = LdsH2::kRow;
-  constexpr int kG = LdsH2::kG;
-  constexpr int NP = 16;
-  constexpr int kPieces = kCh * T / 8;     // (channel, 8-token) pieces of Delta/u/z per tile
-  static_assert(kPieces == NT, "one piece per thread");
-  constexpr int kBCPieces = 2 * NP * kG;   // (B or C, state, 4-token group) pieces per tile
-  static_assert(kBCPieces == NT, "one B/C piece per thread");
-  constexpr int kEsz = (int)sizeof(IoT);
-  constexpr float kLog2e = 1.4426950408889634f;
-  constexpr float kLn2 = 0.6931471805599453f;
-  constexpr bool kSp = (kMode & kModeSoftplus) != 0;
-  constexpr bool kEuler = (kMode & kModeEuler) != 0;
-
-  extern __shared__ float smem[];
-  float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
-  float* ubuf = dbuf + LdsH2::kDU;         // [2][64][kRow]  u
-  float* bcs = ubuf + LdsH2::kDU;          // [2][kG][4 tokens][NP][B, C]
-  float* par = bcs + LdsH2::kBC;           // [2][64]        bias, D
-  float* ypart = par + LdsH2::kPar;        // [4][64][kRow]  partial readouts (output pass only)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hf = lane >> 5;                // lane half: which state pair of the wave's four states
-  const int chw = (w & 1) * 32 + (lane & 31);   // the lane's channel within the workgroup
-  const int sp = w >> 1;                   // partial-readout slot of the wave pair
-  const int pc = tid / 8;                  // this thread's staging/epilogue piece: channel
-  const int pg = tid % 8;                  //   and tokens 8 pg .. 8 pg + 7
-
-  int64_t wid = work_id(blockIdx.x, a.nwork);
-  const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
-  const int64_t kc = wid % nck;
-  wid /= nck;
-  const int64_t cg = wid % a.chgroups;
-  const int64_t b = wid / a.chgroups;
-  const int64_t d0 = cg * kCh;
-  const int64_t t_begin = kc * a.chunk_len;
-  const int64_t t_end = min(t_begin + a.chunk_len, a.seqlen);
-  const int64_t ntile = (t_end - t_begin + T - 1) / T;
-
-  const IoT* __restrict__ gu = static_cast<const IoT*>(a.u);
-  const IoT* __restrict__ gd = static_cast<const IoT*>(a.delta);
-  const IoT* __restrict__ gz = static_cast<const IoT*>(a.z);
-  const IoT* __restrict__ gB = static_cast<const IoT*>(a.B);
-  const IoT* __restrict__ gC = static_cast<const IoT*>(a.C);
-  IoT* __restrict__ gy = static_cast<IoT*>(a.y);
-
-  if (tid < kCh) {
-    const int64_t dd = d0 + tid;
-    const bool ok = dd < a.dim;
-    par[tid] = (ok && a.bias) ? a.bias[dd] : 0.0f;
-    par[kCh + tid] = (ok && a.D) ? a.D[dd] : 0.0f;
-  }
-
-  // ---- per-lane constants and state ----
-  const int64_t d = d0 + chw;
-  const bool ch_ok = d < a.dim;
-  const int64_t bd = b * a.dim + d;
-  float A[2], iA[2], h[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = a.n0 + sp * 4 + hf * 2 + j;
-    const bool valid = ch_ok && n < a.dstate;
-    const float An = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
-    A[j] = An;
-    iA[j] = valid ? 1.0f / An : 0.0f;
-    float hv = 0.0f;
-    if (!kAgg && valid) {
-      if (kc > 0)
-        hv = a.carry[(bd * a.nchunks + kc) * a.np + n];
-      else if (a.h0)
-        hv = a.h0[bd * a.dstate + n];
-    }
-    h[j] = hv;
-  }
-  float dsum_acc = 0.0f;
-  const bool gate_on = a.gated != 0;
-  const float gate_off = gate_on ? 0.0f : 1.0f;
-
-  // ---- buffer descriptors (as in the four-states layout) ----
-  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
-  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
-  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
-  const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
-  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
-  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
-  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(gate_on ? gz + row0 : gu + row0, gate_on ? nrec_ch : 0);
-  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
-  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
-
-  // B/C piece: state bn, 4-token group bg; waves 0-3 load B, 4-7 load C
-  const int bn = tid % NP;          // state of this thread's B/C piece within the pass's 16
-  const int bg = (tid / NP) % kG;
-  const bool isB = w < 4;
-
-  struct Pf {
-    V8 d, u, z;
-    V4 bc;
-  };
-  struct Keep {
-    float u[8];
-    V8 z;
-  };
-
-  auto prefetch = [&](int64_t tile, Pf& p) {
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    p.d = IO::buf_load8(rs_d, off, kVec);
-    p.u = IO::buf_load8(rs_u, off, kVec);
-    if constexpr (!kAgg) p.z = IO::buf_load8(rs_z, off, kVec);
-    const int boff = (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz);   // past dstate: reads 0
-    p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
-  };
-
-  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp, auto full_c) {
-    constexpr bool kFull = decltype(full_c)::value;
-    const int nv = kFull ? 8 : (int)max((int64_t)0, min((int64_t)8, t_end - (tile + pg * 8)));
-    float fd[8], fu[8];
-    IO::to_f32(p.d, fd);
-    IO::to_f32(p.u, fu);
-    const float bi = par[pc];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x = fd[j] + bi;
-      const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
-      const bool ok = j < nv;   // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
-      fd[j] = ok ? dl : 0.0f;
-      fu[j] = ok ? fu[j] : 0.0f;
-    }
-    float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
-#pragma unroll
-    for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
-    float* dp = dbuf + (buf * kCh + pc) * kRow + pg * 8;
-    float* up = ubuf + (buf * kCh + pc) * kRow + pg * 8;
-    reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-    reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-    reinterpret_cast<float4*>(up)[0] = make_float4(fs[0], fs[1], fs[2], fs[3]);
-    reinterpret_cast<float4*>(up)[1] = make_float4(fs[4], fs[5], fs[6], fs[7]);
-    if constexpr (!kAgg) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kp.u[j] = fu[j];
-      kp.z = p.z;
-    }
-    {
-      const int nvb = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + bg * 4)));
-      float f[4];
-      IO::to_f32(p.bc, f);
-      float* q = bcs + buf * kG * NP * 8 + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
-    }
-  };
-
-  auto epi_read = [&](float4 (&yp)[4][2]) {
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      const float4* q = reinterpret_cast<const float4*>(ypart + (s2 * kCh + pc) * kRow + pg * 8);
-      yp[s2][0] = q[0];
-      yp[s2][1] = q[1];
-    }
-  };
-  // returns false when this pass only accumulates into yacc (no y store)
-  auto epi_finish = [&](const float4 (&yp)[4][2], const Keep& kp, float (&yv)[8], int64_t tile) -> bool {
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      float* o = yv + 4 * h2;
-      o[0] = yp[0][h2].x; o[1] = yp[0][h2].y; o[2] = yp[0][h2].z; o[3] = yp[0][h2].w;
-#pragma unroll
-      for (int s2 = 1; s2 < 4; ++s2) {
-        o[0] += yp[s2][h2].x; o[1] += yp[s2][h2].y; o[2] += yp[s2][h2].z; o[3] += yp[s2][h2].w;
-      }
-    }
-    if constexpr (kMulti) {
-      // the pipelined body calls the epilogue of tile k-1 at k = 0 too, where
-      // y stores are dropped by an empty buffer descriptor; yacc is a plain
-      // pointer, so that call must not touch it
-      if (tile < t_begin) return false;
-      using IOF = Io<float>;
-      const int64_t t0 = tile + pg * 8;
-      int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-      if (d0 + pc >= a.dim) nv = 0;
-      float* ya = a.yacc + (b * a.dim + d0 + pc) * a.seqlen + t0;
-      const bool vec8 = nv == 8 && (a.seqlen & 3) == 0;
-      if (a.acc >= 2) {
-        float prev[8];
-        IOF::to_f32(vec8 ? IOF::load8(ya) : IOF::load_n(ya, nv), prev);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) yv[j] += prev[j];
-      }
-      if (a.acc < 3) {
-        if (vec8)
-          IOF::store8(ya, IOF::from_f32(yv));
-        else
-          IOF::store_n(ya, IOF::from_f32(yv), nv);
-        return false;
-      }
-    }
-    const float Dd = par[kCh + pc];
-    float zf[8];
-    IO::to_f32(kp.z, zf);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
-    return true;
-  };
-  auto epi_store_full = [&](int64_t tile, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    IO::buf_store8(rs, off, IO::from_f32(yv), kVec);
-  };
-  auto epi_store_tail = [&](int64_t tile, const float (&yv)[8]) {
-    const int64_t t0 = tile + pg * 8;
-    int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-    if (d0 + pc >= a.dim) nv = 0;
-    IO::store_n(gy + (b * a.dim + d0 + pc) * a.seqlen + t0, IO::from_f32(yv), nv);
-  };
-
-  auto body = [&](int64_t k, auto P_c, Pf& pfCur, Pf& pfOther, Keep& kpOther) {
-    constexpr int P = decltype(P_c)::value;
-    const int64_t tile = t_begin + k * T;
-    const float* drow = dbuf + (P * kCh + chw) * kRow;
-    const float* urow = ubuf + (P * kCh + chw) * kRow;
-    const int sel = lane & 15;
-    // lane 4j + kk of each row holds (B, C) of token kk, state j of the row's pair
-    const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + sp * 4 + hf * 2 + ((sel >> 2) & 1)) * 2;
-    float* yrow = ypart + (sp * kCh + chw) * kRow + 2 * hf;
-
-    float4 dv = *reinterpret_cast<const float4*>(drow);
-    float4 uv = *reinterpret_cast<const float4*>(urow);
-    float2 bcv = *reinterpret_cast<const float2*>(bcl);
-    prefetch(tile + 2 * T, pfCur);
-    float4 yp[4][2];
-    if constexpr (!kAgg) {
-      // tile k-1's partials must be read by every wave before tile k's are written
-      epi_read(yp);
-      lds_barrier();
-    }
-    const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
-
-    auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
-      constexpr int kk = decltype(kk_c)::value;
-      const float av0 = __builtin_amdgcn_exp2f(dl * A[0]);
-      const float av1 = __builtin_amdgcn_exp2f(dl * A[1]);
-      if constexpr (kEuler) {
-        const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * Delta * u
-        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
-        h[0] = fmaf(av0, h[0], s0);                                 // Abar h + s
-        h[1] = fmaf(av1, h[1], s1);
-      } else {
-        const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);       // s = B * u / A
-        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
-        h[0] = fmaf(av0, h[0] + s0, -s0);                           // Abar (h + s) - s
-        h[1] = fmaf(av1, h[1] + s1, -s1);
-      }
-      if constexpr (!kAgg) return dpp_bcast_fmac<4 + kk>(dpp_bcast_mul<kk>(bq.y, h[0]), bq.y, h[1]);   // C . h
-      return 0.0f;
-    };
-
-#pragma unroll
-    for (int g = 0; g < kG; ++g) {
-      // next group's LDS reads first, then the four tokens in one scheduling
-      // region (a DPP result needs two instructions before its first use)
-      float4 dn = dv, un = uv;
-      float2 bcn = bcv;
-      if (g + 1 < kG) {
-        dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
-        un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
-        bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
-      const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
-      const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
-      const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
-      if constexpr (!kAgg) {
-        // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
-        *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
-      } else {
-        dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
-      }
-      if constexpr (!kAgg) {
-        if (g == 1) {
-          float yv[8];
-          if (epi_finish(yp, kpOther, yv, tile - T)) epi_store_full(tile - T, yv, rs_y);
-        }
-      }
-      if (g == 2) {
-        if (tile + 2 * T <= t_end)
-          stage(tile + T, pfOther, 1 - P, kpOther, IntC<1>{});
-        else
-          stage(tile + T, pfOther, 1 - P, kpOther, IntC<0>{});
-      }
-      if (g + 1 < kG) {
-        dv = dn;
-        uv = un;
-        bcv = bcn;
-      }
-    }
-    lds_barrier();
-  };
-
-  auto last_epilogue = [&](int64_t k, const Keep& kp) {
-    if constexpr (!kAgg) {
-      float4 yp[4][2];
-      epi_read(yp);
-      float yv[8];
-      if (epi_finish(yp, kp, yv, t_begin + k * T)) epi_store_tail(t_begin + k * T, yv);
-    }
-  };
-
-  Pf pf0, pf1;
-  Keep kp0 = {}, kp1 = {};
-  prefetch(t_begin, pf0);
-  prefetch(t_begin + T, pf1);
-  __syncthreads();   // par[] visible
-  stage(t_begin, pf0, 0, kp0, IntC<0>{});
-  lds_barrier();
-  for (int64_t k = 0; k < ntile; k += 2) {
-    body(k, IntC<0>{}, pf0, pf1, kp1);
-    if (k + 1 >= ntile) {
-      last_epilogue(k, kp0);
-      break;
-    }
-    body(k + 1, IntC<1>{}, pf1, pf0, kp0);
-    if (k + 2 >= ntile) {
-      last_epilogue(k + 1, kp1);
-      break;
-    }
-  }
-
-  // ---- final state or chunk aggregate ----
-  if (ch_ok) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = a.n0 + sp * 4 + hf * 2 + j;
-      if (!kAgg) {
-        if (kc == a.nchunks - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
-      } else {
-        a.carry[(bd * a.nchunks + kc) * a.np + n] = h[j];
-      }
-    }
-    if (kAgg && sp == 0 && hf == 0) a.dsum[bd * a.nchunks + kc] = dsum_acc;
-  }
-}
-
 // Folds the chunk aggregates in time order; leaves in carry[.., k, ..] the
 // state entering chunk k.  One thread per (batch, channel, state).
 __global__ __launch_bounds__(256) void carry_kernel(float* __restrict__ carry, const float* __restrict__ dsum,
@@ -903,18 +494,6 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
                                                          int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) fs[i] = h0 ? h0[i] : 0.0f;
-}
-
-inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-template <template <typename, bool, bool, int> class Pick, typename IoT, bool kAgg>
-auto pick_kernel(bool vec, int mode) {
-  switch (mode) {
-    case 1: return vec ? Pick<IoT, kAgg, true, 1>::get() : Pick<IoT, kAgg, false, 1>::get();
-    case 2: return vec ? Pick<IoT, kAgg, true, 2>::get() : Pick<IoT, kAgg, false, 2>::get();
-    case 3: return vec ? Pick<IoT, kAgg, true, 3>::get() : Pick<IoT, kAgg, false, 3>::get();
-    default: return vec ? Pick<IoT, kAgg, true, 0>::get() : Pick<IoT, kAgg, false, 0>::get();
-  }
 }
 
 template <int NPW, int NSPLIT, int T>

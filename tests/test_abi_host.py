@@ -184,3 +184,30 @@ def test_fwd_workspace_holds_readout_sum_for_wide_state():
     assert mscan.bwd_workspace_size(b, d, 16, L, mscan.BF16) > 0
     with pytest.raises(ValueError):
         mscan.bwd_workspace_size(b, d, 17, L, mscan.BF16)
+
+
+def varlen(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, cu=P, h0=None, fs=None, y=P,
+           nseq=3, dim=64, dstate=16, total=300, io=1, flags=1, ws=None, wsb=0):
+    return lib.mamba_scan_fwd_varlen(u, delta, A_log, B, C, D, z, bias, cu, h0, fs, y, nseq, dim, dstate, total, io,
+                                     flags, ws, wsb, None)
+
+
+def test_varlen_validation_errors(lib):
+    assert varlen(lib, nseq=0) == ESHAPE
+    assert varlen(lib, cu=None) == ENULL
+    assert varlen(lib, u=None) == ENULL
+    assert varlen(lib, A_log=None) == ENULL
+    assert varlen(lib, cu=P + 4) == EALIGN
+    assert varlen(lib, u=P + 1) == EALIGN
+    assert varlen(lib, flags=4) == EUNSUP
+    assert varlen(lib, dstate=65) == EUNSUP
+    assert varlen(lib, io=7) == EDTYPE
+    assert varlen(lib, dstate=32) == EWS                        # dstate > 16 needs the fp32 readout buffer
+    assert varlen(lib, nseq=1 << 40) == EUNSUP                  # grid size
+
+
+def test_varlen_workspace_size(lib):
+    assert mscan.fwd_varlen_workspace_size(4, 64, 16, 1000) == 0
+    assert mscan.fwd_varlen_workspace_size(4, 64, 64, 1000) >= 64 * 1000 * 4
+    with pytest.raises(ValueError):
+        mscan.fwd_varlen_workspace_size(0, 64, 16, 1000)
