@@ -48,6 +48,8 @@ def _bind(path: str):
     lib.oracle_scan_step.restype = ctypes.c_int
     lib.oracle_scan_fwd_varlen.restype = ctypes.c_int
     lib.oracle_scan_fwd_varlen.argtypes = [P] * 12 + [I64] * 4 + [ctypes.c_int] * 3
+    lib.oracle_ssd_fwd.restype = ctypes.c_int
+    lib.oracle_ssd_fwd.argtypes = [P] * 11 + [I64] * 5 + [ctypes.c_int] * 3
     lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
     lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
@@ -166,6 +168,35 @@ def scan_fwd_varlen(u, delta, A_log, B, C, cu_seqlens, D=None, z=None, delta_bia
     return y, fs
 
 
+def ssd_fwd(x, dt, A_log, B, C, D=None, z=None, dt_bias=None, initial_state=None, dt_softplus: bool = True,
+            discretization: str = "zoh", nthreads: int = 0, _lib_override=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Multi-head SSM with a scalar decay per head, fp64.  x, z: (batch, L, H, P); dt: (batch, L, H);
+    B, C: (batch, L, N); A_log, D, dt_bias: (H,); initial_state: (batch, H, P, N).
+    Returns (y (batch, L, H, P), final_state (batch, H, P, N))."""
+    x = _f64(x)
+    if x.ndim != 4:
+        raise ValueError("oracle: x must be (batch, L, H, P)")
+    batch, L, H, P = x.shape
+    B = _f64(B)
+    N = B.shape[-1]
+    dt = _f64(dt, (batch, L, H))
+    A_log = _f64(A_log, (H,))
+    B = _f64(B, (batch, L, N))
+    C = _f64(C, (batch, L, N))
+    D = _f64(D, (H,))
+    z = _f64(z, (batch, L, H, P))
+    dt_bias = _f64(dt_bias, (H,))
+    initial_state = _f64(initial_state, (batch, H, P, N))
+    y = np.empty((batch, L, H, P), dtype=np.float64)
+    fs = np.empty((batch, H, P, N), dtype=np.float64)
+    rc = (_lib_override or _load()).oracle_ssd_fwd(
+        _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(initial_state),
+        _ptr(fs), _ptr(y), batch, L, H, P, N, int(bool(dt_softplus)), _euler(discretization), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_ssd_fwd returned {rc}")
+    return y, fs
+
+
 def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softplus: bool = True,
               nthreads: int = 0, _lib_override=None, discretization: str = "zoh") -> Tuple[np.ndarray, np.ndarray]:
     """One recurrent step in fp64.  Returns (y (batch, dim), new_state (batch, dim, dstate)).
@@ -269,6 +300,9 @@ class Variant:
 
     def scan_fwd_varlen(self, *a, **k):
         return scan_fwd_varlen(*a, _lib_override=self._lib, **k)
+
+    def ssd_fwd(self, *a, **k):
+        return ssd_fwd(*a, _lib_override=self._lib, **k)
 
     def scan_bwd(self, *a, **k):
         return scan_bwd(*a, _lib_override=self._lib, **k)

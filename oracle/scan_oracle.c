@@ -208,6 +208,71 @@ int oracle_scan_fwd_varlen(const double* u, const double* delta, const double* A
   return 0;
 }
 
+/*
+ * Multi-head SSM with a scalar decay per head (the state-space-duality form;
+ * State space models and Mamba, jonathanding.github.io, §5: head dim P > 1,
+ * the P channels of a head share A, and the dual matrix has
+ * Lambda_ij = prod_{t=j+1..i} a_t).  Per batch row b, head h, head channel p
+ * and state n, with A_h = -exp(A_log[h]):
+ *
+ *   Delta_t = softplus(dt[b,t,h] + dt_bias[h])        (or without softplus)
+ *   a_t     = exp(Delta_t A_h)                        scalar per (b, t, h)
+ *   w_t     = (a_t - 1) / A_h   zero-order hold       (or Delta_t: Euler, flag)
+ *   h_t[p,n]= a_t h_{t-1}[p,n] + w_t B[b,t,n] x[b,t,h,p]
+ *   y[b,t,h,p] = sum_n C[b,t,n] h_t[p,n] + D[h] x[b,t,h,p]   (times SiLU(z) if z)
+ *
+ * This is the selective scan above with A and Delta shared by the P channels
+ * of a head (B and C are shared by all heads, as they are by all channels
+ * there).  Token-major layouts (the layout of the projections that feed it):
+ *   x, z, y : (batch, L, H, P)    dt : (batch, L, H)    B, C : (batch, L, N)
+ *   A_log, D, dt_bias : (H)       initial_state, final_state : (batch, H, P, N)
+ */
+int oracle_ssd_fwd(const double* x, const double* dt, const double* A_log, const double* B, const double* C,
+                   const double* D, const double* z, const double* dt_bias, const double* initial_state,
+                   double* final_state, double* y, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                   int64_t dstate, int dt_softplus, int euler, int nthreads) {
+  if (!A_log || !y || (seqlen > 0 && (!x || !dt || !B || !C))) return 1;
+  if (batch < 0 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1) return 2;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const int64_t HP = nheads * headdim;
+  const int64_t BHP = batch * HP;
+#pragma omp parallel for schedule(static)
+  for (int64_t bhp = 0; bhp < BHP; ++bhp) {
+    const int64_t b = bhp / HP, hp = bhp % HP, hh = hp / headdim, p = hp % headdim;
+    double* h = (double*)malloc(sizeof(double) * (size_t)dstate);
+    const double A = -exp(A_log[hh]);
+    for (int64_t n = 0; n < dstate; ++n)
+      h[n] = initial_state ? initial_state[((b * nheads + hh) * headdim + p) * dstate + n] : 0.0;
+    const double bias = dt_bias ? dt_bias[hh] : 0.0;
+    const double Dh = D ? D[hh] : 0.0;
+    for (int64_t t = 0; t < seqlen; ++t) {
+      const double xv = dt[(b * seqlen + t) * nheads + hh] + bias;
+      const double Delta = dt_softplus ? oracle_softplus(xv) : xv;
+      const double a = exp(Delta * A);
+      const double w = euler ? Delta : ((A != 0.0) ? expm1(Delta * A) / A : Delta);
+      const int64_t xi = (b * seqlen + t) * HP + hp;      /* (b, t, h, p) */
+      const double* Bt = B + (b * seqlen + t) * dstate;
+      const double* Ct = C + (b * seqlen + t) * dstate;
+      double acc = 0.0;
+      for (int64_t n = 0; n < dstate; ++n) {
+        h[n] = a * h[n] + w * Bt[n] * x[xi];
+        acc += Ct[n] * h[n];
+      }
+      double yv = acc + Dh * x[xi];
+      if (z) yv *= oracle_silu(z[xi]);
+      y[xi] = yv;
+    }
+    if (final_state)
+      for (int64_t n = 0; n < dstate; ++n) final_state[((b * nheads + hh) * headdim + p) * dstate + n] = h[n];
+    free(h);
+  }
+  return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();
