@@ -262,9 +262,9 @@ def bench_bwd(args, c) -> int:
     return 0
 
 
-def _conv_graph_timing(args, step, u, stream):
-    """Times K conv launches replayed from one HIP graph: (ms per launch, wall s), or
-    None if the replayed output differs from the eager launch's."""
+def _graph_timing(args, step, u, stream):
+    """Times K launches replayed from one HIP graph: (ms per launch, wall s), or None if the
+    replayed output u differs from the eager launch's."""
     import torch
 
     # One launch is shorter than the Python call that makes it, so the K steps
@@ -281,7 +281,7 @@ def _conv_graph_timing(args, step, u, stream):
     graph.replay()
     torch.cuda.synchronize()
     if not torch.equal(u, u_eager):
-        print("bench.py: graph replay of the conv differs from the eager launch", file=sys.stderr)
+        print("bench.py: graph replay differs from the eager launch", file=sys.stderr)
         return None
     for _ in range(max(1, args.warmup // max(1, args.steps))):
         graph.replay()
@@ -330,7 +330,7 @@ def bench_conv(args, c) -> int:
         wall = time.perf_counter() - w0
         launch_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
     else:
-        r = _conv_graph_timing(args, step, u, stream)
+        r = _graph_timing(args, step, u, stream)
         if r is None:
             return 1
         launch_ms, wall = r
@@ -473,6 +473,96 @@ def bench_varlen(args, c) -> int:
     return 0
 
 
+def bench_ssd(args) -> int:
+    """Multi-head SSM with a scalar decay per head (state-space-duality form) on a layer of the same
+    width as the 1.4B-shaped forward: batch 4, L 8192, 64 heads of 64 channels (d_inner 4096),
+    d_state 128, bf16, D skip, no gate, final state."""
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import max_rel_err, ssd_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    b, L, H, P, N = 4, 8192, 64, 64, 128
+    inp = ssd_inputs(b, L, H, P, N, seed=0)
+    a = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    y = torch.empty_like(a["x"])
+    fs = torch.empty(b, H, P, N, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(strm=None):
+        mscan.ssd_fwd(a["x"], a["dt"], a["A_log"], a["B"], a["C"], D=a["D"], dt_bias=a["dt_bias"], out=y,
+                      final_state=fs, return_final_state=True, stream=strm)
+
+    for _ in range(args.warmup):
+        step(stream)
+    torch.cuda.synchronize()
+    r = _graph_timing(args, step, y, stream)
+    if r is None:
+        return 1
+    launch_ms, wall = r
+    ms_per_step = wall * 1e3 / args.steps
+    tok_ch = b * L * H * P
+    alg_bytes = 2 * tok_ch * 2 + 2 * b * L * N * 2 + b * L * H * 2 + b * H * P * N * 4 + 3 * H * 4
+    gbps = alg_bytes / (launch_ms * 1e-3) / 1e9
+    # matrix-core work as implemented per (batch, head, 64-token chunk): three 32x32 tiles of
+    # B C^T over N, C S (64 x 64 over N), the masked M X (two 32-row tiles over 32 and 64 tokens),
+    # the state update (N x 64 over 64 tokens, high and low parts)
+    chunks = b * H * ((L + 63) // 64)
+    macs = chunks * (3 * 32 * 32 * N + 64 * 64 * N + 32 * 32 * (32 + 64) * 2 + 2 * N * 64 * 64)
+    tflops = 2 * macs / (launch_ms * 1e-3) / 1e12
+
+    parity = None
+    if not args.no_parity:
+        import oracle
+
+        errs = {}
+        for bb, hh in [(0, 0), (3, 63)]:
+            sub = dict(x=inp["x"][bb:bb + 1, :, hh:hh + 1], dt=inp["dt"][bb:bb + 1, :, hh:hh + 1],
+                       A_log=inp["A_log"][hh:hh + 1], B=inp["B"][bb:bb + 1], C=inp["C"][bb:bb + 1],
+                       D=inp["D"][hh:hh + 1], dt_bias=inp["dt_bias"][hh:hh + 1])
+            yr, fr = oracle.ssd_fwd(**sub)
+            errs[f"b{bb}h{hh}"] = {"y": max_rel_err(y[bb:bb + 1, :, hh:hh + 1].cpu(), yr),
+                                   "final_state": max_rel_err(fs[bb:bb + 1, hh:hh + 1].cpu(), fr)}
+        parity = {"heads": errs, "tol": 1e-2}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = host_cores()
+        nh = 8   # a bounded sample: batch row 0, 8 heads, the whole sequence
+        sub = dict(x=inp["x"][:1, :, :nh], dt=inp["dt"][:1, :, :nh], A_log=inp["A_log"][:nh], B=inp["B"][:1],
+                   C=inp["C"][:1], D=inp["D"][:nh], dt_bias=inp["dt_bias"][:nh])
+        c0 = time.perf_counter()
+        oracle.ssd_fwd(**sub, nthreads=cores)
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(L * nh * P / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"batch row 0, {nh} of {H} heads x {P} channels x {L} tokens x {N} states, fp64, "
+                         f"{cs:.2f} s wall incl. fp64 widening of inputs"}
+
+    out = {
+        "metric": "multi-head SSM (state-space-duality form) fwd Gtok·ch/s and achieved HBM GB/s",
+        "value": round(tok_ch / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"SSD layer: batch {b}, L {L}, {H} heads x head dim {P} (d_inner {H * P}), "
+                               f"d_state {N}, bf16 io, D skip, no gate, final state, launches replayed from one "
+                               "HIP graph", "batch": b, "seqlen": L, "nheads": H, "headdim": P, "d_state": N},
+        "kernel_ms": round(launch_ms, 4),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": 2500.0, "frac": round(tflops / 2500.0, 4)},
+        "cpu_baseline": cpu,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -485,6 +575,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--ssd", action="store_true",
+                    help="time the multi-head SSM with a scalar decay per head (state-space-duality form)")
     ap.add_argument("--varlen", action="store_true",
                     help="time a variable-length batch with the forward config's channels and total tokens")
     ap.add_argument("--dstate", type=int, default=0,
@@ -521,6 +613,8 @@ def main() -> int:
         print(json.dumps({"calibrate_copy_bytes_read": n, "calibrate_copy_bytes_written": n, "launches": 3}))
         return 0
 
+    if args.ssd:
+        return bench_ssd(args)
     c = CONFIGS[args.config]
     if args.dstate:
         import dataclasses

@@ -231,6 +231,35 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
 size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
 
 /*
+ * Multi-head SSM with a scalar decay per head -- the state-space-duality form
+ * (State space models and Mamba, §5: head dim P > 1, the P channels of a head
+ * share A, the dual matrix carries Lambda_ij = prod_{t=j+1..i} a_t; computed
+ * chunk-wise with matrix products inside a chunk and the N x P state passed
+ * between chunks).  Per batch row b, head h, head channel p, state n, with
+ * A_h = -exp(A_log[h]) and Delta_t = softplus(dt[b,t,h] + dt_bias[h]):
+ *
+ *   a_t = exp(Delta_t A_h),  w_t = (a_t - 1) / A_h  (Delta_t with MAMBA_SCAN_FLAG_EULER)
+ *   h_t[p,n] = a_t h_{t-1}[p,n] + w_t B[b,t,n] x[b,t,h,p]
+ *   y[b,t,h,p] = (sum_n C[b,t,n] h_t[p,n] + D[h] x[b,t,h,p]) * SiLU(z[b,t,h,p])
+ *
+ * i.e. the selective scan above with A and Delta shared by a head's channels.
+ * Token-major layouts (as the projections that feed the layer produce them):
+ *   x, z, y          (batch, seqlen, nheads, headdim)  bf16, 16-byte aligned
+ *   dt               (batch, seqlen, nheads)           bf16
+ *   B, C             (batch, seqlen, dstate)           bf16, 16-byte aligned (shared by all heads)
+ *   A_log, D, dt_bias (nheads)                          f32 (D, dt_bias may be NULL)
+ *   initial_state, final_state (batch, nheads, headdim, dstate) f32, 16-byte aligned, NULL allowed
+ *   z                NULL means no gate
+ * Supported: io_dtype MAMBA_SCAN_BF16, headdim 64, dstate 64 or 128 (others return
+ * MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads < 2^31.  Products use bf16 operands with fp32
+ * accumulation; the state is carried in fp32.  No workspace.
+ */
+int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void* B, const void* C, const float* D,
+                  const void* z, const float* dt_bias, const float* initial_state, float* final_state, void* y,
+                  int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype,
+                  int flags, void* stream);
+
+/*
  * Causal depthwise 1-D convolution + SiLU, the step in front of the scan in the
  * Mamba block (Mamba notes, 设计 3 block pseudo-code, kernel size 4; State space
  * models and Mamba, Mamba block architecture: Conv1d -> SiLU -> SSM).  Per

@@ -25,8 +25,9 @@ STATUS = {
 }
 EXPORTED = (
     "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
-    "mamba_scan_fwd_varlen", "mamba_scan_fwd_varlen_workspace_size", "mamba_scan_step", "mamba_scan_bwd", "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd",
-    "mamba_scan_status_str", "mamba_scan_abi_version",
+    "mamba_scan_fwd_varlen", "mamba_scan_fwd_varlen_workspace_size", "mamba_scan_step", "mamba_scan_bwd",
+    "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd", "mamba_ssd_fwd", "mamba_scan_status_str",
+    "mamba_scan_abi_version",
 )
 
 _lib = None
@@ -65,6 +66,8 @@ def load_library():
     lib.mamba_scan_fwd_varlen.argtypes = [P] * 12 + [I64] * 4 + [I, I, P, SZ, P]
     lib.mamba_scan_fwd_varlen_workspace_size.restype = SZ
     lib.mamba_scan_fwd_varlen_workspace_size.argtypes = [I64] * 4 + [I]
+    lib.mamba_ssd_fwd.restype = I
+    lib.mamba_ssd_fwd.argtypes = [P] * 11 + [I64] * 5 + [I, I, P]
     lib.mamba_conv1d_fwd.restype = I
     lib.mamba_conv1d_fwd.argtypes = [P] * 6 + [I64] * 4 + [I, I, P]
     lib.mamba_scan_status_str.restype = ctypes.c_char_p
@@ -384,3 +387,43 @@ def conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tenso
                               L, K, io, int(bool(silu)), _stream(dev, stream))
     _check("mamba_conv1d_fwd", rc)
     return (u, so) if return_state else u
+
+
+def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+            D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+            dt_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+            dt_softplus: bool = True, return_final_state: bool = False, *, out: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None, discretization: str = "zoh", stream=None):
+    """Multi-head SSM with a scalar decay per head (state-space-duality form).  x, z: (batch, L, H, P);
+    dt: (batch, L, H); B, C: (batch, L, N) in bfloat16; A_log, D, dt_bias: (H,) float32;
+    initial_state (batch, H, P, N) float32.  Returns y (batch, L, H, P), or (y, final_state)."""
+    lib = load_library()
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, L, H, P)")
+    batch, L, H, P = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("ssd_fwd needs device tensors (HIP)")
+    io = _io_dtype(x)
+    iot = x.dtype
+    N = B.shape[-1] if B.dim() == 3 else -1
+    _req("x", x, (batch, L, H, P), iot, dev)
+    _req("dt", dt, (batch, L, H), iot, dev)
+    _req("A_log", A_log, (H,), torch.float32, dev)
+    _req("B", B, (batch, L, N), iot, dev)
+    _req("C", C, (batch, L, N), iot, dev)
+    _req("D", D, (H,), torch.float32, dev)
+    _req("z", z, (batch, L, H, P), iot, dev)
+    _req("dt_bias", dt_bias, (H,), torch.float32, dev)
+    _req("initial_state", initial_state, (batch, H, P, N), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, L, H, P), dtype=iot, device=dev)
+    _req("out", y, (batch, L, H, P), iot, dev)
+    fs = final_state
+    if fs is None and return_final_state:
+        fs = torch.empty((batch, H, P, N), dtype=torch.float32, device=dev)
+    _req("final_state", fs, (batch, H, P, N), torch.float32, dev)
+    rc = lib.mamba_ssd_fwd(_ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias),
+                           _ptr(initial_state), _ptr(fs), _ptr(y), batch, L, H, P, N, io,
+                           _flags(dt_softplus, discretization), _stream(dev, stream))
+    _check("mamba_ssd_fwd", rc)
+    return (y, fs) if return_final_state else y

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIB_DIR, "libmamba_scan.so")
-SOURCES = ["api.hip", "scan_fwd.hip", "scan_fwd_varlen.hip", "scan_step.hip", "scan_bwd.hip", "conv1d.hip"]
+SOURCES = ["api.hip", "scan_fwd.hip", "scan_fwd_varlen.hip", "scan_step.hip", "scan_bwd.hip", "conv1d.hip", "ssd_fwd.hip"]
 ARCH = "gfx950"
 
 

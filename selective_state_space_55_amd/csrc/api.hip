@@ -232,6 +232,37 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
 }
 
+int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void* B, const void* C, const float* D,
+                  const void* z, const float* dt_bias, const float* initial_state, float* final_state, void* y,
+                  int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int io_dtype,
+                  int flags, void* stream) {
+  if (io_dtype != MAMBA_SCAN_F32 && io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
+  if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1) return MAMBA_SCAN_ERR_SHAPE;
+  if (io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_UNSUPPORTED;              // bf16 operands only
+  if (headdim != 64 || (dstate != 64 && dstate != 128)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!mul_ok(batch, nheads, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (!mul_ok(t, seqlen, &t) || !mul_ok(t, headdim * 2, &t)) return MAMBA_SCAN_ERR_SHAPE;
+  if (!A_log) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
+  const void* v16[] = {x, B, C, z, y, initial_state, final_state};   // 16-byte vector accesses
+  for (const void* p : v16)
+    if (p && !aligned(p, 16)) return MAMBA_SCAN_ERR_ALIGN;
+  if (dt && !aligned(dt, 2)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, dt_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::SsdArgs a{};
+  a.x = x; a.dt = dt; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.dt_bias = dt_bias;
+  a.h0 = initial_state; a.final_state = final_state; a.y = y;
+  a.batch = batch; a.seqlen = seqlen; a.nheads = nheads; a.headdim = headdim; a.dstate = dstate;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
+  hipError_t e = mscan::launch_ssd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
 int mamba_conv1d_fwd(const void* x, const float* weight, const float* bias, const void* conv_state_in,
                      void* conv_state_out, void* u, int64_t batch, int64_t dim, int64_t seqlen, int64_t kernel_size,
                      int io_dtype, int silu, void* stream) {

@@ -130,4 +130,23 @@ struct ConvArgs {
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
 
+// Multi-head SSM with a scalar decay per head (state-space-duality form), bf16 io.
+struct SsdArgs {
+  const void* x;          // (batch, L, H, P) bf16
+  const void* dt;         // (batch, L, H) bf16
+  const float* A_log;     // (H)
+  const void* B;          // (batch, L, N) bf16
+  const void* C;          // (batch, L, N) bf16
+  const float* D;         // (H) or NULL
+  const void* z;          // (batch, L, H, P) bf16 or NULL
+  const float* dt_bias;   // (H) or NULL
+  const float* h0;        // (batch, H, P, N) or NULL
+  float* final_state;     // (batch, H, P, N) or NULL
+  void* y;                // (batch, L, H, P) bf16
+  int64_t batch, seqlen, nheads, headdim, dstate;
+  int softplus, euler;
+};
+
+hipError_t launch_ssd(const SsdArgs& a, hipStream_t stream);
+
 }  // namespace mscan

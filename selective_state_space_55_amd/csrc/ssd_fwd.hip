@@ -1,0 +1,449 @@
+// ssd_fwd.hip -- multi-head SSM with a scalar decay per head (the
+// state-space-duality form) on gfx950 matrix cores.
+//
+// Method (State space models and Mamba, jonathanding.github.io, §5): the P
+// channels of a head share A, so the decay a_t = exp(Delta_t A_h) is one scalar
+// per (batch, token, head); the sequence is cut into chunks of Q tokens; inside
+// a chunk the output is a Q x Q masked matrix product (the dual,
+// attention-like form with mask Lambda_ij = prod_{t=j+1..i} a_t), and only the
+// N x P state crosses chunk boundaries.  Per chunk, with cum_i the running sum
+// of log a_t inside the chunk and w_j the input weight ((a_j - 1)/A_h, or
+// Delta_j for the Euler input term):
+//
+//   G      = B C^T                               (Q x Q, over N)
+//   M_ij   = G_ji exp(cum_i - cum_j) w_j  (j <= i, else 0)
+//   Y      = diag(exp(cum)) C S_in + M X + D X   (Q x P), times SiLU(z)
+//   S_out  = exp(cum_Q) S_in + (B diag(exp(cum_Q - cum_j) w_j))^T X   (N x P)
+//
+// Mapping.  One workgroup (8 waves, two per SIMD) owns one (batch, head) and
+// walks its chunks in order, keeping S (N x P, fp32) in MFMA accumulators --
+// nothing but x, dt, B, C, z in and y, the final state out touches HBM.
+// Q = 64, P = 64, N = 64 or 128.  Every product is v_mfma_f32_32x32x16_bf16
+// on bf16 operands in LDS with fp32 accumulation; the operand layouts (lane l
+// holds 8 consecutive k) make each operand one 16-byte LDS read.  Per chunk:
+//   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes);
+//              one wave turns dt into log a (softplus, A_h), w and a running
+//              sum over the chunk (DPP prefix scan)
+//   A2      -- transposes by column reads of the staged rows (x^T, B^T, and
+//              x scaled by exp(cum_Q - cum_j) w_j as a high plus a low bf16
+//              part, so the state update keeps ~16 bits); waves 0-2: the
+//              three causal 32 x 32 tiles of B C^T and the masked, decayed M;
+//              waves 4-7: the Y tiles' C S_in, rows scaled by exp(cum_i)
+//   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); every wave (N =
+//              128) one 32 x 32 tile of S = exp(cum_Q) S + B^T Xs
+//   epilogue -- y = Y + D x (x kept in registers from its load), SiLU(z) gate,
+//              one 16-byte store per thread
+// Three barriers per chunk; chunk c+1's global loads are issued at the start
+// of A2 of chunk c.
+#include "internal.h"
+#include "io.h"
+
+namespace mscan {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kQ = 64;      // tokens per chunk
+constexpr int kP = 64;      // head dim
+constexpr int kPadH = 8;    // LDS row padding, bf16 elements (keeps rows 16-byte aligned)
+constexpr int kNT = 512;    // threads per workgroup
+
+struct SArgs {
+  const uint16_t* x;        // (batch, L, H, P) bf16
+  const uint16_t* dt;       // (batch, L, H)
+  const float* A_log;       // (H)
+  const uint16_t* B;        // (batch, L, N)
+  const uint16_t* C;        // (batch, L, N)
+  const float* D;           // (H) or null
+  const uint16_t* z;        // (batch, L, H, P) or null
+  const float* dt_bias;     // (H) or null
+  const float* h0;          // (batch, H, P, N) or null
+  float* hT;                // (batch, H, P, N) or null
+  uint16_t* y;              // (batch, L, H, P)
+  int64_t L;
+  int H, softplus, euler;
+};
+
+template <int N>
+struct SsdLds {
+  static constexpr int kRowQ = kQ + kPadH;    // rows over Q tokens
+  static constexpr int kRowN = N + kPadH;     // rows over N states
+  static constexpr int kRowP = kP + kPadH;    // rows over P channels
+  static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
+  static constexpr int kCs = kQ * kRowN;      // C     [i][n]
+  static constexpr int kBs = kQ * kRowN;      // B     [j][n]
+  static constexpr int kXT = kP * kRowQ;      // x^T   [p][j]   (also the two scaled parts)
+  static constexpr int kBT = N * kRowQ;       // B^T   [n][j]
+  static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
+  static constexpr int kST = kP * kRowN;      // S^T   [p][n]
+  static constexpr int kHalves = kXtm + kCs + kBs + 3 * kXT + kBT + kMs + kST;
+  static constexpr int kYRow = kP + 4;        // Y fp32 [i][p]
+  static constexpr int kFloats = kQ * kYRow + 4 * kQ + 4;
+  static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
+};
+
+__device__ __forceinline__ bf16x8 lds_b8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float bf(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// exp(x) - 1 without cancellation for small |x| (Taylor to x^3 below 1e-2)
+__device__ __forceinline__ float expm1_f(float x) {
+  if (fabsf(x) < 1e-2f) return x * (1.0f + x * (0.5f + x * (1.0f / 6.0f)));
+  return __expf(x) - 1.0f;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add_src(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, true));
+}
+
+// inclusive prefix sum over the 64 lanes: shifts by 1, 2, 4, 8 inside each
+// 16-lane row, then row 0's total into row 1, rows 0-1's into rows 2-3, etc.
+__device__ __forceinline__ float wave_prefix_sum(float v) {
+  v += dpp_add_src<0x111, 0xf>(v);   // row_shr:1
+  v += dpp_add_src<0x112, 0xf>(v);   // row_shr:2
+  v += dpp_add_src<0x114, 0xf>(v);   // row_shr:4
+  v += dpp_add_src<0x118, 0xf>(v);   // row_shr:8
+  v += dpp_add_src<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v += dpp_add_src<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// 8 bf16 of one column (stride `stride` elements) packed into 16 bytes
+__device__ __forceinline__ uint4 col8(const uint16_t* p, int stride) {
+  uint32_t w[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) w[k] = (uint32_t)p[(2 * k) * stride] | ((uint32_t)p[(2 * k + 1) * stride] << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <int N>
+__global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
+  using L = SsdLds<N>;
+  constexpr int kRowQ = L::kRowQ, kRowN = L::kRowN, kRowP = L::kRowP, kYRow = L::kYRow;
+  extern __shared__ __align__(16) uint16_t sm[];
+  uint16_t* Xtm = sm;
+  uint16_t* Cs = Xtm + L::kXtm;
+  uint16_t* Bs = Cs + L::kCs;
+  uint16_t* XT = Bs + L::kBs;
+  uint16_t* XsH = XT + L::kXT;
+  uint16_t* XsL = XsH + L::kXT;
+  uint16_t* BT = XsL + L::kXT;
+  uint16_t* Ms = BT + L::kBT;
+  uint16_t* ST = Ms + L::kMs;
+  float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
+  float* cum = Yf + kQ * kYRow;                         // running sum of log a in the chunk
+  float* ecum = cum + kQ;                               // exp(cum_i)
+  float* scl = ecum + kQ;                               // exp(cum_Q - cum_j) w_j
+  float* wv = scl + kQ;                                 // w_j
+  float* atot = wv + kQ;                                // exp(cum_Q)
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, h32 = lane >> 5;
+  const int64_t bh = blockIdx.x;
+  const int H = a.H;
+  const int64_t b = bh / H;
+  const int h = (int)(bh % H);
+  const int64_t Lq = a.L;
+  const int64_t nchunk = (Lq + kQ - 1) / kQ;
+
+  const int64_t xs_t = (int64_t)H * kP;   // x/z/y token stride
+  const uint16_t* xb = a.x + b * Lq * xs_t + (int64_t)h * kP;
+  const uint16_t* zb = a.z ? a.z + b * Lq * xs_t + (int64_t)h * kP : nullptr;
+  uint16_t* yb = a.y + b * Lq * xs_t + (int64_t)h * kP;
+  const uint16_t* Bb = a.B + b * Lq * N;
+  const uint16_t* Cb = a.C + b * Lq * N;
+  const uint16_t* dtb = a.dt + b * Lq * H + h;
+
+  const float Ah = -__expf(a.A_log[h]);
+  const float Dh = a.D ? a.D[h] : 0.0f;
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+
+  // x / z / y piece of this thread: token xj, channels xp8 .. xp8 + 7
+  const int xj = tid >> 3, xp8 = (tid & 7) * 8;
+  // B / C pieces: e = tid + 512 r -> token e / (N/8), states 8 (e % (N/8))
+  constexpr int kBCr = kQ * (N / 8) / kNT;    // 1 (N = 64) or 2 (N = 128)
+  constexpr int kDtWave = 3;
+
+  struct Pf {
+    uint4 x, z;
+    uint4 bq[kBCr], cq[kBCr];
+    uint32_t dt;
+  };
+  auto ld16 = [&](const uint16_t* p, bool ok) -> uint4 {
+    return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+  };
+  auto prefetch = [&](int64_t c, Pf& f) {
+    const int64_t t0 = c * kQ;
+    {
+      const int64_t t = t0 + xj;
+      const bool ok = t < Lq;
+      f.x = ld16(xb + t * xs_t + xp8, ok);
+      f.z = zb ? ld16(zb + t * xs_t + xp8, ok) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < kBCr; ++r) {
+      const int e = tid + kNT * r;
+      const int j = e / (N / 8), n8 = (e % (N / 8)) * 8;
+      const int64_t t = t0 + j;
+      const bool ok = t < Lq;
+      f.bq[r] = ld16(Bb + t * N + n8, ok);
+      f.cq[r] = ld16(Cb + t * N + n8, ok);
+    }
+    if (w == kDtWave) {
+      const int64_t t = t0 + lane;
+      f.dt = t < Lq ? (uint32_t)dtb[t * H] : 0u;
+    }
+  };
+
+  // ---- state tiles: S[n][p] rows 32 nb .., columns 32 pb .. ----
+  constexpr int kSTiles = (N / 32) * 2;             // 8 (N = 128) or 4 (N = 64)
+  const bool has_s = w < kSTiles;
+  const int s_nb = w >> 1, s_pb = w & 1;
+  f32x16 S = {};
+  if (has_s) {
+    const int p = s_pb * 32 + l32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = s_nb * 32 + 8 * q + 4 * h32;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.h0) v = *reinterpret_cast<const float4*>(a.h0 + ((bh * kP + p) * N + n));
+      S[4 * q + 0] = v.x; S[4 * q + 1] = v.y; S[4 * q + 2] = v.z; S[4 * q + 3] = v.w;
+    }
+  }
+  auto write_ST = [&]() {
+    if (!has_s) return;
+    const int p = s_pb * 32 + l32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = s_nb * 32 + 8 * q + 4 * h32;
+      *reinterpret_cast<uint2*>(ST + p * kRowN + n) =
+          make_uint2(pack_bf16x2(S[4 * q + 0], S[4 * q + 1]), pack_bf16x2(S[4 * q + 2], S[4 * q + 3]));
+    }
+  };
+  write_ST();
+
+  // Y tiles (waves 4-7): rows 32 yi .., columns 32 yp ..
+  const bool has_y = w >= 4;
+  const int yi = (w >> 1) & 1, yp = w & 1;
+
+  Pf pf;
+  prefetch(0, pf);
+  uint4 xcur, zcur;
+
+  for (int64_t c = 0; c < nchunk; ++c) {
+    const int64_t t0 = c * kQ;
+    // ---- stage: rows as loaded; decay terms ----
+    xcur = pf.x;
+    zcur = pf.z;
+    *reinterpret_cast<uint4*>(Xtm + xj * kRowP + xp8) = pf.x;
+#pragma unroll
+    for (int r = 0; r < kBCr; ++r) {
+      const int e = tid + kNT * r;
+      const int j = e / (N / 8), n8 = (e % (N / 8)) * 8;
+      *reinterpret_cast<uint4*>(Cs + j * kRowN + n8) = pf.cq[r];
+      *reinterpret_cast<uint4*>(Bs + j * kRowN + n8) = pf.bq[r];
+    }
+    if (w == kDtWave) {
+      const bool ok = t0 + lane < Lq;
+      const float x = bf(pf.dt) + bias;
+      float Delta = a.softplus ? softplus_log2e(x) * 0.6931471805599453f : x;
+      Delta = ok ? Delta : 0.0f;                       // past the end: a = 1, w = 0 (state unchanged)
+      const float la = Delta * Ah;
+      const float wj = a.euler ? Delta : (Ah != 0.0f ? expm1_f(la) / Ah : Delta);
+      const float cs = wave_prefix_sum(la);
+      const float tot = __shfl(cs, 63);
+      cum[lane] = cs;
+      ecum[lane] = __expf(cs);
+      scl[lane] = __expf(tot - cs) * wj;
+      wv[lane] = wj;
+      if (lane == 0) atot[0] = __expf(tot);
+    }
+    __syncthreads();
+
+    // ---- A2: next loads; transposes; G -> M (waves 0-2); C S_in (waves 4-7) ----
+    if (c + 1 < nchunk) prefetch(c + 1, pf);
+    {
+      // x^T and the scaled x: column p of tokens 8 w .. 8 w + 7
+      const int p = lane, j0 = 8 * w;
+      const uint4 col = col8(Xtm + j0 * kRowP + p, kRowP);
+      *reinterpret_cast<uint4*>(XT + p * kRowQ + j0) = col;
+      const uint32_t cw[4] = {col.x, col.y, col.z, col.w};
+      const float4 s0 = *reinterpret_cast<const float4*>(scl + j0);
+      const float4 s1 = *reinterpret_cast<const float4*>(scl + j0 + 4);
+      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float e0 = bf(cw[k] & 0xffffu) * sc[2 * k], e1 = bf(cw[k] >> 16) * sc[2 * k + 1];
+        hi[k] = pack_bf16x2(e0, e1);
+        lo[k] = pack_bf16x2(e0 - bf(hi[k] & 0xffffu), e1 - bf(hi[k] >> 16));
+      }
+      *reinterpret_cast<uint4*>(XsH + p * kRowQ + j0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(XsL + p * kRowQ + j0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    }
+#pragma unroll
+    for (int r = 0; r < N / 64; ++r) {
+      // B^T: column n of tokens 8 j8 .. 8 j8 + 7
+      const int e = tid + kNT * r;
+      const int n = e % N, j0 = 8 * (e / N);
+      *reinterpret_cast<uint4*>(BT + n * kRowQ + j0) = col8(Bs + j0 * kRowN + n, kRowN);
+    }
+    f32x16 yacc = {};
+    if (w < 3) {
+      // G^T tile (rows j-block jb, columns i-block ib) over N, two accumulation chains
+      const int jb = w == 2 ? 1 : 0, ib = w == 0 ? 0 : 1;
+      f32x16 g0 = {}, g1 = {};
+#pragma unroll
+      for (int s = 0; s < N / 16; s += 2) {
+        g0 = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowN + 16 * s + 8 * h32),
+                  lds_b8(Cs + (ib * 32 + l32) * kRowN + 16 * s + 8 * h32), g0);
+        g1 = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32),
+                  lds_b8(Cs + (ib * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32), g1);
+      }
+      // M[i][j] = G^T[j][i] exp(cum_i - cum_j) w_j for j <= i: the lane holds column i, rows j in runs of 4
+      const int i = ib * 32 + l32;
+      const float ci = cum[i];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j0 = jb * 32 + 8 * q + 4 * h32;
+        const float4 cj = *reinterpret_cast<const float4*>(cum + j0);
+        const float4 wj = *reinterpret_cast<const float4*>(wv + j0);
+        const float cja[4] = {cj.x, cj.y, cj.z, cj.w}, wja[4] = {wj.x, wj.y, wj.z, wj.w};
+        float m4[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          m4[r] = (j0 + r <= i) ? (g0[4 * q + r] + g1[4 * q + r]) * __expf(ci - cja[r]) * wja[r] : 0.0f;
+        *reinterpret_cast<uint2*>(Ms + i * kRowQ + j0) = make_uint2(pack_bf16x2(m4[0], m4[1]), pack_bf16x2(m4[2], m4[3]));
+      }
+    } else if (has_y) {
+      // C S_in over N (two chains), rows scaled by exp(cum_i)
+      f32x16 y1 = {};
+#pragma unroll
+      for (int s = 0; s < N / 16; s += 2) {
+        yacc = mfma(lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * s + 8 * h32),
+                    lds_b8(ST + (yp * 32 + l32) * kRowN + 16 * s + 8 * h32), yacc);
+        y1 = mfma(lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32),
+                  lds_b8(ST + (yp * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32), y1);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 e = *reinterpret_cast<const float4*>(ecum + yi * 32 + 8 * q + 4 * h32);
+        yacc[4 * q + 0] = (yacc[4 * q + 0] + y1[4 * q + 0]) * e.x;
+        yacc[4 * q + 1] = (yacc[4 * q + 1] + y1[4 * q + 1]) * e.y;
+        yacc[4 * q + 2] = (yacc[4 * q + 2] + y1[4 * q + 2]) * e.z;
+        yacc[4 * q + 3] = (yacc[4 * q + 3] + y1[4 * q + 3]) * e.w;
+      }
+    }
+    __syncthreads();
+
+    // ---- A3: Y += M x (waves 4-7) -> Yf; S = exp(cum_Q) S + B^T (x_hi + x_lo) ----
+    if (has_y) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (yi == 0 && s >= 2) break;                 // rows 0..31 see tokens 0..31 only
+        yacc = mfma(lds_b8(Ms + (yi * 32 + l32) * kRowQ + 16 * s + 8 * h32),
+                    lds_b8(XT + (yp * 32 + l32) * kRowQ + 16 * s + 8 * h32), yacc);
+      }
+      const int p = yp * 32 + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = yacc[4 * q + r];
+    }
+    if (has_s) {
+      const float at = atot[0];
+      f32x16 slo = {};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] *= at;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 av = lds_b8(BT + (s_nb * 32 + l32) * kRowQ + 16 * s + 8 * h32);
+        S = mfma(av, lds_b8(XsH + (s_pb * 32 + l32) * kRowQ + 16 * s + 8 * h32), S);
+        slo = mfma(av, lds_b8(XsL + (s_pb * 32 + l32) * kRowQ + 16 * s + 8 * h32), slo);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] += slo[r];
+    }
+    write_ST();
+    __syncthreads();
+
+    // ---- epilogue: token xj, channels xp8 .. +7: y = Y + D x, gate, store ----
+    {
+      const int64_t t = t0 + xj;
+      if (t < Lq) {
+        const float4 y0 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8);
+        const float4 y1 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4);
+        const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+        const uint32_t xw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
+        const uint32_t zw[4] = {zcur.x, zcur.y, zcur.z, zcur.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float v0 = fmaf(Dh, bf(xw[q] & 0xffffu), yv[2 * q]);
+          float v1 = fmaf(Dh, bf(xw[q] >> 16), yv[2 * q + 1]);
+          if (zb) {
+            v0 *= silu(bf(zw[q] & 0xffffu));
+            v1 *= silu(bf(zw[q] >> 16));
+          }
+          o[q] = pack_bf16x2(v0, v1);
+        }
+        *reinterpret_cast<uint4*>(yb + t * xs_t + xp8) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+    }
+  }
+
+  // ---- final state ----
+  if (a.hT && has_s) {
+    const int p = s_pb * 32 + l32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = s_nb * 32 + 8 * q + 4 * h32;
+      *reinterpret_cast<float4*>(a.hT + ((bh * kP + p) * N + n)) =
+          make_float4(S[4 * q], S[4 * q + 1], S[4 * q + 2], S[4 * q + 3]);
+    }
+  }
+}
+
+template <int N>
+hipError_t run_ssd(const SArgs& a, int64_t batch, hipStream_t s) {
+  const size_t lds = SsdLds<N>::bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)ssd_fwd_kernel<N>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ssd_fwd_kernel<N>, dim3((unsigned)(batch * a.H)), dim3(kNT), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_ssd(const SsdArgs& p, hipStream_t stream) {
+  SArgs a{};
+  a.x = static_cast<const uint16_t*>(p.x);
+  a.dt = static_cast<const uint16_t*>(p.dt);
+  a.A_log = p.A_log;
+  a.B = static_cast<const uint16_t*>(p.B);
+  a.C = static_cast<const uint16_t*>(p.C);
+  a.D = p.D;
+  a.z = static_cast<const uint16_t*>(p.z);
+  a.dt_bias = p.dt_bias;
+  a.h0 = p.h0;
+  a.hT = p.final_state;
+  a.y = static_cast<uint16_t*>(p.y);
+  a.L = p.seqlen;
+  a.H = (int)p.nheads;
+  a.softplus = p.softplus;
+  a.euler = p.euler;
+  return p.dstate == 128 ? run_ssd<128>(a, p.batch, stream) : run_ssd<64>(a, p.batch, stream);
+}
+
+}  // namespace mscan

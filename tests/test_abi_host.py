@@ -24,7 +24,7 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba_(?:scan|conv1d)_\w+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mamba_(?:scan|conv1d|ssd)_\w+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -211,3 +211,23 @@ def test_varlen_workspace_size(lib):
     assert mscan.fwd_varlen_workspace_size(4, 64, 64, 1000) >= 64 * 1000 * 4
     with pytest.raises(ValueError):
         mscan.fwd_varlen_workspace_size(0, 64, 16, 1000)
+
+
+def ssd(lib, x=P, dt=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None, fs=None, y=P, batch=2, L=100,
+        H=4, hd=64, N=128, io=1, flags=1):
+    return lib.mamba_ssd_fwd(x, dt, A_log, B, C, D, z, bias, h0, fs, y, batch, L, H, hd, N, io, flags, None)
+
+
+def test_ssd_validation_errors(lib):
+    assert ssd(lib, io=0) == EUNSUP                  # bf16 operands only
+    assert ssd(lib, io=5) == EDTYPE
+    assert ssd(lib, hd=32) == EUNSUP
+    assert ssd(lib, N=16) == EUNSUP
+    assert ssd(lib, flags=8) == EUNSUP
+    assert ssd(lib, batch=0) == ESHAPE
+    assert ssd(lib, L=-1) == ESHAPE
+    assert ssd(lib, x=None) == ENULL
+    assert ssd(lib, A_log=None) == ENULL
+    assert ssd(lib, x=P + 2) == EALIGN               # 16-byte vector loads
+    assert ssd(lib, h0=P + 4) == EALIGN
+    assert ssd(lib, batch=1 << 20, H=1 << 12) == EUNSUP

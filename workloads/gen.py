@@ -20,7 +20,8 @@ import torch
 from .configs import Config, get_config
 
 # stream keys, fixed order
-K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS, K_CONVW, K_CONVB, K_CONVS = range(14)
+(K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS, K_CONVW, K_CONVB, K_CONVS,
+ K_SSDA) = range(15)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -179,3 +180,28 @@ def conv_inputs(batch: int, dim: int, seqlen: int, K: int, io: str, *, seed: int
     if state:
         st = _normal_rows(seed, (K_CONVS,), batch * dim, K - 1, io, threads=threads).view(batch, dim, K - 1)
     return x, w, bias, st
+
+
+def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, *, seed: int = 0,
+               gated: bool = False, initial_state: bool = False, threads: Optional[int] = None):
+    """Inputs of the multi-head SSM (state-space-duality form), token-major, bf16 io:
+    x, z (batch, L, H, P) ~ N(0, 1); dt (batch, L, H) ~ N(0, 1); B, C (batch, L, N) ~ N(0, 1/N) (a
+    readout over N states then has unit scale); A_log = log(U[1, 16]) per head; D ~ N(0, 1);
+    dt_bias = log(expm1(U[1e-3, 1e-1])) per head; initial_state (batch, H, P, N) ~ N(0, 0.1^2)."""
+    x = _normal_rows(seed, (K_U,), batch * seqlen, nheads * headdim, "bf16", threads=threads)
+    dt = _normal_rows(seed, (K_DELTA,), batch * seqlen, nheads, "bf16", threads=threads)
+    B = _normal_rows(seed, (K_B,), batch * seqlen, dstate, "bf16", std=1.0 / math.sqrt(dstate), threads=threads)
+    C = _normal_rows(seed, (K_C,), batch * seqlen, dstate, "bf16", std=1.0 / math.sqrt(dstate), threads=threads)
+    z = (_normal_rows(seed, (K_Z,), batch * seqlen, nheads * headdim, "bf16", threads=threads)
+         .view(batch, seqlen, nheads, headdim) if gated else None)
+    A_log = torch.from_numpy(np.log(_gen(seed, (K_SSDA, 0)).uniform(1.0, 16.0, size=nheads)).astype(np.float32))
+    D = torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(nheads, dtype=np.float32))
+    u = _gen(seed, (K_BIAS, 0)).uniform(1e-3, 1e-1, size=nheads)
+    dt_bias = torch.from_numpy(np.log(np.expm1(u)).astype(np.float32))
+    h0 = None
+    if initial_state:
+        h0 = torch.from_numpy(_gen(seed, (K_STATE, 0)).standard_normal((batch, nheads, headdim, dstate),
+                                                                        dtype=np.float32) * np.float32(0.1))
+    return dict(x=x.view(batch, seqlen, nheads, headdim), dt=dt.view(batch, seqlen, nheads), A_log=A_log,
+                B=B.view(batch, seqlen, dstate), C=C.view(batch, seqlen, dstate), D=D, z=z, dt_bias=dt_bias,
+                initial_state=h0)
