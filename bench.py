@@ -532,15 +532,14 @@ def bench_ssd(args) -> int:
         import oracle
 
         cores = host_cores()
-        nh = 8   # a bounded sample: batch row 0, 8 heads, the whole sequence
-        sub = dict(x=inp["x"][:1, :, :nh], dt=inp["dt"][:1, :, :nh], A_log=inp["A_log"][:nh], B=inp["B"][:1],
-                   C=inp["C"][:1], D=inp["D"][:nh], dt_bias=inp["dt_bias"][:nh])
+        # the whole workload (a few seconds of fp64 work on the host cores)
         c0 = time.perf_counter()
-        oracle.ssd_fwd(**sub, nthreads=cores)
+        oracle.ssd_fwd(inp["x"], inp["dt"], inp["A_log"], inp["B"], inp["C"], D=inp["D"], dt_bias=inp["dt_bias"],
+                       nthreads=cores)
         cs = time.perf_counter() - c0
-        cpu = {"value": round(L * nh * P / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
-               "sample": f"batch row 0, {nh} of {H} heads x {P} channels x {L} tokens x {N} states, fp64, "
-                         f"{cs:.2f} s wall incl. fp64 widening of inputs"}
+        cpu = {"value": round(tok_ch / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": cores, "kind": "oracle",
+               "sample": f"the whole workload: {b} batch rows x {H} heads x {P} channels x {L} tokens x {N} states, "
+                         f"fp64, {cs:.2f} s wall incl. fp64 widening of inputs"}
 
     out = {
         "metric": "multi-head SSM (state-space-duality form) fwd Gtok·ch/s and achieved HBM GB/s",

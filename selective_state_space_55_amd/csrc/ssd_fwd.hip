@@ -24,17 +24,22 @@
 //   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes);
 //              one wave turns dt into log a (softplus, A_h), w and a running
 //              sum over the chunk (DPP prefix scan)
-//   A2      -- transposes by column reads of the staged rows (x^T, B^T, and
-//              x scaled by exp(cum_Q - cum_j) w_j as a high plus a low bf16
-//              part, so the state update keeps ~16 bits); waves 0-2: the
-//              three causal 32 x 32 tiles of B C^T and the masked, decayed M;
-//              waves 4-7: the Y tiles' C S_in, rows scaled by exp(cum_i)
+//   A2      -- x scaled by exp(cum_Q - cum_j) w_j as a high plus a low bf16
+//              part (so the state update keeps ~16 bits), token-major rows;
+//              waves 0-2: the three causal 32 x 32 tiles of B C^T and the
+//              masked, decayed M; waves 4-7: the Y tiles' C S_in, rows scaled
+//              by exp(cum_i)
 //   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); every wave (N =
 //              128) one 32 x 32 tile of S = exp(cum_Q) S + B^T Xs
 //   epilogue -- y = Y + D x (x kept in registers from its load), SiLU(z) gate,
 //              one 16-byte store per thread
-// Three barriers per chunk; chunk c+1's global loads are issued at the start
-// of A2 of chunk c.
+// Operands whose k (token) index must be contiguous per lane -- x for M x, B
+// and the scaled x for the state update -- are read straight from the
+// token-major tiles with ds_read_b64_tr_b16 (gfx950's transposing LDS read:
+// in each 16-lane group, lane 4a + c receives element c of the 4-element row
+// pieces addressed by lanes a, a + 4, a + 8, a + 12), so nothing is transposed
+// explicitly.  Three barriers per chunk; chunk c+1's global loads are issued
+// at the start of A2 of chunk c.
 #include "internal.h"
 #include "io.h"
 
@@ -73,11 +78,10 @@ struct SsdLds {
   static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
   static constexpr int kCs = kQ * kRowN;      // C     [i][n]
   static constexpr int kBs = kQ * kRowN;      // B     [j][n]
-  static constexpr int kXT = kP * kRowQ;      // x^T   [p][j]   (also the two scaled parts)
-  static constexpr int kBT = N * kRowQ;       // B^T   [n][j]
+  static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], high and low parts
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
   static constexpr int kST = kP * kRowN;      // S^T   [p][n]
-  static constexpr int kHalves = kXtm + kCs + kBs + 3 * kXT + kBT + kMs + kST;
+  static constexpr int kHalves = kXtm + kCs + kBs + 2 * kXs + kMs + kST;
   static constexpr int kYRow = kP + 4;        // Y fp32 [i][p]
   static constexpr int kFloats = kQ * kYRow + 4 * kQ + 4;
   static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
@@ -116,12 +120,23 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   return v;
 }
 
-// 8 bf16 of one column (stride `stride` elements) packed into 16 bytes
-__device__ __forceinline__ uint4 col8(const uint16_t* p, int stride) {
-  uint32_t w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) w[k] = (uint32_t)p[(2 * k) * stride] | ((uint32_t)p[(2 * k + 1) * stride] << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint2 lds_tr16(const uint16_t* p) {
+  const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Operand of a 32x32x16 MFMA whose k index runs along the rows of a row-major
+// bf16 tile: lane l gets rows k0 + 8 (l / 32) .. + 7 of column n0 + l % 32.
+// Two transposing reads of 4 rows each; in 16-lane group g the lane
+// m = a + 4 kk addresses row k0 + 8 (g / 2) + kk, columns n0 + 16 (g % 2) + 4 a .. + 3.
+__device__ __forceinline__ bf16x8 lds_opnd_tr(const uint16_t* base, int stride, int k0, int n0, int lane) {
+  const int g = lane >> 4, m = lane & 15;
+  const uint16_t* p = base + (k0 + 8 * (g >> 1) + (m >> 2)) * stride + n0 + 16 * (g & 1) + 4 * (m & 3);
+  const uint2 lo = lds_tr16(p);
+  const uint2 hi = lds_tr16(p + 4 * stride);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
 template <int N>
@@ -132,11 +147,9 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   uint16_t* Xtm = sm;
   uint16_t* Cs = Xtm + L::kXtm;
   uint16_t* Bs = Cs + L::kCs;
-  uint16_t* XT = Bs + L::kBs;
-  uint16_t* XsH = XT + L::kXT;
-  uint16_t* XsL = XsH + L::kXT;
-  uint16_t* BT = XsL + L::kXT;
-  uint16_t* Ms = BT + L::kBT;
+  uint16_t* XsH = Bs + L::kBs;
+  uint16_t* XsL = XsH + L::kXs;
+  uint16_t* Ms = XsL + L::kXs;
   uint16_t* ST = Ms + L::kMs;
   float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
   float* cum = Yf + kQ * kYRow;                         // running sum of log a in the chunk
@@ -149,8 +162,12 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31, h32 = lane >> 5;
-  const int64_t bh = blockIdx.x;
   const int H = a.H;
+  // XCD-aware placement: workgroup ids are dealt round-robin over the 8 XCDs;
+  // give each XCD a contiguous range of (batch, head) items, so the heads of a
+  // batch row (which all read the same B and C) share an L2
+  const int64_t nwg = gridDim.x;
+  const int64_t bh = (nwg & 7) == 0 ? (int64_t)(blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : blockIdx.x;
   const int64_t b = bh / H;
   const int h = (int)(bh % H);
   const int64_t Lq = a.L;
@@ -182,22 +199,30 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   auto ld16 = [&](const uint16_t* p, bool ok) -> uint4 {
     return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
   };
+  // per-thread element offsets inside a chunk (chunk c adds c * kQ tokens)
+  const int64_t x_off = (int64_t)xj * xs_t + xp8;
+  int bc_off[kBCr], bc_j[kBCr];
+#pragma unroll
+  for (int r = 0; r < kBCr; ++r) {
+    const int e = tid + kNT * r;
+    bc_j[r] = e / (N / 8);
+    bc_off[r] = bc_j[r] * N + (e % (N / 8)) * 8;
+  }
   auto prefetch = [&](int64_t c, Pf& f) {
     const int64_t t0 = c * kQ;
+    const bool full = t0 + kQ <= Lq;   // uniform: only the last chunk is partial
     {
-      const int64_t t = t0 + xj;
-      const bool ok = t < Lq;
-      f.x = ld16(xb + t * xs_t + xp8, ok);
-      f.z = zb ? ld16(zb + t * xs_t + xp8, ok) : make_uint4(0, 0, 0, 0);
+      const bool ok = full || t0 + xj < Lq;
+      const int64_t o = t0 * xs_t + x_off;
+      f.x = ld16(xb + o, ok);
+      f.z = zb ? ld16(zb + o, ok) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int r = 0; r < kBCr; ++r) {
-      const int e = tid + kNT * r;
-      const int j = e / (N / 8), n8 = (e % (N / 8)) * 8;
-      const int64_t t = t0 + j;
-      const bool ok = t < Lq;
-      f.bq[r] = ld16(Bb + t * N + n8, ok);
-      f.cq[r] = ld16(Cb + t * N + n8, ok);
+      const bool ok = full || t0 + bc_j[r] < Lq;
+      const int64_t o = t0 * N + bc_off[r];
+      f.bq[r] = ld16(Bb + o, ok);
+      f.cq[r] = ld16(Cb + o, ok);
     }
     if (w == kDtWave) {
       const int64_t t = t0 + lane;
@@ -273,30 +298,19 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
     // ---- A2: next loads; transposes; G -> M (waves 0-2); C S_in (waves 4-7) ----
     if (c + 1 < nchunk) prefetch(c + 1, pf);
     {
-      // x^T and the scaled x: column p of tokens 8 w .. 8 w + 7
-      const int p = lane, j0 = 8 * w;
-      const uint4 col = col8(Xtm + j0 * kRowP + p, kRowP);
-      *reinterpret_cast<uint4*>(XT + p * kRowQ + j0) = col;
-      const uint32_t cw[4] = {col.x, col.y, col.z, col.w};
-      const float4 s0 = *reinterpret_cast<const float4*>(scl + j0);
-      const float4 s1 = *reinterpret_cast<const float4*>(scl + j0 + 4);
-      const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j,
+      // as a high bf16 part and the bf16 of the remainder
+      const float sc = scl[xj];
+      const uint32_t cw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const float e0 = bf(cw[k] & 0xffffu) * sc[2 * k], e1 = bf(cw[k] >> 16) * sc[2 * k + 1];
+        const float e0 = bf(cw[k] & 0xffffu) * sc, e1 = bf(cw[k] >> 16) * sc;
         hi[k] = pack_bf16x2(e0, e1);
         lo[k] = pack_bf16x2(e0 - bf(hi[k] & 0xffffu), e1 - bf(hi[k] >> 16));
       }
-      *reinterpret_cast<uint4*>(XsH + p * kRowQ + j0) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(XsL + p * kRowQ + j0) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-    }
-#pragma unroll
-    for (int r = 0; r < N / 64; ++r) {
-      // B^T: column n of tokens 8 j8 .. 8 j8 + 7
-      const int e = tid + kNT * r;
-      const int n = e % N, j0 = 8 * (e / N);
-      *reinterpret_cast<uint4*>(BT + n * kRowQ + j0) = col8(Bs + j0 * kRowN + n, kRowN);
+      *reinterpret_cast<uint4*>(XsH + xj * kRowP + xp8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(XsL + xj * kRowP + xp8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
     f32x16 yacc = {};
     if (w < 3) {
@@ -352,7 +366,7 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
       for (int s = 0; s < 4; ++s) {
         if (yi == 0 && s >= 2) break;                 // rows 0..31 see tokens 0..31 only
         yacc = mfma(lds_b8(Ms + (yi * 32 + l32) * kRowQ + 16 * s + 8 * h32),
-                    lds_b8(XT + (yp * 32 + l32) * kRowQ + 16 * s + 8 * h32), yacc);
+                    lds_opnd_tr(Xtm, kRowP, 16 * s, yp * 32, lane), yacc);
       }
       const int p = yp * 32 + l32;
 #pragma unroll
@@ -367,9 +381,9 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
       for (int r = 0; r < 16; ++r) S[r] *= at;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 av = lds_b8(BT + (s_nb * 32 + l32) * kRowQ + 16 * s + 8 * h32);
-        S = mfma(av, lds_b8(XsH + (s_pb * 32 + l32) * kRowQ + 16 * s + 8 * h32), S);
-        slo = mfma(av, lds_b8(XsL + (s_pb * 32 + l32) * kRowQ + 16 * s + 8 * h32), slo);
+        const bf16x8 av = lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane);
+        S = mfma(av, lds_opnd_tr(XsH, kRowP, 16 * s, s_pb * 32, lane), S);
+        slo = mfma(av, lds_opnd_tr(XsL, kRowP, 16 * s, s_pb * 32, lane), slo);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] += slo[r];
