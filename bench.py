@@ -44,6 +44,8 @@ PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traf
 KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
 PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
 KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h")]
+PROFILE_TRAFFIC_SSD = os.path.join(ROOT, "profiles", "ssd_fwd_layer_traffic.txt")
+KERNEL_SOURCES_SSD = [os.path.join(CSRC, f) for f in ("ssd_fwd.hip", "io.h")]
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -553,7 +555,8 @@ def bench_ssd(args) -> int:
                                "HIP graph", "batch": b, "seqlen": L, "nheads": H, "headdim": P, "d_state": N},
         "kernel_ms": round(launch_ms, 4),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": read_traffic(alg_bytes, PROFILE_TRAFFIC_SSD, KERNEL_SOURCES_SSD)},
         "mfma": {"achieved_tflops": round(tflops, 1), "peak_tflops": 2500.0, "frac": round(tflops / 2500.0, 4)},
         "cpu_baseline": cpu,
         "parity_sampled": parity,
