@@ -112,7 +112,10 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const int pc = tid / 8;                  // this thread's staging/epilogue piece: channel
   const int pg = tid % 8;                  //   and tokens 8 pg .. 8 pg + 7
 
-  int64_t wid = work_id(blockIdx.x, a.nwork);
+  // varlen: work items of unequal length are dealt round-robin over the XCDs as
+  // launched (a contiguous range per XCD would give one XCD all of a long
+  // sequence's channel groups)
+  int64_t wid = kVarlen ? (int64_t)blockIdx.x : work_id(blockIdx.x, a.nwork);
   int64_t kc, cg, b, t_begin, t_end, sidx;   // sidx: batch row or sequence of the state arrays
   if constexpr (kVarlen) {
     kc = 0;
