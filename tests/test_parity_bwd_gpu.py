@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import selective_state_space_55_amd as mscan
-from workloads import CONFIGS, backward_inputs, err_report, forward_inputs
+from workloads import backward_inputs, by_name, err_report, forward_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -108,10 +108,10 @@ def test_bwd_seqlen_zero():
 
 def test_bwd_config1_full():
     """The 130M-layer shape (b8 d1536 L2048, bf16, gated), every gradient in full."""
-    c = CONFIGS[1]
+    c = by_name("mamba-130m-layer")
     inp = forward_inputs(c)
     dy, _ = grad_inputs(inp, seed=11, with_dfs=False)
-    say("config 1 full backward")
+    say("mamba-130m-layer full backward")
     got = run(inp, dy, None)
     want = ref(inp, dy, None)
     check_all(got, want, c.tol)

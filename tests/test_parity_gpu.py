@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import selective_state_space_55_amd as mscan
-from workloads import CONFIGS, err_report, forward_inputs, max_rel_err, step_initial, step_inputs
+from workloads import by_name, err_report, forward_inputs, max_rel_err, step_initial, step_inputs
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
@@ -197,24 +197,24 @@ def test_chained_steps_match_scan():
 
 
 # ------------------------------------------------------- the five workloads
-def test_config0_tiny_fp32():
-    c = CONFIGS[0]
+def test_tiny_fp32():
+    c = by_name("tiny-fp32")
     inp = forward_inputs(c)
-    say("config 0")
+    say("tiny-fp32")
     y, fs = gpu_fwd(inp)
     yr, fsr = oracle_fwd(inp)
-    check("c0 y", y, yr, c.tol)
-    check("c0 final_state", fs, fsr, c.tol)
+    check("tiny y", y, yr, c.tol)
+    check("tiny final_state", fs, fsr, c.tol)
 
 
-def test_config1_full_compare():
-    c = CONFIGS[1]
+def test_mamba130m_layer_full_compare():
+    c = by_name("mamba-130m-layer")
     inp = forward_inputs(c)
-    say("config 1 (full compare)")
+    say("mamba-130m-layer (full compare)")
     y, fs = gpu_fwd(inp)
     yr, fsr = oracle_fwd(inp)
-    check("c1 y", y, yr, c.tol)
-    check("c1 final_state", fs, fsr, c.tol)
+    check("130m y", y, yr, c.tol)
+    check("130m final_state", fs, fsr, c.tol)
 
 
 def _sampled_rows(c, nrows, seed):
@@ -242,30 +242,30 @@ def _oracle_rows(inp, rows, dim):
     return np.stack(ys), np.stack(fss)
 
 
-@pytest.mark.parametrize("cfg", [2, 3])
+@pytest.mark.parametrize("cfg", ["mamba-1.4b-layer", "million-length"])
 def test_large_configs_sampled(cfg):
-    c = CONFIGS[cfg]
-    say(f"config {cfg}: generating inputs")
+    c = by_name(cfg)
+    say(f"{cfg}: generating inputs")
     inp = forward_inputs(c)
     a = {k: dev(v) for k, v in inp.items()}
-    say(f"config {cfg}: GPU run (default launch plan)")
+    say(f"{cfg}: GPU run (default launch plan)")
     y, fs = mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
                            delta_bias=a["delta_bias"], return_final_state=True)
     torch.cuda.synchronize()
-    rows = _sampled_rows(c, 24 if cfg == 2 else 6, seed=cfg)
+    rows = _sampled_rows(c, 24 if cfg == "mamba-1.4b-layer" else 6, seed=c.idx)
     yg = y.view(c.batch * c.dim, c.seqlen)[rows].cpu()
     fg = fs.view(c.batch * c.dim, c.dstate)[rows].cpu()
     del y, fs, a
-    say(f"config {cfg}: oracle on {len(rows)} rows")
+    say(f"{cfg}: oracle on {len(rows)} rows")
     yr, fsr = _oracle_rows(inp, rows, c.dim)
-    check(f"c{cfg} y (sampled rows)", yg, yr, c.tol)
-    check(f"c{cfg} final_state (sampled rows)", fg, fsr, c.tol)
+    check(f"{cfg} y (sampled rows)", yg, yr, c.tol)
+    check(f"{cfg} final_state (sampled rows)", fg, fsr, c.tol)
 
 
-def test_config4_decode_1024_steps_sampled():
+def test_decode_2_8b_1024_steps_sampled():
     """1024 chained steps at full size; the oracle follows a 16 x 16 grid of
     (batch row, channel) samples, i.e. one (16, 16) oracle step per token."""
-    c = CONFIGS[4]
+    c = by_name("decode-2.8b")
     init = step_initial(c)
     rng = np.random.default_rng(4)
     bs = torch.tensor(sorted(rng.choice(c.batch, 16, replace=False)))
@@ -276,7 +276,7 @@ def test_config4_decode_1024_steps_sampled():
     Ad, Dd, biasd = dev(A), dev(D), dev(bias)
     bsd, dsd = bs.to(DEV), ds.to(DEV)
     worst = 0.0
-    say("config 4: 1024 chained decode steps")
+    say("decode-2.8b: 1024 chained decode steps")
     for k in range(c.steps):
         s = step_inputs(c, k)
         y = mscan.scan_step(st, dev(s["x"]), dev(s["dt"]), Ad, dev(s["B"]), dev(s["C"]), D=Dd, z=dev(s["z"]),
@@ -288,7 +288,7 @@ def test_config4_decode_1024_steps_sampled():
         worst = max(worst, e)
         assert e <= c.tol, (k, e)
         if k % 256 == 0:
-            say(f"config 4: step {k} max_rel {e:.3e}")
+            say(f"decode-2.8b: step {k} max_rel {e:.3e}")
     fg = st[bsd][:, dsd].cpu()
     check("c4 final state (sampled)", fg, ref_state, c.tol)
-    say(f"config 4: worst per-step y error {worst:.3e}")
+    say(f"decode-2.8b: worst per-step y error {worst:.3e}")

@@ -83,3 +83,11 @@ CONFIGS: Dict[int, Config] = {
 
 def get_config(idx: int) -> Config:
     return CONFIGS[int(idx)]
+
+
+def by_name(name: str) -> Config:
+    """The workload called ``name`` (e.g. ``"mamba-1.4b-layer"``)."""
+    for c in CONFIGS.values():
+        if c.name == name:
+            return c
+    raise KeyError(name)
