@@ -211,7 +211,7 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *   ddelta_bias      (dim)                f32   NULL: not computed
  *   d_initial_state  (batch, dim, dstate) f32   NULL: not computed
  *   workspace        at least mamba_scan_bwd_workspace_size(...) bytes, 256-byte aligned:
- *                    the state entering every 32-token tile (batch x ceil(seqlen/32) x 16 x
+ *                    the state entering every 8-token sub-chunk (batch x ceil(seqlen/8) x 16 x
  *                    dim fp32) and per-channel-group / per-row partial sums
  *   flags            MAMBA_SCAN_FLAG_SOFTPLUS or 0; the backward pass is built for the
  *                    zero-order hold only (MAMBA_SCAN_FLAG_EULER returns MAMBA_SCAN_ERR_UNSUPPORTED)

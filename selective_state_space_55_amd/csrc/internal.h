@@ -75,8 +75,9 @@ hipError_t launch_step(const StepArgs& a, hipStream_t stream);
 // Backward pass: workspace layout (byte offsets, each part 256-byte aligned).
 struct BwdPlan {
   int64_t ntile;      // 32-token tiles
+  int64_t nsub;       // 8-token sub-chunks
   int64_t chgroups;   // 64-channel groups
-  size_t off_ckpt;    // (batch, ntile, 16, dim) fp32: state before each tile
+  size_t off_ckpt;    // (batch, nsub, 16, dim) fp32: state before each sub-chunk
   size_t off_dB;      // (batch, chgroups, 16, seqlen) fp32: per-group partial dB
   size_t off_dC;      // same for dC
   size_t off_dA;      // (batch, dim, 16) fp32: per-row partial dA_log

@@ -15,18 +15,18 @@
 //
 // Three launches:
 //   1. checkpoint pass: the forward recurrence (no readout) writes the state
-//      entering every 32-token tile to the workspace;
-//   2. gradient pass, tiles in reverse order.  A workgroup owns 64 channels of
-//      one batch row (one per lane) and 4 waves; wave w holds states 4w..4w+3.
-//      Per tile: stage Delta, u, B, C in LDS; rerun the forward from the tile's
-//      checkpoint for the readout (four partial sums per token-channel, summed
-//      with D u into the pre-gate output, giving dz and dytil) and the states
-//      at four 8-token boundaries; then per 8-token sub-chunk in reverse,
-//      rerun those 8 tokens keeping every state and decay in registers and
-//      sweep them backwards carrying Abar lam.  dDelta and du are partial over
-//      a wave's states and summed across waves through LDS; dB and dC are
-//      summed over the 64 lanes (channels) by a reduce-scatter in registers
-//      and written per channel group to the workspace;
+//      entering every 8-token sub-chunk to the workspace;
+//   2. gradient pass, 32-token tiles in reverse order.  A workgroup owns 64
+//      channels of one batch row (one per lane) and 4 waves; wave w holds
+//      states 4w..4w+3.  Per tile: stage Delta, u, dytil, B, C in LDS; then per
+//      8-token sub-chunk in reverse, rerun those 8 tokens from the sub-chunk's
+//      checkpoint keeping every state and decay in registers (and the readout
+//      partial sums), and sweep them backwards carrying Abar lam.  The
+//      readout, dDelta and du are partial over a wave's states and summed
+//      across waves through LDS at the end of the tile, where the pre-gate
+//      output gives dz; dB and dC are summed over the 64 lanes (channels) by a
+//      reduce-scatter in registers and written per channel group to the
+//      workspace;
 //   3. reductions of the per-group and per-row partials in a fixed order
 //      (deterministic results).
 #include <algorithm>
@@ -70,7 +70,7 @@ struct BArgs {
   float* wsA;
   float* wsD;
   float* wsBias;
-  int64_t dim, seqlen, chgroups, ntile, nwork;
+  int64_t dim, seqlen, chgroups, ntile, nsub, nwork;
   int dstate, softplus;
 };
 
@@ -202,6 +202,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const int pc = tid / 4, pg = tid % 4;            // piece: channel, tokens 8 pg .. 8 pg + 7
   const int bn = tid % NP, bg = (tid / NP) % kG;   // B piece (threads 0..127): state, 4-token group
   const int sel = lane & 15;
+  float* ck = a.ckpt + (b * a.nsub * NP + w * NPW) * a.dim + d;   // + (s8 * NP + j) * dim
   __syncthreads();
 
   // tile k's loads are issued while tile k-1 is scanned
@@ -213,15 +214,11 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   };
   V8 rd = IO::zero(), ru = IO::zero();
   V4 rb{};
-  if (a.ntile > 1) load_tile(0, rd, ru, rb);
+  load_tile(0, rd, ru, rb);
   for (int64_t k = 0; k < a.ntile; ++k) {
     const int64_t tile = k * kT;
-    if (ch_ok) {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) a.ckpt[((b * a.ntile + k) * NP + w * NPW + j) * a.dim + d] = h[j];
-    }
-    if (k + 1 == a.ntile) break;   // the last tile's entering state is all the gradient pass needs
-    // every tile but the last is full
+    const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
+    const int nv = max(0, min(8, nv_tile - pg * 8));   // valid tokens of this thread's piece
     float fd[8], fu[8];
     IO::to_f32(rd, fd);
     IO::to_f32(ru, fu);
@@ -229,7 +226,9 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float x = fd[j] + bi;
-      fd[j] = kSp ? softplus_log2e(x) : x * kLog2e;
+      const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
+      fd[j] = j < nv ? dl : 0.0f;   // tokens past the end: Delta = 0, u = 0 leave the state unchanged
+      fu[j] = j < nv ? fu[j] : 0.0f;
     }
     float* dp = dbuf + pc * kRow + pg * 8;
     float* up = ubuf + pc * kRow + pg * 8;
@@ -238,15 +237,23 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
     reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
     reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
     if (w < 2) {
+      const int nvb = max(0, min(4, nv_tile - bg * 4));
       float f[4];
       IO::to_f32(rb, f);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bbuf[(bg * 4 + kk) * NP + bn] = f[kk];
+      for (int kk = 0; kk < 4; ++kk) bbuf[(bg * 4 + kk) * NP + bn] = kk < nvb ? f[kk] : 0.0f;
     }
-    if (k + 2 < a.ntile) load_tile(tile + kT, rd, ru, rb);
+    if (k + 1 < a.ntile) load_tile(tile + kT, rd, ru, rb);
     lds_barrier();
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
+      if (g % 2 == 0) {   // the state entering each 8-token sub-chunk that starts before the end
+        const int64_t s8 = k * (kT / kSub) + g / 2;
+        if (ch_ok && s8 < a.nsub) {
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) ck[(s8 * NP + j) * a.dim] = h[j];
+        }
+      }
       const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * g);
       const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * g);
       const float bq = bbuf[(g * 4 + (sel & 3)) * NP + w * NPW + (sel >> 2)];   // lane 4j+kk: state j, token kk
@@ -270,10 +277,11 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
 struct LdsB {
   static constexpr int kDU = kCh * kRow;            // Delta*log2e, u, dytil: one tile each
   static constexpr int kBC = kG * 4 * NP * 2;       // (B, C) pairs
-  static constexpr int kPart = 4 * kCh * kRow;      // per-wave partials (readout, then dDelta), and du
+  static constexpr int kPart = 4 * kCh * kRow;      // per-wave partials over one tile: readout, dDelta, du
   static constexpr int kHB = 4 * 4 * kCh * NPW;     // state entering each 8-token sub-chunk, per wave and lane
-  static constexpr int kFloats = 3 * kDU + kBC + 2 * kPart + kHB + 2 * kCh;
+  static constexpr int kFloats = 3 * kDU + kBC + 3 * kPart + kHB + 2 * kCh;
 };
+static_assert(sizeof(float) * LdsB::kFloats <= 160 * 1024, "LDS of the gradient kernel");
 
 template <typename IoT, bool kVec, bool kSp, bool kGate>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
@@ -286,7 +294,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float* ubuf = dbuf + LdsB::kDU;         // [64][kRow] u
   float* ybuf = ubuf + LdsB::kDU;         // [64][kRow] dytil
   float* bcs = ybuf + LdsB::kDU;          // [kG][4 tokens][NP][B, C]
-  float* part1 = bcs + LdsB::kBC;         // [4][64][kRow] readout partials, then dDelta partials
+  float* party = bcs + LdsB::kBC;         // [4][64][kRow] readout partials
+  float* part1 = party + LdsB::kPart;     // [4][64][kRow] dDelta partials
   float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
   float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][4 waves][64 lanes][4 states]
   float* par = hbuf + LdsB::kHB;          // [2][64] bias, D
@@ -307,6 +316,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     par[kCh + tid] = (ok && a.D) ? a.D[d0 + tid] : 0.0f;
   }
 
+  // X, Y: running sums of Delta g q and l e B u per state (dA_log = X - Y, derived below)
   float A[NPW], iA[NPW], g[NPW], X[NPW], Y[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -347,11 +357,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   const bool isB = w < 2;                            // waves 0-1 stage B, 2-3 stage C
   const int sel = lane & 15;
   const float* bcl = bcs + ((sel & 3) * NP + w * NPW + (sel >> 2)) * 2;   // lane 4j+kk: state j, token kk
+  const float* ck = a.ckpt + (b * a.nsub * NP + w * NPW) * a.dim + d;    // + (s8 * NP + j) * dim
   float dD_acc = 0.0f, db_acc = 0.0f;
   __syncthreads();
 
-  // (issuing the next tile's loads a tile ahead was measured: no gain, the
-  // kernel is issue-bound, and it raises register pressure)
   for (int64_t k = a.ntile - 1; k >= 0; --k) {
     const int64_t tile = k * kT;
     const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
@@ -366,114 +375,67 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     V8 rz = IO::zero();
     if constexpr (kGate) rz = IO::buf_load8(rs_z, off, kVec);
     const V4 rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
-    float h0t[NPW];   // state entering the tile
+    float hq[4][NPW];   // states entering the tile's sub-chunks (0 for sub-chunks past the end)
 #pragma unroll
-    for (int j = 0; j < NPW; ++j) h0t[j] = ch_ok ? a.ckpt[((b * a.ntile + k) * NP + w * NPW + j) * a.dim + d] : 0.0f;
+    for (int s = 0; s < 4; ++s) {
+      const int64_t s8 = k * (kT / kSub) + s;
+      const bool ok = ch_ok && s8 < a.nsub;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) hq[s][j] = ok ? ck[(s8 * NP + j) * a.dim] : 0.0f;
+    }
 
-    float fd[8], fu[8], fdy[8], fz[8], xs[8];
-    IO::to_f32(rd, fd);
-    IO::to_f32(ru, fu);
-    IO::to_f32(rdy, fdy);
-    IO::to_f32(rz, fz);
+    // piece owners keep, for the end of the tile: u, dytil, dz / ytil and dDelta / d(pre-softplus)
+    float fu[8], dyt[8], gzf[8], sgx[8];
     {
+      float fd[8], fdy[8], fz[8];
+      IO::to_f32(rd, fd);
+      IO::to_f32(ru, fu);
+      IO::to_f32(rdy, fdy);
+      IO::to_f32(rz, fz);
       const float bi = par[pc];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const bool ok = j < nv;   // tokens past the end: Delta = 0, u = 0, dy = 0 change nothing
-        xs[j] = fd[j] + bi;
-        const float dl = kSp ? softplus_log2e(xs[j]) : xs[j] * kLog2e;
+        const float xs = fd[j] + bi;
+        const float dl = kSp ? softplus_log2e(xs) : xs * kLog2e;
+        sgx[j] = kSp ? sigmoidf_fast(xs) : 1.0f;
         fd[j] = ok ? dl : 0.0f;
         fu[j] = ok ? fu[j] : 0.0f;
-        fdy[j] = ok ? fdy[j] : 0.0f;
+        const float dyv = ok ? fdy[j] : 0.0f;
+        if constexpr (kGate) {
+          const float sg = sigmoidf_fast(fz[j]);
+          dyt[j] = dyv * fz[j] * sg;                              // dy SiLU(z)
+          gzf[j] = dyv * sg * fmaf(fz[j], 1.0f - sg, 1.0f);      // dz = gzf * ytil
+        } else {
+          dyt[j] = dyv;
+          gzf[j] = 0.0f;
+        }
+        dD_acc = fmaf(dyt[j], fu[j], dD_acc);
       }
       float* dp = dbuf + pc * kRow + pg * 8;
       float* up = ubuf + pc * kRow + pg * 8;
+      float* yp = ybuf + pc * kRow + pg * 8;
       reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
       reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
       reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
       reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+      reinterpret_cast<float4*>(yp)[0] = make_float4(dyt[0], dyt[1], dyt[2], dyt[3]);
+      reinterpret_cast<float4*>(yp)[1] = make_float4(dyt[4], dyt[5], dyt[6], dyt[7]);
       const int nvb = max(0, min(4, nv_tile - bg * 4));
       float f[4];
       IO::to_f32(rbc, f);
       float* q = bcs + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        *reinterpret_cast<float4*>(hbuf + ((s * 4 + w) * kCh + lane) * NPW) = make_float4(hq[s][0], hq[s][1], hq[s][2], hq[s][3]);
     }
     lds_barrier();
 
-    // ---- forward over the tile: readout partials and sub-chunk boundary states ----
-    {
-      float h[NPW];
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) h[j] = h0t[j];
-#pragma unroll
-      for (int gq = 0; gq < kG; ++gq) {
-        if (gq % 2 == 0)   // state entering sub-chunk gq / 2
-          *reinterpret_cast<float4*>(hbuf + (((gq / 2) * 4 + w) * kCh + lane) * NPW) = make_float4(h[0], h[1], h[2], h[3]);
-        const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * gq);
-        const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * gq);
-        const float2 bq = *reinterpret_cast<const float2*>(bcl + gq * NP * 8);
-        const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
-        const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
-        float ys[4];
-        static_for<4>([&](auto kk_c) {
-          constexpr int kk = decltype(kk_c)::value;
-          float acc = 0.0f;
-          static_for<NPW>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
-            const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
-            const float sv = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk] * iA[j]);
-            h[j] = fmaf(av, h[j] + sv, -sv);
-            acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
-          });
-          ys[kk] = acc;
-        });
-        *reinterpret_cast<float4*>(part1 + (w * kCh + lane) * kRow + 4 * gq) = make_float4(ys[0], ys[1], ys[2], ys[3]);
-      }
-    }
-    lds_barrier();
-
-    // ---- piece owners: pre-gate output, dz, dytil ----
-    {
-      float dyt[8];
-      const float Dd = par[kCh + pc];
-      float ysum[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ysum[j] = 0.0f;
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        const float4* q = reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * 8);
-        const float4 q0 = q[0], q1 = q[1];
-        ysum[0] += q0.x; ysum[1] += q0.y; ysum[2] += q0.z; ysum[3] += q0.w;
-        ysum[4] += q1.x; ysum[5] += q1.y; ysum[6] += q1.z; ysum[7] += q1.w;
-      }
-      float dzv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float ytil = fmaf(Dd, fu[j], ysum[j]);
-        if constexpr (kGate) {
-          const float sg = sigmoidf_fast(fz[j]);
-          dzv[j] = fdy[j] * ytil * sg * fmaf(fz[j], 1.0f - sg, 1.0f);
-          dyt[j] = fdy[j] * fz[j] * sg;
-        } else {
-          dzv[j] = 0.0f;
-          dyt[j] = fdy[j];
-        }
-        dD_acc = fmaf(dyt[j], fu[j], dD_acc);
-      }
-      if constexpr (kGate) {
-        if (full)
-          IO::buf_store8(rs_dz, off, IO::from_f32(dzv), kVec);
-        else if (d0 + pc < a.dim)
-          IO::store_n(gdz + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(dzv), nv);
-      }
-      float* yp = ybuf + pc * kRow + pg * 8;
-      reinterpret_cast<float4*>(yp)[0] = make_float4(dyt[0], dyt[1], dyt[2], dyt[3]);
-      reinterpret_cast<float4*>(yp)[1] = make_float4(dyt[4], dyt[5], dyt[6], dyt[7]);
-    }
-    lds_barrier();
-
-    // ---- reverse sweep, one 8-token sub-chunk at a time ----
+    // ---- one 8-token sub-chunk at a time, latest first: rerun its forward from the
+    //      checkpoint (readout partials, every state and decay kept in registers),
+    //      then sweep it backwards ----
 #pragma unroll 1
     for (int s = 3; s >= 0; --s) {
       float hb[NPW], hh[kSub][NPW], ha[kSub][NPW];
@@ -489,8 +451,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
           const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
           const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
           const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+          float ys[4];
           static_for<4>([&](auto kk_c) {
             constexpr int kk = decltype(kk_c)::value;
+            float acc = 0.0f;
             static_for<NPW>([&](auto j_c) {
               constexpr int j = decltype(j_c)::value;
               const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
@@ -498,10 +462,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
               h[j] = fmaf(av, h[j] + sv, -sv);
               hh[4 * gq + kk][j] = h[j];
               ha[4 * gq + kk][j] = av;
+              acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
             });
+            ys[kk] = acc;
           });
+          *reinterpret_cast<float4*>(party + (w * kCh + lane) * kRow + 4 * tg) = make_float4(ys[0], ys[1], ys[2], ys[3]);
         });
       }
+      // Per (token, state), with l = lam_t, e = (Abar - 1) / A (so Bbar = e B) and
+      // q = A h_{t-1} + B u (so dh_t/dDelta = Abar q):
+      //   dDelta += Abar l q,  du += l e B,  dB += l e u,  dC += dytil h_t, and
+      //   dh_t/dA = Delta Abar h_{t-1} + (Delta Abar - e) B u / A, so
+      //   dA = (sum Delta (Abar l) q - sum l e B u) / A, and dA_log = A dA = X - Y.
       static_for<2>([&](auto gr_c) {
         constexpr int gq = 1 - decltype(gr_c)::value;   // the sub-chunk's two 4-token groups, later first
         const int tg = 2 * s + gq;
@@ -525,17 +497,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             const float av = ha[t][j];
             const float l = dpp_bcast_fmac<src>(g[j], bq.y, dys[kk]);   // lam_t = dytil C + Abar lam_{t+1}
             g[j] = av * l;                                              // Abar_t lam_t, for token t-1
-            const float v = uus[kk] * iA[j];
-            const float sv = dpp_bcast_mul<src>(bq.x, v);               // s = B u / A
-            const float t1 = hp + sv;
-            dD_p = fmaf(g[j] * A[j], t1, dD_p);                         // lam Abar (A h_{t-1} + B u)
-            const float am1 = av - 1.0f;
-            const float la = l * am1;
-            dBv[j * 4 + kk] = la * v;                                   // lam u (Abar - 1) / A
-            du_p = fmaf(la, dpp_bcast_mul<src>(bq.x, iA[j]), du_p);     // lam Bbar / u
-            X[j] = fmaf(l * (Delta * av), t1, X[j]);
-            Y[j] = fmaf(l * sv, am1, Y[j]);
-            dCv[j * 4 + kk] = dys[kk] * hh[t][j];                       // dytil h_t
+            const float bu = dpp_bcast_mul<src>(bq.x, uus[kk]);         // B u
+            const float q = fmaf(A[j], hp, bu);
+            dD_p = fmaf(g[j], q, dD_p);
+            X[j] = fmaf(Delta * g[j], q, X[j]);
+            const float le = l * fmaf(av, iA[j], -iA[j]);               // l e
+            Y[j] = fmaf(le, bu, Y[j]);
+            du_p = dpp_bcast_fmac<src>(du_p, bq.x, le);
+            dBv[j * 4 + kk] = le * uus[kk];
+            dCv[j * 4 + kk] = dys[kk] * hh[t][j];
           });
           dDp[kk] = dD_p;
           dup[kk] = du_p;
@@ -556,48 +526,51 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     }
     lds_barrier();
 
-    // ---- piece owners: ddelta, du ----
+    // ---- piece owners: pre-gate output, dz, ddelta, du ----
+    // (no barrier after this step: the next tile's staging writes only buffers
+    // last read before the barrier above, and the partials are rewritten only
+    // after the next tile's first barrier)
     {
       const float Dd = par[kCh + pc];
-      float dyt[8];
-      {
-        const float4* q = reinterpret_cast<const float4*>(ybuf + pc * kRow + pg * 8);
-        const float4 q0 = q[0], q1 = q[1];
-        dyt[0] = q0.x; dyt[1] = q0.y; dyt[2] = q0.z; dyt[3] = q0.w;
-        dyt[4] = q1.x; dyt[5] = q1.y; dyt[6] = q1.z; dyt[7] = q1.w;
-      }
-      float sd[8], su[8];
+      float sy[8], sd[8], su[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        sy[j] = 0.0f;
         sd[j] = 0.0f;
         su[j] = 0.0f;
       }
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
+        const float4* q0 = reinterpret_cast<const float4*>(party + (s2 * kCh + pc) * kRow + pg * 8);
         const float4* q1 = reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * 8);
         const float4* q2 = reinterpret_cast<const float4*>(part2 + (s2 * kCh + pc) * kRow + pg * 8);
-        const float4 a0 = q1[0], a1 = q1[1], c0 = q2[0], c1 = q2[1];
+        const float4 y0 = q0[0], y1 = q0[1], a0 = q1[0], a1 = q1[1], c0 = q2[0], c1 = q2[1];
+        sy[0] += y0.x; sy[1] += y0.y; sy[2] += y0.z; sy[3] += y0.w;
+        sy[4] += y1.x; sy[5] += y1.y; sy[6] += y1.z; sy[7] += y1.w;
         sd[0] += a0.x; sd[1] += a0.y; sd[2] += a0.z; sd[3] += a0.w;
         sd[4] += a1.x; sd[5] += a1.y; sd[6] += a1.z; sd[7] += a1.w;
         su[0] += c0.x; su[1] += c0.y; su[2] += c0.z; su[3] += c0.w;
         su[4] += c1.x; su[5] += c1.y; su[6] += c1.z; su[7] += c1.w;
       }
-      float ddv[8], duv[8];
+      float dzv[8], ddv[8], duv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        ddv[j] = kSp ? sd[j] * sigmoidf_fast(xs[j]) : sd[j];
+        dzv[j] = gzf[j] * fmaf(Dd, fu[j], sy[j]);   // ytil = C h + D u
+        ddv[j] = sd[j] * sgx[j];
         duv[j] = fmaf(dyt[j], Dd, su[j]);
         db_acc += (j < nv) ? ddv[j] : 0.0f;
       }
       if (full) {
+        if constexpr (kGate) IO::buf_store8(rs_dz, off, IO::from_f32(dzv), kVec);
         IO::buf_store8(rs_dd, off, IO::from_f32(ddv), kVec);
         IO::buf_store8(rs_du, off, IO::from_f32(duv), kVec);
       } else if (d0 + pc < a.dim) {
-        IO::store_n(gdd + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(ddv), nv);
-        IO::store_n(gdu + row0 + (int64_t)pc * a.seqlen + tile + pg * 8, IO::from_f32(duv), nv);
+        const int64_t o = row0 + (int64_t)pc * a.seqlen + tile + pg * 8;
+        if constexpr (kGate) IO::store_n(gdz + o, IO::from_f32(dzv), nv);
+        IO::store_n(gdd + o, IO::from_f32(ddv), nv);
+        IO::store_n(gdu + o, IO::from_f32(duv), nv);
       }
     }
-    lds_barrier();
   }
 
   // ---- per-row partials of the parameter gradients, gradient of the initial state ----
@@ -605,7 +578,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
       const int n = w * NPW + j;
-      a.wsA[bd * NP + n] = (X[j] - iA[j] * Y[j]) * A[j];   // dA * dA/dA_log
+      a.wsA[bd * NP + n] = X[j] - Y[j];   // dA * dA/dA_log
       if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
     }
   }
@@ -694,7 +667,7 @@ hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   k.wsA = reinterpret_cast<float*>(ws + p.off_dA);
   k.wsD = reinterpret_cast<float*>(ws + p.off_dD);
   k.wsBias = reinterpret_cast<float*>(ws + p.off_dbias);
-  k.dim = a.dim; k.seqlen = a.seqlen; k.chgroups = p.chgroups; k.ntile = p.ntile;
+  k.dim = a.dim; k.seqlen = a.seqlen; k.chgroups = p.chgroups; k.ntile = p.ntile; k.nsub = p.nsub;
   k.nwork = a.batch * p.chgroups;
   k.dstate = (int)a.dstate; k.softplus = a.softplus;
   const size_t esz = sizeof(IoT);
@@ -739,10 +712,11 @@ hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
 
 void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* p) {
   p->ntile = (seqlen + kT - 1) / kT;
+  p->nsub = (seqlen + kSub - 1) / kSub;
   p->chgroups = (dim + kCh - 1) / kCh;
   size_t off = 0;
   p->off_ckpt = off;
-  off += align256(sizeof(float) * (size_t)(batch * p->ntile * NP * dim));
+  off += align256(sizeof(float) * (size_t)(batch * p->nsub * NP * dim));
   p->off_dB = off;
   off += align256(sizeof(float) * (size_t)(batch * p->chgroups * NP * seqlen));
   p->off_dC = off;

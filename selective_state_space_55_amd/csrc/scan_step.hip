@@ -12,7 +12,8 @@
 // channel, so A = -exp(A_log) and 1/A are formed once per channel and reused,
 // and all rows' loads are issued before the arithmetic.  The readout sum over
 // a channel's lanes uses cross-lane adds in a fixed order, so results are
-// deterministic.
+// deterministic.  For d_state 16 (the common case) a variant lets lane q of
+// a channel's quad do the per-(batch, channel) scalar work of row q once.
 #include "internal.h"
 #include "io.h"
 
@@ -151,6 +152,110 @@ __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
   }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// value of lane R of the lane's quad (DPP quad_perm [R, R, R, R])
+template <int R>
+__device__ __forceinline__ float quad_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), R * 0x55, 0xf, 0xf, false));
+}
+// value of lane l ^ 1 (CTRL 0xB1) or l ^ 2 (CTRL 0x4E) of the quad
+template <int CTRL>
+__device__ __forceinline__ float quad_swap(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// d_state 16 with vector-aligned rows: the quad of lanes of a channel walks
+// four batch rows, and lane q does the per-(batch, channel) work of row q --
+// loads of x, dt, z, softplus, the gate and the output -- once for the quad
+// (the general kernel repeats it on every lane); Delta and x of row r reach
+// the other lanes by a DPP broadcast.  Same arithmetic in the same order as
+// the general kernel, so the results are identical.  Offsets are 32-bit from
+// per-workgroup base addresses (4 rows x dim x 64 bytes < 4 GiB, checked on
+// the host).  kFull: batch % 4 == 0 and 4 dim % 256 == 0, so no lane is idle.
+template <typename IoT, bool kFull, bool kEuler>
+__global__ __launch_bounds__(256) void scan_step_quad_kernel(SArgs a) {
+  using IO = Io<IoT>;
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t dq = gid >> 2;
+  const int q = (int)(gid & 3);
+  const uint32_t dim = (uint32_t)a.dim;
+  const bool live_d = kFull || dq < dim;
+  const uint32_t d = live_d ? dq : 0u;
+  const int64_t b0 = (int64_t)blockIdx.y * 4;
+
+  const IoT* gx = static_cast<const IoT*>(a.x) + b0 * a.dim;
+  const IoT* gdt = static_cast<const IoT*>(a.dt) + b0 * a.dim;
+  const IoT* gz = a.z ? static_cast<const IoT*>(a.z) + b0 * a.dim : nullptr;
+  const IoT* gB = static_cast<const IoT*>(a.B) + b0 * 16;
+  const IoT* gC = static_cast<const IoT*>(a.C) + b0 * 16;
+  float* gst = a.state + b0 * a.dim * 16;
+  IoT* gy = static_cast<IoT*>(a.y) + b0 * a.dim;
+
+  // row q's scalars
+  const bool live_q = kFull || (live_d && b0 + q < a.batch);
+  const uint32_t oq = live_q ? (uint32_t)q * dim + d : 0u;
+  const float xq = live_q ? IO::load1(gx + oq) : 0.0f;
+  const float rq = live_q ? IO::load1(gdt + oq) : 0.0f;
+  const float zq = (live_q && gz) ? IO::load1(gz + oq) : 0.0f;
+
+  // every row's B, C and states 4q .. 4q+3
+  float Bv[4][4], Cv[4][4], hs[4][4];
+  bool live[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    live[r] = kFull || (live_d && b0 + r < a.batch);
+    const uint32_t rr = live[r] ? (uint32_t)r : 0u;
+    load_bc4<IoT, true>(gB, rr, q, 16, Bv[r]);
+    load_bc4<IoT, true>(gC, rr, q, 16, Cv[r]);
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live[r]) v = *reinterpret_cast<const f32x4*>(gst + (rr * dim + d) * 16u + 4u * q);
+    hs[r][0] = v.x; hs[r][1] = v.y; hs[r][2] = v.z; hs[r][3] = v.w;
+  }
+  float An[4], iA[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    An[j] = -expf(a.A_log[d * 16u + 4u * q + j]);
+    iA[j] = 1.0f / An[j];
+  }
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float Dd = a.D ? a.D[d] : 0.0f;
+  const float xb = rq + bias;
+  const float dlq = a.softplus ? softplus_log2e(xb) : xb * 1.4426950408889634f;   // Delta * log2e of row q
+  const float gq = gz ? silu(zq) : 1.0f;
+
+  static_for<4>([&](auto r_c) {
+    constexpr int r = decltype(r_c)::value;
+    const float dl = quad_bcast<r>(dlq);
+    const float xv = quad_bcast<r>(xq);
+    float acc = 0.0f;
+    if constexpr (kEuler) {
+      const float du = (dl * 0.6931471805599453f) * xv;   // Delta u
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float s = Bv[r][j] * (xv * iA[j]);   // B u / A
+        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
+    }
+    acc += quad_swap<0xB1>(acc);   // pairs, then pairs of pairs, as the general kernel
+    acc += quad_swap<0x4E>(acc);
+    if (live[r]) {
+      const f32x4 v = {hs[r][0], hs[r][1], hs[r][2], hs[r][3]};
+      *reinterpret_cast<f32x4*>(gst + ((uint32_t)r * dim + d) * 16u + 4u * q) = v;
+      if (q == r) IO::store1(gy + oq, fmaf(Dd, xq, acc) * gq);
+    }
+  });
+}
+
 template <typename IoT>
 hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   SArgs a{};
@@ -163,6 +268,14 @@ hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   const bool vec = (s.dstate == 4 * lpc) && ((reinterpret_cast<uintptr_t>(s.state) & 15) == 0) &&
                    ((bc_mis & (4 * sizeof(IoT) - 1)) == 0);
   const int64_t threads = s.dim * lpc;
+  if (vec && lpc == 4 && s.dim < (int64_t(1) << 26)) {
+    const dim3 g4((unsigned)((threads + 255) / 256), (unsigned)((s.batch + 3) / 4));
+    const bool full = (s.batch % 4 == 0) && (threads % 256 == 0);
+    auto k = full ? (s.euler ? scan_step_quad_kernel<IoT, true, true> : scan_step_quad_kernel<IoT, true, false>)
+                  : (s.euler ? scan_step_quad_kernel<IoT, false, true> : scan_step_quad_kernel<IoT, false, false>);
+    hipLaunchKernelGGL(k, g4, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((s.batch + kRows - 1) / kRows));
   switch (lpc * 2 + (vec ? 1 : 0)) {
     case 9: hipLaunchKernelGGL((scan_step_kernel<IoT, true, 4>), grid, dim3(256), 0, stream, a); break;
