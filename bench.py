@@ -45,6 +45,7 @@ KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
 PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
 KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h")]
 PROFILE_TRAFFIC_SSD = os.path.join(ROOT, "profiles", "ssd_fwd_layer_traffic.txt")
+PROFILE_TRAFFIC_CONV_FUSED = os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba1.4b_kernel_trace.txt")
 KERNEL_SOURCES_SSD = [os.path.join(CSRC, f) for f in ("ssd_fwd.hip", "io.h")]
 
 
@@ -390,6 +391,138 @@ def bench_conv(args, c) -> int:
     return 0
 
 
+# causal conv1d (K = 4) + SiLU per (token, channel): 4 FMAs, exp (2 slots), add, rcp (2 slots), multiply
+SLOTS_PER_TC_CONV = 10.0
+
+
+def bench_conv_fused(args, c) -> int:
+    """The causal conv1d (K = 4) + SiLU fused into the forward scan's load stage, over the forward
+    config (the scan input u never goes through HBM); the same work as two separate launches
+    (conv1d, then the scan) is timed alongside for comparison."""
+    import numpy as np
+    import torch
+
+    import selective_state_space_55_amd as mscan
+    from workloads import conv_inputs, forward_inputs, max_rel_err
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = forward_inputs(c)
+    _, w, cbias, _ = conv_inputs(c.batch, c.dim, c.seqlen, 4, c.io, seed=0)
+    a = {k: (None if v is None else v.to(dev)) for k, v in inp.items()}
+    wd, cbd = w.to(dev), cbias.to(dev)
+    b, d, n, L = c.batch, c.dim, c.dstate, c.seqlen
+    io = mscan.BF16 if c.io == "bf16" else mscan.F32
+    ws_bytes = mscan.fwd_workspace_size(b, d, n, L, io)
+    ws = torch.empty(max(ws_bytes, 1) + 256, dtype=torch.uint8, device=dev)
+    y = torch.empty((b, d, L), dtype=a["u"].dtype, device=dev)
+    fs = torch.empty((b, d, n), dtype=torch.float32, device=dev)
+    u = torch.empty_like(a["u"])
+    stream = torch.cuda.current_stream(dev)
+
+    def fused():
+        mscan.scan_fwd_conv(a["u"], wd, a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                            delta_bias=a["delta_bias"], conv_bias=cbd, out=y, final_state=fs,
+                            return_final_state=True, workspace=ws, stream=stream,
+                            discretization=args.discretization)
+
+    def separate():
+        mscan.conv1d_fwd(a["u"], wd, cbd, out=u, stream=stream)
+        mscan.scan_fwd(u, a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"], delta_bias=a["delta_bias"],
+                       out=y, final_state=fs, return_final_state=True, workspace=ws, stream=stream,
+                       discretization=args.discretization)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps, wall * 1e3 / args.steps
+
+    sep_ms, _ = timed(separate)
+    y_sep = y.clone()
+    fs_sep = fs.clone()
+    launch_ms, ms_per_step = timed(fused)
+    identical = bool(torch.equal(y.view(torch.int16) if y.dtype == torch.bfloat16 else y,
+                                 y_sep.view(torch.int16) if y.dtype == torch.bfloat16 else y_sep)
+                     and torch.equal(fs, fs_sep))
+
+    tc = b * d * L
+    per_tcn = SLOTS_PER_TCN if args.discretization == "zoh" else SLOTS_PER_TCN_EULER
+    slots = tc * n * per_tcn + tc * ((SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED) + SLOTS_PER_TC_CONV)
+    achieved = slots / (launch_ms * 1e-3) / 1e12
+    peak = VALU_SLOTS_PEAK / 1e12
+    alg_bytes = c.algorithmic_bytes() + d * 5 * 4   # x in place of u, plus taps and conv bias
+
+    def oracle_rows(rows):
+        import oracle
+
+        ys, fss = [], []
+        for r in rows:
+            bb, dd = divmod(r, d)
+            u64 = oracle.conv1d_fwd(inp["u"][bb:bb + 1, dd:dd + 1], w[dd:dd + 1], cbias[dd:dd + 1])
+            u_io = torch.from_numpy(np.asarray(u64, dtype=np.float32)).to(inp["u"].dtype)
+            yr, fr = oracle.scan_fwd(u_io, inp["delta"][bb:bb + 1, dd:dd + 1], inp["A_log"][dd:dd + 1],
+                                     inp["B"][bb:bb + 1], inp["C"][bb:bb + 1],
+                                     D=None if inp["D"] is None else inp["D"][dd:dd + 1],
+                                     z=None if inp["z"] is None else inp["z"][bb:bb + 1, dd:dd + 1],
+                                     delta_bias=None if inp["delta_bias"] is None else inp["delta_bias"][dd:dd + 1],
+                                     discretization=args.discretization)
+            ys.append(yr[0, 0])
+            fss.append(fr[0, 0])
+        return np.stack(ys), np.stack(fss)
+
+    parity = None
+    if not args.no_parity:
+        rows = [0, d // 2 + 7, (b - 1) * d + d - 1]
+        yr, fr = oracle_rows(rows)
+        parity = {"rows": rows, "y_max_rel": max_rel_err(y.view(b * d, L)[rows].cpu(), yr),
+                  "final_state_max_rel": max_rel_err(fs.view(b * d, n)[rows].cpu(), fr), "tol": c.tol}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        nrow = 512
+        c0 = time.perf_counter()
+        oracle_rows(list(range(nrow)))
+        cs = time.perf_counter() - c0
+        cpu = {"value": round(nrow * L / cs / 1e9, 6), "unit": "Gtok·ch/s", "cores": 1, "kind": "oracle",
+               "sample": f"{nrow} of {b * d} (batch, channel) rows x {L} tokens: oracle conv1d, u rounded to "
+                         f"{c.io}, oracle scan, fp64, one row at a time, {cs:.2f} s wall"}
+
+    out = {
+        "metric": "causal conv1d + SiLU + selective-scan fwd Gtok·ch/s (conv fused into the scan)",
+        "value": round(tc / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "Gtok·ch/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{c.name} conv1d (K 4, bias) + SiLU + selective scan: batch {b}, d_inner {d}, "
+                               f"d_state {n}, L {L}, {c.io} io, fp32 state, "
+                               + ("gated" if c.gated else "ungated") + f", {args.discretization}",
+                   "batch": b, "d_inner": d, "d_state": n, "seqlen": L},
+        "kernel_ms": round(launch_ms, 4),
+        "separate_ms": round(sep_ms, 4),
+        "identical_to_separate": identical,
+        "hbm_gbps": round(alg_bytes / (launch_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(peak, 3),
+                     "unit": "T VALU issue-slots/s", "frac": round(achieved / peak, 4),
+                     "traffic": (read_traffic(alg_bytes, PROFILE_TRAFFIC_CONV_FUSED)
+                                 if args.discretization == "zoh" else None)},
+        "cpu_baseline": cpu,
+        "parity_sampled": parity,
+    }
+    print(json.dumps(out), flush=True)
+    return 0 if identical else 1
+
+
 def bench_varlen(args, c) -> int:
     """Variable-length batch over the forward config's channels and total tokens: batch x L tokens
     per channel split into a seeded mix of sequence lengths (uniform 64..2048, the last one
@@ -577,6 +710,8 @@ def main() -> int:
     ap.add_argument("--nchunks", type=int, default=0, help="time chunks (0 = library default)")
     ap.add_argument("--bwd", action="store_true", help="time the backward pass of the forward config instead")
     ap.add_argument("--conv", action="store_true", help="time the causal conv1d + SiLU on the forward config's input")
+    ap.add_argument("--conv-fused", action="store_true",
+                    help="time the causal conv1d + SiLU fused into the forward scan (and the two separate launches)")
     ap.add_argument("--ssd", action="store_true",
                     help="time the multi-head SSM with a scalar decay per head (state-space-duality form)")
     ap.add_argument("--varlen", action="store_true",
@@ -628,6 +763,8 @@ def main() -> int:
         return bench_bwd(args, c)
     if args.conv:
         return bench_conv(args, c)
+    if args.conv_fused:
+        return bench_conv_fused(args, c)
     if args.varlen:
         return bench_varlen(args, c)
     dev = torch.device("cuda:0")

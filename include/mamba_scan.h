@@ -135,6 +135,36 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
                                         int64_t nchunks, int states_per_wave);
 
 /*
+ * Causal depthwise conv1d (4 taps) + SiLU fused into the forward scan's load
+ * stage: the scan input u is computed on chip from x and never round-trips
+ * through HBM (Mamba notes, 设计 3 block pseudo-code: conv1d, SiLU, then the
+ * SSM; State space models and Mamba, Mamba block architecture).  Exactly
+ * mamba_conv1d_fwd(x, conv_weight, conv_bias, conv_state_in, conv_state_out,
+ * kernel_size 4, silu on) followed by mamba_scan_fwd on its output u: u is
+ * rounded to the io dtype before the scan uses it, as a stored u would be, so
+ * the results are identical to the two calls.
+ *
+ *   x               (batch, dim, seqlen)  io    conv input
+ *   conv_weight     (dim, 4)              f32   taps, oldest input first
+ *   conv_bias       (dim)                 f32   NULL means 0
+ *   conv_state_in   (batch, dim, 3)       io    the 3 inputs before x, oldest first; NULL means 0
+ *   conv_state_out  (batch, dim, 3)       io    OUT: the last 3 inputs; NULL: not written; may
+ *                                               equal conv_state_in
+ *   u_out           (batch, dim, seqlen)  io    OUT: the conv output (what the scan consumed);
+ *                                               NULL: not written
+ *   delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, flags,
+ *   workspace (mamba_scan_fwd_workspace_size bytes): as for mamba_scan_fwd.
+ * Sizes and limits as for mamba_scan_fwd, except 1 <= dstate <= 16 (larger returns
+ * MAMBA_SCAN_ERR_UNSUPPORTED).  No output may overlap x.
+ */
+int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias, const void* conv_state_in,
+                        void* conv_state_out, const void* delta, const float* A_log, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                        float* final_state, void* u_out, void* y, int64_t batch, int64_t dim, int64_t dstate,
+                        int64_t seqlen, int io_dtype, int flags, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * Forward scan over a variable-length batch: nseq sequences packed one after
  * another along the time axis, sequence s on tokens [cu_seqlens[s],
  * cu_seqlens[s+1]).  Each sequence is scanned exactly as mamba_scan_fwd scans

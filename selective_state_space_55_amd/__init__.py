@@ -25,6 +25,7 @@ STATUS = {
 }
 EXPORTED = (
     "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
+    "mamba_scan_fwd_conv",
     "mamba_scan_fwd_varlen", "mamba_scan_fwd_varlen_workspace_size", "mamba_scan_step", "mamba_scan_bwd",
     "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd", "mamba_ssd_fwd", "mamba_scan_status_str",
     "mamba_scan_abi_version",
@@ -54,6 +55,8 @@ def load_library():
     lib.mamba_scan_fwd_ex.argtypes = [P] * 11 + [I64] * 4 + [I, I, I64, I, P, SZ, P]
     lib.mamba_scan_fwd_workspace_size.restype = SZ
     lib.mamba_scan_fwd_workspace_size.argtypes = [I64] * 4 + [I]
+    lib.mamba_scan_fwd_conv.restype = I
+    lib.mamba_scan_fwd_conv.argtypes = [P] * 16 + [I64] * 4 + [I, I, P, SZ, P]
     lib.mamba_scan_fwd_workspace_size_ex.restype = SZ
     lib.mamba_scan_fwd_workspace_size_ex.argtypes = [I64] * 4 + [I, I64, I]
     lib.mamba_scan_step.restype = I
@@ -194,6 +197,80 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
                                _stream(dev, stream))
     _check("mamba_scan_fwd", rc)
     return (y, fs) if return_final_state else y
+
+
+def scan_fwd_conv(x: torch.Tensor, conv_weight: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor,
+                  B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                  delta_bias: Optional[torch.Tensor] = None, conv_bias: Optional[torch.Tensor] = None,
+                  conv_state: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                  delta_softplus: bool = True, return_final_state: bool = False, return_conv_state: bool = False,
+                  return_u: bool = False, *, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, conv_state_out: Optional[torch.Tensor] = None,
+                  u_out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                  discretization: str = "zoh", stream=None):
+    """Causal depthwise conv1d (4 taps) + SiLU fused into the forward scan: u = SiLU(conv(x)) is formed
+    on chip.  x, delta, z: (batch, dim, L) and B, C: (batch, dstate <= 16, L) in the io dtype;
+    conv_weight (dim, 4), conv_bias (dim,), A_log (dim, dstate), D, delta_bias (dim,) float32;
+    conv_state (batch, dim, 3) in the io dtype.  Returns y, followed by the final state, the final
+    conv state and u for each of return_final_state, return_conv_state, return_u that is set."""
+    lib = load_library()
+    if x.dim() != 3:
+        raise ValueError("x must be (batch, dim, L)")
+    batch, dim, L = x.shape
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_conv needs device tensors (HIP)")
+    io = _io_dtype(x)
+    iot = x.dtype
+    dstate = A_log.shape[-1] if A_log.dim() == 2 else -1
+    _req("x", x, (batch, dim, L), iot, dev)
+    _req("conv_weight", conv_weight, (dim, 4), torch.float32, dev)
+    _req("conv_bias", conv_bias, (dim,), torch.float32, dev)
+    _req("conv_state", conv_state, (batch, dim, 3), iot, dev)
+    _req("delta", delta, (batch, dim, L), iot, dev)
+    _req("A_log", A_log, (dim, dstate), torch.float32, dev)
+    _req("B", B, (batch, dstate, L), iot, dev)
+    _req("C", C, (batch, dstate, L), iot, dev)
+    _req("D", D, (dim,), torch.float32, dev)
+    _req("z", z, (batch, dim, L), iot, dev)
+    _req("delta_bias", delta_bias, (dim,), torch.float32, dev)
+    _req("initial_state", initial_state, (batch, dim, dstate), torch.float32, dev)
+    y = out if out is not None else torch.empty((batch, dim, L), dtype=iot, device=dev)
+    _req("out", y, (batch, dim, L), iot, dev)
+    fs = final_state
+    if fs is None and return_final_state:
+        fs = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _req("final_state", fs, (batch, dim, dstate), torch.float32, dev)
+    cso = conv_state_out
+    if cso is None and return_conv_state:
+        cso = torch.empty((batch, dim, 3), dtype=iot, device=dev)
+    _req("conv_state_out", cso, (batch, dim, 3), iot, dev)
+    uo = u_out
+    if uo is None and return_u:
+        uo = torch.empty((batch, dim, L), dtype=iot, device=dev)
+    _req("u_out", uo, (batch, dim, L), iot, dev)
+    need = fwd_workspace_size(batch, dim, dstate, L, io)
+    ws = workspace
+    if ws is None and need > 0:
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if ws is not None:
+        base = ws.data_ptr()
+        off = (-base) % 256
+        ws_ptr, ws_bytes = ctypes.c_void_p(base + off), max(0, ws.numel() * ws.element_size() - off)
+    rc = lib.mamba_scan_fwd_conv(_ptr(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(cso),
+                                 _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                                 _ptr(initial_state), _ptr(fs), _ptr(uo), _ptr(y), batch, dim, dstate, L, io,
+                                 _flags(delta_softplus, discretization), ws_ptr, ws_bytes, _stream(dev, stream))
+    _check("mamba_scan_fwd_conv", rc)
+    res = [y]
+    if return_final_state:
+        res.append(fs)
+    if return_conv_state:
+        res.append(cso)
+    if return_u:
+        res.append(uo)
+    return res[0] if len(res) == 1 else tuple(res)
 
 
 def fwd_varlen_workspace_size(nseq: int, dim: int, dstate: int, total_len: int, io_dtype: int = BF16) -> int:

@@ -113,6 +113,50 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const v
                            dstate, seqlen, io_dtype, flags, 0, 0, workspace, workspace_bytes, stream);
 }
 
+int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* conv_bias, const void* conv_state_in,
+                        void* conv_state_out, const void* delta, const float* A_log, const void* B, const void* C,
+                        const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                        float* final_state, void* u_out, void* y, int64_t batch, int64_t dim, int64_t dstate,
+                        int64_t seqlen, int io_dtype, int flags, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (dstate > 16) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (!A_log || !conv_weight) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!x || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {x, delta, B, C, z, y, u_out, conv_state_in, conv_state_out};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, delta_bias, initial_state, final_state, conv_weight, conv_bias};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  mscan::FwdPlan plan;
+  if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, 0, 0, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (plan.ws_total > 0) {
+    if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
+  }
+  mscan::FwdArgs a{};
+  a.u = x; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_state; a.final_state = final_state; a.y = y;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
+  a.workspace = workspace;
+  a.conv_w = conv_weight; a.conv_b = conv_bias; a.conv_state = conv_state_in; a.u_out = u_out;
+  hipError_t e = mscan::launch_fwd(a, plan, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess && conv_state_out) {
+    // after the scan, which reads conv_state_in (the two may be the same buffer)
+    mscan::ConvArgs c{};
+    c.x = x; c.state_in = conv_state_in; c.state_out = conv_state_out;
+    c.batch = batch; c.dim = dim; c.seqlen = seqlen; c.K = 4; c.io_bf16 = a.io_bf16;
+    e = mscan::launch_conv_state(c, static_cast<hipStream_t>(stream));
+  }
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
 size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t dstate, int64_t total_len,
                                             int io_dtype) {
   if (nseq < 1) return (size_t)-1;

@@ -176,10 +176,24 @@ hipError_t run_conv(const ConvArgs& c, hipStream_t s) {
   return hipSuccess;
 }
 
+template <typename IoT>
+hipError_t run_conv_state(const ConvArgs& c, hipStream_t s) {
+  if (!c.state_out || c.K <= 1) return hipSuccess;
+  CArgs a{};
+  a.x = c.x; a.state_in = c.state_in; a.state_out = c.state_out;
+  a.rows = c.batch * c.dim; a.seqlen = c.seqlen; a.dim = c.dim; a.K = (int)c.K;
+  hipLaunchKernelGGL(conv_state_kernel<IoT>, dim3((unsigned)((a.rows + 255) / 256)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream) {
   return a.io_bf16 ? run_conv<uint16_t>(a, stream) : run_conv<float>(a, stream);
+}
+
+hipError_t launch_conv_state(const ConvArgs& a, hipStream_t stream) {
+  return a.io_bf16 ? run_conv_state<uint16_t>(a, stream) : run_conv_state<float>(a, stream);
 }
 
 }  // namespace mscan

@@ -47,6 +47,11 @@ struct FwdArgs {
   void* workspace;
   const int64_t* cu;  // variable-length batch: sequence offsets (nseq + 1), device; rows are (dim, seqlen)
   int64_t nseq;
+  // fused causal conv1d (K = 4) + SiLU: u is the conv input; conv_w non-NULL turns it on
+  const float* conv_w;       // (dim, 4)
+  const float* conv_b;       // (dim) or NULL
+  const void* conv_state;    // (batch, dim, 3) io or NULL
+  void* u_out;               // (batch, dim, seqlen) io or NULL
 };
 
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
@@ -130,6 +135,8 @@ struct ConvArgs {
 };
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t stream);
+// only the conv state update of launch_conv (state_out from x and state_in)
+hipError_t launch_conv_state(const ConvArgs& a, hipStream_t stream);
 
 // Multi-head SSM with a scalar decay per head (state-space-duality form), bf16 io.
 struct SsdArgs {

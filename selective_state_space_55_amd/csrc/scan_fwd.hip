@@ -512,6 +512,13 @@ struct PickH2 {
   };
 };
 
+struct PickH2Conv {
+  template <typename IoT, bool kAgg, bool kVec, int kMode>
+  struct P {
+    static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, false, false, true>; }
+  };
+};
+
 template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
 hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
   auto kern = pick_kernel<PickNpw<NPW, NSPLIT, T>::template P, IoT, kAgg>(vec, k.mode);
@@ -528,6 +535,7 @@ hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s)
   if constexpr (!kAgg) {
     if (k.acc != 0) kern = pick_kernel<PickH2<true>::template P, IoT, kAgg>(vec, k.mode);
   }
+  if (k.conv_w != nullptr) kern = pick_kernel<PickH2Conv::template P, IoT, kAgg>(vec, k.mode);   // 16 states, two per lane
   const size_t lds = sizeof(float) * LdsH2::floats(kAgg);
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -562,9 +570,11 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   const size_t esz = sizeof(IoT);
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a.u) | reinterpret_cast<uintptr_t>(a.delta) |
                         reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z) |
-                        reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C);
+                        reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.C) |
+                        reinterpret_cast<uintptr_t>(a.u_out);
   const bool vec = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
   KArgs k{};
+  k.conv_w = a.conv_w; k.conv_b = a.conv_b; k.conv_state = a.conv_state; k.u_out = a.u_out;
   k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;

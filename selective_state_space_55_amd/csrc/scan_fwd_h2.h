@@ -36,6 +36,11 @@ struct KArgs {
   const int64_t* cu;   // varlen: sequence start offsets (nseq + 1), device memory
   int n0;              // first state of this pass (a multiple of 16)
   int acc;             // state-group pass: 1 first (writes yacc), 2 middle (adds), 3 last (adds, writes y)
+  // fused causal conv1d (K = 4) + SiLU in front of the scan: u holds the conv input x
+  const float* conv_w;     // (dim, 4) taps, oldest input first
+  const float* conv_b;     // (dim) or NULL
+  const void* conv_state;  // (batch, dim, 3) io: the inputs before the sequence, or NULL (zeros)
+  void* u_out;             // (batch, dim, seqlen) io: the conv output, or NULL
 };
 
 // Work id with XCD-aware placement: the hardware deals consecutive workgroup
@@ -76,7 +81,13 @@ struct LdsH2 {
 // from the sequence's own initial state.  Tiles stay aligned to 64 tokens of
 // the row (whole-line loads); tokens of the first tile before the sequence
 // start are staged as Delta = 0, u = 0 (state unchanged) and not stored.
-template <typename IoT, bool kAgg, bool kVec, int kMode, bool kMulti, bool kVarlen = false>
+// kConv: u is the output of a causal depthwise conv1d (4 taps) + SiLU of the
+// input in a.u, computed while staging: a piece's three inputs before its first
+// token come from the neighbouring piece (cross-lane read) or, for a tile's
+// first piece, from the previous tile (kept in registers), the chunk's
+// preceding inputs or the conv state.  The conv output is rounded to the io
+// dtype, so the result equals the conv1d launch followed by the scan.
+template <typename IoT, bool kAgg, bool kVec, int kMode, bool kMulti, bool kVarlen = false, bool kConv = false>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -188,6 +199,29 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
   const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
 
+  // conv taps and bias of the staging piece's channel; xlast: the three inputs
+  // before the next tile's first piece (meaningful on the pieces that end a tile)
+  float cw[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cbias = 0.0f, xlast[3] = {0.0f, 0.0f, 0.0f};
+  if constexpr (kConv) {
+    const int64_t dp = d0 + pc;
+    if (dp < a.dim) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) cw[k] = a.conv_w[dp * 4 + k];
+      cbias = a.conv_b ? a.conv_b[dp] : 0.0f;
+      if (pg == 7) {
+        if (t_first > 0) {
+#pragma unroll
+          for (int i = 0; i < 3; ++i) xlast[i] = IO::load1(gu + (b * a.dim + dp) * a.seqlen + t_first - 3 + i);
+        } else if (a.conv_state) {
+          const IoT* cs = static_cast<const IoT*>(a.conv_state) + (b * a.dim + dp) * 3;
+#pragma unroll
+          for (int i = 0; i < 3; ++i) xlast[i] = IO::load1(cs + i);
+        }
+      }
+    }
+  }
+  IoT* __restrict__ guo = static_cast<IoT*>(a.u_out);
+
   // B/C piece: state bn, 4-token group bg; waves 0-3 load B, 4-7 load C
   const int bn = tid % NP;          // state of this thread's B/C piece within the pass's 16
   const int bg = (tid / NP) % kG;
@@ -219,6 +253,39 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     float fd[8], fu[8];
     IO::to_f32(p.d, fd);
     IO::to_f32(p.u, fu);
+    if constexpr (kConv) {
+      // xx[0..2]: inputs before the piece (from the piece below, or for the
+      // first piece of the tile from the previous tile's last piece), xx[3..10]: the piece
+      float xx[11];
+      const int src = pg == 0 ? lane + 7 : lane - 1;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const float pv = pg == 7 ? xlast[i] : fu[5 + i];
+        xx[i] = __shfl(pv, src);
+        xlast[i] = fu[5 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xx[3 + i] = fu[i];
+      float cu[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float acc = cbias;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc = fmaf(cw[k], xx[i + k], acc);   // input time t - 3 + k
+        cu[i] = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * kLog2e));
+      }
+      const V8 cr = IO::from_f32(cu);   // rounded to the io dtype, as a stored conv output
+      IO::to_f32(cr, fu);
+      if constexpr (!kAgg) {
+        if (guo != nullptr && d0 + pc < a.dim) {
+          IoT* uo = guo + (b * a.dim + d0 + pc) * a.seqlen + tile + pg * 8;
+          if (kFull && kVec)
+            IO::store8(uo, cr);
+          else
+            IO::store_n(uo, cr, nv);
+        }
+      }
+    }
     const float bi = par[pc];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

@@ -231,3 +231,27 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, x=P + 2) == EALIGN               # 16-byte vector loads
     assert ssd(lib, h0=P + 4) == EALIGN
     assert ssd(lib, batch=1 << 20, H=1 << 12) == EUNSUP
+
+
+def fwd_conv(lib, x=P, w=P, cb=None, csi=None, cso=None, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None,
+             h0=None, fs=None, uo=None, y=P, batch=2, dim=64, dstate=16, seqlen=128, io=1, flags=1, ws=None, wsb=0):
+    return lib.mamba_scan_fwd_conv(x, w, cb, csi, cso, delta, A_log, B, C, D, z, bias, h0, fs, uo, y, batch, dim,
+                                   dstate, seqlen, io, flags, ws, wsb, None)
+
+
+def test_fwd_conv_validation_errors(lib):
+    assert fwd_conv(lib, w=None) == ENULL
+    assert fwd_conv(lib, x=None) == ENULL
+    assert fwd_conv(lib, A_log=None, seqlen=0) == ENULL
+    assert fwd_conv(lib, dstate=17) == EUNSUP          # the fused path covers one 16-state group
+    assert fwd_conv(lib, dstate=65) == EUNSUP
+    assert fwd_conv(lib, flags=4) == EUNSUP
+    assert fwd_conv(lib, io=3) == EDTYPE
+    assert fwd_conv(lib, x=P + 1) == EALIGN
+    assert fwd_conv(lib, csi=P + 1) == EALIGN
+    assert fwd_conv(lib, uo=P + 1) == EALIGN
+    assert fwd_conv(lib, w=P + 2) == EALIGN
+    assert fwd_conv(lib, seqlen=-1) == ESHAPE
+    # a single time chunk needs no workspace; four chunks do
+    assert mscan.fwd_workspace_size(1, 64, 16, 2048, mscan.BF16) > 0
+    assert fwd_conv(lib, batch=1, dim=64, seqlen=2048, ws=None) == EWS

@@ -1,0 +1,116 @@
+"""Causal conv1d (4 taps) + SiLU fused into the forward scan (mamba_scan_fwd_conv)
+on the GPU, through the C ABI.
+
+* Bit for bit against the two separate launches it replaces (mamba_conv1d_fwd,
+  then mamba_scan_fwd on its output): y, the final state, the conv output u and
+  the final conv state, over ragged lengths and widths, one and several time
+  chunks, with and without conv bias, conv state, gate, D and delta bias, ZOH
+  and Euler, fp32 and bf16.
+* Against the fp64 oracle's composition (oracle conv1d, u rounded to the io
+  dtype as a stored conv output is, oracle scan) at the forward tolerances.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import selective_state_space_55_amd as mscan
+from workloads import conv_inputs, err_report, forward_inputs
+
+pytestmark = pytest.mark.gpu
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def say(msg):
+    print(f"[conv+scan] {msg}", flush=True)
+
+
+def dev(t):
+    return None if t is None else t.to("cuda:0")
+
+
+def same(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a, b)
+
+
+# (batch, dim, dstate, L, io, gated, has_D, has_bias, conv_bias, conv_state, h0, disc)
+CASES = [
+    (1, 64, 16, 256, "f32", True, True, True, True, False, False, "zoh"),
+    (2, 70, 16, 100, "bf16", True, True, True, True, True, True, "zoh"),
+    (1, 130, 5, 33, "bf16", False, True, False, False, True, False, "zoh"),
+    (2, 64, 16, 1, "f32", True, False, True, True, True, True, "zoh"),
+    (1, 3, 1, 31, "f32", False, True, False, True, False, False, "zoh"),
+    (3, 65, 12, 160, "bf16", True, True, True, True, True, False, "euler"),
+    (1, 64, 16, 2048, "bf16", True, True, True, True, True, True, "zoh"),     # four time chunks
+    (1, 96, 16, 1000, "f32", False, True, True, False, True, True, "euler"),  # chunks, ragged tail
+    (2, 128, 16, 640, "bf16", True, True, True, True, False, False, "zoh"),
+]
+IDS = [f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}{'g' if c[5] else ''}-{c[11]}" for c in CASES]
+
+
+def make(case):
+    b, d, n, L, io, gated, hasD, hasB, cb, cs, h0, disc = case
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, has_D=hasD, has_bias=hasB,
+                         initial_state=h0, seed=L + d)
+    _, w, bias, st = conv_inputs(b, d, L, 4, io, seed=L + d, state=cs)
+    return inp, w, (bias if cb else None), st
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_fused_equals_conv_then_scan(case):
+    inp, w, cbias, cst = make(case)
+    disc = case[11]
+    a = {k: dev(v) for k, v in inp.items()}
+    wd, cbd, csd = dev(w), dev(cbias), dev(cst)
+    say(f"fused vs separate {case}")
+    y, fs, cso, u = mscan.scan_fwd_conv(a["u"], wd, a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                                        delta_bias=a["delta_bias"], conv_bias=cbd, conv_state=csd,
+                                        initial_state=a["initial_state"], return_final_state=True,
+                                        return_conv_state=True, return_u=True, discretization=disc)
+    u_ref, cso_ref = mscan.conv1d_fwd(a["u"], wd, cbd, csd, silu=True, return_state=True)
+    y_ref, fs_ref = mscan.scan_fwd(u_ref, a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                                   delta_bias=a["delta_bias"], initial_state=a["initial_state"],
+                                   return_final_state=True, discretization=disc)
+    torch.cuda.synchronize()
+    assert same(u, u_ref), "conv output"
+    assert same(cso, cso_ref), "final conv state"
+    assert same(y, y_ref), "y"
+    assert torch.equal(fs, fs_ref), "final state"
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[5], CASES[7]], ids=[IDS[0], IDS[1], IDS[5], IDS[7]])
+def test_fused_vs_oracle(case):
+    inp, w, cbias, cst = make(case)
+    io, disc = case[4], case[11]
+    a = {k: dev(v) for k, v in inp.items()}
+    say(f"fused vs oracle {case}")
+    y, fs = mscan.scan_fwd_conv(a["u"], dev(w), a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                                delta_bias=a["delta_bias"], conv_bias=dev(cbias), conv_state=dev(cst),
+                                initial_state=a["initial_state"], return_final_state=True, discretization=disc)
+    u64 = oracle.conv1d_fwd(inp["u"], w, cbias, conv_state=cst, silu=True)
+    u_io = torch.from_numpy(np.asarray(u64, dtype=np.float32)).to(DT[io])   # as a stored conv output
+    yr, fsr = oracle.scan_fwd(u_io, inp["delta"], inp["A_log"], inp["B"], inp["C"], D=inp["D"], z=inp["z"],
+                              delta_bias=inp["delta_bias"], initial_state=inp["initial_state"],
+                              discretization=disc)
+    ry, rf = err_report(y.float().cpu(), yr), err_report(fs.cpu(), fsr)
+    say(f"  y {ry}  final state {rf}")
+    assert ry["max_rel"] <= TOL[io] and rf["max_rel"] <= TOL[io]
+
+
+def test_fused_seqlen_zero():
+    """No tokens: the final state is the initial state and the conv state passes through."""
+    b, d, n = 2, 70, 16
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=0, io="bf16", initial_state=True)
+    _, w, bias, st = conv_inputs(b, d, 0, 4, "bf16", state=True)
+    a = {k: dev(v) for k, v in inp.items()}
+    y, fs, cso = mscan.scan_fwd_conv(a["u"], dev(w), a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                                     delta_bias=a["delta_bias"], conv_bias=dev(bias), conv_state=dev(st),
+                                     initial_state=a["initial_state"], return_final_state=True,
+                                     return_conv_state=True)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(fs.cpu(), inp["initial_state"])
+    assert same(cso.cpu(), st)
