@@ -256,6 +256,97 @@ __global__ __launch_bounds__(256) void scan_step_quad_kernel(SArgs a) {
   });
 }
 
+// The same idea for d_state 32 and 64 (LPC = 8 or 16 lanes per channel, dstate
+// = 4 LPC, vector-aligned rows): lanes q < 4 of a channel's group do row q's
+// scalar work, and Delta and x of row r reach the group's other lanes by a
+// cross-lane read.  Identical results to the general kernel.
+template <typename IoT, int LPC, bool kFull, bool kEuler>
+__global__ __launch_bounds__(256) void scan_step_rows_kernel(SArgs a) {
+  using IO = Io<IoT>;
+  static_assert(LPC == 8 || LPC == 16, "lanes per channel");
+  constexpr uint32_t N = 4 * LPC;
+  const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
+  const uint32_t dq = gid / LPC;
+  const int q = (int)(gid % LPC);
+  const int lane = (int)(threadIdx.x & 63);
+  const int gbase = lane & ~(LPC - 1);   // first lane of the channel's group
+  const uint32_t dim = (uint32_t)a.dim;
+  const bool live_d = kFull || dq < dim;
+  const uint32_t d = live_d ? dq : 0u;
+  const int64_t b0 = (int64_t)blockIdx.y * 4;
+
+  const IoT* gx = static_cast<const IoT*>(a.x) + b0 * a.dim;
+  const IoT* gdt = static_cast<const IoT*>(a.dt) + b0 * a.dim;
+  const IoT* gz = a.z ? static_cast<const IoT*>(a.z) + b0 * a.dim : nullptr;
+  const IoT* gB = static_cast<const IoT*>(a.B) + b0 * N;
+  const IoT* gC = static_cast<const IoT*>(a.C) + b0 * N;
+  float* gst = a.state + b0 * a.dim * N;
+  IoT* gy = static_cast<IoT*>(a.y) + b0 * a.dim;
+
+  // lanes 0-3 of the group: row q's scalars
+  const bool own = q < 4;
+  const bool live_q = own && (kFull || (live_d && b0 + q < a.batch));
+  const uint32_t oq = live_q ? (uint32_t)q * dim + d : 0u;
+  const float xq = live_q ? IO::load1(gx + oq) : 0.0f;
+  const float rq = live_q ? IO::load1(gdt + oq) : 0.0f;
+  const float zq = (live_q && gz) ? IO::load1(gz + oq) : 0.0f;
+
+  float Bv[4][4], Cv[4][4], hs[4][4];
+  bool live[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    live[r] = kFull || (live_d && b0 + r < a.batch);
+    const uint32_t rr = live[r] ? (uint32_t)r : 0u;
+    load_bc4<IoT, true>(gB, rr, q, N, Bv[r]);
+    load_bc4<IoT, true>(gC, rr, q, N, Cv[r]);
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (live[r]) v = *reinterpret_cast<const f32x4*>(gst + (rr * dim + d) * N + 4u * q);
+    hs[r][0] = v.x; hs[r][1] = v.y; hs[r][2] = v.z; hs[r][3] = v.w;
+  }
+  float An[4], iA[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    An[j] = -expf(a.A_log[d * N + 4u * q + j]);
+    iA[j] = 1.0f / An[j];
+  }
+  const float bias = a.bias ? a.bias[d] : 0.0f;
+  const float Dd = a.D ? a.D[d] : 0.0f;
+  const float xb = rq + bias;
+  const float dlq = a.softplus ? softplus_log2e(xb) : xb * 1.4426950408889634f;   // Delta * log2e of row q
+  const float gq = gz ? silu(zq) : 1.0f;
+
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const float dl = __shfl(dlq, gbase + r);
+    const float xv = __shfl(xq, gbase + r);
+    float acc = 0.0f;
+    if constexpr (kEuler) {
+      const float du = (dl * 0.6931471805599453f) * xv;   // Delta u
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float s = Bv[r][j] * (xv * iA[j]);   // B u / A
+        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        acc = fmaf(Cv[r][j], hs[r][j], acc);
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPC; m <<= 1) acc += __shfl_xor(acc, m, LPC);   // as the general kernel
+    if (live[r]) {
+      const f32x4 v = {hs[r][0], hs[r][1], hs[r][2], hs[r][3]};
+      *reinterpret_cast<f32x4*>(gst + ((uint32_t)r * dim + d) * N + 4u * q) = v;
+      if (q == r) IO::store1(gy + oq, fmaf(Dd, xq, acc) * gq);
+    }
+  }
+}
+
 template <typename IoT>
 hipError_t run_step(const StepArgs& s, hipStream_t stream) {
   SArgs a{};
@@ -274,6 +365,19 @@ hipError_t run_step(const StepArgs& s, hipStream_t stream) {
     auto k = full ? (s.euler ? scan_step_quad_kernel<IoT, true, true> : scan_step_quad_kernel<IoT, true, false>)
                   : (s.euler ? scan_step_quad_kernel<IoT, false, true> : scan_step_quad_kernel<IoT, false, false>);
     hipLaunchKernelGGL(k, g4, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
+  if (vec && lpc > 4 && s.dim * s.dstate < (int64_t(1) << 27)) {
+    const dim3 g4((unsigned)((threads + 255) / 256), (unsigned)((s.batch + 3) / 4));
+    const bool full = (s.batch % 4 == 0) && (threads % 256 == 0);
+#define MSCAN_STEP_ROWS(L)                                                                               \
+    {                                                                                                    \
+      auto k = full ? (s.euler ? scan_step_rows_kernel<IoT, L, true, true> : scan_step_rows_kernel<IoT, L, true, false>) \
+                    : (s.euler ? scan_step_rows_kernel<IoT, L, false, true> : scan_step_rows_kernel<IoT, L, false, false>); \
+      hipLaunchKernelGGL(k, g4, dim3(256), 0, stream, a);                                               \
+    }
+    if (lpc == 8) MSCAN_STEP_ROWS(8) else MSCAN_STEP_ROWS(16)
+#undef MSCAN_STEP_ROWS
     return hipGetLastError();
   }
   const dim3 grid((unsigned)((threads + 255) / 256), (unsigned)((s.batch + kRows - 1) / kRows));

@@ -192,17 +192,18 @@ def _offset_copy(t):
 @pytest.mark.parametrize("b,d", [(8, 128), (3, 70), (5, 64), (4, 200)])
 @pytest.mark.parametrize("disc", ["zoh", "euler"])
 @pytest.mark.parametrize("gated", [True, False])
-def test_step_quad_path_matches_general(b, d, disc, gated):
-    """d_state 16 with aligned rows runs the four-rows-per-quad decode kernel; the same
-    steps with B and C off alignment run the general kernel.  Same arithmetic in the same
-    order: bit-identical results, and both within tolerance of the oracle."""
-    n = 16
+@pytest.mark.parametrize("n", [16, 32, 64])
+def test_step_row_owner_path_matches_general(b, d, disc, gated, n):
+    """d_state 16, 32 or 64 with aligned rows runs the decode kernels where one lane of a
+    channel's group does a batch row's scalar work; the same steps with B and C off alignment
+    run the general kernel.  Same arithmetic in the same order: bit-identical results, and
+    both within tolerance of the oracle."""
     init = step_initial(None, batch=b, dim=d, dstate=n)
     A, D, bias = dev(init["A_log"]), dev(init["D"]), dev(init["dt_bias"])
     st_q = dev(init["state"]).clone()
     st_g = st_q.clone()
     st_ref = init["state"].double().numpy()
-    say(f"quad vs general b={b} d={d} {disc} gated={gated}")
+    say(f"row-owner vs general b={b} d={d} n={n} {disc} gated={gated}")
     for k in range(6):
         s = step_inputs(None, k, batch=b, dim=d, dstate=n, io="bf16", gated=gated)
         Bq, Cq = dev(s["B"]), dev(s["C"])
