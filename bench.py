@@ -538,6 +538,9 @@ def bench_varlen(args, c) -> int:
     total = c.batch * c.seqlen
     rng = np.random.default_rng(1234)
     lens = []
+    if args.varlen_lens:
+        lens = [int(x) for x in args.varlen_lens.split(",")]
+        total = sum(lens)
     while sum(lens) < total:
         lens.append(int(min(rng.integers(64, 2049), total - sum(lens))))
     nseq = len(lens)
@@ -593,8 +596,9 @@ def bench_varlen(args, c) -> int:
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": f"{c.name} channels, variable-length batch: {nseq} sequences of 64-2048 tokens "
-                               f"(seeded uniform), {total} tokens, d_inner {c.dim}, d_state {c.dstate}, {c.io} io, "
+        "config": {"workload": f"{c.name} channels, variable-length batch: {nseq} sequences of "
+                               + (f"lengths {args.varlen_lens}" if args.varlen_lens else "64-2048 tokens (seeded uniform)")
+                               + f", {total} tokens, d_inner {c.dim}, d_state {c.dstate}, {c.io} io, "
                                f"{'gated' if c.gated else 'ungated'}, per-sequence initial and final states",
                    "nseq": nseq, "total_tokens": total, "d_inner": c.dim, "d_state": c.dstate},
         "kernel_ms": round(launch_ms, 4),
@@ -716,6 +720,8 @@ def main() -> int:
                     help="time the multi-head SSM with a scalar decay per head (state-space-duality form)")
     ap.add_argument("--varlen", action="store_true",
                     help="time a variable-length batch with the forward config's channels and total tokens")
+    ap.add_argument("--varlen-lens", default="",
+                    help="varlen: comma-separated sequence lengths instead of the seeded 64-2048 mix")
     ap.add_argument("--dstate", type=int, default=0,
                     help="override the workload's d_state (up to 64; the headline workload uses 16)")
     ap.add_argument("--discretization", choices=["zoh", "euler"], default="zoh",

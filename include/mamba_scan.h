@@ -183,12 +183,16 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
  *                     array gives wrong results but no out-of-bounds access.
  *   initial_states    (nseq, dim, dstate) f32   NULL means zeros
  *   final_states      (nseq, dim, dstate) f32   OUT, NULL means not written
- *   A_log, D, delta_bias, flags, workspace: as for mamba_scan_fwd (workspace from
- *                     mamba_scan_fwd_varlen_workspace_size; 0 bytes for dstate <= 16)
+ *   A_log, D, delta_bias, flags: as for mamba_scan_fwd
+ *   workspace         at least mamba_scan_fwd_varlen_workspace_size(...) bytes (never 0),
+ *                     256-byte aligned: the number of pieces per sequence, the state
+ *                     entering each piece, and for dstate > 16 a readout sum
+ * Sequences are cut into pieces of at most 2048 tokens that are scanned in
+ * parallel and joined through their carried states (as the time chunks of
+ * mamba_scan_fwd), so one long sequence is not one long serial scan.
  * Sizes: nseq >= 1, dim >= 1, 1 <= dstate <= 64, total_len >= 0 with the seqlen
- * limit of mamba_scan_fwd; nseq * ceil(dim / 64) < 2^31.  No time chunking: work
- * items are (sequence, 64-channel group), so a few very long sequences use few
- * workgroups.
+ * limit of mamba_scan_fwd; (nseq + ceil(total_len / 2048)) * ceil(dim / 64) < 2^31
+ * and nseq * dim * dstate < 2^31 (else MAMBA_SCAN_ERR_UNSUPPORTED).
  */
 int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, const int64_t* cu_seqlens,
@@ -196,7 +200,7 @@ int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, 
                           int64_t dstate, int64_t total_len, int io_dtype, int flags, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace mamba_scan_fwd_varlen needs; (size_t)-1 for rejected sizes. */
+/* Bytes of workspace mamba_scan_fwd_varlen needs (> 0); (size_t)-1 for rejected sizes. */
 size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t dstate, int64_t total_len,
                                             int io_dtype);
 

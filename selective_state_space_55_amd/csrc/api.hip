@@ -161,8 +161,8 @@ size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t d
                                             int io_dtype) {
   if (nseq < 1) return (size_t)-1;
   if (check_fwd_sizes(1, dim, dstate, total_len, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
-  mscan::FwdPlan p;
-  if (!mscan::make_fwd_plan(1, dim, dstate, total_len, 1, 2, &p)) return (size_t)-1;
+  mscan::VarlenPlan p;
+  if (!mscan::make_varlen_plan(nseq, dim, dstate, total_len, &p)) return (size_t)-1;
   return p.ws_total;
 }
 
@@ -175,8 +175,11 @@ int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, 
   int st = check_fwd_sizes(1, dim, dstate, total_len, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
   if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  mscan::VarlenPlan plan;
+  if (!mscan::make_varlen_plan(nseq, dim, dstate, total_len, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
-  if (!mul_ok(nseq, (dim + 63) / 64, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid size
+  if (!mul_ok(plan.maxp, (dim + 63) / 64, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid size
+  if (!mul_ok(nseq, dim * dstate, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // carry threads
   if (!A_log || !cu_seqlens) return MAMBA_SCAN_ERR_NULL;
   if (total_len > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
   const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
@@ -187,11 +190,7 @@ int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, 
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   if (!aligned(cu_seqlens, 8)) return MAMBA_SCAN_ERR_ALIGN;
-  mscan::FwdPlan plan;
-  if (!mscan::make_fwd_plan(1, dim, dstate, total_len, 1, 2, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
-  if (plan.ws_total > 0) {
-    if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
-  }
+  if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
   mscan::FwdArgs a{};
   a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
   a.h0 = initial_states; a.final_state = final_states; a.y = y;

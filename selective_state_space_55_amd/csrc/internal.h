@@ -55,8 +55,24 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
-// batch must be 1 in the plan; h0 / final_state are (nseq, dim, dstate)
-hipError_t launch_fwd_varlen(const FwdArgs& a, const FwdPlan& p, hipStream_t stream);
+
+// Variable-length batch: each sequence is cut into pieces of at most `piece`
+// tokens, scanned like the time chunks of a row (aggregate pass, carry, output
+// pass).  The pieces per sequence are counted on the device (the offsets are
+// device memory), so launches cover the upper bound maxp.
+struct VarlenPlan {
+  int64_t piece;       // tokens per piece, a multiple of 64
+  int64_t maxp;        // nseq + ceil(total / piece) >= the number of pieces
+  int ngroups, np;     // 16-state groups, padded states
+  size_t off_pstart;   // (nseq + 1) int64: first piece of each sequence, then the total
+  size_t off_carry;    // (maxp, dim, np) fp32: piece aggregates, then the state entering each piece
+  size_t off_dsum;     // (maxp, dim) fp32: sum of Delta*log2e over each piece
+  size_t off_yacc;     // (dim, total) fp32 readout sum when dstate > 16
+  size_t ws_total;
+};
+bool make_varlen_plan(int64_t nseq, int64_t dim, int64_t dstate, int64_t total, VarlenPlan* p);
+// h0 / final_state are (nseq, dim, dstate)
+hipError_t launch_fwd_varlen(const FwdArgs& a, const VarlenPlan& p, hipStream_t stream);
 
 struct StepArgs {
   float* state;

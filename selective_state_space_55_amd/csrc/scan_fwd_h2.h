@@ -34,6 +34,8 @@ struct KArgs {
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
   const int64_t* cu;   // varlen: sequence start offsets (nseq + 1), device memory
+  const int64_t* pstart;   // varlen: first piece of each sequence (nseq + 1), device memory
+  int64_t nseq;            // varlen: number of sequences
   int n0;              // first state of this pass (a multiple of 16)
   int acc;             // state-group pass: 1 first (writes yacc), 2 middle (adds), 3 last (adds, writes y)
   // fused causal conv1d (K = 4) + SiLU in front of the scan: u holds the conv input x
@@ -77,10 +79,12 @@ struct LdsH2 {
 // the pass is summed into an fp32 buffer, and the last pass adds D u, gates
 // and writes y.
 // kVarlen: sequences packed along the time axis of one row per channel; a
-// work item is (sequence, channel group) and scans tokens [cu[s], cu[s+1])
-// from the sequence's own initial state.  Tiles stay aligned to 64 tokens of
-// the row (whole-line loads); tokens of the first tile before the sequence
-// start are staged as Delta = 0, u = 0 (state unchanged) and not stored.
+// work item is (piece, channel group), a piece being up to chunk_len tokens of
+// one sequence [cu[s], cu[s+1]): the first piece starts from the sequence's
+// own initial state, later ones from the carry, as the time chunks of a row
+// do.  Tiles stay aligned to 64 tokens of the row (whole-line loads); tokens of
+// the first tile before the piece start are staged as Delta = 0, u = 0 (state
+// unchanged) and not stored.
 // kConv: u is the output of a causal depthwise conv1d (4 taps) + SiLU of the
 // input in a.u, computed while staging: a piece's three inputs before its first
 // token come from the neighbouring piece (cross-lane read) or, for a tile's
@@ -127,14 +131,30 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   // launched (a contiguous range per XCD would give one XCD all of a long
   // sequence's channel groups)
   int64_t wid = kVarlen ? (int64_t)blockIdx.x : work_id(blockIdx.x, a.nwork);
-  int64_t kc, cg, b, t_begin, t_end, sidx;   // sidx: batch row or sequence of the state arrays
+  // kc of nk: this work item's time chunk (varlen: piece pidx, the kc-th of its sequence's nk)
+  int64_t kc, nk, cg, b, t_begin, t_end, sidx, pidx = 0;   // sidx: batch row or sequence of the state arrays
   if constexpr (kVarlen) {
-    kc = 0;
     cg = wid % a.chgroups;
-    sidx = wid / a.chgroups;
+    pidx = wid / a.chgroups;
+    const int64_t* ps = a.pstart;
+    if (pidx >= ps[a.nseq]) return;   // the grid is an upper bound on the number of pieces
+    int64_t lo = 0, hi = a.nseq - 1;  // the sequence: the last s with ps[s] <= pidx
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (ps[mid] <= pidx)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    sidx = lo;
+    kc = pidx - ps[lo];
+    nk = ps[lo + 1] - ps[lo];
+    if (kAgg && kc >= nk - 1) return;   // a sequence's last piece needs no aggregate
     b = 0;
-    t_begin = min(max(a.cu[sidx], (int64_t)0), a.seqlen);   // clamped: any offsets stay in bounds
-    t_end = min(max(a.cu[sidx + 1], t_begin), a.seqlen);
+    const int64_t s_begin = min(max(a.cu[sidx], (int64_t)0), a.seqlen);   // clamped: any offsets stay in bounds
+    const int64_t s_end = min(max(a.cu[sidx + 1], s_begin), a.seqlen);
+    t_begin = min(s_begin + kc * a.chunk_len, s_end);
+    t_end = min(t_begin + a.chunk_len, s_end);
   } else {
     const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
     kc = wid % nck;
@@ -142,6 +162,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     cg = wid % a.chgroups;
     b = wid / a.chgroups;
     sidx = b;
+    nk = a.nchunks;
     t_begin = kc * a.chunk_len;
     t_end = min(t_begin + a.chunk_len, a.seqlen);
   }
@@ -167,6 +188,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   const int64_t d = d0 + chw;
   const bool ch_ok = d < a.dim;
   const int64_t bd = sidx * a.dim + d;   // (batch row or sequence, channel) of the state arrays
+  const int64_t cslot = kVarlen ? pidx * a.dim + d : bd * a.nchunks + kc;   // chunk slot of carry and dsum
   float A[2], iA[2], h[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     float hv = 0.0f;
     if (!kAgg && valid) {
       if (kc > 0)
-        hv = a.carry[(bd * a.nchunks + kc) * a.np + n];
+        hv = a.carry[cslot * a.np + n];
       else if (a.h0)
         hv = a.h0[bd * a.dstate + n];
     }
@@ -535,12 +557,12 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     for (int j = 0; j < 2; ++j) {
       const int n = a.n0 + sp * 4 + hf * 2 + j;
       if (!kAgg) {
-        if (kc == a.nchunks - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
+        if (kc == nk - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
       } else {
-        a.carry[(bd * a.nchunks + kc) * a.np + n] = h[j];
+        a.carry[cslot * a.np + n] = h[j];
       }
     }
-    if (kAgg && sp == 0 && hf == 0) a.dsum[bd * a.nchunks + kc] = dsum_acc;
+    if (kAgg && sp == 0 && hf == 0) a.dsum[cslot] = dsum_acc;
   }
 }
 

@@ -202,13 +202,18 @@ def test_varlen_validation_errors(lib):
     assert varlen(lib, flags=4) == EUNSUP
     assert varlen(lib, dstate=65) == EUNSUP
     assert varlen(lib, io=7) == EDTYPE
-    assert varlen(lib, dstate=32) == EWS                        # dstate > 16 needs the fp32 readout buffer
+    assert varlen(lib) == EWS                                   # piece counts and carries live in the workspace
+    assert varlen(lib, dstate=32) == EWS
     assert varlen(lib, nseq=1 << 40) == EUNSUP                  # grid size
 
 
 def test_varlen_workspace_size(lib):
-    assert mscan.fwd_varlen_workspace_size(4, 64, 16, 1000) == 0
-    assert mscan.fwd_varlen_workspace_size(4, 64, 64, 1000) >= 64 * 1000 * 4
+    # piece counts (nseq + 1 int64), piece carries and sums over at most nseq + ceil(total / 2048) pieces
+    maxp = 4 + 1
+    small = mscan.fwd_varlen_workspace_size(4, 64, 16, 1000)
+    assert 5 * 8 + maxp * 64 * 17 * 4 <= small <= 5 * 8 + maxp * 64 * 17 * 4 + 3 * 256
+    assert mscan.fwd_varlen_workspace_size(4, 64, 64, 1000) >= 64 * 1000 * 4 + maxp * 64 * 65 * 4
+    assert mscan.fwd_varlen_workspace_size(1, 64, 16, 32768) >= (1 + 16) * 64 * 17 * 4
     with pytest.raises(ValueError):
         mscan.fwd_varlen_workspace_size(0, 64, 16, 1000)
 

@@ -2,7 +2,8 @@
 mamba_scan_fwd_varlen) against the fp64 oracle's varlen scan, and bit-for-bit
 against the fixed-length kernel run on each sequence alone: sequence starts at
 any offset (not tile- or vector-aligned), empty and one-token sequences,
-d_state 16 and above (multi-pass), both input terms, fp32 and bf16."""
+sequences longer than one 2048-token piece, d_state 16 and above (multi-pass),
+both input terms, fp32 and bf16."""
 import sys
 
 import numpy as np
@@ -57,6 +58,11 @@ CASES = [  # (lens, dim, dstate, io, gated, h0, disc)
     ((33, 0, 0, 91, 200), 96, 64, "f32", True, True, "zoh"),
     ((17, 300, 2), 64, 20, "bf16", True, True, "euler"),
     ((129, 1, 77), 65, 16, "f32", True, True, "euler"),
+    # sequences longer than a 2048-token piece: several pieces joined through the carry
+    ((5000, 37, 2048, 0, 4100, 1), 64, 16, "bf16", True, True, "zoh"),
+    ((2049, 3, 6150), 70, 16, "f32", False, True, "euler"),
+    ((3000, 50), 64, 48, "bf16", True, True, "zoh"),
+    ((8192,), 130, 16, "f32", True, False, "zoh"),
 ]
 
 
@@ -96,6 +102,26 @@ def test_varlen_bitexact_vs_fixed_length(dstate, io):
                                  z=sl(p["z"]), delta_bias=dev(p["delta_bias"]),
                                  initial_state=dev(p["initial_states"][s:s + 1].contiguous()),
                                  return_final_state=True, nchunks=1)
+        assert torch.equal(ys[0].cpu(), y[:, a:b]), s
+        assert torch.equal(fss[0].cpu(), fs[s]), s
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_varlen_pieces_bitexact_vs_fixed_length_chunks(io):
+    """Long sequences at tile-aligned offsets: their 2048-token pieces are the time chunks the
+    fixed-length forward uses with 2048-token chunks, so the results agree bit for bit."""
+    lens = (6144, 4096, 64)
+    p = packed_inputs(lens, 96, 16, io, seed=11)
+    say(f"pieces bit-exact io={io}")
+    y, fs = gpu_varlen(p)
+    cu = p["cu"].tolist()
+    for s, ln in enumerate(lens):
+        a, b = cu[s], cu[s + 1]
+        sl = lambda t: None if t is None else dev(t[:, a:b].contiguous()[None])  # noqa: E731
+        ys, fss = mscan.scan_fwd(sl(p["u"]), sl(p["delta"]), dev(p["A_log"]), sl(p["B"]), sl(p["C"]), D=dev(p["D"]),
+                                 z=sl(p["z"]), delta_bias=dev(p["delta_bias"]),
+                                 initial_state=dev(p["initial_states"][s:s + 1].contiguous()),
+                                 return_final_state=True, nchunks=max(1, ln // 2048))
         assert torch.equal(ys[0].cpu(), y[:, a:b]), s
         assert torch.equal(fss[0].cpu(), fs[s]), s
 
