@@ -67,7 +67,7 @@ struct SArgs {
   float* hT;                // (batch, H, P, N) or null
   uint16_t* y;              // (batch, L, H, P)
   int64_t L;
-  int H, softplus, euler;
+  int H, S, softplus, euler;   // S: 64-channel slices per head (head dim 64 S)
 };
 
 template <int N>
@@ -163,20 +163,24 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   const int lane = tid & 63;
   const int l32 = lane & 31, h32 = lane >> 5;
   const int H = a.H;
-  // XCD-aware placement: workgroup ids are dealt round-robin over the 8 XCDs;
-  // give each XCD a contiguous range of (batch, head) items, so the heads of a
-  // batch row (which all read the same B and C) share an L2
+  const int HS = H * a.S;   // (head, 64-channel slice) items per batch row
+  // A head of dim 64 S is S independent slices of 64 channels sharing the
+  // head's decay, B and C; a workgroup owns one slice.  XCD-aware placement:
+  // workgroup ids are dealt round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of (batch, head, slice) items, so the heads of a batch row
+  // (which all read the same B and C) share an L2
   const int64_t nwg = gridDim.x;
   const int64_t bh = (nwg & 7) == 0 ? (int64_t)(blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int64_t b = bh / H;
-  const int h = (int)(bh % H);
+  const int64_t b = bh / HS;
+  const int hs = (int)(bh % HS);
+  const int h = hs / a.S;
   const int64_t Lq = a.L;
   const int64_t nchunk = (Lq + kQ - 1) / kQ;
 
-  const int64_t xs_t = (int64_t)H * kP;   // x/z/y token stride
-  const uint16_t* xb = a.x + b * Lq * xs_t + (int64_t)h * kP;
-  const uint16_t* zb = a.z ? a.z + b * Lq * xs_t + (int64_t)h * kP : nullptr;
-  uint16_t* yb = a.y + b * Lq * xs_t + (int64_t)h * kP;
+  const int64_t xs_t = (int64_t)HS * kP;   // x/z/y token stride (H heads of dim 64 S)
+  const uint16_t* xb = a.x + b * Lq * xs_t + (int64_t)hs * kP;
+  const uint16_t* zb = a.z ? a.z + b * Lq * xs_t + (int64_t)hs * kP : nullptr;
+  uint16_t* yb = a.y + b * Lq * xs_t + (int64_t)hs * kP;
   const uint16_t* Bb = a.B + b * Lq * N;
   const uint16_t* Cb = a.C + b * Lq * N;
   const uint16_t* dtb = a.dt + b * Lq * H + h;
@@ -434,7 +438,7 @@ hipError_t run_ssd(const SArgs& a, int64_t batch, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)ssd_fwd_kernel<N>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ssd_fwd_kernel<N>, dim3((unsigned)(batch * a.H)), dim3(kNT), lds, s, a);
+  hipLaunchKernelGGL(ssd_fwd_kernel<N>, dim3((unsigned)(batch * a.H * a.S)), dim3(kNT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -455,6 +459,7 @@ hipError_t launch_ssd(const SsdArgs& p, hipStream_t stream) {
   a.y = static_cast<uint16_t*>(p.y);
   a.L = p.seqlen;
   a.H = (int)p.nheads;
+  a.S = (int)(p.headdim / kP);
   a.softplus = p.softplus;
   a.euler = p.euler;
   return p.dstate == 128 ? run_ssd<128>(a, p.batch, stream) : run_ssd<64>(a, p.batch, stream);

@@ -227,6 +227,8 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, io=0) == EUNSUP                  # bf16 operands only
     assert ssd(lib, io=5) == EDTYPE
     assert ssd(lib, hd=32) == EUNSUP
+    assert ssd(lib, hd=96) == EUNSUP                 # head dims are multiples of 64
+    assert ssd(lib, hd=320) == EUNSUP
     assert ssd(lib, N=16) == EUNSUP
     assert ssd(lib, flags=8) == EUNSUP
     assert ssd(lib, batch=0) == ESHAPE

@@ -1,7 +1,7 @@
 """GPU parity of the multi-head SSM with a scalar decay per head (state-space-
 duality form, mamba_ssd_fwd, matrix cores) against the fp64 oracle: ragged
 lengths (partial last chunk), one-token and empty sequences, d_state 64 and
-128, gate / no gate, initial state, both input terms, softplus off; repeat
+128, head dims 64 to 256, gate / no gate, initial state, both input terms, softplus off; repeat
 runs are identical; a split at a chunk boundary resumes bit for bit and at any
 other token within tolerance; the full-size layer on sampled heads.
 
@@ -76,6 +76,34 @@ def test_ssd_vs_oracle(case):
     yr, fsr = ref(inp, sp, disc)
     check("y", y, yr)
     check("final_state", fs, fsr)
+
+
+@pytest.mark.parametrize("P,N,disc", [(128, 128, "zoh"), (128, 64, "euler"), (192, 64, "zoh"), (256, 128, "zoh")])
+def test_ssd_wide_heads_vs_oracle(P, N, disc):
+    """Head dims above 64: each head runs as P / 64 slices of 64 channels sharing its decay."""
+    b, L, H = 2, 150, 2
+    inp = ssd_inputs(b, L, H, P, N, seed=P + N, gated=True, initial_state=True)
+    say(f"head dim {P}, N {N}, {disc}")
+    y, fs = gpu(inp, True, disc)
+    yr, fsr = ref(inp, True, disc)
+    check("y", y, yr)
+    check("final_state", fs, fsr)
+
+
+def test_ssd_head_of_128_equals_two_heads_of_64():
+    """A head of dim 128 is two heads of dim 64 with the same dt, A, D: identical results bit for bit
+    (same memory layout; dt, A_log, D, dt_bias repeated per half)."""
+    b, L, H, P, N = 1, 200, 3, 128, 128
+    inp = ssd_inputs(b, L, H, P, N, seed=3, gated=True, initial_state=True)
+    y1, fs1 = gpu(inp)
+    two = dict(x=inp["x"].view(b, L, 2 * H, 64), z=inp["z"].view(b, L, 2 * H, 64),
+               dt=inp["dt"].repeat_interleave(2, dim=2).contiguous(), B=inp["B"], C=inp["C"],
+               A_log=inp["A_log"].repeat_interleave(2), D=inp["D"].repeat_interleave(2),
+               dt_bias=inp["dt_bias"].repeat_interleave(2),
+               initial_state=inp["initial_state"].view(b, 2 * H, 64, N))
+    y2, fs2 = gpu(two)
+    assert torch.equal(y1.view(torch.int16), y2.view(b, L, H, P).view(torch.int16))
+    assert torch.equal(fs1, fs2.view(b, H, P, N))
 
 
 def test_ssd_empty_sequence():
