@@ -17,16 +17,16 @@
 //   1. checkpoint pass: the forward recurrence (no readout) writes the state
 //      entering every 8-token sub-chunk to the workspace;
 //   2. gradient pass, 32-token tiles in reverse order.  A workgroup owns 64
-//      channels of one batch row (one per lane) and 4 waves; wave w holds
-//      states 4w..4w+3.  Per tile: stage Delta, u, dytil, B, C in LDS; then per
-//      8-token sub-chunk in reverse, rerun those 8 tokens from the sub-chunk's
-//      checkpoint keeping every state and decay in registers (and the readout
-//      partial sums), and sweep them backwards carrying Abar lam.  The
-//      readout, dDelta and du are partial over a wave's states and summed
-//      across waves through LDS at the end of the tile, where the pre-gate
-//      output gives dz; dB and dC are summed over the 64 lanes (channels) by a
-//      reduce-scatter in registers and written per channel group to the
-//      workspace;
+//      channels of one batch row and 8 waves (two per SIMD), two states per
+//      lane, laid out as in the forward kernel (below).  Per tile: stage
+//      Delta, u, dytil, B, C in LDS; then per 8-token sub-chunk in reverse,
+//      rerun those 8 tokens from the sub-chunk's checkpoint keeping every state
+//      and decay in registers (and the readout partial sums), and sweep them
+//      backwards carrying Abar lam.  The readout, dDelta and du are summed
+//      over a wave's four states in the wave and over wave pairs through LDS
+//      at the end of the tile, where the pre-gate output gives dz; dB and dC
+//      are summed over each half-wave's 32 channels by a reduce-scatter in
+//      registers and written per 32-channel group to the workspace;
 //   3. reductions of the per-group and per-row partials in a fixed order
 //      (deterministic results).
 #include <algorithm>
@@ -43,8 +43,9 @@ constexpr int kRow = kT + 4;     // LDS row of one channel (floats)
 constexpr int kG = kT / 4;       // 4-token groups per tile
 constexpr int kSub = 8;          // tokens per recompute sub-chunk
 constexpr int NP = 16;           // padded states
-constexpr int NPW = 4;           // states per lane
-constexpr int NT = 256;          // threads per workgroup
+constexpr int NPW = 2;           // states per lane
+constexpr int NT = 512;          // threads per workgroup (8 waves, two per SIMD)
+constexpr int kPiece = 4;        // tokens of a tile per staging thread (64 channels x 32 tokens / 512)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -97,46 +98,14 @@ __device__ __forceinline__ float row_pair_sum2(float a, float b) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum over the 64 lanes of a wave of 32 values held by every lane: a
-// reduce-scatter (each stage halves the values per lane and doubles the lanes
-// summed), then one all-reduce step.  Afterwards lanes 2i and 2i+1 hold the
-// total of value i.
-__device__ __forceinline__ float reduce64(const float (&v)[32], int lane) {
-  float w16[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) w16[i] = half_sum2(v[i], v[i + 16]);        // lanes l, l ^ 32
-  float w8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w8[i] = row_pair_sum2(w16[i], w16[i + 8]);   // lanes l, l ^ 16
-  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0;
+// Sum over the 32 lanes of each half of a wave of 8 values held by every lane:
+// a reduce-scatter (each stage halves the values per lane and doubles the
+// lanes summed), then an all-reduce over the last four lanes.  Afterwards
+// lanes 4i .. 4i+3 of each half hold that half's total of value i.
+__device__ __forceinline__ float reduce32_8(const float (&v)[8], int lane) {
   float w4[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {                                            // lanes l, l ^ 8
-    const float keep = b3 ? w8[i + 4] : w8[i];
-    const float send = b3 ? w8[i] : w8[i + 4];
-    w4[i] = keep + dpp_mov<kRowRor8>(send);
-  }
-  float w2[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {                                            // lanes l, l ^ 7
-    const float keep = b2 ? w4[i + 2] : w4[i];
-    const float send = b2 ? w4[i] : w4[i + 2];
-    w2[i] = keep + dpp_mov<kRowHalfMirror>(send);
-  }
-  const float keep = b1 ? w2[1] : w2[0];                                   // lanes l, l ^ 2
-  const float send = b1 ? w2[0] : w2[1];
-  const float r = keep + dpp_mov<kQuad2301>(send);
-  return r + dpp_mov<kQuad1032>(r);                                        // lanes l, l ^ 1
-}
-
-// The same for 16 values per lane: afterwards lanes 4i .. 4i+3 hold the total of value i.
-__device__ __forceinline__ float reduce64_16(const float (&v)[16], int lane) {
-  float w8[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w8[i] = half_sum2(v[i], v[i + 8]);          // lanes l, l ^ 32
-  float w4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w4[i] = row_pair_sum2(w8[i], w8[i + 4]);    // lanes l, l ^ 16
+  for (int i = 0; i < 4; ++i) w4[i] = row_pair_sum2(v[i], v[i + 4]);    // lanes l, l ^ 16
   const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
   float w2[2];
 #pragma unroll
@@ -156,11 +125,19 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
+// ---------------------------------------------------------------- layout
+// Both passes use the forward's two-states-per-lane layout: 8 waves (two per
+// SIMD) over 64 channels; wave w covers channels (w & 1) * 32 .. +31, and its
+// lanes l and l + 32 hold the same channel and different state pairs, states
+// (w >> 1) * 4 + (l >> 5) * 2 + {0, 1}.  Staging threads own 4-token pieces of
+// a tile: channel tid / 8, tokens 4 (tid % 8) .. +3.  B and C of a 4-token
+// group reach the lanes through DPP row broadcasts: lane 4j + kk of each row
+// holds (state j of the lane's pair, token kk).
+
 // ---------------------------------------------------------------- checkpoints
 template <typename IoT, bool kVec, bool kSp>
 __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   using IO = Io<IoT>;
-  using V8 = typename IO::V8;
   using V4 = typename IO::V4;
   constexpr int kEsz = (int)sizeof(IoT);
   __shared__ float dbuf[kCh * kRow];
@@ -171,11 +148,14 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;
+  const int chw = (w & 1) * 32 + (lane & 31);   // the lane's channel within the workgroup
+  const int nb = (w >> 1) * 4 + hf * 2;          // the lane's first state
   const int64_t wid = work_id(blockIdx.x, a.nwork);
   const int64_t cg = wid % a.chgroups;
   const int64_t b = wid / a.chgroups;
   const int64_t d0 = cg * kCh;
-  const int64_t d = d0 + lane;
+  const int64_t d = d0 + chw;
   const bool ch_ok = d < a.dim;
   const int64_t bd = b * a.dim + d;
   if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
@@ -183,7 +163,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   float A[NPW], iA[NPW], h[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    const int n = w * NPW + j;
+    const int n = nb + j;
     const bool valid = ch_ok && n < a.dstate;
     A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     iA[j] = valid ? 1.0f / A[j] : 0.0f;
@@ -199,43 +179,39 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
   const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
   const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, (int)((int64_t)a.dstate * a.seqlen * kEsz));
-  const int pc = tid / 4, pg = tid % 4;            // piece: channel, tokens 8 pg .. 8 pg + 7
+  const int pc = tid / 8, pg = tid % 8;            // piece: channel, tokens 4 pg .. 4 pg + 3
   const int bn = tid % NP, bg = (tid / NP) % kG;   // B piece (threads 0..127): state, 4-token group
   const int sel = lane & 15;
-  float* ck = a.ckpt + (b * a.nsub * NP + w * NPW) * a.dim + d;   // + (s8 * NP + j) * dim
+  const float* bl = bbuf + (sel & 3) * NP + nb + ((sel >> 2) & 1);   // + g * 4 * NP
+  float* ck = a.ckpt + (b * a.nsub * NP + nb) * a.dim + d;         // + (s8 * NP + j) * dim
   __syncthreads();
 
   // tile k's loads are issued while tile k-1 is scanned
-  auto load_tile = [&](int64_t tile, V8& rd, V8& ru, V4& rb) {
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    rd = IO::buf_load8(rs_d, off, kVec);
-    ru = IO::buf_load8(rs_u, off, kVec);
+  auto load_tile = [&](int64_t tile, V4& rd, V4& ru, V4& rb) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);
+    rd = IO::buf_load4(rs_d, off, kVec);
+    ru = IO::buf_load4(rs_u, off, kVec);
     if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
   };
-  V8 rd = IO::zero(), ru = IO::zero();
-  V4 rb{};
+  V4 rd{}, ru{}, rb{};
   load_tile(0, rd, ru, rb);
   for (int64_t k = 0; k < a.ntile; ++k) {
     const int64_t tile = k * kT;
     const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
-    const int nv = max(0, min(8, nv_tile - pg * 8));   // valid tokens of this thread's piece
-    float fd[8], fu[8];
+    const int nv = max(0, min(kPiece, nv_tile - pg * kPiece));   // valid tokens of this thread's piece
+    float fd[4], fu[4];
     IO::to_f32(rd, fd);
     IO::to_f32(ru, fu);
     const float bi = par[pc];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       const float x = fd[j] + bi;
       const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
       fd[j] = j < nv ? dl : 0.0f;   // tokens past the end: Delta = 0, u = 0 leave the state unchanged
       fu[j] = j < nv ? fu[j] : 0.0f;
     }
-    float* dp = dbuf + pc * kRow + pg * 8;
-    float* up = ubuf + pc * kRow + pg * 8;
-    reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-    reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-    reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-    reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
+    *reinterpret_cast<float4*>(dbuf + pc * kRow + pg * kPiece) = make_float4(fd[0], fd[1], fd[2], fd[3]);
+    *reinterpret_cast<float4*>(ubuf + pc * kRow + pg * kPiece) = make_float4(fu[0], fu[1], fu[2], fu[3]);
     if (w < 2) {
       const int nvb = max(0, min(4, nv_tile - bg * 4));
       float f[4];
@@ -254,9 +230,9 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
           for (int j = 0; j < NPW; ++j) ck[(s8 * NP + j) * a.dim] = h[j];
         }
       }
-      const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * g);
-      const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * g);
-      const float bq = bbuf[(g * 4 + (sel & 3)) * NP + w * NPW + (sel >> 2)];   // lane 4j+kk: state j, token kk
+      const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * g);
+      const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * g);
+      const float bq = bl[g * 4 * NP];   // lane 4j+kk: state j of the pair, token kk
       const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
       const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
       static_for<4>([&](auto kk_c) {
@@ -277,8 +253,8 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
 struct LdsB {
   static constexpr int kDU = kCh * kRow;            // Delta*log2e, u, dytil: one tile each
   static constexpr int kBC = kG * 4 * NP * 2;       // (B, C) pairs
-  static constexpr int kPart = 4 * kCh * kRow;      // per-wave partials over one tile: readout, dDelta, du
-  static constexpr int kHB = 4 * 4 * kCh * NPW;     // state entering each 8-token sub-chunk, per wave and lane
+  static constexpr int kPart = 4 * kCh * kRow;      // per wave pair partials over one tile: readout, dDelta, du
+  static constexpr int kHB = 4 * 8 * 64 * NPW;      // state entering each 8-token sub-chunk, per wave and lane
   static constexpr int kFloats = 3 * kDU + kBC + 3 * kPart + kHB + 2 * kCh;
 };
 static_assert(sizeof(float) * LdsB::kFloats <= 160 * 1024, "LDS of the gradient kernel");
@@ -286,7 +262,6 @@ static_assert(sizeof(float) * LdsB::kFloats <= 160 * 1024, "LDS of the gradient 
 template <typename IoT, bool kVec, bool kSp, bool kGate>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   using IO = Io<IoT>;
-  using V8 = typename IO::V8;
   using V4 = typename IO::V4;
   constexpr int kEsz = (int)sizeof(IoT);
   extern __shared__ float smem[];
@@ -297,17 +272,21 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float* party = bcs + LdsB::kBC;         // [4][64][kRow] readout partials
   float* part1 = party + LdsB::kPart;     // [4][64][kRow] dDelta partials
   float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
-  float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][4 waves][64 lanes][4 states]
+  float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][8 waves][64 lanes][2 states]
   float* par = hbuf + LdsB::kHB;          // [2][64] bias, D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5;
+  const int chw = (w & 1) * 32 + (lane & 31);   // the lane's channel within the workgroup
+  const int sp = w >> 1;                         // wave pair: states 4 sp .. 4 sp + 3
+  const int nb = sp * 4 + hf * 2;                // the lane's first state
   const int64_t wid = work_id(blockIdx.x, a.nwork);
   const int64_t cg = wid % a.chgroups;
   const int64_t b = wid / a.chgroups;
   const int64_t d0 = cg * kCh;
-  const int64_t d = d0 + lane;
+  const int64_t d = d0 + chw;
   const bool ch_ok = d < a.dim;
   const int64_t bd = b * a.dim + d;
   if (tid < kCh) {
@@ -320,7 +299,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float A[NPW], iA[NPW], g[NPW], X[NPW], Y[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    const int n = w * NPW + j;
+    const int n = nb + j;
     const bool valid = ch_ok && n < a.dstate;
     A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     iA[j] = valid ? 1.0f / A[j] : 0.0f;
@@ -352,12 +331,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   const __amdgpu_buffer_rsrc_t rs_dd = make_rsrc(gdd + row0, nrec_ch);
   const __amdgpu_buffer_rsrc_t rs_dz = make_rsrc(kGate ? gdz + row0 : gdu + row0, kGate ? nrec_ch : 0);
 
-  const int pc = tid / 4, pg = tid % 4;              // piece: channel, tokens 8 pg .. 8 pg + 7
-  const int bn = tid % NP, bg = (tid / NP) % kG;     // (B or C) piece: state, 4-token group
-  const bool isB = w < 2;                            // waves 0-1 stage B, 2-3 stage C
+  const int pc = tid / 8, pg = tid % 8;              // piece: channel, tokens 4 pg .. 4 pg + 3
+  const int bn = tid % NP, bg = (tid / NP) % kG;     // (B or C) piece (waves 0-3): state, 4-token group
+  const bool stageBC = w < 4;                        // wave-uniform, so the buffer descriptor below is too
+  const bool isB = w < 2;                            // waves 0-1 stage B, 2-3 C
   const int sel = lane & 15;
-  const float* bcl = bcs + ((sel & 3) * NP + w * NPW + (sel >> 2)) * 2;   // lane 4j+kk: state j, token kk
-  const float* ck = a.ckpt + (b * a.nsub * NP + w * NPW) * a.dim + d;    // + (s8 * NP + j) * dim
+  // lane 4j + kk of each row: (B, C) of token kk, state j of the lane's pair
+  const float* bcl = bcs + ((sel & 3) * NP + nb + ((sel >> 2) & 1)) * 2;
+  const float* ck = a.ckpt + (b * a.nsub * NP + nb) * a.dim + d;   // + (s8 * NP + j) * dim
+  const int yoff = 2 * hf;                           // half_sum2 results: tokens 2 hf, 2 hf + 1 of a group
+  // dB / dC partials over this wave's 32 channels: (batch, 32-channel group, state, token)
+  const int64_t g32 = cg * 2 + (w & 1);
   float dD_acc = 0.0f, db_acc = 0.0f;
   __syncthreads();
 
@@ -365,16 +349,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     const int64_t tile = k * kT;
     const int nv_tile = (int)min((int64_t)kT, a.seqlen - tile);
     const bool full = nv_tile == kT;
-    const int nv = max(0, min(8, nv_tile - pg * 8));   // valid tokens of this thread's piece
+    const int nv = max(0, min(kPiece, nv_tile - pg * kPiece));   // valid tokens of this thread's piece
 
     // ---- load and stage ----
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    const V8 rd = IO::buf_load8(rs_d, off, kVec);
-    const V8 ru = IO::buf_load8(rs_u, off, kVec);
-    const V8 rdy = IO::buf_load8(rs_dy, off, kVec);
-    V8 rz = IO::zero();
-    if constexpr (kGate) rz = IO::buf_load8(rs_z, off, kVec);
-    const V4 rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);
+    const V4 rd = IO::buf_load4(rs_d, off, kVec);
+    const V4 ru = IO::buf_load4(rs_u, off, kVec);
+    const V4 rdy = IO::buf_load4(rs_dy, off, kVec);
+    V4 rz{};
+    if constexpr (kGate) rz = IO::buf_load4(rs_z, off, kVec);
+    V4 rbc{};
+    if (stageBC) rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
     float hq[4][NPW];   // states entering the tile's sub-chunks (0 for sub-chunks past the end)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -385,16 +370,16 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     }
 
     // piece owners keep, for the end of the tile: u, dytil, dz / ytil and dDelta / d(pre-softplus)
-    float fu[8], dyt[8], gzf[8], sgx[8];
+    float fu[4], dyt[4], gzf[4], sgx[4];
     {
-      float fd[8], fdy[8], fz[8];
+      float fd[4], fdy[4], fz[4];
       IO::to_f32(rd, fd);
       IO::to_f32(ru, fu);
       IO::to_f32(rdy, fdy);
       IO::to_f32(rz, fz);
       const float bi = par[pc];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         const bool ok = j < nv;   // tokens past the end: Delta = 0, u = 0, dy = 0 change nothing
         const float xs = fd[j] + bi;
         const float dl = kSp ? softplus_log2e(xs) : xs * kLog2e;
@@ -412,24 +397,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         }
         dD_acc = fmaf(dyt[j], fu[j], dD_acc);
       }
-      float* dp = dbuf + pc * kRow + pg * 8;
-      float* up = ubuf + pc * kRow + pg * 8;
-      float* yp = ybuf + pc * kRow + pg * 8;
-      reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-      reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-      reinterpret_cast<float4*>(up)[0] = make_float4(fu[0], fu[1], fu[2], fu[3]);
-      reinterpret_cast<float4*>(up)[1] = make_float4(fu[4], fu[5], fu[6], fu[7]);
-      reinterpret_cast<float4*>(yp)[0] = make_float4(dyt[0], dyt[1], dyt[2], dyt[3]);
-      reinterpret_cast<float4*>(yp)[1] = make_float4(dyt[4], dyt[5], dyt[6], dyt[7]);
-      const int nvb = max(0, min(4, nv_tile - bg * 4));
-      float f[4];
-      IO::to_f32(rbc, f);
-      float* q = bcs + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
+      *reinterpret_cast<float4*>(dbuf + pc * kRow + pg * kPiece) = make_float4(fd[0], fd[1], fd[2], fd[3]);
+      *reinterpret_cast<float4*>(ubuf + pc * kRow + pg * kPiece) = make_float4(fu[0], fu[1], fu[2], fu[3]);
+      *reinterpret_cast<float4*>(ybuf + pc * kRow + pg * kPiece) = make_float4(dyt[0], dyt[1], dyt[2], dyt[3]);
+      if (stageBC) {
+        const int nvb = max(0, min(4, nv_tile - bg * 4));
+        float f[4];
+        IO::to_f32(rbc, f);
+        float* q = bcs + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+        for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+      }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<float4*>(hbuf + ((s * 4 + w) * kCh + lane) * NPW) = make_float4(hq[s][0], hq[s][1], hq[s][2], hq[s][3]);
+        *reinterpret_cast<float2*>(hbuf + ((s * 8 + w) * 64 + lane) * NPW) = make_float2(hq[s][0], hq[s][1]);
     }
     lds_barrier();
 
@@ -438,16 +419,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     //      then sweep it backwards ----
 #pragma unroll 1
     for (int s = 3; s >= 0; --s) {
-      float hb[NPW], hh[kSub][NPW], ha[kSub][NPW];
+      // per token and state: h_t, Abar, e = (Abar - 1) / A and B u, kept for the sweep
+      float hb[NPW], hh[kSub][NPW], ha[kSub][NPW], he[kSub][NPW], hbu[kSub][NPW];
       {
-        const float4 q = *reinterpret_cast<const float4*>(hbuf + ((s * 4 + w) * kCh + lane) * NPW);
-        hb[0] = q.x; hb[1] = q.y; hb[2] = q.z; hb[3] = q.w;
-        float h[NPW] = {hb[0], hb[1], hb[2], hb[3]};
+        const float2 q = *reinterpret_cast<const float2*>(hbuf + ((s * 8 + w) * 64 + lane) * NPW);
+        hb[0] = q.x; hb[1] = q.y;
+        float h[NPW] = {hb[0], hb[1]};
         static_for<2>([&](auto gq_c) {
           constexpr int gq = decltype(gq_c)::value;
           const int tg = 2 * s + gq;
-          const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * tg);
-          const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * tg);
+          const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * tg);
+          const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * tg);
           const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
           const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
           const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
@@ -457,16 +439,22 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             float acc = 0.0f;
             static_for<NPW>([&](auto j_c) {
               constexpr int j = decltype(j_c)::value;
+              constexpr int t = 4 * gq + kk;
               const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
-              const float sv = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk] * iA[j]);
-              h[j] = fmaf(av, h[j] + sv, -sv);
-              hh[4 * gq + kk][j] = h[j];
-              ha[4 * gq + kk][j] = av;
+              const float e = fmaf(av, iA[j], -iA[j]);                // (Abar - 1) / A, so Bbar = e B
+              const float bu = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk]);   // B u
+              h[j] = fmaf(av, h[j], e * bu);
+              hh[t][j] = h[j];
+              ha[t][j] = av;
+              he[t][j] = e;
+              hbu[t][j] = bu;
               acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
             });
             ys[kk] = acc;
           });
-          *reinterpret_cast<float4*>(party + (w * kCh + lane) * kRow + 4 * tg) = make_float4(ys[0], ys[1], ys[2], ys[3]);
+          // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over the wave's four states
+          *reinterpret_cast<float2*>(party + (sp * kCh + chw) * kRow + 4 * tg + yoff) =
+              make_float2(half_sum2(ys[0], ys[2]), half_sum2(ys[1], ys[3]));
         });
       }
       // Per (token, state), with l = lam_t, e = (Abar - 1) / A (so Bbar = e B) and
@@ -477,14 +465,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
       static_for<2>([&](auto gr_c) {
         constexpr int gq = 1 - decltype(gr_c)::value;   // the sub-chunk's two 4-token groups, later first
         const int tg = 2 * s + gq;
-        const float4 dv = *reinterpret_cast<const float4*>(dbuf + lane * kRow + 4 * tg);
-        const float4 uv = *reinterpret_cast<const float4*>(ubuf + lane * kRow + 4 * tg);
-        const float4 yv = *reinterpret_cast<const float4*>(ybuf + lane * kRow + 4 * tg);
+        const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * tg);
+        const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * tg);
+        const float4 yv = *reinterpret_cast<const float4*>(ybuf + chw * kRow + 4 * tg);
         const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
         const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
         const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
         const float dys[4] = {yv.x, yv.y, yv.z, yv.w};
-        float dDp[4], dup[4], dBv[16], dCv[16];   // dBv, dCv: value j*4 + kk
+        float dDp[4], dup[4], dBv[8], dCv[8];   // dBv, dCv: value j*4 + kk
         static_for<4>([&](auto kr_c) {
           constexpr int kk = 3 - decltype(kr_c)::value;   // tokens in reverse
           constexpr int t = 4 * gq + kk;                  // token within the sub-chunk
@@ -497,11 +485,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             const float av = ha[t][j];
             const float l = dpp_bcast_fmac<src>(g[j], bq.y, dys[kk]);   // lam_t = dytil C + Abar lam_{t+1}
             g[j] = av * l;                                              // Abar_t lam_t, for token t-1
-            const float bu = dpp_bcast_mul<src>(bq.x, uus[kk]);         // B u
+            const float bu = hbu[t][j];                                 // B u
             const float q = fmaf(A[j], hp, bu);
             dD_p = fmaf(g[j], q, dD_p);
             X[j] = fmaf(Delta * g[j], q, X[j]);
-            const float le = l * fmaf(av, iA[j], -iA[j]);               // l e
+            const float le = l * he[t][j];                              // l e
             Y[j] = fmaf(le, bu, Y[j]);
             du_p = dpp_bcast_fmac<src>(du_p, bq.x, le);
             dBv[j * 4 + kk] = le * uus[kk];
@@ -510,15 +498,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
           dDp[kk] = dD_p;
           dup[kk] = du_p;
         });
-        *reinterpret_cast<float4*>(part1 + (w * kCh + lane) * kRow + 4 * tg) = make_float4(dDp[0], dDp[1], dDp[2], dDp[3]);
-        *reinterpret_cast<float4*>(part2 + (w * kCh + lane) * kRow + 4 * tg) = make_float4(dup[0], dup[1], dup[2], dup[3]);
-        // sums over the 64 channels: lanes 4i .. 4i+3 hold value i = j*4 + kk
-        const float rB = reduce64_16(dBv, lane);
-        const float rC = reduce64_16(dCv, lane);
-        const int i = lane >> 2;
+        *reinterpret_cast<float2*>(part1 + (sp * kCh + chw) * kRow + 4 * tg + yoff) =
+            make_float2(half_sum2(dDp[0], dDp[2]), half_sum2(dDp[1], dDp[3]));
+        *reinterpret_cast<float2*>(part2 + (sp * kCh + chw) * kRow + 4 * tg + yoff) =
+            make_float2(half_sum2(dup[0], dup[2]), half_sum2(dup[1], dup[3]));
+        // sums over the half's 32 channels: lanes 4i .. 4i+3 of each half hold value i = j*4 + kk
+        const float rB = reduce32_8(dBv, lane);
+        const float rC = reduce32_8(dCv, lane);
+        const int i = (lane & 31) >> 2;
         const int64_t tt = tile + 4 * tg + (i & 3);
         if ((lane & 3) == 0 && tt < a.seqlen) {
-          const int64_t o = ((b * a.chgroups + cg) * NP + w * NPW + (i >> 2)) * a.seqlen + tt;
+          const int64_t o = ((b * 2 * a.chgroups + g32) * NP + nb + (i >> 2)) * a.seqlen + tt;
           a.wsB[o] = rB;
           a.wsC[o] = rC;
         }
@@ -532,40 +522,36 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     // after the next tile's first barrier)
     {
       const float Dd = par[kCh + pc];
-      float sy[8], sd[8], su[8];
+      float sy[4], sd[4], su[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         sy[j] = 0.0f;
         sd[j] = 0.0f;
         su[j] = 0.0f;
       }
 #pragma unroll
       for (int s2 = 0; s2 < 4; ++s2) {
-        const float4* q0 = reinterpret_cast<const float4*>(party + (s2 * kCh + pc) * kRow + pg * 8);
-        const float4* q1 = reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * 8);
-        const float4* q2 = reinterpret_cast<const float4*>(part2 + (s2 * kCh + pc) * kRow + pg * 8);
-        const float4 y0 = q0[0], y1 = q0[1], a0 = q1[0], a1 = q1[1], c0 = q2[0], c1 = q2[1];
+        const float4 y0 = *reinterpret_cast<const float4*>(party + (s2 * kCh + pc) * kRow + pg * kPiece);
+        const float4 a0 = *reinterpret_cast<const float4*>(part1 + (s2 * kCh + pc) * kRow + pg * kPiece);
+        const float4 c0 = *reinterpret_cast<const float4*>(part2 + (s2 * kCh + pc) * kRow + pg * kPiece);
         sy[0] += y0.x; sy[1] += y0.y; sy[2] += y0.z; sy[3] += y0.w;
-        sy[4] += y1.x; sy[5] += y1.y; sy[6] += y1.z; sy[7] += y1.w;
         sd[0] += a0.x; sd[1] += a0.y; sd[2] += a0.z; sd[3] += a0.w;
-        sd[4] += a1.x; sd[5] += a1.y; sd[6] += a1.z; sd[7] += a1.w;
         su[0] += c0.x; su[1] += c0.y; su[2] += c0.z; su[3] += c0.w;
-        su[4] += c1.x; su[5] += c1.y; su[6] += c1.z; su[7] += c1.w;
       }
-      float dzv[8], ddv[8], duv[8];
+      float dzv[4], ddv[4], duv[4];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 4; ++j) {
         dzv[j] = gzf[j] * fmaf(Dd, fu[j], sy[j]);   // ytil = C h + D u
         ddv[j] = sd[j] * sgx[j];
         duv[j] = fmaf(dyt[j], Dd, su[j]);
         db_acc += (j < nv) ? ddv[j] : 0.0f;
       }
       if (full) {
-        if constexpr (kGate) IO::buf_store8(rs_dz, off, IO::from_f32(dzv), kVec);
-        IO::buf_store8(rs_dd, off, IO::from_f32(ddv), kVec);
-        IO::buf_store8(rs_du, off, IO::from_f32(duv), kVec);
+        if constexpr (kGate) IO::buf_store4(rs_dz, off, IO::from_f32(dzv), kVec);
+        IO::buf_store4(rs_dd, off, IO::from_f32(ddv), kVec);
+        IO::buf_store4(rs_du, off, IO::from_f32(duv), kVec);
       } else if (d0 + pc < a.dim) {
-        const int64_t o = row0 + (int64_t)pc * a.seqlen + tile + pg * 8;
+        const int64_t o = row0 + (int64_t)pc * a.seqlen + tile + pg * kPiece;
         if constexpr (kGate) IO::store_n(gdz + o, IO::from_f32(dzv), nv);
         IO::store_n(gdd + o, IO::from_f32(ddv), nv);
         IO::store_n(gdu + o, IO::from_f32(duv), nv);
@@ -577,15 +563,18 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   if (ch_ok) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-      const int n = w * NPW + j;
+      const int n = nb + j;
       a.wsA[bd * NP + n] = X[j] - Y[j];   // dA * dA/dA_log
       if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
     }
   }
-  dD_acc += __shfl_xor(dD_acc, 1, 4);
-  dD_acc += __shfl_xor(dD_acc, 2, 4);
-  db_acc += __shfl_xor(db_acc, 1, 4);
-  db_acc += __shfl_xor(db_acc, 2, 4);
+  // the 8 piece threads of a channel
+  dD_acc += __shfl_xor(dD_acc, 1, 8);
+  dD_acc += __shfl_xor(dD_acc, 2, 8);
+  dD_acc += __shfl_xor(dD_acc, 4, 8);
+  db_acc += __shfl_xor(db_acc, 1, 8);
+  db_acc += __shfl_xor(db_acc, 2, 8);
+  db_acc += __shfl_xor(db_acc, 4, 8);
   if (pg == 0 && d0 + pc < a.dim) {
     a.wsD[b * a.dim + d0 + pc] = dD_acc;
     a.wsBias[b * a.dim + d0 + pc] = db_acc;
@@ -604,7 +593,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int64_t r = i % ((int64_t)dstate * seqlen);
   const int64_t n = r / seqlen, t = r % seqlen;
   float sb = 0.0f, sc = 0.0f;
-  for (int64_t c = 0; c < chgroups; ++c) {
+  for (int64_t c = 0; c < chgroups; ++c) {   // groups of 32 channels
     const int64_t o = ((b * chgroups + c) * NP + n) * seqlen + t;
     sb += wsB[o];
     sc += wsC[o];
@@ -699,7 +688,8 @@ hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
 
   const int64_t nbc = a.batch * a.dstate * a.seqlen;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel<IoT>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, k.wsB, k.wsC,
-                     static_cast<IoT*>(a.dB), static_cast<IoT*>(a.dC), a.batch, p.chgroups, (int)a.dstate, a.seqlen);
+                     static_cast<IoT*>(a.dB), static_cast<IoT*>(a.dC), a.batch, 2 * p.chgroups, (int)a.dstate,
+                     a.seqlen);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t np = std::max<int64_t>(a.dim * a.dstate, a.dim);
@@ -717,10 +707,10 @@ void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* p) {
   size_t off = 0;
   p->off_ckpt = off;
   off += align256(sizeof(float) * (size_t)(batch * p->nsub * NP * dim));
-  p->off_dB = off;
-  off += align256(sizeof(float) * (size_t)(batch * p->chgroups * NP * seqlen));
+  p->off_dB = off;   // partial sums per 32-channel group
+  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * NP * seqlen));
   p->off_dC = off;
-  off += align256(sizeof(float) * (size_t)(batch * p->chgroups * NP * seqlen));
+  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * NP * seqlen));
   p->off_dA = off;
   off += align256(sizeof(float) * (size_t)(batch * dim * NP));
   p->off_dD = off;
