@@ -52,7 +52,7 @@ def _bind(path: str):
     lib.oracle_ssd_fwd.argtypes = [P] * 11 + [I64] * 5 + [ctypes.c_int] * 3
     lib.oracle_scan_step.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P] + [I64] * 3 + [ctypes.c_int]
     lib.oracle_scan_bwd.restype = ctypes.c_int
-    lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
+    lib.oracle_scan_bwd.argtypes = [P] * 20 + [I64] * 4 + [ctypes.c_int] * 3
     lib.oracle_conv1d_fwd.restype = ctypes.c_int
     lib.oracle_conv1d_fwd.argtypes = [P] * 6 + [I64] * 4 + [ctypes.c_int, ctypes.c_int]
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -227,9 +227,10 @@ def scan_step(state, x, dt, A_log, B, C, D=None, z=None, dt_bias=None, dt_softpl
 
 
 def scan_bwd(u, delta, A_log, B, C, dy, D=None, z=None, delta_bias=None, initial_state=None,
-             d_final_state=None, delta_softplus: bool = True, nthreads: int = 0, _lib_override=None) -> dict:
-    """Gradients of the selective-scan forward in fp64, given dL/dy (and optionally
-    dL/d final_state).  Returns a dict with du, ddelta, dA_log, dB, dC (always) and dD,
+             d_final_state=None, delta_softplus: bool = True, nthreads: int = 0, _lib_override=None,
+             discretization: str = "zoh") -> dict:
+    """Gradients of the selective-scan forward in fp64 (discretization "zoh", or "euler" for
+    Bbar u = Delta B u), given dL/dy (and optionally dL/d final_state).  Returns a dict with du, ddelta, dA_log, dB, dC (always) and dD,
     dz, ddelta_bias, d_initial_state (when D, z, delta_bias, initial_state are given)."""
     u = _f64(u)
     if u.ndim != 3:
@@ -256,7 +257,8 @@ def scan_bwd(u, delta, A_log, B, C, dy, D=None, z=None, delta_bias=None, initial
         _ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
         _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]),
         _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]), _ptr(g["ddelta_bias"]),
-        _ptr(g["d_initial_state"]), batch, dim, dstate, L, int(bool(delta_softplus)), int(nthreads))
+        _ptr(g["d_initial_state"]), batch, dim, dstate, L, int(bool(delta_softplus)), _euler(discretization),
+        int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle_scan_bwd returned {rc}")
     return g

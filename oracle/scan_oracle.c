@@ -306,6 +306,10 @@ int oracle_max_threads(void) {
  *   ddelta_t = dDelta_t sigma(delta_t + bias)       (dDelta_t without softplus)
  *   dbias   += ddelta_t;  dD += dytil_t u_t;  d(initial state) = Abar_0 lam_0
  *
+ * With the Euler input term (euler != 0: Bbar = Delta B, the pages' simplified
+ * form) the terms that differ are dB_t[n] += lam u Delta, Bbar = Delta B in du,
+ * dDelta_t = sum_n lam (A Abar h_{t-1} + B u) and dA[n] += lam Delta Abar h_{t-1}.
+ *
  * Outputs (float64, row-major like the inputs): du, ddelta, dz (batch, dim, L);
  * dB, dC (batch, dstate, L); dA_log (dim, dstate); dD, ddelta_bias (dim);
  * d_initial_state (batch, dim, dstate).  dz, dD, ddelta_bias and
@@ -322,7 +326,7 @@ int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, c
                     const double* initial_state, const double* dy, const double* d_final_state,
                     double* du, double* ddelta, double* dA_log, double* dB, double* dC, double* dD,
                     double* dz, double* ddelta_bias, double* d_initial_state, int64_t batch, int64_t dim,
-                    int64_t dstate, int64_t seqlen, int delta_softplus, int nthreads) {
+                    int64_t dstate, int64_t seqlen, int delta_softplus, int euler, int nthreads) {
   if (!u || !delta || !A_log || !B || !C || !dy || !du || !ddelta || !dA_log || !dB || !dC) return 1;
   if (batch < 0 || dim < 0 || dstate < 1 || seqlen < 0) return 2;
 #ifdef _OPENMP
@@ -378,7 +382,7 @@ int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, c
         for (int64_t n = 0; n < N; ++n) {
           const double dA = Delta * A[n];
           const double Bn = B[bcrow + n * L + t];
-          const double Bbar = (A[n] != 0.0) ? expm1(dA) / A[n] * Bn : Delta * Bn;
+          const double Bbar = euler ? Delta * Bn : ((A[n] != 0.0) ? expm1(dA) / A[n] * Bn : Delta * Bn);
           const double hn = exp(dA) * H[t * N + n] + Bbar * u[row + t];
           H[(t + 1) * N + n] = hn;
           acc += C[bcrow + n * L + t] * hn;
@@ -408,11 +412,16 @@ int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, c
           /* lam currently holds Abar_{t+1} lam_{t+1} (or dL/d final state) */
           const double l = lam[n] + dyt * Cn;
           pC[n * L + t] += dyt * H[(t + 1) * N + n];
-          const double bq = (A[n] != 0.0) ? em1 / A[n] : Delta;     /* Bbar / B */
+          /* Bbar / B and its derivative in A: (e^{Delta A} - 1) / A for the zero-order hold, Delta
+             (independent of A) for the Euler input term */
+          const double bq = euler ? Delta : ((A[n] != 0.0) ? em1 / A[n] : Delta);     /* Bbar / B */
           pB[n * L + t] += l * ut * bq;
           dut += l * bq * Bn;
-          dDelta += l * Abar * (A[n] * hprev + Bn * ut);
-          const double dbq = (A[n] != 0.0) ? (Delta * Abar * A[n] - em1) / (A[n] * A[n]) : 0.5 * Delta * Delta;
+          if (euler)
+            dDelta += l * (Abar * A[n] * hprev + Bn * ut);   /* dh/dDelta = A Abar h_{t-1} + B u */
+          else
+            dDelta += l * Abar * (A[n] * hprev + Bn * ut);
+          const double dbq = euler ? 0.0 : ((A[n] != 0.0) ? (Delta * Abar * A[n] - em1) / (A[n] * A[n]) : 0.5 * Delta * Delta);
           dAn[n] += l * (Delta * Abar * hprev + ut * Bn * dbq);
           lam[n] = Abar * l;
         }

@@ -12,7 +12,9 @@ The backward oracle is checked against things other than itself:
   readout-side gradient is zero; with C = 0 and D = 0 the output is zero and
   so are dz, du and ddelta;
 * planted mistakes in copies of the backward code, each of which must fail
-  one of the pins above.
+  one of the pins above;
+* the same finite-difference pins for the Euler input term, with planted
+  mistakes in its branch.
 """
 import numpy as np
 import pytest
@@ -37,15 +39,15 @@ def problem(b, d, n, L, gated=True, hasD=True, hasbias=True, h0=True, dfs=True, 
     return p, dy, dfs_
 
 
-def loss(o, p, dy, dfs, softplus):
-    y, fs = o.scan_fwd(**p, delta_softplus=softplus)
+def loss(o, p, dy, dfs, softplus, disc="zoh"):
+    y, fs = o.scan_fwd(**p, delta_softplus=softplus, discretization=disc)
     out = float((y * dy).sum())
     if dfs is not None:
         out += float((fs * dfs).sum())
     return out
 
 
-def fd_grads(o, p, dy, dfs, softplus, eps=1e-6):
+def fd_grads(o, p, dy, dfs, softplus, eps=1e-6, disc="zoh"):
     g = {}
     for name, key in NAMES:
         arr = p[name]
@@ -57,25 +59,25 @@ def fd_grads(o, p, dy, dfs, softplus, eps=1e-6):
             a1 = arr.copy()
             a1[idx] += eps
             pp[name] = a1
-            lp = loss(o, pp, dy, dfs, softplus)
+            lp = loss(o, pp, dy, dfs, softplus, disc)
             a2 = arr.copy()
             a2[idx] -= eps
             pp[name] = a2
-            lm = loss(o, pp, dy, dfs, softplus)
+            lm = loss(o, pp, dy, dfs, softplus, disc)
             fd[idx] = (lp - lm) / (2 * eps)
         g[key] = fd
     return g
 
 
-def bwd(o, p, dy, dfs, softplus):
+def bwd(o, p, dy, dfs, softplus, disc="zoh"):
     return o.scan_bwd(p["u"], p["delta"], p["A_log"], p["B"], p["C"], dy, D=p["D"], z=p["z"],
                       delta_bias=p["delta_bias"], initial_state=p["initial_state"], d_final_state=dfs,
-                      delta_softplus=softplus)
+                      delta_softplus=softplus, discretization=disc)
 
 
-def check_fd(o, p, dy, dfs, softplus, tol=1e-7):
-    g = bwd(o, p, dy, dfs, softplus)
-    ref = fd_grads(o, p, dy, dfs, softplus)
+def check_fd(o, p, dy, dfs, softplus, tol=1e-7, disc="zoh"):
+    g = bwd(o, p, dy, dfs, softplus, disc)
+    ref = fd_grads(o, p, dy, dfs, softplus, disc=disc)
     for key, fd in ref.items():
         err = np.abs(g[key] - fd).max() / max(np.abs(fd).max(), 1e-12)
         assert err < tol, (key, err)
@@ -100,6 +102,26 @@ def test_bwd_matches_finite_differences(case):
         p["delta"] = np.abs(p["delta"]) * 0.5 + 0.01   # a positive step without softplus
         p["delta_bias"] = None if p["delta_bias"] is None else np.abs(p["delta_bias"]) * 0.1
     check_fd(oracle, p, dy, dfs_, sp)
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}" + ("g" if c[4] else "")
+                                                + ("" if c[9] else "-nosp") for c in CASES[:4]])
+def test_bwd_euler_matches_finite_differences(case):
+    """The Euler input term (Bbar u = Delta B u): every gradient against finite differences of the
+    Euler forward oracle (itself pinned to the zero-order hold to O(Delta^2))."""
+    b, d, n, L, gated, hasD, hasbias, h0, dfs, sp = case
+    p, dy, dfs_ = problem(b, d, n, L, gated, hasD, hasbias, h0, dfs, seed=L + 10 * n + 1)
+    if not sp:
+        p["delta"] = np.abs(p["delta"]) * 0.5 + 0.01
+        p["delta_bias"] = None if p["delta_bias"] is None else np.abs(p["delta_bias"]) * 0.1
+    check_fd(oracle, p, dy, dfs_, sp, disc="euler")
+
+
+def test_bwd_euler_differs_from_zoh():
+    p, dy, dfs = problem(2, 3, 4, 9, seed=12)
+    ge, gz = bwd(oracle, p, dy, dfs, True, "euler"), bwd(oracle, p, dy, dfs, True, "zoh")
+    for k in ("du", "ddelta", "dA_log", "dB", "dz"):
+        assert np.abs(ge[k] - gz[k]).max() > 1e-6, k
 
 
 def test_bwd_adjoint_identity():
@@ -163,6 +185,23 @@ BWD_MUTANTS = [
     ("dA_missing_input_term", "dAn[n] += l * (Delta * Abar * hprev + ut * Bn * dbq);",
      "dAn[n] += l * (Delta * Abar * hprev);"),
 ]
+# planted mistakes in the Euler branch, caught by the Euler finite differences
+BWD_EULER_MUTANTS = [
+    ("euler_dDelta_zoh_form", "dDelta += l * (Abar * A[n] * hprev + Bn * ut);",
+     "dDelta += l * Abar * (A[n] * hprev + Bn * ut) + 0.0;"),
+    ("euler_bbar_zoh", "const double bq = euler ? Delta : ", "const double bq = euler ? em1 / A[n] : "),
+    ("euler_dA_input_term", "const double dbq = euler ? 0.0 : ", "const double dbq = euler ? 0.5 * Delta * Delta : "),
+]
+
+
+@pytest.mark.parametrize("name,old,new", BWD_EULER_MUTANTS, ids=[m[0] for m in BWD_EULER_MUTANTS])
+def test_bwd_euler_planted_mistake_is_caught(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) == 1, name
+    var = oracle.build_variant(src.replace(old, new), str(tmp_path), "me_" + name)
+    p, dy, dfs = problem(2, 3, 4, 9, seed=4)
+    with pytest.raises(AssertionError):
+        check_fd(var, p, dy, dfs, True, disc="euler")
 
 
 @pytest.mark.parametrize("name,old,new", BWD_MUTANTS, ids=[m[0] for m in BWD_MUTANTS])
