@@ -204,7 +204,8 @@ def bench_bwd(args, c) -> int:
 
     def step():
         return mscan.scan_bwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], dyd, D=a["D"], z=a["z"],
-                              delta_bias=a["delta_bias"], workspace=ws, stream=stream)
+                              delta_bias=a["delta_bias"], workspace=ws, stream=stream,
+                              discretization=args.discretization)
 
     for _ in range(args.warmup):
         g = step()
@@ -237,9 +238,9 @@ def bench_bwd(args, c) -> int:
         gs = mscan.scan_bwd(*(t.contiguous().to(dev) for t in (sub["u"], sub["delta"], sub["A_log"], sub["B"],
                                                                sub["C"], dys)),
                             D=sub["D"].to(dev), z=None if sub["z"] is None else sub["z"].contiguous().to(dev),
-                            delta_bias=sub["delta_bias"].to(dev))
+                            delta_bias=sub["delta_bias"].to(dev), discretization=args.discretization)
         r = oracle.scan_bwd(sub["u"], sub["delta"], sub["A_log"], sub["B"], sub["C"], dys, D=sub["D"], z=sub["z"],
-                            delta_bias=sub["delta_bias"])
+                            delta_bias=sub["delta_bias"], discretization=args.discretization)
         parity = {k: max_rel_err(gs[k].float().cpu(), r[k]) for k in ("du", "ddelta", "dA_log", "dB", "dC", "dD")}
         parity["tol"] = c.tol
         parity["sample"] = "batch row 0, channels 0-63, full length"
@@ -252,7 +253,7 @@ def bench_bwd(args, c) -> int:
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{c.name} selective-scan backward: batch {b}, d_inner {d}, d_state {n}, L {L}, "
-                               f"{c.io} io, fp32 state, {'gated' if c.gated else 'ungated'}",
+                               f"{c.io} io, fp32 state, {'gated' if c.gated else 'ungated'}, {args.discretization}",
                    "batch": b, "d_inner": d, "d_state": n, "seqlen": L},
         "kernel_ms": round(launch_ms, 4),
         "roofline": {"bound": "alu", "achieved": round(achieved, 3), "peak": round(VALU_SLOTS_PEAK / 1e12, 3),

@@ -247,8 +247,7 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *   workspace        at least mamba_scan_bwd_workspace_size(...) bytes, 256-byte aligned:
  *                    the state entering every 8-token sub-chunk (batch x ceil(seqlen/8) x 16 x
  *                    dim fp32) and per-channel-group / per-row partial sums
- *   flags            MAMBA_SCAN_FLAG_SOFTPLUS or 0; the backward pass is built for the
- *                    zero-order hold only (MAMBA_SCAN_FLAG_EULER returns MAMBA_SCAN_ERR_UNSUPPORTED)
+ *   flags            as for mamba_scan_fwd: MAMBA_SCAN_FLAG_SOFTPLUS, MAMBA_SCAN_FLAG_EULER
  * Sizes and limits as for mamba_scan_fwd, except 1 <= dstate <= 16
  * (MAMBA_SCAN_MAX_DSTATE_BWD).  Sums over channels (dB, dC) and
  * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so

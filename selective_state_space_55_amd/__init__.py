@@ -379,7 +379,7 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
              dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
              d_final_state: Optional[torch.Tensor] = None, delta_softplus: bool = True, *,
-             workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+             workspace: Optional[torch.Tensor] = None, discretization: str = "zoh", stream=None) -> dict:
     """Selective-scan backward.  Inputs as in scan_fwd plus dy (batch, dim, L) in the io dtype and
     d_final_state (batch, dim, dstate) float32.  Returns a dict of gradients: du, ddelta, dz, dB, dC in
     the io dtype; dA_log, dD, ddelta_bias, d_initial_state in float32 (dD, dz, ddelta_bias and
@@ -429,7 +429,7 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
                             _ptr(delta_bias), _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(g["du"]),
                             _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["d_initial_state"]), batch, dim, dstate,
-                            L, io, int(bool(delta_softplus)), ws_ptr, ws_bytes, _stream(dev, stream))
+                            L, io, _flags(delta_softplus, discretization), ws_ptr, ws_bytes, _stream(dev, stream))
     _check("mamba_scan_bwd", rc)
     return g
 

@@ -245,7 +245,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
                    size_t workspace_bytes, void* stream) {
   int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
-  if (flags & ~MAMBA_SCAN_FLAG_SOFTPLUS) return MAMBA_SCAN_ERR_UNSUPPORTED;   // zero-order hold only
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (dstate > MAMBA_SCAN_MAX_DSTATE_BWD) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!A_log || !dA_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!u || !delta || !B || !C || !dy || !du || !ddelta || !dB || !dC)) return MAMBA_SCAN_ERR_NULL;
@@ -270,6 +270,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
   a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
   a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
   a.workspace = workspace;
   hipError_t e = mscan::launch_bwd(a, plan, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;

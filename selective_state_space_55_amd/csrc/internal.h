@@ -133,6 +133,7 @@ struct BwdArgs {
   int64_t batch, dim, dstate, seqlen;
   int io_bf16;
   int softplus;
+  int euler;          // Bbar = Delta B (Euler) instead of the zero-order hold
   void* workspace;
 };
 

@@ -135,7 +135,8 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
 // holds (state j of the lane's pair, token kk).
 
 // ---------------------------------------------------------------- checkpoints
-template <typename IoT, bool kVec, bool kSp>
+// kEuler: the Euler input term, h = Abar h + Delta B u (u is staged as Delta u)
+template <typename IoT, bool kVec, bool kSp, bool kEuler>
 __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -209,6 +210,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
       const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
       fd[j] = j < nv ? dl : 0.0f;   // tokens past the end: Delta = 0, u = 0 leave the state unchanged
       fu[j] = j < nv ? fu[j] : 0.0f;
+      if constexpr (kEuler) fu[j] *= fd[j] * kLn2;   // Delta u
     }
     *reinterpret_cast<float4*>(dbuf + pc * kRow + pg * kPiece) = make_float4(fd[0], fd[1], fd[2], fd[3]);
     *reinterpret_cast<float4*>(ubuf + pc * kRow + pg * kPiece) = make_float4(fu[0], fu[1], fu[2], fu[3]);
@@ -240,8 +242,12 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
         static_for<NPW>([&](auto j_c) {
           constexpr int j = decltype(j_c)::value;
           const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
-          const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk] * iA[j]);
-          h[j] = fmaf(av, h[j] + sv, -sv);
+          if constexpr (kEuler) {
+            h[j] = fmaf(av, h[j], dpp_bcast_mul<4 * j + kk>(bq, uus[kk]));   // Abar h + B (Delta u)
+          } else {
+            const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk] * iA[j]);
+            h[j] = fmaf(av, h[j] + sv, -sv);
+          }
         });
       });
     }
@@ -259,7 +265,7 @@ struct LdsB {
 };
 static_assert(sizeof(float) * LdsB::kFloats <= 160 * 1024, "LDS of the gradient kernel");
 
-template <typename IoT, bool kVec, bool kSp, bool kGate>
+template <typename IoT, bool kVec, bool kSp, bool kGate, bool kEuler>
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -441,7 +447,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
               constexpr int j = decltype(j_c)::value;
               constexpr int t = 4 * gq + kk;
               const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
-              const float e = fmaf(av, iA[j], -iA[j]);                // (Abar - 1) / A, so Bbar = e B
+              // Bbar = e B: e = (Abar - 1) / A (zero-order hold) or Delta (Euler)
+              const float e = kEuler ? dls[kk] * kLn2 : fmaf(av, iA[j], -iA[j]);
               const float bu = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk]);   // B u
               h[j] = fmaf(av, h[j], e * bu);
               hh[t][j] = h[j];
@@ -486,11 +493,17 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             const float l = dpp_bcast_fmac<src>(g[j], bq.y, dys[kk]);   // lam_t = dytil C + Abar lam_{t+1}
             g[j] = av * l;                                              // Abar_t lam_t, for token t-1
             const float bu = hbu[t][j];                                 // B u
-            const float q = fmaf(A[j], hp, bu);
-            dD_p = fmaf(g[j], q, dD_p);
-            X[j] = fmaf(Delta * g[j], q, X[j]);
             const float le = l * he[t][j];                              // l e
-            Y[j] = fmaf(le, bu, Y[j]);
+            if constexpr (kEuler) {
+              // dh_t/dDelta = A Abar h_{t-1} + B u, dh_t/dA = Delta Abar h_{t-1}: dA_log = A X
+              dD_p = fmaf(g[j] * A[j], hp, fmaf(l, bu, dD_p));
+              X[j] = fmaf(Delta * g[j], hp, X[j]);
+            } else {
+              const float q = fmaf(A[j], hp, bu);
+              dD_p = fmaf(g[j], q, dD_p);
+              X[j] = fmaf(Delta * g[j], q, X[j]);
+              Y[j] = fmaf(le, bu, Y[j]);
+            }
             du_p = dpp_bcast_fmac<src>(du_p, bq.x, le);
             dBv[j * 4 + kk] = le * uus[kk];
             dCv[j * 4 + kk] = dys[kk] * hh[t][j];
@@ -564,7 +577,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
       const int n = nb + j;
-      a.wsA[bd * NP + n] = X[j] - Y[j];   // dA * dA/dA_log
+      a.wsA[bd * NP + n] = kEuler ? A[j] * X[j] : X[j] - Y[j];   // dA * dA/dA_log
       if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
     }
   }
@@ -639,6 +652,28 @@ __global__ __launch_bounds__(256) void bwd_empty_kernel(float* dA_log, float* dD
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename IoT>
+auto pick_ckpt(bool vec, bool sp, bool eu) {
+  if (vec) {
+    if (sp) return eu ? bwd_ckpt_kernel<IoT, true, true, true> : bwd_ckpt_kernel<IoT, true, true, false>;
+    return eu ? bwd_ckpt_kernel<IoT, true, false, true> : bwd_ckpt_kernel<IoT, true, false, false>;
+  }
+  if (sp) return eu ? bwd_ckpt_kernel<IoT, false, true, true> : bwd_ckpt_kernel<IoT, false, true, false>;
+  return eu ? bwd_ckpt_kernel<IoT, false, false, true> : bwd_ckpt_kernel<IoT, false, false, false>;
+}
+
+template <typename IoT, bool kVec, bool kSp>
+auto pick_grad_ge(bool gate, bool eu) {
+  if (gate) return eu ? bwd_grad_kernel<IoT, kVec, kSp, true, true> : bwd_grad_kernel<IoT, kVec, kSp, true, false>;
+  return eu ? bwd_grad_kernel<IoT, kVec, kSp, false, true> : bwd_grad_kernel<IoT, kVec, kSp, false, false>;
+}
+
+template <typename IoT>
+auto pick_grad(bool vec, bool sp, bool gate, bool eu) {
+  if (vec) return sp ? pick_grad_ge<IoT, true, true>(gate, eu) : pick_grad_ge<IoT, true, false>(gate, eu);
+  return sp ? pick_grad_ge<IoT, false, true>(gate, eu) : pick_grad_ge<IoT, false, false>(gate, eu);
+}
+
+template <typename IoT>
 hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   if (a.seqlen == 0) {
     const int64_t n = std::max<int64_t>(a.dim * a.dstate, a.batch * a.dim * a.dstate);
@@ -668,17 +703,13 @@ hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   const bool vec = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
   const dim3 grid((unsigned)k.nwork);
 
-  auto ck = vec ? (a.softplus ? bwd_ckpt_kernel<IoT, true, true> : bwd_ckpt_kernel<IoT, true, false>)
-                : (a.softplus ? bwd_ckpt_kernel<IoT, false, true> : bwd_ckpt_kernel<IoT, false, false>);
+  auto ck = pick_ckpt<IoT>(vec, a.softplus != 0, a.euler != 0);
   hipLaunchKernelGGL(ck, grid, dim3(NT), 0, s, k);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const bool gate = a.z != nullptr;
-  auto gk = vec ? (a.softplus ? (gate ? bwd_grad_kernel<IoT, true, true, true> : bwd_grad_kernel<IoT, true, true, false>)
-                              : (gate ? bwd_grad_kernel<IoT, true, false, true> : bwd_grad_kernel<IoT, true, false, false>))
-                : (a.softplus ? (gate ? bwd_grad_kernel<IoT, false, true, true> : bwd_grad_kernel<IoT, false, true, false>)
-                              : (gate ? bwd_grad_kernel<IoT, false, false, true> : bwd_grad_kernel<IoT, false, false, false>));
+  auto gk = pick_grad<IoT>(vec, a.softplus != 0, a.z != nullptr, a.euler != 0);
   const size_t lds = sizeof(float) * LdsB::kFloats;
   e = hipFuncSetAttribute((const void*)gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

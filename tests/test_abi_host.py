@@ -135,8 +135,7 @@ def test_bwd_validation_errors(lib):
     assert bwd(lib, io=3) == EDTYPE
     assert bwd(lib, dim=0) == ESHAPE
     assert bwd(lib, dstate=17) == EUNSUP
-    assert bwd(lib, sp=2) == EUNSUP                              # Euler: zero-order hold only
-    assert bwd(lib, sp=3) == EUNSUP
+    assert bwd(lib, sp=4) == EUNSUP                              # unknown flag bit
     assert bwd(lib, du=P + 1) == EALIGN
     assert bwd(lib, dA=P + 2) == EALIGN
     assert bwd(lib, ws=None) == EWS

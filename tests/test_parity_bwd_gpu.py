@@ -35,17 +35,17 @@ def grad_inputs(inp, seed, with_dfs):
     return backward_inputs(b, d, inp["A_log"].shape[1], L, io, seed=seed, d_final_state=with_dfs)
 
 
-def run(inp, dy, dfs, softplus=True):
+def run(inp, dy, dfs, softplus=True, disc="zoh"):
     return mscan.scan_bwd(dev(inp["u"]), dev(inp["delta"]), dev(inp["A_log"]), dev(inp["B"]), dev(inp["C"]),
                           dev(dy), D=dev(inp["D"]), z=dev(inp["z"]), delta_bias=dev(inp["delta_bias"]),
                           initial_state=dev(inp["initial_state"]), d_final_state=dev(dfs),
-                          delta_softplus=softplus)
+                          delta_softplus=softplus, discretization=disc)
 
 
-def ref(inp, dy, dfs, softplus=True):
+def ref(inp, dy, dfs, softplus=True, disc="zoh"):
     return oracle.scan_bwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], dy, D=inp["D"], z=inp["z"],
                            delta_bias=inp["delta_bias"], initial_state=inp["initial_state"], d_final_state=dfs,
-                           delta_softplus=softplus)
+                           delta_softplus=softplus, discretization=disc)
 
 
 def check_all(got, want, tol):
@@ -83,6 +83,23 @@ def test_bwd_vs_oracle(case):
     say(f"case {case}")
     got = run(inp, dy, dfs, sp)
     want = ref(inp, dy, dfs, sp)
+    check_all(got, want, TOL[io])
+
+
+@pytest.mark.parametrize("case", [CASES[1], CASES[2], CASES[5], CASES[6]],
+                         ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}" + ("g" if c[5] else "") + ("" if c[10] else "-nosp")
+                              for c in [CASES[1], CASES[2], CASES[5], CASES[6]]])
+def test_bwd_euler_vs_oracle(case):
+    """The Euler input term (Bbar u = Delta B u): every gradient against the oracle."""
+    b, d, n, L, io, gated, hasD, hasB, h0, dfs, sp = case
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, has_D=hasD, has_bias=hasB,
+                         initial_state=h0, seed=L + d + 1)
+    if not sp:
+        inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
+    dy, dfs_t = grad_inputs(inp, seed=L + 1, with_dfs=dfs)
+    say(f"euler case {case}")
+    got = run(inp, dy, dfs_t, sp, "euler")
+    want = ref(inp, dy, dfs_t, sp, "euler")
     check_all(got, want, TOL[io])
 
 
