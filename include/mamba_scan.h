@@ -58,7 +58,7 @@ extern "C" {
 
 #define MAMBA_SCAN_ABI_VERSION 2
 #define MAMBA_SCAN_MAX_DSTATE 64     /* forward scan and decode step */
-#define MAMBA_SCAN_MAX_DSTATE_BWD 16 /* backward pass */
+#define MAMBA_SCAN_MAX_DSTATE_BWD 64 /* backward pass */
 
 /* Bits of the `flags` argument; any other bit set returns MAMBA_SCAN_ERR_UNSUPPORTED. */
 #define MAMBA_SCAN_FLAG_SOFTPLUS 1 /* Delta = softplus(delta + bias); without it Delta = delta + bias */
@@ -246,10 +246,12 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *   d_initial_state  (batch, dim, dstate) f32   NULL: not computed
  *   workspace        at least mamba_scan_bwd_workspace_size(...) bytes, 256-byte aligned:
  *                    the state entering every 8-token sub-chunk (batch x ceil(seqlen/8) x 16 x
- *                    dim fp32) and per-channel-group / per-row partial sums
+ *                    dim fp32, for one group of 16 states at a time), per-channel-group /
+ *                    per-row partial sums, and for dstate > 16 three (batch, dim, seqlen) fp32
+ *                    running sums over state groups
  *   flags            as for mamba_scan_fwd: MAMBA_SCAN_FLAG_SOFTPLUS, MAMBA_SCAN_FLAG_EULER
- * Sizes and limits as for mamba_scan_fwd, except 1 <= dstate <= 16
- * (MAMBA_SCAN_MAX_DSTATE_BWD).  Sums over channels (dB, dC) and
+ * Sizes and limits as for mamba_scan_fwd (1 <= dstate <= 64, MAMBA_SCAN_MAX_DSTATE_BWD;
+ * dstate > 16 runs one pass per 16 states).  Sums over channels (dB, dC) and
  * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so
  * repeated calls give identical results.
  */

@@ -233,7 +233,7 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
   if (check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype) != MAMBA_SCAN_OK) return (size_t)-1;
   if (dstate > MAMBA_SCAN_MAX_DSTATE_BWD) return (size_t)-1;
   mscan::BwdPlan p;
-  mscan::make_bwd_plan(batch, dim, seqlen, &p);
+  mscan::make_bwd_plan(batch, dim, dstate, seqlen, &p);
   return p.ws_total;
 }
 
@@ -258,7 +258,7 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
   for (const void* p : f_ptrs)
     if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   mscan::BwdPlan plan;
-  mscan::make_bwd_plan(batch, dim, seqlen, &plan);
+  mscan::make_bwd_plan(batch, dim, dstate, seqlen, &plan);
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
   }

@@ -99,15 +99,17 @@ struct BwdPlan {
   int64_t nsub;       // 8-token sub-chunks
   int64_t chgroups;   // 64-channel groups
   size_t off_ckpt;    // (batch, nsub, 16, dim) fp32: state before each sub-chunk
-  size_t off_dB;      // (batch, chgroups, 16, seqlen) fp32: per-group partial dB
+  size_t off_dB;      // (batch, 2 chgroups, 16 ngroups, seqlen) fp32: per-32-channel-group partial dB
   size_t off_dC;      // same for dC
-  size_t off_dA;      // (batch, dim, 16) fp32: per-row partial dA_log
+  size_t off_dA;      // (batch, dim, 16 ngroups) fp32: per-row partial dA_log
   size_t off_dD;      // (batch, dim) fp32: per-row partial dD
   size_t off_dbias;   // (batch, dim) fp32: per-row partial ddelta_bias
+  size_t off_acc;     // dstate > 16: 3 x (batch, dim, seqlen) fp32 running sums over state groups
+  int ngroups;        // passes of 16 states
   size_t ws_total;
 };
 
-void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* plan);
+void make_bwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, BwdPlan* plan);
 
 struct BwdArgs {
   const void* u;

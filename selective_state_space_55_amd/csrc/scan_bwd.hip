@@ -71,8 +71,16 @@ struct BArgs {
   float* wsA;
   float* wsD;
   float* wsBias;
+  // dstate > 16: one checkpoint + gradient pass per group of 16 states (n0 = first state); the
+  // per-(token, channel) sums over states (readout, dDelta, du) accumulate in fp32 across passes
+  float* accY;
+  float* accD;
+  float* accU;
   int64_t dim, seqlen, chgroups, ntile, nsub, nwork;
   int dstate, softplus;
+  int n0;     // first state of this pass
+  int npt;    // 16 x number of passes: state slots of the dB / dC / dA partials
+  int acc;    // 0: one pass; 1 first, 2 middle, 3 last of several
 };
 
 // XCD-aware placement, as in the forward kernels.
@@ -164,7 +172,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   float A[NPW], iA[NPW], h[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    const int n = nb + j;
+    const int n = a.n0 + nb + j;
     const bool valid = ch_ok && n < a.dstate;
     A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     iA[j] = valid ? 1.0f / A[j] : 0.0f;
@@ -192,7 +200,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);
     rd = IO::buf_load4(rs_d, off, kVec);
     ru = IO::buf_load4(rs_u, off, kVec);
-    if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    if (w < 2) rb = IO::buf_load4(rs_B, (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz), kVec);
   };
   V4 rd{}, ru{}, rb{};
   load_tile(0, rd, ru, rb);
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float A[NPW], iA[NPW], g[NPW], X[NPW], Y[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
-    const int n = nb + j;
+    const int n = a.n0 + nb + j;
     const bool valid = ch_ok && n < a.dstate;
     A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     iA[j] = valid ? 1.0f / A[j] : 0.0f;
@@ -365,7 +373,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     V4 rz{};
     if constexpr (kGate) rz = IO::buf_load4(rs_z, off, kVec);
     V4 rbc{};
-    if (stageBC) rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)bn * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    if (stageBC)
+      rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz), kVec);
     float hq[4][NPW];   // states entering the tile's sub-chunks (0 for sub-chunks past the end)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -521,7 +530,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         const int i = (lane & 31) >> 2;
         const int64_t tt = tile + 4 * tg + (i & 3);
         if ((lane & 3) == 0 && tt < a.seqlen) {
-          const int64_t o = ((b * 2 * a.chgroups + g32) * NP + nb + (i >> 2)) * a.seqlen + tt;
+          const int64_t o = ((b * 2 * a.chgroups + g32) * a.npt + a.n0 + nb + (i >> 2)) * a.seqlen + tt;
           a.wsB[o] = rB;
           a.wsC[o] = rC;
         }
@@ -551,6 +560,25 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         sd[0] += a0.x; sd[1] += a0.y; sd[2] += a0.z; sd[3] += a0.w;
         su[0] += c0.x; su[1] += c0.y; su[2] += c0.z; su[3] += c0.w;
       }
+      if (a.acc != 0 && d0 + pc < a.dim) {
+        // several passes: this pass's sums over its 16 states join the running ones
+        const int64_t o = row0 + (int64_t)pc * a.seqlen + tile + pg * kPiece;
+        float* acc3[3] = {a.accY + o, a.accD + o, a.accU + o};
+        float* mine[3] = {sy, sd, su};
+#pragma unroll
+        for (int q3 = 0; q3 < 3; ++q3) {
+          if (a.acc >= 2) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (j < nv) mine[q3][j] += acc3[q3][j];
+          }
+          if (a.acc < 3) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              if (j < nv) acc3[q3][j] = mine[q3][j];
+          }
+        }
+      }
       float dzv[4], ddv[4], duv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -559,7 +587,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         duv[j] = fmaf(dyt[j], Dd, su[j]);
         db_acc += (j < nv) ? ddv[j] : 0.0f;
       }
-      if (full) {
+      if (a.acc == 1 || a.acc == 2) {
+        // not the last pass: the outputs wait for the remaining states
+      } else if (full) {
         if constexpr (kGate) IO::buf_store4(rs_dz, off, IO::from_f32(dzv), kVec);
         IO::buf_store4(rs_dd, off, IO::from_f32(ddv), kVec);
         IO::buf_store4(rs_du, off, IO::from_f32(duv), kVec);
@@ -576,8 +606,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   if (ch_ok) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
-      const int n = nb + j;
-      a.wsA[bd * NP + n] = kEuler ? A[j] * X[j] : X[j] - Y[j];   // dA * dA/dA_log
+      const int n = a.n0 + nb + j;
+      a.wsA[bd * a.npt + n] = kEuler ? A[j] * X[j] : X[j] - Y[j];   // dA * dA/dA_log
       if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
     }
   }
@@ -588,7 +618,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   db_acc += __shfl_xor(db_acc, 1, 8);
   db_acc += __shfl_xor(db_acc, 2, 8);
   db_acc += __shfl_xor(db_acc, 4, 8);
-  if (pg == 0 && d0 + pc < a.dim) {
+  if (pg == 0 && d0 + pc < a.dim && (a.acc == 0 || a.acc == 3)) {   // dD and dbias need every state
     a.wsD[b * a.dim + d0 + pc] = dD_acc;
     a.wsBias[b * a.dim + d0 + pc] = db_acc;
   }
@@ -598,7 +628,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
 template <typename IoT>
 __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restrict__ wsB, const float* __restrict__ wsC,
                                                             IoT* __restrict__ dB, IoT* __restrict__ dC, int64_t batch,
-                                                            int64_t chgroups, int dstate, int64_t seqlen) {
+                                                            int64_t chgroups, int dstate, int npt, int64_t seqlen) {
   using IO = Io<IoT>;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= batch * dstate * seqlen) return;
@@ -607,7 +637,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
   const int64_t n = r / seqlen, t = r % seqlen;
   float sb = 0.0f, sc = 0.0f;
   for (int64_t c = 0; c < chgroups; ++c) {   // groups of 32 channels
-    const int64_t o = ((b * chgroups + c) * NP + n) * seqlen + t;
+    const int64_t o = ((b * chgroups + c) * npt + n) * seqlen + t;
     sb += wsB[o];
     sc += wsC[o];
   }
@@ -618,12 +648,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc_kernel(const float* __restr
 __global__ __launch_bounds__(256) void bwd_reduce_param_kernel(const float* __restrict__ wsA, const float* __restrict__ wsD,
                                                                const float* __restrict__ wsBias, float* __restrict__ dA_log,
                                                                float* __restrict__ dD, float* __restrict__ dbias,
-                                                               int64_t batch, int64_t dim, int dstate) {
+                                                               int64_t batch, int64_t dim, int dstate, int npt) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < dim * dstate) {
     const int64_t d = i / dstate, n = i % dstate;
     float s = 0.0f;
-    for (int64_t b = 0; b < batch; ++b) s += wsA[(b * dim + d) * NP + n];
+    for (int64_t b = 0; b < batch; ++b) s += wsA[(b * dim + d) * npt + n];
     dA_log[i] = s;
   }
   if (i < dim) {
@@ -703,51 +733,63 @@ hipError_t run_bwd(const BwdArgs& a, const BwdPlan& p, hipStream_t s) {
   const bool vec = ((mis & 15) == 0) && ((a.seqlen * (int64_t)esz) % 16 == 0);
   const dim3 grid((unsigned)k.nwork);
 
+  k.npt = 16 * p.ngroups;
+  k.accY = p.ngroups > 1 ? reinterpret_cast<float*>(ws + p.off_acc) : nullptr;
+  const size_t nacc = (size_t)(a.batch * a.dim * a.seqlen);
+  k.accD = k.accY ? k.accY + nacc : nullptr;
+  k.accU = k.accY ? k.accY + 2 * nacc : nullptr;
   auto ck = pick_ckpt<IoT>(vec, a.softplus != 0, a.euler != 0);
-  hipLaunchKernelGGL(ck, grid, dim3(NT), 0, s, k);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
-  const bool gate = a.z != nullptr;
   auto gk = pick_grad<IoT>(vec, a.softplus != 0, a.z != nullptr, a.euler != 0);
   const size_t lds = sizeof(float) * LdsB::kFloats;
-  e = hipFuncSetAttribute((const void*)gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)gk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(gk, grid, dim3(NT), lds, s, k);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // one checkpoint + gradient pass per group of 16 states (the checkpoints are reused)
+  for (int gi = 0; gi < p.ngroups; ++gi) {
+    k.n0 = 16 * gi;
+    k.acc = p.ngroups == 1 ? 0 : (gi == 0 ? 1 : (gi == p.ngroups - 1 ? 3 : 2));
+    hipLaunchKernelGGL(ck, grid, dim3(NT), 0, s, k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gk, grid, dim3(NT), lds, s, k);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   const int64_t nbc = a.batch * a.dstate * a.seqlen;
   hipLaunchKernelGGL(bwd_reduce_bc_kernel<IoT>, dim3((unsigned)((nbc + 255) / 256)), dim3(256), 0, s, k.wsB, k.wsC,
                      static_cast<IoT*>(a.dB), static_cast<IoT*>(a.dC), a.batch, 2 * p.chgroups, (int)a.dstate,
-                     a.seqlen);
+                     k.npt, a.seqlen);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t np = std::max<int64_t>(a.dim * a.dstate, a.dim);
   hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3((unsigned)((np + 255) / 256)), dim3(256), 0, s, k.wsA, k.wsD,
-                     k.wsBias, a.dA_log, a.dD, a.dbias, a.batch, a.dim, (int)a.dstate);
+                     k.wsBias, a.dA_log, a.dD, a.dbias, a.batch, a.dim, (int)a.dstate, k.npt);
   return hipGetLastError();
 }
 
 }  // namespace
 
-void make_bwd_plan(int64_t batch, int64_t dim, int64_t seqlen, BwdPlan* p) {
+void make_bwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, BwdPlan* p) {
   p->ntile = (seqlen + kT - 1) / kT;
   p->nsub = (seqlen + kSub - 1) / kSub;
   p->chgroups = (dim + kCh - 1) / kCh;
+  p->ngroups = (int)((dstate + 15) / 16);
+  const int64_t npt = 16 * p->ngroups;
   size_t off = 0;
-  p->off_ckpt = off;
+  p->off_ckpt = off;   // one group's checkpoints, reused by each pass
   off += align256(sizeof(float) * (size_t)(batch * p->nsub * NP * dim));
   p->off_dB = off;   // partial sums per 32-channel group
-  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * NP * seqlen));
+  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * npt * seqlen));
   p->off_dC = off;
-  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * NP * seqlen));
+  off += align256(sizeof(float) * (size_t)(batch * 2 * p->chgroups * npt * seqlen));
   p->off_dA = off;
-  off += align256(sizeof(float) * (size_t)(batch * dim * NP));
+  off += align256(sizeof(float) * (size_t)(batch * dim * npt));
   p->off_dD = off;
   off += align256(sizeof(float) * (size_t)(batch * dim));
   p->off_dbias = off;
   off += align256(sizeof(float) * (size_t)(batch * dim));
+  p->off_acc = off;   // several passes: running sums over states of the readout, dDelta and du
+  if (p->ngroups > 1) off += align256(3 * sizeof(float) * (size_t)(batch * dim * seqlen));
   p->ws_total = seqlen == 0 ? 0 : off;
 }
 

@@ -134,7 +134,7 @@ def test_bwd_validation_errors(lib):
     assert bwd(lib, z=P, dz=None) == ENULL             # a gate needs its gradient output
     assert bwd(lib, io=3) == EDTYPE
     assert bwd(lib, dim=0) == ESHAPE
-    assert bwd(lib, dstate=17) == EUNSUP
+    assert bwd(lib, dstate=65) == EUNSUP
     assert bwd(lib, sp=4) == EUNSUP                              # unknown flag bit
     assert bwd(lib, du=P + 1) == EALIGN
     assert bwd(lib, dA=P + 2) == EALIGN
@@ -150,7 +150,10 @@ def test_bwd_workspace_size(lib):
     ckpt = 4 * (8192 // 8) * 16 * 4096 * 4
     parts = 2 * 4 * 128 * 16 * 8192 * 4   # dB, dC partial sums per 32-channel group
     assert ckpt + parts <= n <= ckpt + parts + 4 * 4096 * 18 * 4 + 6 * 256
-    assert f(2, 64, 17, 100, 1) == ctypes.c_size_t(-1).value
+    # d_state 64: four passes share one group's checkpoints; partials for 64 states, three running sums
+    n64 = f(4, 4096, 64, 8192, 1)
+    assert n64 >= ckpt + 4 * parts + 3 * 4 * 4096 * 8192 * 4
+    assert f(2, 64, 65, 100, 1) == ctypes.c_size_t(-1).value
 
 
 def conv(lib, x=P, w=P, bias=None, si=None, so=None, u=P, batch=2, dim=64, seqlen=100, K=4, io=1, silu=1):
@@ -181,8 +184,9 @@ def test_fwd_workspace_holds_readout_sum_for_wide_state():
     assert mscan.fwd_workspace_size(b, d, 64, L, mscan.BF16, 4) > mscan.fwd_workspace_size(b, d, 64, L, mscan.BF16, 1)
     assert mscan.fwd_workspace_size(b, d, 64, 0, mscan.BF16, 0) == 0
     assert mscan.bwd_workspace_size(b, d, 16, L, mscan.BF16) > 0
+    assert mscan.bwd_workspace_size(b, d, 17, L, mscan.BF16) >= 3 * b * d * L * 4
     with pytest.raises(ValueError):
-        mscan.bwd_workspace_size(b, d, 17, L, mscan.BF16)
+        mscan.bwd_workspace_size(b, d, 65, L, mscan.BF16)
 
 
 def varlen(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, cu=P, h0=None, fs=None, y=P,

@@ -1,7 +1,8 @@
 """Backward pass on the GPU (through the C ABI) against the fp64 oracle.
 
 Every gradient is compared element by element with the error metric of the
-forward tests (max |g - r| / max(|r|, rms(r))) at the io dtype's tolerance:
+forward tests (max |g - r| / max(|r|, rms(r))) at the io dtype's tolerance
+(d_state up to 64, zero-order hold and Euler):
 1e-4 for float32 io, 1e-2 for bfloat16 io (gradients stored in bf16 are
 rounded to nearest even).  Shapes span several 64-channel workgroups, several
 32-token tiles and ragged tails in both; the 130M-layer shape is compared in
@@ -100,6 +101,30 @@ def test_bwd_euler_vs_oracle(case):
     say(f"euler case {case}")
     got = run(inp, dy, dfs_t, sp, "euler")
     want = ref(inp, dy, dfs_t, sp, "euler")
+    check_all(got, want, TOL[io])
+
+
+WIDE = [  # d_state above 16: one checkpoint + gradient pass per 16 states
+    (2, 70, 32, 100, "f32", True, True, True, True, True, True),
+    (1, 130, 64, 33, "bf16", True, True, True, True, False, True),
+    (2, 64, 20, 257, "bf16", False, True, False, False, True, True),
+    (1, 96, 48, 96, "f32", True, False, False, True, True, False),   # no softplus: no bias, so Delta > 0
+]
+
+
+@pytest.mark.parametrize("case", WIDE, ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}" + ("g" if c[5] else "")
+                                            + ("" if c[10] else "-nosp") for c in WIDE])
+@pytest.mark.parametrize("disc", ["zoh", "euler"])
+def test_bwd_wide_state_vs_oracle(case, disc):
+    b, d, n, L, io, gated, hasD, hasB, h0, dfs_on, sp = case
+    inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, has_D=hasD, has_bias=hasB,
+                         initial_state=h0, seed=L + d + n)
+    if not sp:
+        inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
+    dy, dfs = grad_inputs(inp, seed=L * 3 + n, with_dfs=dfs_on)
+    say(f"wide case {case} {disc}")
+    got = run(inp, dy, dfs, sp, disc)
+    want = ref(inp, dy, dfs, sp, disc)
     check_all(got, want, TOL[io])
 
 
