@@ -22,8 +22,10 @@
 // on bf16 operands in LDS with fp32 accumulation; the operand layouts (lane l
 // holds 8 consecutive k) make each operand one 16-byte LDS read.  Per chunk:
 //   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes);
-//              one wave turns dt into log a (softplus, A_h), w and a running
-//              sum over the chunk (DPP prefix scan)
+//              the chunk's decay terms were computed during the previous
+//              chunk (one wave turns dt into log a (softplus, A_h), w and a
+//              running sum over the chunk with a DPP prefix scan, into the
+//              other of two buffers)
 //   A2      -- x scaled by exp(cum_Q - cum_j) w_j as a high plus a low bf16
 //              part (so the state update keeps ~16 bits), token-major rows;
 //              waves 0-2: the three causal 32 x 32 tiles of B C^T and the
@@ -83,7 +85,7 @@ struct SsdLds {
   static constexpr int kST = kP * kRowN;      // S^T   [p][n]
   static constexpr int kHalves = kXtm + kCs + kBs + 2 * kXs + kMs + kST;
   static constexpr int kYRow = kP + 4;        // Y fp32 [i][p]
-  static constexpr int kFloats = kQ * kYRow + 4 * kQ + 4;
+  static constexpr int kFloats = kQ * kYRow + 2 * (4 * kQ + 4);   // Y, then two sets of decay terms
   static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
 };
 
@@ -152,11 +154,10 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   uint16_t* Ms = XsL + L::kXs;
   uint16_t* ST = Ms + L::kMs;
   float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
-  float* cum = Yf + kQ * kYRow;                         // running sum of log a in the chunk
-  float* ecum = cum + kQ;                               // exp(cum_i)
-  float* scl = ecum + kQ;                               // exp(cum_Q - cum_j) w_j
-  float* wv = scl + kQ;                                 // w_j
-  float* atot = wv + kQ;                                // exp(cum_Q)
+  // decay terms of a chunk, double-buffered (chunk c uses set c & 1, while one wave
+  // computes chunk c+1's into the other set): [set][cum | ecum | scl | wv | atot]
+  float* dterms = Yf + kQ * kYRow;
+  constexpr int kDSet = 4 * kQ + 4;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -265,9 +266,28 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   const bool has_y = w >= 4;
   const int yi = (w >> 1) & 1, yp = w & 1;
 
+  // one wave turns a chunk's dt into its decay terms (written to set `set`)
+  auto dt_terms = [&](uint32_t dtv, int64_t tc0, int set) {
+    const bool ok = tc0 + lane < Lq;
+    const float x = bf(dtv) + bias;
+    float Delta = a.softplus ? softplus_log2e(x) * 0.6931471805599453f : x;
+    Delta = ok ? Delta : 0.0f;                       // past the end: a = 1, w = 0 (state unchanged)
+    const float la = Delta * Ah;
+    const float wj = a.euler ? Delta : (Ah != 0.0f ? expm1_f(la) / Ah : Delta);
+    const float cs = wave_prefix_sum(la);
+    const float tot = __shfl(cs, 63);
+    float* o = dterms + set * kDSet;
+    o[lane] = cs;
+    o[kQ + lane] = __expf(cs);
+    o[2 * kQ + lane] = __expf(tot - cs) * wj;
+    o[3 * kQ + lane] = wj;
+    if (lane == 0) o[4 * kQ] = __expf(tot);
+  };
+
   Pf pf;
   prefetch(0, pf);
   uint4 xcur, zcur;
+  if (w == kDtWave) dt_terms(pf.dt, 0, 0);
 
   for (int64_t c = 0; c < nchunk; ++c) {
     const int64_t t0 = c * kQ;
@@ -282,21 +302,12 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
       *reinterpret_cast<uint4*>(Cs + j * kRowN + n8) = pf.cq[r];
       *reinterpret_cast<uint4*>(Bs + j * kRowN + n8) = pf.bq[r];
     }
-    if (w == kDtWave) {
-      const bool ok = t0 + lane < Lq;
-      const float x = bf(pf.dt) + bias;
-      float Delta = a.softplus ? softplus_log2e(x) * 0.6931471805599453f : x;
-      Delta = ok ? Delta : 0.0f;                       // past the end: a = 1, w = 0 (state unchanged)
-      const float la = Delta * Ah;
-      const float wj = a.euler ? Delta : (Ah != 0.0f ? expm1_f(la) / Ah : Delta);
-      const float cs = wave_prefix_sum(la);
-      const float tot = __shfl(cs, 63);
-      cum[lane] = cs;
-      ecum[lane] = __expf(cs);
-      scl[lane] = __expf(tot - cs) * wj;
-      wv[lane] = wj;
-      if (lane == 0) atot[0] = __expf(tot);
-    }
+    const int dset = (int)(c & 1);
+    const float* cum = dterms + dset * kDSet;   // running sum of log a in the chunk
+    const float* ecum = cum + kQ;               // exp(cum_i)
+    const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j
+    const float* wv = scl + kQ;                 // w_j
+    const float* atot = wv + kQ;                // exp(cum_Q)
     __syncthreads();
 
     // ---- A2: next loads; transposes; G -> M (waves 0-2); C S_in (waves 4-7) ----
@@ -378,6 +389,7 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = yacc[4 * q + r];
     }
+    if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
     if (has_s) {
       const float at = atot[0];
       f32x16 slo = {};
