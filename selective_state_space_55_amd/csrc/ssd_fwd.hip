@@ -18,16 +18,17 @@
 // Mapping.  One workgroup (8 waves, two per SIMD) owns one (batch, head) and
 // walks its chunks in order, keeping S (N x P, fp32) in MFMA accumulators --
 // nothing but x, dt, B, C, z in and y, the final state out touches HBM.
-// Q = 64, P = 64, N = 64 or 128.  Every product is v_mfma_f32_32x32x16_bf16
-// on bf16 operands in LDS with fp32 accumulation; the operand layouts (lane l
+// Q = 64, P = 64, N = 64 or 128.  Every product is a 32x32x16 MFMA (bf16
+// operands, fp16 for the state update) from LDS with fp32 accumulation; the operand layouts (lane l
 // holds 8 consecutive k) make each operand one 16-byte LDS read.  Per chunk:
 //   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes);
 //              the chunk's decay terms were computed during the previous
 //              chunk (one wave turns dt into log a (softplus, A_h), w and a
 //              running sum over the chunk with a DPP prefix scan, into the
 //              other of two buffers)
-//   A2      -- x scaled by exp(cum_Q - cum_j) w_j as a high plus a low bf16
-//              part (so the state update keeps ~16 bits), token-major rows;
+//   A2      -- x scaled by exp(cum_Q - cum_j) w_j in fp16 (11 significant bits
+//              for the state update, whose products are fp16 with B converted
+//              from bf16 -- one bf16 part lost too much), token-major rows;
 //              waves 0-2: the three causal 32 x 32 tiles of B C^T and the
 //              masked, decayed M; waves 4-7: the Y tiles' C S_in, rows scaled
 //              by exp(cum_i)
@@ -49,6 +50,7 @@ namespace mscan {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQ = 64;      // tokens per chunk
@@ -80,10 +82,10 @@ struct SsdLds {
   static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
   static constexpr int kCs = kQ * kRowN;      // C     [i][n]
   static constexpr int kBs = kQ * kRowN;      // B     [j][n]
-  static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], high and low parts
+  static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], fp16
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
   static constexpr int kST = kP * kRowN;      // S^T   [p][n]
-  static constexpr int kHalves = kXtm + kCs + kBs + 2 * kXs + kMs + kST;
+  static constexpr int kHalves = kXtm + kCs + kBs + kXs + kMs + kST;
   static constexpr int kYRow = kP + 4;        // Y fp32 [i][p]
   static constexpr int kFloats = kQ * kYRow + 2 * (4 * kQ + 4);   // Y, then two sets of decay terms
   static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
@@ -95,6 +97,24 @@ __device__ __forceinline__ bf16x8 lds_b8(const uint16_t* p) {
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// bf16 -> fp16, element by element (B values are well inside fp16's range; the
+// conversion is exact for them down to fp16's normal minimum)
+__device__ __forceinline__ f16x8 to_f16(bf16x8 v) {
+  f16x8 r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = (_Float16)(float)v[k];
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
 __device__ __forceinline__ float bf(uint32_t h16) { return __uint_as_float(h16 << 16); }
@@ -149,9 +169,8 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
   uint16_t* Xtm = sm;
   uint16_t* Cs = Xtm + L::kXtm;
   uint16_t* Bs = Cs + L::kCs;
-  uint16_t* XsH = Bs + L::kBs;
-  uint16_t* XsL = XsH + L::kXs;
-  uint16_t* Ms = XsL + L::kXs;
+  uint16_t* Xs = Bs + L::kBs;   // fp16 bits
+  uint16_t* Ms = Xs + L::kXs;
   uint16_t* ST = Ms + L::kMs;
   float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
   // decay terms of a chunk, double-buffered (chunk c uses set c & 1, while one wave
@@ -314,18 +333,13 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
     if (c + 1 < nchunk) prefetch(c + 1, pf);
     {
       // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j,
-      // as a high bf16 part and the bf16 of the remainder
+      // in fp16 (11 significant bits; the state update's products are fp16 x fp16)
       const float sc = scl[xj];
       const uint32_t cw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
-      uint32_t hi[4], lo[4];
+      uint32_t hv[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float e0 = bf(cw[k] & 0xffffu) * sc, e1 = bf(cw[k] >> 16) * sc;
-        hi[k] = pack_bf16x2(e0, e1);
-        lo[k] = pack_bf16x2(e0 - bf(hi[k] & 0xffffu), e1 - bf(hi[k] >> 16));
-      }
-      *reinterpret_cast<uint4*>(XsH + xj * kRowP + xp8) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(XsL + xj * kRowP + xp8) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      for (int k = 0; k < 4; ++k) hv[k] = pack_f16x2(bf(cw[k] & 0xffffu) * sc, bf(cw[k] >> 16) * sc);
+      *reinterpret_cast<uint4*>(Xs + xj * kRowP + xp8) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
     f32x16 yacc = {};
     if (w < 3) {
@@ -392,17 +406,13 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
     if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
     if (has_s) {
       const float at = atot[0];
-      f32x16 slo = {};
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] *= at;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 av = lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane);
-        S = mfma(av, lds_opnd_tr(XsH, kRowP, 16 * s, s_pb * 32, lane), S);
-        slo = mfma(av, lds_opnd_tr(XsL, kRowP, 16 * s, s_pb * 32, lane), slo);
+        const f16x8 av = to_f16(lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane));
+        S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] += slo[r];
     }
     write_ST();
     __syncthreads();
