@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
     const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j
     const float* wv = scl + kQ;                 // w_j
     const float* atot = wv + kQ;                // exp(cum_Q)
-    __syncthreads();
+    lds_barrier();
 
     // ---- A2: next loads; transposes; G -> M (waves 0-2); C S_in (waves 4-7) ----
     if (c + 1 < nchunk) prefetch(c + 1, pf);
@@ -387,7 +387,7 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
         yacc[4 * q + 3] = (yacc[4 * q + 3] + y1[4 * q + 3]) * e.w;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- A3: Y += M x (waves 4-7) -> Yf; S = exp(cum_Q) S + B^T (x_hi + x_lo) ----
     if (has_y) {
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kNT) void ssd_fwd_kernel(SArgs a) {
       }
     }
     write_ST();
-    __syncthreads();
+    lds_barrier();
 
     // ---- epilogue: token xj, channels xp8 .. +7: y = Y + D x, gate, store ----
     {
