@@ -285,9 +285,10 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *   A_log, D, dt_bias (nheads)                          f32 (D, dt_bias may be NULL)
  *   initial_state, final_state (batch, nheads, headdim, dstate) f32, 16-byte aligned, NULL allowed
  *   z                NULL means no gate
- * Supported: io_dtype MAMBA_SCAN_BF16, headdim 64, 128, 192 or 256, dstate 64 or 128 (others
- * return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 64 < 2^31.  Products use bf16
- * operands with fp32 accumulation; the state is carried in fp32.  No workspace.
+ * Supported: io_dtype MAMBA_SCAN_BF16, headdim a multiple of 32 up to 256, dstate 64 or 128
+ * (others return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 32 < 2^31.  Products use
+ * bf16 operands (fp16 for the state update) with fp32 accumulation; the state is carried in fp32.
+ * No workspace.
  */
 int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void* B, const void* C, const float* D,
                   const void* z, const float* dt_bias, const float* initial_state, float* final_state, void* y,

@@ -283,10 +283,10 @@ int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void*
   if (io_dtype != MAMBA_SCAN_F32 && io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
   if (batch < 1 || seqlen < 0 || nheads < 1 || headdim < 1 || dstate < 1) return MAMBA_SCAN_ERR_SHAPE;
   if (io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_UNSUPPORTED;              // bf16 operands only
-  if (headdim % 64 != 0 || headdim > 256 || (dstate != 64 && dstate != 128)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (headdim % 32 != 0 || headdim > 256 || (dstate != 64 && dstate != 128)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
-  if (!mul_ok(batch, nheads * (headdim / 64), &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid
+  if (!mul_ok(batch, nheads * (headdim / 32), &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid
   if (!mul_ok(t, seqlen, &t) || !mul_ok(t, headdim * 2, &t)) return MAMBA_SCAN_ERR_SHAPE;
   if (!A_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;

@@ -229,9 +229,9 @@ def ssd(lib, x=P, dt=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None, f
 def test_ssd_validation_errors(lib):
     assert ssd(lib, io=0) == EUNSUP                  # bf16 operands only
     assert ssd(lib, io=5) == EDTYPE
-    assert ssd(lib, hd=32) == EUNSUP
-    assert ssd(lib, hd=96) == EUNSUP                 # head dims are multiples of 64
-    assert ssd(lib, hd=320) == EUNSUP
+    assert ssd(lib, hd=48) == EUNSUP                 # head dims are multiples of 32
+    assert ssd(lib, hd=16) == EUNSUP
+    assert ssd(lib, hd=288) == EUNSUP                # up to 256
     assert ssd(lib, N=16) == EUNSUP
     assert ssd(lib, flags=8) == EUNSUP
     assert ssd(lib, batch=0) == ESHAPE
@@ -241,6 +241,7 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, x=P + 2) == EALIGN               # 16-byte vector loads
     assert ssd(lib, h0=P + 4) == EALIGN
     assert ssd(lib, batch=1 << 20, H=1 << 12) == EUNSUP
+    assert ssd(lib, batch=1 << 20, H=1 << 9, hd=256) == EUNSUP   # 2^31 32-channel slices
 
 
 def fwd_conv(lib, x=P, w=P, cb=None, csi=None, cso=None, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None,

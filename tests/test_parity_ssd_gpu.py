@@ -1,7 +1,7 @@
 """GPU parity of the multi-head SSM with a scalar decay per head (state-space-
 duality form, mamba_ssd_fwd, matrix cores) against the fp64 oracle: ragged
 lengths (partial last chunk), one-token and empty sequences, d_state 64 and
-128, head dims 64 to 256, gate / no gate, initial state, both input terms, softplus off; repeat
+128, head dims 32 to 256 (32- and 64-channel slices), gate / no gate, initial state, both input terms, softplus off; repeat
 runs are identical; a split at a chunk boundary resumes bit for bit and at any
 other token within tolerance; the full-size layer on sampled heads.
 
@@ -78,12 +78,25 @@ def test_ssd_vs_oracle(case):
     check("final_state", fs, fsr)
 
 
-@pytest.mark.parametrize("P,N,disc", [(128, 128, "zoh"), (128, 64, "euler"), (192, 64, "zoh"), (256, 128, "zoh")])
-def test_ssd_wide_heads_vs_oracle(P, N, disc):
-    """Head dims above 64: each head runs as P / 64 slices of 64 channels sharing its decay."""
+@pytest.mark.parametrize("P,N,disc", [(128, 128, "zoh"), (128, 64, "euler"), (192, 64, "zoh"), (256, 128, "zoh"),
+                                     (32, 128, "zoh"), (96, 64, "euler"), (160, 128, "zoh")])
+def test_ssd_head_dims_vs_oracle(P, N, disc):
+    """Head dims other than 64: each head runs as slices of 32 or 64 channels sharing its decay."""
     b, L, H = 2, 150, 2
     inp = ssd_inputs(b, L, H, P, N, seed=P + N, gated=True, initial_state=True)
     say(f"head dim {P}, N {N}, {disc}")
+    y, fs = gpu(inp, True, disc)
+    yr, fsr = ref(inp, True, disc)
+    check("y", y, yr)
+    check("final_state", fs, fsr)
+
+
+@pytest.mark.parametrize("N,disc,gated", [(128, "zoh", True), (64, "euler", False)])
+def test_ssd_many_heads_vs_oracle(N, disc, gated):
+    """More (batch, head) pairs than the GPU has CUs (260 workgroups), with a ragged last chunk."""
+    b, L, H = 2, 70, 130
+    inp = ssd_inputs(b, L, H, 64, N, seed=H + N, gated=gated, initial_state=True)
+    say(f"{b * H} heads, N {N}, {disc}")
     y, fs = gpu(inp, True, disc)
     yr, fsr = ref(inp, True, disc)
     check("y", y, yr)
