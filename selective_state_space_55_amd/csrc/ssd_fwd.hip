@@ -293,7 +293,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
 
   // Y tiles (waves 4-7 at P = 64, 4-5 at P = 32): rows 32 yi .., columns 32 yp ..
   constexpr int kYT = 2 * (P / 32);
-  const bool has_y = w >= 4 && w < 4 + kYT;
+  const bool has_y = w >= 4 && (kYT == 4 || w < 4 + kYT);
   const int yi = P == 64 ? (w >> 1) & 1 : w & 1, yp = P == 64 ? w & 1 : 0;
 
   // one wave turns a chunk's dt into its decay terms (written to set `set`)
