@@ -169,6 +169,8 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const int64_t bd = b * a.dim + d;
   if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
 
+  // zero-order hold carries the scaled state A h: A h_t = Abar (A h_{t-1} + B u) - B u
+  // (one multiply fewer per step than h + B u / A); checkpoints store h = (A h) / A
   float A[NPW], iA[NPW], h[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
     A[j] = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     iA[j] = valid ? 1.0f / A[j] : 0.0f;
     h[j] = (valid && a.h0) ? a.h0[bd * a.dstate + n] : 0.0f;
+    if constexpr (!kEuler) h[j] *= A[j];
   }
 
   const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
         const int64_t s8 = k * (kT / kSub) + g / 2;
         if (ch_ok && s8 < a.nsub) {
 #pragma unroll
-          for (int j = 0; j < NPW; ++j) ck[(s8 * NP + j) * a.dim] = h[j];
+          for (int j = 0; j < NPW; ++j) ck[(s8 * NP + j) * a.dim] = kEuler ? h[j] : h[j] * iA[j];
         }
       }
       const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * g);
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
           if constexpr (kEuler) {
             h[j] = fmaf(av, h[j], dpp_bcast_mul<4 * j + kk>(bq, uus[kk]));   // Abar h + B (Delta u)
           } else {
-            const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk] * iA[j]);
+            const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk]);   // B u
             h[j] = fmaf(av, h[j] + sv, -sv);
           }
         });
