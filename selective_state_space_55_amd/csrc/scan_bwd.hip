@@ -312,7 +312,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     par[kCh + tid] = (ok && a.D) ? a.D[d0 + tid] : 0.0f;
   }
 
-  // X, Y: running sums of Delta g q and l e B u per state (dA_log = X - Y, derived below)
+  // X, Y: running sums of Delta g q (kept in units of log2(e), as Delta is staged) and l e B u per
+  // state (dA_log = ln2 X - Y, derived below)
   float A[NPW], iA[NPW], g[NPW], X[NPW], Y[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -495,7 +496,6 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         static_for<4>([&](auto kr_c) {
           constexpr int kk = 3 - decltype(kr_c)::value;   // tokens in reverse
           constexpr int t = 4 * gq + kk;                  // token within the sub-chunk
-          const float Delta = dls[kk] * kLn2;
           float dD_p = 0.0f, du_p = 0.0f;
           static_for<NPW>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
@@ -509,11 +509,11 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             if constexpr (kEuler) {
               // dh_t/dDelta = A Abar h_{t-1} + B u, dh_t/dA = Delta Abar h_{t-1}: dA_log = A X
               dD_p = fmaf(g[j] * A[j], hp, fmaf(l, bu, dD_p));
-              X[j] = fmaf(Delta * g[j], hp, X[j]);
+              X[j] = fmaf(dls[kk] * g[j], hp, X[j]);
             } else {
               const float q = fmaf(A[j], hp, bu);
               dD_p = fmaf(g[j], q, dD_p);
-              X[j] = fmaf(Delta * g[j], q, X[j]);
+              X[j] = fmaf(dls[kk] * g[j], q, X[j]);
               Y[j] = fmaf(le, bu, Y[j]);
             }
             du_p = dpp_bcast_fmac<src>(du_p, bq.x, le);
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
 #pragma unroll
     for (int j = 0; j < NPW; ++j) {
       const int n = a.n0 + nb + j;
-      a.wsA[bd * a.npt + n] = kEuler ? A[j] * X[j] : X[j] - Y[j];   // dA * dA/dA_log
+      a.wsA[bd * a.npt + n] = kEuler ? A[j] * (X[j] * kLn2) : fmaf(X[j], kLn2, -Y[j]);   // dA * dA/dA_log
       if (a.dh0 && n < a.dstate) a.dh0[bd * a.dstate + n] = g[j];
     }
   }
