@@ -516,7 +516,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
               X[j] = fmaf(dls[kk] * g[j], q, X[j]);
               Y[j] = fmaf(le, bu, Y[j]);
             }
-            du_p = dpp_bcast_fmac<src>(du_p, bq.x, le);
+            du_p = j == 0 ? dpp_bcast_mul<src>(bq.x, le) : dpp_bcast_fmac<src>(du_p, bq.x, le);
             dBv[j * 4 + kk] = le * uus[kk];
             dCv[j * 4 + kk] = dys[kk] * hh[t][j];
           });
