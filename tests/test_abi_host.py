@@ -266,3 +266,15 @@ def test_fwd_conv_validation_errors(lib):
     # a single time chunk needs no workspace; four chunks do
     assert mscan.fwd_workspace_size(1, 64, 16, 2048, mscan.BF16) > 0
     assert fwd_conv(lib, batch=1, dim=64, seqlen=2048, ws=None) == EWS
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built HIP library every entry point raises before doing any work."""
+    import torch
+    monkeypatch.setattr(mscan, "_lib", None)
+    monkeypatch.setattr(mscan, "LIB_PATH", str(tmp_path / "libmamba_scan.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mscan.load_library()
+    u = torch.zeros(1, 64, 8)
+    with pytest.raises(RuntimeError, match="not built"):
+        mscan.scan_fwd(u, u, torch.zeros(64, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
