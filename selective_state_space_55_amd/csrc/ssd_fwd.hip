@@ -24,19 +24,19 @@
 // wave 7 computes the decay terms, and only waves 0-3 stage x).  Every product is a 32x32x16 MFMA (bf16
 // operands, fp16 for the state update) from LDS with fp32 accumulation; the operand layouts (lane l
 // holds 8 consecutive k) make each operand one 16-byte LDS read.  Per chunk:
-//   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes);
-//              the chunk's decay terms were computed during the previous
-//              chunk (one wave turns dt into log a (softplus, A_h), w and a
-//              running sum over the chunk with a DPP prefix scan, into the
-//              other of two buffers)
-//   A2      -- x scaled by exp(cum_Q - cum_j) w_j in fp16 (11 significant bits
-//              for the state update, whose products are fp16 with B converted
-//              from bf16 -- one bf16 part lost too much), token-major rows;
-//              waves 0-2: the three causal 32 x 32 tiles of B C^T and the
+//   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes),
+//              and x scaled by exp(cum_Q - cum_j) w_j in fp16 (11 significant
+//              bits for the state update, whose products are fp16 with B
+//              converted from bf16 -- one bf16 part lost too much); the
+//              chunk's decay terms were computed during the previous chunk
+//              (one wave turns dt into log a (softplus, A_h), w and a running
+//              sum over the chunk with a DPP prefix scan, into the other of
+//              two buffers)
+//   A2      -- waves 0-2: the three causal 32 x 32 tiles of B C^T and the
 //              masked, decayed M; waves 4-7: the Y tiles' C S_in, rows scaled
-//              by exp(cum_i)
-//   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); every wave (N =
-//              128) one 32 x 32 tile of S = exp(cum_Q) S + B^T Xs
+//              by exp(cum_i); then every wave (N = 128) one 32 x 32 tile of
+//              S = exp(cum_Q) S + B^T Xs (C S_in reads the copy of S_in in LDS)
+//   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); S to LDS
 //   epilogue -- y = Y + D x (x kept in registers from its load), SiLU(z) gate,
 //              one 16-byte store per thread
 // Operands whose k (token) index must be contiguous per lane -- x for M x, B
@@ -318,6 +318,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   prefetch(0, pf);
   uint4 xcur, zcur;
   if (w == kDtWave) dt_terms(pf.dt, 0, 0);
+  lds_barrier();   // chunk 0's decay terms, read at its stage
 
   for (int64_t c = 0; c < nchunk; ++c) {
     const int64_t t0 = c * kQ;
@@ -343,10 +344,6 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j
     const float* wv = scl + kQ;                 // w_j
     const float* atot = wv + kQ;                // exp(cum_Q)
-    lds_barrier();
-
-    // ---- A2: next loads; transposes; G -> M (waves 0-2); C S_in (waves 4-7) ----
-    if (c + 1 < nchunk) prefetch(c + 1, pf);
     if (has_x) {
       // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j,
       // in fp16 (11 significant bits; the state update's products are fp16 x fp16)
@@ -357,6 +354,10 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       for (int k = 0; k < 4; ++k) hv[k] = pack_f16x2(bf(cw[k] & 0xffffu) * sc, bf(cw[k] >> 16) * sc);
       *reinterpret_cast<uint4*>(Xs + xj * kRowP + xp8) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
+    lds_barrier();
+
+    // ---- A2: next loads; G -> M (waves 0-2); C S_in (waves 4-7); state update ----
+    if (c + 1 < nchunk) prefetch(c + 1, pf);
     f32x16 yacc = {};
     if (w < 3) {
       // G^T tile (rows j-block jb, columns i-block ib) over N, two accumulation chains
@@ -407,9 +408,19 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
           yacc[4 * q + r] = (P == 64 ? yacc[4 * q + r] + y1[4 * q + r] : yacc[4 * q + r]) * ev[r];
       }
     }
+    if (has_s) {
+      const float at = atot[0];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] *= at;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 av = to_f16(lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane));
+        S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
+      }
+    }
     lds_barrier();
 
-    // ---- A3: Y += M x (waves 4-7) -> Yf; S = exp(cum_Q) S + B^T (x_hi + x_lo) ----
+    // ---- A3: Y += M x (waves 4-7) -> Yf; S -> LDS for the next chunk's C S_in ----
     if (has_y) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -424,16 +435,6 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = yacc[4 * q + r];
     }
     if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
-    if (has_s) {
-      const float at = atot[0];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] *= at;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 av = to_f16(lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane));
-        S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
-      }
-    }
     write_ST();
     lds_barrier();
 
