@@ -453,6 +453,13 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
         h[0] = fmaf(av0, h[0], s0);                                 // Abar h + s
         h[1] = fmaf(av1, h[1], s1);
+      } else if constexpr (kAgg) {
+        // the aggregate pass carries the scaled state A h (no readout needs h):
+        // A h_t = Abar (A h_{t-1} + B u) - B u, one multiply fewer per step
+        const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * u
+        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
+        h[0] = fmaf(av0, h[0] + s0, -s0);
+        h[1] = fmaf(av1, h[1] + s1, -s1);
       } else {
         const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);       // s = B * u / A
         const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
@@ -559,7 +566,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       if (!kAgg) {
         if (kc == nk - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
       } else {
-        a.carry[cslot * a.np + n] = h[j];
+        a.carry[cslot * a.np + n] = kEuler ? h[j] : h[j] * iA[j];   // zero-order hold: (A h) / A
       }
     }
     if (kAgg && sp == 0 && hf == 0) a.dsum[cslot] = dsum_acc;
