@@ -39,6 +39,11 @@
 //   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); S to LDS
 //   epilogue -- y = Y + D x (x kept in registers from its load), SiLU(z) gate,
 //              one 16-byte store per thread
+// At P = 64 (two x and two M tiles in LDS) chunk c's A3 moves into chunk c+1's
+// A2 -- waves 4-7 first finish chunk c's Y with M X and store it -- and its
+// epilogue into chunk c+1's last phase, so a chunk has two barriers; the decay
+// terms of chunk c+1 are computed in chunk c's A2 from a dt loaded a chunk
+// earlier.
 // Operands whose k (token) index must be contiguous per lane -- x for M x, B
 // and the scaled x for the state update -- are read straight from the
 // token-major tiles with ds_read_b64_tr_b16 (gfx950's transposing LDS read:
@@ -87,7 +92,10 @@ struct SsdLds {
   static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], fp16
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
   static constexpr int kST = P * kRowN;      // S^T   [p][n]
-  static constexpr int kHalves = kXtm + kCs + kBs + kXs + kMs + kST;
+  // P = 64 keeps two x tiles and two M tiles: chunk c's M X runs in chunk c+1's
+  // second phase (one barrier fewer per chunk)
+  static constexpr int kBuf = P == 64 ? 2 : 1;
+  static constexpr int kHalves = kBuf * kXtm + kCs + kBs + kXs + kBuf * kMs + kST;
   static constexpr int kYRow = P + 4;         // Y fp32 [i][p]
   static constexpr int kFloats = kQ * kYRow + 2 * (4 * kQ + 4);   // Y, then two sets of decay terms
   static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
@@ -169,11 +177,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   constexpr int kRowQ = L::kRowQ, kRowN = L::kRowN, kRowP = L::kRowP, kYRow = L::kYRow;
   extern __shared__ __align__(16) uint16_t sm[];
   uint16_t* Xtm = sm;
-  uint16_t* Cs = Xtm + L::kXtm;
+  uint16_t* Cs = Xtm + L::kBuf * L::kXtm;
   uint16_t* Bs = Cs + L::kCs;
   uint16_t* Xs = Bs + L::kBs;   // fp16 bits
   uint16_t* Ms = Xs + L::kXs;
-  uint16_t* ST = Ms + L::kMs;
+  uint16_t* ST = Ms + L::kBuf * L::kMs;
   float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
   // decay terms of a chunk, double-buffered (chunk c uses set c & 1, while one wave
   // computes chunk c+1's into the other set): [set][cum | ecum | scl | wv | atot]
@@ -224,6 +232,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   // thread's x piece back from the x tile (which only this thread rewrites, at
   // the next stage) instead of keeping it in registers
   constexpr bool kLean = P == 32;
+  // At P = 64, chunk c's M X, Y store and epilogue run in chunk c+1 (after its
+  // C S_in, in the same phase as B C^T and the state update), so a chunk has two
+  // barriers; the decay terms of chunk c+1 are then computed in chunk c's second
+  // phase, from a dt loaded one chunk earlier
+  constexpr bool kDefer = P == 64;
 
   struct Pf {
     uint4 x, z;
@@ -259,7 +272,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       f.cq[r] = ld16(Cb + o, ok);
     }
     if (w == kDtWave) {
-      const int64_t t = t0 + lane;
+      const int64_t t = t0 + (kDefer ? kQ : 0) + lane;
       f.dt = t < Lq ? (uint32_t)dtb[t * H] : 0u;
     }
   };
@@ -314,10 +327,55 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     if (lane == 0) o[4 * kQ] = __expf(tot);
   };
 
+  // Y += M X over a Y tile's causal k range, then the tile to LDS (token-major)
+  auto mx_store = [&](f32x16& acc, const uint16_t* Mb, const uint16_t* Xb) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (yi == 0 && s >= 2) break;                 // rows 0..31 see tokens 0..31 only
+      acc = mfma(lds_b8(Mb + (yi * 32 + l32) * kRowQ + 16 * s + 8 * h32), lds_opnd_tr(Xb, kRowP, 16 * s, yp * 32, lane),
+                 acc);
+    }
+    const int p = yp * 32 + l32;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = acc[4 * q + r];
+  };
+  // token xj, channels xp8 .. +7 of chunk ce: y = Y + D x, gate, store (x from the
+  // thread's registers, or its own piece of the x tile Xb)
+  auto epilogue = [&](int64_t ce, const uint16_t* Xb, uint4 xreg, uint4 zreg) {
+    const int64_t t = ce * kQ + xj;
+    if (has_x && t < Lq) {
+      const float4 y0 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8);
+      const float4 y1 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4);
+      const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      const uint4 xe = (kLean || kDefer) ? *reinterpret_cast<const uint4*>(Xb + xj * kRowP + xp8) : xreg;
+      const uint32_t xw[4] = {xe.x, xe.y, xe.z, xe.w};
+      const uint32_t zw[4] = {zreg.x, zreg.y, zreg.z, zreg.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v0 = fmaf(Dh, bf(xw[q] & 0xffffu), yv[2 * q]);
+        float v1 = fmaf(Dh, bf(xw[q] >> 16), yv[2 * q + 1]);
+        if (zb) {
+          v0 *= silu(bf(zw[q] & 0xffffu));
+          v1 *= silu(bf(zw[q] >> 16));
+        }
+        o[q] = pack_bf16x2(v0, v1);
+      }
+      *reinterpret_cast<uint4*>(yb + t * xs_t + xp8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  };
+
   Pf pf;
   prefetch(0, pf);
-  uint4 xcur, zcur;
-  if (w == kDtWave) dt_terms(pf.dt, 0, 0);
+  uint4 xcur, zcur, zprev = make_uint4(0, 0, 0, 0);
+  f32x16 yprev = {};   // chunk c-1's C S_in, waiting for its M X (kDefer)
+  if (w == kDtWave) {
+    uint32_t dt0 = pf.dt;
+    if constexpr (kDefer) dt0 = lane < Lq ? (uint32_t)dtb[(int64_t)lane * H] : 0u;
+    dt_terms(dt0, 0, 0);
+  }
   lds_barrier();   // chunk 0's decay terms, read at its stage
 
   for (int64_t c = 0; c < nchunk; ++c) {
@@ -330,7 +388,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     } else {
       zcur = pf.z;
     }
-    if (has_x) *reinterpret_cast<uint4*>(Xtm + xj * kRowP + xp8) = pf.x;
+    uint16_t* const Xc = Xtm + (kDefer ? (int)(c & 1) * L::kXtm : 0);   // this chunk's x and M tiles
+    uint16_t* const Mc = Ms + (kDefer ? (int)(c & 1) * L::kMs : 0);
+    uint16_t* const Xprev = Xtm + (kDefer ? (int)((c + 1) & 1) * L::kXtm : 0);   // chunk c-1's
+    uint16_t* const Mprev = Ms + (kDefer ? (int)((c + 1) & 1) * L::kMs : 0);
+    if (has_x) *reinterpret_cast<uint4*>(Xc + xj * kRowP + xp8) = pf.x;
 #pragma unroll
     for (int r = 0; r < kBCr; ++r) {
       const int e = tid + kNT * r;
@@ -357,7 +419,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     lds_barrier();
 
     // ---- A2: next loads; G -> M (waves 0-2); C S_in (waves 4-7); state update ----
+    const uint32_t dt_next = pf.dt;   // kDefer: chunk c+1's dt, loaded during chunk c-1
     if (c + 1 < nchunk) prefetch(c + 1, pf);
+    if constexpr (kDefer) {
+      if (has_y && c > 0) mx_store(yprev, Mprev, Xprev);   // chunk c-1's Y, read after this phase
+    }
     f32x16 yacc = {};
     if (w < 3) {
       // G^T tile (rows j-block jb, columns i-block ib) over N, two accumulation chains
@@ -386,7 +452,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         for (int r = 0; r < 4; ++r)
           m4[r] = (j0 + r <= i) ? (P == 64 ? g0[4 * q + r] + g1[4 * q + r] : g0[4 * q + r]) * __expf(ci - cja[r]) * wja[r]
                                 : 0.0f;
-        *reinterpret_cast<uint2*>(Ms + i * kRowQ + j0) = make_uint2(pack_bf16x2(m4[0], m4[1]), pack_bf16x2(m4[2], m4[3]));
+        *reinterpret_cast<uint2*>(Mc + i * kRowQ + j0) = make_uint2(pack_bf16x2(m4[0], m4[1]), pack_bf16x2(m4[2], m4[3]));
       }
     } else if (has_y) {
       // C S_in over N (two chains), rows scaled by exp(cum_i)
@@ -418,49 +484,35 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
       }
     }
-    lds_barrier();
-
-    // ---- A3: Y += M x (waves 4-7) -> Yf; S -> LDS for the next chunk's C S_in ----
-    if (has_y) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (yi == 0 && s >= 2) break;                 // rows 0..31 see tokens 0..31 only
-        yacc = mfma(lds_b8(Ms + (yi * 32 + l32) * kRowQ + 16 * s + 8 * h32),
-                    lds_opnd_tr(Xtm, kRowP, 16 * s, yp * 32, lane), yacc);
-      }
-      const int p = yp * 32 + l32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = yacc[4 * q + r];
+    if constexpr (kDefer) {
+      if (w == kDtWave && c + 1 < nchunk) dt_terms(dt_next, t0 + kQ, dset ^ 1);   // the next chunk's
     }
-    if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
-    write_ST();
     lds_barrier();
 
-    // ---- epilogue: token xj, channels xp8 .. +7: y = Y + D x, gate, store ----
-    {
-      const int64_t t = t0 + xj;
-      if (has_x && t < Lq) {
-        const float4 y0 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8);
-        const float4 y1 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4);
-        const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-        const uint4 xe = kLean ? *reinterpret_cast<const uint4*>(Xtm + xj * kRowP + xp8) : xcur;
-        const uint32_t xw[4] = {xe.x, xe.y, xe.z, xe.w};
-        const uint32_t zw[4] = {zcur.x, zcur.y, zcur.z, zcur.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float v0 = fmaf(Dh, bf(xw[q] & 0xffffu), yv[2 * q]);
-          float v1 = fmaf(Dh, bf(xw[q] >> 16), yv[2 * q + 1]);
-          if (zb) {
-            v0 *= silu(bf(zw[q] & 0xffffu));
-            v1 *= silu(bf(zw[q] >> 16));
-          }
-          o[q] = pack_bf16x2(v0, v1);
-        }
-        *reinterpret_cast<uint4*>(yb + t * xs_t + xp8) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+    if constexpr (!kDefer) {
+      // ---- A3: Y += M x (waves 4-7) -> Yf; S -> LDS for the next chunk's C S_in ----
+      if (has_y) mx_store(yacc, Mc, Xc);
+      if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
+      write_ST();
+      lds_barrier();
+      // ---- epilogue ----
+      epilogue(c, Xc, xcur, zcur);
+    } else {
+      // ---- S -> LDS for the next chunk's C S_in; chunk c-1's epilogue ----
+      write_ST();
+      if (c > 0) epilogue(c - 1, Xprev, xcur, zprev);
+      yprev = yacc;
+      zprev = zcur;
+    }
+  }
+  if constexpr (kDefer) {
+    if (nchunk > 0) {   // the last chunk's M X and epilogue
+      const int64_t cl = nchunk - 1;
+      uint16_t* const Xl = Xtm + (int)(cl & 1) * L::kXtm;
+      lds_barrier();   // the previous epilogue has read Y
+      if (has_y) mx_store(yprev, Ms + (int)(cl & 1) * L::kMs, Xl);
+      lds_barrier();
+      epilogue(cl, Xl, xcur, zprev);
     }
   }
 
