@@ -116,11 +116,11 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  * Same as mamba_scan_fwd with two explicit launch choices (0 = automatic):
  *   nchunks          number of time chunks scanned in parallel, joined by an
  *                    inter-chunk carry of the state (1 = one sequential pass);
- *                    chunks are whole tiles of 32 tokens, and a request for
+ *                    chunks are whole tiles of 64 tokens, and a request for
  *                    more chunks than tiles is reduced to one chunk per tile.
- *   states_per_wave  states held per lane: 2 (eight waves per workgroup, two
- *                    per SIMD; the automatic choice) or 4 (four waves; only
- *                    for dstate <= 16, otherwise MAMBA_SCAN_ERR_UNSUPPORTED).
+ *   states_per_wave  states held per lane: 0 or 2 (eight waves per workgroup,
+ *                    two per SIMD, the only layout); any other value returns
+ *                    MAMBA_SCAN_ERR_UNSUPPORTED.
  * The result is the same function; only rounding order differs.  The
  * workspace must be at least mamba_scan_fwd_workspace_size_ex(...) bytes.
  * Used for testing the chunked path at small sizes and for tuning.

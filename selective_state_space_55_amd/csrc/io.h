@@ -235,6 +235,29 @@ __device__ __forceinline__ float softplus_log2e(float x) {
   return fmaf(fmaxf(x, 0.0f), kLog2e, l);
 }
 
+// The decrement of a decay, m = Abar - 1 = expm1(x) with x = y ln 2, from the
+// base-2 exponent y = Delta A log2(e) and ab = 2^y (the hardware exp2).
+// Abar - 1 alone carries exp2's absolute rounding error (a few 1e-8), which is
+// a large relative error of m once |x| is small, and over the ~1/|x| steps a
+// state remembers its input that error adds up (State space models and Mamba,
+// jonathanding.github.io, §4: a small step keeps the state for a long time).
+// For x <= 0 two upper bounds of expm1(x) are taken and the smaller kept:
+//   x + x^2/2 (Taylor remainder x^3/6 e^xi < 0), relative error x^2/6;
+//   ab - 1 + 2^-23 (exp2 within two units in the last place below 1).
+// The smaller is within ~2e-5 relative of expm1(x) for every x <= 0, and is
+// exactly 0 at x = 0 (Delta = 0 leaves the state unchanged).  kAnySign: y may
+// be positive (Delta without softplus); there x + x^2/2 is a lower bound, and
+// the larger of it and ab - 1 - 2^-23 is taken.
+template <bool kAnySign>
+__device__ __forceinline__ float decay_m1(float y, float ab) {
+  constexpr float kC1 = 0.6931471805599453f;    // ln 2
+  constexpr float kC2 = 0.2402265069591007f;    // (ln 2)^2 / 2
+  const float p2 = y * fmaf(y, kC2, kC1);       // x + x^2 / 2
+  const float up = fminf(ab - 0.99999988079071044921875f, p2);   // ab - (1 - 2^-23)
+  if constexpr (!kAnySign) return up;
+  return fmaxf(up, ab - 1.00000011920928955078125f);            // ab - (1 + 2^-23)
+}
+
 // z * sigmoid(z) = z / (1 + 2^(-z log2e))
 __device__ __forceinline__ float silu(float z) {
   constexpr float kLog2e = 1.4426950408889634f;

@@ -169,8 +169,8 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const int64_t bd = b * a.dim + d;
   if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
 
-  // zero-order hold carries the scaled state A h: A h_t = Abar (A h_{t-1} + B u) - B u
-  // (one multiply fewer per step than h + B u / A); checkpoints store h = (A h) / A
+  // zero-order hold carries the scaled state A h: A h_t = A h + m (A h + B u), m = Abar - 1
+  // (one multiply fewer per step than h + m (h + B u / A)); checkpoints store h = (A h) / A
   float A[NPW], iA[NPW], h[NPW];
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -252,12 +252,13 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
         constexpr int kk = decltype(kk_c)::value;
         static_for<NPW>([&](auto j_c) {
           constexpr int j = decltype(j_c)::value;
-          const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
+          const float yv = dls[kk] * A[j];
+          const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
           if constexpr (kEuler) {
-            h[j] = fmaf(av, h[j], dpp_bcast_mul<4 * j + kk>(bq, uus[kk]));   // Abar h + B (Delta u)
+            h[j] += fmaf(m, h[j], dpp_bcast_mul<4 * j + kk>(bq, uus[kk]));   // h + (m h + B (Delta u))
           } else {
             const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk]);   // B u
-            h[j] = fmaf(av, h[j] + sv, -sv);
+            h[j] = fmaf(m, h[j] + sv, h[j]);                           // A h + m (A h + B u)
           }
         });
       });
@@ -438,7 +439,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     //      then sweep it backwards ----
 #pragma unroll 1
     for (int s = 3; s >= 0; --s) {
-      // per token and state: h_t, Abar, e = (Abar - 1) / A and B u, kept for the sweep
+      // per token and state: h_t, m = Abar - 1, e = (Abar - 1) / A and B u, kept for the sweep
       float hb[NPW], hh[kSub][NPW], ha[kSub][NPW], he[kSub][NPW], hbu[kSub][NPW];
       {
         const float2 q = *reinterpret_cast<const float2*>(hbuf + ((s * 8 + w) * 64 + lane) * NPW);
@@ -459,13 +460,14 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             static_for<NPW>([&](auto j_c) {
               constexpr int j = decltype(j_c)::value;
               constexpr int t = 4 * gq + kk;
-              const float av = __builtin_amdgcn_exp2f(dls[kk] * A[j]);
+              const float yv = dls[kk] * A[j];
+              const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
               // Bbar = e B: e = (Abar - 1) / A (zero-order hold) or Delta (Euler)
-              const float e = kEuler ? dls[kk] * kLn2 : fmaf(av, iA[j], -iA[j]);
+              const float e = kEuler ? dls[kk] * kLn2 : m * iA[j];
               const float bu = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk]);   // B u
-              h[j] = fmaf(av, h[j], e * bu);
+              h[j] += fmaf(m, h[j], e * bu);                               // h + (m h + e B u)
               hh[t][j] = h[j];
-              ha[t][j] = av;
+              ha[t][j] = m;
               he[t][j] = e;
               hbu[t][j] = bu;
               acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
@@ -501,9 +503,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             constexpr int j = decltype(j_c)::value;
             constexpr int src = 4 * j + kk;               // lane of the row holding (state j, token kk)
             const float hp = (t > 0) ? hh[t > 0 ? t - 1 : 0][j] : hb[j];
-            const float av = ha[t][j];
-            const float l = dpp_bcast_fmac<src>(g[j], bq.y, dys[kk]);   // lam_t = dytil C + Abar lam_{t+1}
-            g[j] = av * l;                                              // Abar_t lam_t, for token t-1
+            const float mt = ha[t][j];                                  // Abar_t - 1
+            const float cdy = dpp_bcast_mul<src>(bq.y, dys[kk]);        // dytil C
+            const float l = g[j] + cdy;                                 // lam_t = dytil C + Abar lam_{t+1}
+            // Abar_t lam_t = Abar lam_{t+1} + (dytil C + m lam_t), for token t-1: the small increment
+            // is formed first, so its rounding onto g's grid varies with dytil C from token to token
+            g[j] += fmaf(mt, l, cdy);
             const float bu = hbu[t][j];                                 // B u
             const float le = l * he[t][j];                              // l e
             if constexpr (kEuler) {

@@ -10,10 +10,8 @@
 // final state) are written back.
 //
 // Mapping.  A workgroup owns 64 channels of one batch row and all 16 states
-// of each, held in VGPRs and scanned sequentially in time, tile by tile (32
-// tokens).  Two layouts: (a) four states per lane, 4 waves: wave w holds
-// states 4w .. 4w+3 of all 64 channels, one channel per lane (one wave per
-// SIMD); (b) two states per lane, 8 waves (two per SIMD), described above
+// of each, held in VGPRs and scanned sequentially in time, tile by tile (64
+// tokens): two states per lane, 8 waves (two per SIMD), described above
 // scan_fwd_h2_kernel.  Three stages touch every tile:
 //   stage    -- convert the tile's delta/u rows (16-byte buffer loads), compute
 //               Delta*log2e = softplus(delta+bias)*log2e once per token-channel,
@@ -29,12 +27,10 @@
 // across tiles inside one instruction stream: while a wave
 // scans tile k it also finishes tile k-1's epilogue and stages tile k+1, and
 // the global loads of tile k+2 are in flight.  That work sits inside the
-// scan's group loop, so the compiler interleaves it with the recurrence.  LDS
-// holds two copies of the staged inputs and of the partial readouts; one
-// barrier per tile.
-// Inner step per (token, state): Abar = 2^(Delta*log2e * A); s = B u / A;
-// h = Abar (h + s) - s  (= Abar h + (Abar - 1)/A B u);  y += C h.  Six VALU
-// instructions and one exp per (token, state), two of them with a DPP operand.
+// scan's group loop, so the compiler interleaves it with the recurrence.
+// Inner step per (token, state): y = Delta*log2e * A; m = 2^y - 1 (decay_m1,
+// accurate for small Delta |A|); s = B u / A; h = h + m (h + s)
+// (= Abar h + (Abar - 1)/A B u);  y += C h.
 //
 // Time chunks.  When batch x channel groups cannot fill the GPU (e.g. one
 // batch row of 2048 channels and a million tokens) the sequence is cut into
@@ -50,421 +46,6 @@
 
 namespace mscan {
 namespace {
-
-template <int NPW, int NSPLIT, int T, bool kAgg>
-struct Lds {
-  static constexpr int kRow = T + kPad;
-  static constexpr int kNp = NPW * NSPLIT;
-  static constexpr int kDU = 2 * kCh * kRow;            // Delta or u, two tiles
-  static constexpr int kBC = 2 * (T / 4) * kNp * 8;     // B/C pairs, two tiles
-  static constexpr int kPar = 2 * kCh;                  // bias, D
-  static constexpr int kY = kAgg ? 0 : 2 * NSPLIT * kCh * kRow;   // partial readouts, two tiles
-  static constexpr int kFloats = 2 * kDU + kBC + kPar + kY;
-};
-
-template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg, bool kVec, int kMode>
-__global__ __launch_bounds__(NSPLIT * 64) void scan_fwd_kernel(KArgs a) {
-  using IO = Io<IoT>;
-  using V8 = typename IO::V8;
-  using V4 = typename IO::V4;
-  using L = Lds<NPW, NSPLIT, T, kAgg>;
-  constexpr int NT = NSPLIT * 64;       // threads
-  constexpr int kRow = L::kRow;
-  constexpr int NP = L::kNp;            // padded state count (== a.np)
-  constexpr int kG = T / 4;             // 4-token groups per tile
-  constexpr int kPieces = kCh * T / 8;  // 8-token pieces of Delta/u/z per tile
-  constexpr int CPT = (kPieces + NT - 1) / NT;
-  constexpr bool kAllBusy = (kPieces % NT) == 0;
-  constexpr int kBCPieces = 2 * NP * kG;        // (B or C, state, 4-token group) pieces per tile
-  constexpr int BPT = (kBCPieces + NT - 1) / NT;
-  constexpr bool kBCAllBusy = (kBCPieces % NT) == 0;
-  constexpr int CK = kAgg ? 1 : CPT;    // u/z kept from staging to the epilogue (output pass only)
-  constexpr int kEsz = (int)sizeof(IoT);
-  constexpr float kLog2e = 1.4426950408889634f;
-  constexpr float kLn2 = 0.6931471805599453f;
-  constexpr bool kSp = (kMode & kModeSoftplus) != 0;
-  constexpr bool kEuler = (kMode & kModeEuler) != 0;
-  static_assert(kG >= 4, "the pipeline places work in groups 0..3");
-
-  extern __shared__ float smem[];
-  float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
-  float* ubuf = dbuf + L::kDU;             // [2][64][kRow]  u
-  float* bcs = ubuf + L::kDU;              // [2][kG][4 tokens][NP][B, C]
-  float* par = bcs + L::kBC;               // [2][64]        bias, D
-  float* ypart = par + L::kPar;            // [2][NSPLIT][64][kRow] partial readouts (output pass only)
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  int64_t wid = work_id(blockIdx.x, a.nwork);
-  const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
-  const int64_t kc = wid % nck;
-  wid /= nck;
-  const int64_t cg = wid % a.chgroups;
-  const int64_t b = wid / a.chgroups;
-  const int64_t d0 = cg * kCh;
-  const int64_t t_begin = kc * a.chunk_len;
-  const int64_t t_end = min(t_begin + a.chunk_len, a.seqlen);   // valid tokens of this chunk
-  const int64_t ntile = (t_end - t_begin + T - 1) / T;
-
-  const IoT* __restrict__ gu = static_cast<const IoT*>(a.u);
-  const IoT* __restrict__ gd = static_cast<const IoT*>(a.delta);
-  const IoT* __restrict__ gz = static_cast<const IoT*>(a.z);
-  const IoT* __restrict__ gB = static_cast<const IoT*>(a.B);
-  const IoT* __restrict__ gC = static_cast<const IoT*>(a.C);
-  IoT* __restrict__ gy = static_cast<IoT*>(a.y);
-
-  if (tid < kCh) {
-    const int64_t dd = d0 + tid;
-    const bool ok = dd < a.dim;
-    par[tid] = (ok && a.bias) ? a.bias[dd] : 0.0f;
-    par[kCh + tid] = (ok && a.D) ? a.D[dd] : 0.0f;
-  }
-
-  // ---- per-lane constants and state ----
-  const int64_t d = d0 + lane;
-  const bool ch_ok = d < a.dim;
-  const int64_t bd = b * a.dim + d;
-  float A[NPW], iA[NPW], h[NPW];
-#pragma unroll
-  for (int j = 0; j < NPW; ++j) {
-    const int n = w * NPW + j;
-    const bool valid = ch_ok && n < a.dstate;
-    const float An = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
-    A[j] = An;
-    iA[j] = valid ? 1.0f / An : 0.0f;
-    float hv = 0.0f;
-    if (!kAgg && valid) {
-      if (kc > 0)
-        hv = a.carry[(bd * a.nchunks + kc) * a.np + n];   // carried-in state of this chunk
-      else if (a.h0)
-        hv = a.h0[bd * a.dstate + n];
-    }
-    h[j] = hv;
-  }
-  float dsum_acc = 0.0f;
-  const bool gate_on = a.gated != 0;
-  // gate factor = SiLU(z) + gate_off: ungated calls read z as zero, and SiLU(0) = 0
-  const float gate_off = gate_on ? 0.0f : 1.0f;
-
-  // ---- buffer descriptors ----
-  // Each covers exactly this workgroup's valid rows, so loads of rows past dim
-  // (and of bytes past a tensor's end) read zero and stores there are dropped,
-  // without branches.  Tokens past the chunk end read neighbouring data and are
-  // zeroed when staged.
-  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
-  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
-  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
-  const int nrec_bc = (int)((int64_t)a.dstate * a.seqlen * kEsz);
-  const __amdgpu_buffer_rsrc_t rs_u = make_rsrc(gu + row0, nrec_ch);
-  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
-  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(gate_on ? gz + row0 : gu + row0, gate_on ? nrec_ch : 0);
-  const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, nrec_bc);
-  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(gC + b * a.dstate * a.seqlen, nrec_bc);
-
-  struct Pf {   // one tile's global data, in flight until staged
-    V8 d[CPT], u[CPT], z[CK];
-    V4 bc[BPT];
-  };
-  struct Keep {   // one tile's u (fp32) and z, from staging to the epilogue
-    float u[CK][8];
-    V8 z[CK];
-  };
-
-  auto prefetch = [&](int64_t tile, Pf& p) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = min(tid + c * NT, kPieces - 1);   // idle threads re-load a valid piece
-      const int ch = e / (T / 8);
-      const int c8 = e % (T / 8);
-      const int off = (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz);
-      p.d[c] = IO::buf_load8(rs_d, off, kVec);
-      p.u[c] = IO::buf_load8(rs_u, off, kVec);
-      if constexpr (!kAgg) p.z[c] = IO::buf_load8(rs_z, off, kVec);
-    }
-#pragma unroll
-    for (int c = 0; c < BPT; ++c) {
-      const int e = min(tid + c * NT, kBCPieces - 1);
-      const int g = e % kG;
-      const int n = (e / kG) % NP;
-      const int off = (int)(((int64_t)n * a.seqlen + tile + g * 4) * kEsz);
-      // B rows fill whole waves, then C rows: the choice is uniform per wave
-      static_assert((NP * kG) % 64 == 0, "B/C pieces must fill whole waves");
-      const bool isB = __builtin_amdgcn_readfirstlane(e / (NP * kG)) == 0;
-      p.bc[c] = IO::buf_load4(isB ? rs_B : rs_C, off, kVec);
-    }
-  };
-
-  // stage: tile -> LDS buffer `buf` (Delta*log2e, u, B/C), and u/z into kp
-  auto stage = [&](int64_t tile, const Pf& p, int buf, Keep& kp, auto full_c) {
-    constexpr bool kFull = decltype(full_c)::value;   // every token of the tile is valid
-    float* dw = dbuf + buf * kCh * kRow;
-    float* uw = ubuf + buf * kCh * kRow;
-    float* bw = bcs + buf * kG * NP * 8;
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int e = tid + c * NT;
-      if (!kAllBusy && e >= kPieces) break;
-      const int ch = e / (T / 8);
-      const int c8 = e % (T / 8);
-      const int nv = kFull ? 8 : (int)max((int64_t)0, min((int64_t)8, t_end - (tile + c8 * 8)));   // valid tokens
-      float fd[8], fu[8];
-      IO::to_f32(p.d[c], fd);
-      IO::to_f32(p.u[c], fu);
-      const float bi = par[ch];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = fd[j] + bi;
-        const float dl = kSp ? softplus_log2e(x) : x * kLog2e;
-        const bool ok = j < nv;   // tokens past the chunk end: Delta = 0, u = 0 leave h unchanged
-        fd[j] = ok ? dl : 0.0f;
-        fu[j] = ok ? fu[j] : 0.0f;
-      }
-      float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
-#pragma unroll
-      for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
-      float* dp = dw + ch * kRow + c8 * 8;
-      float* up = uw + ch * kRow + c8 * 8;
-      reinterpret_cast<float4*>(dp)[0] = make_float4(fd[0], fd[1], fd[2], fd[3]);
-      reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
-      reinterpret_cast<float4*>(up)[0] = make_float4(fs[0], fs[1], fs[2], fs[3]);
-      reinterpret_cast<float4*>(up)[1] = make_float4(fs[4], fs[5], fs[6], fs[7]);
-      if constexpr (!kAgg) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kp.u[c][j] = fu[j];
-        kp.z[c] = p.z[c];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < BPT; ++c) {
-      const int e = tid + c * NT;
-      if (!kBCAllBusy && e >= kBCPieces) break;
-      const int g = e % kG;
-      const int n = (e / kG) % NP;
-      const int which = e / (NP * kG);   // 0: B, 1: C
-      const int nv = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + g * 4)));
-      float f[4];
-      IO::to_f32(p.bc[c], f);
-      // (group, token, state) holds the pair (B, C)
-      float* q = bw + (g * 4 * NP + n) * 2 + which;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nv) ? f[kk] : 0.0f;
-    }
-  };
-
-  // epilogue, in two halves: issue the partial-readout reads, then finish
-  struct Yp {
-    float4 v[CK][NSPLIT][2];
-  };
-  auto epi_read = [&](int ybuf, Yp& yp) {
-    const float* yr = ypart + ybuf * NSPLIT * kCh * kRow;
-#pragma unroll
-    for (int c = 0; c < CK; ++c) {
-      const int e = min(tid + c * NT, kPieces - 1);
-      const int ch = e / (T / 8);
-      const int c8 = e % (T / 8);
-#pragma unroll
-      for (int s2 = 0; s2 < NSPLIT; ++s2) {
-        const float4* ps = reinterpret_cast<const float4*>(yr + (s2 * kCh + ch) * kRow + c8 * 8);
-        yp.v[c][s2][0] = ps[0];
-        yp.v[c][s2][1] = ps[1];
-      }
-    }
-  };
-  auto epi_finish = [&](const Yp& yp, const Keep& kp, int c, float (&yv)[8]) {
-    const int e = min(tid + c * NT, kPieces - 1);
-    const int ch = e / (T / 8);
-    yv[0] = yp.v[c][0][0].x; yv[1] = yp.v[c][0][0].y; yv[2] = yp.v[c][0][0].z; yv[3] = yp.v[c][0][0].w;
-    yv[4] = yp.v[c][0][1].x; yv[5] = yp.v[c][0][1].y; yv[6] = yp.v[c][0][1].z; yv[7] = yp.v[c][0][1].w;
-#pragma unroll
-    for (int s2 = 1; s2 < NSPLIT; ++s2) {
-      yv[0] += yp.v[c][s2][0].x; yv[1] += yp.v[c][s2][0].y; yv[2] += yp.v[c][s2][0].z; yv[3] += yp.v[c][s2][0].w;
-      yv[4] += yp.v[c][s2][1].x; yv[5] += yp.v[c][s2][1].y; yv[6] += yp.v[c][s2][1].z; yv[7] += yp.v[c][s2][1].w;
-    }
-    const float Dd = par[kCh + ch];
-    float zf[8];
-    IO::to_f32(kp.z[c], zf);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      yv[j] = fmaf(Dd, kp.u[c][j], yv[j]) * (silu(zf[j]) + gate_off);
-    }
-  };
-  // full tile, output rows: branch-free stores (rows past dim and disabled
-  // descriptors drop the writes)
-  auto epi_store_full = [&](int64_t tile, int c, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
-    if (!kAllBusy && tid + c * NT >= kPieces) return;   // threads without a piece store nothing
-    const int e = tid + c * NT;
-    const int ch = e / (T / 8);
-    const int c8 = e % (T / 8);
-    const int off = (int)(((int64_t)ch * a.seqlen + tile + c8 * 8) * kEsz);
-    IO::buf_store8(rs, off, IO::from_f32(yv), kVec);
-  };
-  // any tile (the last one may be partial): guarded element stores
-  auto epi_store_tail = [&](int64_t tile, int c, const float (&yv)[8]) {
-    const int e = tid + c * NT;
-    if (!kAllBusy && e >= kPieces) return;
-    const int ch = e / (T / 8);
-    const int c8 = e % (T / 8);
-    const int64_t t0 = tile + c8 * 8;
-    int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
-    if (d0 + ch >= a.dim) nv = 0;
-    IO::store_n(gy + (b * a.dim + d0 + ch) * a.seqlen + t0, IO::from_f32(yv), nv);
-  };
-
-  // ---- the scan of one tile with the pipelined extra work ----
-  // Tile k, parity P: scan LDS buffer P into partial readouts P; finish the
-  // epilogue of tile k-1 (partials 1-P, keep kpOther); stage tile k+1 from
-  // pfOther into buffer 1-P and kpOther; issue the loads of tile k+2 into pfCur.
-  auto body = [&](int64_t k, auto P_c, Pf& pfCur, Pf& pfOther, Keep& kpOther) {
-    constexpr int P = decltype(P_c)::value;
-    const int64_t tile = t_begin + k * T;
-    const float* drow = dbuf + P * kCh * kRow + lane * kRow;
-    const float* urow = ubuf + P * kCh * kRow + lane * kRow;
-    const int sel = lane & 15;
-    const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + w * NPW + ((sel >> 2) % NPW)) * 2;
-    float* yrow = ypart + P * NSPLIT * kCh * kRow + (w * kCh + lane) * kRow;
-
-    float4 dv = *reinterpret_cast<const float4*>(drow);
-    float4 uv = *reinterpret_cast<const float4*>(urow);
-    float2 bcv = *reinterpret_cast<const float2*>(bcl);
-    Yp yp;
-    if constexpr (!kAgg) epi_read(1 - P, yp);
-    prefetch(tile + 2 * T, pfCur);
-    // the epilogue of tile k-1 stores only when there is such a tile
-    const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
-
-    auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
-      constexpr int kk = decltype(kk_c)::value;
-      float acc = 0.0f;
-      float av[NPW], sv[NPW];
-      // all DPP products first: a DPP result read by the next VALU
-      // instruction costs a wait state
-      static_for<NPW>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        constexpr int src = 4 * j + kk;   // lane of the row holding (state j, token kk)
-        av[j] = __builtin_amdgcn_exp2f(dl * A[j]);
-        if constexpr (kEuler)
-          sv[j] = dpp_bcast_mul<src>(bq.x, uu);                // s = B * Delta * u
-        else
-          sv[j] = dpp_bcast_mul<src>(bq.x, uu * iA[j]);        // s = B * u / A
-      });
-      static_for<NPW>([&](auto j_c) {
-        constexpr int j = decltype(j_c)::value;
-        constexpr int src = 4 * j + kk;
-        if constexpr (kEuler)
-          h[j] = fmaf(av[j], h[j], sv[j]);                     // Abar h + s
-        else
-          h[j] = fmaf(av[j], h[j] + sv[j], -sv[j]);            // Abar (h + s) - s
-        if constexpr (!kAgg) {
-          if constexpr (j == 0)
-            acc = dpp_bcast_mul<src>(bq.y, h[j]);              // C * h
-          else
-            acc = dpp_bcast_fmac<src>(acc, bq.y, h[j]);
-        }
-      });
-      return acc;
-    };
-
-#pragma unroll
-    for (int g = 0; g < kG; ++g) {
-      const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
-      __builtin_amdgcn_sched_barrier(0);
-      float4 dn = dv, un = uv;
-      float2 bcn = bcv;
-      if (g + 1 < kG) {
-        dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
-        un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
-        bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
-      const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
-      const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
-      if constexpr (!kAgg)
-        *reinterpret_cast<float4*>(yrow + 4 * g) = make_float4(y0, y1, y2, y3);
-      else
-        dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
-      // interleaved work of the neighbouring tiles
-      if constexpr (!kAgg) {
-        if (g == 1) {
-#pragma unroll
-          for (int c = 0; c < CK; ++c) {
-            float yv[8];
-            epi_finish(yp, kpOther, c, yv);
-            epi_store_full(tile - T, c, yv, rs_y);
-          }
-        }
-      }
-      if (g == 2) {
-        if (tile + 2 * T <= t_end)
-          stage(tile + T, pfOther, 1 - P, kpOther, IntC<1>{});
-        else
-          stage(tile + T, pfOther, 1 - P, kpOther, IntC<0>{});
-      }
-      if (g + 1 < kG) {
-        dv = dn;
-        uv = un;
-        bcv = bcn;
-      }
-    }
-    lds_barrier();
-  };
-
-  // final epilogue of tile k (after the barrier that follows its scan)
-  auto last_epilogue = [&](int64_t k, int P, const Keep& kp) {
-    if constexpr (!kAgg) {
-      Yp yp;
-      epi_read(P, yp);
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        float yv[8];
-        epi_finish(yp, kp, c, yv);
-        epi_store_tail(t_begin + k * T, c, yv);
-      }
-    }
-  };
-
-  Pf pf0, pf1;
-  Keep kp0 = {}, kp1 = {};
-  prefetch(t_begin, pf0);
-  prefetch(t_begin + T, pf1);
-  __syncthreads();   // par[] visible
-  stage(t_begin, pf0, 0, kp0, IntC<0>{});
-  lds_barrier();
-  for (int64_t k = 0; k < ntile; k += 2) {
-    body(k, IntC<0>{}, pf0, pf1, kp1);
-    if (k + 1 >= ntile) {
-      last_epilogue(k, 0, kp0);
-      break;
-    }
-    body(k + 1, IntC<1>{}, pf1, pf0, kp0);
-    if (k + 2 >= ntile) {
-      last_epilogue(k + 1, 1, kp1);
-      break;
-    }
-  }
-
-  // ---- final state or chunk aggregate ----
-  if (ch_ok) {
-    if (!kAgg) {
-      if (kc == a.nchunks - 1 && a.final_state) {
-#pragma unroll
-        for (int j = 0; j < NPW; ++j) {
-          const int n = w * NPW + j;
-          if (n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < NPW; ++j) {
-        const int n = w * NPW + j;
-        a.carry[(bd * a.nchunks + kc) * a.np + n] = h[j];
-      }
-      if (w == 0) a.dsum[bd * a.nchunks + kc] = dsum_acc;
-    }
-  }
-}
 
 // Folds the chunk aggregates in time order; leaves in carry[.., k, ..] the
 // state entering chunk k.  One thread per (batch, channel, state).
@@ -496,14 +77,6 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
   if (i < n) fs[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <int NPW, int NSPLIT, int T>
-struct PickNpw {
-  template <typename IoT, bool kAgg, bool kVec, int kMode>
-  struct P {
-    static auto get() { return scan_fwd_kernel<IoT, NPW, NSPLIT, T, kAgg, kVec, kMode>; }
-  };
-};
-
 template <bool kMulti>
 struct PickH2 {
   template <typename IoT, bool kAgg, bool kVec, int kMode>
@@ -518,16 +91,6 @@ struct PickH2Conv {
     static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, false, false, true>; }
   };
 };
-
-template <typename IoT, int NPW, int NSPLIT, int T, bool kAgg>
-hipError_t launch_scan(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = pick_kernel<PickNpw<NPW, NSPLIT, T>::template P, IoT, kAgg>(vec, k.mode);
-  const size_t lds = sizeof(float) * Lds<NPW, NSPLIT, T, kAgg>::kFloats;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NSPLIT * 64), lds, s, k);
-  return hipGetLastError();
-}
 
 template <typename IoT, bool kAgg>
 hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
@@ -545,8 +108,6 @@ hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s)
 
 template <typename IoT>
 hipError_t dispatch_scan(const KArgs& k, const FwdPlan& p, bool agg, bool vec, int64_t grid, hipStream_t s) {
-  if (p.npw == 4) return agg ? launch_scan<IoT, 4, 4, 32, true>(k, vec, grid, s)
-                             : launch_scan<IoT, 4, 4, 32, false>(k, vec, grid, s);
   return agg ? launch_scan_h2<IoT, true>(k, vec, grid, s) : launch_scan_h2<IoT, false>(k, vec, grid, s);
 }
 
@@ -612,17 +173,14 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
 
 bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t nchunks_req, int npw_req,
                    FwdPlan* p) {
-  if (npw_req != 0 && npw_req != 2 && npw_req != 4) return false;
+  if (npw_req != 0 && npw_req != 2) return false;   // one layout: two states per lane
   if (nchunks_req < 0) return false;
   if (dstate < 1 || dstate > 64) return false;
   p->ngroups = (int)((dstate + 15) / 16);
-  if (p->ngroups > 1 && npw_req == 4) return false;   // the four-states layout covers 16 states only
-  // two layouts: 4 states per lane x 4 waves with 32-token tiles, or 2 states
-  // per lane x 8 waves with 64-token tiles; states past dstate are padding that
-  // contributes exactly zero
-  p->npw = npw_req ? npw_req : 2;   // two waves per SIMD hide more stalls (measured faster at all shapes)
-  p->tile = p->npw == 4 ? 32 : 64;
-  p->nsplit = p->npw == 4 ? 4 : 8;   // waves per workgroup
+  // states past dstate are padding that contributes exactly zero
+  p->npw = 2;
+  p->tile = 64;
+  p->nsplit = 8;   // waves per workgroup
   p->np = 16 * p->ngroups;
   const int64_t T = p->tile;
   const int64_t tiles = (seqlen + T - 1) / T;
@@ -639,7 +197,6 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   const int64_t tiles_per = (tiles + nch - 1) / nch;
   p->chunk_len = std::max<int64_t>(1, tiles_per) * T;
   p->nchunks = tiles > 0 ? (tiles + tiles_per - 1) / tiles_per : 1;
-  p->ws_bc = 0;
   p->ws_carry = 0;
   if (p->nchunks > 1)
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +

@@ -444,27 +444,39 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     }
     const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(gy + row0, k >= 1 ? nrec_ch : 0);
 
+    // The update is written with the decrement m = Abar - 1 of the decay (decay_m1):
+    //   zero-order hold  h_t = h + m (h + s),  s = B u / A   (= Abar h + (Abar - 1)/A B u),
+    //   Euler            h_t = h + (m h + s),  s = B Delta u.
+    // Rounding h + s costs eps |s| absolutely, but it is scaled by m, so the
+    // step stays accurate however small Delta |A| is (the form Abar (h + s) - s
+    // loses eps |B u / A| per token, without decay, when Delta |A| -> 0).  The
+    // small increment is formed before it meets h, so the one rounding onto h's
+    // grid varies with the input from token to token; adding a slowly varying
+    // m h to an h + s already on that grid would round the same way every token
+    // and drift.
     auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
       constexpr int kk = decltype(kk_c)::value;
-      const float av0 = __builtin_amdgcn_exp2f(dl * A[0]);
-      const float av1 = __builtin_amdgcn_exp2f(dl * A[1]);
+      const float y0 = dl * A[0];
+      const float y1 = dl * A[1];
+      const float m0 = decay_m1<!kSp>(y0, __builtin_amdgcn_exp2f(y0));
+      const float m1 = decay_m1<!kSp>(y1, __builtin_amdgcn_exp2f(y1));
       if constexpr (kEuler) {
         const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * Delta * u
         const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
-        h[0] = fmaf(av0, h[0], s0);                                 // Abar h + s
-        h[1] = fmaf(av1, h[1], s1);
+        h[0] += fmaf(m0, h[0], s0);                                 // h + (m h + s)
+        h[1] += fmaf(m1, h[1], s1);
       } else if constexpr (kAgg) {
         // the aggregate pass carries the scaled state A h (no readout needs h):
-        // A h_t = Abar (A h_{t-1} + B u) - B u, one multiply fewer per step
+        // A h_t = A h + m (A h + B u), one multiply fewer per step
         const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * u
         const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
-        h[0] = fmaf(av0, h[0] + s0, -s0);
-        h[1] = fmaf(av1, h[1] + s1, -s1);
+        h[0] = fmaf(m0, h[0] + s0, h[0]);
+        h[1] = fmaf(m1, h[1] + s1, h[1]);
       } else {
         const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);       // s = B * u / A
         const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
-        h[0] = fmaf(av0, h[0] + s0, -s0);                           // Abar (h + s) - s
-        h[1] = fmaf(av1, h[1] + s1, -s1);
+        h[0] = fmaf(m0, h[0] + s0, h[0]);                           // h + m (h + s)
+        h[1] = fmaf(m1, h[1] + s1, h[1]);
       }
       if constexpr (!kAgg) return dpp_bcast_fmac<4 + kk>(dpp_bcast_mul<kk>(bq.y, h[0]), bq.y, h[1]);   // C . h
       return 0.0f;

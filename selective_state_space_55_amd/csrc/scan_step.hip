@@ -14,6 +14,8 @@
 // a channel's lanes uses cross-lane adds in a fixed order, so results are
 // deterministic.  For d_state 16 (the common case) a variant lets lane q of
 // a channel's quad do the per-(batch, channel) scalar work of row q once.
+// The update is the forward scan's: h = h + m (h + B u / A) with the decay
+// decrement m = Abar - 1 formed accurately for small Delta |A| (decay_m1).
 #include "internal.h"
 #include "io.h"
 
@@ -118,16 +120,18 @@ __global__ __launch_bounds__(256) void scan_step_kernel(SArgs a) {
       const float du = (dl * 0.6931471805599453f) * xv[r];   // Delta u
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
-        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);           // Abar h + Delta B u
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
+        hs[r][j] += fmaf(m, hs[r][j], Bv[r][j] * du);   // h + (m h + Delta B u)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
         const float s = Bv[r][j] * (xv[r] * iA[j]);   // B u / A (zero for states past dstate)
-        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        hs[r][j] = fmaf(m, hs[r][j] + s, hs[r][j]);    // h + m (h + s)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     }
@@ -233,16 +237,18 @@ __global__ __launch_bounds__(256) void scan_step_quad_kernel(SArgs a) {
       const float du = (dl * 0.6931471805599453f) * xv;   // Delta u
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
-        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
+        hs[r][j] += fmaf(m, hs[r][j], Bv[r][j] * du);   // h + (m h + Delta B u)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
         const float s = Bv[r][j] * (xv * iA[j]);   // B u / A
-        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        hs[r][j] = fmaf(m, hs[r][j] + s, hs[r][j]);    // h + m (h + s)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     }
@@ -324,16 +330,18 @@ __global__ __launch_bounds__(256) void scan_step_rows_kernel(SArgs a) {
       const float du = (dl * 0.6931471805599453f) * xv;   // Delta u
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
-        hs[r][j] = fmaf(av, hs[r][j], Bv[r][j] * du);
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
+        hs[r][j] += fmaf(m, hs[r][j], Bv[r][j] * du);   // h + (m h + Delta B u)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float av = __builtin_amdgcn_exp2f(dl * An[j]);
+        const float yv = dl * An[j];
+        const float m = decay_m1<true>(yv, __builtin_amdgcn_exp2f(yv));
         const float s = Bv[r][j] * (xv * iA[j]);   // B u / A
-        hs[r][j] = fmaf(av, hs[r][j] + s, -s);
+        hs[r][j] = fmaf(m, hs[r][j] + s, hs[r][j]);    // h + m (h + s)
         acc = fmaf(Cv[r][j], hs[r][j], acc);
       }
     }

@@ -63,7 +63,7 @@ def test_fwd_validation_errors(lib):
     assert fwd(lib, dstate=0) == ESHAPE
     assert fwd(lib, seqlen=-1) == ESHAPE
     assert fwd(lib, dstate=65) == EUNSUP
-    assert fwd(lib, dstate=17, npw=4) == EUNSUP                # four-states layout: 16 states only
+    assert fwd(lib, npw=4) == EUNSUP                           # one layout: two states per lane
     assert fwd(lib, seqlen=1 << 24) == EUNSUP                 # 64 rows x L x 2 B must fit 31 bits
     assert fwd(lib, batch=1 << 40, dim=1 << 30) == ESHAPE       # size overflow
     assert fwd(lib, u=P + 1) == EALIGN                         # bf16 needs 2-byte alignment
@@ -90,9 +90,10 @@ def test_workspace_size(lib):
     # one sequential pass needs no workspace
     assert lib.mamba_scan_fwd_workspace_size(4, 4096, 16, 8192, 1) == 0
     # a chunked plan also carries (h_end, sum Delta) per chunk
-    one = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 1, 4)
-    four = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 4, 4)
+    one = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 1, 2)
+    four = lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 4, 2)
     assert four > one
+    assert lib.mamba_scan_fwd_workspace_size_ex(1, 64, 16, 4096, 1, 4, 4) == bad   # one layout
 
 
 def step(lib, state=P, x=P, dt=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, sp=1, y=P, batch=2, dim=64,

@@ -1,6 +1,5 @@
 """GPU parity of the Euler variant (Bbar u = Delta B u, MAMBA_SCAN_FLAG_EULER)
-against the fp64 oracle's Euler variant, through the C ABI: edge shapes in
-both lane layouts, the chunked carry path, decode steps, chained steps equal
+against the fp64 oracle's Euler variant, through the C ABI: edge shapes, the chunked carry path, decode steps, chained steps equal
 to one scan; same tolerances as the zero-order-hold tests."""
 import sys
 
@@ -25,11 +24,11 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-def gpu_fwd(inp, softplus=True, nchunks=0, npw=0, disc="euler"):
+def gpu_fwd(inp, softplus=True, nchunks=0, disc="euler"):
     a = {k: dev(v) for k, v in inp.items()}
     y, fs = mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
                            delta_bias=a["delta_bias"], initial_state=a["initial_state"], delta_softplus=softplus,
-                           return_final_state=True, nchunks=nchunks, states_per_wave=npw, discretization=disc)
+                           return_final_state=True, nchunks=nchunks, discretization=disc)
     torch.cuda.synchronize()
     return y.cpu(), fs.cpu()
 
@@ -58,15 +57,14 @@ EDGE = [
 
 
 @pytest.mark.parametrize("case", EDGE, ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}" for c in EDGE])
-@pytest.mark.parametrize("npw", [4, 2])
-def test_euler_edge_shapes(case, npw):
+def test_euler_edge_shapes(case):
     b, d, n, L, io, gated, h0, sp = case
     inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, initial_state=h0, seed=L + d)
     if not sp:
         inp["delta"] = (inp["delta"].float().abs() * 0.05).to(inp["delta"].dtype)
         inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
-    say(f"edge {case} npw={npw}")
-    y, fs = gpu_fwd(inp, softplus=sp, nchunks=1, npw=npw)
+    say(f"edge {case}")
+    y, fs = gpu_fwd(inp, softplus=sp, nchunks=1)
     yr, fsr = oracle_fwd(inp, softplus=sp)
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])
@@ -74,11 +72,10 @@ def test_euler_edge_shapes(case, npw):
 
 @pytest.mark.parametrize("nchunks", [2, 5])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("npw", [4, 2])
-def test_euler_chunked_carry(nchunks, io, npw):
+def test_euler_chunked_carry(nchunks, io):
     inp = forward_inputs(batch=2, dim=96, dstate=16, seqlen=3001, io=io, initial_state=True, seed=nchunks)
-    say(f"chunked nchunks={nchunks} io={io} npw={npw}")
-    y, fs = gpu_fwd(inp, nchunks=nchunks, npw=npw)
+    say(f"chunked nchunks={nchunks} io={io}")
+    y, fs = gpu_fwd(inp, nchunks=nchunks)
     yr, fsr = oracle_fwd(inp)
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])

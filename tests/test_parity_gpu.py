@@ -32,11 +32,11 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-def gpu_fwd(inp, softplus=True, nchunks=0, npw=0):
+def gpu_fwd(inp, softplus=True, nchunks=0):
     a = {k: dev(v) for k, v in inp.items()}
     y, fs = mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
                            delta_bias=a["delta_bias"], initial_state=a["initial_state"], delta_softplus=softplus,
-                           return_final_state=True, nchunks=nchunks, states_per_wave=npw)
+                           return_final_state=True, nchunks=nchunks)
     torch.cuda.synchronize()
     return y.cpu(), fs.cpu()
 
@@ -81,15 +81,14 @@ EDGE = [
 
 @pytest.mark.parametrize("case", EDGE, ids=[f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}" + ("g" if c[5] else "")
                                             + ("" if c[9] else "-nosp") for c in EDGE])
-@pytest.mark.parametrize("npw", [4, 2])
-def test_edge_shapes_vs_oracle(case, npw):
+def test_edge_shapes_vs_oracle(case):
     b, d, n, L, io, gated, hasD, hasB, h0, sp = case
     inp = forward_inputs(batch=b, dim=d, dstate=n, seqlen=L, io=io, gated=gated, has_D=hasD, has_bias=hasB,
                          initial_state=h0, seed=L + d)
     if not sp:
         inp = positive_delta(inp)
-    say(f"edge {case} npw={npw}")
-    y, fs = gpu_fwd(inp, softplus=sp, nchunks=1, npw=npw)
+    say(f"edge {case}")
+    y, fs = gpu_fwd(inp, softplus=sp, nchunks=1)
     yr, fsr = oracle_fwd(inp, softplus=sp)
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])
@@ -97,15 +96,14 @@ def test_edge_shapes_vs_oracle(case, npw):
 
 @pytest.mark.parametrize("nchunks", [2, 5, 47])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("npw", [4, 2])
-def test_chunked_carry_vs_oracle(nchunks, io, npw):
+def test_chunked_carry_vs_oracle(nchunks, io):
     inp = forward_inputs(batch=2, dim=96, dstate=16, seqlen=3001, io=io, initial_state=True, seed=nchunks)
-    say(f"chunked nchunks={nchunks} io={io} npw={npw}")
-    y, fs = gpu_fwd(inp, nchunks=nchunks, npw=npw)
+    say(f"chunked nchunks={nchunks} io={io}")
+    y, fs = gpu_fwd(inp, nchunks=nchunks)
     yr, fsr = oracle_fwd(inp)
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])
-    y1, fs1 = gpu_fwd(inp, nchunks=1, npw=npw)
+    y1, fs1 = gpu_fwd(inp, nchunks=1)
     # same function, different rounding order only
     assert max_rel_err(y, y1.double()) <= (1e-5 if io == "f32" else 1e-2)
 
@@ -120,33 +118,31 @@ def test_seqlen_zero():
         assert torch.equal(fs, ref)
 
 
-@pytest.mark.parametrize("npw", [4, 2])
-def test_deterministic_repeat(npw):
+def test_deterministic_repeat():
     inp = forward_inputs(batch=2, dim=256, dstate=16, seqlen=777, io="bf16", initial_state=True)
-    say(f"determinism npw={npw}")
-    y1, f1 = gpu_fwd(inp, npw=npw)
-    y2, f2 = gpu_fwd(inp, npw=npw)
+    say("determinism")
+    y1, f1 = gpu_fwd(inp)
+    y2, f2 = gpu_fwd(inp)
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
-    y3, f3 = gpu_fwd(inp, nchunks=6, npw=npw)
-    y4, f4 = gpu_fwd(inp, nchunks=6, npw=npw)
+    y3, f3 = gpu_fwd(inp, nchunks=6)
+    y4, f4 = gpu_fwd(inp, nchunks=6)
     assert torch.equal(y3, y4) and torch.equal(f3, f4)
 
 
 @pytest.mark.parametrize("k", [1, 100, 128, 333])
-@pytest.mark.parametrize("npw", [4, 2])
-def test_split_resume_bitexact(k, npw):
+def test_split_resume_bitexact(k):
     """scan(0..L) == scan(0..k) followed by scan(k..L) from the returned state (same arithmetic)."""
     L = 600
     inp = forward_inputs(batch=2, dim=80, dstate=16, seqlen=L, io="f32", initial_state=True, seed=k)
-    say(f"split at {k} npw={npw}")
-    y, fs = gpu_fwd(inp, nchunks=1, npw=npw)
+    say(f"split at {k}")
+    y, fs = gpu_fwd(inp, nchunks=1)
     first = {kk: (v[..., :k].contiguous() if v is not None and v.dim() == 3 and v.shape[-1] == L else v)
              for kk, v in inp.items()}
     second = {kk: (v[..., k:].contiguous() if v is not None and v.dim() == 3 and v.shape[-1] == L else v)
               for kk, v in inp.items()}
-    y1, f1 = gpu_fwd(first, nchunks=1, npw=npw)
+    y1, f1 = gpu_fwd(first, nchunks=1)
     second["initial_state"] = f1
-    y2, f2 = gpu_fwd(second, nchunks=1, npw=npw)
+    y2, f2 = gpu_fwd(second, nchunks=1)
     assert torch.equal(torch.cat([y1, y2], dim=-1), y)
     assert torch.equal(f2, fs)
 

@@ -21,7 +21,7 @@ from .configs import Config, get_config
 
 # stream keys, fixed order
 (K_U, K_DELTA, K_Z, K_B, K_C, K_D, K_BIAS, K_STATE, K_STEPS, K_DY, K_DFS, K_CONVW, K_CONVB, K_CONVS,
- K_SSDA) = range(15)
+ K_SSDA, K_ALOG) = range(16)
 _BLOCK_ELEMS = 1 << 20
 
 
@@ -73,6 +73,20 @@ def a_log_s4d_real(dim: int, dstate: int) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(np.broadcast_to(row, (dim, dstate))).copy())
 
 
+def a_log_learned(seed: int, dim: int, dstate: int, lo: float = -6.0, hi: float = 3.0) -> torch.Tensor:
+    """float32 A_log ~ U[lo, hi] per (channel, state): a learned-range A_log (|A| = e^-6 .. e^3),
+    where the S4D-Real log(1..N) is only the initialisation."""
+    return torch.from_numpy(_gen(seed, (K_ALOG, 0)).uniform(lo, hi, size=(dim, dstate)).astype(np.float32))
+
+
+def make_a_log(a_log: str, seed: int, dim: int, dstate: int) -> torch.Tensor:
+    if a_log == "s4d":
+        return a_log_s4d_real(dim, dstate)
+    if a_log == "learned":
+        return a_log_learned(seed, dim, dstate)
+    raise ValueError(f"a_log must be 's4d' or 'learned', not {a_log!r}")
+
+
 def delta_bias_init(seed: int, dim: int, lo: float = 0.001, hi: float = 0.1) -> torch.Tensor:
     """float32(log(expm1(U[lo, hi]))) per channel: softplus of it is uniform on [lo, hi]."""
     uni = _gen(seed, (K_BIAS, 0)).uniform(lo, hi, size=dim)
@@ -82,12 +96,19 @@ def delta_bias_init(seed: int, dim: int, lo: float = 0.001, hi: float = 0.1) -> 
 def forward_inputs(cfg: Union[int, Config, None] = None, *, seed: int = 0, batch: int = None, dim: int = None,
                    dstate: int = None, seqlen: int = None, io: str = None, gated: bool = None,
                    has_D: bool = None, has_bias: bool = None, initial_state: bool = False,
+                   a_log: str = "s4d", bias_range=(0.001, 0.1), delta_std: float = 1.0,
                    threads: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
     """Inputs of one forward scan as CPU tensors.
 
     Either a config (index or Config) or explicit shape keywords (which override
     the config's values).  Keys: u, delta, z, B, C (io dtype), A_log, D,
     delta_bias (float32), initial_state (float32 or None).
+
+    Value regime (defaults: the workloads' distributions):
+      a_log       "s4d" (log(1..N) per channel) or "learned" (U[-6, 3] per (channel, state));
+      bias_range  softplus(delta_bias) ~ U[lo, hi] per channel; (1e-4, 2e-4) gives the
+                  Delta ~ 1/L initialisation of the Mamba notes (训练策略) at L ~ 8192;
+      delta_std   delta ~ N(0, delta_std^2); 0 makes delta exactly zero (Delta = softplus(bias)).
     """
     c = get_config(cfg) if isinstance(cfg, int) else cfg
     pick = lambda v, attr, dflt: v if v is not None else (getattr(c, attr) if c is not None else dflt)
@@ -101,37 +122,43 @@ def forward_inputs(cfg: Union[int, Config, None] = None, *, seed: int = 0, batch
     hasB = pick(has_bias, "has_bias", True)
     out: Dict[str, Optional[torch.Tensor]] = {}
     out["u"] = _normal_rows(seed, (K_U,), b * d, L, io_, threads=threads).view(b, d, L)
-    out["delta"] = _normal_rows(seed, (K_DELTA,), b * d, L, io_, threads=threads).view(b, d, L)
+    if delta_std == 0.0:
+        out["delta"] = torch.zeros((b, d, L), dtype=torch.float32 if io_ == "f32" else torch.bfloat16)
+    else:
+        out["delta"] = _normal_rows(seed, (K_DELTA,), b * d, L, io_, std=delta_std, threads=threads).view(b, d, L)
     out["z"] = _normal_rows(seed, (K_Z,), b * d, L, io_, threads=threads).view(b, d, L) if gated_ else None
     out["B"] = _normal_rows(seed, (K_B,), b * n, L, io_, threads=threads).view(b, n, L)
     out["C"] = _normal_rows(seed, (K_C,), b * n, L, io_, threads=threads).view(b, n, L)
-    out["A_log"] = a_log_s4d_real(d, n)
+    out["A_log"] = make_a_log(a_log, seed, d, n)
     out["D"] = torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(d, dtype=np.float32)) if hasD else None
-    out["delta_bias"] = delta_bias_init(seed, d) if hasB else None
+    out["delta_bias"] = delta_bias_init(seed, d, *bias_range) if hasB else None
     out["initial_state"] = (_normal_rows(seed, (K_STATE,), b * d, n, "f32", std=0.1, threads=threads)
                             .view(b, d, n) if initial_state else None)
     return out
 
 
 def step_initial(cfg: Union[int, Config, None] = None, *, seed: int = 0, batch: int = None, dim: int = None,
-                 dstate: int = None, threads: Optional[int] = None) -> Dict[str, torch.Tensor]:
-    """Decode-step state and parameters: state (b,d,n) fp32 ~ N(0, 0.1^2), A_log, D, dt_bias."""
+                 dstate: int = None, a_log: str = "s4d", bias_range=(0.001, 0.1),
+                 threads: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Decode-step state and parameters: state (b,d,n) fp32 ~ N(0, 0.1^2), A_log, D, dt_bias
+    (a_log and bias_range as in forward_inputs)."""
     c = get_config(cfg) if isinstance(cfg, int) else cfg
     b = batch if batch is not None else c.batch
     d = dim if dim is not None else c.dim
     n = dstate if dstate is not None else c.dstate
     return {
         "state": _normal_rows(seed, (K_STATE,), b * d, n, "f32", std=0.1, threads=threads).view(b, d, n),
-        "A_log": a_log_s4d_real(d, n),
+        "A_log": make_a_log(a_log, seed, d, n),
         "D": torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(d, dtype=np.float32)),
-        "dt_bias": delta_bias_init(seed, d),
+        "dt_bias": delta_bias_init(seed, d, *bias_range),
     }
 
 
 def step_inputs(cfg: Union[int, Config, None], k: int, *, seed: int = 0, batch: int = None, dim: int = None,
-                dstate: int = None, io: str = None, gated: bool = None,
+                dstate: int = None, io: str = None, gated: bool = None, dt_std: float = 1.0,
                 threads: Optional[int] = None) -> Dict[str, Optional[torch.Tensor]]:
-    """Fresh per-step inputs of decode step k: x, dt, z (b,d) and B, C (b,n) in the io dtype."""
+    """Fresh per-step inputs of decode step k: x, dt, z (b,d) and B, C (b,n) in the io dtype;
+    dt ~ N(0, dt_std^2) (0: exactly zero)."""
     c = get_config(cfg) if isinstance(cfg, int) else cfg
     b = batch if batch is not None else c.batch
     d = dim if dim is not None else c.dim
@@ -141,7 +168,8 @@ def step_inputs(cfg: Union[int, Config, None], k: int, *, seed: int = 0, batch: 
     key = (K_STEPS, int(k))
     return {
         "x": _normal_rows(seed, key + (0,), b, d, io_, threads=threads),
-        "dt": _normal_rows(seed, key + (1,), b, d, io_, threads=threads),
+        "dt": (_normal_rows(seed, key + (1,), b, d, io_, std=dt_std, threads=threads) if dt_std != 0.0
+               else torch.zeros((b, d), dtype=torch.float32 if io_ == "f32" else torch.bfloat16)),
         "z": _normal_rows(seed, key + (2,), b, d, io_, threads=threads) if g_ else None,
         "B": _normal_rows(seed, key + (3,), b, n, io_, threads=threads),
         "C": _normal_rows(seed, key + (4,), b, n, io_, threads=threads),
