@@ -2,13 +2,21 @@
 
 This module only marshals arguments: it checks torch tensors (device, dtype,
 contiguity, shape), allocates outputs and the workspace with torch, and calls
-the C ABI declared in include/mamba_scan.h on the current HIP stream.  Every
-step of the computation runs in the library's HIP kernels.  If the library is
-not built, importing works but every call raises; there is no fallback.
+the C ABI declared in include/mamba_scan.h.  Every step of the computation
+runs in the library's HIP kernels.  If the library is not built, importing
+works but every call raises; there is no fallback.
+
+Streams: each call runs on its `stream` argument (a torch stream or a raw HIP
+stream handle), or on the current stream when it is None.  Outputs and the
+workspace a call allocates are allocated while that stream is current, so
+torch's caching allocator hands their memory to no other stream's work before
+the kernels are done with it.  Tensors the caller passes in (inputs, `out=`,
+`workspace=`) are the caller's to keep alive and ordered with that stream.
 """
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Tuple
 
@@ -137,6 +145,25 @@ def _stream(device: torch.device, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
+def _on_stream(fn):
+    """Runs fn with its `stream` argument made the current stream, so that the outputs and workspace fn
+    allocates belong to the stream its kernels are enqueued on (a raw handle is wrapped as an
+    ExternalStream of the first argument's device)."""
+
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, stream=None, **kwargs)
+        t0 = args[0] if args else None
+        dev = t0.device if isinstance(t0, torch.Tensor) else torch.device("cuda", torch.cuda.current_device())
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream), device=dev)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+
+    return run
+
+
 def fwd_workspace_size(batch: int, dim: int, dstate: int, seqlen: int, io_dtype: int = BF16, nchunks: int = 0,
                        states_per_wave: int = 0) -> int:
     n = load_library().mamba_scan_fwd_workspace_size_ex(batch, dim, dstate, seqlen, io_dtype, nchunks,
@@ -146,6 +173,7 @@ def fwd_workspace_size(batch: int, dim: int, dstate: int, seqlen: int, io_dtype:
     return int(n)
 
 
+@_on_stream
 def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
              D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
@@ -199,6 +227,7 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
     return (y, fs) if return_final_state else y
 
 
+@_on_stream
 def scan_fwd_conv(x: torch.Tensor, conv_weight: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor,
                   B: torch.Tensor, C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                   delta_bias: Optional[torch.Tensor] = None, conv_bias: Optional[torch.Tensor] = None,
@@ -280,6 +309,7 @@ def fwd_varlen_workspace_size(nseq: int, dim: int, dstate: int, total_len: int, 
     return int(n)
 
 
+@_on_stream
 def scan_fwd_varlen(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
                     cu_seqlens: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
                     delta_bias: Optional[torch.Tensor] = None, initial_states: Optional[torch.Tensor] = None,
@@ -335,6 +365,7 @@ def scan_fwd_varlen(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B
     return (y, fs) if return_final_states else y
 
 
+@_on_stream
 def scan_step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor,
               C: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
               dt_bias: Optional[torch.Tensor] = None, dt_softplus: bool = True, *,
@@ -375,6 +406,7 @@ def bwd_workspace_size(batch: int, dim: int, dstate: int, seqlen: int, io_dtype:
     return int(n)
 
 
+@_on_stream
 def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
              dy: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
              delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
@@ -434,6 +466,7 @@ def scan_bwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
     return g
 
 
+@_on_stream
 def conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
                conv_state: Optional[torch.Tensor] = None, silu: bool = True, return_state: bool = False, *,
                out: Optional[torch.Tensor] = None, state_out: Optional[torch.Tensor] = None, stream=None):
@@ -466,6 +499,7 @@ def conv1d_fwd(x: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tenso
     return (u, so) if return_state else u
 
 
+@_on_stream
 def ssd_fwd(x: torch.Tensor, dt: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
             D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
             dt_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,

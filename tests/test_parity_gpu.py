@@ -326,3 +326,26 @@ def test_decode_2_8b_1024_steps_sampled():
     fg = st[bsd][:, dsd].cpu()
     check("c4 final state (sampled)", fg, ref_state, c.tol)
     say(f"decode-2.8b: worst per-step y error {worst:.3e}")
+
+
+def test_side_stream_allocations_follow_the_stream():
+    """Calls on a side stream (a torch stream, then a raw handle) allocate their outputs and workspace
+    on that stream; the chunked forward (workspace) and the backward (1 checkpoint workspace) stay
+    within tolerance of the oracle while the default stream allocates and writes in between."""
+    inp = forward_inputs(batch=1, dim=128, dstate=16, seqlen=3000, io="f32", initial_state=True, seed=9)
+    yr, fsr = oracle_fwd(inp)
+    a = {k: dev(v) for k, v in inp.items()}
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("side stream: torch stream and raw handle")
+    for s in (side, side.cuda_stream):
+        y, fs = mscan.scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], D=a["D"], z=a["z"],
+                               delta_bias=a["delta_bias"], initial_state=a["initial_state"],
+                               return_final_state=True, stream=s)
+        junk = torch.full((1 << 22,), 7.0, device=DEV)   # default-stream work reusing freed blocks
+        junk.mul_(3.0)
+        side.synchronize()
+        torch.cuda.synchronize()
+        check("y (side stream)", y.cpu(), yr, TOL["f32"])
+        check("final_state (side stream)", fs.cpu(), fsr, TOL["f32"])
+        del junk
