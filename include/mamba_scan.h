@@ -112,6 +112,34 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const v
  * Returns (size_t)-1 for sizes mamba_scan_fwd would reject. */
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
 
+/* Scratch held by the library for mamba_scan_fwd_noalloc: one array of this many
+ * bytes in each GPU's memory, from the first call on that GPU until the process ends. */
+#define MAMBA_SCAN_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * mamba_scan_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  It calls no hipMalloc, hipFree or other allocating routine:
+ * the chunk carry and the multi-pass readout sum live in a static device array of
+ * MAMBA_SCAN_NOALLOC_SCRATCH_BYTES bytes per GPU, whose device address is looked up
+ * once per device (on the first call with that device current).  The caller still
+ * passes every input and output; arguments, layouts, status codes and results are
+ * those of mamba_scan_fwd with the automatic launch plan (bit-identical results).
+ * The device is the current HIP device; the stream must belong to it.
+ *
+ * Limit: calls whose mamba_scan_fwd_workspace_size(...) exceeds
+ * MAMBA_SCAN_NOALLOC_SCRATCH_BYTES return MAMBA_SCAN_ERR_WORKSPACE and launch
+ * nothing (the chunk carry is at most ~4.3 MB for any size; a dstate > 16 call adds
+ * batch x dim x seqlen x 4 bytes).  Every call on one GPU shares that GPU's array
+ * and leaves its contents behind (each call writes what it reads, so nothing needs
+ * clearing): calls that overlap in time on one GPU -- on different streams or
+ * threads -- race on it and must be serialized by the caller.
+ */
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                           float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate,
+                           int64_t seqlen, int io_dtype, int flags, void* stream);
+
 /*
  * Same as mamba_scan_fwd with two explicit launch choices (0 = automatic):
  *   nchunks          number of time chunks scanned in parallel, joined by an

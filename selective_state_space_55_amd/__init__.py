@@ -32,7 +32,8 @@ STATUS = {
     7: "MAMBA_SCAN_ERR_HIP",
 }
 EXPORTED = (
-    "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_workspace_size", "mamba_scan_fwd_workspace_size_ex",
+    "mamba_scan_fwd", "mamba_scan_fwd_ex", "mamba_scan_fwd_noalloc", "mamba_scan_fwd_workspace_size",
+    "mamba_scan_fwd_workspace_size_ex",
     "mamba_scan_fwd_conv",
     "mamba_scan_fwd_varlen", "mamba_scan_fwd_varlen_workspace_size", "mamba_scan_step", "mamba_scan_bwd",
     "mamba_scan_bwd_workspace_size", "mamba_conv1d_fwd", "mamba_ssd_fwd", "mamba_scan_status_str",
@@ -59,6 +60,8 @@ def load_library():
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     lib.mamba_scan_fwd.restype = I
     lib.mamba_scan_fwd.argtypes = [P] * 11 + [I64] * 4 + [I, I, P, SZ, P]
+    lib.mamba_scan_fwd_noalloc.restype = I
+    lib.mamba_scan_fwd_noalloc.argtypes = [P] * 11 + [I64] * 4 + [I, I, P]
     lib.mamba_scan_fwd_ex.restype = I
     lib.mamba_scan_fwd_ex.argtypes = [P] * 11 + [I64] * 4 + [I, I, I64, I, P, SZ, P]
     lib.mamba_scan_fwd_workspace_size.restype = SZ
@@ -225,6 +228,46 @@ def scan_fwd(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch
                                _stream(dev, stream))
     _check("mamba_scan_fwd", rc)
     return (y, fs) if return_final_state else y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MAMBA_SCAN_NOALLOC_SCRATCH_BYTES
+
+
+@_on_stream
+def scan_fwd_noalloc(u: torch.Tensor, delta: torch.Tensor, A_log: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                     out: torch.Tensor, D: Optional[torch.Tensor] = None, z: Optional[torch.Tensor] = None,
+                     delta_bias: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                     final_state: Optional[torch.Tensor] = None, delta_softplus: bool = True,
+                     discretization: str = "zoh", stream=None) -> torch.Tensor:
+    """scan_fwd through mamba_scan_fwd_noalloc: the caller passes every output (out: y, and optionally
+    final_state) and nothing is allocated, by this function or the library (the chunk carry lives in
+    the library's static per-GPU scratch).  Calls that overlap in time on one GPU race on that scratch.
+    Returns out."""
+    lib = load_library()
+    if u.dim() != 3:
+        raise ValueError("u must be (batch, dim, L)")
+    batch, dim, L = u.shape
+    dev = u.device
+    if dev.type != "cuda":
+        raise ValueError("scan_fwd_noalloc needs device tensors (HIP)")
+    io = _io_dtype(u)
+    iot = u.dtype
+    dstate = A_log.shape[-1] if A_log.dim() == 2 else -1
+    for name, t, shape, dt in (("u", u, (batch, dim, L), iot), ("delta", delta, (batch, dim, L), iot),
+                               ("A_log", A_log, (dim, dstate), torch.float32), ("B", B, (batch, dstate, L), iot),
+                               ("C", C, (batch, dstate, L), iot), ("D", D, (dim,), torch.float32),
+                               ("z", z, (batch, dim, L), iot), ("delta_bias", delta_bias, (dim,), torch.float32),
+                               ("initial_state", initial_state, (batch, dim, dstate), torch.float32),
+                               ("out", out, (batch, dim, L), iot),
+                               ("final_state", final_state, (batch, dim, dstate), torch.float32)):
+        _req(name, t, shape, dt, dev)
+    if out is None:
+        raise ValueError("scan_fwd_noalloc needs out (y)")
+    rc = lib.mamba_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(delta_bias), _ptr(initial_state), _ptr(final_state), _ptr(out), batch, dim,
+                                    dstate, L, io, _flags(delta_softplus, discretization), _stream(dev, stream))
+    _check("mamba_scan_fwd_noalloc", rc)
+    return out
 
 
 @_on_stream

@@ -5,9 +5,19 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 
 #include "../../include/mamba_scan.h"
 #include "internal.h"
+
+// ---- scratch for the allocation-free forward (mamba_scan_fwd_noalloc) ----
+// One array per GPU: each device that loads the library holds its own copy
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory; the device address comes from hipGetSymbolAddress (see
+// scratch_address), once per device with that device current, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[MAMBA_SCAN_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -35,6 +45,71 @@ int check_fwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, 
   // (batch*dim*(seqlen+64)*4 bytes must be representable)
   if (!mul_ok(batch * dim, seqlen + 64, &t) || !mul_ok(t, 16, &t)) return MAMBA_SCAN_ERR_SHAPE;
   return MAMBA_SCAN_OK;
+}
+
+// Validation shared by the forward entry points: sizes, flags, pointers and the launch plan.
+int check_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
+              const void* z, const float* delta_bias, const float* initial_state, const float* final_state,
+              const void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int flags,
+              int64_t nchunks, int states_per_wave, mscan::FwdPlan* plan) {
+  int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  // tensors with a seqlen dimension are zero-sized when seqlen == 0 and may then be NULL
+  if (!A_log) return MAMBA_SCAN_ERR_NULL;
+  if (seqlen > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
+  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
+  const void* io_ptrs[] = {u, delta, B, C, z, y};
+  for (const void* p : io_ptrs)
+    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
+  const void* f_ptrs[] = {A_log, D, delta_bias, initial_state, final_state};
+  for (const void* p : f_ptrs)
+    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
+  if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, nchunks, states_per_wave, plan))
+    return MAMBA_SCAN_ERR_UNSUPPORTED;
+  return MAMBA_SCAN_OK;
+}
+
+int run_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
+            const void* z, const float* delta_bias, const float* initial_state, float* final_state, void* y,
+            int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype, int flags,
+            const mscan::FwdPlan& plan, void* workspace, void* stream) {
+  mscan::FwdArgs a{};
+  a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
+  a.h0 = initial_state; a.final_state = final_state; a.y = y;
+  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
+  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
+  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
+  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
+  a.workspace = workspace;
+  hipError_t e = mscan::launch_fwd(a, plan, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+}
+
+// The device address of this GPU's copy of `scratch` (below), looked up once
+// per device with that device current.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr || !aligned(p, 256)) return hipErrorInvalidSymbol;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
 }
 
 }  // namespace
@@ -74,35 +149,34 @@ int mamba_scan_fwd_ex(const void* u, const void* delta, const float* A_log, cons
                       float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                       int io_dtype, int flags, int64_t nchunks, int states_per_wave, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  int st = check_fwd_sizes(batch, dim, dstate, seqlen, io_dtype);
-  if (st != MAMBA_SCAN_OK) return st;
-  if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
-  // tensors with a seqlen dimension are zero-sized when seqlen == 0 and may then be NULL
-  if (!A_log) return MAMBA_SCAN_ERR_NULL;
-  if (seqlen > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
-  const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;
-  const void* io_ptrs[] = {u, delta, B, C, z, y};
-  for (const void* p : io_ptrs)
-    if (p && !aligned(p, esz)) return MAMBA_SCAN_ERR_ALIGN;
-  const void* f_ptrs[] = {A_log, D, delta_bias, initial_state, final_state};
-  for (const void* p : f_ptrs)
-    if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   mscan::FwdPlan plan;
-  if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, nchunks, states_per_wave, &plan))
-    return MAMBA_SCAN_ERR_UNSUPPORTED;
+  int st = check_fwd(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim, dstate,
+                     seqlen, io_dtype, flags, nchunks, states_per_wave, &plan);
+  if (st != MAMBA_SCAN_OK) return st;
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
   }
-  mscan::FwdArgs a{};
-  a.u = u; a.delta = delta; a.A_log = A_log; a.B = B; a.C = C; a.D = D; a.z = z; a.bias = delta_bias;
-  a.h0 = initial_state; a.final_state = final_state; a.y = y;
-  a.batch = batch; a.dim = dim; a.dstate = dstate; a.seqlen = seqlen;
-  a.io_bf16 = io_dtype == MAMBA_SCAN_BF16;
-  a.softplus = (flags & MAMBA_SCAN_FLAG_SOFTPLUS) != 0;
-  a.euler = (flags & MAMBA_SCAN_FLAG_EULER) != 0;
-  a.workspace = workspace;
-  hipError_t e = mscan::launch_fwd(a, plan, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? MAMBA_SCAN_OK : MAMBA_SCAN_ERR_HIP;
+  return run_fwd(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim, dstate,
+                 seqlen, io_dtype, flags, plan, workspace, stream);
+}
+
+int mamba_scan_fwd_noalloc(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, const float* initial_state,
+                           float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
+                           int io_dtype, int flags, void* stream) {
+  mscan::FwdPlan plan;
+  int st = check_fwd(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim, dstate,
+                     seqlen, io_dtype, flags, 0, 0, &plan);
+  if (st != MAMBA_SCAN_OK) return st;
+  if (plan.ws_total > (size_t)MAMBA_SCAN_NOALLOC_SCRATCH_BYTES) return MAMBA_SCAN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_total > 0) {
+    // everything in the scratch is written before it is read within one call (chunk
+    // aggregates, then the carry; the first state group's readout sum), so nothing is cleared
+    if (scratch_address(&ws) != hipSuccess) return MAMBA_SCAN_ERR_HIP;
+  }
+  return run_fwd(u, delta, A_log, B, C, D, z, delta_bias, initial_state, final_state, y, batch, dim, dstate,
+                 seqlen, io_dtype, flags, plan, ws, stream);
 }
 
 int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,

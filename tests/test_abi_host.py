@@ -279,3 +279,38 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     u = torch.zeros(1, 64, 8)
     with pytest.raises(RuntimeError, match="not built"):
         mscan.scan_fwd(u, u, torch.zeros(64, 16), torch.zeros(1, 16, 8), torch.zeros(1, 16, 8))
+
+
+def noalloc(lib, u=P, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None, h0=None, fs=None, y=P,
+            batch=2, dim=64, dstate=16, seqlen=128, io=1, flags=1):
+    return lib.mamba_scan_fwd_noalloc(u, delta, A_log, B, C, D, z, bias, h0, fs, y, batch, dim, dstate, seqlen,
+                                      io, flags, None)
+
+
+def test_noalloc_validation_errors(lib):
+    """The allocation-free forward validates like mamba_scan_fwd and refuses plans whose workspace
+    would not fit its static per-GPU scratch -- all before any HIP call."""
+    assert noalloc(lib, u=None) == ENULL
+    assert noalloc(lib, A_log=None) == ENULL
+    assert noalloc(lib, io=7) == EDTYPE
+    assert noalloc(lib, batch=0) == ESHAPE
+    assert noalloc(lib, dstate=65) == EUNSUP
+    assert noalloc(lib, flags=4) == EUNSUP
+    assert noalloc(lib, u=P + 1) == EALIGN
+    # d_state 32 sums two 16-state passes in an fp32 (batch, dim, L) buffer: 4 x 4096 x 8192 x 4 B
+    # is far past the scratch, so the call is refused rather than allocating
+    need = lib.mamba_scan_fwd_workspace_size(4, 4096, 32, 8192, 1)
+    assert need > mscan.NOALLOC_SCRATCH_BYTES
+    assert noalloc(lib, batch=4, dim=4096, dstate=32, seqlen=8192) == EWS
+    assert "workspace" in mscan.status_str(EWS)
+    # the chunk carry of any chunked d_state-16 plan fits
+    assert lib.mamba_scan_fwd_workspace_size(1, 2048, 16, 1 << 20, 1) <= mscan.NOALLOC_SCRATCH_BYTES
+    # and the binding refuses bad arguments (here host tensors) before calling in
+    with pytest.raises(ValueError):
+        mscan.scan_fwd_noalloc(*([__import__("torch").zeros(1, 1, 1)] * 5), out=None)
+
+
+def test_noalloc_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define MAMBA_SCAN_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == mscan.NOALLOC_SCRATCH_BYTES
