@@ -114,7 +114,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   extern __shared__ float smem[];
   float* dbuf = smem;                      // [2][64][kRow]  Delta*log2e
   float* ubuf = dbuf + LdsH2::kDU;         // [2][64][kRow]  u
-  float* bcs = ubuf + LdsH2::kDU;          // [2][kG][4 tokens][NP][B, C]
+  float* bcs = ubuf + LdsH2::kDU;          // [2][kG][NP/2 state pairs][4 tokens][B0, B1, C0, C1]
   float* par = bcs + LdsH2::kBC;           // [2][64]        bias, D
   float* ypart = par + LdsH2::kPar;        // [4][64][kRow]  partial readouts (output pass only)
 
@@ -335,9 +335,10 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       const int nvb = kFull ? 4 : (int)max((int64_t)0, min((int64_t)4, t_end - (tile + bg * 4)));
       float f[4];
       IO::to_f32(p.bc, f);
-      float* q = bcs + buf * kG * NP * 8 + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
+      // state bn is element (bn & 1) of its pair's B (0, 1) or C (2, 3) quadruple
+      float* q = bcs + buf * kG * NP * 8 + (bg * (NP / 2) + (bn >> 1)) * 16 + (isB ? 0 : 2) + (bn & 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+      for (int kk = 0; kk < 4; ++kk) q[kk * 4] = (kk < nvb) ? f[kk] : 0.0f;
     }
   };
 
@@ -427,14 +428,16 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     const int64_t tile = t_first + k * T;
     const float* drow = dbuf + (P * kCh + chw) * kRow;
     const float* urow = ubuf + (P * kCh + chw) * kRow;
-    const int sel = lane & 15;
-    // lane 4j + kk of each row holds (B, C) of token kk, state j of the row's pair
-    const float* bcl = bcs + P * kG * NP * 8 + ((sel & 3) * NP + sp * 4 + hf * 2 + ((sel >> 2) & 1)) * 2;
+    // (B, C) of the lane's two states for the four tokens of a group: 16 floats, read as
+    // four float4 (every lane of a wave half reads the same ones: an LDS broadcast)
+    const float* bcl = bcs + P * kG * NP * 8 + (sp * 2 + hf) * 16;
     float* yrow = ypart + (sp * kCh + chw) * kRow + 2 * hf;
 
     float4 dv = *reinterpret_cast<const float4*>(drow);
     float4 uv = *reinterpret_cast<const float4*>(urow);
-    float2 bcv = *reinterpret_cast<const float2*>(bcl);
+    float4 bcv[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) bcv[kk] = reinterpret_cast<const float4*>(bcl)[kk];
     prefetch(tile + 2 * T, pfCur);
     float4 yp[4][2];
     if constexpr (!kAgg) {
@@ -454,50 +457,50 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     // grid varies with the input from token to token; adding a slowly varying
     // m h to an h + s already on that grid would round the same way every token
     // and drift.
-    auto token = [&](float dl, float uu, float2 bq, auto kk_c) -> float {
-      constexpr int kk = decltype(kk_c)::value;
+    // bq = (B of state 0, B of state 1, C of state 0, C of state 1) of this token
+    auto token = [&](float dl, float uu, float4 bq) -> float {
       const float y0 = dl * A[0];
       const float y1 = dl * A[1];
       const float m0 = decay_m1<!kSp>(y0, __builtin_amdgcn_exp2f(y0));
       const float m1 = decay_m1<!kSp>(y1, __builtin_amdgcn_exp2f(y1));
       if constexpr (kEuler) {
-        const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * Delta * u
-        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
+        const float s0 = bq.x * uu;                                 // s = B * Delta * u
+        const float s1 = bq.y * uu;
         h[0] += fmaf(m0, h[0], s0);                                 // h + (m h + s)
         h[1] += fmaf(m1, h[1], s1);
       } else if constexpr (kAgg) {
         // the aggregate pass carries the scaled state A h (no readout needs h):
         // A h_t = A h + m (A h + B u), one multiply fewer per step
-        const float s0 = dpp_bcast_mul<kk>(bq.x, uu);               // s = B * u
-        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu);
+        const float s0 = bq.x * uu;                                 // s = B * u
+        const float s1 = bq.y * uu;
         h[0] = fmaf(m0, h[0] + s0, h[0]);
         h[1] = fmaf(m1, h[1] + s1, h[1]);
       } else {
-        const float s0 = dpp_bcast_mul<kk>(bq.x, uu * iA[0]);       // s = B * u / A
-        const float s1 = dpp_bcast_mul<4 + kk>(bq.x, uu * iA[1]);
+        const float s0 = bq.x * (uu * iA[0]);                       // s = B * u / A
+        const float s1 = bq.y * (uu * iA[1]);
         h[0] = fmaf(m0, h[0] + s0, h[0]);                           // h + m (h + s)
         h[1] = fmaf(m1, h[1] + s1, h[1]);
       }
-      if constexpr (!kAgg) return dpp_bcast_fmac<4 + kk>(dpp_bcast_mul<kk>(bq.y, h[0]), bq.y, h[1]);   // C . h
+      if constexpr (!kAgg) return fmaf(bq.w, h[1], bq.z * h[0]);   // C . h
       return 0.0f;
     };
 
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      // next group's LDS reads first, then the four tokens in one scheduling
-      // region (a DPP result needs two instructions before its first use)
+      // next group's LDS reads first, then the four tokens in one scheduling region
       float4 dn = dv, un = uv;
-      float2 bcn = bcv;
+      float4 bcn[4] = {bcv[0], bcv[1], bcv[2], bcv[3]};
       if (g + 1 < kG) {
         dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
         un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
-        bcn = *reinterpret_cast<const float2*>(bcl + (g + 1) * NP * 8);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) bcn[kk] = reinterpret_cast<const float4*>(bcl + (g + 1) * NP * 8)[kk];
       }
       __builtin_amdgcn_sched_barrier(0);
-      const float y0 = token(dv.x, uv.x, bcv, IntC<0>{});
-      const float y1 = token(dv.y, uv.y, bcv, IntC<1>{});
-      const float y2 = token(dv.z, uv.z, bcv, IntC<2>{});
-      const float y3 = token(dv.w, uv.w, bcv, IntC<3>{});
+      const float y0 = token(dv.x, uv.x, bcv[0]);
+      const float y1 = token(dv.y, uv.y, bcv[1]);
+      const float y2 = token(dv.z, uv.z, bcv[2]);
+      const float y3 = token(dv.w, uv.w, bcv[3]);
       if constexpr (!kAgg) {
         // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
         *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
@@ -530,7 +533,8 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       if (g + 1 < kG) {
         dv = dn;
         uv = un;
-        bcv = bcn;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) bcv[kk] = bcn[kk];
       }
     }
     lds_barrier();
