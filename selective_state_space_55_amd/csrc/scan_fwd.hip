@@ -34,11 +34,13 @@
 //
 // Time chunks.  When batch x channel groups cannot fill the GPU (e.g. one
 // batch row of 2048 channels and a million tokens) the sequence is cut into
-// chunks scanned in parallel: pass 1 scans each chunk from a zero state and
-// records (sum of Delta, h_end); a small carry kernel folds the chunks in
+// chunks scanned in parallel, each in one pass that writes its outputs: the
+// first chunk from the initial state, the others from a zero state, each
+// recording (sum of Delta, h_end).  A small carry kernel folds the chunks in
 // order with (a1,b1) o (a2,b2) = (a2 a1, a2 b1 + b2), using the chunk decay
-// exp(A * sum Delta) (exact for a diagonal, time-invariant A); pass 2 rescans
-// every chunk from its carried-in state and writes the outputs (MAMBA
+// exp(A * sum Delta) (exact for a diagonal, time-invariant A), and a fix-up
+// kernel adds to each later chunk's outputs what its carried-in state
+// contributes, C_t exp(A cumDelta_t) h_in, until that has decayed away (MAMBA
 // walkthrough, x-humanoid.csdn.net, §2.2: chunks in parallel, only the state
 // crosses chunk boundaries; State space models and Mamba, Parallel Scan: the
 // associative operator).
@@ -47,27 +49,31 @@
 namespace mscan {
 namespace {
 
-// Folds the chunk aggregates in time order; leaves in carry[.., k, ..] the
-// state entering chunk k.  One thread per (batch, channel, state).
+// Folds the chunk aggregates in time order.  Chunk 0 ran from the initial
+// state, so its end state is exact; chunk k > 0 ran from zero and left its
+// end state h_end(k) and sum Delta*log2e.  With (a1,b1) o (a2,b2) = (a2 a1,
+// a2 b1 + b2) and the chunk decay exp(A sum Delta) (exact for a diagonal,
+// time-invariant A), the state entering chunk k is left in carry[.., k, ..]
+// and the state after the last chunk in final_state.  One thread per
+// (batch, channel, state).
 __global__ __launch_bounds__(256) void carry_kernel(float* __restrict__ carry, const float* __restrict__ dsum,
-                                                    const float* __restrict__ A_log, const float* __restrict__ h0,
-                                                    int64_t batch, int64_t dim, int dstate, int np,
-                                                    int64_t nchunks) {
+                                                    const float* __restrict__ A_log, float* __restrict__ final_state,
+                                                    int64_t batch, int64_t dim, int dstate, int np, int64_t nchunks) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= batch * dim * dstate) return;
   const int n = (int)(i % dstate);
   const int64_t bd = i / dstate;
   const int64_t d = bd % dim;
   const float An = -expf(A_log[d * dstate + n]);
-  float h = h0 ? h0[bd * dstate + n] : 0.0f;
-  for (int64_t k = 0; k + 1 < nchunks; ++k) {
+  float h = carry[(bd * nchunks) * np + n];
+  for (int64_t k = 1; k < nchunks; ++k) {
     float* slot = carry + (bd * nchunks + k) * np + n;
     const float hend = *slot;
-    const float P = exp2f(An * dsum[bd * nchunks + k]);   // decay over chunk k: exp(A * sum Delta)
     *slot = h;
+    const float P = exp2f(An * dsum[bd * nchunks + k]);   // decay over chunk k: exp(A * sum Delta)
     h = fmaf(P, h, hend);
   }
-  carry[(bd * nchunks + nchunks - 1) * np + n] = h;
+  if (final_state) final_state[bd * dstate + n] = h;
 }
 
 // seqlen == 0: final_state = initial_state or zeros.
@@ -79,37 +85,31 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
 
 template <bool kMulti>
 struct PickH2 {
-  template <typename IoT, bool kAgg, bool kVec, int kMode>
+  template <typename IoT, bool kVec, int kMode>
   struct P {
-    static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, kMulti>; }
+    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, kMulti>; }
   };
 };
 
 struct PickH2Conv {
-  template <typename IoT, bool kAgg, bool kVec, int kMode>
+  template <typename IoT, bool kVec, int kMode>
   struct P {
-    static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, false, false, true>; }
+    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, false, false, true>; }
   };
 };
 
-template <typename IoT, bool kAgg>
+template <typename IoT>
 hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = pick_kernel<PickH2<false>::template P, IoT, kAgg>(vec, k.mode);
-  if constexpr (!kAgg) {
-    if (k.acc != 0) kern = pick_kernel<PickH2<true>::template P, IoT, kAgg>(vec, k.mode);
-  }
-  if (k.conv_w != nullptr) kern = pick_kernel<PickH2Conv::template P, IoT, kAgg>(vec, k.mode);   // 16 states, two per lane
-  const size_t lds = sizeof(float) * LdsH2::floats(kAgg);
+  auto kern = pick_kernel<PickH2<false>::template P, IoT>(vec, k.mode);
+  if (k.acc != 0) kern = pick_kernel<PickH2<true>::template P, IoT>(vec, k.mode);
+  if (k.conv_w != nullptr) kern = pick_kernel<PickH2Conv::template P, IoT>(vec, k.mode);   // 16 states, two per lane
+  const size_t lds = sizeof(float) * LdsH2::floats();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, s, k);
   return hipGetLastError();
 }
 
-template <typename IoT>
-hipError_t dispatch_scan(const KArgs& k, const FwdPlan& p, bool agg, bool vec, int64_t grid, hipStream_t s) {
-  return agg ? launch_scan_h2<IoT, true>(k, vec, grid, s) : launch_scan_h2<IoT, false>(k, vec, grid, s);
-}
 
 template <typename IoT>
 hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
@@ -145,26 +145,27 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   // dstate > 16: one pass per 16-state group; the readouts are summed in yacc
   const int ng = p.ngroups;
   k.yacc = ng > 1 ? reinterpret_cast<float*>(ws + p.off_yacc) : nullptr;
-  if (p.nchunks > 1) {
-    k.nwork = groups * (p.nchunks - 1);
-    for (int g = 0; g < ng; ++g) {
-      k.n0 = 16 * g;
-      hipError_t e = dispatch_scan<IoT>(k, p, true, vec, k.nwork, s);
-      if (e != hipSuccess) return e;
-    }
-    hipError_t e;
-    const int64_t n = a.batch * a.dim * a.dstate;
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, carry, dsum, a.A_log,
-                       a.h0, a.batch, a.dim, (int)a.dstate, p.np, p.nchunks);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  // every chunk is scanned at once (chunks after the first from a zero state),
+  // then the carry is folded and the fix-up adds the carried-in part to y
   k.nwork = groups * p.nchunks;
   for (int g = 0; g < ng; ++g) {
     k.n0 = 16 * g;
     k.acc = ng == 1 ? 0 : (g == 0 ? 1 : (g == ng - 1 ? 3 : 2));
-    hipError_t e = dispatch_scan<IoT>(k, p, false, vec, k.nwork, s);
+    hipError_t e = launch_scan_h2<IoT>(k, vec, k.nwork, s);
     if (e != hipSuccess) return e;
+  }
+  if (p.nchunks > 1) {
+    const int64_t n = a.batch * a.dim * a.dstate;
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, carry, dsum, a.A_log,
+                       a.final_state, a.batch, a.dim, (int)a.dstate, p.np, p.nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    FixArgs f{};
+    f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = carry;
+    f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks; f.chgroups = k.chgroups;
+    f.nwork = groups * (p.nchunks - 1); f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
+    launch_fix_ng<IoT, false>(f, ng, vec, s);
+    return hipGetLastError();
   }
   return hipSuccess;
 }

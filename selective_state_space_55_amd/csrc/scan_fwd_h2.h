@@ -72,7 +72,7 @@ struct LdsH2 {
   static constexpr int kBC = 2 * kG * 16 * 8;
   static constexpr int kPar = 2 * kCh;
   static constexpr int kY = 4 * kCh * kRow;
-  static constexpr int floats(bool agg) { return 2 * kDU + kBC + kPar + (agg ? 0 : kY); }
+  static constexpr int floats() { return 2 * kDU + kBC + kPar + kY; }
 };
 
 // kMulti: one of several 16-state passes of a dstate > 16 scan; the readout of
@@ -91,7 +91,7 @@ struct LdsH2 {
 // first piece, from the previous tile (kept in registers), the chunk's
 // preceding inputs or the conv state.  The conv output is rounded to the io
 // dtype, so the result equals the conv1d launch followed by the scan.
-template <typename IoT, bool kAgg, bool kVec, int kMode, bool kMulti, bool kVarlen = false, bool kConv = false>
+template <typename IoT, bool kVec, int kMode, bool kMulti, bool kVarlen = false, bool kConv = false>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -149,16 +149,14 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     sidx = lo;
     kc = pidx - ps[lo];
     nk = ps[lo + 1] - ps[lo];
-    if (kAgg && kc >= nk - 1) return;   // a sequence's last piece needs no aggregate
     b = 0;
     const int64_t s_begin = min(max(a.cu[sidx], (int64_t)0), a.seqlen);   // clamped: any offsets stay in bounds
     const int64_t s_end = min(max(a.cu[sidx + 1], s_begin), a.seqlen);
     t_begin = min(s_begin + kc * a.chunk_len, s_end);
     t_end = min(t_begin + a.chunk_len, s_end);
   } else {
-    const int64_t nck = kAgg ? a.nchunks - 1 : a.nchunks;
-    kc = wid % nck;
-    wid /= nck;
+    kc = wid % a.nchunks;
+    wid /= a.nchunks;
     cg = wid % a.chgroups;
     b = wid / a.chgroups;
     sidx = b;
@@ -197,13 +195,10 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     const float An = valid ? -expf(a.A_log[d * a.dstate + n]) : 0.0f;
     A[j] = An;
     iA[j] = valid ? 1.0f / An : 0.0f;
+    // the first chunk (piece of a sequence) starts from the initial state, later
+    // ones from zero: their carried-in part is added to y by the fix-up kernel
     float hv = 0.0f;
-    if (!kAgg && valid) {
-      if (kc > 0)
-        hv = a.carry[cslot * a.np + n];
-      else if (a.h0)
-        hv = a.h0[bd * a.dstate + n];
-    }
+    if (valid && kc == 0 && a.h0) hv = a.h0[bd * a.dstate + n];
     h[j] = hv;
   }
   float dsum_acc = 0.0f;
@@ -262,7 +257,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     p.d = IO::buf_load8(rs_d, off, kVec);
     p.u = IO::buf_load8(rs_u, off, kVec);
-    if constexpr (!kAgg) p.z = IO::buf_load8(rs_z, off, kVec);
+    p.z = IO::buf_load8(rs_z, off, kVec);
     const int boff = (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz);   // past dstate: reads 0
     p.bc = IO::buf_load4(isB ? rs_B : rs_C, boff, kVec);
   };
@@ -298,7 +293,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       }
       const V8 cr = IO::from_f32(cu);   // rounded to the io dtype, as a stored conv output
       IO::to_f32(cr, fu);
-      if constexpr (!kAgg) {
+      {
         if (guo != nullptr && d0 + pc < a.dim) {
           IoT* uo = guo + (b * a.dim + d0 + pc) * a.seqlen + tile + pg * 8;
           if (kFull && kVec)
@@ -326,7 +321,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     reinterpret_cast<float4*>(dp)[1] = make_float4(fd[4], fd[5], fd[6], fd[7]);
     reinterpret_cast<float4*>(up)[0] = make_float4(fs[0], fs[1], fs[2], fs[3]);
     reinterpret_cast<float4*>(up)[1] = make_float4(fs[4], fs[5], fs[6], fs[7]);
-    if constexpr (!kAgg) {
+    {
 #pragma unroll
       for (int j = 0; j < 8; ++j) kp.u[j] = fu[j];
       kp.z = p.z;
@@ -440,7 +435,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     for (int kk = 0; kk < 4; ++kk) bcv[kk] = reinterpret_cast<const float4*>(bcl)[kk];
     prefetch(tile + 2 * T, pfCur);
     float4 yp[4][2];
-    if constexpr (!kAgg) {
+    {
       // tile k-1's partials must be read by every wave before tile k's are written
       epi_read(yp);
       lds_barrier();
@@ -468,21 +463,13 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         const float s1 = bq.y * uu;
         h[0] += fmaf(m0, h[0], s0);                                 // h + (m h + s)
         h[1] += fmaf(m1, h[1], s1);
-      } else if constexpr (kAgg) {
-        // the aggregate pass carries the scaled state A h (no readout needs h):
-        // A h_t = A h + m (A h + B u), one multiply fewer per step
-        const float s0 = bq.x * uu;                                 // s = B * u
-        const float s1 = bq.y * uu;
-        h[0] = fmaf(m0, h[0] + s0, h[0]);
-        h[1] = fmaf(m1, h[1] + s1, h[1]);
       } else {
         const float s0 = bq.x * (uu * iA[0]);                       // s = B * u / A
         const float s1 = bq.y * (uu * iA[1]);
         h[0] = fmaf(m0, h[0] + s0, h[0]);                           // h + m (h + s)
         h[1] = fmaf(m1, h[1] + s1, h[1]);
       }
-      if constexpr (!kAgg) return fmaf(bq.w, h[1], bq.z * h[0]);   // C . h
-      return 0.0f;
+      return fmaf(bq.w, h[1], bq.z * h[0]);   // C . h
     };
 
 #pragma unroll
@@ -501,13 +488,12 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       const float y1 = token(dv.y, uv.y, bcv[1]);
       const float y2 = token(dv.z, uv.z, bcv[2]);
       const float y3 = token(dv.w, uv.w, bcv[3]);
-      if constexpr (!kAgg) {
+      {
         // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
         *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
-      } else {
-        dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);
       }
-      if constexpr (!kAgg) {
+      dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);   // the chunk's sum of Delta*log2e
+      {
         if (g == 1) {
           float yv[8];
           if (epi_finish(yp, kpOther, yv, tile - T)) {
@@ -541,7 +527,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   };
 
   auto last_epilogue = [&](int64_t k, const Keep& kp) {
-    if constexpr (!kAgg) {
+    {
       float4 yp[4][2];
       epi_read(yp);
       float yv[8];
@@ -575,30 +561,271 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   }
 
   // ---- final state or chunk aggregate ----
+  // rows in several chunks, and every varlen piece: each chunk leaves (h_end,
+  // sum Delta) for the carry kernel, which writes the final state
+  const bool chunk_out = kVarlen || a.nchunks > 1;
   if (ch_ok) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = a.n0 + sp * 4 + hf * 2 + j;
-      if (!kAgg) {
-        if (kc == nk - 1 && a.final_state && n < a.dstate) a.final_state[bd * a.dstate + n] = h[j];
-      } else {
-        a.carry[cslot * a.np + n] = kEuler ? h[j] : h[j] * iA[j];   // zero-order hold: (A h) / A
+      if (chunk_out) {
+        a.carry[cslot * a.np + n] = h[j];
+      } else if (kc == nk - 1 && a.final_state && n < a.dstate) {
+        a.final_state[bd * a.dstate + n] = h[j];
       }
     }
-    if (kAgg && sp == 0 && hf == 0) a.dsum[cslot] = dsum_acc;
+    if (chunk_out && sp == 0 && hf == 0) a.dsum[cslot] = dsum_acc;
+  }
+}
+
+// Fix-up of chunks k > 0 after they were scanned from a zero state: the
+// recurrence is linear in the state, so h_t = h_t(from 0) + P_t h_in with
+// P_t = exp(A cumDelta_t) (cumDelta from the chunk start through token t), and
+// y_t gains (sum_n C_t[n] P_t[n] h_in[n]) SiLU(z_t).  A thread owns an 8-token
+// piece of one channel (the 8 threads of a channel read its 128-byte line
+// segment of a tile), so the sum over states stays in registers; the pieces'
+// cumDelta come from a prefix sum over the channel's 8 lanes; C of the tile is
+// staged in LDS.  The correction decays with cumDelta: with softplus (Delta >=
+// 0) the workgroup stops once every lane's decay is below 2^-32 at the end of
+// a tile (a multiple of the state scale far below fp32 resolution of y), so
+// usually only the head of a chunk is touched.  3 VALU + 1 exp per (token,
+// state).
+struct FixArgs {
+  const int64_t* cu;       // varlen: sequence offsets (nseq + 1), device memory
+  const int64_t* pstart;   // varlen: first piece of each sequence (nseq + 1), device memory
+  int64_t nseq;
+  const void* delta;
+  const float* bias;
+  const float* A_log;
+  const void* C;
+  const void* z;
+  void* y;
+  const float* carry;
+  int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
+  int dstate, np, softplus;
+};
+
+
+// kVarlen: rows (dim, total) hold sequences back to back; a work item is
+// (piece, channel group) as in the scan kernel, pieces after a sequence's first
+// are fixed, and tiles stay aligned to 64 tokens of the row (the first may
+// start before the piece: its earlier tokens are masked).
+template <typename IoT, bool kVec, int NG, bool kVarlen>
+__global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
+  using IO = Io<IoT>;
+  using V4 = typename IO::V4;
+  using V8 = typename IO::V8;
+  constexpr int T = 64;
+  constexpr int NPS = 16 * NG;          // states, processed 16 at a time
+  constexpr int kCRow = T + 4;          // LDS row of C (floats)
+  constexpr int kSRow = NPS + 4;        // LDS row of a channel's A or h_in
+  constexpr int kEsz = (int)sizeof(IoT);
+  constexpr float kLog2e = 1.4426950408889634f;
+  __shared__ float cbuf[NPS * kCRow];   // [state][token]
+  __shared__ float sA[kCh * kSRow];     // [channel][state]
+  __shared__ float sH[kCh * kSRow];
+  __shared__ float par[kCh];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int pc = tid / 8;               // channel within the group
+  const int pg = tid % 8;               // tokens 8 pg .. 8 pg + 7 of a tile
+  int64_t kc, cg, b, t_begin, t_end, slot0;   // slot0: carry slot of channel 0 of the group
+  if constexpr (kVarlen) {
+    cg = blockIdx.x % a.chgroups;
+    const int64_t pidx = blockIdx.x / a.chgroups;
+    const int64_t* ps = a.pstart;
+    if (pidx >= ps[a.nseq]) return;   // the grid is an upper bound on the number of pieces
+    int64_t lo = 0, hi = a.nseq - 1;  // the sequence: the last s with ps[s] <= pidx
+    while (lo < hi) {
+      const int64_t mid = (lo + hi + 1) >> 1;
+      if (ps[mid] <= pidx)
+        lo = mid;
+      else
+        hi = mid - 1;
+    }
+    kc = pidx - ps[lo];
+    if (kc == 0) return;              // a sequence's first piece ran from its initial state
+    b = 0;
+    const int64_t s_begin = min(max(a.cu[lo], (int64_t)0), a.seqlen);
+    const int64_t s_end = min(max(a.cu[lo + 1], s_begin), a.seqlen);
+    t_begin = min(s_begin + kc * a.chunk_len, s_end);
+    t_end = min(t_begin + a.chunk_len, s_end);
+    slot0 = pidx * a.dim;
+  } else {
+    int64_t wid = work_id(blockIdx.x, a.nwork);
+    const int64_t nk1 = a.nchunks - 1;
+    kc = wid % nk1 + 1;
+    wid /= nk1;
+    cg = wid % a.chgroups;
+    b = wid / a.chgroups;
+    t_begin = kc * a.chunk_len;
+    t_end = min(t_begin + a.chunk_len, a.seqlen);
+    slot0 = -1;
+  }
+  const int64_t d0 = cg * kCh;
+  const int64_t d = d0 + pc;
+  const bool ch_ok = d < a.dim;
+  const int64_t t_first = kVarlen ? (t_begin & ~(int64_t)(T - 1)) : t_begin;
+  if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
+  bool finite = true;
+  for (int i = tid; i < kCh * NPS; i += 512) {
+    const int c = i / NPS, n = i % NPS;
+    const int64_t dc = d0 + c;
+    const bool valid = dc < a.dim && n < a.dstate;
+    const int64_t slot = kVarlen ? slot0 + dc : (b * a.dim + dc) * a.nchunks + kc;
+    const float hv = valid ? a.carry[slot * a.np + n] : 0.0f;
+    sA[c * kSRow + n] = valid ? -expf(a.A_log[dc * a.dstate + n]) : 0.0f;
+    sH[c * kSRow + n] = hv;
+    finite = finite && (fabsf(hv) <= 3.4e38f);
+  }
+  // a non-finite carried-in state propagates to the chunk's end (no early stop)
+  const bool may_stop = a.softplus != 0 && __syncthreads_and(finite ? 1 : 0) != 0;
+
+  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int64_t row0 = (b * a.dim + d0) * a.seqlen;
+  const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
+  const bool gated = a.z != nullptr;
+  const IoT* gd = static_cast<const IoT*>(a.delta);
+  const __amdgpu_buffer_rsrc_t rs_d = make_rsrc(gd + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_z = make_rsrc(gated ? static_cast<const IoT*>(a.z) + row0 : gd + row0,
+                                                gated ? nrec_ch : 0);
+  const __amdgpu_buffer_rsrc_t rs_y = make_rsrc(static_cast<IoT*>(a.y) + row0, nrec_ch);
+  const __amdgpu_buffer_rsrc_t rs_C = make_rsrc(static_cast<const IoT*>(a.C) + b * a.dstate * a.seqlen,
+                                                (int)((int64_t)a.dstate * a.seqlen * kEsz));
+  IoT* gy = static_cast<IoT*>(a.y);
+  const float bi = par[pc];
+  constexpr int kCP = (NPS * 16 + 511) / 512;   // four-token pieces of C per thread
+
+  float base = 0.0f;   // cumDelta*log2e of the channel before the tile
+  for (int64_t tile = t_first; tile < t_end; tile += T) {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    const V8 vd = IO::buf_load8(rs_d, off, kVec);
+    const V8 vy = IO::buf_load8(rs_y, off, kVec);
+    const V8 vz = IO::buf_load8(rs_z, off, kVec);
+    V4 vc[kCP];
+#pragma unroll
+    for (int r = 0; r < kCP; ++r) {
+      const int i = tid + r * 512;
+      const int n = i / 16, g4 = i % 16;
+      if (i < NPS * 16) vc[r] = IO::buf_load4(rs_C, (int)(((int64_t)n * a.seqlen + tile + 4 * g4) * kEsz), kVec);
+    }
+    __syncthreads();   // the previous tile's C reads are done
+#pragma unroll
+    for (int r = 0; r < kCP; ++r) {
+      const int i = tid + r * 512;
+      const int n = i / 16, g4 = i % 16;
+      if (i < NPS * 16) {
+        float f[4];
+        IO::to_f32(vc[r], f);
+        const int64_t t4 = tile + 4 * g4;
+        float4 cv;
+        cv.x = (t4 >= t_begin && t4 < t_end) ? f[0] : 0.0f;
+        cv.y = (t4 + 1 >= t_begin && t4 + 1 < t_end) ? f[1] : 0.0f;
+        cv.z = (t4 + 2 >= t_begin && t4 + 2 < t_end) ? f[2] : 0.0f;
+        cv.w = (t4 + 3 >= t_begin && t4 + 3 < t_end) ? f[3] : 0.0f;
+        *reinterpret_cast<float4*>(cbuf + n * kCRow + 4 * g4) = cv;
+      }
+    }
+    __syncthreads();
+    // this thread's tokens inside [t_begin, t_end): j in [lo, nv)
+    const int nv = (int)max((int64_t)0, min((int64_t)8, t_end - (tile + pg * 8)));
+    const int lo = kVarlen ? (int)min((int64_t)8, max((int64_t)0, t_begin - (tile + pg * 8))) : 0;
+    float fd[8], c[8];
+    IO::to_f32(vd, fd);
+    float run = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float x = fd[j] + bi;
+      const float dl = a.softplus ? softplus_log2e(x) : x * kLog2e;
+      run += (j >= lo && j < nv) ? dl : 0.0f;
+      c[j] = run;   // inclusive within the piece
+    }
+    // exclusive prefix of the pieces' sums over the channel's 8 lanes
+    float incl = run;
+#pragma unroll
+    for (int sh = 1; sh < 8; sh <<= 1) {
+      const float o = __shfl_up(incl, sh, 8);
+      if (pg >= sh) incl += o;
+    }
+    const float excl = incl - run;
+    const float total = __shfl(incl, (lane & ~7) | 7);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] += base + excl;
+    base += total;
+    float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    float pmax = 0.0f;
+#pragma unroll 1
+    for (int g = 0; g < NG; ++g) {
+      float An[16], Hn[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 va = *reinterpret_cast<const float4*>(sA + pc * kSRow + 16 * g + 4 * q);
+        const float4 vh = *reinterpret_cast<const float4*>(sH + pc * kSRow + 16 * g + 4 * q);
+        An[4 * q] = va.x; An[4 * q + 1] = va.y; An[4 * q + 2] = va.z; An[4 * q + 3] = va.w;
+        Hn[4 * q] = vh.x; Hn[4 * q + 1] = vh.y; Hn[4 * q + 2] = vh.z; Hn[4 * q + 3] = vh.w;
+      }
+#pragma unroll 4
+      for (int n = 0; n < 16; ++n) {
+        const float* crow = cbuf + (16 * g + n) * kCRow + 8 * pg;
+        const float4 c0 = *reinterpret_cast<const float4*>(crow);
+        const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
+        const float cn[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float P = __builtin_amdgcn_exp2f(An[n] * c[j]);   // exp(A cumDelta)
+          acc[j] = fmaf(cn[j], P * Hn[n], acc[j]);
+          if (j == 7) pmax = fmaxf(pmax, P);
+        }
+      }
+    }
+    float fy[8], fz[8];
+    IO::to_f32(vy, fy);
+    IO::to_f32(vz, fz);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) fy[j] = fmaf(acc[j], gated ? silu(fz[j]) : 1.0f, fy[j]);
+    if (nv == 8 && lo == 0) {
+      IO::buf_store8(rs_y, off, IO::from_f32(fy), kVec);
+    } else if (nv > lo && ch_ok) {
+      IoT* py = gy + row0 + (int64_t)pc * a.seqlen + tile + pg * 8;
+      if (lo == 0) {
+        IO::store_n(py, IO::from_f32(fy), nv);
+      } else {
+        for (int j = lo; j < nv; ++j) IO::store1(py + j, fy[j]);
+      }
+    }
+    // decay below 2^-32 on every lane: the rest of the chunk needs no correction
+    if (may_stop && __syncthreads_and((!ch_ok || pmax < 2.3283064e-10f) ? 1 : 0) != 0) break;
+  }
+}
+
+template <typename IoT, int NG, bool kVarlen>
+void launch_fix(const FixArgs& f, bool vec, hipStream_t s) {
+  auto kern = vec ? fix_kernel<IoT, true, NG, kVarlen> : fix_kernel<IoT, false, NG, kVarlen>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)f.nwork), dim3(512), 0, s, f);
+}
+
+// Fix-up launch for 16-state groups ng = 1..4.
+template <typename IoT, bool kVarlen>
+void launch_fix_ng(const FixArgs& f, int ng, bool vec, hipStream_t s) {
+  switch (ng) {
+    case 1: launch_fix<IoT, 1, kVarlen>(f, vec, s); break;
+    case 2: launch_fix<IoT, 2, kVarlen>(f, vec, s); break;
+    case 3: launch_fix<IoT, 3, kVarlen>(f, vec, s); break;
+    default: launch_fix<IoT, 4, kVarlen>(f, vec, s); break;
   }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Kernel pointer for a runtime (vec, mode) pair; Pick<IoT, kAgg, kVec, kMode>::get() names the kernel.
-template <template <typename, bool, bool, int> class Pick, typename IoT, bool kAgg>
+// Kernel pointer for a runtime (vec, mode) pair; Pick<IoT, kVec, kMode>::get() names the kernel.
+template <template <typename, bool, int> class Pick, typename IoT>
 auto pick_kernel(bool vec, int mode) {
   switch (mode) {
-    case 1: return vec ? Pick<IoT, kAgg, true, 1>::get() : Pick<IoT, kAgg, false, 1>::get();
-    case 2: return vec ? Pick<IoT, kAgg, true, 2>::get() : Pick<IoT, kAgg, false, 2>::get();
-    case 3: return vec ? Pick<IoT, kAgg, true, 3>::get() : Pick<IoT, kAgg, false, 3>::get();
-    default: return vec ? Pick<IoT, kAgg, true, 0>::get() : Pick<IoT, kAgg, false, 0>::get();
+    case 1: return vec ? Pick<IoT, true, 1>::get() : Pick<IoT, false, 1>::get();
+    case 2: return vec ? Pick<IoT, true, 2>::get() : Pick<IoT, false, 2>::get();
+    case 3: return vec ? Pick<IoT, true, 3>::get() : Pick<IoT, false, 3>::get();
+    default: return vec ? Pick<IoT, true, 0>::get() : Pick<IoT, false, 0>::get();
   }
 }
 

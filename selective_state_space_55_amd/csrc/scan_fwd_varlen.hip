@@ -8,15 +8,16 @@
 //
 // A sequence is cut into pieces of at most `piece` tokens, which are scanned
 // as the time chunks of a fixed-length row are (the associative combine of
-// the pages' parallel scan, applied between pieces): an aggregate pass gives
-// each piece but the last its end state from zero and its sum of Delta, a
-// carry kernel folds them in order from the sequence's initial state, and the
-// output pass rescans every piece from the state entering it.  Work items are
-// (piece, 64-channel group), so one long sequence still fills the GPU.  The
-// offsets are device memory: a one-workgroup kernel counts the pieces of each
-// sequence (prefix sums) and the passes launch over an upper bound, with work
-// items past the last piece exiting at once.  The scan kernel is the
-// two-states-per-lane kernel of scan_fwd_h2.h.
+// the pages' parallel scan, applied between pieces): every piece is scanned at
+// once -- a sequence's first from its initial state, the others from zero --
+// leaving its end state and sum of Delta; a carry kernel folds them in order
+// per sequence, and the fix-up kernel adds each later piece's carried-in part
+// to its outputs.  Work items are (piece, 64-channel group), so one long
+// sequence still fills the GPU.  The offsets are device memory: a
+// one-workgroup kernel counts the pieces of each sequence (prefix sums) and
+// the passes launch over an upper bound, with work items past the last piece
+// exiting at once.  The scan kernel is the two-states-per-lane kernel of
+// scan_fwd_h2.h.
 #include "scan_fwd_h2.h"
 
 namespace mscan {
@@ -55,12 +56,15 @@ __global__ __launch_bounds__(1024) void varlen_plan_kernel(const int64_t* __rest
   if (tid == 0) pstart[nseq] = run;
 }
 
-// Per (sequence, channel, state): folds the aggregates of the sequence's
-// pieces in order from its initial state; leaves in carry[piece k] the state
-// entering piece k.  Pieces at or past maxp (possible only for offsets that
-// are not non-decreasing) are not touched.
+// Per (sequence, channel, state): folds the sequence's pieces in order.  Its
+// first piece ran from the initial state (its end state is exact); piece k > 0
+// ran from zero and left h_end(k) and its sum of Delta*log2e.  Leaves in
+// carry[piece k] the state entering piece k and writes the sequence's final
+// state.  Pieces at or past maxp (possible only for offsets that are not
+// non-decreasing) were not scanned and are not touched.
 __global__ __launch_bounds__(256) void varlen_carry_kernel(float* __restrict__ carry, const float* __restrict__ dsum,
-                                                           const float* __restrict__ A_log, const float* __restrict__ h0,
+                                                           const float* __restrict__ A_log,
+                                                           float* __restrict__ final_states,
                                                            const int64_t* __restrict__ pstart, int64_t nseq,
                                                            int64_t dim, int dstate, int np, int64_t maxp) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -71,24 +75,24 @@ __global__ __launch_bounds__(256) void varlen_carry_kernel(float* __restrict__ c
   const int64_t s = sd / dim;
   const int64_t p0 = pstart[s];
   const int64_t p1 = min(pstart[s + 1], maxp);
-  if (p1 - p0 < 2) return;   // one piece: it starts from the initial state
+  if (p1 <= p0) return;
   const float An = -expf(A_log[d * dstate + n]);
-  float h = h0 ? h0[sd * dstate + n] : 0.0f;
-  for (int64_t k = p0; k + 1 < p1; ++k) {
+  float h = carry[(p0 * dim + d) * np + n];
+  for (int64_t k = p0 + 1; k < p1; ++k) {
     float* slot = carry + (k * dim + d) * np + n;
     const float hend = *slot;
-    const float P = exp2f(An * dsum[k * dim + d]);   // decay over piece k: exp(A * sum Delta)
     *slot = h;
+    const float P = exp2f(An * dsum[k * dim + d]);   // decay over piece k: exp(A * sum Delta)
     h = fmaf(P, h, hend);
   }
-  carry[((p1 - 1) * dim + d) * np + n] = h;
+  if (final_states) final_states[sd * dstate + n] = h;
 }
 
-template <bool kAgg, bool kMulti>
+template <bool kMulti>
 struct PickVarlen {
-  template <typename IoT, bool kAgg_, bool kVec, int kMode>
+  template <typename IoT, bool kVec, int kMode>
   struct P {
-    static auto get() { return scan_fwd_h2_kernel<IoT, kAgg, kVec, kMode, kMulti, true>; }
+    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, kMulti, true>; }
   };
 };
 
@@ -115,38 +119,35 @@ hipError_t run_varlen(const FwdArgs& a, const VarlenPlan& p, hipStream_t s) {
   k.nwork = p.maxp * k.chgroups;
   const int ng = p.ngroups;
   k.yacc = ng > 1 ? reinterpret_cast<float*>(ws + p.off_yacc) : nullptr;
-  const size_t lds_agg = sizeof(float) * LdsH2::floats(true);
-  const size_t lds = sizeof(float) * LdsH2::floats(false);
+  const size_t lds = sizeof(float) * LdsH2::floats();
 
   hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(1024), 0, s, a.cu, a.nseq, a.seqlen, p.piece, pstart);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // aggregates of every piece but each sequence's last, for every state group
-  for (int g = 0; g < ng; ++g) {
-    k.n0 = 16 * g;
-    auto kern = pick_kernel<PickVarlen<true, false>::template P, IoT, true>(vec, k.mode);
-    e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_agg);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)k.nwork), dim3(512), lds_agg, s, k);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t nthr = a.nseq * a.dim * a.dstate;
-  hipLaunchKernelGGL(varlen_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, k.carry, k.dsum,
-                     a.A_log, a.h0, pstart, a.nseq, a.dim, (int)a.dstate, p.np, p.maxp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   for (int g = 0; g < ng; ++g) {
     k.n0 = 16 * g;
     k.acc = ng == 1 ? 0 : (g == 0 ? 1 : (g == ng - 1 ? 3 : 2));
-    auto kern = k.acc ? pick_kernel<PickVarlen<false, true>::template P, IoT, false>(vec, k.mode)
-                      : pick_kernel<PickVarlen<false, false>::template P, IoT, false>(vec, k.mode);
+    auto kern = k.acc ? pick_kernel<PickVarlen<true>::template P, IoT>(vec, k.mode)
+                      : pick_kernel<PickVarlen<false>::template P, IoT>(vec, k.mode);
     e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)k.nwork), dim3(512), lds, s, k);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int64_t nthr = a.nseq * a.dim * a.dstate;
+  hipLaunchKernelGGL(varlen_carry_kernel, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, k.carry, k.dsum,
+                     a.A_log, a.final_state, pstart, a.nseq, a.dim, (int)a.dstate, p.np, p.maxp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  FixArgs f{};
+  f.cu = a.cu; f.pstart = pstart; f.nseq = a.nseq;
+  f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = k.carry;
+  f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.piece; f.nchunks = 1; f.chgroups = k.chgroups;
+  f.nwork = k.nwork; f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
+  launch_fix_ng<IoT, true>(f, ng, vec, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -104,8 +104,10 @@ def test_chunked_carry_vs_oracle(nchunks, io):
     check("y", y, yr, TOL[io])
     check("final_state", fs, fsr, TOL[io])
     y1, fs1 = gpu_fwd(inp, nchunks=1)
-    # same function, different rounding order only
-    assert max_rel_err(y, y1.double()) <= (1e-5 if io == "f32" else 1e-2)
+    # same function, different rounding order only; in bf16 both are within 1e-2 of the oracle (checked
+    # above), and a chunk's head is rounded twice (scanned from zero, then the fix-up adds the carried-in
+    # part), so the two may differ by up to the sum of their errors
+    assert max_rel_err(y, y1.double()) <= (1e-5 if io == "f32" else 2e-2)
 
 
 def test_seqlen_zero():
