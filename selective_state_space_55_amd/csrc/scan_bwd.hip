@@ -138,9 +138,11 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
 // SIMD) over 64 channels; wave w covers channels (w & 1) * 32 .. +31, and its
 // lanes l and l + 32 hold the same channel and different state pairs, states
 // (w >> 1) * 4 + (l >> 5) * 2 + {0, 1}.  Staging threads own 4-token pieces of
-// a tile: channel tid / 8, tokens 4 (tid % 8) .. +3.  B and C of a 4-token
-// group reach the lanes through DPP row broadcasts: lane 4j + kk of each row
-// holds (state j of the lane's pair, token kk).
+// a tile: channel tid / 8, tokens 4 (tid % 8) .. +3.  B and C are staged per
+// state pair and token, (B0, B1, C0, C1), and every lane reads its pair's
+// values for a 4-token group (an LDS broadcast within a wave half), so they
+// enter the arithmetic as plain VGPR operands, which gfx950 issues at about
+// twice the rate of DPP-operand instructions.
 
 // ---------------------------------------------------------------- checkpoints
 // kEuler: the Euler input term, h = Abar h + Delta B u (u is staged as Delta u)
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   constexpr int kEsz = (int)sizeof(IoT);
   __shared__ float dbuf[kCh * kRow];
   __shared__ float ubuf[kCh * kRow];
-  __shared__ float bbuf[kG * 4 * NP];   // [group][token][state]
+  __shared__ float bbuf[kG * 4 * NP];   // [group][state pair][token][B of the pair's two states]
   __shared__ float par[kCh];
 
   const int tid = threadIdx.x;
@@ -193,8 +195,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   const __amdgpu_buffer_rsrc_t rs_B = make_rsrc(gB + b * a.dstate * a.seqlen, (int)((int64_t)a.dstate * a.seqlen * kEsz));
   const int pc = tid / 8, pg = tid % 8;            // piece: channel, tokens 4 pg .. 4 pg + 3
   const int bn = tid % NP, bg = (tid / NP) % kG;   // B piece (threads 0..127): state, 4-token group
-  const int sel = lane & 15;
-  const float* bl = bbuf + (sel & 3) * NP + nb + ((sel >> 2) & 1);   // + g * 4 * NP
+  const float* bl = bbuf + (nb / 2) * 8;   // the lane's state pair, + g * 4 * NP
   float* ck = a.ckpt + (b * a.nsub * NP + nb) * a.dim + d;         // + (s8 * NP + j) * dim
   __syncthreads();
 
@@ -230,7 +231,7 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
       float f[4];
       IO::to_f32(rb, f);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) bbuf[(bg * 4 + kk) * NP + bn] = kk < nvb ? f[kk] : 0.0f;
+      for (int kk = 0; kk < 4; ++kk) bbuf[(bg * (NP / 2) + (bn >> 1)) * 8 + kk * 2 + (bn & 1)] = kk < nvb ? f[kk] : 0.0f;
     }
     if (k + 1 < a.ntile) load_tile(tile + kT, rd, ru, rb);
     lds_barrier();
@@ -245,7 +246,9 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
       }
       const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * g);
       const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * g);
-      const float bq = bl[g * 4 * NP];   // lane 4j+kk: state j of the pair, token kk
+      const float4 bq01 = reinterpret_cast<const float4*>(bl + g * 4 * NP)[0];   // tokens 0, 1: B0, B1
+      const float4 bq23 = reinterpret_cast<const float4*>(bl + g * 4 * NP)[1];   // tokens 2, 3
+      const float bqs[8] = {bq01.x, bq01.y, bq01.z, bq01.w, bq23.x, bq23.y, bq23.z, bq23.w};
       const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
       const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
       static_for<4>([&](auto kk_c) {
@@ -255,9 +258,9 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
           const float yv = dls[kk] * A[j];
           const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
           if constexpr (kEuler) {
-            h[j] += fmaf(m, h[j], dpp_bcast_mul<4 * j + kk>(bq, uus[kk]));   // h + (m h + B (Delta u))
+            h[j] += fmaf(m, h[j], bqs[kk * 2 + j] * uus[kk]);   // h + (m h + B (Delta u))
           } else {
-            const float sv = dpp_bcast_mul<4 * j + kk>(bq, uus[kk]);   // B u
+            const float sv = bqs[kk * 2 + j] * uus[kk];   // B u
             h[j] = fmaf(m, h[j] + sv, h[j]);                           // A h + m (A h + B u)
           }
         });
@@ -286,7 +289,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float* dbuf = smem;                     // [64][kRow] Delta*log2e
   float* ubuf = dbuf + LdsB::kDU;         // [64][kRow] u
   float* ybuf = ubuf + LdsB::kDU;         // [64][kRow] dytil
-  float* bcs = ybuf + LdsB::kDU;          // [kG][4 tokens][NP][B, C]
+  float* bcs = ybuf + LdsB::kDU;          // [kG][NP/2 state pairs][4 tokens][B0, B1, C0, C1]
   float* party = bcs + LdsB::kBC;         // [4][64][kRow] readout partials
   float* part1 = party + LdsB::kPart;     // [4][64][kRow] dDelta partials
   float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
@@ -354,9 +357,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   const int bn = tid % NP, bg = (tid / NP) % kG;     // (B or C) piece (waves 0-3): state, 4-token group
   const bool stageBC = w < 4;                        // wave-uniform, so the buffer descriptor below is too
   const bool isB = w < 2;                            // waves 0-1 stage B, 2-3 C
-  const int sel = lane & 15;
-  // lane 4j + kk of each row: (B, C) of token kk, state j of the lane's pair
-  const float* bcl = bcs + ((sel & 3) * NP + nb + ((sel >> 2) & 1)) * 2;
+  // (B, C) of the lane's two states for the four tokens of a group: four float4, read by every
+  // lane of a wave half alike (an LDS broadcast), used as plain VGPR operands
+  const float* bcl = bcs + (nb / 2) * 16;
   const float* ck = a.ckpt + (b * a.nsub * NP + nb) * a.dim + d;   // + (s8 * NP + j) * dim
   const int yoff = 2 * hf;                           // half_sum2 results: tokens 2 hf, 2 hf + 1 of a group
   // dB / dC partials over this wave's 32 channels: (batch, 32-channel group, state, token)
@@ -424,9 +427,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         const int nvb = max(0, min(4, nv_tile - bg * 4));
         float f[4];
         IO::to_f32(rbc, f);
-        float* q = bcs + (bg * 4 * NP + bn) * 2 + (isB ? 0 : 1);
+        // state bn is element (bn & 1) of its pair's B (0, 1) or C (2, 3) quadruple
+        float* q = bcs + (bg * (NP / 2) + (bn >> 1)) * 16 + (isB ? 0 : 2) + (bn & 1);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) q[kk * NP * 2] = (kk < nvb) ? f[kk] : 0.0f;
+        for (int kk = 0; kk < 4; ++kk) q[kk * 4] = (kk < nvb) ? f[kk] : 0.0f;
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -450,7 +454,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
           const int tg = 2 * s + gq;
           const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * tg);
           const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * tg);
-          const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
+          float4 bcq[4];   // per token: B0, B1, C0, C1 of the lane's states
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) bcq[kk] = reinterpret_cast<const float4*>(bcl + tg * NP * 8)[kk];
           const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
           const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
           float ys[4];
@@ -464,13 +470,13 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
               const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
               // Bbar = e B: e = (Abar - 1) / A (zero-order hold) or Delta (Euler)
               const float e = kEuler ? dls[kk] * kLn2 : m * iA[j];
-              const float bu = dpp_bcast_mul<4 * j + kk>(bq.x, uus[kk]);   // B u
+              const float bu = (j == 0 ? bcq[kk].x : bcq[kk].y) * uus[kk];   // B u
               h[j] += fmaf(m, h[j], e * bu);                               // h + (m h + e B u)
               hh[t][j] = h[j];
               ha[t][j] = m;
               he[t][j] = e;
               hbu[t][j] = bu;
-              acc = (j == 0) ? dpp_bcast_mul<4 * j + kk>(bq.y, h[j]) : dpp_bcast_fmac<4 * j + kk>(acc, bq.y, h[j]);
+              acc = (j == 0) ? bcq[kk].z * h[j] : fmaf(bcq[kk].w, h[j], acc);
             });
             ys[kk] = acc;
           });
@@ -490,7 +496,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
         const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * tg);
         const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * tg);
         const float4 yv = *reinterpret_cast<const float4*>(ybuf + chw * kRow + 4 * tg);
-        const float2 bq = *reinterpret_cast<const float2*>(bcl + tg * NP * 8);
+        float4 bcq[4];   // per token: B0, B1, C0, C1 of the lane's states
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) bcq[kk] = reinterpret_cast<const float4*>(bcl + tg * NP * 8)[kk];
         const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
         const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
         const float dys[4] = {yv.x, yv.y, yv.z, yv.w};
@@ -501,10 +509,9 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
           float dD_p = 0.0f, du_p = 0.0f;
           static_for<NPW>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
-            constexpr int src = 4 * j + kk;               // lane of the row holding (state j, token kk)
             const float hp = (t > 0) ? hh[t > 0 ? t - 1 : 0][j] : hb[j];
             const float mt = ha[t][j];                                  // Abar_t - 1
-            const float cdy = dpp_bcast_mul<src>(bq.y, dys[kk]);        // dytil C
+            const float cdy = (j == 0 ? bcq[kk].z : bcq[kk].w) * dys[kk];   // dytil C
             const float l = g[j] + cdy;                                 // lam_t = dytil C + Abar lam_{t+1}
             // Abar_t lam_t = Abar lam_{t+1} + (dytil C + m lam_t), for token t-1: the small increment
             // is formed first, so its rounding onto g's grid varies with dytil C from token to token
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
               X[j] = fmaf(dls[kk] * g[j], q, X[j]);
               Y[j] = fmaf(le, bu, Y[j]);
             }
-            du_p = j == 0 ? dpp_bcast_mul<src>(bq.x, le) : dpp_bcast_fmac<src>(du_p, bq.x, le);
+            du_p = j == 0 ? bcq[kk].x * le : fmaf(bcq[kk].y, le, du_p);
             dBv[j * 4 + kk] = le * uus[kk];
             dCv[j * 4 + kk] = dys[kk] * hh[t][j];
           });
