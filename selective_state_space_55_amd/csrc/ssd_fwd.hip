@@ -25,9 +25,11 @@
 // operands, fp16 for the state update) from LDS with fp32 accumulation; the operand layouts (lane l
 // holds 8 consecutive k) make each operand one 16-byte LDS read.  Per chunk:
 //   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes),
-//              and x scaled by exp(cum_Q - cum_j) w_j in fp16 (11 significant
+//              and x scaled by exp(cum_Q - cum_j) w_j 2^k in fp16 (11 significant
 //              bits for the state update, whose products are fp16 with B
-//              converted from bf16 -- one bf16 part lost too much); the
+//              converted from bf16 -- one bf16 part lost too much; 2^k puts
+//              the chunk's largest weight in [1, 2), so a small Delta does not
+//              push the operand into fp16's subnormals); the
 //              chunk's decay terms were computed during the previous chunk
 //              (one wave turns dt into log a (softplus, A_h), w and a running
 //              sum over the chunk with a DPP prefix scan, into the other of
@@ -39,6 +41,7 @@
 //   A3      -- waves 4-7: Y += M X, Y to LDS (token-major); S to LDS
 //   epilogue -- y = Y + D x (x kept in registers from its load), SiLU(z) gate,
 //              one 16-byte store per thread
+// At P = 32 a barrier ends each of the first three phases (three per chunk).
 // At P = 64 (two x and two M tiles in LDS) chunk c's A3 moves into chunk c+1's
 // A2 -- waves 4-7 first finish chunk c's Y with M X and store it -- and its
 // epilogue into chunk c+1's last phase, so a chunk has two barriers; the decay
@@ -49,8 +52,11 @@
 // token-major tiles with ds_read_b64_tr_b16 (gfx950's transposing LDS read:
 // in each 16-lane group, lane 4a + c receives element c of the 4-element row
 // pieces addressed by lanes a, a + 4, a + 8, a + 12), so nothing is transposed
-// explicitly.  Three barriers per chunk; chunk c+1's global loads are issued
-// at the start of A2 of chunk c.
+// explicitly.  Chunk c+1's global loads are issued at the start of A2 of chunk c.
+//
+// Ranges: B converted to fp16 keeps its bits for |B| in [2^-14, 65504]; the
+// scaled x for |x| in [2^-14, 2^15) at the chunk's largest weight (from 2^15 up
+// it can overflow to inf); everything else has fp32's range.
 #include "internal.h"
 #include "io.h"
 
@@ -91,13 +97,18 @@ struct SsdLds {
   static constexpr int kBs = kQ * kRowN;      // B     [j][n]
   static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], fp16
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
-  static constexpr int kST = P * kRowN;      // S^T   [p][n]
+  static constexpr int kST = P * kRowN;      // S^T   [p][n], twice: bf16 S and bf16 (S - that)
   // P = 64 keeps two x tiles and two M tiles: chunk c's M X runs in chunk c+1's
   // second phase (one barrier fewer per chunk)
   static constexpr int kBuf = P == 64 ? 2 : 1;
-  static constexpr int kHalves = kBuf * kXtm + kCs + kBs + kXs + kBuf * kMs + kST;
+  static constexpr int kHalves = kBuf * kXtm + kCs + kBs + kXs + kBuf * kMs + 2 * kST;
   static constexpr int kYRow = P + 4;         // Y fp32 [i][p]
-  static constexpr int kFloats = kQ * kYRow + 2 * (4 * kQ + 4);   // Y, then two sets of decay terms
+  // At P = 32 the fp32 Y tile takes the M tile's place (the same 144-byte rows):
+  // a Y wave writes only the rows of M it has just multiplied, and M is next
+  // written after the following stage barrier.  This keeps two workgroups per CU.
+  static constexpr bool kYinM = P == 32;
+  static_assert(!kYinM || (kYRow * 4 == kRowQ * 2 && kBuf == 1), "Y rows must match M rows");
+  static constexpr int kFloats = (kYinM ? 0 : kQ * kYRow) + 2 * (4 * kQ + 4);   // Y, then two sets of decay terms
   static constexpr size_t bytes() { return 2 * (size_t)kHalves + 4 * (size_t)kFloats; }
 };
 
@@ -113,8 +124,9 @@ __device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// bf16 -> fp16, element by element (B values are well inside fp16's range; the
-// conversion is exact for them down to fp16's normal minimum)
+// bf16 -> fp16, element by element: exact for |B| in [2^-14, 65504] (bf16's 8
+// significant bits fit in fp16's 11); below 2^-14 fp16 is subnormal and keeps
+// fewer bits, from 2^-24 down it is 0, and from 65520 up it is inf
 __device__ __forceinline__ f16x8 to_f16(bf16x8 v) {
   f16x8 r;
 #pragma unroll
@@ -135,6 +147,7 @@ __device__ __forceinline__ float expm1_f(float x) {
   return __expf(x) - 1.0f;
 }
 
+// v from another lane (DPP move; lanes with no source get 0)
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add_src(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xf, true));
@@ -150,6 +163,20 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   v += dpp_add_src<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
   v += dpp_add_src<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
   return v;
+}
+
+// largest |v| over the 64 lanes: the same shifts and row broadcasts as the
+// prefix sum with max in place of +, which leaves the total in lane 63 (lanes
+// with no source read 0, which |v| >= 0 absorbs)
+__device__ __forceinline__ float wave_max_abs(float v) {
+  v = fabsf(v);
+  v = fmaxf(v, dpp_add_src<0x111, 0xf>(v));
+  v = fmaxf(v, dpp_add_src<0x112, 0xf>(v));
+  v = fmaxf(v, dpp_add_src<0x114, 0xf>(v));
+  v = fmaxf(v, dpp_add_src<0x118, 0xf>(v));
+  v = fmaxf(v, dpp_add_src<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_add_src<0x143, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -182,10 +209,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   uint16_t* Xs = Bs + L::kBs;   // fp16 bits
   uint16_t* Ms = Xs + L::kXs;
   uint16_t* ST = Ms + L::kBuf * L::kMs;
-  float* Yf = reinterpret_cast<float*>(ST + L::kST);   // [i][p]
+  uint16_t* STlo = ST + L::kST;
+  float* Yf = L::kYinM ? reinterpret_cast<float*>(Ms) : reinterpret_cast<float*>(STlo + L::kST);   // [i][p]
   // decay terms of a chunk, double-buffered (chunk c uses set c & 1, while one wave
   // computes chunk c+1's into the other set): [set][cum | ecum | scl | wv | atot]
-  float* dterms = Yf + kQ * kYRow;
+  float* dterms = L::kYinM ? reinterpret_cast<float*>(STlo + L::kST) : Yf + kQ * kYRow;
   constexpr int kDSet = 4 * kQ + 4;
 
   const int tid = threadIdx.x;
@@ -292,14 +320,25 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       S[4 * q + 0] = v.x; S[4 * q + 1] = v.y; S[4 * q + 2] = v.z; S[4 * q + 3] = v.w;
     }
   }
+  // S for the next chunk's C S_in as two bf16 parts, hi = bf16(S) and
+  // lo = bf16(S - hi) (S - hi is exact in fp32): C hi + C lo carries S to 2^-17,
+  // where hi alone (2^-9) is read by every token of the chunk and, once the
+  // decay is slow, by many chunks -- the same rounding each time
   auto write_ST = [&]() {
     if (!has_s) return;
     const int p = s_pb * 32 + l32;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int n = s_nb * 32 + 8 * q + 4 * h32;
-      *reinterpret_cast<uint2*>(ST + p * kRowN + n) =
-          make_uint2(pack_bf16x2(S[4 * q + 0], S[4 * q + 1]), pack_bf16x2(S[4 * q + 2], S[4 * q + 3]));
+      uint32_t hw[2], lw[2];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float s0 = S[4 * q + 2 * k], s1 = S[4 * q + 2 * k + 1];
+        hw[k] = pack_bf16x2(s0, s1);
+        lw[k] = pack_bf16x2(s0 - bf(hw[k] & 0xffffu), s1 - bf(hw[k] >> 16));
+      }
+      *reinterpret_cast<uint2*>(ST + p * kRowN + n) = make_uint2(hw[0], hw[1]);
+      *reinterpret_cast<uint2*>(STlo + p * kRowN + n) = make_uint2(lw[0], lw[1]);
     }
   };
   write_ST();
@@ -319,12 +358,24 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     const float wj = a.euler ? Delta : (Ah != 0.0f ? expm1_f(la) / Ah : Delta);
     const float cs = wave_prefix_sum(la);
     const float tot = __shfl(cs, 63);
+    // The state update's x operand is x exp(cum_Q - cum_j) w_j in fp16, whose
+    // normal range starts at 2^-14: at Delta ~ 1e-4 the weight alone is ~2^-13.
+    // Scale the chunk's weights by 2^k so the largest is in [1, 2) (exact; S is
+    // scaled by 2^k before the products and by 2^-k after): x then keeps its
+    // 11 bits for |x| in [2^-14, 2^15) whatever Delta is
+    const float sc = __expf(tot - cs) * wj;
+    const float mx = wave_max_abs(sc);
+    const int e2 = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 1;   // mx = f 2^e2, f in [0.5, 1)
+    const int k2 = min(max(1 - e2, -64), 64);
     float* o = dterms + set * kDSet;
     o[lane] = cs;
     o[kQ + lane] = __expf(cs);
-    o[2 * kQ + lane] = __expf(tot - cs) * wj;
+    o[2 * kQ + lane] = ldexpf(sc, k2);
     o[3 * kQ + lane] = wj;
-    if (lane == 0) o[4 * kQ] = __expf(tot);
+    if (lane == 0) {
+      o[4 * kQ] = ldexpf(__expf(tot), k2);
+      o[4 * kQ + 1] = ldexpf(1.0f, -k2);
+    }
   };
 
   // Y += M X over a Y tile's causal k range, then the tile to LDS (token-major)
@@ -403,11 +454,11 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     const int dset = (int)(c & 1);
     const float* cum = dterms + dset * kDSet;   // running sum of log a in the chunk
     const float* ecum = cum + kQ;               // exp(cum_i)
-    const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j
+    const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j 2^k
     const float* wv = scl + kQ;                 // w_j
-    const float* atot = wv + kQ;                // exp(cum_Q)
+    const float* atot = wv + kQ;                // exp(cum_Q) 2^k, 2^-k
     if (has_x) {
-      // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j,
+      // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j 2^k,
       // in fp16 (11 significant bits; the state update's products are fp16 x fp16)
       const float sc = scl[xj];
       const uint32_t cw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
@@ -455,15 +506,18 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         *reinterpret_cast<uint2*>(Mc + i * kRowQ + j0) = make_uint2(pack_bf16x2(m4[0], m4[1]), pack_bf16x2(m4[2], m4[3]));
       }
     } else if (has_y) {
-      // C S_in over N (two chains), rows scaled by exp(cum_i)
+      // C S_in = C hi + C lo over N (two chains), rows scaled by exp(cum_i)
       f32x16 y1 = {};
 #pragma unroll
       for (int s = 0; s < N / 16; s += 2) {
-        yacc = mfma(lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * s + 8 * h32),
-                    lds_b8(ST + (yp * 32 + l32) * kRowN + 16 * s + 8 * h32), yacc);
+        const bf16x8 c0 = lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * s + 8 * h32);
+        const bf16x8 c1 = lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32);
+        const int o0 = (yp * 32 + l32) * kRowN + 16 * s + 8 * h32, o1 = o0 + 16;
         f32x16& y = P == 64 ? y1 : yacc;
-        y = mfma(lds_b8(Cs + (yi * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32),
-                 lds_b8(ST + (yp * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32), y);
+        yacc = mfma(c0, lds_b8(STlo + o0), yacc);
+        y = mfma(c1, lds_b8(STlo + o1), y);
+        yacc = mfma(c0, lds_b8(ST + o0), yacc);
+        y = mfma(c1, lds_b8(ST + o1), y);
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -475,7 +529,8 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       }
     }
     if (has_s) {
-      const float at = atot[0];
+      // S 2^k = exp(cum_Q) 2^k S + B^T (x exp(cum_Q - cum_j) w_j 2^k), then S = 2^-k (S 2^k)
+      const float at = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(atot[0])));
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] *= at;
 #pragma unroll
@@ -483,6 +538,9 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         const f16x8 av = to_f16(lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane));
         S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
       }
+      const float unscale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(atot[1])));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[r] *= unscale;
     }
     if constexpr (kDefer) {
       if (w == kDtWave && c + 1 < nchunk) dt_terms(dt_next, t0 + kQ, dset ^ 1);   // the next chunk's

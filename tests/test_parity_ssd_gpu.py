@@ -6,8 +6,11 @@ runs are identical; a split at a chunk boundary resumes bit for bit and at any
 other token within tolerance; the full-size layer on sampled heads.
 
 Tolerance: the products take bf16 operands (x, B, C as given; the masked decay
-matrix, the scaled B and the state rounded to bf16) with fp32 accumulation, so
-the bar is the bf16 one used throughout, 1e-2 (max error over max(|ref|, rms))."""
+matrix and the copy of the state that C reads rounded to bf16) or, in the state
+update, fp16 ones (B, and x times its decayed weight and a per-chunk power of
+two) with fp32 accumulation, so the bar is the bf16 one used throughout, 1e-2
+(max error over max(|ref|, rms)).  The small-Delta cases run where the weight
+alone is near fp16's subnormal range."""
 import sys
 
 import pytest
@@ -170,3 +173,19 @@ def test_ssd_full_size_sampled_heads():
         yr, fr = ref(sub)
         check(f"y b{bb} h{hh}", y[bb:bb + 1, :, hh:hh + 1], yr)
         check(f"final b{bb} h{hh}", fs[bb:bb + 1, hh:hh + 1], fr)
+
+
+@pytest.mark.parametrize("x_std,disc", [(1.0, "zoh"), (0.01, "zoh"), (0.01, "euler")])
+def test_ssd_small_delta(x_std, disc):
+    """Delta ~ 1e-4 (softplus(dt_bias) in [1e-4, 2e-4], dt ~ N(0, 0.1^2)): the state update's weight
+    exp(cum_Q - cum_j) w_j is then ~2^-13, at the bottom of fp16's normal range, and with x ~ N(0, 0.01^2)
+    the product x w is ~1e-6 (fp16 subnormal, 4 bits) unless the chunk is scaled; B, C ~ N(0, 1) and
+    4096 tokens, so the state keeps its inputs over the whole sequence (|A| Delta L <= 6.5)."""
+    b, L, H, N = 1, 4096, 4, 128
+    inp = ssd_inputs(b, L, H, 64, N, seed=7, gated=True, initial_state=True, x_std=x_std, dt_std=0.1,
+                     bc_std=1.0, bias_range=(1e-4, 2e-4))
+    say(f"small Delta x_std={x_std} {disc}")
+    y, fs = gpu(inp, True, disc)
+    yr, fsr = ref(inp, True, disc)
+    check("y", y, yr)
+    check("final_state", fs, fsr)

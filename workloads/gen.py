@@ -211,20 +211,25 @@ def conv_inputs(batch: int, dim: int, seqlen: int, K: int, io: str, *, seed: int
 
 
 def ssd_inputs(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int, *, seed: int = 0,
-               gated: bool = False, initial_state: bool = False, threads: Optional[int] = None):
+               gated: bool = False, initial_state: bool = False, threads: Optional[int] = None,
+               x_std: float = 1.0, dt_std: float = 1.0, bc_std: Optional[float] = None,
+               bias_range: tuple = (1e-3, 1e-1)):
     """Inputs of the multi-head SSM (state-space-duality form), token-major, bf16 io:
-    x, z (batch, L, H, P) ~ N(0, 1); dt (batch, L, H) ~ N(0, 1); B, C (batch, L, N) ~ N(0, 1/N) (a
-    readout over N states then has unit scale); A_log = log(U[1, 16]) per head; D ~ N(0, 1);
-    dt_bias = log(expm1(U[1e-3, 1e-1])) per head; initial_state (batch, H, P, N) ~ N(0, 0.1^2)."""
-    x = _normal_rows(seed, (K_U,), batch * seqlen, nheads * headdim, "bf16", threads=threads)
-    dt = _normal_rows(seed, (K_DELTA,), batch * seqlen, nheads, "bf16", threads=threads)
-    B = _normal_rows(seed, (K_B,), batch * seqlen, dstate, "bf16", std=1.0 / math.sqrt(dstate), threads=threads)
-    C = _normal_rows(seed, (K_C,), batch * seqlen, dstate, "bf16", std=1.0 / math.sqrt(dstate), threads=threads)
+    x, z (batch, L, H, P) ~ N(0, 1) (x ~ N(0, x_std^2)); dt (batch, L, H) ~ N(0, dt_std^2); B, C
+    (batch, L, N) ~ N(0, 1/N) (a readout over N states then has unit scale; N(0, bc_std^2) when
+    given); A_log = log(U[1, 16]) per head; D ~ N(0, 1); dt_bias = log(expm1(U[bias_range])) per
+    head (softplus(dt_bias) uniform on bias_range, default [1e-3, 1e-1]); initial_state
+    (batch, H, P, N) ~ N(0, 0.1^2)."""
+    bcs = 1.0 / math.sqrt(dstate) if bc_std is None else bc_std
+    x = _normal_rows(seed, (K_U,), batch * seqlen, nheads * headdim, "bf16", std=x_std, threads=threads)
+    dt = _normal_rows(seed, (K_DELTA,), batch * seqlen, nheads, "bf16", std=dt_std, threads=threads)
+    B = _normal_rows(seed, (K_B,), batch * seqlen, dstate, "bf16", std=bcs, threads=threads)
+    C = _normal_rows(seed, (K_C,), batch * seqlen, dstate, "bf16", std=bcs, threads=threads)
     z = (_normal_rows(seed, (K_Z,), batch * seqlen, nheads * headdim, "bf16", threads=threads)
          .view(batch, seqlen, nheads, headdim) if gated else None)
     A_log = torch.from_numpy(np.log(_gen(seed, (K_SSDA, 0)).uniform(1.0, 16.0, size=nheads)).astype(np.float32))
     D = torch.from_numpy(_gen(seed, (K_D, 0)).standard_normal(nheads, dtype=np.float32))
-    u = _gen(seed, (K_BIAS, 0)).uniform(1e-3, 1e-1, size=nheads)
+    u = _gen(seed, (K_BIAS, 0)).uniform(bias_range[0], bias_range[1], size=nheads)
     dt_bias = torch.from_numpy(np.log(np.expm1(u)).astype(np.float32))
     h0 = None
     if initial_state:
