@@ -314,13 +314,11 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *   initial_state, final_state (batch, nheads, headdim, dstate) f32, 16-byte aligned, NULL allowed
  *   z                NULL means no gate
  * Supported: io_dtype MAMBA_SCAN_BF16, headdim a multiple of 32 up to 256, dstate 64 or 128
- * (others return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 32 < 2^31.  Products use
- * bf16 operands (fp16 for the state update) with fp32 accumulation; the state is carried in fp32.
- * The state update's fp16 operands are B and x w_t times the chunk's decay, the latter scaled per
- * 64-token chunk by a power of two that puts its largest weight in [1, 2) (undone exactly on the
- * fp32 state), so Delta's size costs no precision; they keep their full precision for |B| in
- * [2^-14, 65504] and |x| in [2^-14, 2^15): smaller values lose bits gradually (fp16 subnormals),
- * |B| > 65504 or |x| >= 2^15 can overflow to inf.  No workspace.
+ * (others return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 32 < 2^31 and
+ * nheads * headdim <= 2^24.  Products take bf16 operands with fp32 accumulation, and the state is
+ * carried in fp32.  Where a product reads the fp32 state, or x times its decayed input weight,
+ * that operand is split as bf16 hi + bf16 (rest), which gives 16 significant bits over fp32's
+ * range.  No workspace.
  */
 int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void* B, const void* C, const float* D,
                   const void* z, const float* dt_bias, const float* initial_state, float* final_state, void* y,

@@ -361,6 +361,8 @@ int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void*
   if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
   if (!mul_ok(batch, nheads * (headdim / 32), &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid
+  // a chunk's 64 token rows of x / y (nheads * headdim bf16 each) are addressed with 32-bit offsets
+  if (nheads > (1 << 24) / headdim) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!mul_ok(t, seqlen, &t) || !mul_ok(t, headdim * 2, &t)) return MAMBA_SCAN_ERR_SHAPE;
   if (!A_log) return MAMBA_SCAN_ERR_NULL;
   if (seqlen > 0 && (!x || !dt || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;

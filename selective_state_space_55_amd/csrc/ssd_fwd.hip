@@ -64,7 +64,6 @@ namespace mscan {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kQ = 64;      // tokens per chunk
@@ -95,13 +94,13 @@ struct SsdLds {
   static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
   static constexpr int kCs = kQ * kRowN;      // C     [i][n]
   static constexpr int kBs = kQ * kRowN;      // B     [j][n]
-  static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], fp16
+  static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], twice: bf16 and bf16 of the rest
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
   static constexpr int kST = P * kRowN;      // S^T   [p][n], twice: bf16 S and bf16 (S - that)
   // P = 64 keeps two x tiles and two M tiles: chunk c's M X runs in chunk c+1's
   // second phase (one barrier fewer per chunk)
   static constexpr int kBuf = P == 64 ? 2 : 1;
-  static constexpr int kHalves = kBuf * kXtm + kCs + kBs + kXs + kBuf * kMs + 2 * kST;
+  static constexpr int kHalves = kBuf * kXtm + kCs + kBs + 2 * kXs + kBuf * kMs + 2 * kST;
   static constexpr int kYRow = P + 4;         // Y fp32 [i][p]
   // At P = 32 the fp32 Y tile takes the M tile's place (the same 144-byte rows):
   // a Y wave writes only the rows of M it has just multiplied, and M is next
@@ -120,24 +119,6 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-// bf16 -> fp16, element by element: exact for |B| in [2^-14, 65504] (bf16's 8
-// significant bits fit in fp16's 11); below 2^-14 fp16 is subnormal and keeps
-// fewer bits, from 2^-24 down it is 0, and from 65520 up it is inf
-__device__ __forceinline__ f16x8 to_f16(bf16x8 v) {
-  f16x8 r;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) r[k] = (_Float16)(float)v[k];
-  return r;
-}
-
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  const _Float16 a = (_Float16)lo, b = (_Float16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
 
 __device__ __forceinline__ float bf(uint32_t h16) { return __uint_as_float(h16 << 16); }
 
@@ -163,20 +144,6 @@ __device__ __forceinline__ float wave_prefix_sum(float v) {
   v += dpp_add_src<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
   v += dpp_add_src<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
   return v;
-}
-
-// largest |v| over the 64 lanes: the same shifts and row broadcasts as the
-// prefix sum with max in place of +, which leaves the total in lane 63 (lanes
-// with no source read 0, which |v| >= 0 absorbs)
-__device__ __forceinline__ float wave_max_abs(float v) {
-  v = fabsf(v);
-  v = fmaxf(v, dpp_add_src<0x111, 0xf>(v));
-  v = fmaxf(v, dpp_add_src<0x112, 0xf>(v));
-  v = fmaxf(v, dpp_add_src<0x114, 0xf>(v));
-  v = fmaxf(v, dpp_add_src<0x118, 0xf>(v));
-  v = fmaxf(v, dpp_add_src<0x142, 0xa>(v));
-  v = fmaxf(v, dpp_add_src<0x143, 0xc>(v));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -206,8 +173,9 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   uint16_t* Xtm = sm;
   uint16_t* Cs = Xtm + L::kBuf * L::kXtm;
   uint16_t* Bs = Cs + L::kCs;
-  uint16_t* Xs = Bs + L::kBs;   // fp16 bits
-  uint16_t* Ms = Xs + L::kXs;
+  uint16_t* Xs = Bs + L::kBs;     // x exp(cum_Q - cum_j) w_j: bf16 part
+  uint16_t* XsLo = Xs + L::kXs;   // and bf16 of what that leaves
+  uint16_t* Ms = XsLo + L::kXs;
   uint16_t* ST = Ms + L::kBuf * L::kMs;
   uint16_t* STlo = ST + L::kST;
   float* Yf = L::kYinM ? reinterpret_cast<float*>(Ms) : reinterpret_cast<float*>(STlo + L::kST);   // [i][p]
@@ -271,38 +239,43 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     uint4 bq[kBCr], cq[kBCr];
     uint32_t dt;
   };
-  auto ld16 = [&](const uint16_t* p, bool ok) -> uint4 {
-    return ok ? *reinterpret_cast<const uint4*>(p) : make_uint4(0, 0, 0, 0);
+  // Global traffic goes through buffer descriptors over the chunk's rows (built
+  // in scalar registers per chunk): the per-thread offsets stay fixed, and rows
+  // past the sequence's end fall outside the descriptor, so their loads return
+  // 0 and their stores are dropped -- no per-lane bounds checks or 64-bit
+  // address arithmetic.  Tokens t0 .. t0 + 63 of a (token, element) array with
+  // tstride elements per token, of which the first tail belong to this thread
+  // block: 64 whole rows while they last, then up to the last token's tail.
+  auto rs_chunk = [&](const uint16_t* base, int64_t t0, int64_t tstride, int tail) {
+    const int64_t left = Lq - t0;
+    const int64_t bytes = left <= 0 ? 0 : left >= kQ ? kQ * tstride * 2 : ((left - 1) * tstride + tail) * 2;
+    return make_rsrc(base + (left <= 0 ? 0 : t0 * tstride), (int)bytes);
   };
-  // per-thread element offsets inside a chunk (chunk c adds c * kQ tokens)
-  const int64_t x_off = (int64_t)xj * xs_t + xp8;
-  int bc_off[kBCr], bc_j[kBCr];
+  auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+  };
+  // per-thread byte offsets inside a chunk's rows
+  const int x_off = (xj * (int)xs_t + xp8) * 2;
+  int bc_off[kBCr];
 #pragma unroll
   for (int r = 0; r < kBCr; ++r) {
     const int e = tid + kNT * r;
-    bc_j[r] = e / (N / 8);
-    bc_off[r] = bc_j[r] * N + (e % (N / 8)) * 8;
+    bc_off[r] = ((e / (N / 8)) * N + (e % (N / 8)) * 8) * 2;
   }
   auto prefetch = [&](int64_t c, Pf& f) {
     const int64_t t0 = c * kQ;
-    const bool full = t0 + kQ <= Lq;   // uniform: only the last chunk is partial
     if (has_x) {
-      const bool ok = full || t0 + xj < Lq;
-      const int64_t o = t0 * xs_t + x_off;
-      f.x = ld16(xb + o, ok);
-      if (!kLean) f.z = zb ? ld16(zb + o, ok) : make_uint4(0, 0, 0, 0);
+      f.x = ld16(rs_chunk(xb, t0, xs_t, P), x_off);
+      if (!kLean) f.z = zb ? ld16(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
     }
+    const __amdgpu_buffer_rsrc_t rb = rs_chunk(Bb, t0, N, N), rc = rs_chunk(Cb, t0, N, N);
 #pragma unroll
     for (int r = 0; r < kBCr; ++r) {
-      const bool ok = full || t0 + bc_j[r] < Lq;
-      const int64_t o = t0 * N + bc_off[r];
-      f.bq[r] = ld16(Bb + o, ok);
-      f.cq[r] = ld16(Cb + o, ok);
+      f.bq[r] = ld16(rb, bc_off[r]);
+      f.cq[r] = ld16(rc, bc_off[r]);
     }
-    if (w == kDtWave) {
-      const int64_t t = t0 + (kDefer ? kQ : 0) + lane;
-      f.dt = t < Lq ? (uint32_t)dtb[t * H] : 0u;
-    }
+    if (w == kDtWave)
+      f.dt = __builtin_amdgcn_raw_buffer_load_b16(rs_chunk(dtb, t0 + (kDefer ? kQ : 0), H, 1), lane * H * 2, 0, 0);
   };
 
   // ---- state tiles: S[n][p] rows 32 nb .., columns 32 pb .. ----
@@ -358,24 +331,12 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     const float wj = a.euler ? Delta : (Ah != 0.0f ? expm1_f(la) / Ah : Delta);
     const float cs = wave_prefix_sum(la);
     const float tot = __shfl(cs, 63);
-    // The state update's x operand is x exp(cum_Q - cum_j) w_j in fp16, whose
-    // normal range starts at 2^-14: at Delta ~ 1e-4 the weight alone is ~2^-13.
-    // Scale the chunk's weights by 2^k so the largest is in [1, 2) (exact; S is
-    // scaled by 2^k before the products and by 2^-k after): x then keeps its
-    // 11 bits for |x| in [2^-14, 2^15) whatever Delta is
-    const float sc = __expf(tot - cs) * wj;
-    const float mx = wave_max_abs(sc);
-    const int e2 = mx > 0.0f ? __builtin_amdgcn_frexp_expf(mx) : 1;   // mx = f 2^e2, f in [0.5, 1)
-    const int k2 = min(max(1 - e2, -64), 64);
     float* o = dterms + set * kDSet;
     o[lane] = cs;
     o[kQ + lane] = __expf(cs);
-    o[2 * kQ + lane] = ldexpf(sc, k2);
+    o[2 * kQ + lane] = __expf(tot - cs) * wj;
     o[3 * kQ + lane] = wj;
-    if (lane == 0) {
-      o[4 * kQ] = ldexpf(__expf(tot), k2);
-      o[4 * kQ + 1] = ldexpf(1.0f, -k2);
-    }
+    if (lane == 0) o[4 * kQ] = __expf(tot);
   };
 
   // Y += M X over a Y tile's causal k range, then the tile to LDS (token-major)
@@ -395,8 +356,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   // token xj, channels xp8 .. +7 of chunk ce: y = Y + D x, gate, store (x from the
   // thread's registers, or its own piece of the x tile Xb)
   auto epilogue = [&](int64_t ce, const uint16_t* Xb, uint4 xreg, uint4 zreg) {
-    const int64_t t = ce * kQ + xj;
-    if (has_x && t < Lq) {
+    if (has_x) {
       const float4 y0 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8);
       const float4 y1 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4);
       const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
@@ -414,7 +374,9 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         }
         o[q] = pack_bf16x2(v0, v1);
       }
-      *reinterpret_cast<uint4*>(yb + t * xs_t + xp8) = make_uint4(o[0], o[1], o[2], o[3]);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_uint4(o[0], o[1], o[2], o[3])),
+          rs_chunk(yb, ce * kQ, xs_t, P), x_off, 0, 0);
     }
   };
 
@@ -424,7 +386,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   f32x16 yprev = {};   // chunk c-1's C S_in, waiting for its M X (kDefer)
   if (w == kDtWave) {
     uint32_t dt0 = pf.dt;
-    if constexpr (kDefer) dt0 = lane < Lq ? (uint32_t)dtb[(int64_t)lane * H] : 0u;
+    if constexpr (kDefer) dt0 = __builtin_amdgcn_raw_buffer_load_b16(rs_chunk(dtb, 0, H, 1), lane * H * 2, 0, 0);
     dt_terms(dt0, 0, 0);
   }
   lds_barrier();   // chunk 0's decay terms, read at its stage
@@ -434,8 +396,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     // ---- stage: rows as loaded; decay terms ----
     xcur = pf.x;
     if constexpr (kLean) {
-      const bool ok = t0 + kQ <= Lq || t0 + xj < Lq;
-      zcur = has_x && zb ? ld16(zb + t0 * xs_t + x_off, ok) : make_uint4(0, 0, 0, 0);
+      zcur = has_x && zb ? ld16(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
     } else {
       zcur = pf.z;
     }
@@ -454,18 +415,24 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     const int dset = (int)(c & 1);
     const float* cum = dterms + dset * kDSet;   // running sum of log a in the chunk
     const float* ecum = cum + kQ;               // exp(cum_i)
-    const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j 2^k
+    const float* scl = ecum + kQ;               // exp(cum_Q - cum_j) w_j
     const float* wv = scl + kQ;                 // w_j
-    const float* atot = wv + kQ;                // exp(cum_Q) 2^k, 2^-k
+    const float* atot = wv + kQ;                // exp(cum_Q)
     if (has_x) {
-      // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j 2^k,
-      // in fp16 (11 significant bits; the state update's products are fp16 x fp16)
+      // the thread's own x piece (token xj, channels xp8 ..) scaled by exp(cum_Q - cum_j) w_j, as
+      // two bf16 parts hi + lo (the rest after hi is exact in fp32): 16 significant bits over
+      // fp32's range
       const float sc = scl[xj];
       const uint32_t cw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
-      uint32_t hv[4];
+      uint32_t hv[4], lv[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) hv[k] = pack_f16x2(bf(cw[k] & 0xffffu) * sc, bf(cw[k] >> 16) * sc);
+      for (int k = 0; k < 4; ++k) {
+        const float v0 = bf(cw[k] & 0xffffu) * sc, v1 = bf(cw[k] >> 16) * sc;
+        hv[k] = pack_bf16x2(v0, v1);
+        lv[k] = pack_bf16x2(v0 - bf(hv[k] & 0xffffu), v1 - bf(hv[k] >> 16));
+      }
       *reinterpret_cast<uint4*>(Xs + xj * kRowP + xp8) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      *reinterpret_cast<uint4*>(XsLo + xj * kRowP + xp8) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
     }
     lds_barrier();
 
@@ -500,9 +467,14 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         const float cja[4] = {cj.x, cj.y, cj.z, cj.w}, wja[4] = {wj.x, wj.y, wj.z, wj.w};
         float m4[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          m4[r] = (j0 + r <= i) ? (P == 64 ? g0[4 * q + r] + g1[4 * q + r] : g0[4 * q + r]) * __expf(ci - cja[r]) * wja[r]
-                                : 0.0f;
+        for (int r = 0; r < 4; ++r) {
+          // every element computed, the upper triangle selected away (no branch per element)
+          // (exp(-200) is 0 in fp32, so the upper triangle comes out 0 from the same
+          // instructions: no branch per element)
+          const float d = j0 + r <= i ? ci - cja[r] : -200.0f;
+          const float g = P == 64 ? g0[4 * q + r] + g1[4 * q + r] : g0[4 * q + r];
+          m4[r] = g * __expf(d) * wja[r];
+        }
         *reinterpret_cast<uint2*>(Mc + i * kRowQ + j0) = make_uint2(pack_bf16x2(m4[0], m4[1]), pack_bf16x2(m4[2], m4[3]));
       }
     } else if (has_y) {
@@ -529,18 +501,16 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       }
     }
     if (has_s) {
-      // S 2^k = exp(cum_Q) 2^k S + B^T (x exp(cum_Q - cum_j) w_j 2^k), then S = 2^-k (S 2^k)
+      // S = exp(cum_Q) S + B^T (x exp(cum_Q - cum_j) w_j), the scaled x as hi + lo
       const float at = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(atot[0])));
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] *= at;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f16x8 av = to_f16(lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane));
-        S = mfma(av, __builtin_bit_cast(f16x8, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane)), S);
+        const bf16x8 bv = lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane);
+        S = mfma(bv, lds_opnd_tr(XsLo, kRowP, 16 * s, s_pb * 32, lane), S);
+        S = mfma(bv, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane), S);
       }
-      const float unscale = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(atot[1])));
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[r] *= unscale;
     }
     if constexpr (kDefer) {
       if (w == kDtWave && c + 1 < nchunk) dt_terms(dt_next, t0 + kQ, dset ^ 1);   // the next chunk's

@@ -16,7 +16,7 @@ import pytest
 
 from selective_state_space_55_amd import build as hipbuild
 
-ASM_SRCS = ["scan_fwd.hip", "scan_step.hip"]
+ASM_SRCS = ["scan_fwd.hip", "scan_fwd_varlen.hip", "scan_step.hip", "scan_bwd.hip", "conv1d.hip", "ssd_fwd.hip"]
 
 
 @pytest.fixture(scope="module")
