@@ -90,10 +90,13 @@ template <int N, int P>
 struct SsdLds {
   static constexpr int kRowQ = kQ + kPadH;    // rows over Q tokens
   static constexpr int kRowN = N + kPadH;     // rows over N states
+  // B's rows take 16 elements of padding: its transposing reads take 32 bytes
+  // from each of 4 consecutive rows, which a 288-byte pitch puts in distinct banks
+  static constexpr int kRowNB = N + 2 * kPadH;
   static constexpr int kRowP = P + kPadH;     // rows over P channels
   static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
   static constexpr int kCs = kQ * kRowN;      // C     [i][n]
-  static constexpr int kBs = kQ * kRowN;      // B     [j][n]
+  static constexpr int kBs = kQ * kRowNB;     // B     [j][n]
   static constexpr int kXs = kQ * kRowP;      // scaled x [j][p], twice: bf16 and bf16 of the rest
   static constexpr int kMs = kQ * kRowQ;      // M     [i][j]
   static constexpr int kST = P * kRowN;      // S^T   [p][n], twice: bf16 S and bf16 (S - that)
@@ -101,7 +104,9 @@ struct SsdLds {
   // second phase (one barrier fewer per chunk)
   static constexpr int kBuf = P == 64 ? 2 : 1;
   static constexpr int kHalves = kBuf * kXtm + kCs + kBs + 2 * kXs + kBuf * kMs + 2 * kST;
-  static constexpr int kYRow = P + 4;         // Y fp32 [i][p]
+  // Y fp32 [i][p]; at P = 64 a 288-byte pitch puts the two half-waves' rows (4
+  // apart) in disjoint banks
+  static constexpr int kYRow = P == 64 ? P + 8 : P + 4;
   // At P = 32 the fp32 Y tile takes the M tile's place (the same 144-byte rows):
   // a Y wave writes only the rows of M it has just multiplied, and M is next
   // written after the following stage barrier.  This keeps two workgroups per CU.
@@ -168,7 +173,7 @@ __device__ __forceinline__ bf16x8 lds_opnd_tr(const uint16_t* base, int stride, 
 template <int N, int P>
 __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) {
   using L = SsdLds<N, P>;
-  constexpr int kRowQ = L::kRowQ, kRowN = L::kRowN, kRowP = L::kRowP, kYRow = L::kYRow;
+  constexpr int kRowQ = L::kRowQ, kRowN = L::kRowN, kRowNB = L::kRowNB, kRowP = L::kRowP, kYRow = L::kYRow;
   extern __shared__ __align__(16) uint16_t sm[];
   uint16_t* Xtm = sm;
   uint16_t* Cs = Xtm + L::kBuf * L::kXtm;
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       const int e = tid + kNT * r;
       const int j = e / (N / 8), n8 = (e % (N / 8)) * 8;
       *reinterpret_cast<uint4*>(Cs + j * kRowN + n8) = pf.cq[r];
-      *reinterpret_cast<uint4*>(Bs + j * kRowN + n8) = pf.bq[r];
+      *reinterpret_cast<uint4*>(Bs + j * kRowNB + n8) = pf.bq[r];
     }
     const int dset = (int)(c & 1);
     const float* cum = dterms + dset * kDSet;   // running sum of log a in the chunk
@@ -450,10 +455,10 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       f32x16 g0 = {}, g1 = {};
 #pragma unroll
       for (int s = 0; s < N / 16; s += 2) {
-        g0 = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowN + 16 * s + 8 * h32),
+        g0 = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowNB + 16 * s + 8 * h32),
                   lds_b8(Cs + (ib * 32 + l32) * kRowN + 16 * s + 8 * h32), g0);
         f32x16& g = P == 64 ? g1 : g0;
-        g = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32),
+        g = mfma(lds_b8(Bs + (jb * 32 + l32) * kRowNB + 16 * (s + 1) + 8 * h32),
                  lds_b8(Cs + (ib * 32 + l32) * kRowN + 16 * (s + 1) + 8 * h32), g);
       }
       // M[i][j] = G^T[j][i] exp(cum_i - cum_j) w_j for j <= i: the lane holds column i, rows j in runs of 4
@@ -468,9 +473,8 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
         float m4[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          // every element computed, the upper triangle selected away (no branch per element)
-          // (exp(-200) is 0 in fp32, so the upper triangle comes out 0 from the same
-          // instructions: no branch per element)
+          // exp(-200) is 0 in fp32, so the upper triangle comes out 0 from the same
+          // instructions (no branch per element)
           const float d = j0 + r <= i ? ci - cja[r] : -200.0f;
           const float g = P == 64 ? g0[4 * q + r] + g1[4 * q + r] : g0[4 * q + r];
           m4[r] = g * __expf(d) * wja[r];
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       for (int r = 0; r < 16; ++r) S[r] *= at;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 bv = lds_opnd_tr(Bs, kRowN, 16 * s, s_nb * 32, lane);
+        const bf16x8 bv = lds_opnd_tr(Bs, kRowNB, 16 * s, s_nb * 32, lane);
         S = mfma(bv, lds_opnd_tr(XsLo, kRowP, 16 * s, s_pb * 32, lane), S);
         S = mfma(bv, lds_opnd_tr(Xs, kRowP, 16 * s, s_pb * 32, lane), S);
       }

@@ -243,6 +243,8 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, h0=P + 4) == EALIGN
     assert ssd(lib, batch=1 << 20, H=1 << 12) == EUNSUP
     assert ssd(lib, batch=1 << 20, H=1 << 9, hd=256) == EUNSUP   # 2^31 32-channel slices
+    assert ssd(lib, H=(1 << 16) + 1, hd=256) == EUNSUP             # a chunk's rows exceed 32-bit offsets
+    assert ssd(lib, x=None, H=1 << 16, hd=256) == ENULL               # 2^24 channels per token still accepted
 
 
 def fwd_conv(lib, x=P, w=P, cb=None, csi=None, cso=None, delta=P, A_log=P, B=P, C=P, D=None, z=None, bias=None,
