@@ -29,14 +29,21 @@ _LIB_PATH = os.path.join(_HERE, "liboracle_scan.so")
 _lib = None
 
 
-def build(verbose: bool = False) -> str:
-    """Compile scan_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", _LIB_PATH + ".tmp", _SRC, "-lm"]
+def build(verbose: bool = False, out_path: str = _LIB_PATH, sanitize: bool = False) -> str:
+    """Compile scan_oracle.c with gcc (-O2, no fast-math, OpenMP).  sanitize: clang
+    with AddressSanitizer + UndefinedBehaviorSanitizer instead (clang's OpenMP
+    runtime; no sanitizer runtime linked in: the process preloads clang's)."""
+    if sanitize:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+               "-Wl,-rpath,/opt/rocm/llvm/lib", "-o", out_path + ".tmp", _SRC, "-lm"]
+    else:
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", out_path + ".tmp", _SRC, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
-    return _LIB_PATH
+    os.replace(out_path + ".tmp", out_path)
+    return out_path
 
 
 def _bind(path: str):
@@ -63,6 +70,10 @@ def _bind(path: str):
 def _load():
     global _lib
     if _lib is not None:
+        return _lib
+    other = os.environ.get("ORACLE_SCAN_LIBRARY")   # another build (a sanitizer build)
+    if other:
+        _lib = _bind(other)
         return _lib
     if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
         build()

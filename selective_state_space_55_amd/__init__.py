@@ -23,7 +23,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libmamba_scan.so")
+# MAMBA_SCAN_LIBRARY names another build of the same library (a sanitizer or
+# debug build); by default the in-tree build is loaded
+LIB_PATH = os.environ.get("MAMBA_SCAN_LIBRARY") or os.path.join(_HERE, "lib", "libmamba_scan.so")
 
 F32, BF16 = 0, 1
 STATUS = {
