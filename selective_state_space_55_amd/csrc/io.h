@@ -320,4 +320,22 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Debug builds (-DMSCAN_LDS_POISON): a kernel fills its floating-point LDS
+// arrays with all-ones words (NaN as fp32 and as bf16) before first use, and
+// the SSD kernel refills its staging tiles before each chunk; a read of a word
+// that no thread has written since then turns into NaN in the outputs (a
+// missing barrier or an unwritten row).  Whole workgroup; ends at a barrier.
+// In normal builds it is empty.
+__device__ __forceinline__ void lds_poison(void* p, int bytes) {
+#ifdef MSCAN_LDS_POISON
+  __syncthreads();
+  uint32_t* q = static_cast<uint32_t*>(p);
+  for (int i = (int)threadIdx.x; i < bytes / 4; i += (int)blockDim.x) q[i] = 0xffffffffu;
+  __syncthreads();
+#else
+  (void)p;
+  (void)bytes;
+#endif
+}
+
 }  // namespace mscan

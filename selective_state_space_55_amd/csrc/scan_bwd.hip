@@ -155,6 +155,10 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
   __shared__ float ubuf[kCh * kRow];
   __shared__ float bbuf[kG * 4 * NP];   // [group][state pair][token][B of the pair's two states]
   __shared__ float par[kCh];
+  lds_poison(dbuf, (int)sizeof(dbuf));
+  lds_poison(ubuf, (int)sizeof(ubuf));
+  lds_poison(bbuf, (int)sizeof(bbuf));
+  lds_poison(par, (int)sizeof(par));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
   float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][8 waves][64 lanes][2 states]
   float* par = hbuf + LdsB::kHB;          // [2][64] bias, D
+  lds_poison(smem, (int)sizeof(float) * LdsB::kFloats);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   float* bcs = ubuf + LdsH2::kDU;          // [2][kG][NP/2 state pairs][4 tokens][B0, B1, C0, C1]
   float* par = bcs + LdsH2::kBC;           // [2][64]        bias, D
   float* ypart = par + LdsH2::kPar;        // [4][64][kRow]  partial readouts (output pass only)
+  lds_poison(smem, (int)sizeof(float) * LdsH2::floats());
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -625,6 +626,10 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   __shared__ float sA[kCh * kSRow];     // [channel][state]
   __shared__ float sH[kCh * kSRow];
   __shared__ float par[kCh];
+  lds_poison(cbuf, (int)sizeof(cbuf));
+  lds_poison(sA, (int)sizeof(sA));
+  lds_poison(sH, (int)sizeof(sH));
+  lds_poison(par, (int)sizeof(par));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

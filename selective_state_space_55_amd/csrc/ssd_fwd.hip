@@ -187,6 +187,7 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   // decay terms of a chunk, double-buffered (chunk c uses set c & 1, while one wave
   // computes chunk c+1's into the other set): [set][cum | ecum | scl | wv | atot]
   float* dterms = L::kYinM ? reinterpret_cast<float*>(STlo + L::kST) : Yf + kQ * kYRow;
+  lds_poison(sm, (int)L::bytes());
   constexpr int kDSet = 4 * kQ + 4;
 
   const int tid = threadIdx.x;
@@ -409,6 +410,14 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     uint16_t* const Mc = Ms + (kDefer ? (int)(c & 1) * L::kMs : 0);
     uint16_t* const Xprev = Xtm + (kDefer ? (int)((c + 1) & 1) * L::kXtm : 0);   // chunk c-1's
     uint16_t* const Mprev = Ms + (kDefer ? (int)((c + 1) & 1) * L::kMs : 0);
+#ifdef MSCAN_LDS_POISON
+    // every tile this chunk writes before reading it: C, B, the scaled x, this chunk's x and M
+    // tiles and Y (none of them still holds data a later phase reads)
+    lds_poison(Cs, 2 * (L::kCs + L::kBs + 2 * L::kXs));
+    lds_poison(Xc, 2 * L::kXtm);
+    lds_poison(Mc, 2 * L::kMs);
+    if constexpr (!L::kYinM) lds_poison(Yf, 4 * kQ * kYRow);
+#endif
     if (has_x) *reinterpret_cast<uint4*>(Xc + xj * kRowP + xp8) = pf.x;
 #pragma unroll
     for (int r = 0; r < kBCr; ++r) {
@@ -524,6 +533,9 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
     if constexpr (!kDefer) {
       // ---- A3: Y += M x (waves 4-7) -> Yf; S -> LDS for the next chunk's C S_in ----
       if (has_y) mx_store(yacc, Mc, Xc);
+#ifdef MSCAN_LDS_POISON
+      lds_poison(ST, 4 * L::kST);   // hi and lo: read last in this chunk's second phase
+#endif
       if (w == kDtWave && c + 1 < nchunk) dt_terms(pf.dt, t0 + kQ, dset ^ 1);   // the next chunk's, off the stage path
       write_ST();
       lds_barrier();
@@ -531,6 +543,9 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
       epilogue(c, Xc, xcur, zcur);
     } else {
       // ---- S -> LDS for the next chunk's C S_in; chunk c-1's epilogue ----
+#ifdef MSCAN_LDS_POISON
+      lds_poison(ST, 4 * L::kST);   // hi and lo: read last in this chunk's second phase
+#endif
       write_ST();
       if (c > 0) epilogue(c - 1, Xprev, xcur, zprev);
       yprev = yacc;
