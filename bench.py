@@ -45,6 +45,8 @@ SLOTS_PER_TC_UNGATED = (2 * TRANS + 3) + 1
 CSRC = os.path.join(ROOT, "selective_state_space_55_amd", "csrc")
 # committed rocprofv3 traffic summaries and the device sources (kernel file + io helpers) they were taken on
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "scan_fwd_mamba1.4b_traffic.txt")
+# HBM-traffic summaries of the forward per workload index (all kernels of one call, default plan)
+PROFILE_TRAFFIC_FWD = {2: PROFILE_TRAFFIC, 3: os.path.join(ROOT, "profiles", "scan_fwd_million_traffic.txt")}
 KERNEL_SOURCES = [os.path.join(CSRC, f) for f in ("scan_fwd.hip", "scan_fwd_h2.h", "io.h")]
 PROFILE_TRAFFIC_STEP = os.path.join(ROOT, "profiles", "scan_step_decode2.8b_traffic.txt")
 KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
@@ -927,8 +929,11 @@ def main() -> int:
     slots = tc * n * per_tcn + tc * (SLOTS_PER_TC_GATED if c.gated else SLOTS_PER_TC_UNGATED)
     achieved = slots / (launch_ms_avg * 1e-3) / 1e12
     peak = VALU_SLOTS_PEAK / 1e12
-    # the committed counters were taken on the ZOH kernel at the workload's own d_state
-    traffic = read_traffic(alg_bytes) if (args.discretization == "zoh" and not args.dstate) else None
+    # the committed counters were taken on the ZOH kernel at the workload's own d_state and the
+    # default plan, per workload
+    prof = PROFILE_TRAFFIC_FWD.get(args.config)
+    default_plan = args.discretization == "zoh" and not args.dstate and not args.nchunks and not args.npw
+    traffic = read_traffic(alg_bytes, prof) if (prof and default_plan) else None
     flushed = None
     if alg_bytes < CACHE_BYTES:
         # the workload fits the 256 MB Infinity Cache: also time launches that follow a 1 GiB
