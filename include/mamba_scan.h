@@ -165,8 +165,9 @@ size_t mamba_scan_fwd_workspace_size_ex(int64_t batch, int64_t dim, int64_t dsta
 /*
  * Causal depthwise conv1d (4 taps) + SiLU fused into the forward scan's load
  * stage: the scan input u is computed on chip from x and never round-trips
- * through HBM (Mamba notes, 设计 3 block pseudo-code: conv1d, SiLU, then the
- * SSM; State space models and Mamba, Mamba block architecture).  Exactly
+ * through HBM (conv, SiLU, then the SSM: Mamba concept page §3.3 flow; State
+ * space models and Mamba, Mamba block architecture; the Mamba notes' 设计 3
+ * pseudo-code puts SiLU before the conv and is not followed).  Exactly
  * mamba_conv1d_fwd(x, conv_weight, conv_bias, conv_state_in, conv_state_out,
  * kernel_size 4, silu on) followed by mamba_scan_fwd on its output u: u is
  * rounded to the io dtype before the scan uses it, as a stored u would be, so
@@ -327,8 +328,10 @@ int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void*
 
 /*
  * Causal depthwise 1-D convolution + SiLU, the step in front of the scan in the
- * Mamba block (Mamba notes, 设计 3 block pseudo-code, kernel size 4; State space
- * models and Mamba, Mamba block architecture: Conv1d -> SiLU -> SSM).  Per
+ * Mamba block: conv, then SiLU, then the SSM (Mamba concept page §3.3 flow;
+ * State space models and Mamba, Mamba block architecture; the Mamba notes' 设计 3
+ * pseudo-code applies SiLU first and is not followed), kernel size 4 (Mamba
+ * notes, 设计 3).  Per
  * (batch, channel) with K = kernel_size taps:
  *
  *   a[t] = bias[d] + sum_{k<K} weight[d,k] * x[t - (K-1) + k],   u[t] = a[t] * sigmoid(a[t])

@@ -459,10 +459,13 @@ int oracle_scan_bwd(const double* u, const double* delta, const double* A_log, c
 
 /*
  * Causal depthwise 1-D convolution followed by SiLU, the step in front of the
- * scan in the Mamba block (Mamba notes, awesome.papernotes.org, 设计 3 block
- * pseudo-code: kernel size 4; State space models and Mamba,
- * jonathanding.github.io, Mamba block architecture: Conv1d -> SiLU -> SSM; the
- * layer configuration in MAMBA walkthrough, x-humanoid.csdn.net, §6: d_conv=4).
+ * scan in the Mamba block.  Order: the conv, then SiLU, then the SSM, as the
+ * Mamba concept page (compassingai.com, §3.3 flow) and State space models and
+ * Mamba (jonathanding.github.io, Mamba block architecture) draw it; the Mamba
+ * notes' block pseudo-code (awesome.papernotes.org, 设计 3) applies SiLU before
+ * the conv, a minority reading not followed.  Kernel size 4: the notes' 设计 3
+ * and the layer configuration of the MAMBA walkthrough (x-humanoid.csdn.net,
+ * §6: d_conv=4).
  * Per (batch, channel) with K taps:
  *
  *   a[t] = bias[d] + sum_{k=0}^{K-1} w[d,k] * x[t - (K-1) + k]

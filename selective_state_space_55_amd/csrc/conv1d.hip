@@ -1,7 +1,9 @@
 // conv1d.hip -- causal depthwise conv1d + SiLU on gfx950, the step in front of
-// the scan in the Mamba block (Mamba notes, awesome.papernotes.org, 设计 3
-// block pseudo-code, kernel size 4; State space models and Mamba,
-// jonathanding.github.io, Mamba block architecture: Conv1d -> SiLU -> SSM).
+// the scan in the Mamba block: conv, then SiLU, then the SSM (Mamba concept
+// page, compassingai.com, §3.3 flow; State space models and Mamba,
+// jonathanding.github.io, Mamba block architecture -- the Mamba notes' 设计 3
+// pseudo-code, which applies SiLU first, is not followed), kernel size 4 (Mamba
+// notes, awesome.papernotes.org, 设计 3).
 //
 //   a[t] = bias[d] + sum_{k<K} w[d,k] x[t - (K-1) + k],   u[t] = a[t] sigmoid(a[t])
 //

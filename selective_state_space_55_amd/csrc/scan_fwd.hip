@@ -18,10 +18,10 @@
 //               and put Delta, u and the tile's B/C values (shared by the 64
 //               channels) as fp32 in LDS;
 //   scan     -- per group of 4 tokens read Delta/u of the lane's channel and
-//               one (B, C) pair per lane from LDS; every B/C use takes its value
-//               through a DPP row_newbcast operand (lane 4j+t of each 16-lane
-//               row holds state j, token t); leave a partial readout over the
-//               wave's states in LDS;
+//               the B/C values of the lane's two states for the four tokens
+//               (four 16-byte LDS reads that every lane of a wave half shares,
+//               so the values arrive as plain VGPR operands); leave a partial
+//               readout over the wave's states in LDS;
 //   epilogue -- sum the four partials, add D u, apply the SiLU gate, store y.
 // A wave cannot hide its own stalls, so the stages are software-pipelined
 // across tiles inside one instruction stream: while a wave
