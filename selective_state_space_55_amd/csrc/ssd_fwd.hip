@@ -251,10 +251,13 @@ __global__ __launch_bounds__(kNT, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs a) 
   // 0 and their stores are dropped -- no per-lane bounds checks or 64-bit
   // address arithmetic.  Tokens t0 .. t0 + 63 of a (token, element) array with
   // tstride elements per token, of which the first tail belong to this thread
-  // block: 64 whole rows while they last, then up to the last token's tail.
+  // block: the descriptor ends at the tail of the chunk's last token inside the
+  // sequence (at the largest accepted width, nheads * headdim = 2^24, that is
+  // 63 * 2^25 + 2 P bytes, inside the 32-bit range).
   auto rs_chunk = [&](const uint16_t* base, int64_t t0, int64_t tstride, int tail) {
     const int64_t left = Lq - t0;
-    const int64_t bytes = left <= 0 ? 0 : left >= kQ ? kQ * tstride * 2 : ((left - 1) * tstride + tail) * 2;
+    const int64_t rows = left < kQ ? left : kQ;
+    const int64_t bytes = left <= 0 ? 0 : ((rows - 1) * tstride + tail) * 2;
     return make_rsrc(base + (left <= 0 ? 0 : t0 * tstride), (int)bytes);
   };
   auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
