@@ -93,7 +93,10 @@ struct SsdLds {
   // B's rows take 16 elements of padding: its transposing reads take 32 bytes
   // from each of 4 consecutive rows, which a 288-byte pitch puts in distinct banks
   static constexpr int kRowNB = N + 2 * kPadH;
-  static constexpr int kRowP = P + kPadH;     // rows over P channels
+  // rows over P channels (the x tile and the scaled x); their transposing reads
+  // take 64 bytes from each of 4 consecutive rows, which a pitch of 192 bytes at
+  // P = 64 puts in distinct banks (144 bytes overlapped rows r and r + 2)
+  static constexpr int kRowP = P == 64 ? P + 4 * kPadH : P + kPadH;
   static constexpr int kXtm = kQ * kRowP;     // x     [j][p]
   static constexpr int kCs = kQ * kRowN;      // C     [i][n]
   static constexpr int kBs = kQ * kRowNB;     // B     [j][n]
