@@ -253,12 +253,13 @@ __device__ __forceinline__ float softplus_log2e(float x) {
 // waves at about twice the rate of v_min_f32.  kAnySign: y may be positive
 // (Delta without softplus); there x + x^2/2 is a lower bound, and the larger
 // of it and ab - 1 - 2^-23 is taken.
+constexpr float kDecayC1 = 0.6931471805599453f;            // ln 2
+constexpr float kDecayC2 = 0.2402265069591007f;            // (ln 2)^2 / 2
+constexpr float kDecayHi = 0.99999988079071044921875f;     // 1 - 2^-23
 template <bool kAnySign>
 __device__ __forceinline__ float decay_m1(float y, float ab) {
-  constexpr float kC1 = 0.6931471805599453f;    // ln 2
-  constexpr float kC2 = 0.2402265069591007f;    // (ln 2)^2 / 2
-  const float p2 = y * fmaf(y, kC2, kC1);       // x + x^2 / 2
-  const float m0 = ab - 0.99999988079071044921875f;   // ab - (1 - 2^-23)
+  const float p2 = y * fmaf(y, kDecayC2, kDecayC1);   // x + x^2 / 2
+  const float m0 = ab - kDecayHi;                     // ab - (1 - 2^-23)
   if constexpr (!kAnySign) return m0 - __builtin_amdgcn_fmed3f(m0 - p2, 0.0f, 1.0f);   // min(m0, p2)
   return fmaxf(fminf(m0, p2), ab - 1.00000011920928955078125f);   // ab - (1 + 2^-23)
 }

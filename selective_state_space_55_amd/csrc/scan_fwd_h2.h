@@ -202,7 +202,9 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     if (valid && kc == 0 && a.h0) hv = a.h0[bd * a.dstate + n];
     h[j] = hv;
   }
-  float dsum_acc = 0.0f;
+  // the chunk's sum of Delta*log2e over this thread's staging pieces (channel pc, tokens
+  // 8 pg .. 8 pg + 7 of every tile; masked tokens are staged as 0)
+  float dsum_st = 0.0f;
   const bool gate_on = a.gated != 0;
   const float gate_off = gate_on ? 0.0f : 1.0f;
 
@@ -313,6 +315,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       fd[j] = ok ? dl : 0.0f;
       fu[j] = ok ? fu[j] : 0.0f;
     }
+    dsum_st += ((fd[0] + fd[1]) + (fd[2] + fd[3])) + ((fd[4] + fd[5]) + (fd[6] + fd[7]));
     float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
 #pragma unroll
     for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
@@ -454,11 +457,17 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     // m h to an h + s already on that grid would round the same way every token
     // and drift.
     // bq = (B of state 0, B of state 1, C of state 0, C of state 1) of this token
-    auto token = [&](float dl, float uu, float4 bq) -> float {
-      const float y0 = dl * A[0];
-      const float y1 = dl * A[1];
-      const float m0 = decay_m1<!kSp>(y0, __builtin_amdgcn_exp2f(y0));
-      const float m1 = decay_m1<!kSp>(y1, __builtin_amdgcn_exp2f(y1));
+    // The decays of a group's four tokens do not depend on h: their eight exp2 are
+    // issued first (a scheduling barrier keeps them ahead), so each has the
+    // others' issue to cover its latency before its result is read.
+    auto decay_exp = [&](float dl, float (&y)[2], float (&ab)[2]) {
+      y[0] = dl * A[0];
+      y[1] = dl * A[1];
+      ab[0] = __builtin_amdgcn_exp2f(y[0]);
+      ab[1] = __builtin_amdgcn_exp2f(y[1]);
+    };
+    auto token = [&](const float (&m)[2], float uu, float4 bq) -> float {
+      const float m0 = m[0], m1 = m[1];
       if constexpr (kEuler) {
         const float s0 = bq.x * uu;                                 // s = B * Delta * u
         const float s1 = bq.y * uu;
@@ -485,15 +494,47 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         for (int kk = 0; kk < 4; ++kk) bcn[kk] = reinterpret_cast<const float4*>(bcl + (g + 1) * NP * 8)[kk];
       }
       __builtin_amdgcn_sched_barrier(0);
-      const float y0 = token(dv.x, uv.x, bcv[0]);
-      const float y1 = token(dv.y, uv.y, bcv[1]);
-      const float y2 = token(dv.z, uv.z, bcv[2]);
-      const float y3 = token(dv.w, uv.w, bcv[3]);
+      float ye[4][2], ab[4][2], m[4][2];
+      decay_exp(dv.x, ye[0], ab[0]);
+      decay_exp(dv.y, ye[1], ab[1]);
+      decay_exp(dv.z, ye[2], ab[2]);
+      decay_exp(dv.w, ye[3], ab[3]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kSp) {
+        // decay_m1's steps (y <= 0) eight at a time, so no step waits on the one before it
+        float p1[4][2], m0[4][2], t[4][2];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            p1[q][j] = fmaf(ye[q][j], kDecayC2, kDecayC1);
+            m0[q][j] = ab[q][j] - kDecayHi;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) t[q][j] = __builtin_amdgcn_fmed3f(m0[q][j] - ye[q][j] * p1[q][j], 0.0f, 1.0f);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) m[q][j] = m0[q][j] - t[q][j];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          m[q][0] = decay_m1<true>(ye[q][0], ab[q][0]);
+          m[q][1] = decay_m1<true>(ye[q][1], ab[q][1]);
+        }
+      }
+      const float y0 = token(m[0], uv.x, bcv[0]);
+      const float y1 = token(m[1], uv.y, bcv[1]);
+      const float y2 = token(m[2], uv.z, bcv[2]);
+      const float y3 = token(m[3], uv.w, bcv[3]);
       {
         // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
         *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
       }
-      dsum_acc += (dv.x + dv.y) + (dv.z + dv.w);   // the chunk's sum of Delta*log2e
       {
         if (g == 1) {
           float yv[8];
@@ -575,7 +616,15 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         a.final_state[bd * a.dstate + n] = h[j];
       }
     }
-    if (chunk_out && sp == 0 && hf == 0) a.dsum[cslot] = dsum_acc;
+  }
+  if (chunk_out) {
+    // the 8 staging pieces of a channel are lanes 8 pc .. 8 pc + 7
+    float ds = dsum_st;
+    ds += __shfl_xor(ds, 1);
+    ds += __shfl_xor(ds, 2);
+    ds += __shfl_xor(ds, 4);
+    const int64_t dp = d0 + pc;
+    if (pg == 0 && dp < a.dim) a.dsum[kVarlen ? pidx * a.dim + dp : (sidx * a.dim + dp) * a.nchunks + kc] = ds;
   }
 }
 
