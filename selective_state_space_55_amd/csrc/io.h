@@ -264,6 +264,50 @@ __device__ __forceinline__ float decay_m1(float y, float ab) {
   return fmaxf(fminf(m0, p2), ab - 1.00000011920928955078125f);   // ab - (1 + 2^-23)
 }
 
+// decay_m1 of four tokens (Delta*log2e in dl) times two states (A in A), laid out
+// for the issue order: the eight exp2 first, each of decay_m1's steps eight at a
+// time (scheduling barriers keep the phases apart), so no instruction reads a
+// result issued just before it -- a scan's h-independent work, formed before the
+// recurrence meets it.
+template <bool kAnySign>
+__device__ __forceinline__ void decay_m1_4x2(const float (&dl)[4], const float (&A)[2], float (&m)[4][2]) {
+  float y[4][2], ab[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) y[q][j] = dl[q] * A[j];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) ab[q][j] = __builtin_amdgcn_exp2f(y[q][j]);
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (kAnySign) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) m[q][j] = decay_m1<true>(y[q][j], ab[q][j]);
+  } else {
+    float p1[4][2], m0[4][2], t[4][2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        p1[q][j] = fmaf(y[q][j], kDecayC2, kDecayC1);
+        m0[q][j] = ab[q][j] - kDecayHi;
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) t[q][j] = __builtin_amdgcn_fmed3f(m0[q][j] - y[q][j] * p1[q][j], 0.0f, 1.0f);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) m[q][j] = m0[q][j] - t[q][j];   // min(m0, p2), as in decay_m1
+  }
+}
+
 // z * sigmoid(z) = z / (1 + 2^(-z log2e))
 __device__ __forceinline__ float silu(float z) {
   constexpr float kLog2e = 1.4426950408889634f;

@@ -255,12 +255,13 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
       const float bqs[8] = {bq01.x, bq01.y, bq01.z, bq01.w, bq23.x, bq23.y, bq23.z, bq23.w};
       const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
       const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
+      float m4[4][NPW];   // Abar - 1, formed ahead of the recurrence (h-independent)
+      decay_m1_4x2<!kSp>(dls, A, m4);
       static_for<4>([&](auto kk_c) {
         constexpr int kk = decltype(kk_c)::value;
         static_for<NPW>([&](auto j_c) {
           constexpr int j = decltype(j_c)::value;
-          const float yv = dls[kk] * A[j];
-          const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
+          const float m = m4[kk][j];
           if constexpr (kEuler) {
             h[j] += fmaf(m, h[j], bqs[kk * 2 + j] * uus[kk]);   // h + (m h + B (Delta u))
           } else {
@@ -465,14 +466,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
           const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
           const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
           float ys[4];
+          float m4[4][NPW];   // Abar - 1, formed ahead of the recurrence (h-independent)
+          decay_m1_4x2<!kSp>(dls, A, m4);
           static_for<4>([&](auto kk_c) {
             constexpr int kk = decltype(kk_c)::value;
             float acc = 0.0f;
             static_for<NPW>([&](auto j_c) {
               constexpr int j = decltype(j_c)::value;
               constexpr int t = 4 * gq + kk;
-              const float yv = dls[kk] * A[j];
-              const float m = decay_m1<!kSp>(yv, __builtin_amdgcn_exp2f(yv));   // Abar - 1
+              const float m = m4[kk][j];
               // Bbar = e B: e = (Abar - 1) / A (zero-order hold) or Delta (Euler)
               const float e = kEuler ? dls[kk] * kLn2 : m * iA[j];
               const float bu = (j == 0 ? bcq[kk].x : bcq[kk].y) * uus[kk];   // B u

@@ -457,15 +457,6 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     // m h to an h + s already on that grid would round the same way every token
     // and drift.
     // bq = (B of state 0, B of state 1, C of state 0, C of state 1) of this token
-    // The decays of a group's four tokens do not depend on h: their eight exp2 are
-    // issued first (a scheduling barrier keeps them ahead), so each has the
-    // others' issue to cover its latency before its result is read.
-    auto decay_exp = [&](float dl, float (&y)[2], float (&ab)[2]) {
-      y[0] = dl * A[0];
-      y[1] = dl * A[1];
-      ab[0] = __builtin_amdgcn_exp2f(y[0]);
-      ab[1] = __builtin_amdgcn_exp2f(y[1]);
-    };
     auto token = [&](const float (&m)[2], float uu, float4 bq) -> float {
       const float m0 = m[0], m1 = m[1];
       if constexpr (kEuler) {
@@ -494,39 +485,10 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         for (int kk = 0; kk < 4; ++kk) bcn[kk] = reinterpret_cast<const float4*>(bcl + (g + 1) * NP * 8)[kk];
       }
       __builtin_amdgcn_sched_barrier(0);
-      float ye[4][2], ab[4][2], m[4][2];
-      decay_exp(dv.x, ye[0], ab[0]);
-      decay_exp(dv.y, ye[1], ab[1]);
-      decay_exp(dv.z, ye[2], ab[2]);
-      decay_exp(dv.w, ye[3], ab[3]);
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (kSp) {
-        // decay_m1's steps (y <= 0) eight at a time, so no step waits on the one before it
-        float p1[4][2], m0[4][2], t[4][2];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            p1[q][j] = fmaf(ye[q][j], kDecayC2, kDecayC1);
-            m0[q][j] = ab[q][j] - kDecayHi;
-          }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) t[q][j] = __builtin_amdgcn_fmed3f(m0[q][j] - ye[q][j] * p1[q][j], 0.0f, 1.0f);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) m[q][j] = m0[q][j] - t[q][j];
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          m[q][0] = decay_m1<true>(ye[q][0], ab[q][0]);
-          m[q][1] = decay_m1<true>(ye[q][1], ab[q][1]);
-        }
-      }
+      // the decays of the four tokens do not depend on h: formed first
+      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+      float m[4][2];
+      decay_m1_4x2<!kSp>(dls, A, m);
       const float y0 = token(m[0], uv.x, bcv[0]);
       const float y1 = token(m[1], uv.y, bcv[1]);
       const float y2 = token(m[2], uv.z, bcv[2]);
