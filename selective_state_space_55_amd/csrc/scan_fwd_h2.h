@@ -637,13 +637,16 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   __shared__ float sA[kCh * kSRow];     // [channel][state]
   __shared__ float sH[kCh * kSRow];
   __shared__ float par[kCh];
+  __shared__ unsigned long long live_w[8];   // per wave: states still above the cut-off
   lds_poison(cbuf, (int)sizeof(cbuf));
+  lds_poison(live_w, (int)sizeof(live_w));
   lds_poison(sA, (int)sizeof(sA));
   lds_poison(sH, (int)sizeof(sH));
   lds_poison(par, (int)sizeof(par));
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
+  const int w = tid >> 6;
   const int pc = tid / 8;               // channel within the group
   const int pg = tid % 8;               // tokens 8 pg .. 8 pg + 7 of a tile
   int64_t kc, cg, b, t_begin, t_end, slot0;   // slot0: carry slot of channel 0 of the group
@@ -714,6 +717,13 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   constexpr int kCP = (NPS * 16 + 511) / 512;   // four-token pieces of C per thread
 
   float base = 0.0f;   // cumDelta*log2e of the channel before the tile
+  // States still corrected (bit 16 g + n).  With Delta >= 0 a state's decay only
+  // shrinks, so once it is below 2^-32 at every lane's last token of a tile the
+  // state's term stays under fp32 resolution of its own carried-in scale for the
+  // rest of the chunk and is dropped; the workgroup stops when none is left.
+  // States decay at their own rates (|A_n| spans an order of magnitude), so most
+  // are dropped long before the slowest.
+  uint64_t live = NPS == 64 ? ~0ull : ((1ull << NPS) - 1);
   for (int64_t tile = t_first; tile < t_end; tile += T) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     const V8 vd = IO::buf_load8(rs_d, off, kVec);
@@ -770,7 +780,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
     for (int j = 0; j < 8; ++j) c[j] += base + excl;
     base += total;
     float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
-    float pmax = 0.0f;
+    unsigned long long alive = 0;   // this wave's lanes: states whose decay is still >= 2^-32
 #pragma unroll 1
     for (int g = 0; g < NG; ++g) {
       float An[16], Hn[16];
@@ -783,6 +793,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
       }
 #pragma unroll 4
       for (int n = 0; n < 16; ++n) {
+        if (((live >> (16 * g + n)) & 1) == 0) continue;   // uniform over the workgroup
         const float* crow = cbuf + (16 * g + n) * kCRow + 8 * pg;
         const float4 c0 = *reinterpret_cast<const float4*>(crow);
         const float4 c1 = *reinterpret_cast<const float4*>(crow + 4);
@@ -791,7 +802,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
         for (int j = 0; j < 8; ++j) {
           const float P = __builtin_amdgcn_exp2f(An[n] * c[j]);   // exp(A cumDelta)
           acc[j] = fmaf(cn[j], P * Hn[n], acc[j]);
-          if (j == 7) pmax = fmaxf(pmax, P);
+          if (j == 7) alive |= (__ballot(ch_ok && P >= 2.3283064e-10f) != 0 ? 1ull : 0ull) << (16 * g + n);
         }
       }
     }
@@ -810,8 +821,18 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
         for (int j = lo; j < nv; ++j) IO::store1(py + j, fy[j]);
       }
     }
-    // decay below 2^-32 on every lane: the rest of the chunk needs no correction
-    if (may_stop && __syncthreads_and((!ch_ok || pmax < 2.3283064e-10f) ? 1 : 0) != 0) break;
+    if (may_stop) {
+      // live_w is next written after the next tile's two barriers
+      if (lane == 0) live_w[w] = alive;
+      __syncthreads();
+      unsigned long long al = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) al |= live_w[i];
+      const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)al);
+      const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(al >> 32));
+      live &= ((uint64_t)hi32 << 32) | lo32;
+      if (live == 0) break;   // no state needs correcting in the rest of the chunk
+    }
   }
 }
 
