@@ -475,7 +475,8 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
 
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      // next group's LDS reads first, then the four tokens in one scheduling region
+      // next group's LDS reads first, then the four tokens (no scheduling barrier here: the
+      // epilogue and staging groups interleave their work with the decays)
       float4 dn = dv, un = uv;
       float4 bcn[4] = {bcv[0], bcv[1], bcv[2], bcv[3]};
       if (g + 1 < kG) {
@@ -484,7 +485,6 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) bcn[kk] = reinterpret_cast<const float4*>(bcl + (g + 1) * NP * 8)[kk];
       }
-      __builtin_amdgcn_sched_barrier(0);
       // the decays of the four tokens do not depend on h: formed first
       const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
       float m[4][2];
