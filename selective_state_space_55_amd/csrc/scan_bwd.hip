@@ -95,36 +95,36 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
-constexpr int kRowRor8 = 0x128;        // lane (l + 8) mod 16 of the row  == l ^ 8
-constexpr int kRowHalfMirror = 0x141;  // lane 7 - (l mod 8) of the half-row: flips bits 0-2
 constexpr int kQuad2301 = 0x4E;        // l ^ 2
 constexpr int kQuad1032 = 0xB1;        // l ^ 1
 
-// Rows 0, 2 return a[l] + a[l ^ 16]; rows 1, 3 return b[l] + b[l ^ 16].
-__device__ __forceinline__ float row_pair_sum2(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+// Sum over the 32 lanes (channels) of each wave half of 8 values per lane,
+// through the wave's own 512-float LDS scratch, in two steps so the LDS round
+// trip overlaps other work.  reduce32_8_issue: lane (half h, channel c) writes
+// value i to row (h, i), column c ^ f(i), and lane 4i + m of the half reads value
+// i of channels 8m .. 8m+7 back (two 16-byte reads, not yet waited for).  A
+// wave's LDS accesses execute in issue order, so no barrier is needed, and the
+// scratch can be rewritten as soon as the reads are issued; the wavefront-scope
+// fences keep the compiler from moving the reads above the writes (other
+// lanes' words) or the next writes above the reads.  reduce32_8_finish adds the
+// eight words and two quad steps finish the sum, so lanes 4i .. 4i+3 of each
+// half hold that half's total of value i.  Rows are 32 floats, so rows i and
+// i + 2 share banks; the column swizzle f(i) = 4 ((i >> 1) & 1) puts the four
+// rows that one 16-lane pass of the reads touches in distinct banks.
+__device__ __forceinline__ void reduce32_8_issue(const float (&v)[8], int lane, float* scr, float4 (&r)[2]) {
+  float* base = scr + (lane >> 5) * 256;
+  const int c = lane & 31;
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");   // after the previous reads
+#pragma unroll
+  for (int i = 0; i < 8; ++i) base[i * 32 + (c ^ (4 * ((i >> 1) & 1)))] = v[i];
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+  const int i = c >> 2, m = c & 3;
+  const int f = 4 * ((i >> 1) & 1);
+  r[0] = *reinterpret_cast<const float4*>(base + i * 32 + ((8 * m) ^ f));
+  r[1] = *reinterpret_cast<const float4*>(base + i * 32 + ((8 * m + 4) ^ f));
 }
-
-// Sum over the 32 lanes of each half of a wave of 8 values held by every lane:
-// a reduce-scatter (each stage halves the values per lane and doubles the
-// lanes summed), then an all-reduce over the last four lanes.  Afterwards
-// lanes 4i .. 4i+3 of each half hold that half's total of value i.
-__device__ __forceinline__ float reduce32_8(const float (&v)[8], int lane) {
-  float w4[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w4[i] = row_pair_sum2(v[i], v[i + 4]);    // lanes l, l ^ 16
-  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
-  float w2[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {                                           // lanes l, l ^ 8
-    const float keep = b3 ? w4[i + 2] : w4[i];
-    const float send = b3 ? w4[i] : w4[i + 2];
-    w2[i] = keep + dpp_mov<kRowRor8>(send);
-  }
-  const float keep = b2 ? w2[1] : w2[0];                                  // lanes l, l ^ 7
-  const float send = b2 ? w2[0] : w2[1];
-  float r = keep + dpp_mov<kRowHalfMirror>(send);
+__device__ __forceinline__ float reduce32_8_finish(const float4 (&q)[2]) {
+  float r = ((q[0].x + q[0].y) + (q[0].z + q[0].w)) + ((q[1].x + q[1].y) + (q[1].z + q[1].w));
   r += dpp_mov<kQuad2301>(r);                                             // lanes l, l ^ 2
   return r + dpp_mov<kQuad1032>(r);                                       // lanes l, l ^ 1
 }
@@ -280,8 +280,8 @@ struct LdsB {
   static constexpr int kDU = kCh * kRow;            // Delta*log2e, u, dytil: one tile each
   static constexpr int kBC = kG * 4 * NP * 2;       // (B, C) pairs
   static constexpr int kPart = 4 * kCh * kRow;      // per wave pair partials over one tile: readout, dDelta, du
-  static constexpr int kHB = 4 * 8 * 64 * NPW;      // state entering each 8-token sub-chunk, per wave and lane
-  static constexpr int kFloats = 3 * kDU + kBC + 3 * kPart + kHB + 2 * kCh;
+  static constexpr int kScr = 8 * 512;             // per wave: the channel sums' scratch
+  static constexpr int kFloats = 3 * kDU + kBC + 3 * kPart + kScr + 2 * kCh;
 };
 static_assert(sizeof(float) * LdsB::kFloats <= 160 * 1024, "LDS of the gradient kernel");
 
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   float* party = bcs + LdsB::kBC;         // [4][64][kRow] readout partials
   float* part1 = party + LdsB::kPart;     // [4][64][kRow] dDelta partials
   float* part2 = part1 + LdsB::kPart;     // [4][64][kRow] du partials
-  float* hbuf = part2 + LdsB::kPart;      // [4 sub-chunks][8 waves][64 lanes][2 states]
-  float* par = hbuf + LdsB::kHB;          // [2][64] bias, D
+  float* scr = part2 + LdsB::kPart;       // [8 waves][512]: each wave's channel-sum scratch
+  float* par = scr + LdsB::kScr;          // [2][64] bias, D
   lds_poison(smem, (int)sizeof(float) * LdsB::kFloats);
 
   const int tid = threadIdx.x;
@@ -438,22 +438,38 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) q[kk * 4] = (kk < nvb) ? f[kk] : 0.0f;
       }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<float2*>(hbuf + ((s * 8 + w) * 64 + lane) * NPW) = make_float2(hq[s][0], hq[s][1]);
     }
     lds_barrier();
 
     // ---- one 8-token sub-chunk at a time, latest first: rerun its forward from the
     //      checkpoint (readout partials, every state and decay kept in registers),
     //      then sweep it backwards ----
+    // a group's channel sums of dB and dC, pending in registers until the next group
+    // (pend_tg < 0: none)
+    float* const wscr = scr + w * 512;
+    float4 pendB[2], pendC[2];
+    int pend_tg = -1;
+    auto store_sums = [&]() {
+      if (pend_tg < 0) return;
+      const float rB = reduce32_8_finish(pendB);
+      const float rC = reduce32_8_finish(pendC);
+      const int i = (lane & 31) >> 2;
+      const int64_t tt = tile + 4 * pend_tg + (i & 3);
+      if ((lane & 3) == 0 && tt < a.seqlen) {
+        const int64_t o = ((b * 2 * a.chgroups + g32) * a.npt + a.n0 + nb + (i >> 2)) * a.seqlen + tt;
+        a.wsB[o] = rB;
+        a.wsC[o] = rC;
+      }
+      pend_tg = -1;
+    };
 #pragma unroll 1
     for (int s = 3; s >= 0; --s) {
       // per token and state: h_t, m = Abar - 1, e = (Abar - 1) / A and B u, kept for the sweep
       float hb[NPW], hh[kSub][NPW], ha[kSub][NPW], he[kSub][NPW], hbu[kSub][NPW];
       {
-        const float2 q = *reinterpret_cast<const float2*>(hbuf + ((s * 8 + w) * 64 + lane) * NPW);
-        hb[0] = q.x; hb[1] = q.y;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j)   // the sub-chunk's entering state, kept in registers since staging
+          hb[j] = s == 3 ? hq[3][j] : s == 2 ? hq[2][j] : s == 1 ? hq[1][j] : hq[0][j];
         float h[NPW] = {hb[0], hb[1]};
         static_for<2>([&](auto gq_c) {
           constexpr int gq = decltype(gq_c)::value;
@@ -546,18 +562,15 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
             make_float2(half_sum2(dDp[0], dDp[2]), half_sum2(dDp[1], dDp[3]));
         *reinterpret_cast<float2*>(part2 + (sp * kCh + chw) * kRow + 4 * tg + yoff) =
             make_float2(half_sum2(dup[0], dup[2]), half_sum2(dup[1], dup[3]));
-        // sums over the half's 32 channels: lanes 4i .. 4i+3 of each half hold value i = j*4 + kk
-        const float rB = reduce32_8(dBv, lane);
-        const float rC = reduce32_8(dCv, lane);
-        const int i = (lane & 31) >> 2;
-        const int64_t tt = tile + 4 * tg + (i & 3);
-        if ((lane & 3) == 0 && tt < a.seqlen) {
-          const int64_t o = ((b * 2 * a.chgroups + g32) * a.npt + a.n0 + nb + (i >> 2)) * a.seqlen + tt;
-          a.wsB[o] = rB;
-          a.wsC[o] = rC;
-        }
+        // sums over the half's 32 channels (lanes 4i .. 4i+3 of each half get value i = j*4 + kk):
+        // the previous group's, read back during this group's arithmetic, are stored first
+        store_sums();
+        reduce32_8_issue(dBv, lane, wscr, pendB);
+        reduce32_8_issue(dCv, lane, wscr, pendC);
+        pend_tg = tg;
       });
     }
+    store_sums();   // the tile's last group
     lds_barrier();
 
     // ---- piece owners: pre-gate output, dz, ddelta, du ----
