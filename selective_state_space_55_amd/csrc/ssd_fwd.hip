@@ -30,7 +30,8 @@
 //   all        stage x (waves 0-3 at P = 32) and run the epilogue
 // and at (N, P) = (128, 64) 16 waves, four per SIMD, so that one role's waits
 // overlap another's work: waves 0-7 the S tiles, 8-11 the Y tiles, 12-14 B C^T
-// and M, 15 the decay terms, 8-15 stage x and run the epilogue.  Per chunk:
+// and M, 15 the decay terms; all 16 stage x and run the epilogue, 4 channels
+// of a token per thread.  Per chunk:
 //   stage   -- x, B, C as loaded (token-major rows, coalesced 16-byte writes),
 //              and x scaled by exp(cum_Q - cum_j) w_j as two bf16 parts (hi,
 //              and bf16 of the rest); the chunk's decay terms were computed
@@ -227,12 +228,16 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
   const float Dh = a.D ? a.D[h] : 0.0f;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
 
-  // x / z / y piece of this thread: token xj, channels xp8 .. xp8 + 7 (the first
-  // kQ P / 8 threads: all 8 waves at P = 64, waves 0-3 at P = 32, waves 8-15 of 16)
-  constexpr int kXT = kQ * P / 8;
-  const bool has_x = kW16 ? tid >= kXT : (kXT == kNT || tid < kXT);   // uniform per wave
-  const int xt = kW16 ? tid - kXT : (kXT == kNT ? tid : tid % kXT);
-  const int xj = xt / (P / 8), xp8 = (xt % (P / 8)) * 8;
+  // x / z / y piece of this thread: token xj, channels xp8 .. xp8 + kXC - 1 (kXC = 8:
+  // the first kQ P / 8 threads, all 8 waves at P = 64, waves 0-3 at P = 32; with 16
+  // waves kXC = 4, all of them, so staging and epilogue work is spread over every
+  // wave).  A piece is held as a uint4 whose first kXC / 2 words are used.
+  constexpr int kXC = kW16 ? 4 : 8;
+  constexpr int kXW = kXC / 2;
+  constexpr int kXT = kQ * P / kXC;
+  const bool has_x = kXT == kNT || tid < kXT;   // uniform per wave
+  const int xt = kXT == kNT ? tid : tid % kXT;
+  const int xj = xt / (P / kXC), xp8 = (xt % (P / kXC)) * kXC;
   // B / C pieces: e = tid + kNT r -> token e / (N/8), states 8 (e % (N/8))
   constexpr int kBCr = kQ * (N / 8) / kNT;    // 1 (N = 64 or 16 waves) or 2 (N = 128)
   static_assert(kBCr >= 1, "one B/C piece per thread at least");
@@ -274,6 +279,21 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
   auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   };
+  // an x / z piece from global memory, and an x piece to LDS
+  auto ldx = [&](__amdgpu_buffer_rsrc_t r, int off) -> uint4 {
+    if constexpr (kXC == 8) {
+      return ld16(r, off);
+    } else {
+      const uint2 v = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+      return make_uint4(v.x, v.y, 0u, 0u);
+    }
+  };
+  auto stx = [&](uint16_t* p, uint4 v) {
+    if constexpr (kXC == 8)
+      *reinterpret_cast<uint4*>(p) = v;
+    else
+      *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
+  };
   // per-thread byte offsets inside a chunk's rows
   const int x_off = (xj * (int)xs_t + xp8) * 2;
   int bc_off[kBCr];
@@ -285,8 +305,8 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
   auto prefetch = [&](int64_t c, Pf& f) {
     const int64_t t0 = c * kQ;
     if (has_x) {
-      f.x = ld16(rs_chunk(xb, t0, xs_t, P), x_off);
-      if (!kLean && !kW16) f.z = zb ? ld16(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
+      f.x = ldx(rs_chunk(xb, t0, xs_t, P), x_off);
+      if (!kLean && !kW16) f.z = zb ? ldx(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
     }
     const __amdgpu_buffer_rsrc_t rb = rs_chunk(Bb, t0, N, N), rc = rs_chunk(Cb, t0, N, N);
 #pragma unroll
@@ -373,19 +393,27 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
 #pragma unroll
       for (int r = 0; r < 4; ++r) Yf[(yi * 32 + 8 * q + 4 * h32 + r) * kYRow + p] = acc[4 * q + r];
   };
-  // token xj, channels xp8 .. +7 of chunk ce: y = Y + D x, gate, store (x from the
-  // thread's registers, or its own piece of the x tile Xb)
+  // token xj, channels xp8 .. xp8 + kXC - 1 of chunk ce: y = Y + D x, gate, store (x
+  // from the thread's registers, or its own piece of the x tile Xb)
   auto epilogue = [&](int64_t ce, const uint16_t* Xb, uint4 xreg, uint4 zreg) {
     if (has_x) {
       const float4 y0 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8);
-      const float4 y1 = *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4);
+      const float4 y1 = kXC == 8 ? *reinterpret_cast<const float4*>(Yf + xj * kYRow + xp8 + 4) : y0;
       const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-      const uint4 xe = (kLean || kDefer) ? *reinterpret_cast<const uint4*>(Xb + xj * kRowP + xp8) : xreg;
+      uint4 xe = xreg;
+      if (kLean || kDefer) {
+        if constexpr (kXC == 8) {
+          xe = *reinterpret_cast<const uint4*>(Xb + xj * kRowP + xp8);
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(Xb + xj * kRowP + xp8);
+          xe = make_uint4(v.x, v.y, 0u, 0u);
+        }
+      }
       const uint32_t xw[4] = {xe.x, xe.y, xe.z, xe.w};
       const uint32_t zw[4] = {zreg.x, zreg.y, zreg.z, zreg.w};
-      uint32_t o[4];
+      uint32_t o[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 0; q < kXW; ++q) {
         float v0 = fmaf(Dh, bf(xw[q] & 0xffffu), yv[2 * q]);
         float v1 = fmaf(Dh, bf(xw[q] >> 16), yv[2 * q + 1]);
         if (zb) {
@@ -394,9 +422,14 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
         }
         o[q] = pack_bf16x2(v0, v1);
       }
-      __builtin_amdgcn_raw_buffer_store_b128(
-          __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_uint4(o[0], o[1], o[2], o[3])),
-          rs_chunk(yb, ce * kQ, xs_t, P), x_off, 0, 0);
+      if constexpr (kXC == 8)
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, make_uint4(o[0], o[1], o[2], o[3])),
+            rs_chunk(yb, ce * kQ, xs_t, P), x_off, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(__attribute__((ext_vector_type(2))) unsigned, make_uint2(o[0], o[1])),
+            rs_chunk(yb, ce * kQ, xs_t, P), x_off, 0, 0);
     }
   };
 
@@ -416,7 +449,7 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
     // ---- stage: rows as loaded; decay terms ----
     xcur = pf.x;
     if constexpr (kLean) {
-      zcur = has_x && zb ? ld16(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
+      zcur = has_x && zb ? ldx(rs_chunk(zb, t0, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
     } else if constexpr (!kW16) {
       zcur = pf.z;
     }
@@ -432,7 +465,7 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
     lds_poison(Mc, 2 * L::kMs);
     if constexpr (!L::kYinM) lds_poison(Yf, 4 * kQ * kYRow);
 #endif
-    if (has_x) *reinterpret_cast<uint4*>(Xc + xj * kRowP + xp8) = pf.x;
+    if (has_x) stx(Xc + xj * kRowP + xp8, pf.x);
 #pragma unroll
     for (int r = 0; r < kBCr; ++r) {
       const int e = tid + kNT * r;
@@ -452,15 +485,15 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
       // fp32's range
       const float sc = scl[xj];
       const uint32_t cw[4] = {xcur.x, xcur.y, xcur.z, xcur.w};
-      uint32_t hv[4], lv[4];
+      uint32_t hv[4] = {0u, 0u, 0u, 0u}, lv[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < kXW; ++k) {
         const float v0 = bf(cw[k] & 0xffffu) * sc, v1 = bf(cw[k] >> 16) * sc;
         hv[k] = pack_bf16x2(v0, v1);
         lv[k] = pack_bf16x2(v0 - bf(hv[k] & 0xffffu), v1 - bf(hv[k] >> 16));
       }
-      *reinterpret_cast<uint4*>(Xs + xj * kRowP + xp8) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
-      *reinterpret_cast<uint4*>(XsLo + xj * kRowP + xp8) = make_uint4(lv[0], lv[1], lv[2], lv[3]);
+      stx(Xs + xj * kRowP + xp8, make_uint4(hv[0], hv[1], hv[2], hv[3]));
+      stx(XsLo + xj * kRowP + xp8, make_uint4(lv[0], lv[1], lv[2], lv[3]));
     }
     lds_barrier();
 
@@ -471,7 +504,7 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
     // chunk's last phase, instead of riding along from its own prefetch
     uint4 zE = make_uint4(0, 0, 0, 0);
     if constexpr (kW16) {
-      if (has_x && zb && c > 0) zE = ld16(rs_chunk(zb, t0 - kQ, xs_t, P), x_off);
+      if (has_x && zb && c > 0) zE = ldx(rs_chunk(zb, t0 - kQ, xs_t, P), x_off);
     }
     if constexpr (kDefer) {
       if (has_y && c > 0) mx_store(yprev, Mprev, Xprev);   // chunk c-1's Y, read after this phase
@@ -580,7 +613,7 @@ __global__ __launch_bounds__(NW * 64, P == 32 ? 4 : 1) void ssd_fwd_kernel(SArgs
       if (has_y) mx_store(yprev, Ms + (int)(cl & 1) * L::kMs, Xl);
       lds_barrier();
       if constexpr (kW16) {
-        const uint4 zl = has_x && zb ? ld16(rs_chunk(zb, cl * kQ, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
+        const uint4 zl = has_x && zb ? ldx(rs_chunk(zb, cl * kQ, xs_t, P), x_off) : make_uint4(0, 0, 0, 0);
         epilogue(cl, Xl, xcur, zl);
       } else {
         epilogue(cl, Xl, xcur, zprev);
