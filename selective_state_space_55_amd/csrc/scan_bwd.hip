@@ -25,8 +25,9 @@
 //      backwards carrying Abar lam.  The readout, dDelta and du are summed
 //      over a wave's four states in the wave and over wave pairs through LDS
 //      at the end of the tile, where the pre-gate output gives dz; dB and dC
-//      are summed over each half-wave's 32 channels by a reduce-scatter in
-//      registers and written per 32-channel group to the workspace;
+//      are summed over each half-wave's 32 channels through a wave-private LDS
+//      transpose (reduce32_8_issue / _finish) and written per 32-channel group
+//      to the workspace;
 //   3. reductions of the per-group and per-row partials in a fixed order
 //      (deterministic results).
 #include <algorithm>
