@@ -437,6 +437,9 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     float4 bcv[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) bcv[kk] = reinterpret_cast<const float4*>(bcl)[kk];
+    // varlen: tile k+2's loads at the tile start (its work items are short; issuing them in
+    // group 3, as below, measured 1% slower on the 28-sequence mix)
+    if constexpr (kVarlen) prefetch(tile + 2 * T, pfCur);
     float4 yp[4][2];
     {
       // tile k-1's partials must be read by every wave before tile k's are written
@@ -515,7 +518,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       }
       // tile k+2's loads (pfCur was staged in the previous body), issued after the epilogue and
       // staging groups rather than beside the tile-start barrier: 0.830 -> 0.823 ms at the 1.4B layer
-      if (g == 3) prefetch(tile + 2 * T, pfCur);
+      if (!kVarlen && g == 3) prefetch(tile + 2 * T, pfCur);
       if (g == 2) {
         if (tile + 2 * T <= t_end)
           stage(tile + T, pfOther, 1 - P, kpOther, IntC<1>{});
