@@ -434,6 +434,9 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
 
     float4 dv = *reinterpret_cast<const float4*>(drow);
     float4 uv = *reinterpret_cast<const float4*>(urow);
+    // Delta of the next group: the decays a group forms are the next group's, so
+    // Delta is read two groups ahead of the tokens (softplus on)
+    float4 dv1 = kSp ? *reinterpret_cast<const float4*>(drow + 4) : dv;
     float4 bcv[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) bcv[kk] = reinterpret_cast<const float4*>(bcl)[kk];
@@ -475,26 +478,85 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       return fmaf(bq.w, h[1], bq.z * h[0]);   // C . h
     };
 
+    // decrements of the tile's first group; each group forms the next group's
+    // while it runs its own recurrence (softplus on: Delta > 0)
+    float mc[4][2];
+    {
+      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+      decay_m1_4x2<!kSp>(dls, A, mc);
+    }
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
-      // next group's LDS reads first, then the four tokens (no scheduling barrier here: the
-      // epilogue and staging groups interleave their work with the decays)
+      // next group's LDS reads first (Delta two groups ahead), then the four tokens with the
+      // next group's decays issued between them, so the exp2 results and decay_m1's steps meet
+      // their consumers a group later instead of stalling them (same-box A/B at the 1.4B layer:
+      // 0.817 -> 0.800 ms); the epilogue and staging groups interleave with both
       float4 dn = dv, un = uv;
       float4 bcn[4] = {bcv[0], bcv[1], bcv[2], bcv[3]};
-      if (g + 1 < kG) {
-        dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
+      const bool nxt = g + 1 < kG;
+      float4 dn2 = dv1;
+      if (kSp && g + 2 < kG) dn2 = *reinterpret_cast<const float4*>(drow + 4 * (g + 2));
+      if (nxt) {
+        if (!kSp) dn = *reinterpret_cast<const float4*>(drow + 4 * (g + 1));
         un = *reinterpret_cast<const float4*>(urow + 4 * (g + 1));
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) bcn[kk] = reinterpret_cast<const float4*>(bcl + (g + 1) * NP * 8)[kk];
       }
-      // the decays of the four tokens do not depend on h: formed first
-      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
-      float m[4][2];
-      decay_m1_4x2<!kSp>(dls, A, m);
-      const float y0 = token(m[0], uv.x, bcv[0]);
-      const float y1 = token(m[1], uv.y, bcv[1]);
-      const float y2 = token(m[2], uv.z, bcv[2]);
-      const float y3 = token(m[3], uv.w, bcv[3]);
+      float y0, y1, y2, y3;
+      float mn[4][2];
+      if constexpr (kSp) {
+        // decay_m1 of the next group, one step between each pair of this group's tokens
+        const float dln[4] = {dv1.x, dv1.y, dv1.z, dv1.w};
+        float yy[4][2], ab[4][2], p1[4][2], m0[4][2], tt[4][2];
+        y0 = token(mc[0], uv.x, bcv[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) yy[q][j] = dln[q] * A[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ab[q][j] = __builtin_amdgcn_exp2f(yy[q][j]);
+        }
+        y1 = token(mc[1], uv.y, bcv[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              p1[q][j] = fmaf(yy[q][j], kDecayC2, kDecayC1);
+              m0[q][j] = ab[q][j] - kDecayHi;
+            }
+        }
+        y2 = token(mc[2], uv.z, bcv[2]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) tt[q][j] = __builtin_amdgcn_fmed3f(m0[q][j] - yy[q][j] * p1[q][j], 0.0f, 1.0f);
+        }
+        y3 = token(mc[3], uv.w, bcv[3]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mn[q][j] = m0[q][j] - tt[q][j];   // min(m0, p2), as in decay_m1
+        }
+      } else {
+        y0 = token(mc[0], uv.x, bcv[0]);
+        y1 = token(mc[1], uv.y, bcv[1]);
+        y2 = token(mc[2], uv.z, bcv[2]);
+        y3 = token(mc[3], uv.w, bcv[3]);
+        if (nxt) {
+          const float dln[4] = {dn.x, dn.y, dn.z, dn.w};
+          decay_m1_4x2<true>(dln, A, mn);
+        }
+      }
       {
         // lanes 0-31 get tokens 0, 1 and lanes 32-63 tokens 2, 3 of their channel, over all four states
         *reinterpret_cast<float2*>(yrow + 4 * g) = make_float2(half_sum2(y0, y2), half_sum2(y1, y3));
@@ -525,11 +587,16 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
         else
           stage(tile + T, pfOther, 1 - P, kpOther, IntC<0>{});
       }
-      if (g + 1 < kG) {
+      if (nxt) {
         dv = dn;
+        dv1 = dn2;
         uv = un;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) bcv[kk] = bcn[kk];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) mc[q][j] = mn[q][j];
       }
     }
     lds_barrier();
