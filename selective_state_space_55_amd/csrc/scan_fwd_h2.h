@@ -796,18 +796,36 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   // States decay at their own rates (|A_n| spans an order of magnitude), so most
   // are dropped long before the slowest.
   uint64_t live = NPS == 64 ? ~0ull : ((1ull << NPS) - 1);
-  for (int64_t tile = t_first; tile < t_end; tile += T) {
+  // a tile's global loads; the next tile's are issued before this tile's work,
+  // so their latency overlaps it (the work per tile is small once most states
+  // are dropped, and the loop would otherwise wait a memory round trip per tile;
+  // two tiles ahead measured no better)
+  struct Ld {
+    V8 d, y, z;
+    V4 c[kCP];
+  };
+  auto load = [&](int64_t tile, Ld& l) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
-    const V8 vd = IO::buf_load8(rs_d, off, kVec);
-    const V8 vy = IO::buf_load8(rs_y, off, kVec);
-    const V8 vz = IO::buf_load8(rs_z, off, kVec);
-    V4 vc[kCP];
+    l.d = IO::buf_load8(rs_d, off, kVec);
+    l.y = IO::buf_load8(rs_y, off, kVec);
+    l.z = IO::buf_load8(rs_z, off, kVec);
 #pragma unroll
     for (int r = 0; r < kCP; ++r) {
       const int i = tid + r * 512;
       const int n = i / 16, g4 = i % 16;
-      if (i < NPS * 16) vc[r] = IO::buf_load4(rs_C, (int)(((int64_t)n * a.seqlen + tile + 4 * g4) * kEsz), kVec);
+      if (i < NPS * 16) l.c[r] = IO::buf_load4(rs_C, (int)(((int64_t)n * a.seqlen + tile + 4 * g4) * kEsz), kVec);
     }
+  };
+  // one tile: its loads were issued a tile earlier; true once no state is left
+  auto step = [&](int64_t tile, Ld& ld) -> bool {
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
+    const V8 vd = ld.d;
+    const V8 vy = ld.y;
+    const V8 vz = ld.z;
+    V4 vc[kCP];
+#pragma unroll
+    for (int r = 0; r < kCP; ++r) vc[r] = ld.c[r];
+    if (tile + T < t_end) load(tile + T, ld);   // past the row: the descriptors return 0
     __syncthreads();   // the previous tile's C reads are done
 #pragma unroll
     for (int r = 0; r < kCP; ++r) {
@@ -903,9 +921,14 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
       const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)al);
       const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(al >> 32));
       live &= ((uint64_t)hi32 << 32) | lo32;
-      if (live == 0) break;   // no state needs correcting in the rest of the chunk
+      if (live == 0) return true;   // no state needs correcting in the rest of the chunk
     }
-  }
+    return false;
+  };
+  Ld ld;
+  load(t_first, ld);
+  for (int64_t tile = t_first; tile < t_end; tile += T)
+    if (step(tile, ld)) break;
 }
 
 template <typename IoT, int NG, bool kVarlen>
