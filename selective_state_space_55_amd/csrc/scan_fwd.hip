@@ -162,8 +162,9 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     FixArgs f{};
     f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = carry;
-    f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks; f.chgroups = k.chgroups;
-    f.nwork = groups * (p.nchunks - 1); f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
+    f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks;
+    f.chgroups = (a.dim + kFixCh - 1) / kFixCh;   // the fix-up's narrower channel groups
+    f.nwork = a.batch * f.chgroups * (p.nchunks - 1); f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
     launch_fix_ng<IoT, false>(f, ng, vec, s);
     return hipGetLastError();
   }

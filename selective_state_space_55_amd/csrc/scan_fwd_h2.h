@@ -674,6 +674,13 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
 // a tile (a multiple of the state scale far below fp32 resolution of y), so
 // usually only the head of a chunk is touched.  3 VALU + 1 exp per (token,
 // state).
+// The fix-up's workgroup: 16 channels (two waves).  A workgroup stops once the
+// slowest-decaying state of its channels is below the cut-off, so narrow groups
+// stop sooner (the slowest of 16 channels rather than of 64), and the small
+// groups share a CU, whose other waves cover a group's barrier and memory waits.
+constexpr int kFixCh = 16;
+constexpr int kFixNT = kFixCh * 8;   // a thread per 8-token piece of a channel's tile
+
 struct FixArgs {
   const int64_t* cu;       // varlen: sequence offsets (nseq + 1), device memory
   const int64_t* pstart;   // varlen: first piece of each sequence (nseq + 1), device memory
@@ -695,7 +702,7 @@ struct FixArgs {
 // are fixed, and tiles stay aligned to 64 tokens of the row (the first may
 // start before the piece: its earlier tokens are masked).
 template <typename IoT, bool kVec, int NG, bool kVarlen>
-__global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
+__global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
   using V8 = typename IO::V8;
@@ -706,10 +713,10 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   constexpr int kEsz = (int)sizeof(IoT);
   constexpr float kLog2e = 1.4426950408889634f;
   __shared__ float cbuf[NPS * kCRow];   // [state][token]
-  __shared__ float sA[kCh * kSRow];     // [channel][state]
-  __shared__ float sH[kCh * kSRow];
-  __shared__ float par[kCh];
-  __shared__ unsigned long long live_w[8];   // per wave: states still above the cut-off
+  __shared__ float sA[kFixCh * kSRow];     // [channel][state]
+  __shared__ float sH[kFixCh * kSRow];
+  __shared__ float par[kFixCh];
+  __shared__ unsigned long long live_w[kFixNT / 64];   // per wave: states still above the cut-off
   lds_poison(cbuf, (int)sizeof(cbuf));
   lds_poison(live_w, (int)sizeof(live_w));
   lds_poison(sA, (int)sizeof(sA));
@@ -754,13 +761,13 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
     t_end = min(t_begin + a.chunk_len, a.seqlen);
     slot0 = -1;
   }
-  const int64_t d0 = cg * kCh;
+  const int64_t d0 = cg * kFixCh;
   const int64_t d = d0 + pc;
   const bool ch_ok = d < a.dim;
   const int64_t t_first = kVarlen ? (t_begin & ~(int64_t)(T - 1)) : t_begin;
-  if (tid < kCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
+  if (tid < kFixCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
   bool finite = true;
-  for (int i = tid; i < kCh * NPS; i += 512) {
+  for (int i = tid; i < kFixCh * NPS; i += kFixNT) {
     const int c = i / NPS, n = i % NPS;
     const int64_t dc = d0 + c;
     const bool valid = dc < a.dim && n < a.dstate;
@@ -773,7 +780,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
   // a non-finite carried-in state propagates to the chunk's end (no early stop)
   const bool may_stop = a.softplus != 0 && __syncthreads_and(finite ? 1 : 0) != 0;
 
-  const int rows_ok = (int)min((int64_t)kCh, a.dim - d0);
+  const int rows_ok = (int)min((int64_t)kFixCh, a.dim - d0);
   const int64_t row0 = (b * a.dim + d0) * a.seqlen;
   const int nrec_ch = (int)((int64_t)rows_ok * a.seqlen * kEsz);
   const bool gated = a.z != nullptr;
@@ -786,7 +793,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
                                                 (int)((int64_t)a.dstate * a.seqlen * kEsz));
   IoT* gy = static_cast<IoT*>(a.y);
   const float bi = par[pc];
-  constexpr int kCP = (NPS * 16 + 511) / 512;   // four-token pieces of C per thread
+  constexpr int kCP = (NPS * 16 + kFixNT - 1) / kFixNT;   // four-token pieces of C per thread
 
   float base = 0.0f;   // cumDelta*log2e of the channel before the tile
   // States still corrected (bit 16 g + n).  With Delta >= 0 a state's decay only
@@ -811,7 +818,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
     l.z = IO::buf_load8(rs_z, off, kVec);
 #pragma unroll
     for (int r = 0; r < kCP; ++r) {
-      const int i = tid + r * 512;
+      const int i = tid + r * kFixNT;
       const int n = i / 16, g4 = i % 16;
       if (i < NPS * 16) l.c[r] = IO::buf_load4(rs_C, (int)(((int64_t)n * a.seqlen + tile + 4 * g4) * kEsz), kVec);
     }
@@ -829,7 +836,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
     __syncthreads();   // the previous tile's C reads are done
 #pragma unroll
     for (int r = 0; r < kCP; ++r) {
-      const int i = tid + r * 512;
+      const int i = tid + r * kFixNT;
       const int n = i / 16, g4 = i % 16;
       if (i < NPS * 16) {
         float f[4];
@@ -917,7 +924,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
       __syncthreads();
       unsigned long long al = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) al |= live_w[i];
+      for (int i = 0; i < kFixNT / 64; ++i) al |= live_w[i];
       const uint32_t lo32 = __builtin_amdgcn_readfirstlane((uint32_t)al);
       const uint32_t hi32 = __builtin_amdgcn_readfirstlane((uint32_t)(al >> 32));
       live &= ((uint64_t)hi32 << 32) | lo32;
@@ -934,7 +941,7 @@ __global__ __launch_bounds__(512) void fix_kernel(FixArgs a) {
 template <typename IoT, int NG, bool kVarlen>
 void launch_fix(const FixArgs& f, bool vec, hipStream_t s) {
   auto kern = vec ? fix_kernel<IoT, true, NG, kVarlen> : fix_kernel<IoT, false, NG, kVarlen>;
-  hipLaunchKernelGGL(kern, dim3((unsigned)f.nwork), dim3(512), 0, s, f);
+  hipLaunchKernelGGL(kern, dim3((unsigned)f.nwork), dim3(kFixNT), 0, s, f);
 }
 
 // Fix-up launch for 16-state groups ng = 1..4.
