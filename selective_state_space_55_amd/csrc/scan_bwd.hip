@@ -240,6 +240,16 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
     }
     if (k + 1 < a.ntile) load_tile(tile + kT, rd, ru, rb);
     lds_barrier();
+    // Abar - 1 of the tile's first group; each group forms the next group's decays
+    // (decay_m1's steps, h-independent) between its own tokens, with Delta read a
+    // group ahead, so the exp2 results meet their consumers a group later
+    float mc[4][NPW];
+    {
+      const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow);
+      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
+      decay_m1_4x2<!kSp>(dls, A, mc);
+    }
+    float4 dv1 = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4);
 #pragma unroll
     for (int g = 0; g < kG; ++g) {
       if (g % 2 == 0) {   // the state entering each 8-token sub-chunk that starts before the end
@@ -249,28 +259,82 @@ __global__ __launch_bounds__(NT) void bwd_ckpt_kernel(BArgs a) {
           for (int j = 0; j < NPW; ++j) ck[(s8 * NP + j) * a.dim] = kEuler ? h[j] : h[j] * iA[j];
         }
       }
-      const float4 dv = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * g);
+      const bool nxt = g + 1 < kG;
+      float4 dn2 = dv1;
+      if (g + 2 < kG) dn2 = *reinterpret_cast<const float4*>(dbuf + chw * kRow + 4 * (g + 2));
       const float4 uv = *reinterpret_cast<const float4*>(ubuf + chw * kRow + 4 * g);
       const float4 bq01 = reinterpret_cast<const float4*>(bl + g * 4 * NP)[0];   // tokens 0, 1: B0, B1
       const float4 bq23 = reinterpret_cast<const float4*>(bl + g * 4 * NP)[1];   // tokens 2, 3
       const float bqs[8] = {bq01.x, bq01.y, bq01.z, bq01.w, bq23.x, bq23.y, bq23.z, bq23.w};
-      const float dls[4] = {dv.x, dv.y, dv.z, dv.w};
       const float uus[4] = {uv.x, uv.y, uv.z, uv.w};
-      float m4[4][NPW];   // Abar - 1, formed ahead of the recurrence (h-independent)
-      decay_m1_4x2<!kSp>(dls, A, m4);
-      static_for<4>([&](auto kk_c) {
-        constexpr int kk = decltype(kk_c)::value;
-        static_for<NPW>([&](auto j_c) {
-          constexpr int j = decltype(j_c)::value;
-          const float m = m4[kk][j];
+      const float dln[4] = {dv1.x, dv1.y, dv1.z, dv1.w};
+      float yy[4][NPW], ab[4][NPW], p1[4][NPW], m0[4][NPW], tt[4][NPW], mn[4][NPW];
+      auto tok = [&](int kk) {
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) {
+          const float m = mc[kk][j];
           if constexpr (kEuler) {
             h[j] += fmaf(m, h[j], bqs[kk * 2 + j] * uus[kk]);   // h + (m h + B (Delta u))
           } else {
             const float sv = bqs[kk * 2 + j] * uus[kk];   // B u
             h[j] = fmaf(m, h[j] + sv, h[j]);                           // A h + m (A h + B u)
           }
-        });
-      });
+        }
+      };
+      if constexpr (kSp) {
+        tok(0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) yy[q][j] = dln[q] * A[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) ab[q][j] = __builtin_amdgcn_exp2f(yy[q][j]);
+        }
+        tok(1);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) {
+              p1[q][j] = fmaf(yy[q][j], kDecayC2, kDecayC1);
+              m0[q][j] = ab[q][j] - kDecayHi;
+            }
+        }
+        tok(2);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) tt[q][j] = __builtin_amdgcn_fmed3f(m0[q][j] - yy[q][j] * p1[q][j], 0.0f, 1.0f);
+        }
+        tok(3);
+        __builtin_amdgcn_sched_barrier(0);
+        if (nxt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) mn[q][j] = m0[q][j] - tt[q][j];   // min(m0, p2), as in decay_m1
+        }
+      } else {
+        tok(0);
+        tok(1);
+        tok(2);
+        tok(3);
+        if (nxt) decay_m1_4x2<true>(dln, A, mn);
+      }
+      if (nxt) {
+        dv1 = dn2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < NPW; ++j) mc[q][j] = mn[q][j];
+      }
     }
     lds_barrier();
   }
