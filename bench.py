@@ -53,7 +53,7 @@ KERNEL_SOURCES_STEP = [os.path.join(CSRC, f) for f in ("scan_step.hip", "io.h")]
 PROFILE_TRAFFIC_CONV = os.path.join(ROOT, "profiles", "conv1d_mamba1.4b_traffic.txt")
 KERNEL_SOURCES_CONV = [os.path.join(CSRC, f) for f in ("conv1d.hip", "io.h")]
 PROFILE_TRAFFIC_SSD = os.path.join(ROOT, "profiles", "ssd_fwd_layer_traffic.txt")
-PROFILE_TRAFFIC_CONV_FUSED = os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba1.4b_kernel_trace.txt")
+PROFILE_TRAFFIC_CONV_FUSED = os.path.join(ROOT, "profiles", "scan_fwd_conv_mamba1.4b_traffic.txt")
 KERNEL_SOURCES_SSD = [os.path.join(CSRC, f) for f in ("ssd_fwd.hip", "io.h")]
 
 
