@@ -94,6 +94,19 @@ def test_edge_shapes_vs_oracle(case):
     check("final_state", fs, fsr, TOL[io])
 
 
+@pytest.mark.parametrize("dim,dstate", [(17, 16), (70, 16), (131, 16), (45, 40)])
+def test_chunked_ragged_channel_groups(dim, dstate):
+    """The fix-up runs in 16-channel workgroups and the scan in 64-channel ones: channel counts
+    that fill neither (the last fix-up group partly past dim), one and several 16-state groups."""
+    inp = forward_inputs(batch=3, dim=dim, dstate=dstate, seqlen=1500, io="f32", initial_state=True,
+                         seed=dim + dstate)
+    say(f"chunked ragged channel groups dim={dim} dstate={dstate}")
+    y, fs = gpu_fwd(inp, nchunks=4)
+    yr, fsr = oracle_fwd(inp)
+    check("y", y, yr, TOL["f32"])
+    check("final_state", fs, fsr, TOL["f32"])
+
+
 @pytest.mark.parametrize("nchunks", [2, 5, 47])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_chunked_carry_vs_oracle(nchunks, io):
