@@ -5,12 +5,13 @@ lengths (partial last chunk), one-token and empty sequences, d_state 64 and
 runs are identical; a split at a chunk boundary resumes bit for bit and at any
 other token within tolerance; the full-size layer on sampled heads.
 
-Tolerance: the products take bf16 operands (x, B, C as given; the masked decay
-matrix and the copy of the state that C reads rounded to bf16) or, in the state
-update, fp16 ones (B, and x times its decayed weight and a per-chunk power of
-two) with fp32 accumulation, so the bar is the bf16 one used throughout, 1e-2
-(max error over max(|ref|, rms)).  The small-Delta cases run where the weight
-alone is near fp16's subnormal range."""
+Tolerance: the products take bf16 operands with fp32 accumulation: x, B, C as
+given, the masked decay matrix rounded to bf16, and the two operands that carry
+fp32 values -- the state that C reads and x times its decayed weight in the
+state update -- each split as bf16 hi + bf16 of the rest (~2^-17 relative).  So
+the bar is the bf16 one used throughout, 1e-2 (max error over max(|ref|, rms)).
+The small-Delta cases run where the weight alone is ~1e-4 and a state keeps its
+inputs over many chunks."""
 import sys
 
 import pytest
