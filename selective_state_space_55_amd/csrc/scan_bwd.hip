@@ -436,6 +436,22 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
   // dB / dC partials over this wave's 32 channels: (batch, 32-channel group, state, token)
   const int64_t g32 = cg * 2 + (w & 1);
   float dD_acc = 0.0f, db_acc = 0.0f;
+  // a tile's global loads, issued while the previous (later) tile is worked on: every wave of
+  // the workgroup would otherwise wait the same memory round trip at each tile start
+  struct GLoad {
+    V4 d, u, dy, z, bc;
+  };
+  auto gload = [&](int64_t kt, GLoad& g) {
+    const int off = (int)(((int64_t)pc * a.seqlen + kt * kT + pg * kPiece) * kEsz);
+    g.d = IO::buf_load4(rs_d, off, kVec);
+    g.u = IO::buf_load4(rs_u, off, kVec);
+    g.dy = IO::buf_load4(rs_dy, off, kVec);
+    if constexpr (kGate) g.z = IO::buf_load4(rs_z, off, kVec);
+    if (stageBC)
+      g.bc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)(a.n0 + bn) * a.seqlen + kt * kT + bg * 4) * kEsz), kVec);
+  };
+  GLoad gl{};
+  if (a.ntile > 0) gload(a.ntile - 1, gl);
   __syncthreads();
 
   for (int64_t k = a.ntile - 1; k >= 0; --k) {
@@ -445,15 +461,13 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     const int nv = max(0, min(kPiece, nv_tile - pg * kPiece));   // valid tokens of this thread's piece
 
     // ---- load and stage ----
-    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);
-    const V4 rd = IO::buf_load4(rs_d, off, kVec);
-    const V4 ru = IO::buf_load4(rs_u, off, kVec);
-    const V4 rdy = IO::buf_load4(rs_dy, off, kVec);
-    V4 rz{};
-    if constexpr (kGate) rz = IO::buf_load4(rs_z, off, kVec);
-    V4 rbc{};
-    if (stageBC)
-      rbc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)(a.n0 + bn) * a.seqlen + tile + bg * 4) * kEsz), kVec);
+    const V4 rd = gl.d;
+    const V4 ru = gl.u;
+    const V4 rdy = gl.dy;
+    const V4 rz = gl.z;
+    const V4 rbc = gl.bc;
+    if (k > 0) gload(k - 1, gl);
+    const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);   // this thread's piece
     float hq[4][NPW];   // states entering the tile's sub-chunks (0 for sub-chunks past the end)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
