@@ -450,8 +450,22 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     if (stageBC)
       g.bc = IO::buf_load4(isB ? rs_B : rs_C, (int)(((int64_t)(a.n0 + bn) * a.seqlen + kt * kT + bg * 4) * kEsz), kVec);
   };
+  // the checkpointed states entering a tile's four sub-chunks, loaded a tile ahead as well
+  auto ckload = [&](int64_t kt, float (&hv)[4][NPW]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t s8 = kt * (kT / kSub) + s;
+      const bool ok = ch_ok && s8 < a.nsub;
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) hv[s][j] = ok ? ck[(s8 * NP + j) * a.dim] : 0.0f;
+    }
+  };
   GLoad gl{};
-  if (a.ntile > 0) gload(a.ntile - 1, gl);
+  float hqn[4][NPW] = {};
+  if (a.ntile > 0) {
+    gload(a.ntile - 1, gl);
+    ckload(a.ntile - 1, hqn);
+  }
   __syncthreads();
 
   for (int64_t k = a.ntile - 1; k >= 0; --k) {
@@ -470,12 +484,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BArgs a) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * kPiece) * kEsz);   // this thread's piece
     float hq[4][NPW];   // states entering the tile's sub-chunks (0 for sub-chunks past the end)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int64_t s8 = k * (kT / kSub) + s;
-      const bool ok = ch_ok && s8 < a.nsub;
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int j = 0; j < NPW; ++j) hq[s][j] = ok ? ck[(s8 * NP + j) * a.dim] : 0.0f;
-    }
+      for (int j = 0; j < NPW; ++j) hq[s][j] = hqn[s][j];
+    if (k > 0) ckload(k - 1, hqn);
 
     // piece owners keep, for the end of the tile: u, dytil, dz / ytil and dDelta / d(pre-softplus)
     float fu[4], dyt[4], gzf[4], sgx[4];
