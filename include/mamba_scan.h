@@ -99,7 +99,9 @@ typedef enum {
  *
  * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, seqlen >= 0, and
  * 64 * (seqlen + 8) * sizeof(io element) < 2^31 (seqlen < 4,194,296 for
- * bf16, 8,388,600 for fp32; larger returns MAMBA_SCAN_ERR_UNSUPPORTED).  seqlen == 0
+ * bf16, 8,388,600 for fp32; larger returns MAMBA_SCAN_ERR_UNSUPPORTED).  Every
+ * launch must fit a dispatch's 32-bit work-item count: batch * ceil(dim / 64) *
+ * chunks * 512 and batch * dim * dstate below 2^32 (else MAMBA_SCAN_ERR_UNSUPPORTED).  seqlen == 0
  * writes no y and sets final_state to initial_state (or zeros); the tensors
  * with a seqlen dimension (u, delta, B, C, z, y) are then empty and may be NULL.
  */
@@ -220,8 +222,8 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
  * parallel and joined through their carried states (as the time chunks of
  * mamba_scan_fwd), so one long sequence is not one long serial scan.
  * Sizes: nseq >= 1, dim >= 1, 1 <= dstate <= 64, total_len >= 0 with the seqlen
- * limit of mamba_scan_fwd; (nseq + ceil(total_len / 2048)) * ceil(dim / 64) < 2^31
- * and nseq * dim * dstate < 2^31 (else MAMBA_SCAN_ERR_UNSUPPORTED).
+ * limit of mamba_scan_fwd; (nseq + ceil(total_len / 2048)) * ceil(dim / 64) * 512 < 2^32
+ * (the launches' work-items) and nseq * dim * dstate < 2^31 (else MAMBA_SCAN_ERR_UNSUPPORTED).
  */
 int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, const int64_t* cu_seqlens,
@@ -280,7 +282,8 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
  *                    running sums over state groups
  *   flags            as for mamba_scan_fwd: MAMBA_SCAN_FLAG_SOFTPLUS, MAMBA_SCAN_FLAG_EULER
  * Sizes and limits as for mamba_scan_fwd (1 <= dstate <= 64, MAMBA_SCAN_MAX_DSTATE_BWD;
- * dstate > 16 runs one pass per 16 states).  Sums over channels (dB, dC) and
+ * dstate > 16 runs one pass per 16 states), and batch * dstate * seqlen < 2^32 (the dB/dC
+ * reduction's work-items; else MAMBA_SCAN_ERR_UNSUPPORTED).  Sums over channels (dB, dC) and
  * over batch rows (dA_log, dD, ddelta_bias) are taken in a fixed order, so
  * repeated calls give identical results.
  */
@@ -315,7 +318,8 @@ size_t mamba_scan_bwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  *   initial_state, final_state (batch, nheads, headdim, dstate) f32, 16-byte aligned, NULL allowed
  *   z                NULL means no gate
  * Supported: io_dtype MAMBA_SCAN_BF16, headdim a multiple of 32 up to 256, dstate 64 or 128
- * (others return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 32 < 2^31 and
+ * (others return MAMBA_SCAN_ERR_UNSUPPORTED); batch * nheads * headdim / 32 * 1024 < 2^32 (the
+ * launch's work-items, at most 1024 per slice) and
  * nheads * headdim <= 2^24.  Products take bf16 operands with fp32 accumulation, and the state is
  * carried in fp32.  Where a product reads the fp32 state, or x times its decayed input weight,
  * that operand is split as bf16 hi + bf16 (rest), which gives 16 significant bits over fp32's

@@ -25,6 +25,13 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
+// A launch of `blocks` workgroups of `threads` work-items: the dispatch's grid size
+// counts work-items in 32 bits.
+bool launch_ok(int64_t blocks, int64_t threads) {
+  int64_t t;
+  return blocks >= 0 && mul_ok(blocks, threads, &t) && t <= (int64_t)UINT32_MAX;
+}
+
 int check_common(int64_t batch, int64_t dim, int64_t dstate, int io_dtype) {
   if (io_dtype != MAMBA_SCAN_F32 && io_dtype != MAMBA_SCAN_BF16) return MAMBA_SCAN_ERR_DTYPE;
   if (batch < 1 || dim < 1 || dstate < 1) return MAMBA_SCAN_ERR_SHAPE;
@@ -47,6 +54,16 @@ int check_fwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, 
   return MAMBA_SCAN_OK;
 }
 
+// The forward's launches fit a dispatch: the scan (64-channel groups x time chunks, 512
+// work-items), the chunk fix-up (16-channel groups x later chunks, 128), the carry fold and
+// the state copy (one work-item per state).
+bool fwd_launches_ok(int64_t batch, int64_t dim, int64_t dstate, const mscan::FwdPlan& p) {
+  int64_t t;
+  return mul_ok(batch, (dim + 63) / 64, &t) && mul_ok(t, p.nchunks, &t) && launch_ok(t, 512) &&
+         mul_ok(batch, (dim + 15) / 16, &t) && mul_ok(t, p.nchunks - 1, &t) && launch_ok(t, 128) &&
+         mul_ok(batch * dim, dstate, &t) && launch_ok((t + 255) / 256, 256);
+}
+
 // Validation shared by the forward entry points: sizes, flags, pointers and the launch plan.
 int check_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C, const float* D,
               const void* z, const float* delta_bias, const float* initial_state, const float* final_state,
@@ -67,6 +84,7 @@ int check_fwd(const void* u, const void* delta, const float* A_log, const void* 
     if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, nchunks, states_per_wave, plan))
     return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (!fwd_launches_ok(batch, dim, dstate, *plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   return MAMBA_SCAN_OK;
 }
 
@@ -208,6 +226,7 @@ int mamba_scan_fwd_conv(const void* x, const float* conv_weight, const float* co
     if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   mscan::FwdPlan plan;
   if (!mscan::make_fwd_plan(batch, dim, dstate, seqlen, 0, 0, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (!fwd_launches_ok(batch, dim, dstate, plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
   }
@@ -252,7 +271,10 @@ int mamba_scan_fwd_varlen(const void* u, const void* delta, const float* A_log, 
   mscan::VarlenPlan plan;
   if (!mscan::make_varlen_plan(nseq, dim, dstate, total_len, &plan)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
-  if (!mul_ok(plan.maxp, (dim + 63) / 64, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid size
+  // grid sizes: the scan's (piece, 64-channel group) items of 512 work-items, the fix-up's
+  // (piece, 16-channel group) items of 128
+  if (!mul_ok(plan.maxp, (dim + 63) / 64, &t) || !launch_ok(t, 512)) return MAMBA_SCAN_ERR_UNSUPPORTED;
+  if (!mul_ok(plan.maxp, (dim + 15) / 16, &t) || !launch_ok(t, 128)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!mul_ok(nseq, dim * dstate, &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // carry threads
   if (!A_log || !cu_seqlens) return MAMBA_SCAN_ERR_NULL;
   if (total_len > 0 && (!u || !delta || !B || !C || !y)) return MAMBA_SCAN_ERR_NULL;
@@ -333,6 +355,14 @@ int mamba_scan_bwd(const void* u, const void* delta, const float* A_log, const v
     if (p && !aligned(p, 4)) return MAMBA_SCAN_ERR_ALIGN;
   mscan::BwdPlan plan;
   mscan::make_bwd_plan(batch, dim, dstate, seqlen, &plan);
+  {
+    // launches: checkpoint and gradient passes (64-channel groups, 512 work-items), the dB/dC
+    // reduction (one per (batch, state, token)), the parameter reduction
+    int64_t t, t2;
+    if (!mul_ok(batch, (dim + 63) / 64, &t) || !launch_ok(t, 512) || !mul_ok(batch * dstate, seqlen, &t2) ||
+        !launch_ok((t2 + 255) / 256, 256) || !launch_ok((dim * dstate + 255) / 256, 256))
+      return MAMBA_SCAN_ERR_UNSUPPORTED;
+  }
   if (plan.ws_total > 0) {
     if (!workspace || workspace_bytes < plan.ws_total || !aligned(workspace, 256)) return MAMBA_SCAN_ERR_WORKSPACE;
   }
@@ -360,7 +390,8 @@ int mamba_ssd_fwd(const void* x, const void* dt, const float* A_log, const void*
   if (headdim % 32 != 0 || headdim > 256 || (dstate != 64 && dstate != 128)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   int64_t t;
-  if (!mul_ok(batch, nheads * (headdim / 32), &t) || t > INT32_MAX) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid
+  // grid: at most headdim / 32 slices per head, at most 1024 work-items each
+  if (!mul_ok(batch, nheads * (headdim / 32), &t) || !launch_ok(t, 1024)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   // a chunk's 64 token rows of x / y (nheads * headdim bf16 each) are addressed with 32-bit offsets
   if (nheads > (1 << 24) / headdim) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!mul_ok(t, seqlen, &t) || !mul_ok(t, headdim * 2, &t)) return MAMBA_SCAN_ERR_SHAPE;

@@ -65,6 +65,9 @@ def test_fwd_validation_errors(lib):
     assert fwd(lib, dstate=65) == EUNSUP
     assert fwd(lib, npw=4) == EUNSUP                           # one layout: two states per lane
     assert fwd(lib, seqlen=1 << 24) == EUNSUP                 # 64 rows x L x 2 B must fit 31 bits
+    # a launch's work-items must fit 32 bits: 2^27 64-channel groups of 512 (one token each)
+    assert fwd(lib, batch=1 << 20, dim=1 << 13, seqlen=1) == EUNSUP
+    assert fwd(lib, batch=1 << 20, dim=1 << 13, seqlen=0) == EUNSUP   # the state copy: 2^37 states
     assert fwd(lib, batch=1 << 40, dim=1 << 30) == ESHAPE       # size overflow
     assert fwd(lib, u=P + 1) == EALIGN                         # bf16 needs 2-byte alignment
     assert fwd(lib, io=0, z=P + 2) == EALIGN                   # fp32 io needs 4-byte alignment
@@ -137,6 +140,7 @@ def test_bwd_validation_errors(lib):
     assert bwd(lib, dim=0) == ESHAPE
     assert bwd(lib, dstate=65) == EUNSUP
     assert bwd(lib, sp=4) == EUNSUP                              # unknown flag bit
+    assert bwd(lib, batch=1 << 20, dim=1 << 13, seqlen=1) == EUNSUP   # 2^36 work-items in the passes
     assert bwd(lib, du=P + 1) == EALIGN
     assert bwd(lib, dA=P + 2) == EALIGN
     assert bwd(lib, ws=None) == EWS
@@ -243,6 +247,7 @@ def test_ssd_validation_errors(lib):
     assert ssd(lib, h0=P + 4) == EALIGN
     assert ssd(lib, batch=1 << 20, H=1 << 12) == EUNSUP
     assert ssd(lib, batch=1 << 20, H=1 << 9, hd=256) == EUNSUP   # 2^31 32-channel slices
+    assert ssd(lib, batch=1 << 17, H=1 << 4, hd=64) == EUNSUP    # 2^22 slices x 1024 work-items
     assert ssd(lib, H=(1 << 16) + 1, hd=256) == EUNSUP             # a chunk's rows exceed 32-bit offsets
     assert ssd(lib, x=None, H=1 << 16, hd=256) == ENULL               # 2^24 channels per token still accepted
 
@@ -260,6 +265,7 @@ def test_fwd_conv_validation_errors(lib):
     assert fwd_conv(lib, dstate=17) == EUNSUP          # the fused path covers one 16-state group
     assert fwd_conv(lib, dstate=65) == EUNSUP
     assert fwd_conv(lib, flags=4) == EUNSUP
+    assert fwd_conv(lib, batch=1 << 20, dim=1 << 13, seqlen=1) == EUNSUP   # 2^36 work-items
     assert fwd_conv(lib, io=3) == EDTYPE
     assert fwd_conv(lib, x=P + 1) == EALIGN
     assert fwd_conv(lib, csi=P + 1) == EALIGN
