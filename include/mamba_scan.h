@@ -249,9 +249,10 @@ size_t mamba_scan_fwd_varlen_workspace_size(int64_t nseq, int64_t dim, int64_t d
  *   flags        as for mamba_scan_fwd (softplus of dt + dt_bias; Euler input term)
  *   y         (batch, dim)         io    OUT
  *
- * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, and batch <= 262140 (a
- * launch covers four batch rows per grid row; larger returns
- * MAMBA_SCAN_ERR_UNSUPPORTED).
+ * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, batch <= 262140 (a
+ * launch covers four batch rows per grid row) and dim * (4, 8 or 16 lanes for
+ * dstate up to 16, 32, 64) < 2^32 (a grid row's work-items); larger returns
+ * MAMBA_SCAN_ERR_UNSUPPORTED.
  */
 int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_log, const void* B, const void* C,
                     const float* D, const void* z, const float* dt_bias, int flags, void* y, int64_t batch,

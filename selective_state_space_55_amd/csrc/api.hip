@@ -307,6 +307,8 @@ int mamba_scan_step(float* state, const void* x, const void* dt, const float* A_
   int st = check_common(batch, dim, dstate, io_dtype);
   if (st != MAMBA_SCAN_OK) return st;
   if ((batch + 3) / 4 > 65535) return MAMBA_SCAN_ERR_UNSUPPORTED;   // grid rows of four batch rows
+  // a grid row's work-items: 4, 8 or 16 lanes per channel
+  if (!launch_ok((dim * (dstate <= 16 ? 4 : dstate <= 32 ? 8 : 16) + 255) / 256, 256)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (flags & ~(MAMBA_SCAN_FLAG_SOFTPLUS | MAMBA_SCAN_FLAG_EULER)) return MAMBA_SCAN_ERR_UNSUPPORTED;
   if (!state || !x || !dt || !A_log || !B || !C || !y) return MAMBA_SCAN_ERR_NULL;
   const size_t esz = io_dtype == MAMBA_SCAN_BF16 ? 2 : 4;

@@ -111,6 +111,7 @@ def test_step_validation_errors(lib):
     assert step(lib, batch=0) == ESHAPE
     assert step(lib, dstate=65) == EUNSUP
     assert step(lib, batch=4 * 65535 + 1) == EUNSUP              # grid rows of four batch rows
+    assert step(lib, batch=1, dim=1 << 28, dstate=64) == EUNSUP  # 2^32 work-items in a grid row
     assert step(lib, sp=8) == EUNSUP                             # unknown flag bit
     assert step(lib, state=P + 2) == EALIGN
     assert step(lib, x=P + 1) == EALIGN
