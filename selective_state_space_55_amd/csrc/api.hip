@@ -55,12 +55,13 @@ int check_fwd_sizes(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, 
 }
 
 // The forward's launches fit a dispatch: the scan (64-channel groups x time chunks, 512
-// work-items), the chunk fix-up (16-channel groups x later chunks, 128), the carry fold and
+// work-items), the chunk fix-up (16-channel groups x later chunks x ranges, 128), the carry fold and
 // the state copy (one work-item per state).
 bool fwd_launches_ok(int64_t batch, int64_t dim, int64_t dstate, const mscan::FwdPlan& p) {
   int64_t t;
   return mul_ok(batch, (dim + 63) / 64, &t) && mul_ok(t, p.nchunks, &t) && launch_ok(t, 512) &&
-         mul_ok(batch, (dim + 15) / 16, &t) && mul_ok(t, p.nchunks - 1, &t) && launch_ok(t, 128) &&
+         mul_ok(batch, (dim + 15) / 16, &t) && mul_ok(t, p.nchunks - 1, &t) && mul_ok(t, p.nranges, &t) &&
+         launch_ok(t, 128) &&
          mul_ok(batch * dim, dstate, &t) && launch_ok((t + 255) / 256, 256);
 }
 

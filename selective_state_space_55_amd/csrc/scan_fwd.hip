@@ -128,6 +128,11 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
                     ? reinterpret_cast<float*>(ws + align256(sizeof(float) *
                                                              (size_t)(a.batch * a.dim * p.nchunks * p.np)))
                     : nullptr;
+  // the sum of Delta over each range of a chunk (chunks of several ranges)
+  float* rsum = (p.nchunks > 1 && p.nranges > 1)
+                    ? reinterpret_cast<float*>(reinterpret_cast<char*>(dsum) +
+                                               align256(sizeof(float) * (size_t)(a.batch * a.dim * p.nchunks)))
+                    : nullptr;
   const size_t esz = sizeof(IoT);
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a.u) | reinterpret_cast<uintptr_t>(a.delta) |
                         reinterpret_cast<uintptr_t>(a.y) | reinterpret_cast<uintptr_t>(a.z) |
@@ -138,6 +143,7 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   k.conv_w = a.conv_w; k.conv_b = a.conv_b; k.conv_state = a.conv_state; k.u_out = a.u_out;
   k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
+  k.rsum = rsum; k.nranges = p.nranges;
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.mode = (a.softplus ? kModeSoftplus : 0) | (a.euler ? kModeEuler : 0); k.gated = a.z != nullptr;
@@ -162,9 +168,10 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     FixArgs f{};
     f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = carry;
+    f.rsum = rsum; f.nranges = p.nranges;
     f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks;
     f.chgroups = (a.dim + kFixCh - 1) / kFixCh;   // the fix-up's narrower channel groups
-    f.nwork = a.batch * f.chgroups * (p.nchunks - 1); f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
+    f.nwork = a.batch * f.chgroups * (p.nchunks - 1) * p.nranges; f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
     launch_fix_ng<IoT, false>(f, ng, vec, s);
     return hipGetLastError();
   }
@@ -199,10 +206,12 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   const int64_t tiles_per = (tiles + nch - 1) / nch;
   p->chunk_len = std::max<int64_t>(1, tiles_per) * T;
   p->nchunks = tiles > 0 ? (tiles + tiles_per - 1) / tiles_per : 1;
+  p->nranges = p->nchunks > 1 ? (p->chunk_len + kFixRange - 1) / kFixRange : 1;
   p->ws_carry = 0;
   if (p->nchunks > 1)
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +
-                  align256(sizeof(float) * (size_t)(batch * dim * p->nchunks));
+                  align256(sizeof(float) * (size_t)(batch * dim * p->nchunks)) +
+                  (p->nranges > 1 ? align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->nranges)) : 0);
   p->off_yacc = p->ws_carry;
   p->ws_yacc = p->ngroups > 1 ? align256(sizeof(float) * (size_t)(batch * dim * seqlen)) : 0;
   p->ws_total = seqlen == 0 ? 0 : p->ws_carry + p->ws_yacc;

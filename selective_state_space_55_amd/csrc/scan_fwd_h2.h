@@ -16,6 +16,13 @@ constexpr int kPad = 4;   // LDS row padding in floats
 constexpr int kModeSoftplus = 1;   // Delta = softplus(delta + bias)
 constexpr int kModeEuler = 2;      // Bbar u = Delta B u instead of the zero-order hold
 
+// A chunk's fix-up is cut into ranges of kFixRange tokens, one workgroup each: a range
+// starts from the chunk's Delta summed over the ranges before it (recorded by the scan)
+// and stops when its states have decayed, so a slowly decaying channel's correction runs
+// in parallel ranges rather than as one long sequential walk.
+constexpr int kFixRangeTiles = 32;
+constexpr int64_t kFixRange = 64 * kFixRangeTiles;
+
 struct KArgs {
   const void* u;
   const void* delta;
@@ -30,6 +37,8 @@ struct KArgs {
   void* y;
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
+  float* rsum;         // [batch][dim][nchunks][nranges]: sum of Delta*log2e over each kFixRange-token range
+  int64_t nranges;     // (chunks of more than one range; else rsum is null)
   float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
@@ -205,6 +214,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   // the chunk's sum of Delta*log2e over this thread's staging pieces (channel pc, tokens
   // 8 pg .. 8 pg + 7 of every tile; masked tokens are staged as 0)
   float dsum_st = 0.0f;
+  float rsum_st = 0.0f;   // the same over the current range of the chunk (rsum)
   const bool gate_on = a.gated != 0;
   const float gate_off = gate_on ? 0.0f : 1.0f;
 
@@ -315,7 +325,24 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       fd[j] = ok ? dl : 0.0f;
       fu[j] = ok ? fu[j] : 0.0f;
     }
-    dsum_st += ((fd[0] + fd[1]) + (fd[2] + fd[3])) + ((fd[4] + fd[5]) + (fd[6] + fd[7]));
+    const float psum = ((fd[0] + fd[1]) + (fd[2] + fd[3])) + ((fd[4] + fd[5]) + (fd[6] + fd[7]));
+    dsum_st += psum;
+    if constexpr (!kVarlen) {
+      if (a.rsum != nullptr && tile < t_end) {
+        // the range's sum of Delta*log2e for the fix-up, written when the range's last tile is staged
+        rsum_st += psum;
+        const int64_t lt = (tile - t_begin) / T;
+        if ((lt + 1) % kFixRangeTiles == 0 || tile + T >= t_end) {
+          float rs = rsum_st;
+          rs += __shfl_xor(rs, 1);
+          rs += __shfl_xor(rs, 2);
+          rs += __shfl_xor(rs, 4);
+          if (pg == 0 && d0 + pc < a.dim)
+            a.rsum[((sidx * a.dim + d0 + pc) * a.nchunks + kc) * a.nranges + lt / kFixRangeTiles] = rs;
+          rsum_st = 0.0f;
+        }
+      }
+    }
     float fs[8];   // what the scan reads per token: u, or Delta*u for the Euler input term
 #pragma unroll
     for (int j = 0; j < 8; ++j) fs[j] = kEuler ? (fd[j] * kLn2) * fu[j] : fu[j];
@@ -692,6 +719,8 @@ struct FixArgs {
   const void* z;
   void* y;
   const float* carry;
+  const float* rsum;       // per-range Delta sums (nranges > 1), as written by the scan
+  int64_t nranges;         // ranges per chunk (1 for variable-length pieces)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, softplus;
 };
@@ -717,6 +746,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   __shared__ float sH[kFixCh * kSRow];
   __shared__ float par[kFixCh];
   __shared__ unsigned long long live_w[kFixNT / 64];   // per wave: states still above the cut-off
+  __shared__ unsigned long long live0;                 // states above the cut-off at the range start
   lds_poison(cbuf, (int)sizeof(cbuf));
   lds_poison(live_w, (int)sizeof(live_w));
   lds_poison(sA, (int)sizeof(sA));
@@ -729,6 +759,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   const int pc = tid / 8;               // channel within the group
   const int pg = tid % 8;               // tokens 8 pg .. 8 pg + 7 of a tile
   int64_t kc, cg, b, t_begin, t_end, slot0;   // slot0: carry slot of channel 0 of the group
+  int64_t rj = 0;                              // the range of the chunk (fixed-length rows)
   if constexpr (kVarlen) {
     cg = blockIdx.x % a.chgroups;
     const int64_t pidx = blockIdx.x / a.chgroups;
@@ -751,14 +782,20 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     t_end = min(t_begin + a.chunk_len, s_end);
     slot0 = pidx * a.dim;
   } else {
-    int64_t wid = work_id(blockIdx.x, a.nwork);
+    // launch order: every (chunk, channel group)'s first range, then every second range, ...
+    const int64_t per = a.nwork / a.nranges;
+    rj = (int64_t)blockIdx.x / per;
+    int64_t wid = work_id((int64_t)blockIdx.x % per, per);
     const int64_t nk1 = a.nchunks - 1;
     kc = wid % nk1 + 1;
     wid /= nk1;
     cg = wid % a.chgroups;
     b = wid / a.chgroups;
-    t_begin = kc * a.chunk_len;
-    t_end = min(t_begin + a.chunk_len, a.seqlen);
+    const int64_t c_begin = kc * a.chunk_len;
+    const int64_t c_end = min(c_begin + a.chunk_len, a.seqlen);
+    t_begin = c_begin + rj * kFixRange;
+    if (t_begin >= c_end) return;     // (the last chunk may be shorter)
+    t_end = min(t_begin + kFixRange, c_end);
     slot0 = -1;
   }
   const int64_t d0 = cg * kFixCh;
@@ -766,6 +803,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   const bool ch_ok = d < a.dim;
   const int64_t t_first = kVarlen ? (t_begin & ~(int64_t)(T - 1)) : t_begin;
   if (tid < kFixCh) par[tid] = (d0 + tid < a.dim && a.bias) ? a.bias[d0 + tid] : 0.0f;
+  if (tid == 0) live0 = 0;
   bool finite = true;
   for (int i = tid; i < kFixCh * NPS; i += kFixNT) {
     const int c = i / NPS, n = i % NPS;
@@ -803,6 +841,33 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   // States decay at their own rates (|A_n| spans an order of magnitude), so most
   // are dropped long before the slowest.
   uint64_t live = NPS == 64 ? ~0ull : ((1ull << NPS) - 1);
+  if (!kVarlen && rj > 0) {
+    // cumDelta before the range: the scan's sums over the chunk's earlier ranges, split over
+    // the channel's 8 threads
+    float sb = 0.0f;
+    if (ch_ok) {
+      const float* rs = a.rsum + ((b * a.dim + d) * a.nchunks + kc) * a.nranges;
+      for (int64_t i = pg; i < rj; i += 8) sb += rs[i];
+    }
+    sb += __shfl_xor(sb, 1, 8);
+    sb += __shfl_xor(sb, 2, 8);
+    sb += __shfl_xor(sb, 4, 8);
+    base = sb;
+    if (may_stop) {
+      // states already below the cut-off at the range start stay so (Delta >= 0): dropped,
+      // and a range with none left does nothing
+      unsigned long long m = 0;
+      if (ch_ok)
+        for (int n = pg; n < NPS; n += 8)
+          if (__builtin_amdgcn_exp2f(sA[pc * kSRow + n] * base) >= 2.3283064e-10f) m |= 1ull << n;
+      if (m != 0) atomicOr(&live0, m);
+      __syncthreads();
+      const unsigned long long l0 = live0;
+      live &= ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(l0 >> 32)) << 32) |
+              __builtin_amdgcn_readfirstlane((uint32_t)l0);
+      if (live == 0) return;
+    }
+  }
   // a tile's global loads; the next tile's are issued before this tile's work,
   // so their latency overlaps it (the work per tile is small once most states
   // are dropped, and the loop would otherwise wait a memory round trip per tile;
