@@ -15,7 +15,11 @@ struct FwdPlan {
   int tile;           // tokens staged per workgroup iteration
   int64_t nchunks;    // time chunks scanned in parallel (1 = one pass)
   int64_t chunk_len;  // tokens per chunk, a multiple of tile
-  int64_t nranges;    // ranges of kFixRange tokens per chunk: the chunk fix-up's work items
+  int64_t nranges;    // ranges of range_tiles tiles per chunk: the chunk fix-up's work items
+  int range_tiles;    // a power of two
+  // two chunks of unequal length (a head of chunk_len tokens and the rest), launched chunk
+  // by chunk: every head first, one per CU, then the tails on the CUs left over
+  int head_tail;
   int64_t lp;         // seqlen rounded up to a multiple of tile
   int ngroups;        // 16-state passes (dstate > 16 runs several)
   size_t ws_carry;    // bytes of chunk carry (h_end / h_in) + chunk Delta sums

@@ -143,7 +143,8 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   k.conv_w = a.conv_w; k.conv_b = a.conv_b; k.conv_state = a.conv_state; k.u_out = a.u_out;
   k.u = a.u; k.delta = a.delta; k.A_log = a.A_log; k.B = a.B; k.C = a.C; k.D = a.D; k.z = a.z; k.bias = a.bias;
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
-  k.rsum = rsum; k.nranges = p.nranges;
+  k.rsum = rsum; k.nranges = p.nranges; k.range_tiles = p.range_tiles; k.head_tail = p.head_tail;
+  k.range_shift = __builtin_ctz((unsigned)p.range_tiles);
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.mode = (a.softplus ? kModeSoftplus : 0) | (a.euler ? kModeEuler : 0); k.gated = a.z != nullptr;
@@ -168,7 +169,7 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     if (e != hipSuccess) return e;
     FixArgs f{};
     f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = carry;
-    f.rsum = rsum; f.nranges = p.nranges;
+    f.rsum = rsum; f.nranges = p.nranges; f.range_len = (int64_t)p.range_tiles * p.tile;
     f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks;
     f.chgroups = (a.dim + kFixCh - 1) / kFixCh;   // the fix-up's narrower channel groups
     f.nwork = a.batch * f.chgroups * (p.nchunks - 1) * p.nranges; f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
@@ -179,6 +180,8 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
 }
 
 }  // namespace
+
+constexpr int64_t kCUs = 256;   // MI355X compute units (one scan workgroup per CU, by LDS)
 
 bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int64_t nchunks_req, int npw_req,
                    FwdPlan* p) {
@@ -196,17 +199,34 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   p->lp = tiles * T;
   int64_t nch = 1;
   const int64_t groups = batch * ((dim + kCh - 1) / kCh);
+  int64_t head_tiles = 0;   // > 0: a head and a tail chunk of unequal length
+  p->range_tiles = kFixRangeTiles;
   if (nchunks_req > 0) {
     nch = nchunks_req;
   } else if (groups < 128 && tiles >= 16) {
     // too few workgroups to fill 256 CUs: scan time chunks in parallel (each >= 8 tiles)
-    nch = std::min<int64_t>(256 / groups, tiles / 8);
+    nch = std::min<int64_t>(kCUs / groups, tiles / 8);
+  } else if (groups > 128 && groups < kCUs) {
+    // groups on as many CUs and kCUs - groups idle: each row's head runs on its own CU while
+    // the tails, `rounds` at a time, take the idle CUs; with the tail a (rounds + 1)-th of the
+    // row, heads and tails end together.  The tails' fix-up (every state still live over a
+    // tail) runs in 2-tile ranges, spread over the whole GPU.  At most 4 rounds and tails of
+    // at least 8 tiles: shorter or more tails cost more in start-up and fix-up than they save.
+    const int64_t rounds = (groups + (kCUs - groups) - 1) / (kCUs - groups);
+    const int64_t tail = tiles / (rounds + 1);
+    if (rounds <= 4 && tail >= 8) {
+      head_tiles = tiles - tail;
+      nch = 2;
+      p->range_tiles = 2;
+    }
   }
   nch = std::max<int64_t>(1, std::min<int64_t>(nch, std::max<int64_t>(tiles, 1)));
-  const int64_t tiles_per = (tiles + nch - 1) / nch;
+  const int64_t tiles_per = head_tiles > 0 ? head_tiles : (tiles + nch - 1) / nch;
   p->chunk_len = std::max<int64_t>(1, tiles_per) * T;
   p->nchunks = tiles > 0 ? (tiles + tiles_per - 1) / tiles_per : 1;
-  p->nranges = p->nchunks > 1 ? (p->chunk_len + kFixRange - 1) / kFixRange : 1;
+  p->head_tail = head_tiles > 0 && p->nchunks == 2;
+  const int64_t range_len = (int64_t)p->range_tiles * T;
+  p->nranges = p->nchunks > 1 ? (p->chunk_len + range_len - 1) / range_len : 1;
   p->ws_carry = 0;
   if (p->nchunks > 1)
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +

@@ -16,12 +16,11 @@ constexpr int kPad = 4;   // LDS row padding in floats
 constexpr int kModeSoftplus = 1;   // Delta = softplus(delta + bias)
 constexpr int kModeEuler = 2;      // Bbar u = Delta B u instead of the zero-order hold
 
-// A chunk's fix-up is cut into ranges of kFixRange tokens, one workgroup each: a range
-// starts from the chunk's Delta summed over the ranges before it (recorded by the scan)
-// and stops when its states have decayed, so a slowly decaying channel's correction runs
-// in parallel ranges rather than as one long sequential walk.
+// A chunk's fix-up is cut into ranges (kFixRangeTiles tiles by default), one workgroup
+// each: a range starts from the chunk's Delta summed over the ranges before it (recorded
+// by the scan) and stops when its states have decayed, so a slowly decaying channel's
+// correction runs in parallel ranges rather than as one long sequential walk.
 constexpr int kFixRangeTiles = 32;
-constexpr int64_t kFixRange = 64 * kFixRangeTiles;
 
 struct KArgs {
   const void* u;
@@ -37,8 +36,10 @@ struct KArgs {
   void* y;
   float* carry;        // [batch][dim][nchunks][np]
   float* dsum;         // [batch][dim][nchunks]
-  float* rsum;         // [batch][dim][nchunks][nranges]: sum of Delta*log2e over each kFixRange-token range
+  float* rsum;         // [batch][dim][nchunks][nranges]: sum of Delta*log2e over each range of range_tiles tiles
   int64_t nranges;     // (chunks of more than one range; else rsum is null)
+  int range_tiles, range_shift;   // a power of two and its log2
+  int head_tail;       // work items chunk by chunk in launch order (every head, then the tails)
   float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, mode, gated;   // mode: kModeSoftplus | kModeEuler
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   // varlen: work items of unequal length are dealt round-robin over the XCDs as
   // launched (a contiguous range per XCD would give one XCD all of a long
   // sequence's channel groups)
-  int64_t wid = kVarlen ? (int64_t)blockIdx.x : work_id(blockIdx.x, a.nwork);
+  int64_t wid = (kVarlen || a.head_tail) ? (int64_t)blockIdx.x : work_id(blockIdx.x, a.nwork);
   // kc of nk: this work item's time chunk (varlen: piece pidx, the kc-th of its sequence's nk)
   int64_t kc, nk, cg, b, t_begin, t_end, sidx, pidx = 0;   // sidx: batch row or sequence of the state arrays
   if constexpr (kVarlen) {
@@ -165,8 +166,14 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     t_begin = min(s_begin + kc * a.chunk_len, s_end);
     t_end = min(t_begin + a.chunk_len, s_end);
   } else {
-    kc = wid % a.nchunks;
-    wid /= a.nchunks;
+    if (a.head_tail) {   // chunk-major: every head is dispatched before any tail
+      const int64_t per = a.nwork / a.nchunks;
+      kc = wid / per;
+      wid %= per;
+    } else {
+      kc = wid % a.nchunks;
+      wid /= a.nchunks;
+    }
     cg = wid % a.chgroups;
     b = wid / a.chgroups;
     sidx = b;
@@ -331,14 +338,14 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
       if (a.rsum != nullptr && tile < t_end) {
         // the range's sum of Delta*log2e for the fix-up, written when the range's last tile is staged
         rsum_st += psum;
-        const int64_t lt = (tile - t_begin) / T;
-        if ((lt + 1) % kFixRangeTiles == 0 || tile + T >= t_end) {
+        const int64_t lt = (tile - t_begin) / T;   // the tile within the chunk
+        if (((lt + 1) & (a.range_tiles - 1)) == 0 || tile + T >= t_end) {
           float rs = rsum_st;
           rs += __shfl_xor(rs, 1);
           rs += __shfl_xor(rs, 2);
           rs += __shfl_xor(rs, 4);
           if (pg == 0 && d0 + pc < a.dim)
-            a.rsum[((sidx * a.dim + d0 + pc) * a.nchunks + kc) * a.nranges + lt / kFixRangeTiles] = rs;
+            a.rsum[((sidx * a.dim + d0 + pc) * a.nchunks + kc) * a.nranges + (lt >> a.range_shift)] = rs;
           rsum_st = 0.0f;
         }
       }
@@ -721,6 +728,7 @@ struct FixArgs {
   const float* carry;
   const float* rsum;       // per-range Delta sums (nranges > 1), as written by the scan
   int64_t nranges;         // ranges per chunk (1 for variable-length pieces)
+  int64_t range_len;       // tokens per range (a multiple of 64)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, softplus;
 };
@@ -793,9 +801,9 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     b = wid / a.chgroups;
     const int64_t c_begin = kc * a.chunk_len;
     const int64_t c_end = min(c_begin + a.chunk_len, a.seqlen);
-    t_begin = c_begin + rj * kFixRange;
+    t_begin = c_begin + rj * a.range_len;
     if (t_begin >= c_end) return;     // (the last chunk may be shorter)
-    t_end = min(t_begin + kFixRange, c_end);
+    t_end = min(t_begin + a.range_len, c_end);
     slot0 = -1;
   }
   const int64_t d0 = cg * kFixCh;

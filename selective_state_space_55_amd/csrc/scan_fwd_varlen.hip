@@ -146,6 +146,7 @@ hipError_t run_varlen(const FwdArgs& a, const VarlenPlan& p, hipStream_t s) {
   f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.piece; f.nchunks = 1;
   f.chgroups = (a.dim + kFixCh - 1) / kFixCh;   // the fix-up's narrower channel groups
   f.rsum = nullptr; f.nranges = 1;               // a piece is one range
+  f.range_len = p.piece;
   f.nwork = p.maxp * f.chgroups; f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
   launch_fix_ng<IoT, true>(f, ng, vec, s);
   e = hipGetLastError();
