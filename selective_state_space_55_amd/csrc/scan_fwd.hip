@@ -210,14 +210,16 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
     // groups on as many CUs and kCUs - groups idle: each row's head runs on its own CU while
     // the tails, `rounds` at a time, take the idle CUs; with the tail a (rounds + 1)-th of the
     // row, heads and tails end together.  The tails' fix-up (every state still live over a
-    // tail) runs in 2-tile ranges, spread over the whole GPU.  At most 4 rounds and tails of
-    // at least 8 tiles: shorter or more tails cost more in start-up and fix-up than they save.
+    // tail) runs in ranges of a quarter of a tail (2 or 4 tiles), spread over the whole GPU.
+    // At most 4 rounds and tails of 8 to 16 tiles (measured at 8: the 130M layer): shorter or
+    // more tails cost more in start-up and fix-up than they save, and longer ones are not
+    // measured.
     const int64_t rounds = (groups + (kCUs - groups) - 1) / (kCUs - groups);
     const int64_t tail = tiles / (rounds + 1);
-    if (rounds <= 4 && tail >= 8) {
+    if (rounds <= 4 && tail >= 8 && tail <= 16) {
       head_tiles = tiles - tail;
       nch = 2;
-      p->range_tiles = 2;
+      p->range_tiles = tail > 8 ? 4 : 2;
     }
   }
   nch = std::max<int64_t>(1, std::min<int64_t>(nch, std::max<int64_t>(tiles, 1)));
