@@ -107,6 +107,21 @@ def test_chunked_ragged_channel_groups(dim, dstate):
     check("final_state", fs, fsr, TOL["f32"])
 
 
+@pytest.mark.parametrize("dim,L,io", [(3072, 1600, "f32"), (3000, 3000, "bf16")])
+def test_head_tail_plan_vs_oracle(dim, L, io):
+    """Between 128 and 256 channel groups the automatic plan splits each row into a head (one
+    workgroup per CU, launched first) and a tail on the CUs left idle, whose fix-up runs in short
+    ranges: 141-144 groups, tails of 8 tiles (2-tile ranges) and 15 tiles (4-tile ranges)."""
+    inp = forward_inputs(batch=3, dim=dim, dstate=16, seqlen=L, io=io, initial_state=True, seed=L)
+    say(f"head/tail plan dim={dim} L={L} io={io}")
+    y, fs = gpu_fwd(inp)
+    yr, fsr = oracle_fwd(inp)
+    check("y", y, yr, TOL[io])
+    check("final_state", fs, fsr, TOL[io])
+    y1, _ = gpu_fwd(inp, nchunks=1)
+    assert max_rel_err(y, y1.double()) <= (1e-5 if io == "f32" else 2e-2)
+
+
 @pytest.mark.parametrize("nchunks", [2, 5, 47])
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_chunked_carry_vs_oracle(nchunks, io):
