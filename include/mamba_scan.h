@@ -132,8 +132,9 @@ size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate,
  * Limit: calls whose mamba_scan_fwd_workspace_size(...) exceeds
  * MAMBA_SCAN_NOALLOC_SCRATCH_BYTES return MAMBA_SCAN_ERR_WORKSPACE and launch
  * nothing (the automatic plan's chunk carry is at most ~7 MB for any size, its per-range
- * sums of Delta at most 16 x seqlen bytes + 1.5 MB more; a dstate > 16 call adds
- * batch x dim x seqlen x 4 bytes).  Every call on one GPU shares that GPU's array
+ * sums of Delta at most 16 x seqlen bytes + 1.5 MB more; for 129-204 channel groups of 64
+ * with short sequences the plan's tail chunk keeps its y in fp32, at most ~54 MB; a
+ * dstate > 16 call adds batch x dim x seqlen x 4 bytes).  Every call on one GPU shares that GPU's array
  * and leaves its contents behind (each call writes what it reads, so nothing needs
  * clearing): calls that overlap in time on one GPU -- on different streams or
  * threads -- race on it and must be serialized by the caller.

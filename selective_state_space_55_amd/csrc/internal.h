@@ -20,6 +20,8 @@ struct FwdPlan {
   // two chunks of unequal length (a head of chunk_len tokens and the rest), launched chunk
   // by chunk: every head first, one per CU, then the tails on the CUs left over
   int head_tail;
+  int64_t tail_tiles; // head/tail: the tail's tiles (its fp32 y rows are tail_tiles * tile long)
+  size_t off_yf32;    // head/tail: byte offset of the tail's fp32 y in the workspace
   int64_t lp;         // seqlen rounded up to a multiple of tile
   int ngroups;        // 16-state passes (dstate > 16 runs several)
   size_t ws_carry;    // bytes of chunk carry (h_end / h_in) + chunk Delta sums

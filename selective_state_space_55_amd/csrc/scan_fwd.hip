@@ -145,6 +145,8 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
   k.h0 = a.h0; k.final_state = a.final_state; k.y = a.y; k.carry = carry; k.dsum = dsum;
   k.rsum = rsum; k.nranges = p.nranges; k.range_tiles = p.range_tiles; k.head_tail = p.head_tail;
   k.range_shift = __builtin_ctz((unsigned)p.range_tiles);
+  k.yf32 = p.head_tail ? reinterpret_cast<float*>(ws + p.off_yf32) : nullptr;
+  k.yf32_pitch = p.tail_tiles * p.tile;
   k.dim = a.dim; k.seqlen = a.seqlen; k.chunk_len = p.chunk_len; k.nchunks = p.nchunks;
   k.chgroups = (a.dim + kCh - 1) / kCh;
   k.dstate = (int)a.dstate; k.np = p.np; k.mode = (a.softplus ? kModeSoftplus : 0) | (a.euler ? kModeEuler : 0); k.gated = a.z != nullptr;
@@ -170,6 +172,7 @@ hipError_t run_fwd(const FwdArgs& a, const FwdPlan& p, hipStream_t s) {
     FixArgs f{};
     f.delta = a.delta; f.bias = a.bias; f.A_log = a.A_log; f.C = a.C; f.z = a.z; f.y = a.y; f.carry = carry;
     f.rsum = rsum; f.nranges = p.nranges; f.range_len = (int64_t)p.range_tiles * p.tile;
+    f.yf32 = k.yf32; f.yf32_pitch = k.yf32_pitch;
     f.dim = a.dim; f.seqlen = a.seqlen; f.chunk_len = p.chunk_len; f.nchunks = p.nchunks;
     f.chgroups = (a.dim + kFixCh - 1) / kFixCh;   // the fix-up's narrower channel groups
     f.nwork = a.batch * f.chgroups * (p.nchunks - 1) * p.nranges; f.dstate = (int)a.dstate; f.np = p.np; f.softplus = a.softplus;
@@ -209,14 +212,16 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   } else if (groups > 128 && groups < kCUs) {
     // groups on as many CUs and kCUs - groups idle: each row's head runs on its own CU while
     // the tails, `rounds` at a time, take the idle CUs; with the tail a (rounds + 1)-th of the
-    // row, heads and tails end together.  The tails' fix-up (every state still live over a
-    // tail) runs in ranges of a quarter of a tail (2 or 4 tiles), spread over the whole GPU.
-    // At most 4 rounds and tails of 8 to 16 tiles (measured at 8: the 130M layer): shorter or
-    // more tails cost more in start-up and fix-up than they save, and longer ones are not
-    // measured.
+    // row (less a tile per extra round: a workgroup's start-up, its first prefetches and
+    // staging, costs about a tile, paid by a head once and by the tails once per round), heads
+    // and tails end together.  The tails' fix-up (every state still live over a tail) runs in
+    // ranges of a quarter of a tail (2 or 4 tiles), spread over the whole GPU.  At most 4
+    // rounds and tails of 6 to 16 tiles (measured at 7: the 130M layer; 8 and 9 tiles there
+    // were slower): shorter or more tails cost more in start-up and fix-up than they save,
+    // and longer ones are not measured.
     const int64_t rounds = (groups + (kCUs - groups) - 1) / (kCUs - groups);
-    const int64_t tail = tiles / (rounds + 1);
-    if (rounds <= 4 && tail >= 8 && tail <= 16) {
+    const int64_t tail = (tiles - (rounds - 1)) / (rounds + 1);
+    if (rounds <= 4 && tail >= 6 && tail <= 16) {
       head_tiles = tiles - tail;
       nch = 2;
       p->range_tiles = tail > 8 ? 4 : 2;
@@ -227,6 +232,7 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
   p->chunk_len = std::max<int64_t>(1, tiles_per) * T;
   p->nchunks = tiles > 0 ? (tiles + tiles_per - 1) / tiles_per : 1;
   p->head_tail = head_tiles > 0 && p->nchunks == 2;
+  p->tail_tiles = p->head_tail ? tiles - head_tiles : 0;
   const int64_t range_len = (int64_t)p->range_tiles * T;
   p->nranges = p->nchunks > 1 ? (p->chunk_len + range_len - 1) / range_len : 1;
   p->ws_carry = 0;
@@ -234,6 +240,10 @@ bool make_fwd_plan(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, i
     p->ws_carry = align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->np)) +
                   align256(sizeof(float) * (size_t)(batch * dim * p->nchunks)) +
                   (p->nranges > 1 ? align256(sizeof(float) * (size_t)(batch * dim * p->nchunks * p->nranges)) : 0);
+  // head/tail: the tail's gated y in fp32, so its outputs are rounded to the io dtype once
+  // (after the fix-up's correction), as in a one-pass scan
+  p->off_yf32 = p->ws_carry;
+  if (p->head_tail) p->ws_carry += align256(sizeof(float) * (size_t)(batch * dim * p->tail_tiles * T));
   p->off_yacc = p->ws_carry;
   p->ws_yacc = p->ngroups > 1 ? align256(sizeof(float) * (size_t)(batch * dim * seqlen)) : 0;
   p->ws_total = seqlen == 0 ? 0 : p->ws_carry + p->ws_yacc;

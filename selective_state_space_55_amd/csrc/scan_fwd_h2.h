@@ -39,6 +39,10 @@ struct KArgs {
   float* rsum;         // [batch][dim][nchunks][nranges]: sum of Delta*log2e over each range of range_tiles tiles
   int64_t nranges;     // (chunks of more than one range; else rsum is null)
   int range_tiles, range_shift;   // a power of two and its log2
+  // head/tail plan: the tail chunk's gated y in fp32, (batch, dim, yf32_pitch), rounded to
+  // the io dtype once, by the fix-up, after its correction is added
+  float* yf32;
+  int64_t yf32_pitch;
   int head_tail;       // work items chunk by chunk in launch order (every head, then the tails)
   float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
@@ -436,11 +440,29 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
     for (int j = 0; j < 8; ++j) yv[j] = fmaf(Dd, kp.u[j], yv[j]) * (silu(zf[j]) + gate_off);
     return true;
   };
+  // head/tail plan, tail chunk: y goes to the fp32 buffer (rows padded to whole tiles, so the
+  // pieces past the end are written too, into the padding).  The pipelined body's call for
+  // tile k-1 at k = 0 (tile before the chunk) stores nothing: it would land in the previous row.
+  const bool y_to_f32 = !kVarlen && a.yf32 != nullptr && kc == 1;
+  auto epi_store_f32 = [&](int64_t tile, const float (&yv)[8]) {
+    if (tile < t_begin || d0 + pc >= a.dim) return;
+    float* p = a.yf32 + (b * a.dim + d0 + pc) * a.yf32_pitch + (tile - t_begin) + pg * 8;
+    reinterpret_cast<float4*>(p)[0] = make_float4(yv[0], yv[1], yv[2], yv[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(yv[4], yv[5], yv[6], yv[7]);
+  };
   auto epi_store_full = [&](int64_t tile, const float (&yv)[8], __amdgpu_buffer_rsrc_t rs) {
+    if (y_to_f32) {
+      epi_store_f32(tile, yv);
+      return;
+    }
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     IO::buf_store8(rs, off, IO::from_f32(yv), kVec);
   };
   auto epi_store_tail = [&](int64_t tile, const float (&yv)[8]) {
+    if (y_to_f32) {
+      epi_store_f32(tile, yv);
+      return;
+    }
     const int64_t t0 = tile + pg * 8;
     int nv = (int)max((int64_t)0, min((int64_t)8, t_end - t0));
     if (d0 + pc >= a.dim) nv = 0;
@@ -727,6 +749,8 @@ struct FixArgs {
   void* y;
   const float* carry;
   const float* rsum;       // per-range Delta sums (nranges > 1), as written by the scan
+  const float* yf32;       // head/tail plan: the tail's y in fp32 (the scan's yf32), else null
+  int64_t yf32_pitch;
   int64_t nranges;         // ranges per chunk (1 for variable-length pieces)
   int64_t range_len;       // tokens per range (a multiple of 64)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
@@ -768,6 +792,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   const int pg = tid % 8;               // tokens 8 pg .. 8 pg + 7 of a tile
   int64_t kc, cg, b, t_begin, t_end, slot0;   // slot0: carry slot of channel 0 of the group
   int64_t rj = 0;                              // the range of the chunk (fixed-length rows)
+  int64_t c_begin0 = 0;                        // the chunk's first token (fixed-length rows)
   if constexpr (kVarlen) {
     cg = blockIdx.x % a.chgroups;
     const int64_t pidx = blockIdx.x / a.chgroups;
@@ -801,6 +826,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     b = wid / a.chgroups;
     const int64_t c_begin = kc * a.chunk_len;
     const int64_t c_end = min(c_begin + a.chunk_len, a.seqlen);
+    c_begin0 = c_begin;
     t_begin = c_begin + rj * a.range_len;
     if (t_begin >= c_end) return;     // (the last chunk may be shorter)
     t_end = min(t_begin + a.range_len, c_end);
@@ -824,7 +850,9 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     finite = finite && (fabsf(hv) <= 3.4e38f);
   }
   // a non-finite carried-in state propagates to the chunk's end (no early stop)
-  const bool may_stop = a.softplus != 0 && __syncthreads_and(finite ? 1 : 0) != 0;
+  // (and with the tail's y in fp32, every token is corrected and rounded: no early stop)
+  const bool all_finite = __syncthreads_and(finite ? 1 : 0) != 0;
+  const bool may_stop = a.softplus != 0 && all_finite && a.yf32 == nullptr;
 
   const int rows_ok = (int)min((int64_t)kFixCh, a.dim - d0);
   const int64_t row0 = (b * a.dim + d0) * a.seqlen;
@@ -882,12 +910,23 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   // two tiles ahead measured no better)
   struct Ld {
     V8 d, y, z;
+    float4 yf[2];   // the tail's y in fp32 (head/tail plan)
     V4 c[kCP];
   };
+  const float* const yf_row =
+      (!kVarlen && a.yf32 != nullptr && ch_ok) ? a.yf32 + (b * a.dim + d) * a.yf32_pitch + pg * 8 : nullptr;
   auto load = [&](int64_t tile, Ld& l) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     l.d = IO::buf_load8(rs_d, off, kVec);
-    l.y = IO::buf_load8(rs_y, off, kVec);
+    if (a.yf32 != nullptr) {
+      l.yf[0] = l.yf[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (yf_row != nullptr) {
+        l.yf[0] = reinterpret_cast<const float4*>(yf_row + (tile - c_begin0))[0];
+        l.yf[1] = reinterpret_cast<const float4*>(yf_row + (tile - c_begin0))[1];
+      }
+    } else {
+      l.y = IO::buf_load8(rs_y, off, kVec);
+    }
     l.z = IO::buf_load8(rs_z, off, kVec);
 #pragma unroll
     for (int r = 0; r < kCP; ++r) {
@@ -901,6 +940,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     const V8 vd = ld.d;
     const V8 vy = ld.y;
+    const float4 yf0 = ld.yf[0], yf1 = ld.yf[1];
     const V8 vz = ld.z;
     V4 vc[kCP];
 #pragma unroll
@@ -977,7 +1017,12 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
       }
     }
     float fy[8], fz[8];
-    IO::to_f32(vy, fy);
+    if (a.yf32 != nullptr) {
+      fy[0] = yf0.x; fy[1] = yf0.y; fy[2] = yf0.z; fy[3] = yf0.w;
+      fy[4] = yf1.x; fy[5] = yf1.y; fy[6] = yf1.z; fy[7] = yf1.w;
+    } else {
+      IO::to_f32(vy, fy);
+    }
     IO::to_f32(vz, fz);
 #pragma unroll
     for (int j = 0; j < 8; ++j) fy[j] = fmaf(acc[j], gated ? silu(fz[j]) : 1.0f, fy[j]);

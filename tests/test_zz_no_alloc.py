@@ -2,7 +2,8 @@
 workspace forward (mamba_scan_fwd) through the C ABI: same plan, same kernels, so the results
 must be identical bit for bit, and within the io tolerance of the fp64 oracle.  Two calls in a
 row, the second smaller (it reuses the scratch the first left behind), a d_state-32 call whose
-readout sum over the two state passes lives in the scratch, and a call on a side stream."""
+readout sum over the two state passes lives in the scratch, a head/tail-plan call whose tail
+keeps its y in fp32 in the scratch, and a call on a side stream."""
 import sys
 
 import pytest
@@ -61,6 +62,17 @@ def test_two_calls_second_smaller():
     small = forward_inputs(batch=1, dim=64, dstate=16, seqlen=2048, io="bf16", initial_state=True, seed=2)
     assert mscan.fwd_workspace_size(1, 64, 16, 2048, mscan.BF16) > 0
     say("call 2: b1 d64 L2048 bf16 (chunked, smaller, scratch left by call 1)")
+    check(small, "bf16")
+
+
+def test_head_tail_fp32_tail_y_in_scratch():
+    # b3 d3072 L1600: 144 channel groups, so the plan splits each row into a head and a tail whose
+    # y is kept in fp32 (in the scratch) until the fix-up rounds it once
+    inp = forward_inputs(batch=3, dim=3072, dstate=16, seqlen=1600, io="bf16", initial_state=True, seed=7)
+    say("call 1: b3 d3072 L1600 bf16 (head/tail, fp32 tail y in the scratch)")
+    check(inp, "bf16")
+    small = forward_inputs(batch=1, dim=128, dstate=16, seqlen=4096, io="bf16", initial_state=True, seed=8)
+    say("call 2: b1 d128 L4096 bf16 (chunked, smaller)")
     check(small, "bf16")
 
 
