@@ -83,26 +83,33 @@ __global__ __launch_bounds__(256) void copy_state_kernel(const float* __restrict
   if (i < n) fs[i] = h0 ? h0[i] : 0.0f;
 }
 
-template <bool kMulti>
+template <bool kMulti, bool kYf>
 struct PickH2 {
   template <typename IoT, bool kVec, int kMode>
   struct P {
-    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, kMulti>; }
+    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, kMulti, false, false, kYf>; }
   };
 };
 
+template <bool kYf>
 struct PickH2Conv {
   template <typename IoT, bool kVec, int kMode>
   struct P {
-    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, false, false, true>; }
+    static auto get() { return scan_fwd_h2_kernel<IoT, kVec, kMode, false, false, true, kYf>; }
   };
 };
 
+// the same kernel with or without the fp32 tail rows (head/tail plan)
+template <bool kYf, typename IoT>
+auto pick_scan_h2(const KArgs& k, bool vec) {
+  if (k.conv_w != nullptr) return pick_kernel<PickH2Conv<kYf>::template P, IoT>(vec, k.mode);   // 16 states, two per lane
+  if (k.acc != 0) return pick_kernel<PickH2<true, kYf>::template P, IoT>(vec, k.mode);
+  return pick_kernel<PickH2<false, kYf>::template P, IoT>(vec, k.mode);
+}
+
 template <typename IoT>
 hipError_t launch_scan_h2(const KArgs& k, bool vec, int64_t grid, hipStream_t s) {
-  auto kern = pick_kernel<PickH2<false>::template P, IoT>(vec, k.mode);
-  if (k.acc != 0) kern = pick_kernel<PickH2<true>::template P, IoT>(vec, k.mode);
-  if (k.conv_w != nullptr) kern = pick_kernel<PickH2Conv::template P, IoT>(vec, k.mode);   // 16 states, two per lane
+  auto kern = k.yf32 != nullptr ? pick_scan_h2<true, IoT>(k, vec) : pick_scan_h2<false, IoT>(k, vec);
   const size_t lds = sizeof(float) * LdsH2::floats();
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

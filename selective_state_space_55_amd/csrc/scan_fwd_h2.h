@@ -39,10 +39,6 @@ struct KArgs {
   float* rsum;         // [batch][dim][nchunks][nranges]: sum of Delta*log2e over each range of range_tiles tiles
   int64_t nranges;     // (chunks of more than one range; else rsum is null)
   int range_tiles, range_shift;   // a power of two and its log2
-  // head/tail plan: the tail chunk's gated y in fp32, (batch, dim, yf32_pitch), rounded to
-  // the io dtype once, by the fix-up, after its correction is added
-  float* yf32;
-  int64_t yf32_pitch;
   int head_tail;       // work items chunk by chunk in launch order (every head, then the tails)
   float* yacc;         // [batch][dim][seqlen] fp32 readout summed over state groups (dstate > 16)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
@@ -57,6 +53,10 @@ struct KArgs {
   const float* conv_b;     // (dim) or NULL
   const void* conv_state;  // (batch, dim, 3) io: the inputs before the sequence, or NULL (zeros)
   void* u_out;             // (batch, dim, seqlen) io: the conv output, or NULL
+  // head/tail plan: the tail chunk's gated y in fp32, (batch, dim, yf32_pitch), rounded to
+  // the io dtype once, by the fix-up, after its correction is added
+  float* yf32;
+  int64_t yf32_pitch;
 };
 
 // Work id with XCD-aware placement: the hardware deals consecutive workgroup
@@ -105,8 +105,10 @@ struct LdsH2 {
 // first piece, from the previous tile (kept in registers), the chunk's
 // preceding inputs or the conv state.  The conv output is rounded to the io
 // dtype, so the result equals the conv1d launch followed by the scan.
-template <typename IoT, bool kVec, int kMode, bool kMulti, bool kVarlen = false, bool kConv = false>
+// kYf: head/tail plan, the tail chunk's y goes to the fp32 rows a.yf32 (fixed-length rows only)
+template <typename IoT, bool kVec, int kMode, bool kMulti, bool kVarlen = false, bool kConv = false, bool kYf = false>
 __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
+  static_assert(!(kYf && kVarlen), "the fp32 tail rows exist for fixed-length rows only");
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
   using V8 = typename IO::V8;
@@ -443,7 +445,7 @@ __global__ __launch_bounds__(512) void scan_fwd_h2_kernel(KArgs a) {
   // head/tail plan, tail chunk: y goes to the fp32 buffer (rows padded to whole tiles, so the
   // pieces past the end are written too, into the padding).  The pipelined body's call for
   // tile k-1 at k = 0 (tile before the chunk) stores nothing: it would land in the previous row.
-  const bool y_to_f32 = !kVarlen && a.yf32 != nullptr && kc == 1;
+  const bool y_to_f32 = kYf && kc == 1;
   auto epi_store_f32 = [&](int64_t tile, const float (&yv)[8]) {
     if (tile < t_begin || d0 + pc >= a.dim) return;
     float* p = a.yf32 + (b * a.dim + d0 + pc) * a.yf32_pitch + (tile - t_begin) + pg * 8;
@@ -749,12 +751,12 @@ struct FixArgs {
   void* y;
   const float* carry;
   const float* rsum;       // per-range Delta sums (nranges > 1), as written by the scan
-  const float* yf32;       // head/tail plan: the tail's y in fp32 (the scan's yf32), else null
-  int64_t yf32_pitch;
   int64_t nranges;         // ranges per chunk (1 for variable-length pieces)
   int64_t range_len;       // tokens per range (a multiple of 64)
   int64_t dim, seqlen, chunk_len, nchunks, chgroups, nwork;
   int dstate, np, softplus;
+  const float* yf32;       // head/tail plan: the tail's y in fp32 (the scan's yf32), else null
+  int64_t yf32_pitch;
 };
 
 
@@ -762,7 +764,8 @@ struct FixArgs {
 // (piece, channel group) as in the scan kernel, pieces after a sequence's first
 // are fixed, and tiles stay aligned to 64 tokens of the row (the first may
 // start before the piece: its earlier tokens are masked).
-template <typename IoT, bool kVec, int NG, bool kVarlen>
+// kYf: the chunk's y is read from the fp32 rows a.yf32 (head/tail plan's tail) rather than from y
+template <typename IoT, bool kVec, int NG, bool kVarlen, bool kYf>
 __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   using IO = Io<IoT>;
   using V4 = typename IO::V4;
@@ -852,7 +855,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
   // a non-finite carried-in state propagates to the chunk's end (no early stop)
   // (and with the tail's y in fp32, every token is corrected and rounded: no early stop)
   const bool all_finite = __syncthreads_and(finite ? 1 : 0) != 0;
-  const bool may_stop = a.softplus != 0 && all_finite && a.yf32 == nullptr;
+  const bool may_stop = a.softplus != 0 && all_finite && !kYf;
 
   const int rows_ok = (int)min((int64_t)kFixCh, a.dim - d0);
   const int64_t row0 = (b * a.dim + d0) * a.seqlen;
@@ -914,11 +917,11 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
     V4 c[kCP];
   };
   const float* const yf_row =
-      (!kVarlen && a.yf32 != nullptr && ch_ok) ? a.yf32 + (b * a.dim + d) * a.yf32_pitch + pg * 8 : nullptr;
+      (kYf && ch_ok) ? a.yf32 + (b * a.dim + d) * a.yf32_pitch + pg * 8 : nullptr;
   auto load = [&](int64_t tile, Ld& l) {
     const int off = (int)(((int64_t)pc * a.seqlen + tile + pg * 8) * kEsz);
     l.d = IO::buf_load8(rs_d, off, kVec);
-    if (a.yf32 != nullptr) {
+    if constexpr (kYf) {
       l.yf[0] = l.yf[1] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       if (yf_row != nullptr) {
         l.yf[0] = reinterpret_cast<const float4*>(yf_row + (tile - c_begin0))[0];
@@ -1017,7 +1020,7 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
       }
     }
     float fy[8], fz[8];
-    if (a.yf32 != nullptr) {
+    if constexpr (kYf) {
       fy[0] = yf0.x; fy[1] = yf0.y; fy[2] = yf0.z; fy[3] = yf0.w;
       fy[4] = yf1.x; fy[5] = yf1.y; fy[6] = yf1.z; fy[7] = yf1.w;
     } else {
@@ -1058,7 +1061,14 @@ __global__ __launch_bounds__(kFixNT) void fix_kernel(FixArgs a) {
 
 template <typename IoT, int NG, bool kVarlen>
 void launch_fix(const FixArgs& f, bool vec, hipStream_t s) {
-  auto kern = vec ? fix_kernel<IoT, true, NG, kVarlen> : fix_kernel<IoT, false, NG, kVarlen>;
+  if constexpr (!kVarlen) {
+    if (f.yf32 != nullptr) {
+      auto kern = vec ? fix_kernel<IoT, true, NG, false, true> : fix_kernel<IoT, false, NG, false, true>;
+      hipLaunchKernelGGL(kern, dim3((unsigned)f.nwork), dim3(kFixNT), 0, s, f);
+      return;
+    }
+  }
+  auto kern = vec ? fix_kernel<IoT, true, NG, kVarlen, false> : fix_kernel<IoT, false, NG, kVarlen, false>;
   hipLaunchKernelGGL(kern, dim3((unsigned)f.nwork), dim3(kFixNT), 0, s, f);
 }
 

@@ -47,6 +47,7 @@ CASES = [
     (1, 64, 16, 2048, "bf16", True, True, True, True, True, True, "zoh"),     # four time chunks
     (1, 96, 16, 1000, "f32", False, True, True, False, True, True, "euler"),  # chunks, ragged tail
     (2, 128, 16, 640, "bf16", True, True, True, True, False, False, "zoh"),
+    (3, 3072, 16, 1600, "bf16", True, True, True, True, True, True, "zoh"),  # head/tail plan (144 groups)
 ]
 IDS = [f"b{c[0]}d{c[1]}n{c[2]}L{c[3]}{c[4]}{'g' if c[5] else ''}-{c[11]}" for c in CASES]
 
@@ -81,6 +82,10 @@ def test_fused_equals_conv_then_scan(case):
     assert torch.equal(fs, fs_ref), "final state"
 
 
+# The head/tail case (CASES[9]) is checked bit for bit against conv1d then scan_fwd above, and the
+# scan's head/tail plan against the oracle in the forward parity tests.  Against the oracle here the
+# bf16 conv output is rounded from fp64 on one side and from fp32 on the other, so a u near a
+# rounding tie differs by one bf16 ulp between them; over 14.7M outputs that moves a few past 1e-2.
 @pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[5], CASES[7]], ids=[IDS[0], IDS[1], IDS[5], IDS[7]])
 def test_fused_vs_oracle(case):
     inp, w, cbias, cst = make(case)
