@@ -93,9 +93,11 @@ typedef enum {
  *   flags        MAMBA_SCAN_FLAG_SOFTPLUS and/or MAMBA_SCAN_FLAG_EULER (see above)
  *   workspace    device scratch of at least mamba_scan_fwd_workspace_size(...) bytes,
  *                256-byte aligned; its contents on entry are ignored and on exit undefined.
- *                It holds the chunk carry of a chunked scan and, for dstate > 16 (run as
- *                one pass per 16 states), the fp32 readout summed over the passes
- *                (batch x dim x seqlen x 4 bytes)
+ *                It holds the chunk carry of a chunked scan (with per-range sums of Delta),
+ *                for the plan that splits each row into a head and a shorter tail (129-204
+ *                groups of 64 channels) the tail's y in fp32 (batch x dim x tail tokens x 4
+ *                bytes), and, for dstate > 16 (run as one pass per 16 states), the fp32
+ *                readout summed over the passes (batch x dim x seqlen x 4 bytes)
  *
  * Sizes: batch >= 1, dim >= 1, 1 <= dstate <= 64, seqlen >= 0, and
  * 64 * (seqlen + 8) * sizeof(io element) < 2^31 (seqlen < 4,194,296 for
@@ -110,7 +112,8 @@ int mamba_scan_fwd(const void* u, const void* delta, const float* A_log, const v
                    float* final_state, void* y, int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen,
                    int io_dtype, int flags, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace mamba_scan_fwd needs for these sizes (0 only for seqlen == 0).
+/* Bytes of workspace mamba_scan_fwd needs for these sizes (0 when it needs none: seqlen == 0,
+ * or a one-pass scan with dstate <= 16).
  * Returns (size_t)-1 for sizes mamba_scan_fwd would reject. */
 size_t mamba_scan_fwd_workspace_size(int64_t batch, int64_t dim, int64_t dstate, int64_t seqlen, int io_dtype);
 
