@@ -107,16 +107,19 @@ def test_chunked_ragged_channel_groups(dim, dstate):
     check("final_state", fs, fsr, TOL["f32"])
 
 
-@pytest.mark.parametrize("batch,dim,n,L,io", [(3, 3072, 16, 1600, "f32"), (3, 3000, 16, 3000, "bf16"),
-                                               (8, 1536, 16, 2048, "bf16"), (3, 3072, 32, 1600, "bf16")])
-def test_head_tail_plan_vs_oracle(batch, dim, n, L, io):
+@pytest.mark.parametrize("batch,dim,n,L,io,gated", [(3, 3072, 16, 1600, "f32", True), (3, 3000, 16, 3000, "bf16", True),
+                                                     (8, 1536, 16, 2048, "bf16", True), (3, 3072, 32, 1600, "bf16", True),
+                                                     (3, 3072, 16, 3001, "f32", False)])
+def test_head_tail_plan_vs_oracle(batch, dim, n, L, io, gated):
     """Between 128 and 256 channel groups the automatic plan splits each row into a head (one
     workgroup per CU, launched first) and a tail on the CUs left idle, whose fix-up runs in short
     ranges and rounds the tail's fp32 y to the io dtype once: 141-144 groups with tails of 8 tiles
     (2-tile ranges) and 15 tiles (4-tile ranges), and the 130M layer (192 groups, 3 rounds of
-    tails of 7 tiles); at d_state 32 the tail's fp32 y is the readout summed over both state passes."""
-    inp = forward_inputs(batch=batch, dim=dim, dstate=n, seqlen=L, io=io, initial_state=True, seed=L + n)
-    say(f"head/tail plan batch={batch} dim={dim} n={n} L={L} io={io}")
+    tails of 7 tiles); at d_state 32 the tail's fp32 y is the readout summed over both state passes;
+    L 3001 (rows not 16-byte aligned, a ragged last tile), ungated, tails of 15 tiles."""
+    inp = forward_inputs(batch=batch, dim=dim, dstate=n, seqlen=L, io=io, gated=gated, initial_state=True,
+                         seed=L + n)
+    say(f"head/tail plan batch={batch} dim={dim} n={n} L={L} io={io} gated={gated}")
     y, fs = gpu_fwd(inp)
     yr, fsr = oracle_fwd(inp)
     check("y", y, yr, TOL[io])
